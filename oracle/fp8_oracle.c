@@ -1,0 +1,310 @@
+/*
+ * fp8_oracle.c -- the CPU oracle for the FP8 training hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this file.  Only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark use it, to check and to time the GPU library.  It shares
+ * no code, header, table or constant generator with the GPU library.
+ *
+ * What it computes (plain definitions, written for a reader to check by eye):
+ *
+ *   Sources.  "LLMQ: Efficient Lower-Precision Pretraining for Consumer GPUs"
+ *   (paperlayer.ai summary of arXiv 2512.15306): section 1 (FP8 training with
+ *   dynamic tensor-level scaling), section 3.1 (retained absmax statistics let
+ *   the requantisation fuse with the nonlinearity during recomputation, with no
+ *   second global reduction), section 4 (dynamic quantisation and
+ *   backward-pass transposes are overhead; extra transpose and quantisation
+ *   buffers), section 5 / Figure 2 (E4M3 forward and backward versus E5M2
+ *   activation gradients).  "FastML periodic report" (EU CORDIS), the item on
+ *   FP8 training without delayed scaling: the scale comes just in time from the
+ *   tensor's current absmax, so no value is clipped.
+ *
+ *   The pages give no bit layouts, formula, rounding mode or accumulation
+ *   precision.  This file takes the readings below (each is listed with its
+ *   reason in the design notes):
+ *     - formats: OCP 8-bit floating point (OFP8) E4M3 ("fn": bias 7, no
+ *       infinity, NaN = S.1111.111, max 448) and E5M2 (bias 15, IEEE-like,
+ *       infinity S.11111.00, max 57344);
+ *     - absmax = max |x| over the whole tensor (an exact maximum);
+ *     - scale s = fp8_max / absmax as one IEEE fp32 division, s = 1 when
+ *       absmax = 0, s clamped to FLT_MAX when the division overflows;
+ *       inverse scale = 1 / s in fp32;
+ *     - q = encode(RN32(x * s)): the product rounded to fp32 first, then
+ *       rounded to the 8-bit format, nearest-even, saturating at +-max;
+ *     - SwiGLU: h = silu(g) * u with silu(g) = g / (1 + e^-g), gate and up
+ *       concatenated as [gate | up] along the feature axis, every step one
+ *       fp32 operation in the order E = RN32(e^-g), t = 1 + E, s_g = g / t,
+ *       h = s_g * u, and e^-g correctly rounded to fp32;
+ *     - GEMM: fp32 sum over ascending k of the decoded products (every
+ *       FP8 x FP8 product is exact in fp32), then one multiply by
+ *       RN32(da * db), then round-to-nearest-even to bf16.
+ *
+ * Built with gcc -O2 -ffp-contract=off (no fast-math), so every float
+ * operation below is exactly one IEEE binary32 operation (x86-64 SSE).
+ */
+#include <float.h>
+#include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+#include <stdint.h>
+#include <string.h>
+
+#define FMT_E4M3 0
+#define FMT_E5M2 1
+
+static float f32_from_bits(uint32_t b) { float f; memcpy(&f, &b, 4); return f; }
+static uint32_t bits_from_f32(float f) { uint32_t b; memcpy(&b, &f, 4); return b; }
+
+/* bf16 -> fp32: the bf16 bits are the top half of the fp32 bits (exact). */
+float oracle_bf16_to_f32(uint16_t b) { return f32_from_bits((uint32_t)b << 16); }
+
+/* fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t b = bits_from_f32(f);
+    if (isnan(f)) return (uint16_t)((b >> 16) | 0x0040u);
+    uint32_t lower = b & 0xFFFFu;
+    uint32_t upper = b >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
+    return (uint16_t)upper;
+}
+
+/* Parameters of the two OFP8 formats. */
+struct fmt_desc { int mbits; int bias; float maxv; uint8_t maxcode; };
+static struct fmt_desc fmt_of(int fmt)
+{
+    struct fmt_desc d;
+    if (fmt == FMT_E4M3) { d.mbits = 3; d.bias = 7;  d.maxv = 448.0f;   d.maxcode = 0x7E; }
+    else                 { d.mbits = 2; d.bias = 15; d.maxv = 57344.0f; d.maxcode = 0x7B; }
+    return d;
+}
+
+/*
+ * Encode one fp32 value to an OFP8 byte: round to nearest, ties to even,
+ * saturating.  NaN -> S.1111111 (0x7F | sign).  |v| > max (infinity included)
+ * -> +-max.  Underflow keeps the sign (-tiny -> 0x80).
+ */
+uint8_t oracle_encode(float v, int fmt)
+{
+    struct fmt_desc d = fmt_of(fmt);
+    uint8_t sign = (uint8_t)((bits_from_f32(v) >> 24) & 0x80u);
+    if (isnan(v)) return (uint8_t)(sign | 0x7F);
+    float a = fabsf(v);
+    if (a > d.maxv) return (uint8_t)(sign | d.maxcode);
+
+    int emin = 1 - d.bias;                      /* exponent of the smallest normal */
+    float min_normal = ldexpf(1.0f, emin);
+    if (a < min_normal) {
+        /* Subnormal range: a multiple of the quantum 2^(emin - mbits). */
+        float steps = ldexpf(a, d.mbits - emin);   /* exact: a power-of-two scaling up */
+        float m = nearbyintf(steps);               /* default rounding mode: ties to even */
+        /* m == 2^mbits lands exactly on the smallest normal code (exponent field 1). */
+        return (uint8_t)(sign | (uint8_t)m);
+    }
+    int e;
+    float r = frexpf(a, &e);                    /* a = r * 2^e, r in [0.5, 1) */
+    r *= 2.0f; e -= 1;                          /* a = r * 2^e, r in [1, 2) (exact) */
+    float m = nearbyintf(ldexpf(r - 1.0f, d.mbits));   /* r - 1 and the scaling are exact */
+    if (m == ldexpf(1.0f, d.mbits)) { m = 0.0f; e += 1; }
+    return (uint8_t)(sign | (uint8_t)((e + d.bias) << d.mbits) | (uint8_t)m);
+}
+
+/* Decode one OFP8 byte to fp32 (exact: every OFP8 value is an fp32 value). */
+float oracle_decode(uint8_t c, int fmt)
+{
+    struct fmt_desc d = fmt_of(fmt);
+    int sign = c & 0x80;
+    int ebits = 7 - d.mbits;
+    int efield = (c >> d.mbits) & ((1 << ebits) - 1);
+    int mfield = c & ((1 << d.mbits) - 1);
+    float mag;
+    if (fmt == FMT_E4M3 && (c & 0x7F) == 0x7F) return sign ? -NAN : NAN;
+    if (fmt == FMT_E5M2 && efield == 31) {
+        if (mfield != 0) return sign ? -NAN : NAN;
+        return sign ? -INFINITY : INFINITY;
+    }
+    if (efield == 0) mag = ldexpf((float)mfield, 1 - d.bias - d.mbits);
+    else mag = ldexpf(1.0f + ldexpf((float)mfield, -d.mbits), efield - d.bias);
+    return sign ? -mag : mag;
+}
+
+/*
+ * absmax of a bf16 tensor: the largest magnitude bit pattern.  For finite data
+ * this is max |x_i|; a NaN or infinity anywhere sorts above every finite value,
+ * so it surfaces in the result.
+ */
+float oracle_absmax_bf16(const uint16_t* x, int64_t n)
+{
+    uint32_t best = 0;
+    #pragma omp parallel for reduction(max:best) schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t m = x[i] & 0x7FFFu;
+        if (m > best) best = m;
+    }
+    return f32_from_bits(best << 16);
+}
+
+/* absmax of an fp32 tensor, same rule on the 31 magnitude bits. */
+float oracle_absmax_f32(const float* x, int64_t n)
+{
+    uint32_t best = 0;
+    #pragma omp parallel for reduction(max:best) schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t m = bits_from_f32(x[i]) & 0x7FFFFFFFu;
+        if (m > best) best = m;
+    }
+    return f32_from_bits(best);
+}
+
+/* scale = fp8_max / absmax (fp32), inverse = 1 / scale (fp32). */
+void oracle_scale(float absmax, int fmt, float* scale, float* inv_scale)
+{
+    float s;
+    if (absmax == 0.0f) s = 1.0f;
+    else {
+        s = fmt_of(fmt).maxv / absmax;
+        if (isinf(s) && s > 0.0f) s = FLT_MAX;
+    }
+    *scale = s;
+    *inv_scale = 1.0f / s;
+}
+
+/*
+ * Quantise a row-major bf16 [rows, cols] tensor with scale s.
+ * q[i*cols + j] = encode(RN32(x[i,j] * s)); qt[j*rows + i] is the same byte
+ * (the transposed copy the backward GEMMs read).  Either output may be NULL.
+ */
+void oracle_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, float s,
+                     uint8_t* q, uint8_t* qt)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        for (int64_t j = 0; j < cols; ++j) {
+            float p = oracle_bf16_to_f32(x[i * cols + j]) * s;
+            uint8_t c = oracle_encode(p, fmt);
+            if (q) q[i * cols + j] = c;
+            if (qt) qt[j * rows + i] = c;
+        }
+    }
+}
+
+/* RN32(e^-g): the exact exponential rounded once to fp32 (through libm's double exp). */
+float oracle_exp_neg(float g)
+{
+    return (float)exp(-(double)g);
+}
+
+/* h = silu(g) * u, one fp32 operation at a time. */
+float oracle_swiglu_one(float g, float u)
+{
+    float E = oracle_exp_neg(g);
+    float t = 1.0f + E;
+    float sg = g / t;
+    return sg * u;
+}
+
+/* The SwiGLU output h[M, F] (fp32) of gu = [gate | up], a bf16 [M, 2F] tensor. */
+void oracle_swiglu_h(const uint16_t* gu, int64_t M, int64_t F, float* h)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < F; ++j) {
+            float g = oracle_bf16_to_f32(gu[i * 2 * F + j]);
+            float u = oracle_bf16_to_f32(gu[i * 2 * F + F + j]);
+            h[i * F + j] = oracle_swiglu_one(g, u);
+        }
+}
+
+/*
+ * SwiGLU requantisation.  compute_absmax = 1 (forward): absmax_h is the
+ * absmax of every h and is written out.  compute_absmax = 0 (recomputation):
+ * *absmax_h is the retained statistic and is only read, no reduction runs.
+ * Then hq = encode_e4m3(RN32(h * s_h)); hqt (may be NULL) is its transpose.
+ * h_buf is caller scratch of M*F floats.
+ */
+void oracle_swiglu_requant(const uint16_t* gu, int64_t M, int64_t F, int compute_absmax,
+                           float* absmax_h, float* inv_scale_h, float* h_buf,
+                           uint8_t* hq, uint8_t* hqt)
+{
+    float s, inv;
+    oracle_swiglu_h(gu, M, F, h_buf);
+    if (compute_absmax) *absmax_h = oracle_absmax_f32(h_buf, M * F);
+    oracle_scale(*absmax_h, FMT_E4M3, &s, &inv);
+    if (inv_scale_h) *inv_scale_h = inv;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < F; ++j) {
+            uint8_t c = oracle_encode(h_buf[i * F + j] * s, FMT_E4M3);
+            if (hq) hq[i * F + j] = c;
+            if (hqt) hqt[j * M + i] = c;
+        }
+}
+
+/*
+ * FP8 GEMM with both operands K-contiguous:
+ *   C[m, n] = sum over k = 0..K-1 (ascending) of dec(A[m, k]) * dec(B[n, k])   (fp32)
+ *   Y[m, n] = bf16_RNE(RN32(C[m, n] * RN32(da * db)))
+ * A is [M, K] in format fmt_a, B is [N, K] in format fmt_b.  When rows is not
+ * NULL only the nrows listed rows m = rows[r] are computed, into Y[r, :].
+ * a_dec / b_dec are caller scratch of nrows*K and N*K floats.
+ */
+void oracle_gemm(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
+                 int64_t M, int64_t N, int64_t K, float da, float db,
+                 const int64_t* rows, int64_t nrows, float* a_dec, float* b_dec,
+                 uint16_t* Y)
+{
+    float descale = da * db;
+    if (!rows) nrows = M;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) b_dec[n * K + k] = oracle_decode(B[n * K + k], fmt_b);
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t m = rows ? rows[r] : r;
+        for (int64_t k = 0; k < K; ++k) a_dec[r * K + k] = oracle_decode(A[m * K + k], fmt_a);
+    }
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const float* a = a_dec + r * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const float* b = b_dec + n * K;
+            float acc = 0.0f;
+            for (int64_t k = 0; k < K; ++k) acc += a[k] * b[k];
+            Y[r * N + n] = oracle_f32_to_bf16(acc * descale);
+        }
+    }
+}
+
+/* Element-wise helpers for vectors, so the Python side needs no loops. */
+void oracle_encode_vec(const float* v, int64_t n, int fmt, uint8_t* out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_encode(v[i], fmt);
+}
+
+void oracle_decode_vec(const uint8_t* c, int64_t n, int fmt, float* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_decode(c[i], fmt);
+}
+
+void oracle_exp_neg_vec(const float* g, int64_t n, float* out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_exp_neg(g[i]);
+}
+
+int oracle_num_threads(void)
+{
+    int t = 1;
+    #pragma omp parallel
+    {
+        #pragma omp single
+        {
+#ifdef _OPENMP
+            t = omp_get_num_threads();
+#endif
+        }
+    }
+    return t;
+}
