@@ -1,0 +1,9 @@
+"""MI355X (gfx950) FP8 training hot path: absmax, quantise, SwiGLU requant, FP8 GEMMs.
+
+The compute runs in hand-written HIP kernels behind the C ABI declared in
+``include/fp8_precision.h``; this package is the thin Python binding over it.
+"""
+from ._lib import (  # noqa: F401
+    E4M3, E5M2, EXPORTED, LIB_PATH, Fp8Error,
+    absmax, quantize, swiglu_requant, gemm_fwd, gemm_dgrad, gemm_wgrad,
+)

@@ -1,0 +1,200 @@
+"""ctypes binding of ``libfp8_precision.so`` (the C ABI in include/fp8_precision.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  torch supplies device memory (tensors are passed by ``data_ptr()``)
+and the stream (torch's current stream on the tensor's device).  If the
+library is missing, importing this module raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+E4M3 = 0
+E5M2 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8_precision.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m fp8_precision_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i64, _i32, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+_SIGS = {
+    "fp8_status_string": (ctypes.c_char_p, [_i32]),
+    "fp8_last_error": (ctypes.c_char_p, []),
+    "fp8_absmax": (_i32, [_vp, _i64, _vp, _vp]),
+    "fp8_quantize": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "fp8_swiglu_requant": (_i32, [_vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp]),
+    "fp8_gemm_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "fp8_gemm_dgrad": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "fp8_gemm_wgrad": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class Fp8Error(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        detail = _lib.fp8_last_error().decode()
+        super().__init__(f"{call} failed: {_lib.fp8_status_string(status).decode()} ({detail})")
+
+
+def _check(call: str, status: int) -> None:
+    if status != 0:
+        raise Fp8Error(call, status)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev_tensor(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _scalar(t, name, device):
+    if t is None:
+        return torch.empty(1, dtype=torch.float32, device=device)
+    _dev_tensor(t, name, torch.float32)
+    if t.numel() < 1:
+        raise ValueError(f"{name} must hold at least one fp32")
+    return t
+
+
+def absmax(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """max |x| of a bf16 tensor, as a one-element fp32 device tensor."""
+    _dev_tensor(x, "x", torch.bfloat16)
+    out = _scalar(out, "out", x.device)
+    _check("fp8_absmax", _lib.fp8_absmax(_ptr(x), x.numel(), _ptr(out), _stream(x)))
+    return out
+
+
+def quantize(x: torch.Tensor, fmt: int, amax: torch.Tensor, want_q: bool = True, want_qt: bool = False,
+             q: torch.Tensor | None = None, qt: torch.Tensor | None = None,
+             scale: torch.Tensor | None = None, inv_scale: torch.Tensor | None = None):
+    """Quantise a 2-D bf16 tensor with the scale of ``amax``.
+
+    Returns (q uint8 [rows, cols] or None, qt uint8 [cols, rows] or None,
+    scale fp32 [1], inv_scale fp32 [1]).
+    """
+    _dev_tensor(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    _dev_tensor(amax, "amax", torch.float32)
+    if want_q and q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if want_qt and qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    for t, n in ((q, "q"), (qt, "qt")):
+        if t is not None:
+            _dev_tensor(t, n, torch.uint8)
+            if t.numel() != rows * cols:
+                raise ValueError(f"{n} has the wrong size")
+    scale = _scalar(scale, "scale", x.device)
+    inv_scale = _scalar(inv_scale, "inv_scale", x.device)
+    _check("fp8_quantize", _lib.fp8_quantize(_ptr(x), rows, cols, int(fmt), _ptr(amax), _ptr(q), _ptr(qt),
+                                             _ptr(scale), _ptr(inv_scale), _stream(x)))
+    return q, qt, scale, inv_scale
+
+
+def swiglu_requant(gu: torch.Tensor, absmax_h: torch.Tensor | None = None, compute_absmax: bool = True,
+                   want_hq: bool = True, want_hqt: bool = False, hq: torch.Tensor | None = None,
+                   hqt: torch.Tensor | None = None, inv_scale_h: torch.Tensor | None = None):
+    """SwiGLU of gu = [gate | up] (bf16 [M, 2F]) requantised to e4m3.
+
+    compute_absmax True: absmax_h is computed (forward).  False: the given
+    retained absmax_h is used and no reduction runs (recomputation).
+    Returns (hq or None, hqt or None, absmax_h, inv_scale_h).
+    """
+    _dev_tensor(gu, "gu", torch.bfloat16)
+    if gu.dim() != 2 or gu.shape[1] % 2:
+        raise ValueError("gu must be [M, 2F]")
+    M, F = gu.shape[0], gu.shape[1] // 2
+    if not compute_absmax and absmax_h is None:
+        raise ValueError("recomputation needs the retained absmax_h")
+    absmax_h = _scalar(absmax_h, "absmax_h", gu.device)
+    if want_hq and hq is None:
+        hq = torch.empty((M, F), dtype=torch.uint8, device=gu.device)
+    if want_hqt and hqt is None:
+        hqt = torch.empty((F, M), dtype=torch.uint8, device=gu.device)
+    for t, n in ((hq, "hq"), (hqt, "hqt")):
+        if t is not None:
+            _dev_tensor(t, n, torch.uint8)
+            if t.numel() != M * F:
+                raise ValueError(f"{n} has the wrong size")
+    inv_scale_h = _scalar(inv_scale_h, "inv_scale_h", gu.device)
+    _check("fp8_swiglu_requant", _lib.fp8_swiglu_requant(_ptr(gu), M, F, _ptr(absmax_h), 1 if compute_absmax else 0,
+                                                         _ptr(hq), _ptr(hqt), _ptr(inv_scale_h), _stream(gu)))
+    return hq, hqt, absmax_h, inv_scale_h
+
+
+def _out_bf16(out, shape, device):
+    if out is None:
+        return torch.empty(shape, dtype=torch.bfloat16, device=device)
+    _dev_tensor(out, "out", torch.bfloat16)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must have shape {tuple(shape)}")
+    return out
+
+
+def gemm_fwd(xq, wq, inv_sx, inv_sw, out=None) -> torch.Tensor:
+    """Y[M, N] = X[M, K] . W[N, K]^T (both e4m3), bf16 out."""
+    _dev_tensor(xq, "xq", torch.uint8)
+    _dev_tensor(wq, "wq", torch.uint8)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("xq is [M, K] and wq must be [N, K]")
+    out = _out_bf16(out, (M, N), xq.device)
+    _check("fp8_gemm_fwd", _lib.fp8_gemm_fwd(_ptr(xq), _ptr(wq), _ptr(inv_sx), _ptr(inv_sw), _ptr(out),
+                                             M, N, K, _stream(xq)))
+    return out
+
+
+def gemm_dgrad(dyq, dy_fmt, wqt, inv_sdy, inv_sw, out=None) -> torch.Tensor:
+    """dX[M, K] = dY[M, N] . W[N, K], with W passed transposed as wqt [K, N]."""
+    _dev_tensor(dyq, "dyq", torch.uint8)
+    _dev_tensor(wqt, "wqt", torch.uint8)
+    M, N = dyq.shape
+    K = wqt.shape[0]
+    if wqt.shape[1] != N:
+        raise ValueError("dyq is [M, N] and wqt must be [K, N]")
+    out = _out_bf16(out, (M, K), dyq.device)
+    _check("fp8_gemm_dgrad", _lib.fp8_gemm_dgrad(_ptr(dyq), int(dy_fmt), _ptr(wqt), _ptr(inv_sdy), _ptr(inv_sw),
+                                                 _ptr(out), M, N, K, _stream(dyq)))
+    return out
+
+
+def gemm_wgrad(dyqt, dy_fmt, xqt, inv_sdy, inv_sx, out=None) -> torch.Tensor:
+    """dW[N, K] = dY[M, N]^T . X[M, K], with dY and X passed transposed ([N, M], [K, M])."""
+    _dev_tensor(dyqt, "dyqt", torch.uint8)
+    _dev_tensor(xqt, "xqt", torch.uint8)
+    N, M = dyqt.shape
+    K = xqt.shape[0]
+    if xqt.shape[1] != M:
+        raise ValueError("dyqt is [N, M] and xqt must be [K, M]")
+    out = _out_bf16(out, (N, K), dyqt.device)
+    _check("fp8_gemm_wgrad", _lib.fp8_gemm_wgrad(_ptr(dyqt), int(dy_fmt), _ptr(xqt), _ptr(inv_sdy), _ptr(inv_sx),
+                                                 _ptr(out), M, N, K, _stream(dyqt)))
+    return out

@@ -1,0 +1,234 @@
+// api.cpp -- the C ABI of the FP8 hot path: argument checks, then launches.
+//
+// Every entry point validates its arguments on the host before enqueuing
+// anything; see include/fp8_precision.h for the contract of each call.
+#include "fp8_precision.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "fp8_internal.hpp"
+
+namespace {
+
+thread_local std::string t_last_error;
+
+fp8_status fail(fp8_status st, const char* what)
+{
+    t_last_error = what;
+    return st;
+}
+
+fp8_status fail_hip(const char* call, hipError_t e)
+{
+    char buf[256];
+    std::snprintf(buf, sizeof(buf), "%s: HIP error %d (%s)", call, (int)e, hipGetErrorString(e));
+    t_last_error = buf;
+    return FP8_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte ranges [p, p + n) and [q, q + m) overlap.
+bool overlap(const void* p, int64_t n, const void* q, int64_t m)
+{
+    if (!p || !q || n <= 0 || m <= 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + (uintptr_t)m && b < a + (uintptr_t)n;
+}
+
+struct Range {
+    const void* p;
+    int64_t n;
+};
+
+// True if any two of the ranges overlap.
+template <int N>
+bool any_overlap(const Range (&r)[N])
+{
+    for (int i = 0; i < N; ++i)
+        for (int j = i + 1; j < N; ++j)
+            if (overlap(r[i].p, r[i].n, r[j].p, r[j].n)) return true;
+    return false;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a > 0 && b > 0 && a <= limit / b; }
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+}  // namespace
+
+namespace fp8k {
+
+int device_cu_count()
+{
+    static std::mutex mu;
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lk(mu);
+    if (cache[dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+            cu = 256;
+        cache[dev] = cu;
+    }
+    return cache[dev];
+}
+
+}  // namespace fp8k
+
+extern "C" {
+
+const char* fp8_status_string(fp8_status s)
+{
+    switch (s) {
+    case FP8_OK: return "ok";
+    case FP8_ERR_INVALID: return "invalid argument";
+    case FP8_ERR_UNSUPPORTED: return "unsupported argument (alignment or shape constraint)";
+    case FP8_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* fp8_last_error(void) { return t_last_error.c_str(); }
+
+fp8_status fp8_absmax(const void* x, int64_t n, float* absmax, hipStream_t stream)
+{
+    t_last_error.clear();
+    if (!x || !absmax) return fail(FP8_ERR_INVALID, "fp8_absmax: null pointer");
+    if (n <= 0 || n > kMaxElems) return fail(FP8_ERR_INVALID, "fp8_absmax: n must be in [1, 2^40]");
+    if (overlap(x, 2 * n, absmax, 4)) return fail(FP8_ERR_INVALID, "fp8_absmax: absmax overlaps x");
+    if (!aligned(x, 16) || !aligned(absmax, 4))
+        return fail(FP8_ERR_UNSUPPORTED, "fp8_absmax: x must be 16-byte and absmax 4-byte aligned");
+    hipError_t e = fp8k::launch_absmax_bf16(x, n, absmax, stream);
+    if (e != hipSuccess) return fail_hip("fp8_absmax", e);
+    return FP8_OK;
+}
+
+fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt, const float* absmax,
+                        uint8_t* q, uint8_t* qt, float* scale, float* inv_scale, hipStream_t stream)
+{
+    t_last_error.clear();
+    if (!x || !absmax) return fail(FP8_ERR_INVALID, "fp8_quantize: null x or absmax");
+    if (!q && !qt) return fail(FP8_ERR_INVALID, "fp8_quantize: at least one of q, qt is required");
+    if (fmt != FP8_E4M3 && fmt != FP8_E5M2) return fail(FP8_ERR_INVALID, "fp8_quantize: bad format");
+    if (!mul_ok(rows, cols, kMaxElems)) return fail(FP8_ERR_INVALID, "fp8_quantize: bad shape");
+    const int64_t n = rows * cols;
+    const Range r[] = {{x, 2 * n}, {absmax, 4}, {q, q ? n : 0}, {qt, qt ? n : 0},
+                       {scale, scale ? 4 : 0}, {inv_scale, inv_scale ? 4 : 0}};
+    if (any_overlap(r)) return fail(FP8_ERR_INVALID, "fp8_quantize: overlapping buffers");
+    if (cols % 16) return fail(FP8_ERR_UNSUPPORTED, "fp8_quantize: cols must be a multiple of 16");
+    if (qt && rows % 16) return fail(FP8_ERR_UNSUPPORTED, "fp8_quantize: rows must be a multiple of 16 with qt");
+    if (qt && (rows + 63) / 64 > 65535) return fail(FP8_ERR_UNSUPPORTED, "fp8_quantize: too many rows for qt");
+    if (!aligned(x, 16) || (q && !aligned(q, 16)) || (qt && !aligned(qt, 16)) || !aligned(absmax, 4) ||
+        (scale && !aligned(scale, 4)) || (inv_scale && !aligned(inv_scale, 4)))
+        return fail(FP8_ERR_UNSUPPORTED, "fp8_quantize: misaligned pointer");
+    hipError_t e = fp8k::launch_quantize(x, rows, cols, (int)fmt, absmax, q, qt, scale, inv_scale, stream);
+    if (e != hipSuccess) return fail_hip("fp8_quantize", e);
+    return FP8_OK;
+}
+
+fp8_status fp8_swiglu_requant(const void* gu, int64_t M, int64_t F, float* absmax_h, int compute_absmax,
+                              uint8_t* hq, uint8_t* hqt, float* inv_scale_h, hipStream_t stream)
+{
+    t_last_error.clear();
+    if (!gu || !absmax_h) return fail(FP8_ERR_INVALID, "fp8_swiglu_requant: null gu or absmax_h");
+    if (!hq && !hqt) return fail(FP8_ERR_INVALID, "fp8_swiglu_requant: at least one of hq, hqt is required");
+    if (compute_absmax != 0 && compute_absmax != 1)
+        return fail(FP8_ERR_INVALID, "fp8_swiglu_requant: compute_absmax must be 0 or 1");
+    if (!mul_ok(M, 2 * F, kMaxElems) || F <= 0) return fail(FP8_ERR_INVALID, "fp8_swiglu_requant: bad shape");
+    const int64_t n = M * F;
+    const Range r[] = {{gu, 4 * n}, {absmax_h, 4}, {hq, hq ? n : 0}, {hqt, hqt ? n : 0},
+                       {inv_scale_h, inv_scale_h ? 4 : 0}};
+    if (any_overlap(r)) return fail(FP8_ERR_INVALID, "fp8_swiglu_requant: overlapping buffers");
+    if (F % 16) return fail(FP8_ERR_UNSUPPORTED, "fp8_swiglu_requant: F must be a multiple of 16");
+    if (hqt && M % 16) return fail(FP8_ERR_UNSUPPORTED, "fp8_swiglu_requant: M must be a multiple of 16 with hqt");
+    if (!aligned(gu, 16) || (hq && !aligned(hq, 16)) || (hqt && !aligned(hqt, 16)) || !aligned(absmax_h, 4) ||
+        (inv_scale_h && !aligned(inv_scale_h, 4)))
+        return fail(FP8_ERR_UNSUPPORTED, "fp8_swiglu_requant: misaligned pointer");
+    hipError_t e = fp8k::launch_swiglu_requant(gu, M, F, absmax_h, compute_absmax, hq, hqt, inv_scale_h, stream);
+    if (e != hipSuccess) return fail_hip("fp8_swiglu_requant", e);
+    return FP8_OK;
+}
+
+// Shared checks of the three GEMM calls, in the TN form out[P, Q] = A[P, R] . B[Q, R]^T.
+static fp8_status gemm_common(const char* name, const uint8_t* A, int fmt_a, const uint8_t* B, const float* inv_a,
+                              const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream)
+{
+    char msg[160];
+    if (!A || !B || !inv_a || !inv_b || !out) {
+        std::snprintf(msg, sizeof(msg), "%s: null pointer", name);
+        return fail(FP8_ERR_INVALID, msg);
+    }
+    if (fmt_a != FP8_E4M3 && fmt_a != FP8_E5M2) {
+        std::snprintf(msg, sizeof(msg), "%s: bad operand format", name);
+        return fail(FP8_ERR_INVALID, msg);
+    }
+    if (P <= 0 || Q <= 0 || R <= 0) {
+        std::snprintf(msg, sizeof(msg), "%s: dimensions must be positive", name);
+        return fail(FP8_ERR_INVALID, msg);
+    }
+    const Range r[] = {{A, P * R}, {B, Q * R}, {inv_a, 4}, {inv_b, 4}, {out, 2 * P * Q}};
+    // the two inputs may alias each other (e.g. A == B); the output may alias nothing
+    for (int i = 0; i < 4; ++i)
+        if (overlap(r[i].p, r[i].n, r[4].p, r[4].n)) {
+            std::snprintf(msg, sizeof(msg), "%s: output overlaps an input", name);
+            return fail(FP8_ERR_INVALID, msg);
+        }
+    if (P % 16 || Q % 16 || R % 128 || P < 16 || Q < 16) {
+        std::snprintf(msg, sizeof(msg), "%s: output dimensions must be multiples of 16, the reduction a multiple of 128",
+                      name);
+        return fail(FP8_ERR_UNSUPPORTED, msg);
+    }
+    if (P * R >= ((int64_t)1 << 31) || Q * R >= ((int64_t)1 << 31) || P >= ((int64_t)1 << 30) ||
+        Q >= ((int64_t)1 << 30) || ((P + 255) / 256) * ((Q + 255) / 256) >= ((int64_t)1 << 31)) {
+        std::snprintf(msg, sizeof(msg), "%s: operand larger than 2 GiB", name);
+        return fail(FP8_ERR_UNSUPPORTED, msg);
+    }
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(out, 16) || !aligned(inv_a, 4) || !aligned(inv_b, 4)) {
+        std::snprintf(msg, sizeof(msg), "%s: misaligned pointer", name);
+        return fail(FP8_ERR_UNSUPPORTED, msg);
+    }
+    (void)stream;
+    return FP8_OK;
+}
+
+fp8_status fp8_gemm_fwd(const uint8_t* xq, const uint8_t* wq, const float* inv_sx, const float* inv_sw, void* y,
+                        int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    t_last_error.clear();
+    fp8_status st = gemm_common("fp8_gemm_fwd", xq, FP8_E4M3, wq, inv_sx, inv_sw, y, M, N, K, stream);
+    if (st != FP8_OK) return st;
+    hipError_t e = fp8k::launch_gemm_tn(xq, 0, wq, 0, inv_sx, inv_sw, y, M, N, K, stream);
+    if (e != hipSuccess) return fail_hip("fp8_gemm_fwd", e);
+    return FP8_OK;
+}
+
+fp8_status fp8_gemm_dgrad(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_t* wqt, const float* inv_sdy,
+                          const float* inv_sw, void* dx, int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    t_last_error.clear();
+    fp8_status st = gemm_common("fp8_gemm_dgrad", dyq, (int)dy_fmt, wqt, inv_sdy, inv_sw, dx, M, K, N, stream);
+    if (st != FP8_OK) return st;
+    hipError_t e = fp8k::launch_gemm_tn(dyq, (int)dy_fmt, wqt, 0, inv_sdy, inv_sw, dx, M, K, N, stream);
+    if (e != hipSuccess) return fail_hip("fp8_gemm_dgrad", e);
+    return FP8_OK;
+}
+
+fp8_status fp8_gemm_wgrad(const uint8_t* dyqt, fp8_fmt dy_fmt, const uint8_t* xqt, const float* inv_sdy,
+                          const float* inv_sx, void* dw, int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    t_last_error.clear();
+    fp8_status st = gemm_common("fp8_gemm_wgrad", dyqt, (int)dy_fmt, xqt, inv_sdy, inv_sx, dw, N, K, M, stream);
+    if (st != FP8_OK) return st;
+    hipError_t e = fp8k::launch_gemm_tn(dyqt, (int)dy_fmt, xqt, 0, inv_sdy, inv_sx, dw, N, K, M, stream);
+    if (e != hipSuccess) return fail_hip("fp8_gemm_wgrad", e);
+    return FP8_OK;
+}
+
+}  // extern "C"

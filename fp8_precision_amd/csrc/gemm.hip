@@ -1,0 +1,286 @@
+// gemm.hip -- FP8 GEMM with fp32 accumulation and per-tensor descale, gfx950.
+//
+//   out[p, q] = bf16_RNE( RN32( sum_r dec(A[p, r]) * dec(B[q, r]) ) * RN32(inv_a * inv_b) )
+//
+// One TN kernel serves the forward, dgrad and wgrad products ("LLMQ: Efficient
+// Lower-Precision Pretraining for Consumer GPUs", section 2: low-precision
+// operands on the matrix units; section 4: larger models are dominated by
+// these products).  Both operands are contiguous along the reduction index.
+//
+// Design (CDNA4):
+//  - 256 x 256 output tile per workgroup, reduction step 128 bytes, 256 threads
+//    = 4 waves in a 2 x 2 grid, each wave 128 x 128 outputs held as 4 x 4
+//    blocks of v_mfma_f32_32x32x64_f8f6f4 accumulators (256 fp32 per lane).
+//    The operand formats (E4M3 / E5M2) are selected per operand by the
+//    instruction, so mixed E5M2 x E4M3 products run natively.
+//  - Operand tiles go global -> LDS with 16-byte direct-to-LDS loads
+//    (global_load_lds_dwordx4), two stages of 64 KB; tile k+2 is issued in the
+//    middle of step k, so each load has about one and a half steps to land.
+//  - Fragments are double-buffered in registers: the LDS reads of the next
+//    half-step overlap the matrix instructions of the current one.
+//  - LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
+//    c ^ f(r), f(r) = ((r >> 1) & 7) ^ ((r & 1) << 2), which keeps the 16-byte
+//    fragment reads of 8 or 16 consecutive rows on distinct banks.
+//  - The instruction's operands are swapped (B fragment first), so each lane
+//    ends with 4 consecutive output columns of one row and stores 8 bytes.
+//  - Workgroup ids are remapped so that consecutive tiles of the grouped
+//    raster order land on the same XCD (workgroups are dealt round-robin to
+//    the 8 XCDs, each with its own L2).
+//  - Deterministic: every output is reduced by one wave in a fixed order.
+#include "fp8_device.hpp"
+#include "fp8_internal.hpp"
+
+namespace fp8k {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBM = 256;
+constexpr int kBN = 256;
+constexpr int kBK = 128;
+constexpr int kStageA = kBM * kBK;            // 32 KB
+constexpr int kStageB = kBN * kBK;            // 32 KB
+constexpr int kStage = kStageA + kStageB;     // 64 KB
+constexpr int kLds = 2 * kStage;              // 128 KB
+constexpr int kGroupM = 8;                    // tile rows per raster group
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] at [15:14]); expcnt and lgkmcnt are left at their maxima.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitVm16 = 0x4F70;
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+// 16-byte direct-to-LDS load: lane L of the wave writes LDS bytes
+// [lds_base + 16 L, lds_base + 16 L + 16).  Issued as inline assembly so that
+// the compiler's LDS-DMA hazard tracking does not put a wait for every pending
+// load in front of each LDS read: the kernel orders these loads itself with an
+// explicit vmcnt wait and a barrier before the stage they fill is read.
+__device__ __forceinline__ void lds_load16(const uint8_t* g, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int chunk)
+{
+    const int p = chunk ^ swz(row);
+    const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * kBK + p * 16);
+    const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * kBK + (p ^ 1) * 16);
+    v8i r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+}
+
+// Global -> LDS sources of one workgroup: load ii (0..7) of wave w fills LDS rows
+// (w*8 + ii)*8 .. +8 of the A (B) stage; lane L writes row r = (w*8+ii)*8 + L/8
+// at physical chunk L%8, i.e. it reads logical chunk (L%8) ^ f(r).  f(r) depends
+// on ii only through ii & 1, so a lane needs two byte offsets per operand (even
+// and odd ii) plus the uniform row step 8 * ii * R.
+struct Sources {
+    const uint8_t* a;
+    const uint8_t* b;
+    uint32_t a_off[2];    // interior tiles: byte offset of the lane's first load
+    uint32_t b_off[2];
+    uint32_t step;        // 8 rows
+    int a_row, b_row;     // edge tiles: the lane's first row, and the last valid row
+    int a_last, b_last;
+    uint32_t chunk16[2];  // byte offset of the lane's chunk within a row (even / odd ii)
+    bool edge;
+};
+
+__device__ __forceinline__ void issue_stage(const Sources& src, uint32_t stage, int k0, int wave)
+{
+    if (!src.edge) {
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+            lds_load16(src.a + (src.a_off[ii & 1] + (uint32_t)ii * src.step + (uint32_t)k0),
+                       stage + (uint32_t)(wave * 8 + ii) * 1024u);
+            lds_load16(src.b + (src.b_off[ii & 1] + (uint32_t)ii * src.step + (uint32_t)k0),
+                       stage + (uint32_t)kStageA + (uint32_t)(wave * 8 + ii) * 1024u);
+        }
+    } else {
+        // rows past the edge re-read the last valid row; those outputs are never stored
+        const uint32_t R = src.step / 8u;
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+            const uint32_t ra = (uint32_t)min(src.a_row + ii * 8, src.a_last);
+            const uint32_t rb = (uint32_t)min(src.b_row + ii * 8, src.b_last);
+            lds_load16(src.a + (ra * R + src.chunk16[ii & 1] + (uint32_t)k0),
+                       stage + (uint32_t)(wave * 8 + ii) * 1024u);
+            lds_load16(src.b + (rb * R + src.chunk16[ii & 1] + (uint32_t)k0),
+                       stage + (uint32_t)kStageA + (uint32_t)(wave * 8 + ii) * 1024u);
+        }
+    }
+}
+
+struct Frags {
+    v8i a[4];
+    v8i b[4];
+};
+
+__device__ __forceinline__ void read_frags(Frags& f, const uint8_t* stage, int kk, int wm, int wn, int lane)
+{
+    const int fr = lane & 31;              // fragment row within a 32-row block
+    const int c = kk * 4 + (lane >> 5) * 2;  // first 16-byte chunk of the lane's 32 bytes
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = lds_frag(stage, wm * 128 + i * 32 + fr, c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[j] = lds_frag(stage + kStageA, wn * 128 + j * 32 + fr, c);
+}
+
+template <int FA, int FB>
+__device__ __forceinline__ void mma(v16f (&acc)[4][4], const Frags& f)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA,
+                                                                        0, 0, 0, 0);
+}
+
+// One reduction step on stage `cur` (holding tile kt).  On entry f0 holds the
+// first half-step fragments of tile kt.  The barrier sits between the two
+// half-steps: every wave has then read all of `cur` (so tile kt+2 may be issued
+// into it) and tile kt+1 has landed in `nxt` (so its first fragments are read
+// while the second half-step's matrix instructions run).  After the last tile
+// the read of `nxt` returns stale data that is never used.
+template <int FA, int FB>
+__device__ __forceinline__ void k_step(v16f (&acc)[4][4], Frags& f0, Frags& f1, const Sources& src,
+                                       const uint8_t* cur, uint32_t cur_addr, const uint8_t* nxt,
+                                       bool issue, int k_issue, int wave, int wm, int wn, int lane)
+{
+    read_frags(f1, cur, 1, wm, wn, lane);
+    mma<FA, FB>(acc, f0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);     // tile kt+1 has landed (this wave's loads)
+    __syncthreads();                          // ... for all waves; `cur` fully read
+    if (issue) issue_stage(src, cur_addr, k_issue, wave);
+    read_frags(f0, nxt, 0, wm, wn, lane);
+    mma<FA, FB>(acc, f1);
+}
+
+template <int FA, int FB>
+__global__ void __launch_bounds__(256, 1)
+gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+               const float* __restrict__ inv_a, const float* __restrict__ inv_b,
+               uint16_t* __restrict__ out, int P, int Q, int R, int tiles_m, int tiles_n)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+
+    // ---- tile assignment: XCD-aware remap, then grouped raster order
+    const int ntiles = tiles_m * tiles_n;
+    int wg = blockIdx.x;
+    {
+        const int per_xcd = ntiles / 8;
+        if (wg < per_xcd * 8) wg = (wg % 8) * per_xcd + wg / 8;
+    }
+    const int group_size = kGroupM * tiles_n;
+    const int group = wg / group_size;
+    const int first_m = group * kGroupM;
+    const int gm = min(tiles_m - first_m, kGroupM);
+    const int in_group = wg - group * group_size;
+    const int tile_m = first_m + in_group % gm;
+    const int tile_n = in_group / gm;
+    const int m0 = tile_m * kBM, n0 = tile_n * kBN;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+
+    Sources src;
+    src.a = A;
+    src.b = B;
+    src.a_row = m0 + wave * 64 + (lane >> 3);
+    src.b_row = n0 + wave * 64 + (lane >> 3);
+    src.a_last = P - 1;
+    src.b_last = Q - 1;
+    src.step = 8u * (uint32_t)R;
+    src.edge = (m0 + kBM > P) || (n0 + kBN > Q);
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        const int row = (wave * 8 + par) * 8 + (lane >> 3);     // row within the tile
+        src.chunk16[par] = (uint32_t)(((lane & 7) ^ swz(row)) * 16);
+        src.a_off[par] = (uint32_t)src.a_row * (uint32_t)R + src.chunk16[par];
+        src.b_off[par] = (uint32_t)src.b_row * (uint32_t)R + src.chunk16[par];
+    }
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    const int KT = R / kBK;
+    Frags f0, f1;
+    issue_stage(src, lds_addr, 0, wave);
+    if (KT > 1) {
+        issue_stage(src, lds_addr + kStage, kBK, wave);
+        __builtin_amdgcn_s_waitcnt(kWaitVm16);    // tile 0 landed, tile 1's 16 loads may be in flight
+    } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+    __syncthreads();
+    read_frags(f0, lds, 0, wm, wn, lane);
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        k_step<FA, FB>(acc, f0, f1, src, lds + cur * kStage, lds_addr + cur * kStage,
+                       lds + (cur ^ 1) * kStage, kt + 2 < KT, (kt + 2) * kBK, wave, wm, wn, lane);
+    }
+
+    // ---- epilogue: descale, round to bf16, store 4 consecutive columns per lane
+    const int fr = lane & 31;
+    const float d = inv_a[0] * inv_b[0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 128 + i * 32 + fr;
+        if (m >= P) continue;
+        uint16_t* orow = out + (size_t)m * Q;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * 128 + j * 32 + g * 8 + (lane >> 5) * 4;
+                if (n >= Q) continue;
+                const f32x2 v01 = {acc[i][j][4 * g] * d, acc[i][j][4 * g + 1] * d};
+                const f32x2 v23 = {acc[i][j][4 * g + 2] * d, acc[i][j][4 * g + 3] * d};
+                const bf16x2 b01 = __builtin_convertvector(v01, bf16x2);
+                const bf16x2 b23 = __builtin_convertvector(v23, bf16x2);
+                uint2 w;
+                w.x = __builtin_bit_cast(uint32_t, b01);
+                w.y = __builtin_bit_cast(uint32_t, b23);
+                *reinterpret_cast<uint2*>(orow + n) = w;
+            }
+        }
+    }
+}
+
+template <int FA, int FB>
+static hipError_t launch_fmt(const uint8_t* A, const uint8_t* B, const float* inv_a, const float* inv_b,
+                             void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream)
+{
+    const int tiles_m = (int)((P + kBM - 1) / kBM);
+    const int tiles_n = (int)((Q + kBN - 1) / kBN);
+    gemm_tn_kernel<FA, FB><<<tiles_m * tiles_n, 256, 0, stream>>>(
+        A, B, inv_a, inv_b, reinterpret_cast<uint16_t*>(out), (int)P, (int)Q, (int)R, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_tn(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* inv_a,
+                          const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream)
+{
+    if (fmt_a == 0 && fmt_b == 0) return launch_fmt<0, 0>(A, B, inv_a, inv_b, out, P, Q, R, stream);
+    if (fmt_a == 1 && fmt_b == 0) return launch_fmt<1, 0>(A, B, inv_a, inv_b, out, P, Q, R, stream);
+    if (fmt_a == 0 && fmt_b == 1) return launch_fmt<0, 1>(A, B, inv_a, inv_b, out, P, Q, R, stream);
+    return launch_fmt<1, 1>(A, B, inv_a, inv_b, out, P, Q, R, stream);
+}
+
+}  // namespace fp8k

@@ -1,0 +1,204 @@
+// quant.hip -- absmax reduction and per-tensor FP8 quantisation for gfx950.
+//
+// Dynamic tensor-level scaling ("LLMQ: Efficient Lower-Precision Pretraining
+// for Consumer GPUs", section 1; FastML report, FP8 training without delayed
+// scaling): the scale of every tensor is derived from its own current absmax.
+//
+// All kernels here are HBM-bound streaming kernels:
+//   absmax      reads 2 B per element
+//   quantize    reads 2 B, writes 1 B per element (+1 B with the transposed copy)
+// They move data in 16-byte vectors, each wave instruction covering a
+// contiguous 1 KB (loads) or 512 B (stores).
+#include "fp8_device.hpp"
+#include "fp8_internal.hpp"
+
+namespace fp8k {
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ us2 as_us2(uint32_t w) { return __builtin_bit_cast(us2, w); }
+
+// |bf16| max of the 8 elements of a 16-byte word, accumulated as two packed
+// 16-bit lanes (v_pk_max_u16 on the magnitude bits).
+__device__ __forceinline__ us2 absmax_acc(us2 m, uint4 v)
+{
+    m = __builtin_elementwise_max(m, as_us2(v.x & 0x7FFF7FFFu));
+    m = __builtin_elementwise_max(m, as_us2(v.y & 0x7FFF7FFFu));
+    m = __builtin_elementwise_max(m, as_us2(v.z & 0x7FFF7FFFu));
+    m = __builtin_elementwise_max(m, as_us2(v.w & 0x7FFF7FFFu));
+    return m;
+}
+
+__global__ void __launch_bounds__(64) zero_u32_kernel(uint32_t* p)
+{
+    if (threadIdx.x == 0) *p = 0u;
+}
+
+// One pass over x; each block folds its maximum into *out with one atomicMax on
+// the fp32 bit pattern (for non-negative values the unsigned order of the bits
+// is the numeric order, and NaN patterns sort above infinity).
+__global__ void __launch_bounds__(256) absmax_bf16_kernel(const uint4* __restrict__ x, int64_t nvec,
+                                                          const uint16_t* __restrict__ tail, int ntail,
+                                                          uint32_t* __restrict__ out)
+{
+    us2 m = {0, 0};
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 3 * stride < nvec; i += 4 * stride) {
+        uint4 a = x[i], b = x[i + stride], c = x[i + 2 * stride], d = x[i + 3 * stride];
+        m = absmax_acc(m, a);
+        m = absmax_acc(m, b);
+        m = absmax_acc(m, c);
+        m = absmax_acc(m, d);
+    }
+    for (; i < nvec; i += stride) m = absmax_acc(m, x[i]);
+    uint32_t r = m.x > m.y ? m.x : m.y;
+    if (blockIdx.x == 0 && (int)threadIdx.x < ntail) {
+        uint32_t t = tail[threadIdx.x] & 0x7FFFu;
+        r = r > t ? r : t;
+    }
+    block_max_to_global(r << 16, out);
+}
+
+hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, hipStream_t stream)
+{
+    const int64_t nvec = n / 8;
+    const int ntail = (int)(n - nvec * 8);
+    int64_t blocks = (nvec + 255) / 256;
+    const int64_t cap = (int64_t)device_cu_count() * 8;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    zero_u32_kernel<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax));
+    absmax_bf16_kernel<<<(unsigned)blocks, 256, 0, stream>>>(
+        reinterpret_cast<const uint4*>(x), nvec,
+        reinterpret_cast<const uint16_t*>(x) + nvec * 8, ntail, reinterpret_cast<uint32_t*>(absmax));
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Quantisation without a transposed copy.  A wave tile is 1024 consecutive
+// elements (128 16-byte vectors): lane l converts vectors l and l + 64, so
+// every load instruction reads 1 KB and every store writes 512 B contiguously.
+template <int FMT>
+__global__ void __launch_bounds__(256) quantize_flat_kernel(const uint4* __restrict__ x, int64_t nvec,
+                                                            const float* __restrict__ absmax,
+                                                            uint2* __restrict__ q,
+                                                            float* __restrict__ scale_out,
+                                                            float* __restrict__ inv_out)
+{
+    float s, inv;
+    tensor_scale(*absmax, Fmt<FMT>::max, s, inv);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (scale_out) *scale_out = s;
+        if (inv_out) *inv_out = inv;
+    }
+    const int lane = threadIdx.x & 63;
+    const int64_t ntiles = (nvec + 127) / 128;
+    const int64_t wstride = (int64_t)gridDim.x * 4;
+    for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < ntiles; t += 2 * wstride) {
+        const int64_t t2 = t + wstride;
+        const int64_t v0 = t * 128 + lane, v1 = v0 + 64;
+        const int64_t v2 = t2 * 128 + lane, v3 = v2 + 64;
+        uint4 a = {0, 0, 0, 0}, b = a, c = a, d = a;
+        if (v0 < nvec) a = x[v0];
+        if (v1 < nvec) b = x[v1];
+        if (t2 < ntiles) {
+            if (v2 < nvec) c = x[v2];
+            if (v3 < nvec) d = x[v3];
+        }
+        if (v0 < nvec) q[v0] = quant8<FMT>(a, s);
+        if (v1 < nvec) q[v1] = quant8<FMT>(b, s);
+        if (t2 < ntiles) {
+            if (v2 < nvec) q[v2] = quant8<FMT>(c, s);
+            if (v3 < nvec) q[v3] = quant8<FMT>(d, s);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Quantisation with the transposed copy (and optionally the plain one).  A wave
+// owns a 16-row x 512-column tile: lane l reads the 16-byte vector at columns
+// 8l..8l+7 of each of the 16 rows (1 KB per load instruction), converts them,
+// writes its 8 codes per row to q, transposes the 16 x 8 code block in
+// registers (v_perm_b32) and writes 16 consecutive codes (one 16-byte store) to
+// each of its 8 rows of qt.  A block stacks 4 waves on consecutive row groups,
+// so a 64-byte segment of every qt row is written by one block.
+template <int FMT>
+__global__ void __launch_bounds__(256) quantize_t_kernel(const uint8_t* __restrict__ x, int64_t rows,
+                                                         int64_t cols, const float* __restrict__ absmax,
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ qt,
+                                                         float* __restrict__ scale_out,
+                                                         float* __restrict__ inv_out)
+{
+    float s, inv;
+    tensor_scale(*absmax, Fmt<FMT>::max, s, inv);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        if (scale_out) *scale_out = s;
+        if (inv_out) *inv_out = inv;
+    }
+    const int lane = threadIdx.x & 63;
+    const int64_t i0 = ((int64_t)blockIdx.y * 4 + (threadIdx.x >> 6)) * 16;
+    const int64_t j = (int64_t)blockIdx.x * 512 + lane * 8;
+    if (i0 >= rows || j >= cols) return;
+
+    uint4 v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        v[r] = *reinterpret_cast<const uint4*>(x + ((i0 + r) * cols + j) * 2);
+    uint32_t lo[16], hi[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        uint2 c = quant8<FMT>(v[r], s);
+        lo[r] = c.x;
+        hi[r] = c.y;
+    }
+    if (q) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            *reinterpret_cast<uint2*>(q + (i0 + r) * cols + j) = make_uint2(lo[r], hi[r]);
+    }
+    if (qt) {
+        uint32_t w[8][4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            transpose4x4(lo[4 * g], lo[4 * g + 1], lo[4 * g + 2], lo[4 * g + 3],
+                         w[0][g], w[1][g], w[2][g], w[3][g]);
+            transpose4x4(hi[4 * g], hi[4 * g + 1], hi[4 * g + 2], hi[4 * g + 3],
+                         w[4][g], w[5][g], w[6][g], w[7][g]);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            *reinterpret_cast<uint4*>(qt + (j + k) * rows + i0) = make_uint4(w[k][0], w[k][1], w[k][2], w[k][3]);
+    }
+}
+
+template <int FMT>
+static void launch_quantize_fmt(const void* x, int64_t rows, int64_t cols, const float* absmax,
+                                uint8_t* q, uint8_t* qt, float* scale, float* inv_scale,
+                                hipStream_t stream)
+{
+    if (qt) {
+        dim3 grid((unsigned)((cols + 511) / 512), (unsigned)((rows + 63) / 64));
+        quantize_t_kernel<FMT><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(x), rows, cols,
+                                                         absmax, q, qt, scale, inv_scale);
+    } else {
+        const int64_t nvec = rows * cols / 8;
+        const int64_t ntiles = (nvec + 127) / 128;
+        int64_t blocks = (ntiles + 7) / 8;          // two wave tiles per wave per pass
+        const int64_t cap = (int64_t)device_cu_count() * 8;
+        if (blocks > cap) blocks = cap;
+        if (blocks < 1) blocks = 1;
+        quantize_flat_kernel<FMT><<<(unsigned)blocks, 256, 0, stream>>>(
+            reinterpret_cast<const uint4*>(x), nvec, absmax, reinterpret_cast<uint2*>(q), scale, inv_scale);
+    }
+}
+
+hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, const float* absmax,
+                           uint8_t* q, uint8_t* qt, float* scale, float* inv_scale, hipStream_t stream)
+{
+    if (fmt == 0) launch_quantize_fmt<0>(x, rows, cols, absmax, q, qt, scale, inv_scale, stream);
+    else launch_quantize_fmt<1>(x, rows, cols, absmax, q, qt, scale, inv_scale, stream);
+    return hipGetLastError();
+}
+
+}  // namespace fp8k

@@ -1,0 +1,278 @@
+// swiglu.hip -- SwiGLU fused with its E4M3 requantisation, for gfx950.
+//
+// "LLMQ: Efficient Lower-Precision Pretraining for Consumer GPUs", section 3.1:
+// the block input and the absmax statistics are retained, so during
+// recomputation the quantisation fuses with the nonlinearity and no second
+// global reduction is needed.
+//
+// h = RN32(s_g * u), s_g = RN32(g / RN32(1 + RN32(e^-g))) with e^-g correctly
+// rounded.  g is a bf16 value, so s_g is a function of 16 bits.  It is read
+// from a table for the bf16 exponents where it is non-trivial and given by
+// exact rules elsewhere:
+//   |g| < 2^(E_LO-127): e^-g rounds into [1 - 2^-24, 1 + 2^-23], 1 + E rounds
+//                       to exactly 2, so s_g = RN32(g / 2) = RN32(g * 0.5);
+//   |g| >= 2^(E_HI-126), g > 0 (and +inf, NaN): e^-g < 2^-24, 1 + E = 1, s_g = g;
+//   same range, g < 0: e^-g overflows to +inf, s_g = g / inf = -0; -inf and
+//                       NaN give NaN.
+// The table (2 signs x 34 exponents x 128 mantissas, 34 KB) is built once per
+// device by a kernel that evaluates each entry in binary64 and rounds every
+// step to binary32 in the order above; kernels copy it into LDS.
+#include <mutex>
+#include "fp8_device.hpp"
+#include "fp8_internal.hpp"
+
+namespace fp8k {
+
+constexpr int kELo = 100;                     // bf16 biased exponent range of the table
+constexpr int kEHi = 133;                     // |g| in [2^-27, 128)
+constexpr int kNE = kEHi - kELo + 1;          // 34
+constexpr int kHalf = kNE * 128;              // entries per sign
+constexpr int kTable = 2 * kHalf;             // 8704 entries
+
+__device__ float g_silu_table[kTable];
+
+__global__ void __launch_bounds__(256) silu_table_init_kernel()
+{
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= kTable) return;
+    const uint32_t sign = idx >= kHalf ? 1u : 0u;
+    const uint32_t rem = idx - sign * kHalf;
+    const uint32_t bits = (sign << 15) | ((uint32_t)(kELo + rem / 128) << 7) | (rem % 128);
+    const float g = __uint_as_float(bits << 16);
+    const float E = (float)exp(-(double)g);
+    const float t = 1.0f + E;
+    g_silu_table[idx] = (float)((double)g / (double)t);
+}
+
+static std::mutex g_init_mu;
+static bool g_init_done[64];
+
+// Builds the table on the current device the first time it is needed.  The host
+// waits for it once, so later calls on any stream see a complete table.
+static hipError_t ensure_silu_table(hipStream_t stream)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_init_mu);
+    if (g_init_done[dev]) return hipSuccess;
+    silu_table_init_kernel<<<(kTable + 255) / 256, 256, 0, stream>>>();
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return e;
+    g_init_done[dev] = true;
+    return hipSuccess;
+}
+
+__device__ __forceinline__ void load_table_to_lds(float* lds)
+{
+    const float4* src = reinterpret_cast<const float4*>(g_silu_table);
+    float4* dst = reinterpret_cast<float4*>(lds);
+    for (int i = threadIdx.x; i < kTable / 4; i += blockDim.x) dst[i] = src[i];
+    __syncthreads();
+}
+
+// s_g for one bf16 gate value (16-bit pattern b, fp32 value g).
+__device__ __forceinline__ float silu_of(const float* tbl, uint32_t b, float g)
+{
+    const uint32_t t = (b & 0x7FFFu) - (uint32_t)(kELo * 128);
+    const uint32_t neg = b >> 15;
+    const bool in_table = t < (uint32_t)kHalf;
+    const float tv = tbl[in_table ? t + neg * kHalf : 0u];
+    if (in_table) return tv;
+    if ((int32_t)t < 0) return g * 0.5f;                     // tiny |g|
+    if (!neg) return g;                                      // large g, +inf, +NaN
+    return ((b & 0x7F80u) == 0x7F80u) ? __builtin_nanf("") : -0.0f;
+}
+
+// h for the 8 (gate, up) pairs of two 16-byte words.
+__device__ __forceinline__ void swiglu8(const float* tbl, uint4 gw, uint4 uw, float h[8])
+{
+    const uint32_t g32[4] = {gw.x, gw.y, gw.z, gw.w};
+    const uint32_t u32[4] = {uw.x, uw.y, uw.z, uw.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float g0 = bf16_lo(g32[k]), g1 = bf16_hi(g32[k]);
+        h[2 * k] = silu_of(tbl, g32[k] & 0xFFFFu, g0) * bf16_lo(u32[k]);
+        h[2 * k + 1] = silu_of(tbl, g32[k] >> 16, g1) * bf16_hi(u32[k]);
+    }
+}
+
+__device__ __forceinline__ uint32_t mag_max8(uint32_t m, const float h[8])
+{
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t a = __float_as_uint(h[k]) & 0x7FFFFFFFu;
+        m = m > a ? m : a;
+    }
+    return m;
+}
+
+__device__ __forceinline__ uint2 quant8_h(const float h[8], float s)
+{
+    uint2 r;
+    r.x = enc4<0>(h[0] * s, h[1] * s, h[2] * s, h[3] * s);
+    r.y = enc4<0>(h[4] * s, h[5] * s, h[6] * s, h[7] * s);
+    return r;
+}
+
+// Work decomposition of the row-streaming kernels: a wave item is one row and
+// 1024 consecutive columns j; lane l handles columns 8l..8l+7 and
+// 512+8l..512+8l+7 of the item (one 16-byte load per half row and operand).
+struct RowItems {
+    int64_t chunks;     // items per row
+    int64_t total;      // items in the tensor
+};
+
+__device__ __forceinline__ RowItems row_items(int64_t M, int64_t F)
+{
+    RowItems r;
+    r.chunks = (F + 1023) / 1024;
+    r.total = M * r.chunks;
+    return r;
+}
+
+// Forward pass 1: absmax of h over the whole [M, F] output (no output written).
+__global__ void __launch_bounds__(256) swiglu_absmax_kernel(const uint16_t* __restrict__ gu, int64_t M,
+                                                            int64_t F, uint32_t* __restrict__ out)
+{
+    __shared__ float tbl[kTable];
+    load_table_to_lds(tbl);
+    const RowItems it = row_items(M, F);
+    const int lane = threadIdx.x & 63;
+    uint32_t m = 0;
+    for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < it.total; w += (int64_t)gridDim.x * 4) {
+        const int64_t i = w / it.chunks;
+        const int64_t jb = (w - i * it.chunks) * 1024 + lane * 8;
+        const uint16_t* grow = gu + i * 2 * F;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int64_t j = jb + half * 512;
+            if (j < F) {
+                const uint4 gw = *reinterpret_cast<const uint4*>(grow + j);
+                const uint4 uw = *reinterpret_cast<const uint4*>(grow + F + j);
+                float h[8];
+                swiglu8(tbl, gw, uw, h);
+                m = mag_max8(m, h);
+            }
+        }
+    }
+    block_max_to_global(m, out);
+}
+
+// Pass 2 (forward) or the only pass (recomputation): hq = e4m3(RN32(h * s_h)).
+__global__ void __launch_bounds__(256) swiglu_quant_kernel(const uint16_t* __restrict__ gu, int64_t M,
+                                                           int64_t F, const float* __restrict__ absmax_h,
+                                                           uint8_t* __restrict__ hq,
+                                                           float* __restrict__ inv_out)
+{
+    __shared__ float tbl[kTable];
+    float s, inv;
+    tensor_scale(*absmax_h, kMaxE4M3, s, inv);
+    if (blockIdx.x == 0 && threadIdx.x == 0 && inv_out) *inv_out = inv;
+    load_table_to_lds(tbl);
+    const RowItems it = row_items(M, F);
+    const int lane = threadIdx.x & 63;
+    for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < it.total; w += (int64_t)gridDim.x * 4) {
+        const int64_t i = w / it.chunks;
+        const int64_t jb = (w - i * it.chunks) * 1024 + lane * 8;
+        const uint16_t* grow = gu + i * 2 * F;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int64_t j = jb + half * 512;
+            if (j < F) {
+                const uint4 gw = *reinterpret_cast<const uint4*>(grow + j);
+                const uint4 uw = *reinterpret_cast<const uint4*>(grow + F + j);
+                float h[8];
+                swiglu8(tbl, gw, uw, h);
+                *reinterpret_cast<uint2*>(hq + i * F + j) = quant8_h(h, s);
+            }
+        }
+    }
+}
+
+// Requantisation with the transposed copy hqt [F, M] (and optionally hq): a wave
+// owns 16 rows x 512 columns, lane l columns 8l..8l+7 of each row, as in the
+// transposing quantise kernel.  Blocks are persistent and walk 64-row x
+// 512-column tiles, so the table is copied into LDS once per block.
+__global__ void __launch_bounds__(256) swiglu_quant_t_kernel(const uint16_t* __restrict__ gu, int64_t M,
+                                                             int64_t F, const float* __restrict__ absmax_h,
+                                                             uint8_t* __restrict__ hq, uint8_t* __restrict__ hqt,
+                                                             float* __restrict__ inv_out)
+{
+    __shared__ float tbl[kTable];
+    float s, inv;
+    tensor_scale(*absmax_h, kMaxE4M3, s, inv);
+    if (blockIdx.x == 0 && threadIdx.x == 0 && inv_out) *inv_out = inv;
+    load_table_to_lds(tbl);
+    const int lane = threadIdx.x & 63;
+    const int64_t tiles_j = (F + 511) / 512;
+    const int64_t tiles = tiles_j * ((M + 63) / 64);
+    for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const int64_t ti = tile / tiles_j;
+        const int64_t i0 = (ti * 4 + (threadIdx.x >> 6)) * 16;
+        const int64_t j = (tile - ti * tiles_j) * 512 + lane * 8;
+        if (i0 >= M || j >= F) continue;
+
+        uint32_t lo[16], hi[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint16_t* grow = gu + (i0 + r) * 2 * F;
+            const uint4 gw = *reinterpret_cast<const uint4*>(grow + j);
+            const uint4 uw = *reinterpret_cast<const uint4*>(grow + F + j);
+            float h[8];
+            swiglu8(tbl, gw, uw, h);
+            const uint2 c = quant8_h(h, s);
+            lo[r] = c.x;
+            hi[r] = c.y;
+        }
+        if (hq) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                *reinterpret_cast<uint2*>(hq + (i0 + r) * F + j) = make_uint2(lo[r], hi[r]);
+        }
+        uint32_t w[8][4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            transpose4x4(lo[4 * g], lo[4 * g + 1], lo[4 * g + 2], lo[4 * g + 3], w[0][g], w[1][g], w[2][g], w[3][g]);
+            transpose4x4(hi[4 * g], hi[4 * g + 1], hi[4 * g + 2], hi[4 * g + 3], w[4][g], w[5][g], w[6][g], w[7][g]);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            *reinterpret_cast<uint4*>(hqt + (j + k) * M + i0) = make_uint4(w[k][0], w[k][1], w[k][2], w[k][3]);
+    }
+}
+
+__global__ void __launch_bounds__(64) zero_u32_kernel_sw(uint32_t* p)
+{
+    if (threadIdx.x == 0) *p = 0u;
+}
+
+hipError_t launch_swiglu_requant(const void* gu, int64_t M, int64_t F, float* absmax_h, int compute_absmax,
+                                 uint8_t* hq, uint8_t* hqt, float* inv_scale_h, hipStream_t stream)
+{
+    hipError_t e = ensure_silu_table(stream);
+    if (e != hipSuccess) return e;
+    const uint16_t* g = reinterpret_cast<const uint16_t*>(gu);
+    const int64_t items = M * ((F + 1023) / 1024);
+    int64_t blocks = (items + 3) / 4;
+    const int64_t cap = (int64_t)device_cu_count() * 4;   // 34 KB LDS per block: 4 blocks per CU
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    if (compute_absmax) {
+        zero_u32_kernel_sw<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax_h));
+        swiglu_absmax_kernel<<<(unsigned)blocks, 256, 0, stream>>>(g, M, F, reinterpret_cast<uint32_t*>(absmax_h));
+    }
+    if (hqt) {
+        int64_t tblocks = ((F + 511) / 512) * ((M + 63) / 64);
+        if (tblocks > cap) tblocks = cap;
+        swiglu_quant_t_kernel<<<(unsigned)tblocks, 256, 0, stream>>>(g, M, F, absmax_h, hq, hqt, inv_scale_h);
+    } else {
+        swiglu_quant_kernel<<<(unsigned)blocks, 256, 0, stream>>>(g, M, F, absmax_h, hq, inv_scale_h);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fp8k

@@ -1,0 +1,161 @@
+/*
+ * fp8_precision.h -- C ABI of the MI355X (gfx950) FP8 training hot path.
+ *
+ * The operations are those of an 8-bit training pipeline with dynamic,
+ * per-tensor ("just-in-time") absmax scaling:
+ *
+ *   absmax -> scale = fp8_max / absmax -> round-to-nearest-even saturating
+ *   quantisation to OCP E4M3 (activations, weights) or E5M2 (output
+ *   gradients) -> FP8 GEMMs (forward, dgrad, wgrad) with fp32 accumulation and
+ *   a per-tensor descale to bf16; plus the SwiGLU nonlinearity fused with its
+ *   requantisation, reusing a retained absmax during recomputation.
+ *
+ * Sources: "LLMQ: Efficient Lower-Precision Pretraining for Consumer GPUs"
+ * (paperlayer.ai summary of arXiv 2512.15306), sections 1, 3.1, 4 and 5 /
+ * Figure 2; "FastML periodic report" (EU CORDIS), the item on FP8 training
+ * without delayed scaling.  The bit formats are those of the OCP 8-bit
+ * floating point specification (OFP8).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every pointer argument is a DEVICE pointer owned by the caller.  The
+ *    library allocates no device memory for any call, keeps no reference
+ *    after the call returns, and never synchronises the host.
+ *  - All work is enqueued on `stream` (0 = the null stream).  Inputs must stay
+ *    valid until the stream reaches the work.
+ *  - absmax, scale and inverse-scale values stay in device memory as fp32
+ *    scalars; they are passed by pointer, never copied to the host.
+ *  - bf16 tensors are raw 16-bit patterns, row-major; FP8 tensors are bytes,
+ *    row-major, in the format named by the call.
+ *  - Every tensor pointer must be 16-byte aligned.  fp32 scalar pointers must
+ *    be 4-byte aligned.
+ *  - Return value: FP8_OK, or an error code; on error nothing was enqueued
+ *    (except FP8_ERR_HIP, reported after a launch failed).  Arguments are
+ *    checked on the host before anything is launched.  fp8_last_error()
+ *    gives a message for the calling thread's last failure.
+ *  - Calls are thread-safe.  The device a pointer lives on must be the
+ *    current HIP device.
+ *  - NaN inputs give NaN codes (0x7F or 0xFF); which sign a NaN code carries
+ *    is not specified.  Infinite inputs saturate to +-max.
+ */
+#ifndef FP8_PRECISION_H
+#define FP8_PRECISION_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8_status {
+    FP8_OK = 0,
+    FP8_ERR_INVALID = 1,      /* null pointer, size <= 0, overlapping in/out, bad enum */
+    FP8_ERR_UNSUPPORTED = 2,  /* misaligned pointer or a dimension outside the kernel's constraints */
+    FP8_ERR_HIP = 3           /* the HIP runtime reported an error at launch */
+} fp8_status;
+
+/* OCP OFP8 formats.  E4M3: bias 7, no infinity, NaN S.1111.111, max 448.
+ * E5M2: bias 15, infinity S.11111.00, max 57344. */
+typedef enum fp8_fmt { FP8_E4M3 = 0, FP8_E5M2 = 1 } fp8_fmt;
+
+/* Static text for a status code. */
+const char* fp8_status_string(fp8_status s);
+
+/* Detail message of the calling thread's most recent failed call ("" if none). */
+const char* fp8_last_error(void);
+
+/*
+ * absmax of a bf16 tensor: *absmax = max over i < n of |x[i]| (fp32, exact).
+ * This is the per-tensor statistic of dynamic tensor-level scaling (LLMQ
+ * summary, section 1; FastML report: the scale is taken just in time from
+ * the current tensor, not from a history).  A NaN anywhere gives a NaN, an
+ * infinity gives +inf.  The result does not depend on launch order.
+ *
+ *   x       bf16 [n], 16-byte aligned
+ *   n       number of elements, n >= 1
+ *   absmax  one fp32 in device memory (written)
+ */
+fp8_status fp8_absmax(const void* x, int64_t n, float* absmax, hipStream_t stream);
+
+/*
+ * Quantise a bf16 [rows, cols] tensor with the scale of its absmax:
+ *   s      = fp8_max / absmax  (one fp32 division; 1 when absmax == 0; held at
+ *            FLT_MAX if the division overflows)
+ *   q[i,j] = encode_fmt(RN32(x[i,j] * s))   round to nearest even, saturating
+ * and optionally its transposed copy qt[j,i] = q[i,j], the operand layout the
+ * backward GEMMs read (LLMQ summary, section 4: backward-pass transposes and
+ * the extra transpose/quantisation buffers of FP8).
+ *
+ *   x          bf16 [rows, cols]
+ *   fmt        FP8_E4M3 or FP8_E5M2 (gradients: LLMQ summary, section 5 / Fig. 2)
+ *   absmax     fp32 scalar: fresh from fp8_absmax or a retained statistic
+ *   q          u8 [rows, cols] or NULL
+ *   qt         u8 [cols, rows] or NULL (at least one of q, qt)
+ *   scale      fp32 scalar out (s) or NULL
+ *   inv_scale  fp32 scalar out (RN32(1 / s)), the GEMM descale factor, or NULL
+ * Constraints: cols % 16 == 0; if qt is given, rows % 16 == 0 as well.
+ */
+fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt,
+                        const float* absmax, uint8_t* q, uint8_t* qt,
+                        float* scale, float* inv_scale, hipStream_t stream);
+
+/*
+ * SwiGLU fused with its E4M3 requantisation.  gu = [gate | up] is the bf16
+ * [M, 2F] output of the gate/up GEMM; for i < M, j < F
+ *   g = gu[i, j], u = gu[i, F + j]
+ *   h = RN32(RN32(g / RN32(1 + RN32(e^-g))) * u)       (silu(g) * u, fp32)
+ *   hq[i, j] = encode_e4m3(RN32(h * s_h)),  s_h = 448 / absmax_h
+ * compute_absmax = 1 (forward): absmax_h = max |h| is computed and written.
+ * compute_absmax = 0 (recomputation): *absmax_h is the retained statistic and
+ * is only read; no global reduction runs, and the bytes equal the forward's
+ * for the same gu (LLMQ summary, section 3.1: keeping absmax statistics
+ * avoids another global reduction and lets quantisation fuse with the
+ * nonlinearity during recomputation).
+ *
+ *   gu           bf16 [M, 2F]
+ *   absmax_h     fp32 scalar (written when compute_absmax = 1, read otherwise)
+ *   hq           u8 [M, F] or NULL
+ *   hqt          u8 [F, M] (transpose of hq) or NULL (at least one of hq, hqt)
+ *   inv_scale_h  fp32 scalar out (RN32(1 / s_h)) or NULL
+ * Constraints: F % 16 == 0; if hqt is given, M % 16 == 0.
+ */
+fp8_status fp8_swiglu_requant(const void* gu, int64_t M, int64_t F, float* absmax_h,
+                              int compute_absmax, uint8_t* hq, uint8_t* hqt,
+                              float* inv_scale_h, hipStream_t stream);
+
+/*
+ * FP8 GEMMs with fp32 accumulation and per-tensor descale (LLMQ summary,
+ * section 2: low-precision matrix products on the matrix units; section 4:
+ * large models are dominated by these products).  Every call computes
+ *   out[p, q] = bf16_RNE( RN32( (sum over r of dec(A[p, r]) * dec(B[q, r]))
+ *                               * RN32(inv_a * inv_b) ) )
+ * with both operands contiguous along the reduction index r, fp32
+ * accumulation (each FP8 product is exact in fp32) and the output written
+ * (never accumulated into).  The order of the fp32 sum is not specified, but
+ * a given shape always produces the same bytes (no atomics).
+ *
+ * fp8_gemm_fwd:   Y[M, N]  = X[M, K] . W[N, K]^T      A = xq  (e4m3) [M, K], B = wq  (e4m3) [N, K]
+ * fp8_gemm_dgrad: dX[M, K] = dY[M, N] . W[N, K]       A = dyq (dy_fmt) [M, N], B = wqt (e4m3) [K, N]
+ * fp8_gemm_wgrad: dW[N, K] = dY[M, N]^T . X[M, K]     A = dyqt (dy_fmt) [N, M], B = xqt (e4m3) [K, M]
+ *
+ *   inv_*   fp32 scalars: the inverse scales written by fp8_quantize /
+ *           fp8_swiglu_requant for the two operands
+ *   dy_fmt  FP8_E5M2 (default reading of the pages) or FP8_E4M3
+ * Constraints: every dimension >= 16 and a multiple of 16; the reduction
+ * length (K, N and M respectively) a multiple of 128.
+ */
+fp8_status fp8_gemm_fwd(const uint8_t* xq, const uint8_t* wq, const float* inv_sx,
+                        const float* inv_sw, void* y, int64_t M, int64_t N, int64_t K,
+                        hipStream_t stream);
+fp8_status fp8_gemm_dgrad(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_t* wqt,
+                          const float* inv_sdy, const float* inv_sw, void* dx,
+                          int64_t M, int64_t N, int64_t K, hipStream_t stream);
+fp8_status fp8_gemm_wgrad(const uint8_t* dyqt, fp8_fmt dy_fmt, const uint8_t* xqt,
+                          const float* inv_sdy, const float* inv_sx, void* dw,
+                          int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8_PRECISION_H */

@@ -1,0 +1,141 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects invalid arguments with the documented status codes before
+touching the GPU (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8_precision.h")
+LIB = os.path.join(ROOT, "fp8_precision_amd", "libfp8_precision.so")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:fp8_status|const char\*)\s+(fp8_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} not built: run `python -m fp8_precision_amd.build`")
+    lib = ctypes.CDLL(LIB)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.fp8_absmax.argtypes = [vp, i64, vp, vp]
+    lib.fp8_quantize.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+    lib.fp8_swiglu_requant.argtypes = [vp, i64, i64, vp, i32, vp, vp, vp, vp]
+    lib.fp8_gemm_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.fp8_gemm_dgrad.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.fp8_gemm_wgrad.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.fp8_last_error.restype = ctypes.c_char_p
+    lib.fp8_status_string.restype = ctypes.c_char_p
+    for f in ("fp8_absmax", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd", "fp8_gemm_dgrad",
+              "fp8_gemm_wgrad"):
+        getattr(lib, f).restype = i32
+    return lib
+
+
+def test_header_declares_the_hot_path():
+    names = declared_functions()
+    for want in ("fp8_absmax", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd", "fp8_gemm_dgrad",
+                 "fp8_gemm_wgrad", "fp8_status_string", "fp8_last_error"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in range(4):
+        assert lib.fp8_status_string(s)
+    assert b"unknown" in lib.fp8_status_string(99)
+
+
+# Fake but well-aligned device addresses: validation rejects the call before any
+# HIP call, so they are never dereferenced.
+A16 = 0x10000000
+B16 = 0x20000000
+C16 = 0x30000000
+D16 = 0x40000000
+E16 = 0x50000000
+
+
+def test_absmax_validation(lib):
+    assert lib.fp8_absmax(None, 16, C16, None) == INVALID
+    assert lib.fp8_absmax(A16, 16, None, None) == INVALID
+    assert lib.fp8_absmax(A16, 0, C16, None) == INVALID          # empty input
+    assert lib.fp8_absmax(A16, -5, C16, None) == INVALID
+    assert lib.fp8_absmax(A16, 16, A16 + 8, None) == INVALID     # output inside x
+    assert b"overlaps" in lib.fp8_last_error()
+    assert lib.fp8_absmax(A16 + 2, 16, C16, None) == UNSUPPORTED  # misaligned x
+    assert lib.fp8_absmax(A16, 16, C16 + 1, None) == UNSUPPORTED
+
+
+def test_quantize_validation(lib):
+    q = lib.fp8_quantize
+    assert q(None, 16, 16, 0, C16, B16, None, None, None, None) == INVALID
+    assert q(A16, 16, 16, 0, None, B16, None, None, None, None) == INVALID
+    assert q(A16, 16, 16, 0, C16, None, None, None, None, None) == INVALID     # no output
+    assert q(A16, 16, 16, 2, C16, B16, None, None, None, None) == INVALID      # bad format
+    assert q(A16, 0, 16, 0, C16, B16, None, None, None, None) == INVALID       # empty
+    assert q(A16, 16, 0, 0, C16, B16, None, None, None, None) == INVALID
+    assert q(A16, 16, 16, 0, C16, A16 + 64, None, None, None, None) == INVALID  # q inside x
+    assert q(A16, 16, 16, 0, C16, B16, B16 + 128, None, None, None) == INVALID  # q and qt overlap
+    assert q(A16, 16, 24, 0, C16, B16, None, None, None, None) == UNSUPPORTED  # cols % 16
+    assert q(A16, 8, 16, 0, C16, None, D16, None, None, None) == UNSUPPORTED   # rows % 16 with qt
+    assert q(A16, 16, 16, 0, C16, B16 + 8, None, None, None, None) == UNSUPPORTED  # misaligned q
+    assert q(A16, 16, 16, 1, C16, B16, None, E16 + 2, None, None) == UNSUPPORTED   # misaligned scale
+
+
+def test_swiglu_validation(lib):
+    s = lib.fp8_swiglu_requant
+    assert s(None, 16, 16, C16, 1, B16, None, None, None) == INVALID
+    assert s(A16, 16, 16, None, 1, B16, None, None, None) == INVALID
+    assert s(A16, 16, 16, C16, 1, None, None, None, None) == INVALID
+    assert s(A16, 16, 16, C16, 2, B16, None, None, None) == INVALID
+    assert s(A16, 0, 16, C16, 1, B16, None, None, None) == INVALID
+    assert s(A16, 16, 0, C16, 1, B16, None, None, None) == INVALID
+    assert s(A16, 16, 16, A16 + 4, 1, B16, None, None, None) == INVALID       # absmax inside gu
+    assert s(A16, 16, 24, C16, 1, B16, None, None, None) == UNSUPPORTED       # F % 16
+    assert s(A16, 8, 16, C16, 0, None, D16, None, None) == UNSUPPORTED        # M % 16 with hqt
+
+
+@pytest.mark.parametrize("entry", ["fwd", "dgrad", "wgrad"])
+def test_gemm_validation(lib, entry):
+    if entry == "fwd":
+        call = lambda a, b, ia, ib, out, M, N, K: lib.fp8_gemm_fwd(a, b, ia, ib, out, M, N, K, None)
+    elif entry == "dgrad":
+        call = lambda a, b, ia, ib, out, M, N, K: lib.fp8_gemm_dgrad(a, 1, b, ia, ib, out, M, N, K, None)
+    else:
+        call = lambda a, b, ia, ib, out, M, N, K: lib.fp8_gemm_wgrad(a, 1, b, ia, ib, out, M, N, K, None)
+    assert call(None, B16, C16, C16 + 4, D16, 128, 128, 128) == INVALID
+    assert call(A16, B16, None, C16 + 4, D16, 128, 128, 128) == INVALID
+    assert call(A16, B16, C16, C16 + 4, None, 128, 128, 128) == INVALID
+    assert call(A16, B16, C16, C16 + 4, D16, 0, 128, 128) == INVALID
+    assert call(A16, B16, C16, C16 + 4, A16, 128, 128, 128) == INVALID        # out aliases A
+    assert call(A16, B16, C16, C16 + 4, D16, 136, 136, 136) == UNSUPPORTED    # not a multiple of 16 / 128
+    # the reduction axis (K, N, M for fwd, dgrad, wgrad) must be a multiple of 128
+    red = {"fwd": (128, 128, 192), "dgrad": (128, 192, 128), "wgrad": (192, 128, 128)}[entry]
+    assert call(A16, B16, C16, C16 + 4, D16, *red) == UNSUPPORTED
+    assert call(A16, B16, C16, C16 + 4, D16 + 4, 128, 128, 128) == UNSUPPORTED  # misaligned out
+    assert call(A16 + 1, B16, C16, C16 + 4, D16, 128, 128, 128) == UNSUPPORTED
+
+
+def test_bad_dy_format(lib):
+    assert lib.fp8_gemm_dgrad(A16, 7, B16, C16, C16 + 4, D16, 128, 128, 128, None) == INVALID
+    assert lib.fp8_gemm_wgrad(A16, -1, B16, C16, C16 + 4, D16, 128, 128, 128, None) == INVALID
+
+
+def test_python_binding_imports_and_fails_loudly_without_gpu():
+    import torch
+    import fp8_precision_amd as fp8
+    assert set(fp8.EXPORTED) <= set(declared_functions())
+    x = torch.zeros(16, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        fp8.absmax(x)   # a CPU tensor is refused: there is no CPU path

@@ -1,0 +1,129 @@
+"""GPU parity of the FP8 GEMMs (fwd / dgrad / wgrad) against the oracle.
+
+* exact-arithmetic operands (small integers: every partial sum exact in fp32,
+  so any summation order gives the same value) -> bit-exact;
+* an identity right operand and all-ones operands (closed form K * da * db);
+* random operands at shapes spanning several 256 x 256 tiles with ragged
+  edges, both operand formats: relative Frobenius error <= 5e-3, and every
+  output within the error bound of an fp32 sum in arbitrary order;
+* the pages' shapes at full size on sampled rows;
+* determinism: the same call twice gives identical bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import E4M3, E5M2, assert_within_sum_bound, dev, gemm_compare, say, u16
+
+pytestmark = pytest.mark.gpu
+
+TDT = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
+
+
+@pytest.fixture(scope="module")
+def fp8():
+    import fp8_precision_amd
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return fp8_precision_amd
+
+
+def codes_of(values: np.ndarray, fmt: int) -> np.ndarray:
+    """Encode exactly representable values (test data only) via torch's CPU cast."""
+    return torch.from_numpy(values.astype(np.float32)).to(TDT[fmt]).view(torch.uint8).numpy()
+
+
+def random_codes(rng, shape, fmt, sigma):
+    return codes_of(rng.standard_normal(shape) * sigma, fmt)
+
+
+def scal(v):
+    return torch.tensor([v], dtype=torch.float32, device="cuda")
+
+
+def run(fp8, entry, a, fa, b, inv_a, inv_b):
+    """Call one entry point with TN operands a [P, R], b [Q, R]; returns bf16 [P, Q]."""
+    A, B = dev(torch.from_numpy(a)), dev(torch.from_numpy(b))
+    ia, ib = scal(inv_a), scal(inv_b)
+    if entry == "fwd":
+        return fp8.gemm_fwd(A, B, ia, ib)
+    if entry == "dgrad":
+        return fp8.gemm_dgrad(A, fa, B, ia, ib)
+    return fp8.gemm_wgrad(A, fa, B, ia, ib)
+
+
+ENTRIES = [("fwd", E4M3), ("dgrad", E5M2), ("wgrad", E5M2), ("dgrad", E4M3), ("wgrad", E4M3)]
+
+
+@pytest.mark.parametrize("entry,fa", ENTRIES)
+@pytest.mark.parametrize("P,Q,R", [(256, 256, 256), (384, 512, 1024), (128, 256, 256), (272, 528, 384)])
+def test_exact_small_integers(fp8, orc, entry, fa, P, Q, R):
+    say("gemm exact", entry, fa, P, Q, R)
+    rng = np.random.default_rng(P + Q + R)
+    a = codes_of(rng.integers(-4, 5, (P, R)), fa)
+    b = codes_of(rng.integers(-3, 4, (Q, R)), E4M3)
+    inv_a, inv_b = np.float32(0.25), np.float32(2.0 ** -5)
+    y = u16(run(fp8, entry, a, fa, b, inv_a, inv_b))
+    ref = orc.gemm(a, fa, b, E4M3, inv_a, inv_b)
+    assert np.array_equal(y, ref)
+
+
+def test_identity_and_ones(fp8, orc):
+    say("gemm identity/ones")
+    rng = np.random.default_rng(5)
+    K = 256
+    a = random_codes(rng, (256, K), E4M3, 60.0)
+    eye = np.zeros((K, K), np.uint8)
+    eye[np.arange(K), np.arange(K)] = 0x38
+    y = u16(run(fp8, "fwd", a, E4M3, eye, np.float32(0.5), np.float32(0.75)))
+    assert np.array_equal(y, orc.gemm(a, E4M3, eye, E4M3, np.float32(0.5), np.float32(0.75)))
+    ones_a = np.full((128, 2048), 0x3C, np.uint8)   # 1.0 in e5m2
+    ones_b = np.full((272, 2048), 0x38, np.uint8)   # 1.0 in e4m3
+    y = u16(run(fp8, "wgrad", ones_a, E5M2, ones_b, np.float32(3.0), np.float32(0.1)))
+    assert np.array_equal(y, orc.gemm(ones_a, E5M2, ones_b, E4M3, np.float32(3.0), np.float32(0.1)))
+    assert len(np.unique(y)) == 1
+
+
+@pytest.mark.parametrize("entry,fa", ENTRIES)
+@pytest.mark.parametrize("P,Q,R", [(16, 16, 128), (128, 256, 256), (272, 528, 384), (512, 768, 1024),
+                                   (1040, 272, 640), (768, 1280, 2048)])
+def test_random_shapes(fp8, orc, entry, fa, P, Q, R):
+    say("gemm random", entry, fa, P, Q, R)
+    rng = np.random.default_rng(P * 3 + Q * 5 + R)
+    a = random_codes(rng, (P, R), fa, 40.0 if fa == E4M3 else 2000.0)
+    b = random_codes(rng, (Q, R), E4M3, 40.0)
+    inv_a, inv_b = np.float32(1 / 448.0), np.float32(0.0123)
+    yt = run(fp8, entry, a, fa, b, inv_a, inv_b)
+    y = u16(yt)
+    ref = orc.gemm(a, fa, b, E4M3, inv_a, inv_b)
+    gemm_compare(y, ref, f"{entry} {P}x{Q}x{R}")
+    assert_within_sum_bound(y, ref, a, fa, b, E4M3, inv_a, inv_b, np.arange(P), f"{entry} {P}x{Q}x{R}")
+    # determinism
+    y2 = u16(run(fp8, entry, a, fa, b, inv_a, inv_b))
+    assert np.array_equal(y, y2)
+
+
+FULL = [
+    ("7B gate/up fwd", "fwd", E4M3, 4096, 22016, 4096),
+    ("7B down fwd", "fwd", E4M3, 4096, 4096, 11008),
+    ("7B qkv dgrad", "dgrad", E5M2, 4096, 4096, 12288),
+    ("7B gate/up wgrad", "wgrad", E5M2, 22016, 4096, 4096),
+    ("14B down dgrad", "dgrad", E5M2, 8192, 13824, 5120),
+    ("32B qkv wgrad", "wgrad", E5M2, 7168, 5120, 16384),
+]
+
+
+@pytest.mark.parametrize("name,entry,fa,P,Q,R", FULL)
+def test_full_size_sampled_rows(fp8, orc, name, entry, fa, P, Q, R):
+    say("gemm full", name, P, Q, R)
+    g = torch.Generator(device="cpu").manual_seed(P + Q + R)
+    # operands: decoded values ~N(0, sigma) encoded by torch's cast (test data only)
+    a = torch.randn((P, R), generator=g).mul_(60.0 if fa == E4M3 else 3000.0).to(TDT[fa]).view(torch.uint8)
+    b = torch.randn((Q, R), generator=g).mul_(60.0).to(TDT[E4M3]).view(torch.uint8)
+    inv_a, inv_b = np.float32(1 / 448.0), np.float32(1 / 448.0)
+    yt = run(fp8, entry, a.numpy(), fa, b.numpy(), inv_a, inv_b)
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(P - 8, P),
+                                     np.random.default_rng(1).integers(0, P, 48)])).astype(np.int64)
+    y = u16(yt)[rows]
+    ref = orc.gemm(a.numpy(), fa, b.numpy(), E4M3, inv_a, inv_b, rows=rows)
+    gemm_compare(y, ref, name)
+    assert_within_sum_bound(y, ref, a.numpy(), fa, b.numpy(), E4M3, inv_a, inv_b, rows, name)

@@ -1,0 +1,143 @@
+"""GPU parity of fp8_absmax and fp8_quantize against the oracle (bit-exact).
+
+* absmax: ragged lengths (including n < 8 and n % 8 != 0), planted maxima,
+  -0, infinities, NaN, subnormals;
+* the scale and inverse scale for every positive finite bf16 absmax;
+* every bf16 input pattern quantised under a set of retained absmax values
+  (fresh, stale, zero, tiny -> clamped scale, huge, inf, NaN), both formats,
+  with and without the transposed copy;
+* random tensors whose shapes span several tiles with ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import E4M3, E5M2, assert_codes_equal, assert_f32_equal, dev, say, scalar, u16, u8
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fp8():
+    import fp8_precision_amd
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return fp8_precision_amd
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 8, 9, 15, 17, 255, 1024, 4097, 65536 * 3 + 5, (1 << 22) + 3, 33554432])
+def test_absmax_lengths(fp8, orc, n):
+    say("absmax", n)
+    x = workloads.draw(100, n % 997, (n,), 1.0)
+    bits = u16(x)
+    if n > 3:
+        bits[n // 3] = 0xC4E0       # -1792, planted (negative) maximum
+        bits[-1] = 0x44DF           # a large positive value in the ragged tail
+    xt = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+    got = scalar(fp8.absmax(dev(xt)))
+    torch.cuda.synchronize()
+    assert_f32_equal(got, orc.absmax_bf16(bits), f"absmax n={n}")
+
+
+def test_absmax_special_values(fp8, orc):
+    base = np.zeros(4099, np.uint16)
+    cases = {
+        "zeros": [],
+        "neg_zero": [(5, 0x8000)],
+        "subnormal": [(7, 0x0001), (4000, 0x8003)],
+        "neg_inf": [(11, 0xFF80)],
+        "pos_inf_tail": [(4098, 0x7F80)],
+        "nan": [(13, 0x7FC1), (14, 0x3F80)],
+        "neg_nan": [(4097, 0xFFC0)],
+    }
+    for name, sets in cases.items():
+        say("absmax special", name)
+        b = base.copy()
+        for i, v in sets:
+            b[i] = v
+        xt = torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16)
+        got = scalar(fp8.absmax(dev(xt)))
+        assert_f32_equal(got, orc.absmax_bf16(b), name)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_scale_every_bf16_absmax(fp8, orc, fmt):
+    say("scale sweep", fmt)
+    bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    amax = torch.from_numpy(((bits.astype(np.uint32) << 16).view(np.float32)).copy()).cuda()
+    x = torch.zeros((16, 16), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((16, 16), dtype=torch.uint8, device="cuda")
+    sc = torch.empty(bits.size, dtype=torch.float32, device="cuda")
+    inv = torch.empty(bits.size, dtype=torch.float32, device="cuda")
+    for i in range(bits.size):
+        fp8.quantize(x, fmt, amax[i:i + 1], q=q, scale=sc[i:i + 1], inv_scale=inv[i:i + 1])
+    s_gpu, i_gpu = sc.cpu().numpy(), inv.cpu().numpy()
+    a = amax.cpu().numpy()
+    for i in range(0, bits.size, 1):
+        s_ref, i_ref = orc.scale(a[i], fmt)
+        if s_gpu[i].view(np.uint32) != np.float32(s_ref).view(np.uint32) or \
+                i_gpu[i].view(np.uint32) != np.float32(i_ref).view(np.uint32):
+            raise AssertionError(f"absmax {a[i]!r}: gpu ({s_gpu[i]!r}, {i_gpu[i]!r}) oracle ({s_ref!r}, {i_ref!r})")
+
+
+RETAINED = [0.0, 1e-45, 1e-40, 1.1754944e-38, 1e-37, 1.3e-36, 2.0 ** -20, 0.5, 1.0, 3.0, 448.0, 1000.0,
+            57344.0, 1.0e5, 3.3e38, np.finfo(np.float32).max, np.inf, np.nan]
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_every_bf16_pattern_under_retained_scales(fp8, orc, fmt):
+    all_bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(4096, 16)
+    x = dev(torch.from_numpy(all_bits.view(np.int16).copy()).view(torch.bfloat16))
+    rng = np.random.default_rng(42)
+    values = RETAINED + list(rng.uniform(1e-3, 1e3, 12))
+    for a in values:
+        say("retained", fmt, a)
+        amax = torch.tensor([a], dtype=torch.float32, device="cuda")
+        q, qt, s, inv = fp8.quantize(x, fmt, amax, want_q=True, want_qt=True)
+        s_ref, inv_ref = orc.scale(np.float32(a), fmt)
+        assert_f32_equal(scalar(s), s_ref, f"scale {a}")
+        assert_f32_equal(scalar(inv), inv_ref, f"inv {a}")
+        q_ref, _ = orc.quantize(all_bits, fmt, s_ref)
+        assert_codes_equal(u8(q), q_ref, fmt, f"q absmax={a}")
+        assert_codes_equal(u8(qt), q_ref.T.copy(), fmt, f"qt absmax={a}")
+        q_only, _, _, _ = fp8.quantize(x, fmt, amax, want_q=True, want_qt=False)
+        assert_codes_equal(u8(q_only), q_ref, fmt, f"q (flat kernel) absmax={a}")
+
+
+SHAPES = [(1, 16), (3, 48), (16, 16), (48, 528), (64, 512), (80, 1040), (144, 4112), (130, 2064),
+          (2048, 1008), (16, 65536)]
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_quantize_shapes(fp8, orc, fmt, shape):
+    rows, cols = shape
+    say("quantize", fmt, shape)
+    sigma = 1.0 if fmt == E4M3 else 1e-3
+    x = workloads.draw(7, rows * 31 + cols, shape, sigma)
+    bits = u16(x)
+    xd = dev(x)
+    amax = fp8.absmax(xd)
+    want_qt = rows % 16 == 0
+    q, qt, s, inv = fp8.quantize(xd, fmt, amax, want_q=True, want_qt=want_qt)
+    am_ref = orc.absmax_bf16(bits)
+    assert_f32_equal(scalar(amax), am_ref, "absmax")
+    s_ref, inv_ref = orc.scale(am_ref, fmt)
+    assert_f32_equal(scalar(s), s_ref, "scale")
+    assert_f32_equal(scalar(inv), inv_ref, "inv")
+    q_ref, _ = orc.quantize(bits, fmt, s_ref)
+    assert_codes_equal(u8(q), q_ref, fmt, "q")
+    if want_qt:
+        assert_codes_equal(u8(qt), q_ref.T.copy(), fmt, "qt")
+        _, qt_only, _, _ = fp8.quantize(xd, fmt, amax, want_q=False, want_qt=True)
+        assert_codes_equal(u8(qt_only), q_ref.T.copy(), fmt, "qt only")
+
+
+def test_quantize_rejects_bad_arguments(fp8):
+    x = torch.zeros((16, 24), dtype=torch.bfloat16, device="cuda")
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    with pytest.raises(fp8.Fp8Error):
+        fp8.quantize(x, E4M3, amax)          # cols % 16 != 0
+    x = torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fp8.Fp8Error):
+        fp8.quantize(x, E4M3, amax, want_qt=True)   # rows % 16 != 0 with qt
