@@ -53,16 +53,17 @@ constexpr int kWaitVm16 = 0x4F70;
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
-// 16-byte direct-to-LDS load: lane L of the wave writes LDS bytes
-// [lds_base + 16 L, lds_base + 16 L + 16).  Issued as inline assembly so that
-// the compiler's LDS-DMA hazard tracking does not put a wait for every pending
-// load in front of each LDS read: the kernel orders these loads itself with an
-// explicit vmcnt wait and a barrier before the stage they fill is read.
-__device__ __forceinline__ void lds_load16(const uint8_t* g, uint32_t lds_base)
+// 16-byte direct-to-LDS load in the scalar-base form: lane L reads 16 bytes at
+// sbase + voff[L] and writes LDS bytes [lds + 16 L, lds + 16 L + 16).  Issued
+// as inline assembly so that the compiler's LDS-DMA hazard tracking does not
+// put a wait for every pending load in front of each LDS read: the kernel
+// orders these loads itself with an explicit vmcnt wait and a barrier before
+// the stage they fill is read.
+__device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint32_t lds)
 {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(g), "s"(lds_base)
+                 : "v"(voff), "s"(sbase), "s"(lds)
                  : "memory", "m0");
 }
 
@@ -77,46 +78,47 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int chunk)
     return r;
 }
 
-// Global -> LDS sources of one workgroup: load ii (0..7) of wave w fills LDS rows
-// (w*8 + ii)*8 .. +8 of the A (B) stage; lane L writes row r = (w*8+ii)*8 + L/8
-// at physical chunk L%8, i.e. it reads logical chunk (L%8) ^ f(r).  f(r) depends
-// on ii only through ii & 1, so a lane needs two byte offsets per operand (even
-// and odd ii) plus the uniform row step 8 * ii * R.
+// Global -> LDS sources of one wave.  Load ii (0..7) of wave w fills LDS rows
+// r = (w*8 + ii)*8 + L/8 of the A (B) stage, lane L at physical chunk L%8, i.e.
+// it reads logical chunk (L%8) ^ f(r).  f(r) depends on ii only through ii & 1,
+// so in the interior form a lane keeps two byte offsets per operand and the
+// row step 8 * ii * R goes into the uniform base.  Matrices with fewer than
+// 256 rows (EDGE) clamp each row to the last valid one instead.
 struct Sources {
     const uint8_t* a;
     const uint8_t* b;
-    uint32_t a_off[2];    // interior tiles: byte offset of the lane's first load
+    uint32_t a_off[2];
     uint32_t b_off[2];
     uint32_t step;        // 8 rows
-    int a_row, b_row;     // edge tiles: the lane's first row, and the last valid row
+    int a_row, b_row;     // EDGE: the lane's first row and the last valid row
     int a_last, b_last;
-    uint32_t chunk16[2];  // byte offset of the lane's chunk within a row (even / odd ii)
-    bool edge;
+    uint32_t chunk16[2];
 };
 
+// Load idx (0..15) of a stage: 0..7 fill A, 8..15 fill B.
+template <bool EDGE>
+__device__ __forceinline__ void issue_one(const Sources& src, uint32_t stage, int k0, int wave, int idx)
+{
+    const int ii = idx & 7;
+    const bool is_b = idx >= 8;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(stage + (is_b ? (uint32_t)kStageA : 0u) +
+                                                        (uint32_t)(wave * 8 + ii) * 1024u);
+    const uint8_t* base = is_b ? src.b : src.a;
+    if (!EDGE) {
+        const uint32_t off = is_b ? src.b_off[ii & 1] : src.a_off[ii & 1];
+        dma16(off, base + ((size_t)ii * src.step + (size_t)k0), lds);
+    } else {
+        const uint32_t R = src.step / 8u;
+        const int row = is_b ? min(src.b_row + ii * 8, src.b_last) : min(src.a_row + ii * 8, src.a_last);
+        dma16((uint32_t)row * R + src.chunk16[ii & 1], base + k0, lds);
+    }
+}
+
+template <bool EDGE>
 __device__ __forceinline__ void issue_stage(const Sources& src, uint32_t stage, int k0, int wave)
 {
-    if (!src.edge) {
 #pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
-            lds_load16(src.a + (src.a_off[ii & 1] + (uint32_t)ii * src.step + (uint32_t)k0),
-                       stage + (uint32_t)(wave * 8 + ii) * 1024u);
-            lds_load16(src.b + (src.b_off[ii & 1] + (uint32_t)ii * src.step + (uint32_t)k0),
-                       stage + (uint32_t)kStageA + (uint32_t)(wave * 8 + ii) * 1024u);
-        }
-    } else {
-        // rows past the edge re-read the last valid row; those outputs are never stored
-        const uint32_t R = src.step / 8u;
-#pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
-            const uint32_t ra = (uint32_t)min(src.a_row + ii * 8, src.a_last);
-            const uint32_t rb = (uint32_t)min(src.b_row + ii * 8, src.b_last);
-            lds_load16(src.a + (ra * R + src.chunk16[ii & 1] + (uint32_t)k0),
-                       stage + (uint32_t)(wave * 8 + ii) * 1024u);
-            lds_load16(src.b + (rb * R + src.chunk16[ii & 1] + (uint32_t)k0),
-                       stage + (uint32_t)kStageA + (uint32_t)(wave * 8 + ii) * 1024u);
-        }
-    }
+    for (int idx = 0; idx < 16; ++idx) issue_one<EDGE>(src, stage, k0, wave, idx);
 }
 
 struct Frags {
@@ -124,14 +126,27 @@ struct Frags {
     v8i b[4];
 };
 
-__device__ __forceinline__ void read_frags(Frags& f, const uint8_t* stage, int kk, int wm, int wn, int lane)
+// Fragment f (0..3: A blocks, 4..7: B blocks) of half-step kk.
+__device__ __forceinline__ v8i read_frag(const uint8_t* stage, int kk, int f, int wm, int wn, int lane)
 {
-    const int fr = lane & 31;              // fragment row within a 32-row block
-    const int c = kk * 4 + (lane >> 5) * 2;  // first 16-byte chunk of the lane's 32 bytes
+    const int fr = lane & 31;                  // fragment row within a 32-row block
+    const int c = kk * 4 + (lane >> 5) * 2;    // first 16-byte chunk of the lane's 32 bytes
+    if (f < 4) return lds_frag(stage, wm * 128 + f * 32 + fr, c);
+    return lds_frag(stage + kStageA, wn * 128 + (f - 4) * 32 + fr, c);
+}
+
+__device__ __forceinline__ void read_frags(Frags& fr, const uint8_t* stage, int kk, int wm, int wn, int lane)
+{
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = lds_frag(stage, wm * 128 + i * 32 + fr, c);
+    for (int i = 0; i < 4; ++i) fr.a[i] = read_frag(stage, kk, i, wm, wn, lane);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[j] = lds_frag(stage + kStageA, wn * 128 + j * 32 + fr, c);
+    for (int j = 0; j < 4; ++j) fr.b[j] = read_frag(stage, kk, 4 + j, wm, wn, lane);
+}
+
+template <int FA, int FB>
+__device__ __forceinline__ void mma1(v16f (&acc)[4][4], const Frags& f, int i, int j)
+{
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, 0, 0, 0);
 }
 
 template <int FA, int FB>
@@ -140,32 +155,71 @@ __device__ __forceinline__ void mma(v16f (&acc)[4][4], const Frags& f)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA,
-                                                                        0, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) mma1<FA, FB>(acc, f, i, j);
 }
 
 // One reduction step on stage `cur` (holding tile kt).  On entry f0 holds the
-// first half-step fragments of tile kt.  The barrier sits between the two
-// half-steps: every wave has then read all of `cur` (so tile kt+2 may be issued
-// into it) and tile kt+1 has landed in `nxt` (so its first fragments are read
-// while the second half-step's matrix instructions run).  After the last tile
-// the read of `nxt` returns stale data that is never used.
-template <int FA, int FB>
-__device__ __forceinline__ void k_step(v16f (&acc)[4][4], Frags& f0, Frags& f1, const Sources& src,
-                                       const uint8_t* cur, uint32_t cur_addr, const uint8_t* nxt,
-                                       bool issue, int k_issue, int wave, int wm, int wn, int lane)
+// first half-step fragments of tile kt.
+//   first half:  the 16 matrix instructions on f0, interleaved with the LDS
+//                reads of the second half-step fragments (f1) from `cur`;
+//   barrier:     every wave has read all of `cur`, and tile kt+1 has landed in
+//                `nxt`;
+//   second half: the 16 matrix instructions on f1, interleaved with the LDS
+//                reads of the next tile's first fragments (f0, from `nxt`) and
+//                with the 16 loads of tile kt+2 into `cur`.
+// After the last tile the reads of `nxt` return stale data that is never used.
+// Second half of a step: the 16 matrix instructions on f1, each followed by
+// the LDS reads of one next-tile fragment (f0, first eight slots) and one load
+// of tile kt+2.  sched_barrier pins this order, so the reads and the load issue
+// run while the matrix core works.  Past the last tile the loads re-read the
+// last tile into a stage that is not read again (valid addresses, no branch in
+// the loop, which keeps the register allocation flat).
+template <int FA, int FB, bool EDGE>
+__device__ __forceinline__ void second_half(v16f (&acc)[4][4], Frags& f0, const Frags& f1, const Sources& src,
+                                            const uint8_t* nxt, uint32_t cur_addr, int k_issue, int wave,
+                                            int wm, int wn, int lane)
 {
-    read_frags(f1, cur, 1, wm, wn, lane);
-    mma<FA, FB>(acc, f0);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);     // tile kt+1 has landed (this wave's loads)
-    __syncthreads();                          // ... for all waves; `cur` fully read
-    if (issue) issue_stage(src, cur_addr, k_issue, wave);
-    read_frags(f0, nxt, 0, wm, wn, lane);
-    mma<FA, FB>(acc, f1);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        mma1<FA, FB>(acc, f1, t >> 2, t & 3);
+        if (t < 8) {
+            if (t < 4) f0.a[t] = read_frag(nxt, 0, t, wm, wn, lane);
+            else f0.b[t - 4] = read_frag(nxt, 0, t, wm, wn, lane);
+        }
+        issue_one<EDGE>(src, cur_addr, k_issue, wave, t);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
-template <int FA, int FB>
+// One reduction step on stage `cur` (holding tile kt).  On entry f0 holds the
+// first half-step fragments of tile kt.
+//   first half:  the 16 matrix instructions on f0, interleaved with the LDS
+//                reads of the second half-step fragments (f1) from `cur`;
+//   barrier:     every wave has read all of `cur`, and tile kt+1 has landed in
+//                `nxt`;
+//   second half: as above.
+// After the last tile the reads of `nxt` return stale data that is never used.
+template <int FA, int FB, bool EDGE>
+__device__ __forceinline__ void k_step(v16f (&acc)[4][4], Frags& f0, Frags& f1, const Sources& src,
+                                       const uint8_t* cur, uint32_t cur_addr, const uint8_t* nxt,
+                                       int k_issue, int wave, int wm, int wn, int lane)
+{
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        mma1<FA, FB>(acc, f0, t >> 2, t & 3);
+        if (t < 8) {
+            if (t < 4) f1.a[t] = read_frag(cur, 1, t, wm, wn, lane);
+            else f1.b[t - 4] = read_frag(cur, 1, t, wm, wn, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);     // tile kt+1 has landed (this wave's loads)
+    __syncthreads();                          // ... for all waves; `cur` fully read
+    __builtin_amdgcn_sched_barrier(0);
+    second_half<FA, FB, EDGE>(acc, f0, f1, src, nxt, cur_addr, k_issue, wave, wm, wn, lane);
+}
+
+template <int FA, int FB, bool EDGE>
 __global__ void __launch_bounds__(256, 1)
 gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                const float* __restrict__ inv_a, const float* __restrict__ inv_b,
@@ -187,7 +241,12 @@ gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
     const int in_group = wg - group * group_size;
     const int tile_m = first_m + in_group % gm;
     const int tile_n = in_group / gm;
-    const int m0 = tile_m * kBM, n0 = tile_n * kBN;
+    // Logical tile origin, and the origin actually computed: a last partial tile
+    // is shifted back to end at the matrix edge (P, Q >= 256), recomputing rows
+    // of its neighbour that it then does not store.
+    const int ms = tile_m * kBM, ns = tile_n * kBN;
+    const int m0 = EDGE ? ms : min(ms, P - kBM);
+    const int n0 = EDGE ? ns : min(ns, Q - kBN);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -202,7 +261,6 @@ gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
     src.a_last = P - 1;
     src.b_last = Q - 1;
     src.step = 8u * (uint32_t)R;
-    src.edge = (m0 + kBM > P) || (n0 + kBN > Q);
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
         const int row = (wave * 8 + par) * 8 + (lane >> 3);     // row within the tile
@@ -221,9 +279,9 @@ gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
 
     const int KT = R / kBK;
     Frags f0, f1;
-    issue_stage(src, lds_addr, 0, wave);
+    issue_stage<EDGE>(src, lds_addr, 0, wave);
     if (KT > 1) {
-        issue_stage(src, lds_addr + kStage, kBK, wave);
+        issue_stage<EDGE>(src, lds_addr + kStage, kBK, wave);
         __builtin_amdgcn_s_waitcnt(kWaitVm16);    // tile 0 landed, tile 1's 16 loads may be in flight
     } else {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -232,9 +290,11 @@ gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
     read_frags(f0, lds, 0, wm, wn, lane);
     for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 1;
-        k_step<FA, FB>(acc, f0, f1, src, lds + cur * kStage, lds_addr + cur * kStage,
-                       lds + (cur ^ 1) * kStage, kt + 2 < KT, (kt + 2) * kBK, wave, wm, wn, lane);
+        k_step<FA, FB, EDGE>(acc, f0, f1, src, lds + cur * kStage, lds_addr + cur * kStage,
+                             lds + (cur ^ 1) * kStage, min(kt + 2, KT - 1) * kBK, wave, wm, wn, lane);
     }
+    // no load may land in LDS after the workgroup has exited
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
     // ---- epilogue: descale, round to bf16, store 4 consecutive columns per lane
     const int fr = lane & 31;
@@ -242,14 +302,14 @@ gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = m0 + wm * 128 + i * 32 + fr;
-        if (m >= P) continue;
+        if (m < ms || m >= P) continue;
         uint16_t* orow = out + (size_t)m * Q;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn * 128 + j * 32 + g * 8 + (lane >> 5) * 4;
-                if (n >= Q) continue;
+                if (n < ns || n >= Q) continue;
                 const f32x2 v01 = {acc[i][j][4 * g] * d, acc[i][j][4 * g + 1] * d};
                 const f32x2 v23 = {acc[i][j][4 * g + 2] * d, acc[i][j][4 * g + 3] * d};
                 const bf16x2 b01 = __builtin_convertvector(v01, bf16x2);
@@ -269,8 +329,13 @@ static hipError_t launch_fmt(const uint8_t* A, const uint8_t* B, const float* in
 {
     const int tiles_m = (int)((P + kBM - 1) / kBM);
     const int tiles_n = (int)((Q + kBN - 1) / kBN);
-    gemm_tn_kernel<FA, FB><<<tiles_m * tiles_n, 256, 0, stream>>>(
-        A, B, inv_a, inv_b, reinterpret_cast<uint16_t*>(out), (int)P, (int)Q, (int)R, tiles_m, tiles_n);
+    uint16_t* o = reinterpret_cast<uint16_t*>(out);
+    if (P >= kBM && Q >= kBN)
+        gemm_tn_kernel<FA, FB, false><<<tiles_m * tiles_n, 256, 0, stream>>>(A, B, inv_a, inv_b, o, (int)P, (int)Q,
+                                                                              (int)R, tiles_m, tiles_n);
+    else
+        gemm_tn_kernel<FA, FB, true><<<tiles_m * tiles_n, 256, 0, stream>>>(A, B, inv_a, inv_b, o, (int)P, (int)Q,
+                                                                             (int)R, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
