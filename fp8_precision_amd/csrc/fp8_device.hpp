@@ -100,10 +100,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return v;
 }
 
-// Block-wide max of `v` (blockDim.x == 256) folded into *out with one atomicMax
-// per block.  `out` holds the fp32 bits of a non-negative value (or NaN with
-// the sign bit clear), for which unsigned order equals the magnitude order
-// used by the absmax definition.
+// Block-wide max of `v` (blockDim.x == 256) folded into *out.  `out` holds the
+// fp32 bits of a non-negative value (or NaN with the sign bit clear), for which
+// unsigned order equals the magnitude order used by the absmax definition.
+// A block first reads the running maximum and issues its atomicMax only if it
+// would raise it (a stale read is smaller or equal, so the test is safe); this
+// keeps thousands of blocks from serialising on one address.
 __device__ __forceinline__ void block_max_to_global(uint32_t v, uint32_t* out)
 {
     __shared__ uint32_t part[4];
@@ -116,7 +118,8 @@ __device__ __forceinline__ void block_max_to_global(uint32_t v, uint32_t* out)
         m = m > part[1] ? m : part[1];
         m = m > part[2] ? m : part[2];
         m = m > part[3] ? m : part[3];
-        atomicMax(out, m);
+        const uint32_t seen = __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (m > seen) atomicMax(out, m);
     }
 }
 

@@ -64,8 +64,8 @@ hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, hipStream
 {
     const int64_t nvec = n / 8;
     const int ntail = (int)(n - nvec * 8);
-    int64_t blocks = (nvec + 255) / 256;
-    const int64_t cap = (int64_t)device_cu_count() * 8;
+    int64_t blocks = (nvec + 1023) / 1024;       // at least 4 vectors per thread
+    const int64_t cap = (int64_t)device_cu_count() * 4;
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     zero_u32_kernel<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax));
