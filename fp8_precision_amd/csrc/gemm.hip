@@ -22,10 +22,11 @@
 //    c ^ f(r), f(r) = ((r >> 1) & 7) ^ ((r & 1) << 2), which keeps the 16-byte
 //    fragment reads of 8 or 16 consecutive rows on distinct banks.
 //  - The instruction's operands are swapped (B fragment first), so each lane
-//    ends with 4 consecutive output columns of one row and stores 8 bytes.
-//  - Workgroup ids are remapped so that consecutive tiles of the grouped
-//    raster order land on the same XCD (workgroups are dealt round-robin to
-//    the 8 XCDs, each with its own L2).
+//    ends with 4 consecutive output columns of one row; the epilogue stages
+//    them through LDS and writes full 256-byte row segments.
+//  - Persistent: one workgroup per CU walks tiles in a grouped raster order,
+//    renumbered XCD-major so that the 32 CUs of an XCD (sharing one L2) work on
+//    consecutive tiles; the next tile's first stages load during the epilogue.
 //  - Deterministic: every output is reduced by one wave in a fixed order.
 #include "fp8_device.hpp"
 #include "fp8_internal.hpp"
@@ -44,6 +45,8 @@ constexpr int kStageA = kBM * kBK;            // 32 KB
 constexpr int kStageB = kBN * kBK;            // 32 KB
 constexpr int kStage = kStageA + kStageB;     // 64 KB
 constexpr int kLds = 2 * kStage;              // 128 KB
+constexpr int kEpiRows = 32;                  // epilogue chunk: 32 rows x 128 columns of bf16 per wave
+constexpr int kEpiWave = kEpiRows * 256;      // 8 KB per wave, 32 KB per workgroup (LDS total 160 KB)
 constexpr int kGroupM = 8;                    // tile rows per raster group
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
@@ -143,6 +146,9 @@ __device__ __forceinline__ void read_frags(Frags& fr, const uint8_t* stage, int 
     for (int j = 0; j < 4; ++j) fr.b[j] = read_frag(stage, kk, 4 + j, wm, wn, lane);
 }
 
+// acc[i][j] += A block i x B block j.  The k_step loops run i fastest: the
+// instruction's first source (B block j) then stays for four instructions,
+// which issues measurably faster than rotating it every instruction.
 template <int FA, int FB>
 __device__ __forceinline__ void mma1(v16f (&acc)[4][4], const Frags& f, int i, int j)
 {
@@ -181,7 +187,7 @@ __device__ __forceinline__ void second_half(v16f (&acc)[4][4], Frags& f0, const 
 {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-        mma1<FA, FB>(acc, f1, t >> 2, t & 3);
+        mma1<FA, FB>(acc, f1, t & 3, t >> 2);
         if (t < 8) {
             if (t < 4) f0.a[t] = read_frag(nxt, 0, t, wm, wn, lane);
             else f0.b[t - 4] = read_frag(nxt, 0, t, wm, wn, lane);
@@ -206,7 +212,7 @@ __device__ __forceinline__ void k_step(v16f (&acc)[4][4], Frags& f0, Frags& f1, 
 {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-        mma1<FA, FB>(acc, f0, t >> 2, t & 3);
+        mma1<FA, FB>(acc, f0, t & 3, t >> 2);
         if (t < 8) {
             if (t < 4) f1.a[t] = read_frag(cur, 1, t, wm, wn, lane);
             else f1.b[t - 4] = read_frag(cur, 1, t, wm, wn, lane);
@@ -219,48 +225,35 @@ __device__ __forceinline__ void k_step(v16f (&acc)[4][4], Frags& f0, Frags& f1, 
     second_half<FA, FB, EDGE>(acc, f0, f1, src, nxt, cur_addr, k_issue, wave, wm, wn, lane);
 }
 
-template <int FA, int FB, bool EDGE>
-__global__ void __launch_bounds__(256, 1)
-gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
-               const float* __restrict__ inv_a, const float* __restrict__ inv_b,
-               uint16_t* __restrict__ out, int P, int Q, int R, int tiles_m, int tiles_n)
-{
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+// Output tile of a virtual tile id: grouped raster order (kGroupM tile rows per
+// group, column-major within a group), so consecutive ids share A and B panels.
+struct Tile {
+    int ms, ns;     // logical origin (first row / column this tile stores)
+    int m0, n0;     // origin actually computed (shifted back inside the matrix)
+};
 
-    // ---- tile assignment: XCD-aware remap, then grouped raster order
-    const int ntiles = tiles_m * tiles_n;
-    int wg = blockIdx.x;
-    {
-        const int per_xcd = ntiles / 8;
-        if (wg < per_xcd * 8) wg = (wg % 8) * per_xcd + wg / 8;
-    }
+template <bool EDGE>
+__device__ __forceinline__ Tile tile_of(int v, int P, int Q, int tiles_m, int tiles_n)
+{
     const int group_size = kGroupM * tiles_n;
-    const int group = wg / group_size;
+    const int group = v / group_size;
     const int first_m = group * kGroupM;
     const int gm = min(tiles_m - first_m, kGroupM);
-    const int in_group = wg - group * group_size;
-    const int tile_m = first_m + in_group % gm;
-    const int tile_n = in_group / gm;
-    // Logical tile origin, and the origin actually computed: a last partial tile
-    // is shifted back to end at the matrix edge (P, Q >= 256), recomputing rows
-    // of its neighbour that it then does not store.
-    const int ms = tile_m * kBM, ns = tile_n * kBN;
-    const int m0 = EDGE ? ms : min(ms, P - kBM);
-    const int n0 = EDGE ? ns : min(ns, Q - kBN);
+    const int in_group = v - group * group_size;
+    Tile t;
+    t.ms = (first_m + in_group % gm) * kBM;
+    t.ns = (in_group / gm) * kBN;
+    // A last partial tile is shifted back to end at the matrix edge (P, Q >= 256),
+    // recomputing rows / columns of its neighbour that it then does not store.
+    t.m0 = EDGE ? t.ms : min(t.ms, P - kBM);
+    t.n0 = EDGE ? t.ns : min(t.ns, Q - kBN);
+    return t;
+}
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-    const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
-
-    Sources src;
-    src.a = A;
-    src.b = B;
-    src.a_row = m0 + wave * 64 + (lane >> 3);
-    src.b_row = n0 + wave * 64 + (lane >> 3);
-    src.a_last = P - 1;
-    src.b_last = Q - 1;
-    src.step = 8u * (uint32_t)R;
+__device__ __forceinline__ void set_sources(Sources& src, const Tile& t, int wave, int lane, int R)
+{
+    src.a_row = t.m0 + wave * 64 + (lane >> 3);
+    src.b_row = t.n0 + wave * 64 + (lane >> 3);
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
         const int row = (wave * 8 + par) * 8 + (lane >> 3);     // row within the tile
@@ -268,58 +261,117 @@ gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
         src.a_off[par] = (uint32_t)src.a_row * (uint32_t)R + src.chunk16[par];
         src.b_off[par] = (uint32_t)src.b_row * (uint32_t)R + src.chunk16[par];
     }
+}
 
-    v16f acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+// Persistent kernel: one workgroup per CU walks the tiles v = slot, slot + G,
+// slot + 2G, ... where slot renumbers the workgroups XCD-major (workgroups are
+// dealt round-robin to the 8 XCDs, each with its own L2), so in every round
+// the 32 CUs of one XCD work on 32 consecutive tiles of the raster order.
+// While a tile's epilogue stores run, the first two stages of the next tile
+// are already loading.
+template <int FA, int FB, bool EDGE>
+__global__ void __launch_bounds__(256, 1)
+gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+               const float* __restrict__ inv_a, const float* __restrict__ inv_b,
+               uint16_t* __restrict__ out, int P, int Q, int R, int tiles_m, int tiles_n)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+    __shared__ __attribute__((aligned(1024))) uint8_t epi[4 * kEpiWave];
+
+    const int ntiles = tiles_m * tiles_n;
+    const int G = gridDim.x;
+    int slot = blockIdx.x;
+    if (G % 8 == 0) slot = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+    const int fr = lane & 31;
+    const float d = inv_a[0] * inv_b[0];
+
+    Sources src;
+    src.a = A;
+    src.b = B;
+    src.a_last = P - 1;
+    src.b_last = Q - 1;
+    src.step = 8u * (uint32_t)R;
 
     const int KT = R / kBK;
     Frags f0, f1;
-    issue_stage<EDGE>(src, lds_addr, 0, wave);
-    if (KT > 1) {
-        issue_stage<EDGE>(src, lds_addr + kStage, kBK, wave);
-        __builtin_amdgcn_s_waitcnt(kWaitVm16);    // tile 0 landed, tile 1's 16 loads may be in flight
-    } else {
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    }
-    __syncthreads();
-    read_frags(f0, lds, 0, wm, wn, lane);
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        k_step<FA, FB, EDGE>(acc, f0, f1, src, lds + cur * kStage, lds_addr + cur * kStage,
-                             lds + (cur ^ 1) * kStage, min(kt + 2, KT - 1) * kBK, wave, wm, wn, lane);
-    }
-    // no load may land in LDS after the workgroup has exited
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    v16f acc[4][4];
 
-    // ---- epilogue: descale, round to bf16, store 4 consecutive columns per lane
-    const int fr = lane & 31;
-    const float d = inv_a[0] * inv_b[0];
+    int v = slot;
+    if (v >= ntiles) return;
+    Tile t = tile_of<EDGE>(v, P, Q, tiles_m, tiles_n);
+    set_sources(src, t, wave, lane, R);
+    issue_stage<EDGE>(src, lds_addr, 0, wave);
+    issue_stage<EDGE>(src, lds_addr + kStage, min(1, KT - 1) * kBK, wave);
+    for (;;) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * 128 + i * 32 + fr;
-        if (m < ms || m >= P) continue;
-        uint16_t* orow = out + (size_t)m * Q;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * 128 + j * 32 + g * 8 + (lane >> 5) * 4;
-                if (n < ns || n >= Q) continue;
-                const f32x2 v01 = {acc[i][j][4 * g] * d, acc[i][j][4 * g + 1] * d};
-                const f32x2 v23 = {acc[i][j][4 * g + 2] * d, acc[i][j][4 * g + 3] * d};
-                const bf16x2 b01 = __builtin_convertvector(v01, bf16x2);
-                const bf16x2 b23 = __builtin_convertvector(v23, bf16x2);
-                uint2 w;
-                w.x = __builtin_bit_cast(uint32_t, b01);
-                w.y = __builtin_bit_cast(uint32_t, b23);
-                *reinterpret_cast<uint2*>(orow + n) = w;
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        __builtin_amdgcn_s_waitcnt(kWaitVm16);    // stage 0 landed; stage 1's 16 loads may be in flight
+        __syncthreads();
+        read_frags(f0, lds, 0, wm, wn, lane);
+        for (int kt = 0; kt < KT; ++kt) {
+            const int cur = kt & 1;
+            k_step<FA, FB, EDGE>(acc, f0, f1, src, lds + cur * kStage, lds_addr + cur * kStage,
+                                 lds + (cur ^ 1) * kStage, min(kt + 2, KT - 1) * kBK, wave, wm, wn, lane);
+        }
+        // every load of this tile has landed and every wave is done with LDS
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __syncthreads();
+
+        const Tile done = t;
+        const int next = v + G;
+        if (next < ntiles) {
+            v = next;
+            t = tile_of<EDGE>(v, P, Q, tiles_m, tiles_n);
+            set_sources(src, t, wave, lane, R);
+            issue_stage<EDGE>(src, lds_addr, 0, wave);
+            issue_stage<EDGE>(src, lds_addr + kStage, min(1, KT - 1) * kBK, wave);
+        }
+
+        // ---- epilogue of `done`: descale and round to bf16, stage 32-row chunks of
+        // the wave's 128 x 128 tile in its private LDS region (16-byte chunks of a
+        // 256-byte row XOR-swizzled by row), read back 16 bytes per lane and store
+        // four full 256-byte row segments per instruction.
+        uint8_t* ew = epi + wave * kEpiWave;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x2 v01 = {acc[i][j][4 * g] * d, acc[i][j][4 * g + 1] * d};
+                    const f32x2 v23 = {acc[i][j][4 * g + 2] * d, acc[i][j][4 * g + 3] * d};
+                    uint2 w;
+                    w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
+                    w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
+                    const int chunk = (j * 4 + g) ^ (fr & 15);          // logical 16-byte chunk j*4+g
+                    *reinterpret_cast<uint2*>(ew + fr * 256 + chunk * 16 + (lane >> 5) * 8) = w;
+                }
+            }
+#pragma unroll
+            for (int it = 0; it < kEpiRows / 4; ++it) {
+                const int rr = it * 4 + (lane >> 4);                   // row within the chunk
+                const int c = lane & 15;                              // logical 16-byte chunk
+                const uint4 w = *reinterpret_cast<const uint4*>(ew + rr * 256 + ((c ^ (rr & 15)) * 16));
+                const int m = done.m0 + wm * 128 + i * 32 + rr;
+                const int n = done.n0 + wn * 128 + c * 8;
+                if (m >= done.ms && m < P && n >= done.ns && n < Q)
+                    *reinterpret_cast<uint4*>(out + (size_t)m * Q + n) = w;
             }
         }
+        // The loop-top wait (vmcnt <= 16) then proves the next tile's first stage
+        // has landed: if one of its loads were pending, the 16 later loads of the
+        // second stage would be too (loads complete in order), whatever the
+        // interleaved stores do.
+        if (next >= ntiles) break;
     }
 }
 
@@ -329,13 +381,15 @@ static hipError_t launch_fmt(const uint8_t* A, const uint8_t* B, const float* in
 {
     const int tiles_m = (int)((P + kBM - 1) / kBM);
     const int tiles_n = (int)((Q + kBN - 1) / kBN);
+    const int ntiles = tiles_m * tiles_n;
+    const int grid = ntiles < device_cu_count() ? ntiles : device_cu_count();   // one workgroup per CU
     uint16_t* o = reinterpret_cast<uint16_t*>(out);
     if (P >= kBM && Q >= kBN)
-        gemm_tn_kernel<FA, FB, false><<<tiles_m * tiles_n, 256, 0, stream>>>(A, B, inv_a, inv_b, o, (int)P, (int)Q,
-                                                                              (int)R, tiles_m, tiles_n);
+        gemm_tn_kernel<FA, FB, false><<<grid, 256, 0, stream>>>(A, B, inv_a, inv_b, o, (int)P, (int)Q, (int)R,
+                                                                tiles_m, tiles_n);
     else
-        gemm_tn_kernel<FA, FB, true><<<tiles_m * tiles_n, 256, 0, stream>>>(A, B, inv_a, inv_b, o, (int)P, (int)Q,
-                                                                             (int)R, tiles_m, tiles_n);
+        gemm_tn_kernel<FA, FB, true><<<grid, 256, 0, stream>>>(A, B, inv_a, inv_b, o, (int)P, (int)Q, (int)R,
+                                                               tiles_m, tiles_n);
     return hipGetLastError();
 }
 
