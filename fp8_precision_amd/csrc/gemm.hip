@@ -9,15 +9,17 @@
 //
 // Design (CDNA4):
 //  - 256 x 256 output tile per workgroup, reduction step 128 bytes, 256 threads
-//    = 4 waves in a 2 x 2 grid, each wave 128 x 128 outputs held as 4 x 4
-//    blocks of v_mfma_f32_32x32x64_f8f6f4 accumulators (256 fp32 per lane).
+//    = 4 waves in a 2 x 2 grid, each wave 128 x 128 outputs held as 8 x 8
+//    blocks of v_mfma_f32_16x16x128_f8f6f4 accumulators (256 fp32 per lane);
+//    on gfx950 this instruction issues faster than the 32x32x64 one.
 //    The operand formats (E4M3 / E5M2) are selected per operand by the
 //    instruction, so mixed E5M2 x E4M3 products run natively.
 //  - Operand tiles go global -> LDS with 16-byte direct-to-LDS loads
 //    (global_load_lds_dwordx4), two stages of 64 KB; tile k+2 is issued in the
 //    middle of step k, so each load has about one and a half steps to land.
-//  - Fragments are double-buffered in registers: the LDS reads of the next
-//    half-step overlap the matrix instructions of the current one.
+//  - Fragments are pipelined in registers: the LDS reads for the next half
+//    step and the next step's B fragments (read into each B block's registers
+//    as soon as that block is consumed) overlap the matrix instructions.
 //  - LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
 //    c ^ f(r), f(r) = ((r >> 1) & 7) ^ ((r & 1) << 2), which keeps the 16-byte
 //    fragment reads of 8 or 16 consecutive rows on distinct banks.
@@ -124,105 +126,73 @@ __device__ __forceinline__ void issue_stage(const Sources& src, uint32_t stage, 
     for (int idx = 0; idx < 16; ++idx) issue_one<EDGE>(src, stage, k0, wave, idx);
 }
 
-struct Frags {
-    v8i a[4];
-    v8i b[4];
-};
-
-// Fragment f (0..3: A blocks, 4..7: B blocks) of half-step kk.
-__device__ __forceinline__ v8i read_frag(const uint8_t* stage, int kk, int f, int wm, int wn, int lane)
+// Fragments of the 16x16x128 instruction: block b of 16 rows, lane l holds row
+// l % 16 and the 32 bytes at k offset 32 * (l / 16) of the 128-byte step (the
+// same k mapping for both operands, so the order of k within the instruction
+// does not matter).  A wave owns 128 x 128 outputs = 8 x 8 blocks.
+__device__ __forceinline__ v8i read_frag16(const uint8_t* tile, int row0, int lane)
 {
-    const int fr = lane & 31;                  // fragment row within a 32-row block
-    const int c = kk * 4 + (lane >> 5) * 2;    // first 16-byte chunk of the lane's 32 bytes
-    if (f < 4) return lds_frag(stage, wm * 128 + f * 32 + fr, c);
-    return lds_frag(stage + kStageA, wn * 128 + (f - 4) * 32 + fr, c);
+    return lds_frag(tile, row0 + (lane & 15), (lane >> 4) * 2);
 }
 
-__device__ __forceinline__ void read_frags(Frags& fr, const uint8_t* stage, int kk, int wm, int wn, int lane)
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fr.a[i] = read_frag(stage, kk, i, wm, wn, lane);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fr.b[j] = read_frag(stage, kk, 4 + j, wm, wn, lane);
-}
+typedef float v4f __attribute__((ext_vector_type(4)));
 
-// acc[i][j] += A block i x B block j.  The k_step loops run i fastest: the
-// instruction's first source (B block j) then stays for four instructions,
-// which issues measurably faster than rotating it every instruction.
+// acc[i][j] += A block i x B block j (the instruction's first source is the B
+// block, so each lane ends with 4 consecutive output columns of one row).
 template <int FA, int FB>
-__device__ __forceinline__ void mma1(v16f (&acc)[4][4], const Frags& f, int i, int j)
+__device__ __forceinline__ void mma16(v4f (&acc)[8][8], const v8i& a, const v8i& b, int i, int j)
 {
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], FB, FA, 0, 0, 0, 0);
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, acc[i][j], FB, FA, 0, 0, 0, 0);
 }
 
+// A reduction step (128 bytes of k) runs in two halves split by A rows:
+//   half 0: 32 instructions A[0..3] x B[0..7] (B block outer, A block inner),
+//           interleaved with the LDS reads of A blocks 4..7 (ahi) of the step;
+//   half 1: 32 instructions A[4..7] x B[0..7] in the same order, so B block j
+//           is dead after its four instructions and the next step's B block j
+//           is read into the same registers right then; the next step's A
+//           blocks 0..3 (alo) and the 16 loads of tile k+2 are interleaved too.
+// Between the halves a barrier (after this wave's loads of tile k+1 are waited
+// for) guarantees that every wave has read all of the step's stage and that
+// tile k+1 has landed.  The K loop body is [barrier, half 1 of step k, half 0
+// of step k+1], so each LDS read and its first use lie in one straight-line
+// body.
 template <int FA, int FB>
-__device__ __forceinline__ void mma(v16f (&acc)[4][4], const Frags& f)
+__device__ __forceinline__ void half0(v4f (&acc)[8][8], const v8i (&bq)[8], const v8i (&alo)[4], v8i (&ahi)[4],
+                                      const uint8_t* stage, int wm, int lane)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mma1<FA, FB>(acc, f, i, j);
-}
-
-// One reduction step on stage `cur` (holding tile kt).  On entry f0 holds the
-// first half-step fragments of tile kt.
-//   first half:  the 16 matrix instructions on f0, interleaved with the LDS
-//                reads of the second half-step fragments (f1) from `cur`;
-//   barrier:     every wave has read all of `cur`, and tile kt+1 has landed in
-//                `nxt`;
-//   second half: the 16 matrix instructions on f1, interleaved with the LDS
-//                reads of the next tile's first fragments (f0, from `nxt`) and
-//                with the 16 loads of tile kt+2 into `cur`.
-// After the last tile the reads of `nxt` return stale data that is never used.
-// Second half of a step: the 16 matrix instructions on f1, each followed by
-// the LDS reads of one next-tile fragment (f0, first eight slots) and one load
-// of tile kt+2.  sched_barrier pins this order, so the reads and the load issue
-// run while the matrix core works.  Past the last tile the loads re-read the
-// last tile into a stage that is not read again (valid addresses, no branch in
-// the loop, which keeps the register allocation flat).
-template <int FA, int FB, bool EDGE>
-__device__ __forceinline__ void second_half(v16f (&acc)[4][4], Frags& f0, const Frags& f1, const Sources& src,
-                                            const uint8_t* nxt, uint32_t cur_addr, int k_issue, int wave,
-                                            int wm, int wn, int lane)
-{
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        mma1<FA, FB>(acc, f1, t & 3, t >> 2);
-        if (t < 8) {
-            if (t < 4) f0.a[t] = read_frag(nxt, 0, t, wm, wn, lane);
-            else f0.b[t - 4] = read_frag(nxt, 0, t, wm, wn, lane);
-        }
-        issue_one<EDGE>(src, cur_addr, k_issue, wave, t);
+    for (int t = 0; t < 32; ++t) {
+        const int j = t >> 2, i = t & 3;
+        mma16<FA, FB>(acc, alo[i], bq[j], i, j);
+        if ((t & 7) == 1) ahi[t >> 3] = read_frag16(stage, wm * 128 + (4 + (t >> 3)) * 16, lane);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// One reduction step on stage `cur` (holding tile kt).  On entry f0 holds the
-// first half-step fragments of tile kt.
-//   first half:  the 16 matrix instructions on f0, interleaved with the LDS
-//                reads of the second half-step fragments (f1) from `cur`;
-//   barrier:     every wave has read all of `cur`, and tile kt+1 has landed in
-//                `nxt`;
-//   second half: as above.
-// After the last tile the reads of `nxt` return stale data that is never used.
-template <int FA, int FB, bool EDGE>
-__device__ __forceinline__ void k_step(v16f (&acc)[4][4], Frags& f0, Frags& f1, const Sources& src,
-                                       const uint8_t* cur, uint32_t cur_addr, const uint8_t* nxt,
-                                       int k_issue, int wave, int wm, int wn, int lane)
+template <int FA, int FB, bool EDGE, bool NEXT>
+__device__ __forceinline__ void half1(v4f (&acc)[8][8], v8i (&bq)[8], v8i (&alo)[4], const v8i (&ahi)[4],
+                                      const Sources& src, uint32_t cur_addr, const uint8_t* nxt, int k_issue,
+                                      int wave, int wm, int wn, int lane)
 {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        mma1<FA, FB>(acc, f0, t & 3, t >> 2);
-        if (t < 8) {
-            if (t < 4) f1.a[t] = read_frag(cur, 1, t, wm, wn, lane);
-            else f1.b[t - 4] = read_frag(cur, 1, t, wm, wn, lane);
+    for (int t = 0; t < 32; ++t) {
+        const int j = t >> 2, i = t & 3;
+        mma16<FA, FB>(acc, ahi[i], bq[j], 4 + i, j);
+        if (NEXT) {
+            if (i == 3) bq[j] = read_frag16(nxt + kStageA, wn * 128 + j * 16, lane);
+            if ((t & 7) == 1) alo[t >> 3] = read_frag16(nxt, wm * 128 + (t >> 3) * 16, lane);
+            if ((t & 1) == 0) issue_one<EDGE>(src, cur_addr, k_issue, wave, t >> 1);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);     // tile kt+1 has landed (this wave's loads)
-    __syncthreads();                          // ... for all waves; `cur` fully read
+}
+
+__device__ __forceinline__ void mid_step_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);     // the next tile has landed (this wave's loads)
+    __syncthreads();                          // ... for all waves; the current stage fully read
     __builtin_amdgcn_sched_barrier(0);
-    second_half<FA, FB, EDGE>(acc, f0, f1, src, nxt, cur_addr, k_issue, wave, wm, wn, lane);
 }
 
 // Output tile of a virtual tile id: grouped raster order (kGroupM tile rows per
@@ -298,8 +268,8 @@ gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
     src.step = 8u * (uint32_t)R;
 
     const int KT = R / kBK;
-    Frags f0, f1;
-    v16f acc[4][4];
+    v8i bq[8], alo[4], ahi[4];
+    v4f acc[8][8];
 
     int v = slot;
     if (v >= ntiles) return;
@@ -309,19 +279,27 @@ gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
     issue_stage<EDGE>(src, lds_addr + kStage, min(1, KT - 1) * kBK, wave);
     for (;;) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 8; ++j)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+                for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
         __builtin_amdgcn_s_waitcnt(kWaitVm16);    // stage 0 landed; stage 1's 16 loads may be in flight
         __syncthreads();
-        read_frags(f0, lds, 0, wm, wn, lane);
-        for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bq[j] = read_frag16(lds + kStageA, wn * 128 + j * 16, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) alo[i] = read_frag16(lds, wm * 128 + i * 16, lane);
+        half0<FA, FB>(acc, bq, alo, ahi, lds, wm, lane);
+        for (int kt = 0; kt + 1 < KT; ++kt) {
             const int cur = kt & 1;
-            k_step<FA, FB, EDGE>(acc, f0, f1, src, lds + cur * kStage, lds_addr + cur * kStage,
-                                 lds + (cur ^ 1) * kStage, min(kt + 2, KT - 1) * kBK, wave, wm, wn, lane);
+            mid_step_barrier();
+            half1<FA, FB, EDGE, true>(acc, bq, alo, ahi, src, lds_addr + cur * kStage, lds + (cur ^ 1) * kStage,
+                                      min(kt + 2, KT - 1) * kBK, wave, wm, wn, lane);
+            half0<FA, FB>(acc, bq, alo, ahi, lds + (cur ^ 1) * kStage, wm, lane);
         }
+        mid_step_barrier();
+        half1<FA, FB, EDGE, false>(acc, bq, alo, ahi, src, 0, lds, 0, wave, wm, wn, lane);
         // every load of this tile has landed and every wave is done with LDS
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __syncthreads();
@@ -341,19 +319,23 @@ gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
         // 256-byte row XOR-swizzled by row), read back 16 bytes per lane and store
         // four full 256-byte row segments per instruction.
         uint8_t* ew = epi + wave * kEpiWave;
+        const int r16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int c2 = 0; c2 < 4; ++c2) {                 // chunk: A blocks 2*c2, 2*c2+1 (32 rows)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int h = 0; h < 2; ++h) {
+                const int i = 2 * c2 + h;
+                const int row = h * 16 + r16;             // row within the chunk
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x2 v01 = {acc[i][j][4 * g] * d, acc[i][j][4 * g + 1] * d};
-                    const f32x2 v23 = {acc[i][j][4 * g + 2] * d, acc[i][j][4 * g + 3] * d};
+                for (int j = 0; j < 8; ++j) {
+                    const f32x2 v01 = {acc[i][j][0] * d, acc[i][j][1] * d};
+                    const f32x2 v23 = {acc[i][j][2] * d, acc[i][j][3] * d};
                     uint2 w;
                     w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
                     w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
-                    const int chunk = (j * 4 + g) ^ (fr & 15);          // logical 16-byte chunk j*4+g
-                    *reinterpret_cast<uint2*>(ew + fr * 256 + chunk * 16 + (lane >> 5) * 8) = w;
+                    // columns j*16 + 4*q4 .. +3 = bytes j*32 + 8*q4: 16-byte chunk 2j + q4/2
+                    const int chunk = (2 * j + (q4 >> 1)) ^ (row & 15);
+                    *reinterpret_cast<uint2*>(ew + row * 256 + chunk * 16 + (q4 & 1) * 8) = w;
                 }
             }
 #pragma unroll
@@ -361,7 +343,7 @@ gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                 const int rr = it * 4 + (lane >> 4);                   // row within the chunk
                 const int c = lane & 15;                              // logical 16-byte chunk
                 const uint4 w = *reinterpret_cast<const uint4*>(ew + rr * 256 + ((c ^ (rr & 15)) * 16));
-                const int m = done.m0 + wm * 128 + i * 32 + rr;
+                const int m = done.m0 + wm * 128 + c2 * 32 + rr;
                 const int n = done.n0 + wn * 128 + c * 8;
                 if (m >= done.ms && m < P && n >= done.ns && n < Q)
                     *reinterpret_cast<uint4*>(out + (size_t)m * Q + n) = w;
