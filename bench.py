@@ -38,7 +38,25 @@ FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA peak
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E peak
 
 # rocprofv3 kernel names of the library's kernels
-GEMM_KERNEL = {(0, 0): "fp8k::gemm_tn_kernel<0, 0>", (1, 0): "fp8k::gemm_tn_kernel<1, 0>"}
+GEMM_KERNEL = {(0, 0): "fp8k::gemm_tn_kernel<0, 0, false>", (1, 0): "fp8k::gemm_tn_kernel<1, 0, false>"}
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_traffic_layer7b.txt")
+GEMM_SOURCE = os.path.join(ROOT, "fp8_precision_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic(kernel):
+    """HBM bytes per dispatch of `kernel` from the committed rocprofv3 PMC summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy of known size), or
+    None when the summary is missing or the GEMM source changed since it was taken."""
+    import hashlib
+    try:
+        line = next(l for l in open(TRAFFIC_SUMMARY) if l.startswith("TRAFFIC_JSON "))
+    except (OSError, StopIteration):
+        return None
+    data = json.loads(line[len("TRAFFIC_JSON "):])
+    if hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()[:16] != data["gemm_source_sha256_16"]:
+        return None
+    b = data["per_dispatch_bytes"].get(kernel)
+    return None if b is None else int(b)
 
 
 class Op:
@@ -287,7 +305,8 @@ def main():
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "gemm_only_tflops": round(gemm_flop / gemm_time / 1e12, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(dom_name),
                      "kernel": dom_name, "launches_per_step": dom["launches"],
                      "avg_launch_us": round(dom["time"] / dom["launches"] * 1e6, 2)},
         "cpu_baseline": cpu,
