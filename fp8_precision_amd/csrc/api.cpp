@@ -124,7 +124,7 @@ fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt, 
     if (any_overlap(r)) return fail(FP8_ERR_INVALID, "fp8_quantize: overlapping buffers");
     if (cols % 16) return fail(FP8_ERR_UNSUPPORTED, "fp8_quantize: cols must be a multiple of 16");
     if (qt && rows % 16) return fail(FP8_ERR_UNSUPPORTED, "fp8_quantize: rows must be a multiple of 16 with qt");
-    if (qt && (rows + 63) / 64 > 65535) return fail(FP8_ERR_UNSUPPORTED, "fp8_quantize: too many rows for qt");
+    if (qt && (rows + 127) / 128 > 65535) return fail(FP8_ERR_UNSUPPORTED, "fp8_quantize: too many rows for qt");
     if (!aligned(x, 16) || (q && !aligned(q, 16)) || (qt && !aligned(qt, 16)) || !aligned(absmax, 4) ||
         (scale && !aligned(scale, 4)) || (inv_scale && !aligned(inv_scale, 4)))
         return fail(FP8_ERR_UNSUPPORTED, "fp8_quantize: misaligned pointer");

@@ -100,24 +100,23 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return v;
 }
 
-// Block-wide max of `v` (blockDim.x == 256) folded into *out.  `out` holds the
-// fp32 bits of a non-negative value (or NaN with the sign bit clear), for which
-// unsigned order equals the magnitude order used by the absmax definition.
-// A block first reads the running maximum and issues its atomicMax only if it
-// would raise it (a stale read is smaller or equal, so the test is safe); this
-// keeps thousands of blocks from serialising on one address.
+// Block-wide max of `v` (blockDim.x a multiple of 64, at most 1024) folded into
+// *out.  `out` holds the fp32 bits of a non-negative value (or NaN with the sign
+// bit clear), for which unsigned order equals the magnitude order used by the
+// absmax definition.  One atomicMax per block: device-scope atomics on one
+// address serialise past the (per-XCD) L2, so launches keep to about one block
+// per CU.  A block first reads the running maximum and skips its atomic if it
+// cannot raise it (a stale read is smaller or equal, so the test is safe).
 __device__ __forceinline__ void block_max_to_global(uint32_t v, uint32_t* out)
 {
-    __shared__ uint32_t part[4];
+    __shared__ uint32_t part[16];
     v = wave_max_u32(v);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     if (lane == 0) part[wave] = v;
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t m = part[0];
-        m = m > part[1] ? m : part[1];
-        m = m > part[2] ? m : part[2];
-        m = m > part[3] ? m : part[3];
+        for (int w = 1; w < nw; ++w) m = m > part[w] ? m : part[w];
         const uint32_t seen = __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (m > seen) atomicMax(out, m);
     }

@@ -44,12 +44,12 @@ __global__ void __launch_bounds__(256) absmax_bf16_kernel(const uint4* __restric
     us2 m = {0, 0};
     const int64_t stride = (int64_t)gridDim.x * 256;
     int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    for (; i + 3 * stride < nvec; i += 4 * stride) {
-        uint4 a = x[i], b = x[i + stride], c = x[i + 2 * stride], d = x[i + 3 * stride];
-        m = absmax_acc(m, a);
-        m = absmax_acc(m, b);
-        m = absmax_acc(m, c);
-        m = absmax_acc(m, d);
+    for (; i + 7 * stride < nvec; i += 8 * stride) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = x[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m = absmax_acc(m, v[u]);
     }
     for (; i < nvec; i += stride) m = absmax_acc(m, x[i]);
     uint32_t r = m.x > m.y ? m.x : m.y;
@@ -64,8 +64,8 @@ hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, hipStream
 {
     const int64_t nvec = n / 8;
     const int ntail = (int)(n - nvec * 8);
-    int64_t blocks = (nvec + 1023) / 1024;       // at least 4 vectors per thread
-    const int64_t cap = (int64_t)device_cu_count() * 4;
+    int64_t blocks = (nvec + 2047) / 2048;       // at least 8 vectors per thread
+    const int64_t cap = (int64_t)device_cu_count();  // one block per CU (one atomic per block)
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     zero_u32_kernel<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax));
@@ -116,13 +116,18 @@ __global__ void __launch_bounds__(256) quantize_flat_kernel(const uint4* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Quantisation with the transposed copy (and optionally the plain one).  A wave
-// owns a 16-row x 512-column tile: lane l reads the 16-byte vector at columns
-// 8l..8l+7 of each of the 16 rows (1 KB per load instruction), converts them,
-// writes its 8 codes per row to q, transposes the 16 x 8 code block in
-// registers (v_perm_b32) and writes 16 consecutive codes (one 16-byte store) to
-// each of its 8 rows of qt.  A block stacks 4 waves on consecutive row groups,
-// so a 64-byte segment of every qt row is written by one block.
+// Quantisation with the transposed copy (and optionally the plain one).  A block
+// of 4 waves owns a 128-row x 256-column tile.  Lane l of wave w converts the
+// 16-byte vectors at columns 8 (l % 32) .. +7 of 16 consecutive rows (row group
+// l / 32 of the wave's 32 rows): every load instruction reads two 512-byte row
+// segments, every q store writes two 256-byte segments.  The lane transposes
+// its 16 x 8 code block in registers (v_perm_b32) into 8 column pieces of 16
+// bytes and parks them in an LDS tile laid out as qt ([256 columns][128 rows],
+// 16-byte pieces XOR-swizzled by column); after a barrier the block writes qt
+// back as full 128-byte row segments.
+constexpr int kQtRows = 128;
+constexpr int kQtCols = 256;
+
 template <int FMT>
 __global__ void __launch_bounds__(256) quantize_t_kernel(const uint8_t* __restrict__ x, int64_t rows,
                                                          int64_t cols, const float* __restrict__ absmax,
@@ -130,55 +135,74 @@ __global__ void __launch_bounds__(256) quantize_t_kernel(const uint8_t* __restri
                                                          float* __restrict__ scale_out,
                                                          float* __restrict__ inv_out)
 {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kQtCols * kQtRows];    // 32 KB
     float s, inv;
     tensor_scale(*absmax, Fmt<FMT>::max, s, inv);
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
         if (scale_out) *scale_out = s;
         if (inv_out) *inv_out = inv;
     }
-    const int lane = threadIdx.x & 63;
-    const int64_t i0 = ((int64_t)blockIdx.y * 4 + (threadIdx.x >> 6)) * 16;
-    const int64_t j = (int64_t)blockIdx.x * 512 + lane * 8;
-    if (i0 >= rows || j >= cols) return;
-
-    uint4 v[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-        v[r] = *reinterpret_cast<const uint4*>(x + ((i0 + r) * cols + j) * 2);
-    uint32_t lo[16], hi[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        uint2 c = quant8<FMT>(v[r], s);
-        lo[r] = c.x;
-        hi[r] = c.y;
-    }
-    if (q) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t tr = (int64_t)blockIdx.y * kQtRows, tc = (int64_t)blockIdx.x * kQtCols;
+    const int rt = wave * 32 + (lane >> 5) * 16;          // first row of the lane within the tile
+    const int ct = (lane & 31) * 8;                       // first column of the lane within the tile
+    const bool active = tr + rt < rows && tc + ct < cols;
+    if (active) {
+        const int64_t i0 = tr + rt, j = tc + ct;
+        uint4 v[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            *reinterpret_cast<uint2*>(q + (i0 + r) * cols + j) = make_uint2(lo[r], hi[r]);
-    }
-    if (qt) {
+            v[r] = *reinterpret_cast<const uint4*>(x + ((i0 + r) * cols + j) * 2);
+        uint32_t lo[16], hi[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint2 c = quant8<FMT>(v[r], s);
+            lo[r] = c.x;
+            hi[r] = c.y;
+        }
+        if (q) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                *reinterpret_cast<uint2*>(q + (i0 + r) * cols + j) = make_uint2(lo[r], hi[r]);
+        }
         uint32_t w[8][4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            transpose4x4(lo[4 * g], lo[4 * g + 1], lo[4 * g + 2], lo[4 * g + 3],
-                         w[0][g], w[1][g], w[2][g], w[3][g]);
-            transpose4x4(hi[4 * g], hi[4 * g + 1], hi[4 * g + 2], hi[4 * g + 3],
-                         w[4][g], w[5][g], w[6][g], w[7][g]);
+            transpose4x4(lo[4 * g], lo[4 * g + 1], lo[4 * g + 2], lo[4 * g + 3], w[0][g], w[1][g], w[2][g], w[3][g]);
+            transpose4x4(hi[4 * g], hi[4 * g + 1], hi[4 * g + 2], hi[4 * g + 3], w[4][g], w[5][g], w[6][g], w[7][g]);
         }
+        const int piece = rt >> 4;                        // 16-byte piece of the 128-byte qt row
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            *reinterpret_cast<uint4*>(qt + (j + k) * rows + i0) = make_uint4(w[k][0], w[k][1], w[k][2], w[k][3]);
+        for (int k = 0; k < 8; ++k) {
+            const int col = ct + k;
+            const int phys = piece ^ ((col >> 3) & 7);
+            *reinterpret_cast<uint4*>(tile + col * kQtRows + phys * 16) = make_uint4(w[k][0], w[k][1], w[k][2], w[k][3]);
+        }
+    }
+    __syncthreads();
+    // write-back: 2048 pieces of 16 bytes, 8 per thread; a wave instruction
+    // covers 8 qt rows x 128 bytes
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int id = u * 256 + threadIdx.x;
+        const int col = id >> 3, p = id & 7;
+        const int64_t qrow = tc + col, qcol = tr + p * 16;
+        if (qrow < cols && qcol < rows) {
+            const int phys = p ^ ((col >> 3) & 7);
+            *reinterpret_cast<uint4*>(qt + qrow * rows + qcol) =
+                *reinterpret_cast<const uint4*>(tile + col * kQtRows + phys * 16);
+        }
     }
 }
 
+// Plain quantisation only: the flat kernel above; with qt: the tile kernel.
 template <int FMT>
 static void launch_quantize_fmt(const void* x, int64_t rows, int64_t cols, const float* absmax,
                                 uint8_t* q, uint8_t* qt, float* scale, float* inv_scale,
                                 hipStream_t stream)
 {
     if (qt) {
-        dim3 grid((unsigned)((cols + 511) / 512), (unsigned)((rows + 63) / 64));
+        dim3 grid((unsigned)((cols + kQtCols - 1) / kQtCols), (unsigned)((rows + kQtRows - 1) / kQtRows));
         quantize_t_kernel<FMT><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(x), rows, cols,
                                                          absmax, q, qt, scale, inv_scale);
     } else {

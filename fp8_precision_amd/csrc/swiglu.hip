@@ -135,7 +135,7 @@ __device__ __forceinline__ RowItems row_items(int64_t M, int64_t F)
 }
 
 // Forward pass 1: absmax of h over the whole [M, F] output (no output written).
-__global__ void __launch_bounds__(256) swiglu_absmax_kernel(const uint16_t* __restrict__ gu, int64_t M,
+__global__ void __launch_bounds__(1024) swiglu_absmax_kernel(const uint16_t* __restrict__ gu, int64_t M,
                                                             int64_t F, uint32_t* __restrict__ out)
 {
     __shared__ float tbl[kTable];
@@ -143,7 +143,8 @@ __global__ void __launch_bounds__(256) swiglu_absmax_kernel(const uint16_t* __re
     const RowItems it = row_items(M, F);
     const int lane = threadIdx.x & 63;
     uint32_t m = 0;
-    for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < it.total; w += (int64_t)gridDim.x * 4) {
+    const int wpb = blockDim.x >> 6;
+    for (int64_t w = (int64_t)blockIdx.x * wpb + (threadIdx.x >> 6); w < it.total; w += (int64_t)gridDim.x * wpb) {
         const int64_t i = w / it.chunks;
         const int64_t jb = (w - i * it.chunks) * 1024 + lane * 8;
         const uint16_t* grow = gu + i * 2 * F;
@@ -193,55 +194,81 @@ __global__ void __launch_bounds__(256) swiglu_quant_kernel(const uint16_t* __res
     }
 }
 
-// Requantisation with the transposed copy hqt [F, M] (and optionally hq): a wave
-// owns 16 rows x 512 columns, lane l columns 8l..8l+7 of each row, as in the
-// transposing quantise kernel.  Blocks are persistent and walk 64-row x
-// 512-column tiles, so the table is copied into LDS once per block.
+// Requantisation with the transposed copy hqt [F, M] (and optionally hq).
+// Persistent blocks of 4 waves walk 128-row x 256-column tiles of h: lane l of
+// wave w handles columns 8 (l % 32) .. +7 of 16 consecutive rows (row group
+// l / 32 of the wave's 32 rows), as the transposing quantise kernel does; the
+// transposed 16 x 8 code blocks are parked in an LDS tile laid out as hqt
+// ([256 columns][128 rows], 16-byte pieces XOR-swizzled by column) and written
+// back as full 128-byte row segments.
+constexpr int kHtRows = 128;
+constexpr int kHtCols = 256;
+
 __global__ void __launch_bounds__(256) swiglu_quant_t_kernel(const uint16_t* __restrict__ gu, int64_t M,
                                                              int64_t F, const float* __restrict__ absmax_h,
                                                              uint8_t* __restrict__ hq, uint8_t* __restrict__ hqt,
                                                              float* __restrict__ inv_out)
 {
     __shared__ float tbl[kTable];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kHtCols * kHtRows];   // 32 KB
     float s, inv;
     tensor_scale(*absmax_h, kMaxE4M3, s, inv);
     if (blockIdx.x == 0 && threadIdx.x == 0 && inv_out) *inv_out = inv;
     load_table_to_lds(tbl);
-    const int lane = threadIdx.x & 63;
-    const int64_t tiles_j = (F + 511) / 512;
-    const int64_t tiles = tiles_j * ((M + 63) / 64);
-    for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-        const int64_t ti = tile / tiles_j;
-        const int64_t i0 = (ti * 4 + (threadIdx.x >> 6)) * 16;
-        const int64_t j = (tile - ti * tiles_j) * 512 + lane * 8;
-        if (i0 >= M || j >= F) continue;
-
-        uint32_t lo[16], hi[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rt = wave * 32 + (lane >> 5) * 16;          // first row of the lane within the tile
+    const int ct = (lane & 31) * 8;                       // first column of the lane within the tile
+    const int64_t tiles_c = (F + kHtCols - 1) / kHtCols;
+    const int64_t tiles = tiles_c * ((M + kHtRows - 1) / kHtRows);
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const int64_t tr = (t / tiles_c) * kHtRows, tc = (t % tiles_c) * kHtCols;
+        if (tr + rt < M && tc + ct < F) {
+            const int64_t i0 = tr + rt, j = tc + ct;
+            uint32_t lo[16], hi[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const uint16_t* grow = gu + (i0 + r) * 2 * F;
-            const uint4 gw = *reinterpret_cast<const uint4*>(grow + j);
-            const uint4 uw = *reinterpret_cast<const uint4*>(grow + F + j);
-            float h[8];
-            swiglu8(tbl, gw, uw, h);
-            const uint2 c = quant8_h(h, s);
-            lo[r] = c.x;
-            hi[r] = c.y;
+            for (int r = 0; r < 16; ++r) {
+                const uint16_t* grow = gu + (i0 + r) * 2 * F;
+                const uint4 gw = *reinterpret_cast<const uint4*>(grow + j);
+                const uint4 uw = *reinterpret_cast<const uint4*>(grow + F + j);
+                float h[8];
+                swiglu8(tbl, gw, uw, h);
+                const uint2 c = quant8_h(h, s);
+                lo[r] = c.x;
+                hi[r] = c.y;
+            }
+            if (hq) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    *reinterpret_cast<uint2*>(hq + (i0 + r) * F + j) = make_uint2(lo[r], hi[r]);
+            }
+            uint32_t w[8][4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                transpose4x4(lo[4 * g], lo[4 * g + 1], lo[4 * g + 2], lo[4 * g + 3], w[0][g], w[1][g], w[2][g], w[3][g]);
+                transpose4x4(hi[4 * g], hi[4 * g + 1], hi[4 * g + 2], hi[4 * g + 3], w[4][g], w[5][g], w[6][g], w[7][g]);
+            }
+            const int piece = rt >> 4;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int col = ct + k;
+                const int phys = piece ^ ((col >> 3) & 7);
+                *reinterpret_cast<uint4*>(tile + col * kHtRows + phys * 16) =
+                    make_uint4(w[k][0], w[k][1], w[k][2], w[k][3]);
+            }
         }
-        if (hq) {
+        __syncthreads();
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                *reinterpret_cast<uint2*>(hq + (i0 + r) * F + j) = make_uint2(lo[r], hi[r]);
+        for (int u = 0; u < 8; ++u) {
+            const int id = u * 256 + threadIdx.x;
+            const int col = id >> 3, p = id & 7;
+            const int64_t qrow = tc + col, qcol = tr + p * 16;
+            if (qrow < F && qcol < M) {
+                const int phys = p ^ ((col >> 3) & 7);
+                *reinterpret_cast<uint4*>(hqt + qrow * M + qcol) =
+                    *reinterpret_cast<const uint4*>(tile + col * kHtRows + phys * 16);
+            }
         }
-        uint32_t w[8][4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            transpose4x4(lo[4 * g], lo[4 * g + 1], lo[4 * g + 2], lo[4 * g + 3], w[0][g], w[1][g], w[2][g], w[3][g]);
-            transpose4x4(hi[4 * g], hi[4 * g + 1], hi[4 * g + 2], hi[4 * g + 3], w[4][g], w[5][g], w[6][g], w[7][g]);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            *reinterpret_cast<uint4*>(hqt + (j + k) * M + i0) = make_uint4(w[k][0], w[k][1], w[k][2], w[k][3]);
+        __syncthreads();     // the tile is rewritten by the next iteration
     }
 }
 
@@ -263,11 +290,15 @@ hipError_t launch_swiglu_requant(const void* gu, int64_t M, int64_t F, float* ab
     if (blocks < 1) blocks = 1;
     if (compute_absmax) {
         zero_u32_kernel_sw<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax_h));
-        swiglu_absmax_kernel<<<(unsigned)blocks, 256, 0, stream>>>(g, M, F, reinterpret_cast<uint32_t*>(absmax_h));
+        // one 1024-thread block per CU: one atomic per CU, the table copied once per CU
+        int64_t ablocks = (items + 15) / 16;
+        if (ablocks > device_cu_count()) ablocks = device_cu_count();
+        swiglu_absmax_kernel<<<(unsigned)ablocks, 1024, 0, stream>>>(g, M, F, reinterpret_cast<uint32_t*>(absmax_h));
     }
     if (hqt) {
-        int64_t tblocks = ((F + 511) / 512) * ((M + 63) / 64);
-        if (tblocks > cap) tblocks = cap;
+        // 34 KB table + 32 KB tile per block: two blocks per CU
+        int64_t tblocks = ((F + kHtCols - 1) / kHtCols) * ((M + kHtRows - 1) / kHtRows);
+        if (tblocks > 2 * (int64_t)device_cu_count()) tblocks = 2 * (int64_t)device_cu_count();
         swiglu_quant_t_kernel<<<(unsigned)tblocks, 256, 0, stream>>>(g, M, F, absmax_h, hq, hqt, inv_scale_h);
     } else {
         swiglu_quant_kernel<<<(unsigned)blocks, 256, 0, stream>>>(g, M, F, absmax_h, hq, inv_scale_h);
