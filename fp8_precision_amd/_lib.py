@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8_precision.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m fp8_precision_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python fp8_precision_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -33,6 +33,7 @@ _SIGS = {
     "fp8_gemm_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_gemm_dgrad": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_gemm_wgrad": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "fp8_gemm_backward": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -198,3 +199,19 @@ def gemm_wgrad(dyqt, dy_fmt, xqt, inv_sdy, inv_sx, out=None) -> torch.Tensor:
     _check("fp8_gemm_wgrad", _lib.fp8_gemm_wgrad(_ptr(dyqt), int(dy_fmt), _ptr(xqt), _ptr(inv_sdy), _ptr(inv_sx),
                                                  _ptr(out), M, N, K, _stream(dyqt)))
     return out
+
+
+def gemm_backward(dyq, dyqt, dy_fmt, wqt, xqt, inv_sdy, inv_sw, inv_sx, dx=None, dw=None):
+    """dgrad and wgrad of one linear in one launch: returns (dX [M, K], dW [N, K])."""
+    for t, n in ((dyq, "dyq"), (dyqt, "dyqt"), (wqt, "wqt"), (xqt, "xqt")):
+        _dev_tensor(t, n, torch.uint8)
+    M, N = dyq.shape
+    K = wqt.shape[0]
+    if tuple(dyqt.shape) != (N, M) or wqt.shape[1] != N or tuple(xqt.shape) != (K, M):
+        raise ValueError("expected dyq [M, N], dyqt [N, M], wqt [K, N], xqt [K, M]")
+    dx = _out_bf16(dx, (M, K), dyq.device)
+    dw = _out_bf16(dw, (N, K), dyq.device)
+    _check("fp8_gemm_backward", _lib.fp8_gemm_backward(_ptr(dyq), _ptr(dyqt), int(dy_fmt), _ptr(wqt), _ptr(xqt),
+                                                       _ptr(inv_sdy), _ptr(inv_sw), _ptr(inv_sx), _ptr(dx), _ptr(dw),
+                                                       M, N, K, _stream(dyq)))
+    return dx, dw

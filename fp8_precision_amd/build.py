@@ -1,6 +1,7 @@
 """Build the gfx950 HIP library ``libfp8_precision.so`` in-tree with hipcc.
 
-Usage: ``python -m fp8_precision_amd.build`` (or ``build()`` from Python).
+Usage: ``python fp8_precision_amd/build.py`` (or ``build()`` from Python).  Run it as
+a script: importing the package loads the library this file builds.
 Every call recompiles.  Compilation runs on the CPU; no GPU is needed.
 """
 from __future__ import annotations

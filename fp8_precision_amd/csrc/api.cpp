@@ -231,4 +231,27 @@ fp8_status fp8_gemm_wgrad(const uint8_t* dyqt, fp8_fmt dy_fmt, const uint8_t* xq
     return FP8_OK;
 }
 
+fp8_status fp8_gemm_backward(const uint8_t* dyq, const uint8_t* dyqt, fp8_fmt dy_fmt, const uint8_t* wqt,
+                             const uint8_t* xqt, const float* inv_sdy, const float* inv_sw, const float* inv_sx,
+                             void* dx, void* dw, int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    t_last_error.clear();
+    fp8_status st = gemm_common("fp8_gemm_backward (dgrad)", dyq, (int)dy_fmt, wqt, inv_sdy, inv_sw, dx, M, K, N, stream);
+    if (st != FP8_OK) return st;
+    st = gemm_common("fp8_gemm_backward (wgrad)", dyqt, (int)dy_fmt, xqt, inv_sdy, inv_sx, dw, N, K, M, stream);
+    if (st != FP8_OK) return st;
+    const Range outs[] = {{dx, 2 * M * K}, {dw, 2 * N * K}};
+    const Range ins[] = {{dyq, M * N}, {dyqt, M * N}, {wqt, K * N}, {xqt, K * M},
+                         {inv_sdy, 4}, {inv_sw, 4}, {inv_sx, 4}};
+    if (overlap(dx, 2 * M * K, dw, 2 * N * K))
+        return fail(FP8_ERR_INVALID, "fp8_gemm_backward: dx and dw overlap");
+    for (const Range& o : outs)
+        for (const Range& i : ins)
+            if (overlap(o.p, o.n, i.p, i.n)) return fail(FP8_ERR_INVALID, "fp8_gemm_backward: an output overlaps an input");
+    hipError_t e = fp8k::launch_gemm_tn_pair(dyq, wqt, inv_sdy, inv_sw, dx, M, K, N, dyqt, xqt, inv_sdy, inv_sx, dw,
+                                             N, K, M, (int)dy_fmt, 0, stream);
+    if (e != hipSuccess) return fail_hip("fp8_gemm_backward", e);
+    return FP8_OK;
+}
+
 }  // extern "C"

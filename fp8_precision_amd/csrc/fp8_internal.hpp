@@ -25,4 +25,10 @@ hipError_t launch_gemm_tn(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt
                           const float* inv_a, const float* inv_b, void* out,
                           int64_t P, int64_t Q, int64_t R, hipStream_t stream);
 
+// Two independent products of the same operand formats in one launch.
+hipError_t launch_gemm_tn_pair(const uint8_t* A0, const uint8_t* B0, const float* ia0, const float* ib0, void* out0,
+                               int64_t P0, int64_t Q0, int64_t R0, const uint8_t* A1, const uint8_t* B1,
+                               const float* ia1, const float* ib1, void* out1, int64_t P1, int64_t Q1, int64_t R1,
+                               int fmt_a, int fmt_b, hipStream_t stream);
+
 }  // namespace fp8k

@@ -195,60 +195,105 @@ __device__ __forceinline__ void mid_step_barrier()
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Output tile of a virtual tile id: grouped raster order (kGroupM tile rows per
-// group, column-major within a group), so consecutive ids share A and B panels.
-struct Tile {
+// A launch covers a group of up to kMaxGroup independent problems of the same
+// operand formats (e.g. the dgrad and wgrad products of one linear).  Their
+// tiles form one virtual tile range, problem after problem; the host orders
+// the problems by reduction length, longest first, so that the round-robin
+// walk of the persistent workgroups starts with the longest tiles.
+constexpr int kMaxGroup = 2;
+
+struct GemmProblem {
+    const uint8_t* A;
+    const uint8_t* B;
+    const float* inv_a;
+    const float* inv_b;
+    uint16_t* out;
+    int P, Q, R;
+    int tiles_m, tiles_n;
+    int first_tile;
+};
+
+struct GemmGroup {
+    GemmProblem p[kMaxGroup];
+    int count;
+    int total_tiles;
+};
+
+// Everything a workgroup needs about its current tile (all wave-uniform).
+struct Work {
+    const uint8_t* A;
+    const uint8_t* B;
+    uint16_t* out;
+    const float* inv_a;
+    const float* inv_b;
+    int P, Q, R, KT;
     int ms, ns;     // logical origin (first row / column this tile stores)
     int m0, n0;     // origin actually computed (shifted back inside the matrix)
 };
 
+// Output tile of a virtual tile id: the problem it falls in, then a grouped
+// raster order within it (kGroupM tile rows per group, column-major within a
+// group), so consecutive ids share A and B panels.
 template <bool EDGE>
-__device__ __forceinline__ Tile tile_of(int v, int P, int Q, int tiles_m, int tiles_n)
+__device__ __forceinline__ Work work_of(const GemmGroup& g, int v)
 {
-    const int group_size = kGroupM * tiles_n;
-    const int group = v / group_size;
+    const bool second = g.count > 1 && v >= g.p[1].first_tile;
+    const GemmProblem& pr = second ? g.p[1] : g.p[0];
+    Work w;
+    w.A = pr.A;
+    w.B = pr.B;
+    w.out = pr.out;
+    w.inv_a = pr.inv_a;
+    w.inv_b = pr.inv_b;
+    w.P = pr.P;
+    w.Q = pr.Q;
+    w.R = pr.R;
+    w.KT = pr.R / kBK;
+    const int lv = v - pr.first_tile;
+    const int group_size = kGroupM * pr.tiles_n;
+    const int group = lv / group_size;
     const int first_m = group * kGroupM;
-    const int gm = min(tiles_m - first_m, kGroupM);
-    const int in_group = v - group * group_size;
-    Tile t;
-    t.ms = (first_m + in_group % gm) * kBM;
-    t.ns = (in_group / gm) * kBN;
+    const int gm = min(pr.tiles_m - first_m, kGroupM);
+    const int in_group = lv - group * group_size;
+    w.ms = (first_m + in_group % gm) * kBM;
+    w.ns = (in_group / gm) * kBN;
     // A last partial tile is shifted back to end at the matrix edge (P, Q >= 256),
     // recomputing rows / columns of its neighbour that it then does not store.
-    t.m0 = EDGE ? t.ms : min(t.ms, P - kBM);
-    t.n0 = EDGE ? t.ns : min(t.ns, Q - kBN);
-    return t;
+    w.m0 = EDGE ? w.ms : min(w.ms, w.P - kBM);
+    w.n0 = EDGE ? w.ns : min(w.ns, w.Q - kBN);
+    return w;
 }
 
-__device__ __forceinline__ void set_sources(Sources& src, const Tile& t, int wave, int lane, int R)
+__device__ __forceinline__ void set_sources(Sources& src, const Work& w, int wave, int lane)
 {
-    src.a_row = t.m0 + wave * 64 + (lane >> 3);
-    src.b_row = t.n0 + wave * 64 + (lane >> 3);
+    src.a = w.A;
+    src.b = w.B;
+    src.a_last = w.P - 1;
+    src.b_last = w.Q - 1;
+    src.step = 8u * (uint32_t)w.R;
+    src.a_row = w.m0 + wave * 64 + (lane >> 3);
+    src.b_row = w.n0 + wave * 64 + (lane >> 3);
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
         const int row = (wave * 8 + par) * 8 + (lane >> 3);     // row within the tile
         src.chunk16[par] = (uint32_t)(((lane & 7) ^ swz(row)) * 16);
-        src.a_off[par] = (uint32_t)src.a_row * (uint32_t)R + src.chunk16[par];
-        src.b_off[par] = (uint32_t)src.b_row * (uint32_t)R + src.chunk16[par];
+        src.a_off[par] = (uint32_t)src.a_row * (uint32_t)w.R + src.chunk16[par];
+        src.b_off[par] = (uint32_t)src.b_row * (uint32_t)w.R + src.chunk16[par];
     }
 }
 
-// Persistent kernel: one workgroup per CU walks the tiles v = slot, slot + G,
-// slot + 2G, ... where slot renumbers the workgroups XCD-major (workgroups are
-// dealt round-robin to the 8 XCDs, each with its own L2), so in every round
-// the 32 CUs of one XCD work on 32 consecutive tiles of the raster order.
-// While a tile's epilogue stores run, the first two stages of the next tile
-// are already loading.
+// Persistent kernel: one workgroup per CU walks the virtual tiles v = slot,
+// slot + G, slot + 2G, ... where slot renumbers the workgroups XCD-major
+// (workgroups are dealt round-robin to the 8 XCDs, each with its own L2), so in
+// every round the 32 CUs of one XCD work on 32 consecutive tiles of the raster
+// order.  While a tile's epilogue stores run, the first two stages of the next
+// tile are already loading.
 template <int FA, int FB, bool EDGE>
-__global__ void __launch_bounds__(256, 1)
-gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
-               const float* __restrict__ inv_a, const float* __restrict__ inv_b,
-               uint16_t* __restrict__ out, int P, int Q, int R, int tiles_m, int tiles_n)
+__global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
     __shared__ __attribute__((aligned(1024))) uint8_t epi[4 * kEpiWave];
 
-    const int ntiles = tiles_m * tiles_n;
     const int G = gridDim.x;
     int slot = blockIdx.x;
     if (G % 8 == 0) slot = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
@@ -257,26 +302,17 @@ gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
-    const int fr = lane & 31;
-    const float d = inv_a[0] * inv_b[0];
 
     Sources src;
-    src.a = A;
-    src.b = B;
-    src.a_last = P - 1;
-    src.b_last = Q - 1;
-    src.step = 8u * (uint32_t)R;
-
-    const int KT = R / kBK;
     v8i bq[8], alo[4], ahi[4];
     v4f acc[8][8];
 
     int v = slot;
-    if (v >= ntiles) return;
-    Tile t = tile_of<EDGE>(v, P, Q, tiles_m, tiles_n);
-    set_sources(src, t, wave, lane, R);
+    if (v >= g.total_tiles) return;
+    Work w = work_of<EDGE>(g, v);
+    set_sources(src, w, wave, lane);
     issue_stage<EDGE>(src, lds_addr, 0, wave);
-    issue_stage<EDGE>(src, lds_addr + kStage, min(1, KT - 1) * kBK, wave);
+    issue_stage<EDGE>(src, lds_addr + kStage, min(1, w.KT - 1) * kBK, wave);
     for (;;) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -291,6 +327,7 @@ gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
 #pragma unroll
         for (int i = 0; i < 4; ++i) alo[i] = read_frag16(lds, wm * 128 + i * 16, lane);
         half0<FA, FB>(acc, bq, alo, ahi, lds, wm, lane);
+        const int KT = w.KT;
         for (int kt = 0; kt + 1 < KT; ++kt) {
             const int cur = kt & 1;
             mid_step_barrier();
@@ -304,20 +341,21 @@ gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __syncthreads();
 
-        const Tile done = t;
+        const Work done = w;
         const int next = v + G;
-        if (next < ntiles) {
+        if (next < g.total_tiles) {
             v = next;
-            t = tile_of<EDGE>(v, P, Q, tiles_m, tiles_n);
-            set_sources(src, t, wave, lane, R);
+            w = work_of<EDGE>(g, v);
+            set_sources(src, w, wave, lane);
             issue_stage<EDGE>(src, lds_addr, 0, wave);
-            issue_stage<EDGE>(src, lds_addr + kStage, min(1, KT - 1) * kBK, wave);
+            issue_stage<EDGE>(src, lds_addr + kStage, min(1, w.KT - 1) * kBK, wave);
         }
 
         // ---- epilogue of `done`: descale and round to bf16, stage 32-row chunks of
         // the wave's 128 x 128 tile in its private LDS region (16-byte chunks of a
         // 256-byte row XOR-swizzled by row), read back 16 bytes per lane and store
         // four full 256-byte row segments per instruction.
+        const float d = done.inv_a[0] * done.inv_b[0];
         uint8_t* ew = epi + wave * kEpiWave;
         const int r16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
@@ -330,58 +368,101 @@ gemm_tn_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                 for (int j = 0; j < 8; ++j) {
                     const f32x2 v01 = {acc[i][j][0] * d, acc[i][j][1] * d};
                     const f32x2 v23 = {acc[i][j][2] * d, acc[i][j][3] * d};
-                    uint2 w;
-                    w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
-                    w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
+                    uint2 o;
+                    o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
+                    o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
                     // columns j*16 + 4*q4 .. +3 = bytes j*32 + 8*q4: 16-byte chunk 2j + q4/2
                     const int chunk = (2 * j + (q4 >> 1)) ^ (row & 15);
-                    *reinterpret_cast<uint2*>(ew + row * 256 + chunk * 16 + (q4 & 1) * 8) = w;
+                    *reinterpret_cast<uint2*>(ew + row * 256 + chunk * 16 + (q4 & 1) * 8) = o;
                 }
             }
 #pragma unroll
             for (int it = 0; it < kEpiRows / 4; ++it) {
                 const int rr = it * 4 + (lane >> 4);                   // row within the chunk
                 const int c = lane & 15;                              // logical 16-byte chunk
-                const uint4 w = *reinterpret_cast<const uint4*>(ew + rr * 256 + ((c ^ (rr & 15)) * 16));
+                const uint4 o = *reinterpret_cast<const uint4*>(ew + rr * 256 + ((c ^ (rr & 15)) * 16));
                 const int m = done.m0 + wm * 128 + c2 * 32 + rr;
                 const int n = done.n0 + wn * 128 + c * 8;
-                if (m >= done.ms && m < P && n >= done.ns && n < Q)
-                    *reinterpret_cast<uint4*>(out + (size_t)m * Q + n) = w;
+                if (m >= done.ms && m < done.P && n >= done.ns && n < done.Q)
+                    *reinterpret_cast<uint4*>(done.out + (size_t)m * done.Q + n) = o;
             }
         }
         // The loop-top wait (vmcnt <= 16) then proves the next tile's first stage
         // has landed: if one of its loads were pending, the 16 later loads of the
         // second stage would be too (loads complete in order), whatever the
         // interleaved stores do.
-        if (next >= ntiles) break;
+        if (next >= g.total_tiles) break;
     }
 }
 
-template <int FA, int FB>
-static hipError_t launch_fmt(const uint8_t* A, const uint8_t* B, const float* inv_a, const float* inv_b,
-                             void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream)
+static GemmProblem make_problem(const uint8_t* A, const uint8_t* B, const float* inv_a, const float* inv_b,
+                                void* out, int64_t P, int64_t Q, int64_t R)
 {
-    const int tiles_m = (int)((P + kBM - 1) / kBM);
-    const int tiles_n = (int)((Q + kBN - 1) / kBN);
-    const int ntiles = tiles_m * tiles_n;
-    const int grid = ntiles < device_cu_count() ? ntiles : device_cu_count();   // one workgroup per CU
-    uint16_t* o = reinterpret_cast<uint16_t*>(out);
-    if (P >= kBM && Q >= kBN)
-        gemm_tn_kernel<FA, FB, false><<<grid, 256, 0, stream>>>(A, B, inv_a, inv_b, o, (int)P, (int)Q, (int)R,
-                                                                tiles_m, tiles_n);
+    GemmProblem p;
+    p.A = A;
+    p.B = B;
+    p.inv_a = inv_a;
+    p.inv_b = inv_b;
+    p.out = reinterpret_cast<uint16_t*>(out);
+    p.P = (int)P;
+    p.Q = (int)Q;
+    p.R = (int)R;
+    p.tiles_m = (int)((P + kBM - 1) / kBM);
+    p.tiles_n = (int)((Q + kBN - 1) / kBN);
+    p.first_tile = 0;
+    return p;
+}
+
+template <int FA, int FB>
+static hipError_t launch_group(GemmGroup g, hipStream_t stream)
+{
+    bool edge = false;
+    int total = 0;
+    for (int i = 0; i < g.count; ++i) {
+        g.p[i].first_tile = total;
+        total += g.p[i].tiles_m * g.p[i].tiles_n;
+        edge = edge || g.p[i].P < kBM || g.p[i].Q < kBN;
+    }
+    g.total_tiles = total;
+    const int grid = total < device_cu_count() ? total : device_cu_count();   // one workgroup per CU
+    if (!edge)
+        gemm_tn_kernel<FA, FB, false><<<grid, 256, 0, stream>>>(g);
     else
-        gemm_tn_kernel<FA, FB, true><<<grid, 256, 0, stream>>>(A, B, inv_a, inv_b, o, (int)P, (int)Q, (int)R,
-                                                               tiles_m, tiles_n);
+        gemm_tn_kernel<FA, FB, true><<<grid, 256, 0, stream>>>(g);
     return hipGetLastError();
+}
+
+static hipError_t dispatch(int fmt_a, int fmt_b, const GemmGroup& g, hipStream_t stream)
+{
+    if (fmt_a == 0 && fmt_b == 0) return launch_group<0, 0>(g, stream);
+    if (fmt_a == 1 && fmt_b == 0) return launch_group<1, 0>(g, stream);
+    if (fmt_a == 0 && fmt_b == 1) return launch_group<0, 1>(g, stream);
+    return launch_group<1, 1>(g, stream);
 }
 
 hipError_t launch_gemm_tn(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* inv_a,
                           const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream)
 {
-    if (fmt_a == 0 && fmt_b == 0) return launch_fmt<0, 0>(A, B, inv_a, inv_b, out, P, Q, R, stream);
-    if (fmt_a == 1 && fmt_b == 0) return launch_fmt<1, 0>(A, B, inv_a, inv_b, out, P, Q, R, stream);
-    if (fmt_a == 0 && fmt_b == 1) return launch_fmt<0, 1>(A, B, inv_a, inv_b, out, P, Q, R, stream);
-    return launch_fmt<1, 1>(A, B, inv_a, inv_b, out, P, Q, R, stream);
+    GemmGroup g;
+    g.p[0] = make_problem(A, B, inv_a, inv_b, out, P, Q, R);
+    g.p[1] = g.p[0];
+    g.count = 1;
+    return dispatch(fmt_a, fmt_b, g, stream);
+}
+
+hipError_t launch_gemm_tn_pair(const uint8_t* A0, const uint8_t* B0, const float* ia0, const float* ib0, void* out0,
+                               int64_t P0, int64_t Q0, int64_t R0, const uint8_t* A1, const uint8_t* B1,
+                               const float* ia1, const float* ib1, void* out1, int64_t P1, int64_t Q1, int64_t R1,
+                               int fmt_a, int fmt_b, hipStream_t stream)
+{
+    GemmGroup g;
+    GemmProblem p0 = make_problem(A0, B0, ia0, ib0, out0, P0, Q0, R0);
+    GemmProblem p1 = make_problem(A1, B1, ia1, ib1, out1, P1, Q1, R1);
+    // longest reduction first: the first round then starts the longest tiles
+    g.p[0] = R1 > R0 ? p1 : p0;
+    g.p[1] = R1 > R0 ? p0 : p1;
+    g.count = 2;
+    return dispatch(fmt_a, fmt_b, g, stream);
 }
 
 }  // namespace fp8k

@@ -155,6 +155,25 @@ fp8_status fp8_gemm_wgrad(const uint8_t* dyqt, fp8_fmt dy_fmt, const uint8_t* xq
                           const float* inv_sdy, const float* inv_sx, void* dw,
                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/*
+ * Both backward products of one linear in a single launch: dgrad
+ * dX[M, K] = dY[M, N] . W[N, K] and wgrad dW[N, K] = dY[M, N]^T . X[M, K] are
+ * independent, so one persistent launch runs both tile sets, longest
+ * reduction first (LLMQ summary, section 4: the backward pass and its
+ * transposed operands; large models are dominated by these products).  The
+ * operands are those of fp8_gemm_dgrad (dyq, wqt) and fp8_gemm_wgrad (dyqt,
+ * xqt) and both outputs are bit-identical to those two calls; the launch
+ * pays the per-launch costs (first-stage fill, last-round epilogue) once.
+ *
+ *   dyq [M, N], dyqt [N, M]  (dy_fmt);  wqt [K, N], xqt [K, M]  (e4m3)
+ *   dx  bf16 [M, K],  dw bf16 [N, K]  (must not overlap each other or any input)
+ * Constraints: those of fp8_gemm_dgrad and fp8_gemm_wgrad.
+ */
+fp8_status fp8_gemm_backward(const uint8_t* dyq, const uint8_t* dyqt, fp8_fmt dy_fmt,
+                             const uint8_t* wqt, const uint8_t* xqt,
+                             const float* inv_sdy, const float* inv_sw, const float* inv_sx,
+                             void* dx, void* dw, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

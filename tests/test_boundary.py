@@ -22,7 +22,7 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        pytest.fail(f"{LIB} not built: run `python -m fp8_precision_amd.build`")
+        pytest.fail(f"{LIB} not built: run `python fp8_precision_amd/build.py`")
     lib = ctypes.CDLL(LIB)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     lib.fp8_absmax.argtypes = [vp, i64, vp, vp]
@@ -42,7 +42,7 @@ def lib():
 def test_header_declares_the_hot_path():
     names = declared_functions()
     for want in ("fp8_absmax", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd", "fp8_gemm_dgrad",
-                 "fp8_gemm_wgrad", "fp8_status_string", "fp8_last_error"):
+                 "fp8_gemm_wgrad", "fp8_gemm_backward", "fp8_status_string", "fp8_last_error"):
         assert want in names
 
 
@@ -125,6 +125,25 @@ def test_gemm_validation(lib, entry):
     assert call(A16, B16, C16, C16 + 4, D16, *red) == UNSUPPORTED
     assert call(A16, B16, C16, C16 + 4, D16 + 4, 128, 128, 128) == UNSUPPORTED  # misaligned out
     assert call(A16 + 1, B16, C16, C16 + 4, D16, 128, 128, 128) == UNSUPPORTED
+
+
+def test_backward_validation(lib):
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    f = lib.fp8_gemm_backward
+    f.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    f.restype = i32
+    F16 = 0x60000000
+    ok = (A16, B16, 1, C16, D16, E16, E16 + 4, E16 + 8, F16, F16 + (1 << 24), 256, 256, 256, None)
+    bad = list(ok); bad[0] = None
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[9] = F16 + 1024          # dw overlaps dx
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[8] = B16                 # dx aliases dyqt
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[2] = 5
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[10] = 200                # M not a multiple of 16 / 128
+    assert f(*bad) == UNSUPPORTED
 
 
 def test_bad_dy_format(lib):

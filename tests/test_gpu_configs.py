@@ -89,6 +89,10 @@ def linear_backward(fp8, orc, cfg, li, xqt, inv_x, wqt, inv_w):
     say("gemm_wgrad", cfg.name, L.name)
     dw = fp8.gemm_wgrad(dyqt, E5M2, xqt, inv_dy, inv_x)
     gemm_step(orc, dw, u8(dyqt), E5M2, xqt, inv_dy, inv_x, f"{cfg.name} wgrad {L.name}", 300 + li)
+    say("gemm_backward", cfg.name, L.name)
+    dx2, dw2 = fp8.gemm_backward(dyq, dyqt, E5M2, wqt, xqt, inv_dy, inv_w, inv_x)
+    assert torch.equal(dx2.view(torch.int16), dx.view(torch.int16)), "paired dgrad differs from fp8_gemm_dgrad"
+    assert torch.equal(dw2.view(torch.int16), dw.view(torch.int16)), "paired wgrad differs from fp8_gemm_wgrad"
 
 
 LINEAR_CASES = [(c, i) for c in ("c1", "c3", "c4", "c5") for i in range(len(workloads.CONFIGS[c].linears))]

@@ -127,3 +127,24 @@ def test_full_size_sampled_rows(fp8, orc, name, entry, fa, P, Q, R):
     ref = orc.gemm(a.numpy(), fa, b.numpy(), E4M3, inv_a, inv_b, rows=rows)
     gemm_compare(y, ref, name)
     assert_within_sum_bound(y, ref, a.numpy(), fa, b.numpy(), E4M3, inv_a, inv_b, rows, name)
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 12288, 4096), (256, 512, 384), (4096, 4096, 11008), (128, 256, 256)])
+def test_backward_pair_matches_separate_calls(fp8, orc, M, N, K):
+    """fp8_gemm_backward gives exactly the bytes of fp8_gemm_dgrad and fp8_gemm_wgrad."""
+    say("gemm backward pair", M, N, K)
+    g = torch.Generator(device="cpu").manual_seed(M + N + K)
+    dyq = torch.randn((M, N), generator=g).mul_(3000.0).to(TDT[E5M2]).view(torch.uint8)
+    wqt = torch.randn((K, N), generator=g).mul_(60.0).to(TDT[E4M3]).view(torch.uint8)
+    xqt = torch.randn((K, M), generator=g).mul_(60.0).to(TDT[E4M3]).view(torch.uint8)
+    dyqt = dyq.t().contiguous()
+    d = lambda t: dev(t)
+    ia, ib, ic = scal(1 / 57344.0), scal(1 / 448.0), scal(0.0123)
+    dx, dw = fp8.gemm_backward(d(dyq), d(dyqt), E5M2, d(wqt), d(xqt), ia, ib, ic)
+    dx2 = fp8.gemm_dgrad(d(dyq), E5M2, d(wqt), ia, ib)
+    dw2 = fp8.gemm_wgrad(d(dyqt), E5M2, d(xqt), ia, ic)
+    assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
+    assert torch.equal(dw.view(torch.int16), dw2.view(torch.int16))
+    rows = np.array([0, M // 2, M - 1], np.int64)
+    ref = orc.gemm(dyq.numpy(), E5M2, wqt.numpy(), E4M3, np.float32(1 / 57344.0), np.float32(1 / 448.0), rows=rows)
+    gemm_compare(u16(dx)[rows], ref, "backward dgrad rows")
