@@ -195,80 +195,64 @@ __global__ void __launch_bounds__(256) swiglu_quant_kernel(const uint16_t* __res
 }
 
 // Requantisation with the transposed copy hqt [F, M] (and optionally hq).
-// Persistent blocks of 4 waves walk 128-row x 256-column tiles of h: lane l of
-// wave w handles columns 8 (l % 32) .. +7 of 16 consecutive rows (row group
-// l / 32 of the wave's 32 rows), as the transposing quantise kernel does; the
-// transposed 16 x 8 code blocks are parked in an LDS tile laid out as hqt
-// ([256 columns][128 rows], 16-byte pieces XOR-swizzled by column) and written
-// back as full 128-byte row segments.
-constexpr int kHtRows = 128;
-constexpr int kHtCols = 256;
+// A wave owns 64 rows x 64 columns of h; lane l handles the 8 x 8 block at
+// rows 8 (l / 8) .. +7 and columns 8 (l % 8) .. +7.  Every load instruction
+// reads eight full 128-byte row segments of gate (or up); the lane transposes
+// its 8 x 8 code block in registers (v_perm_b32), so each hq store writes 64
+// contiguous bytes of eight rows and each hqt store 64 contiguous bytes of
+// eight hqt rows.  No LDS tile and no barrier: the only LDS is the s_g table,
+// and waves of one block never wait for each other.  Persistent blocks, three
+// per CU (three 34 KB tables; about 150 VGPRs per lane).
+constexpr int kHtEdge = 64;
 
-__global__ void __launch_bounds__(256) swiglu_quant_t_kernel(const uint16_t* __restrict__ gu, int64_t M,
-                                                             int64_t F, const float* __restrict__ absmax_h,
-                                                             uint8_t* __restrict__ hq, uint8_t* __restrict__ hqt,
-                                                             float* __restrict__ inv_out)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+swiglu_quant_t_kernel(const uint16_t* __restrict__ gu, int64_t M, int64_t F, const float* __restrict__ absmax_h,
+                      uint8_t* __restrict__ hq, uint8_t* __restrict__ hqt, float* __restrict__ inv_out)
 {
     __shared__ float tbl[kTable];
-    __shared__ __attribute__((aligned(16))) uint8_t tile[kHtCols * kHtRows];   // 32 KB
     float s, inv;
     tensor_scale(*absmax_h, kMaxE4M3, s, inv);
     if (blockIdx.x == 0 && threadIdx.x == 0 && inv_out) *inv_out = inv;
     load_table_to_lds(tbl);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rt = wave * 32 + (lane >> 5) * 16;          // first row of the lane within the tile
-    const int ct = (lane & 31) * 8;                       // first column of the lane within the tile
-    const int64_t tiles_c = (F + kHtCols - 1) / kHtCols;
-    const int64_t tiles = tiles_c * ((M + kHtRows - 1) / kHtRows);
-    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-        const int64_t tr = (t / tiles_c) * kHtRows, tc = (t % tiles_c) * kHtCols;
-        if (tr + rt < M && tc + ct < F) {
-            const int64_t i0 = tr + rt, j = tc + ct;
-            uint32_t lo[16], hi[16];
+    const int lane = threadIdx.x & 63;
+    const int ri = (lane >> 3) * 8, ci = (lane & 7) * 8;   // the lane's block within the wave item
+    const int64_t items_c = (F + kHtEdge - 1) / kHtEdge;
+    const int64_t items = items_c * ((M + kHtEdge - 1) / kHtEdge);
+    const int64_t wstride = (int64_t)gridDim.x * 4;
+    for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < items; w += wstride) {
+        const int64_t i0 = (w / items_c) * kHtEdge + ri;
+        const int64_t j0 = (w % items_c) * kHtEdge + ci;
+        if (i0 >= M || j0 >= F) continue;             // M, F are multiples of 8: blocks are whole
+        uint4 gw[8], uw[8];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const uint16_t* grow = gu + (i0 + r) * 2 * F;
-                const uint4 gw = *reinterpret_cast<const uint4*>(grow + j);
-                const uint4 uw = *reinterpret_cast<const uint4*>(grow + F + j);
-                float h[8];
-                swiglu8(tbl, gw, uw, h);
-                const uint2 c = quant8_h(h, s);
-                lo[r] = c.x;
-                hi[r] = c.y;
-            }
-            if (hq) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    *reinterpret_cast<uint2*>(hq + (i0 + r) * F + j) = make_uint2(lo[r], hi[r]);
-            }
-            uint32_t w[8][4];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                transpose4x4(lo[4 * g], lo[4 * g + 1], lo[4 * g + 2], lo[4 * g + 3], w[0][g], w[1][g], w[2][g], w[3][g]);
-                transpose4x4(hi[4 * g], hi[4 * g + 1], hi[4 * g + 2], hi[4 * g + 3], w[4][g], w[5][g], w[6][g], w[7][g]);
-            }
-            const int piece = rt >> 4;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int col = ct + k;
-                const int phys = piece ^ ((col >> 3) & 7);
-                *reinterpret_cast<uint4*>(tile + col * kHtRows + phys * 16) =
-                    make_uint4(w[k][0], w[k][1], w[k][2], w[k][3]);
-            }
+        for (int r = 0; r < 8; ++r) {
+            const uint16_t* grow = gu + (i0 + r) * 2 * F + j0;
+            gw[r] = *reinterpret_cast<const uint4*>(grow);
+            uw[r] = *reinterpret_cast<const uint4*>(grow + F);
         }
-        __syncthreads();
+        uint32_t lo[8], hi[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int id = u * 256 + threadIdx.x;
-            const int col = id >> 3, p = id & 7;
-            const int64_t qrow = tc + col, qcol = tr + p * 16;
-            if (qrow < F && qcol < M) {
-                const int phys = p ^ ((col >> 3) & 7);
-                *reinterpret_cast<uint4*>(hqt + qrow * M + qcol) =
-                    *reinterpret_cast<const uint4*>(tile + col * kHtRows + phys * 16);
-            }
+        for (int r = 0; r < 8; ++r) {
+            float h[8];
+            swiglu8(tbl, gw[r], uw[r], h);
+            const uint2 c = quant8_h(h, s);
+            lo[r] = c.x;
+            hi[r] = c.y;
         }
-        __syncthreads();     // the tile is rewritten by the next iteration
+        if (hq) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                *reinterpret_cast<uint2*>(hq + (i0 + r) * F + j0) = make_uint2(lo[r], hi[r]);
+        }
+        // column k of the block = rows 0..3 (word 0) and rows 4..7 (word 1)
+        uint32_t c0[8], c1[8];
+        transpose4x4(lo[0], lo[1], lo[2], lo[3], c0[0], c0[1], c0[2], c0[3]);
+        transpose4x4(lo[4], lo[5], lo[6], lo[7], c1[0], c1[1], c1[2], c1[3]);
+        transpose4x4(hi[0], hi[1], hi[2], hi[3], c0[4], c0[5], c0[6], c0[7]);
+        transpose4x4(hi[4], hi[5], hi[6], hi[7], c1[4], c1[5], c1[6], c1[7]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            *reinterpret_cast<uint2*>(hqt + (j0 + k) * M + i0) = make_uint2(c0[k], c1[k]);
     }
 }
 
@@ -296,9 +280,10 @@ hipError_t launch_swiglu_requant(const void* gu, int64_t M, int64_t F, float* ab
         swiglu_absmax_kernel<<<(unsigned)ablocks, 1024, 0, stream>>>(g, M, F, reinterpret_cast<uint32_t*>(absmax_h));
     }
     if (hqt) {
-        // 34 KB table + 32 KB tile per block: two blocks per CU
-        int64_t tblocks = ((F + kHtCols - 1) / kHtCols) * ((M + kHtRows - 1) / kHtRows);
-        if (tblocks > 2 * (int64_t)device_cu_count()) tblocks = 2 * (int64_t)device_cu_count();
+        // three resident blocks per CU (register-limited), persistent over the wave items
+        const int64_t witems = ((F + kHtEdge - 1) / kHtEdge) * ((M + kHtEdge - 1) / kHtEdge);
+        int64_t tblocks = (witems + 3) / 4;
+        if (tblocks > 3 * (int64_t)device_cu_count()) tblocks = 3 * (int64_t)device_cu_count();
         swiglu_quant_t_kernel<<<(unsigned)tblocks, 256, 0, stream>>>(g, M, F, absmax_h, hq, hqt, inv_scale_h);
     } else {
         swiglu_quant_kernel<<<(unsigned)blocks, 256, 0, stream>>>(g, M, F, absmax_h, hq, inv_scale_h);
