@@ -36,22 +36,46 @@ __global__ void __launch_bounds__(64) zero_u32_kernel(uint32_t* p)
 
 // One pass over x; each block folds its maximum into *out with one atomicMax on
 // the fp32 bit pattern (for non-negative values the unsigned order of the bits
-// is the numeric order, and NaN patterns sort above infinity).
-__global__ void __launch_bounds__(256) absmax_bf16_kernel(const uint4* __restrict__ x, int64_t nvec,
-                                                          const uint16_t* __restrict__ tail, int ntail,
-                                                          uint32_t* __restrict__ out)
+// is the numeric order, and NaN patterns sort above infinity).  One block of 16
+// waves per CU; every lane keeps eight 16-byte loads in flight.  Tensors of at
+// least kAbsStreamBytes are read with non-temporal loads: measured on MI355X
+// (7B-layer shapes), that makes the pass ~30% faster on 90-180 MB tensors at a
+// small cost to the quantise pass that follows; below that size the plain
+// loads leave the tensor in the 256 MB Infinity Cache, where the quantise pass
+// re-reads it about twice as fast as from HBM.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ us2 absmax_acc4(us2 m, u32x4 v)
+{
+    return absmax_acc(m, make_uint4(v.x, v.y, v.z, v.w));
+}
+
+constexpr int kAbsThreads = 1024;
+constexpr int64_t kAbsStreamBytes = 64ll << 20;
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const u32x4* p)
+{
+    if (NT) return __builtin_nontemporal_load(p);
+    return *p;
+}
+
+template <bool NT>
+__global__ void __launch_bounds__(kAbsThreads) absmax_bf16_kernel(const u32x4* __restrict__ x, int64_t nvec,
+                                                                  const uint16_t* __restrict__ tail, int ntail,
+                                                                  uint32_t* __restrict__ out)
 {
     us2 m = {0, 0};
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kAbsThreads;
+    int64_t i = (int64_t)blockIdx.x * kAbsThreads + threadIdx.x;
     for (; i + 7 * stride < nvec; i += 8 * stride) {
-        uint4 v[8];
+        u32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = x[i + u * stride];
+        for (int u = 0; u < 8; ++u) v[u] = ld16<NT>(x + i + u * stride);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) m = absmax_acc(m, v[u]);
+        for (int u = 0; u < 8; ++u) m = absmax_acc4(m, v[u]);
     }
-    for (; i < nvec; i += stride) m = absmax_acc(m, x[i]);
+    for (; i < nvec; i += stride) m = absmax_acc4(m, ld16<NT>(x + i));
     uint32_t r = m.x > m.y ? m.x : m.y;
     if (blockIdx.x == 0 && (int)threadIdx.x < ntail) {
         uint32_t t = tail[threadIdx.x] & 0x7FFFu;
@@ -64,14 +88,18 @@ hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, hipStream
 {
     const int64_t nvec = n / 8;
     const int ntail = (int)(n - nvec * 8);
-    int64_t blocks = (nvec + 2047) / 2048;       // at least 8 vectors per thread
+    int64_t blocks = (nvec + 8 * kAbsThreads - 1) / (8 * kAbsThreads);   // up to 8 vectors per thread
     const int64_t cap = (int64_t)device_cu_count();  // one block per CU (one atomic per block)
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     zero_u32_kernel<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax));
-    absmax_bf16_kernel<<<(unsigned)blocks, 256, 0, stream>>>(
-        reinterpret_cast<const uint4*>(x), nvec,
-        reinterpret_cast<const uint16_t*>(x) + nvec * 8, ntail, reinterpret_cast<uint32_t*>(absmax));
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+    const uint16_t* tail = reinterpret_cast<const uint16_t*>(x) + nvec * 8;
+    uint32_t* out = reinterpret_cast<uint32_t*>(absmax);
+    if (2 * n >= kAbsStreamBytes)
+        absmax_bf16_kernel<true><<<(unsigned)blocks, kAbsThreads, 0, stream>>>(xv, nvec, tail, ntail, out);
+    else
+        absmax_bf16_kernel<false><<<(unsigned)blocks, kAbsThreads, 0, stream>>>(xv, nvec, tail, ntail, out);
     return hipGetLastError();
 }
 
