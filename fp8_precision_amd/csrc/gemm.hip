@@ -21,8 +21,10 @@
 //    step and the next step's B fragments (read into each B block's registers
 //    as soon as that block is consumed) overlap the matrix instructions.
 //  - LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
-//    c ^ f(r), f(r) = ((r >> 1) & 7) ^ ((r & 1) << 2), which keeps the 16-byte
-//    fragment reads of 8 or 16 consecutive rows on distinct banks.
+//    c ^ f(r), f(r) = ((r >> 1) & 7) ^ ((r & 1) << 2).  A lane's 32 fragment
+//    bytes are chunks g and g + 4 of its row (g = lane / 16); with this pairing
+//    every 16-byte fragment read runs at the 4-cycle LDS minimum on gfx950
+//    (no bank conflicts, measured).
 //  - The instruction's operands are swapped (B fragment first), so each lane
 //    ends with 4 consecutive output columns of one row; the epilogue stages
 //    them through LDS and writes full 256-byte row segments.
@@ -72,11 +74,13 @@ __device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint3
                  : "memory", "m0");
 }
 
+// The 32 bytes of a fragment row are logical chunks c and c + 4 (16 bytes each),
+// at physical chunks p and p ^ 4.
 __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int chunk)
 {
     const int p = chunk ^ swz(row);
     const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * kBK + p * 16);
-    const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * kBK + (p ^ 1) * 16);
+    const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * kBK + (p ^ 4) * 16);
     v8i r;
     r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
     r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
@@ -127,12 +131,16 @@ __device__ __forceinline__ void issue_stage(const Sources& src, uint32_t stage, 
 }
 
 // Fragments of the 16x16x128 instruction: block b of 16 rows, lane l holds row
-// l % 16 and the 32 bytes at k offset 32 * (l / 16) of the 128-byte step (the
-// same k mapping for both operands, so the order of k within the instruction
-// does not matter).  A wave owns 128 x 128 outputs = 8 x 8 blocks.
+// l % 16 and the k bytes 16 g .. 16 g + 15 and 64 + 16 g .. 64 + 16 g + 15 of the
+// 128-byte step, g = l / 16 (the same k mapping for both operands, so the
+// order of k within the instruction does not matter).  With the row swizzle
+// above, each 16-byte LDS read of a block is free of bank conflicts on gfx950
+// (measured with SQ_LDS_BANK_CONFLICT; the pairing of chunks 2g, 2g + 1 costs
+// a 2-way conflict, 8 instead of 4 LDS cycles per read).  A wave owns
+// 128 x 128 outputs = 8 x 8 blocks.
 __device__ __forceinline__ v8i read_frag16(const uint8_t* tile, int row0, int lane)
 {
-    return lds_frag(tile, row0 + (lane & 15), (lane >> 4) * 2);
+    return lds_frag(tile, row0 + (lane & 15), lane >> 4);
 }
 
 typedef float v4f __attribute__((ext_vector_type(4)));
