@@ -224,8 +224,8 @@ def cpu_baseline(ops, gemm_rows):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-gemm-rows", type=int, default=16)
     ap.add_argument("--breakdown", action="store_true", help="also time every call (separate pass)")
