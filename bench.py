@@ -12,11 +12,15 @@ gate/up and down linears, forward and backward --
   backward: absmax -> quantise dY to e5m2 (+ transposed copy) -> dgrad
             (dY . W) and wgrad (dY^T . X) FP8 GEMMs -> bf16.
 
+--layout mn runs the same step without the transposed FP8 copies: the
+quantise and SwiGLU calls write only the row-major codes and the backward
+GEMMs read W, X, dY and h untransposed (fp8_gemm_backward_mn).
+
 `value` is the step's GEMM work (2MNK summed over the 12 GEMMs) divided by the
 wall time of the whole step, quantisation included: effective FP8 TFLOP/s.
 Inputs are resident in HBM before the timed region starts.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout copies|mn] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -38,7 +42,8 @@ FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA peak
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E peak
 
 # rocprofv3 kernel names of the library's kernels
-GEMM_KERNEL = {(0, 0): "fp8k::gemm_tn_kernel<0, 0, false>", (1, 0): "fp8k::gemm_tn_kernel<1, 0, false>"}
+GEMM_KERNEL = {(0, 0, 0): "fp8k::gemm_tn_kernel<0, 0, false, 0>", (1, 0, 0): "fp8k::gemm_tn_kernel<1, 0, false, 0>",
+               (1, 0, 1): "fp8k::gemm_tn_kernel<1, 0, false, 1>"}
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_traffic_layer7b.txt")
 GEMM_SOURCE = os.path.join(ROOT, "fp8_precision_amd", "csrc", "gemm.hip")
 
@@ -67,8 +72,9 @@ class Op:
         self.meta = meta or {}
 
 
-def build_layer7b(fp8, dev):
+def build_layer7b(fp8, dev, layout="copies"):
     """Inputs and the ordered list of calls of one 7B-layer step."""
+    mn = layout == "mn"
     cfg = workloads.CONFIGS["c3"]
     M = cfg.M
     E4M3, E5M2 = fp8.E4M3, fp8.E5M2
@@ -81,12 +87,12 @@ def build_layer7b(fp8, dev):
 
     def quant_ops(tag, x, rows, cols, fmt):
         am, sc, inv = f32(), f32(), f32()
-        q, qt = u8(rows, cols), u8(cols, rows)
+        q, qt = u8(rows, cols), (None if mn else u8(cols, rows))
         n = rows * cols
         ops.append(Op(f"absmax {tag}", lambda: fp8.absmax(x, am), "absmax", 2 * n,
                       meta={"rows": rows, "cols": cols, "fmt": fmt}))
         ops.append(Op(f"quantize {tag}", lambda: fp8.quantize(x, fmt, am, q=q, qt=qt, scale=sc, inv_scale=inv),
-                      "quantize", 4 * n, meta={"rows": rows, "cols": cols, "fmt": fmt}))
+                      "quantize", (3 if mn else 4) * n, meta={"rows": rows, "cols": cols, "fmt": fmt, "qt": not mn}))
         return q, qt, inv
 
     # ---- forward
@@ -100,36 +106,40 @@ def build_layer7b(fp8, dev):
         wq, wqt, inv_w = quant_ops(f"W_{name}", w, L.N, L.K, E4M3)
         y = bf(M, L.N)
         ops.append(Op(f"gemm_fwd {name}", lambda xq=xq, wq=wq, ix=inv_x, iw=inv_w, y=y: fp8.gemm_fwd(xq, wq, ix, iw, y),
-                      "gemm", 2 * M * L.N * L.K, GEMM_KERNEL[(0, 0)], {"probs": [(M, L.N, L.K, E4M3)]}))
-        fwd[name] = (xqt, wqt, inv_x, inv_w, y)
+                      "gemm", 2 * M * L.N * L.K, GEMM_KERNEL[(0, 0, 0)], {"probs": [(M, L.N, L.K, E4M3)]}))
+        fwd[name] = (xq, wq, xqt, wqt, inv_x, inv_w, y)
     # SwiGLU requantisation of the gate/up output feeds the down linear
     li, L = lin["down"]
     F = L.K
-    gu = fwd["gate_up"][4]
+    gu = fwd["gate_up"][6]
     am_h, inv_h = f32(), f32()
-    hq, hqt = u8(M, F), u8(F, M)
+    hq, hqt = u8(M, F), (None if mn else u8(F, M))
     ops.append(Op("swiglu_requant fwd", lambda: fp8.swiglu_requant(gu, am_h, True, hq=hq, hqt=hqt, inv_scale_h=inv_h),
-                  "swiglu", 4 * M * F + 6 * M * F, meta={"M": M, "F": F}))
+                  "swiglu", 4 * M * F + (5 if mn else 6) * M * F, meta={"M": M, "F": F, "qt": not mn}))
     w = workloads.draw_w(cfg, li).to(dev)
     bufs["down"] = (None, w)
     wq, wqt, inv_w = quant_ops("W_down", w, L.N, L.K, E4M3)
     y = bf(M, L.N)
     ops.append(Op("gemm_fwd down", lambda: fp8.gemm_fwd(hq, wq, inv_h, inv_w, y), "gemm", 2 * M * L.N * L.K,
-                  GEMM_KERNEL[(0, 0)], {"probs": [(M, L.N, L.K, E4M3)]}))
-    fwd["down"] = (hqt, wqt, inv_h, inv_w, y)
+                  GEMM_KERNEL[(0, 0, 0)], {"probs": [(M, L.N, L.K, E4M3)]}))
+    fwd["down"] = (hq, wq, hqt, wqt, inv_h, inv_w, y)
 
     # ---- backward
     for name in ("qkv", "o", "gate_up", "down"):
         li, L = lin[name]
         dy = workloads.draw_dy(cfg, li).to(dev)
-        xqt, wqt, inv_x, inv_w, _ = fwd[name]
+        xq, wq, xqt, wqt, inv_x, inv_w, _ = fwd[name]
         dyq, dyqt, inv_dy = quant_ops(f"dY_{name}", dy, M, L.N, E5M2)
         dx = bf(M, L.K)
         dw = bf(L.N, L.K)
         # dgrad dX = dY . W and wgrad dW = dY^T . X in one launch
-        ops.append(Op(f"gemm_backward {name}", lambda dyq=dyq, dyqt=dyqt, wqt=wqt, xqt=xqt, a=inv_dy, b=inv_w,
-                      c=inv_x, dx=dx, dw=dw: fp8.gemm_backward(dyq, dyqt, E5M2, wqt, xqt, a, b, c, dx, dw),
-                      "gemm", 4 * M * L.N * L.K, GEMM_KERNEL[(1, 0)],
+        if mn:
+            fn = (lambda dyq=dyq, wq=wq, xq=xq, a=inv_dy, b=inv_w, c=inv_x, dx=dx, dw=dw:
+                  fp8.gemm_backward_mn(dyq, E5M2, wq, xq, a, b, c, dx, dw))
+        else:
+            fn = (lambda dyq=dyq, dyqt=dyqt, wqt=wqt, xqt=xqt, a=inv_dy, b=inv_w, c=inv_x, dx=dx, dw=dw:
+                  fp8.gemm_backward(dyq, dyqt, E5M2, wqt, xqt, a, b, c, dx, dw))
+        ops.append(Op(f"gemm_backward {name}", fn, "gemm", 4 * M * L.N * L.K, GEMM_KERNEL[(1, 0, 1 if mn else 0)],
                       {"probs": [(M, L.K, L.N, E5M2), (L.N, L.K, M, E5M2)]}))
         bufs["dy_" + name] = dy
     return ops, bufs
@@ -207,12 +217,12 @@ def cpu_baseline(ops, gemm_rows):
             x = rng.integers(0, 0x3F80, (m["rows"], m["cols"]), dtype=np.uint16)
             t = time.perf_counter()
             s_, _ = oracle.scale(oracle.absmax_bf16(x), m["fmt"])
-            oracle.quantize(x, m["fmt"], s_, want_q=True, want_qt=True)
+            oracle.quantize(x, m["fmt"], s_, want_q=True, want_qt=m["qt"])
             est += time.perf_counter() - t
         elif op.kind == "swiglu":
             gu = rng.integers(0, 0x4080, (m["M"], 2 * m["F"]), dtype=np.uint16)
             t = time.perf_counter()
-            oracle.swiglu_requant(gu, want_hq=True, want_hqt=True)
+            oracle.swiglu_requant(gu, want_hq=True, want_hqt=m["qt"])
             est += time.perf_counter() - t
     spent = time.perf_counter() - t_start
     return {"value": round(gemm_flop / est / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
@@ -227,6 +237,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", choices=("copies", "mn"), default="copies",
+                    help="backward GEMM operands: transposed FP8 copies, or the untransposed tensors")
     ap.add_argument("--cpu-gemm-rows", type=int, default=16)
     ap.add_argument("--breakdown", action="store_true", help="also time every call (separate pass)")
     args = ap.parse_args()
@@ -242,7 +254,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
-    ops, bufs = build_layer7b(fp8, dev)
+    ops, bufs = build_layer7b(fp8, dev, args.layout)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         run_step(ops)
@@ -300,6 +312,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "7B-class layer linears fwd+bwd with SwiGLU requant chain (c3 shapes + c2 MLP chain)",
                    "M": 4096, "d": 4096, "ffn": 11008, "qkv_out": 12288, "gemms": 12, "gemm_launches": 8,
+                   "backward_operands": "untransposed (MN-major)" if args.layout == "mn" else "transposed copies",
                    "gemm_gflop_per_step": round(gemm_flop / 1e9, 1)},
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "gemm_only_tflops": round(gemm_flop / gemm_time / 1e12, 1),

@@ -34,6 +34,9 @@ _SIGS = {
     "fp8_gemm_dgrad": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_gemm_wgrad": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_gemm_backward": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "fp8_gemm_dgrad_mn": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "fp8_gemm_wgrad_mn": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "fp8_gemm_backward_mn": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -214,4 +217,48 @@ def gemm_backward(dyq, dyqt, dy_fmt, wqt, xqt, inv_sdy, inv_sw, inv_sx, dx=None,
     _check("fp8_gemm_backward", _lib.fp8_gemm_backward(_ptr(dyq), _ptr(dyqt), int(dy_fmt), _ptr(wqt), _ptr(xqt),
                                                        _ptr(inv_sdy), _ptr(inv_sw), _ptr(inv_sx), _ptr(dx), _ptr(dw),
                                                        M, N, K, _stream(dyq)))
+    return dx, dw
+
+
+def gemm_dgrad_mn(dyq, dy_fmt, wq, inv_sdy, inv_sw, out=None) -> torch.Tensor:
+    """dX[M, K] = dY[M, N] . W[N, K] on the untransposed wq [N, K]."""
+    _dev_tensor(dyq, "dyq", torch.uint8)
+    _dev_tensor(wq, "wq", torch.uint8)
+    M, N = dyq.shape
+    K = wq.shape[1]
+    if wq.shape[0] != N:
+        raise ValueError("dyq is [M, N] and wq must be [N, K]")
+    out = _out_bf16(out, (M, K), dyq.device)
+    _check("fp8_gemm_dgrad_mn", _lib.fp8_gemm_dgrad_mn(_ptr(dyq), int(dy_fmt), _ptr(wq), _ptr(inv_sdy), _ptr(inv_sw),
+                                                       _ptr(out), M, N, K, _stream(dyq)))
+    return out
+
+
+def gemm_wgrad_mn(dyq, dy_fmt, xq, inv_sdy, inv_sx, out=None) -> torch.Tensor:
+    """dW[N, K] = dY[M, N]^T . X[M, K] on the untransposed dyq [M, N] and xq [M, K]."""
+    _dev_tensor(dyq, "dyq", torch.uint8)
+    _dev_tensor(xq, "xq", torch.uint8)
+    M, N = dyq.shape
+    K = xq.shape[1]
+    if xq.shape[0] != M:
+        raise ValueError("dyq is [M, N] and xq must be [M, K]")
+    out = _out_bf16(out, (N, K), dyq.device)
+    _check("fp8_gemm_wgrad_mn", _lib.fp8_gemm_wgrad_mn(_ptr(dyq), int(dy_fmt), _ptr(xq), _ptr(inv_sdy), _ptr(inv_sx),
+                                                       _ptr(out), M, N, K, _stream(dyq)))
+    return out
+
+
+def gemm_backward_mn(dyq, dy_fmt, wq, xq, inv_sdy, inv_sw, inv_sx, dx=None, dw=None):
+    """dgrad and wgrad of one linear in one launch on the untransposed tensors: (dX [M, K], dW [N, K])."""
+    for t, n in ((dyq, "dyq"), (wq, "wq"), (xq, "xq")):
+        _dev_tensor(t, n, torch.uint8)
+    M, N = dyq.shape
+    K = wq.shape[1]
+    if wq.shape[0] != N or tuple(xq.shape) != (M, K):
+        raise ValueError("expected dyq [M, N], wq [N, K], xq [M, K]")
+    dx = _out_bf16(dx, (M, K), dyq.device)
+    dw = _out_bf16(dw, (N, K), dyq.device)
+    _check("fp8_gemm_backward_mn", _lib.fp8_gemm_backward_mn(_ptr(dyq), int(dy_fmt), _ptr(wq), _ptr(xq),
+                                                             _ptr(inv_sdy), _ptr(inv_sw), _ptr(inv_sx), _ptr(dx),
+                                                             _ptr(dw), M, N, K, _stream(dyq)))
     return dx, dw

@@ -204,7 +204,7 @@ fp8_status fp8_gemm_fwd(const uint8_t* xq, const uint8_t* wq, const float* inv_s
     t_last_error.clear();
     fp8_status st = gemm_common("fp8_gemm_fwd", xq, FP8_E4M3, wq, inv_sx, inv_sw, y, M, N, K, stream);
     if (st != FP8_OK) return st;
-    hipError_t e = fp8k::launch_gemm_tn(xq, 0, wq, 0, inv_sx, inv_sw, y, M, N, K, stream);
+    hipError_t e = fp8k::launch_gemm_tn(xq, 0, 0, wq, 0, 0, inv_sx, inv_sw, y, M, N, K, stream);
     if (e != hipSuccess) return fail_hip("fp8_gemm_fwd", e);
     return FP8_OK;
 }
@@ -215,7 +215,7 @@ fp8_status fp8_gemm_dgrad(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_t* wqt
     t_last_error.clear();
     fp8_status st = gemm_common("fp8_gemm_dgrad", dyq, (int)dy_fmt, wqt, inv_sdy, inv_sw, dx, M, K, N, stream);
     if (st != FP8_OK) return st;
-    hipError_t e = fp8k::launch_gemm_tn(dyq, (int)dy_fmt, wqt, 0, inv_sdy, inv_sw, dx, M, K, N, stream);
+    hipError_t e = fp8k::launch_gemm_tn(dyq, (int)dy_fmt, 0, wqt, 0, 0, inv_sdy, inv_sw, dx, M, K, N, stream);
     if (e != hipSuccess) return fail_hip("fp8_gemm_dgrad", e);
     return FP8_OK;
 }
@@ -226,7 +226,7 @@ fp8_status fp8_gemm_wgrad(const uint8_t* dyqt, fp8_fmt dy_fmt, const uint8_t* xq
     t_last_error.clear();
     fp8_status st = gemm_common("fp8_gemm_wgrad", dyqt, (int)dy_fmt, xqt, inv_sdy, inv_sx, dw, N, K, M, stream);
     if (st != FP8_OK) return st;
-    hipError_t e = fp8k::launch_gemm_tn(dyqt, (int)dy_fmt, xqt, 0, inv_sdy, inv_sx, dw, N, K, M, stream);
+    hipError_t e = fp8k::launch_gemm_tn(dyqt, (int)dy_fmt, 0, xqt, 0, 0, inv_sdy, inv_sx, dw, N, K, M, stream);
     if (e != hipSuccess) return fail_hip("fp8_gemm_wgrad", e);
     return FP8_OK;
 }
@@ -248,9 +248,57 @@ fp8_status fp8_gemm_backward(const uint8_t* dyq, const uint8_t* dyqt, fp8_fmt dy
     for (const Range& o : outs)
         for (const Range& i : ins)
             if (overlap(o.p, o.n, i.p, i.n)) return fail(FP8_ERR_INVALID, "fp8_gemm_backward: an output overlaps an input");
-    hipError_t e = fp8k::launch_gemm_tn_pair(dyq, wqt, inv_sdy, inv_sw, dx, M, K, N, dyqt, xqt, inv_sdy, inv_sx, dw,
-                                             N, K, M, (int)dy_fmt, 0, stream);
+    hipError_t e = fp8k::launch_gemm_tn_pair(dyq, 0, wqt, 0, inv_sdy, inv_sw, dx, M, K, N, dyqt, 0, xqt, 0, inv_sdy,
+                                             inv_sx, dw, N, K, M, (int)dy_fmt, 0, stream);
     if (e != hipSuccess) return fail_hip("fp8_gemm_backward", e);
+    return FP8_OK;
+}
+
+// ---- the same products on the untransposed FP8 tensors (MN-major operands)
+
+fp8_status fp8_gemm_dgrad_mn(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_t* wq, const float* inv_sdy,
+                             const float* inv_sw, void* dx, int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    t_last_error.clear();
+    fp8_status st = gemm_common("fp8_gemm_dgrad_mn", dyq, (int)dy_fmt, wq, inv_sdy, inv_sw, dx, M, K, N, stream);
+    if (st != FP8_OK) return st;
+    hipError_t e = fp8k::launch_gemm_tn(dyq, (int)dy_fmt, 0, wq, 0, 1, inv_sdy, inv_sw, dx, M, K, N, stream);
+    if (e != hipSuccess) return fail_hip("fp8_gemm_dgrad_mn", e);
+    return FP8_OK;
+}
+
+fp8_status fp8_gemm_wgrad_mn(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_t* xq, const float* inv_sdy,
+                             const float* inv_sx, void* dw, int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    t_last_error.clear();
+    fp8_status st = gemm_common("fp8_gemm_wgrad_mn", dyq, (int)dy_fmt, xq, inv_sdy, inv_sx, dw, N, K, M, stream);
+    if (st != FP8_OK) return st;
+    hipError_t e = fp8k::launch_gemm_tn(dyq, (int)dy_fmt, 1, xq, 0, 1, inv_sdy, inv_sx, dw, N, K, M, stream);
+    if (e != hipSuccess) return fail_hip("fp8_gemm_wgrad_mn", e);
+    return FP8_OK;
+}
+
+fp8_status fp8_gemm_backward_mn(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_t* wq, const uint8_t* xq,
+                                const float* inv_sdy, const float* inv_sw, const float* inv_sx, void* dx, void* dw,
+                                int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    t_last_error.clear();
+    fp8_status st = gemm_common("fp8_gemm_backward_mn (dgrad)", dyq, (int)dy_fmt, wq, inv_sdy, inv_sw, dx, M, K, N,
+                                stream);
+    if (st != FP8_OK) return st;
+    st = gemm_common("fp8_gemm_backward_mn (wgrad)", dyq, (int)dy_fmt, xq, inv_sdy, inv_sx, dw, N, K, M, stream);
+    if (st != FP8_OK) return st;
+    const Range outs[] = {{dx, 2 * M * K}, {dw, 2 * N * K}};
+    const Range ins[] = {{dyq, M * N}, {wq, K * N}, {xq, K * M}, {inv_sdy, 4}, {inv_sw, 4}, {inv_sx, 4}};
+    if (overlap(dx, 2 * M * K, dw, 2 * N * K))
+        return fail(FP8_ERR_INVALID, "fp8_gemm_backward_mn: dx and dw overlap");
+    for (const Range& o : outs)
+        for (const Range& i : ins)
+            if (overlap(o.p, o.n, i.p, i.n))
+                return fail(FP8_ERR_INVALID, "fp8_gemm_backward_mn: an output overlaps an input");
+    hipError_t e = fp8k::launch_gemm_tn_pair(dyq, 0, wq, 1, inv_sdy, inv_sw, dx, M, K, N, dyq, 1, xq, 1, inv_sdy,
+                                             inv_sx, dw, N, K, M, (int)dy_fmt, 0, stream);
+    if (e != hipSuccess) return fail_hip("fp8_gemm_backward_mn", e);
     return FP8_OK;
 }
 

@@ -20,15 +20,17 @@ hipError_t launch_swiglu_requant(const void* gu, int64_t M, int64_t F, float* ab
                                  int compute_absmax, uint8_t* hq, uint8_t* hqt,
                                  float* inv_scale_h, hipStream_t stream);
 
-// out[P, Q] = bf16(RN32(sum_r A[p, r] B[q, r] * RN32(*inv_a * *inv_b)))
-hipError_t launch_gemm_tn(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
-                          const float* inv_a, const float* inv_b, void* out,
-                          int64_t P, int64_t Q, int64_t R, hipStream_t stream);
+// out[P, Q] = bf16(RN32(sum_r A[p, r] B[q, r] * RN32(*inv_a * *inv_b))).  Operand
+// layouts: 0 = K-major (A[p, r] at A + p R + r), 1 = MN-major (A[p, r] at
+// A + r P + p; B likewise with Q).  Compiled pairs (A, B): (0, 0), (0, 1), (1, 1).
+hipError_t launch_gemm_tn(const uint8_t* A, int fmt_a, int la, const uint8_t* B, int fmt_b, int lb,
+                          const float* inv_a, const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R,
+                          hipStream_t stream);
 
-// Two independent products of the same operand formats in one launch.
-hipError_t launch_gemm_tn_pair(const uint8_t* A0, const uint8_t* B0, const float* ia0, const float* ib0, void* out0,
-                               int64_t P0, int64_t Q0, int64_t R0, const uint8_t* A1, const uint8_t* B1,
-                               const float* ia1, const float* ib1, void* out1, int64_t P1, int64_t Q1, int64_t R1,
-                               int fmt_a, int fmt_b, hipStream_t stream);
+// Two independent products of the same operand formats (and the same B layout) in one launch.
+hipError_t launch_gemm_tn_pair(const uint8_t* A0, int la0, const uint8_t* B0, int lb0, const float* ia0,
+                               const float* ib0, void* out0, int64_t P0, int64_t Q0, int64_t R0, const uint8_t* A1,
+                               int la1, const uint8_t* B1, int lb1, const float* ia1, const float* ib1, void* out1,
+                               int64_t P1, int64_t Q1, int64_t R1, int fmt_a, int fmt_b, hipStream_t stream);
 
 }  // namespace fp8k

@@ -2,10 +2,16 @@
 //
 //   out[p, q] = bf16_RNE( RN32( sum_r dec(A[p, r]) * dec(B[q, r]) ) * RN32(inv_a * inv_b) )
 //
-// One TN kernel serves the forward, dgrad and wgrad products ("LLMQ: Efficient
+// One kernel serves the forward, dgrad and wgrad products ("LLMQ: Efficient
 // Lower-Precision Pretraining for Consumer GPUs", section 2: low-precision
 // operands on the matrix units; section 4: larger models are dominated by
-// these products).  Both operands are contiguous along the reduction index.
+// these products, and the backward pass needs transposed operands).  Each
+// operand is read in one of two layouts:
+//   K-major  (A[p, r] at A + p * R + r): contiguous along the reduction index;
+//   MN-major (A[p, r] at A + r * P + p): contiguous along the output index --
+//            the untransposed FP8 tensor, so the backward products need no
+//            transposed copies (dgrad reads W [N, K] directly, wgrad reads dY
+//            [M, N] and X [M, K] directly).
 //
 // Design (CDNA4):
 //  - 256 x 256 output tile per workgroup, reduction step 128 bytes, 256 threads
@@ -20,11 +26,19 @@
 //  - Fragments are pipelined in registers: the LDS reads for the next half
 //    step and the next step's B fragments (read into each B block's registers
 //    as soon as that block is consumed) overlap the matrix instructions.
-//  - LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
-//    c ^ f(r), f(r) = ((r >> 1) & 7) ^ ((r & 1) << 2).  A lane's 32 fragment
-//    bytes are chunks g and g + 4 of its row (g = lane / 16); with this pairing
-//    every 16-byte fragment read runs at the 4-cycle LDS minimum on gfx950
-//    (no bank conflicts, measured).
+//  - K-major tiles: 256 rows of 128 bytes; the 16-byte chunk c of row r is
+//    stored at chunk c ^ f(r), f(r) = ((r >> 1) & 7) ^ ((r & 1) << 2).  A lane's
+//    32 fragment bytes are chunks g and g + 4 of its row (g = lane / 16), read
+//    with two ds_read_b128.
+//  - MN-major tiles: 128 rows (reduction index) of 256 bytes; chunk c of row r
+//    is stored at c ^ h(r), h(r) = (r & 7) | (((r >> 4) & 1) << 3).  A fragment
+//    is four ds_read_b64_tr_b8: in each 16-lane group, lanes 2t and 2t + 1 name
+//    the two halves of a 16-byte piece of row t and lane i receives byte i of
+//    all eight rows -- the same 32 reduction values per lane, in the same
+//    order, as the K-major read, so both layouts give bit-identical results.
+//    With these swizzles every fragment read runs at the LDS minimum on gfx950
+//    (4 cycles per 1 KB ds_read_b128, 2 per 512-byte transpose read; measured
+//    with SQ_LDS_BANK_CONFLICT = 0).
 //  - The instruction's operands are swapped (B fragment first), so each lane
 //    ends with 4 consecutive output columns of one row; the epilogue stages
 //    them through LDS and writes full 256-byte row segments.
@@ -38,9 +52,12 @@
 namespace fp8k {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kBM = 256;
 constexpr int kBN = 256;
@@ -58,7 +75,12 @@ constexpr int kGroupM = 8;                    // tile rows per raster group
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitVm16 = 0x4F70;
 
+// Operand layouts.
+constexpr int kKMajor = 0;
+constexpr int kMNMajor = 1;
+
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+__device__ __forceinline__ int swz_mn(int r) { return (r & 7) | (((r >> 4) & 1) << 3); }
 
 // 16-byte direct-to-LDS load in the scalar-base form: lane L reads 16 bytes at
 // sbase + voff[L] and writes LDS bytes [lds + 16 L, lds + 16 L + 16).  Issued
@@ -74,11 +96,113 @@ __device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint3
                  : "memory", "m0");
 }
 
-// The 32 bytes of a fragment row are logical chunks c and c + 4 (16 bytes each),
-// at physical chunks p and p ^ 4.
-__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int chunk)
+// Global -> LDS sources of one operand for one wave.  A stage of an operand is
+// filled by 8 loads per wave (1 KB each, load ii of wave w covering the LDS
+// bytes (w * 8 + ii) * 1024 ..):
+//   K-major: LDS rows (w * 8 + ii) * 8 + L / 8, lane L at physical chunk L % 8,
+//            i.e. logical chunk (L % 8) ^ f(row); f depends on ii only through
+//            ii & 1, so a lane keeps two offsets and the row step 8 ii R goes
+//            into the uniform base.  Matrices with fewer than 256 rows (EDGE)
+//            clamp each row to the last valid one instead.
+//   MN-major: LDS rows (w * 8 + ii) * 4 + L / 16, lane L at physical chunk
+//            L % 16, logical chunk (L % 16) ^ h(row); h depends on ii through
+//            bits 0 and 2, so a lane keeps four offsets; the row step 4 ii LD
+//            goes into the base.  Columns past the matrix (EDGE) are clamped
+//            into those offsets.
+struct OpSrc {
+    const uint8_t* base;
+    uint32_t off[4];
+    uint32_t step;        // bytes between loads ii and ii + 1 (interior forms)
+    uint32_t ld;          // leading dimension (K-major: R; MN-major: P or Q)
+    int row, last;        // K-major EDGE: the lane's first row and the last valid row
+};
+
+struct Sources {
+    OpSrc a, b;
+};
+
+template <int L>
+__device__ __forceinline__ void set_op(OpSrc& s, const uint8_t* base, int origin, int extent, int R, int wave,
+                                       int lane)
 {
-    const int p = chunk ^ swz(row);
+    s.base = base;
+    if (L == kKMajor) {
+        s.ld = (uint32_t)R;
+        s.step = 8u * (uint32_t)R;
+        s.row = origin + wave * 64 + (lane >> 3);
+        s.last = extent - 1;
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            const int row = (wave * 8 + par) * 8 + (lane >> 3);      // row within the tile
+            const uint32_t c16 = (uint32_t)(((lane & 7) ^ swz(row)) * 16);
+            s.off[par] = c16;                                         // EDGE form: chunk only
+            s.off[par + 2] = (uint32_t)s.row * (uint32_t)R + c16;     // interior form
+        }
+    } else {
+        s.ld = (uint32_t)extent;
+        s.step = 4u * (uint32_t)extent;
+        s.row = 0;
+        s.last = 0;
+#pragma unroll
+        for (int idx = 0; idx < 4; ++idx) {
+            // ii bit 0 -> row bit 2, ii bit 2 -> row bit 4 (see swz_mn)
+            const int row = wave * 32 + (idx & 1) * 4 + (idx >> 1) * 16 + (lane >> 4);
+            int col = origin + (((lane & 15) ^ swz_mn(row)) * 16);
+            col = min(col, extent - 16);                            // only EDGE tiles reach past the end
+            s.off[idx] = (uint32_t)(wave * 32 + (lane >> 4)) * (uint32_t)extent + (uint32_t)col;
+        }
+    }
+}
+
+// Load ii (0..7) of one operand for the k-step kt.
+template <int L, bool EDGE>
+__device__ __forceinline__ void issue_op(const OpSrc& s, uint32_t lds, int kt, int ii)
+{
+    if (L == kKMajor) {
+        if (!EDGE) {
+            dma16(s.off[2 + (ii & 1)], s.base + ((size_t)ii * s.step + (size_t)kt * kBK), lds);
+        } else {
+            const int row = min(s.row + ii * 8, s.last);
+            dma16((uint32_t)row * s.ld + s.off[ii & 1], s.base + (size_t)kt * kBK, lds);
+        }
+    } else {
+        const int idx = (ii & 1) | (((ii >> 2) & 1) << 1);
+        dma16(s.off[idx], s.base + ((size_t)ii * s.step + (size_t)kt * kBK * s.ld), lds);
+    }
+}
+
+// Load idx (0..15) of a stage: 0..7 fill A, 8..15 fill B.
+template <bool EDGE, int LA, int LB>
+__device__ __forceinline__ void issue_one(const Sources& src, uint32_t stage, int kt, int wave, int idx)
+{
+    const int ii = idx & 7;
+    if (idx < 8) {
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(stage + (uint32_t)(wave * 8 + ii) * 1024u);
+        issue_op<LA, EDGE>(src.a, lds, kt, ii);
+    } else {
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(stage + (uint32_t)kStageA +
+                                                            (uint32_t)(wave * 8 + ii) * 1024u);
+        issue_op<LB, EDGE>(src.b, lds, kt, ii);
+    }
+}
+
+template <bool EDGE, int LA, int LB>
+__device__ __forceinline__ void issue_stage(const Sources& src, uint32_t stage, int kt, int wave)
+{
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) issue_one<EDGE, LA, LB>(src, stage, kt, wave, idx);
+}
+
+// Fragments of the 16x16x128 instruction: block b covers 16 rows of A (or of
+// B), lane l holds row (l % 16) of the block and the reduction bytes
+// 16 g .. 16 g + 15 and 64 + 16 g .. 64 + 16 g + 15 of the 128-byte step,
+// g = l / 16 (the same mapping for both operands, so the order of the
+// reduction within the instruction does not matter).  A wave owns 128 x 128
+// outputs = 8 x 8 blocks; `blk` is the block's index within the tile (0..15).
+__device__ __forceinline__ v8i frag_k(const uint8_t* tile, int blk, int lane)
+{
+    const int row = blk * 16 + (lane & 15);
+    const int p = (lane >> 4) ^ swz(row);
     const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * kBK + p * 16);
     const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * kBK + (p ^ 4) * 16);
     v8i r;
@@ -87,63 +211,31 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int chunk)
     return r;
 }
 
-// Global -> LDS sources of one wave.  Load ii (0..7) of wave w fills LDS rows
-// r = (w*8 + ii)*8 + L/8 of the A (B) stage, lane L at physical chunk L%8, i.e.
-// it reads logical chunk (L%8) ^ f(r).  f(r) depends on ii only through ii & 1,
-// so in the interior form a lane keeps two byte offsets per operand and the
-// row step 8 * ii * R goes into the uniform base.  Matrices with fewer than
-// 256 rows (EDGE) clamp each row to the last valid one instead.
-struct Sources {
-    const uint8_t* a;
-    const uint8_t* b;
-    uint32_t a_off[2];
-    uint32_t b_off[2];
-    uint32_t step;        // 8 rows
-    int a_row, b_row;     // EDGE: the lane's first row and the last valid row
-    int a_last, b_last;
-    uint32_t chunk16[2];
-};
-
-// Load idx (0..15) of a stage: 0..7 fill A, 8..15 fill B.
-template <bool EDGE>
-__device__ __forceinline__ void issue_one(const Sources& src, uint32_t stage, int k0, int wave, int idx)
+// MN-major: the block is the 16-byte column chunk `blk` of the 256-byte rows.
+// Lane l = 16 g + 2 t + e names row kb + t, bytes 8 e .. 8 e + 7 of that chunk,
+// for kb = 16 g, 16 g + 8, 64 + 16 g, 64 + 16 g + 8; h(kb + t) = t | (g & 1) << 3.
+__device__ __forceinline__ v8i frag_mn(const uint8_t* tile, int blk, int lane)
 {
-    const int ii = idx & 7;
-    const bool is_b = idx >= 8;
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(stage + (is_b ? (uint32_t)kStageA : 0u) +
-                                                        (uint32_t)(wave * 8 + ii) * 1024u);
-    const uint8_t* base = is_b ? src.b : src.a;
-    if (!EDGE) {
-        const uint32_t off = is_b ? src.b_off[ii & 1] : src.a_off[ii & 1];
-        dma16(off, base + ((size_t)ii * src.step + (size_t)k0), lds);
-    } else {
-        const uint32_t R = src.step / 8u;
-        const int row = is_b ? min(src.b_row + ii * 8, src.b_last) : min(src.a_row + ii * 8, src.a_last);
-        dma16((uint32_t)row * R + src.chunk16[ii & 1], base + k0, lds);
-    }
+    const int g = lane >> 4, t = (lane & 15) >> 1, e = lane & 1;
+    const int h = t | ((g & 1) << 3);
+    const uint32_t a = (uint32_t)(uintptr_t)tile + (uint32_t)((16 * g + t) * 256 + ((blk ^ h) * 16) + 8 * e);
+    const lds_u8* q = (const lds_u8*)(uintptr_t)a;
+    const v2i x0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(q));
+    const v2i x1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(q + 8 * 256));
+    const v2i x2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(q + 64 * 256));
+    const v2i x3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(q + 72 * 256));
+    v8i r;
+    r[0] = x0[0]; r[1] = x0[1]; r[2] = x1[0]; r[3] = x1[1];
+    r[4] = x2[0]; r[5] = x2[1]; r[6] = x3[0]; r[7] = x3[1];
+    return r;
 }
 
-template <bool EDGE>
-__device__ __forceinline__ void issue_stage(const Sources& src, uint32_t stage, int k0, int wave)
+template <int L>
+__device__ __forceinline__ v8i frag(const uint8_t* tile, int blk, int lane)
 {
-#pragma unroll
-    for (int idx = 0; idx < 16; ++idx) issue_one<EDGE>(src, stage, k0, wave, idx);
+    if (L == kKMajor) return frag_k(tile, blk, lane);
+    return frag_mn(tile, blk, lane);
 }
-
-// Fragments of the 16x16x128 instruction: block b of 16 rows, lane l holds row
-// l % 16 and the k bytes 16 g .. 16 g + 15 and 64 + 16 g .. 64 + 16 g + 15 of the
-// 128-byte step, g = l / 16 (the same k mapping for both operands, so the
-// order of k within the instruction does not matter).  With the row swizzle
-// above, each 16-byte LDS read of a block is free of bank conflicts on gfx950
-// (measured with SQ_LDS_BANK_CONFLICT; the pairing of chunks 2g, 2g + 1 costs
-// a 2-way conflict, 8 instead of 4 LDS cycles per read).  A wave owns
-// 128 x 128 outputs = 8 x 8 blocks.
-__device__ __forceinline__ v8i read_frag16(const uint8_t* tile, int row0, int lane)
-{
-    return lds_frag(tile, row0 + (lane & 15), lane >> 4);
-}
-
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 // acc[i][j] += A block i x B block j (the instruction's first source is the B
 // block, so each lane ends with 4 consecutive output columns of one row).
@@ -165,7 +257,7 @@ __device__ __forceinline__ void mma16(v4f (&acc)[8][8], const v8i& a, const v8i&
 // tile k+1 has landed.  The K loop body is [barrier, half 1 of step k, half 0
 // of step k+1], so each LDS read and its first use lie in one straight-line
 // body.
-template <int FA, int FB>
+template <int FA, int FB, int LA>
 __device__ __forceinline__ void half0(v4f (&acc)[8][8], const v8i (&bq)[8], const v8i (&alo)[4], v8i (&ahi)[4],
                                       const uint8_t* stage, int wm, int lane)
 {
@@ -173,14 +265,14 @@ __device__ __forceinline__ void half0(v4f (&acc)[8][8], const v8i (&bq)[8], cons
     for (int t = 0; t < 32; ++t) {
         const int j = t >> 2, i = t & 3;
         mma16<FA, FB>(acc, alo[i], bq[j], i, j);
-        if ((t & 7) == 1) ahi[t >> 3] = read_frag16(stage, wm * 128 + (4 + (t >> 3)) * 16, lane);
+        if ((t & 7) == 1) ahi[t >> 3] = frag<LA>(stage, wm * 8 + 4 + (t >> 3), lane);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-template <int FA, int FB, bool EDGE, bool NEXT>
+template <int FA, int FB, bool EDGE, int LA, int LB, bool NEXT>
 __device__ __forceinline__ void half1(v4f (&acc)[8][8], v8i (&bq)[8], v8i (&alo)[4], const v8i (&ahi)[4],
-                                      const Sources& src, uint32_t cur_addr, const uint8_t* nxt, int k_issue,
+                                      const Sources& src, uint32_t cur_addr, const uint8_t* nxt, int kt_issue,
                                       int wave, int wm, int wn, int lane)
 {
 #pragma unroll
@@ -188,9 +280,9 @@ __device__ __forceinline__ void half1(v4f (&acc)[8][8], v8i (&bq)[8], v8i (&alo)
         const int j = t >> 2, i = t & 3;
         mma16<FA, FB>(acc, ahi[i], bq[j], 4 + i, j);
         if (NEXT) {
-            if (i == 3) bq[j] = read_frag16(nxt + kStageA, wn * 128 + j * 16, lane);
-            if ((t & 7) == 1) alo[t >> 3] = read_frag16(nxt, wm * 128 + (t >> 3) * 16, lane);
-            if ((t & 1) == 0) issue_one<EDGE>(src, cur_addr, k_issue, wave, t >> 1);
+            if (i == 3) bq[j] = frag<LB>(nxt + kStageA, wn * 8 + j, lane);
+            if ((t & 7) == 1) alo[t >> 3] = frag<LA>(nxt, wm * 8 + (t >> 3), lane);
+            if ((t & 1) == 0) issue_one<EDGE, LA, LB>(src, cur_addr, kt_issue, wave, t >> 1);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -201,6 +293,40 @@ __device__ __forceinline__ void mid_step_barrier()
     __builtin_amdgcn_s_waitcnt(kWaitVm0);     // the next tile has landed (this wave's loads)
     __syncthreads();                          // ... for all waves; the current stage fully read
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// The reduction of one tile whose first two stages have been issued: zero the
+// accumulators, run the K loop, and return with every load of the tile landed
+// and every wave done with the LDS stages.
+template <int FA, int FB, bool EDGE, int LA, int LB>
+__device__ __forceinline__ void tile_mainloop(v4f (&acc)[8][8], v8i (&bq)[8], v8i (&alo)[4], v8i (&ahi)[4],
+                                              const Sources& src, uint8_t* lds, uint32_t lds_addr, int KT, int wave,
+                                              int wm, int wn, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
+    __builtin_amdgcn_s_waitcnt(kWaitVm16);    // stage 0 landed; stage 1's 16 loads may be in flight
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bq[j] = frag<LB>(lds + kStageA, wn * 8 + j, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) alo[i] = frag<LA>(lds, wm * 8 + i, lane);
+    half0<FA, FB, LA>(acc, bq, alo, ahi, lds, wm, lane);
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+        const int cur = kt & 1;
+        mid_step_barrier();
+        half1<FA, FB, EDGE, LA, LB, true>(acc, bq, alo, ahi, src, lds_addr + cur * kStage, lds + (cur ^ 1) * kStage,
+                                          min(kt + 2, KT - 1), wave, wm, wn, lane);
+        half0<FA, FB, LA>(acc, bq, alo, ahi, lds + (cur ^ 1) * kStage, wm, lane);
+    }
+    mid_step_barrier();
+    half1<FA, FB, EDGE, LA, LB, false>(acc, bq, alo, ahi, src, 0, lds, 0, wave, wm, wn, lane);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
 }
 
 // A launch covers a group of up to kMaxGroup independent problems of the same
@@ -217,6 +343,7 @@ struct GemmProblem {
     const float* inv_b;
     uint16_t* out;
     int P, Q, R;
+    int la, lb;           // operand layouts
     int tiles_m, tiles_n;
     int first_tile;
 };
@@ -235,6 +362,7 @@ struct Work {
     const float* inv_a;
     const float* inv_b;
     int P, Q, R, KT;
+    int la, lb;
     int ms, ns;     // logical origin (first row / column this tile stores)
     int m0, n0;     // origin actually computed (shifted back inside the matrix)
 };
@@ -257,6 +385,8 @@ __device__ __forceinline__ Work work_of(const GemmGroup& g, int v)
     w.Q = pr.Q;
     w.R = pr.R;
     w.KT = pr.R / kBK;
+    w.la = pr.la;
+    w.lb = pr.lb;
     const int lv = v - pr.first_tile;
     const int group_size = kGroupM * pr.tiles_n;
     const int group = lv / group_size;
@@ -272,21 +402,34 @@ __device__ __forceinline__ Work work_of(const GemmGroup& g, int v)
     return w;
 }
 
+template <int LA, int LB>
 __device__ __forceinline__ void set_sources(Sources& src, const Work& w, int wave, int lane)
 {
-    src.a = w.A;
-    src.b = w.B;
-    src.a_last = w.P - 1;
-    src.b_last = w.Q - 1;
-    src.step = 8u * (uint32_t)w.R;
-    src.a_row = w.m0 + wave * 64 + (lane >> 3);
-    src.b_row = w.n0 + wave * 64 + (lane >> 3);
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-        const int row = (wave * 8 + par) * 8 + (lane >> 3);     // row within the tile
-        src.chunk16[par] = (uint32_t)(((lane & 7) ^ swz(row)) * 16);
-        src.a_off[par] = (uint32_t)src.a_row * (uint32_t)w.R + src.chunk16[par];
-        src.b_off[par] = (uint32_t)src.b_row * (uint32_t)w.R + src.chunk16[par];
+    set_op<LA>(src.a, w.A, w.m0, w.P, w.R, wave, lane);
+    set_op<LB>(src.b, w.B, w.n0, w.Q, w.R, wave, lane);
+}
+
+// Operand-layout sets a kernel is compiled for: every problem of a launch uses
+// one of the set's (A, B) layout pairs.
+constexpr int kSetKK = 0;       // (K, K)
+constexpr int kSetMN = 1;       // (K, MN) and (MN, MN)
+
+// Set up the sources of tile w and issue its first two stages.
+template <bool EDGE, int SET>
+__device__ __forceinline__ void start_tile(Sources& src, const Work& w, uint32_t lds_addr, int wave, int lane)
+{
+    if (SET == kSetKK) {
+        set_sources<kKMajor, kKMajor>(src, w, wave, lane);
+        issue_stage<EDGE, kKMajor, kKMajor>(src, lds_addr, 0, wave);
+        issue_stage<EDGE, kKMajor, kKMajor>(src, lds_addr + kStage, min(1, w.KT - 1), wave);
+    } else if (w.la == kMNMajor) {
+        set_sources<kMNMajor, kMNMajor>(src, w, wave, lane);
+        issue_stage<EDGE, kMNMajor, kMNMajor>(src, lds_addr, 0, wave);
+        issue_stage<EDGE, kMNMajor, kMNMajor>(src, lds_addr + kStage, min(1, w.KT - 1), wave);
+    } else {
+        set_sources<kKMajor, kMNMajor>(src, w, wave, lane);
+        issue_stage<EDGE, kKMajor, kMNMajor>(src, lds_addr, 0, wave);
+        issue_stage<EDGE, kKMajor, kMNMajor>(src, lds_addr + kStage, min(1, w.KT - 1), wave);
     }
 }
 
@@ -296,7 +439,7 @@ __device__ __forceinline__ void set_sources(Sources& src, const Work& w, int wav
 // every round the 32 CUs of one XCD work on 32 consecutive tiles of the raster
 // order.  While a tile's epilogue stores run, the first two stages of the next
 // tile are already loading.
-template <int FA, int FB, bool EDGE>
+template <int FA, int FB, bool EDGE, int SET>
 __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
@@ -318,45 +461,24 @@ __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
     int v = slot;
     if (v >= g.total_tiles) return;
     Work w = work_of<EDGE>(g, v);
-    set_sources(src, w, wave, lane);
-    issue_stage<EDGE>(src, lds_addr, 0, wave);
-    issue_stage<EDGE>(src, lds_addr + kStage, min(1, w.KT - 1) * kBK, wave);
+    start_tile<EDGE, SET>(src, w, lds_addr, wave, lane);
     for (;;) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
-        __builtin_amdgcn_s_waitcnt(kWaitVm16);    // stage 0 landed; stage 1's 16 loads may be in flight
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 8; ++j) bq[j] = read_frag16(lds + kStageA, wn * 128 + j * 16, lane);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) alo[i] = read_frag16(lds, wm * 128 + i * 16, lane);
-        half0<FA, FB>(acc, bq, alo, ahi, lds, wm, lane);
-        const int KT = w.KT;
-        for (int kt = 0; kt + 1 < KT; ++kt) {
-            const int cur = kt & 1;
-            mid_step_barrier();
-            half1<FA, FB, EDGE, true>(acc, bq, alo, ahi, src, lds_addr + cur * kStage, lds + (cur ^ 1) * kStage,
-                                      min(kt + 2, KT - 1) * kBK, wave, wm, wn, lane);
-            half0<FA, FB>(acc, bq, alo, ahi, lds + (cur ^ 1) * kStage, wm, lane);
-        }
-        mid_step_barrier();
-        half1<FA, FB, EDGE, false>(acc, bq, alo, ahi, src, 0, lds, 0, wave, wm, wn, lane);
-        // every load of this tile has landed and every wave is done with LDS
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        __syncthreads();
+        if (SET == kSetKK)
+            tile_mainloop<FA, FB, EDGE, kKMajor, kKMajor>(acc, bq, alo, ahi, src, lds, lds_addr, w.KT, wave, wm, wn,
+                                                          lane);
+        else if (w.la == kMNMajor)
+            tile_mainloop<FA, FB, EDGE, kMNMajor, kMNMajor>(acc, bq, alo, ahi, src, lds, lds_addr, w.KT, wave, wm,
+                                                            wn, lane);
+        else
+            tile_mainloop<FA, FB, EDGE, kKMajor, kMNMajor>(acc, bq, alo, ahi, src, lds, lds_addr, w.KT, wave, wm, wn,
+                                                           lane);
 
         const Work done = w;
         const int next = v + G;
         if (next < g.total_tiles) {
             v = next;
             w = work_of<EDGE>(g, v);
-            set_sources(src, w, wave, lane);
-            issue_stage<EDGE>(src, lds_addr, 0, wave);
-            issue_stage<EDGE>(src, lds_addr + kStage, min(1, w.KT - 1) * kBK, wave);
+            start_tile<EDGE, SET>(src, w, lds_addr, wave, lane);
         }
 
         // ---- epilogue of `done`: descale and round to bf16, stage 32-row chunks of
@@ -403,8 +525,8 @@ __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
     }
 }
 
-static GemmProblem make_problem(const uint8_t* A, const uint8_t* B, const float* inv_a, const float* inv_b,
-                                void* out, int64_t P, int64_t Q, int64_t R)
+static GemmProblem make_problem(const uint8_t* A, int la, const uint8_t* B, int lb, const float* inv_a,
+                                const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R)
 {
     GemmProblem p;
     p.A = A;
@@ -415,13 +537,15 @@ static GemmProblem make_problem(const uint8_t* A, const uint8_t* B, const float*
     p.P = (int)P;
     p.Q = (int)Q;
     p.R = (int)R;
+    p.la = la;
+    p.lb = lb;
     p.tiles_m = (int)((P + kBM - 1) / kBM);
     p.tiles_n = (int)((Q + kBN - 1) / kBN);
     p.first_tile = 0;
     return p;
 }
 
-template <int FA, int FB>
+template <int FA, int FB, int SET>
 static hipError_t launch_group(GemmGroup g, hipStream_t stream)
 {
     bool edge = false;
@@ -434,38 +558,50 @@ static hipError_t launch_group(GemmGroup g, hipStream_t stream)
     g.total_tiles = total;
     const int grid = total < device_cu_count() ? total : device_cu_count();   // one workgroup per CU
     if (!edge)
-        gemm_tn_kernel<FA, FB, false><<<grid, 256, 0, stream>>>(g);
+        gemm_tn_kernel<FA, FB, false, SET><<<grid, 256, 0, stream>>>(g);
     else
-        gemm_tn_kernel<FA, FB, true><<<grid, 256, 0, stream>>>(g);
+        gemm_tn_kernel<FA, FB, true, SET><<<grid, 256, 0, stream>>>(g);
     return hipGetLastError();
 }
 
+// B is always E4M3 (weights or activations); A is E4M3 or E5M2.  Layout sets:
+// every problem (K, K), or every problem (K, MN) / (MN, MN).
 static hipError_t dispatch(int fmt_a, int fmt_b, const GemmGroup& g, hipStream_t stream)
 {
-    if (fmt_a == 0 && fmt_b == 0) return launch_group<0, 0>(g, stream);
-    if (fmt_a == 1 && fmt_b == 0) return launch_group<1, 0>(g, stream);
-    if (fmt_a == 0 && fmt_b == 1) return launch_group<0, 1>(g, stream);
-    return launch_group<1, 1>(g, stream);
+    for (int i = 0; i < g.count; ++i) {
+        const GemmProblem& p = g.p[i];
+        const bool kk = p.la == kKMajor && p.lb == kKMajor;
+        const bool mn = p.lb == kMNMajor;
+        if (!(kk || mn) || (g.p[0].lb != p.lb)) return hipErrorInvalidValue;
+    }
+    if (fmt_b != 0) return hipErrorInvalidValue;
+    if (g.p[0].lb == kKMajor) {
+        if (fmt_a == 0) return launch_group<0, 0, kSetKK>(g, stream);
+        return launch_group<1, 0, kSetKK>(g, stream);
+    }
+    if (fmt_a == 0) return launch_group<0, 0, kSetMN>(g, stream);
+    return launch_group<1, 0, kSetMN>(g, stream);
 }
 
-hipError_t launch_gemm_tn(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* inv_a,
-                          const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream)
+hipError_t launch_gemm_tn(const uint8_t* A, int fmt_a, int la, const uint8_t* B, int fmt_b, int lb,
+                          const float* inv_a, const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R,
+                          hipStream_t stream)
 {
     GemmGroup g;
-    g.p[0] = make_problem(A, B, inv_a, inv_b, out, P, Q, R);
+    g.p[0] = make_problem(A, la, B, lb, inv_a, inv_b, out, P, Q, R);
     g.p[1] = g.p[0];
     g.count = 1;
     return dispatch(fmt_a, fmt_b, g, stream);
 }
 
-hipError_t launch_gemm_tn_pair(const uint8_t* A0, const uint8_t* B0, const float* ia0, const float* ib0, void* out0,
-                               int64_t P0, int64_t Q0, int64_t R0, const uint8_t* A1, const uint8_t* B1,
-                               const float* ia1, const float* ib1, void* out1, int64_t P1, int64_t Q1, int64_t R1,
-                               int fmt_a, int fmt_b, hipStream_t stream)
+hipError_t launch_gemm_tn_pair(const uint8_t* A0, int la0, const uint8_t* B0, int lb0, const float* ia0,
+                               const float* ib0, void* out0, int64_t P0, int64_t Q0, int64_t R0, const uint8_t* A1,
+                               int la1, const uint8_t* B1, int lb1, const float* ia1, const float* ib1, void* out1,
+                               int64_t P1, int64_t Q1, int64_t R1, int fmt_a, int fmt_b, hipStream_t stream)
 {
     GemmGroup g;
-    GemmProblem p0 = make_problem(A0, B0, ia0, ib0, out0, P0, Q0, R0);
-    GemmProblem p1 = make_problem(A1, B1, ia1, ib1, out1, P1, Q1, R1);
+    GemmProblem p0 = make_problem(A0, la0, B0, lb0, ia0, ib0, out0, P0, Q0, R0);
+    GemmProblem p1 = make_problem(A1, la1, B1, lb1, ia1, ib1, out1, P1, Q1, R1);
     // longest reduction first: the first round then starts the longest tiles
     g.p[0] = R1 > R0 ? p1 : p0;
     g.p[1] = R1 > R0 ? p0 : p1;

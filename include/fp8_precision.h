@@ -174,6 +174,37 @@ fp8_status fp8_gemm_backward(const uint8_t* dyq, const uint8_t* dyqt, fp8_fmt dy
                              const float* inv_sdy, const float* inv_sw, const float* inv_sx,
                              void* dx, void* dw, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/*
+ * The backward products on the untransposed FP8 tensors: the operands the
+ * transposed copies would hold are read in their stored layout instead
+ * (row-major along the product's output index, "MN-major"), staged through
+ * LDS and fed to the matrix instructions with gfx950's transposing LDS reads.
+ * The quantise and SwiGLU calls then need no qt / hqt outputs for the
+ * backward pass (LLMQ summary, section 4: backward-pass transposes and the
+ * extra transpose/quantisation buffers are overhead of FP8 training).  The
+ * results are bit-identical to fp8_gemm_dgrad / fp8_gemm_wgrad /
+ * fp8_gemm_backward on the transposed copies.
+ *
+ * fp8_gemm_dgrad_mn:  dX[M, K] = dY[M, N] . W[N, K]      dyq (dy_fmt) [M, N], wq (e4m3) [N, K]
+ * fp8_gemm_wgrad_mn:  dW[N, K] = dY[M, N]^T . X[M, K]    dyq (dy_fmt) [M, N], xq (e4m3) [M, K]
+ * fp8_gemm_backward_mn: both, in one launch (outputs must not overlap each
+ *                     other or any input)
+ *
+ *   inv_*   fp32 scalars as for the calls above
+ * Constraints: those of fp8_gemm_dgrad / fp8_gemm_wgrad (every dimension a
+ * multiple of 16 and >= 16; the reduction length, N for dgrad and M for
+ * wgrad, a multiple of 128).
+ */
+fp8_status fp8_gemm_dgrad_mn(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_t* wq,
+                             const float* inv_sdy, const float* inv_sw, void* dx,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
+fp8_status fp8_gemm_wgrad_mn(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_t* xq,
+                             const float* inv_sdy, const float* inv_sx, void* dw,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
+fp8_status fp8_gemm_backward_mn(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_t* wq, const uint8_t* xq,
+                                const float* inv_sdy, const float* inv_sw, const float* inv_sx,
+                                void* dx, void* dw, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,7 +42,8 @@ def lib():
 def test_header_declares_the_hot_path():
     names = declared_functions()
     for want in ("fp8_absmax", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd", "fp8_gemm_dgrad",
-                 "fp8_gemm_wgrad", "fp8_gemm_backward", "fp8_status_string", "fp8_last_error"):
+                 "fp8_gemm_wgrad", "fp8_gemm_backward", "fp8_gemm_dgrad_mn", "fp8_gemm_wgrad_mn",
+                 "fp8_gemm_backward_mn", "fp8_status_string", "fp8_last_error"):
         assert want in names
 
 
@@ -143,6 +144,42 @@ def test_backward_validation(lib):
     bad = list(ok); bad[2] = 5
     assert f(*bad) == INVALID
     bad = list(ok); bad[10] = 200                # M not a multiple of 16 / 128
+    assert f(*bad) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("entry", ["dgrad_mn", "wgrad_mn"])
+def test_gemm_mn_validation(lib, entry):
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    f = getattr(lib, "fp8_gemm_" + entry)
+    f.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp]
+    f.restype = i32
+    call = lambda a, b, ia, ib, out, M, N, K, fmt=1: f(a, fmt, b, ia, ib, out, M, N, K, None)
+    assert call(None, B16, C16, C16 + 4, D16, 128, 128, 128) == INVALID
+    assert call(A16, B16, C16, C16 + 4, None, 128, 128, 128) == INVALID
+    assert call(A16, B16, C16, C16 + 4, D16, 128, 128, 128, fmt=3) == INVALID
+    assert call(A16, B16, C16, C16 + 4, B16, 128, 128, 128) == INVALID       # out aliases B
+    red = {"dgrad_mn": (128, 192, 128), "wgrad_mn": (192, 128, 128)}[entry]
+    assert call(A16, B16, C16, C16 + 4, D16, *red) == UNSUPPORTED            # reduction % 128
+    assert call(A16, B16, C16, C16 + 4, D16, 128, 128, 136) == UNSUPPORTED  # K % 16
+    assert call(A16, B16 + 8, C16, C16 + 4, D16, 128, 128, 128) == UNSUPPORTED
+
+
+def test_backward_mn_validation(lib):
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    f = lib.fp8_gemm_backward_mn
+    f.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    f.restype = i32
+    F16 = 0x60000000
+    ok = (A16, 1, C16, D16, E16, E16 + 4, E16 + 8, F16, F16 + (1 << 24), 256, 256, 256, None)
+    bad = list(ok); bad[0] = None
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[8] = F16 + 1024         # dw overlaps dx
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[7] = C16                # dx aliases wq
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[1] = 5
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[9] = 200                # M not a multiple of 16 / 128
     assert f(*bad) == UNSUPPORTED
 
 
