@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the FP8 training hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of synthetic input at
-7B-class shapes (M = 4096 tokens, d = 4096, ffn = 11008): for the QKV, O,
-gate/up and down linears, forward and backward --
+One step = one pass of the whole path over one batch of synthetic input at the
+shapes of one workload configuration (default c3: the 7B-class layer, M = 4096
+tokens, d = 4096, ffn = 11008): for the QKV, O, gate/up and down linears,
+forward and backward --
 
   forward:  absmax -> quantise to e4m3 (with the transposed copies the
             backward reads) for X and W -> FP8 GEMM -> bf16 Y; the gate/up
@@ -12,15 +13,19 @@ gate/up and down linears, forward and backward --
   backward: absmax -> quantise dY to e5m2 (+ transposed copy) -> dgrad
             (dY . W) and wgrad (dY^T . X) FP8 GEMMs -> bf16.
 
+--workload c4 runs the 14B-class shapes (M = 8192, Student-t activations with
+outlier channels); c5 the 32B-class shapes (M = 16384) with the MLP block
+recomputed in the backward from the retained absmax statistics.
 --layout mn runs the same step without the transposed FP8 copies: the
 quantise and SwiGLU calls write only the row-major codes and the backward
 GEMMs read W, X, dY and h untransposed (fp8_gemm_backward_mn).
 
-`value` is the step's GEMM work (2MNK summed over the 12 GEMMs) divided by the
+`value` is the step's GEMM work (2MNK summed over the GEMMs) divided by the
 wall time of the whole step, quantisation included: effective FP8 TFLOP/s.
 Inputs are resident in HBM before the timed region starts.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout copies|mn] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c4|c5]
+                       [--layout copies|mn] [--breakdown] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -72,10 +77,30 @@ class Op:
         self.meta = meta or {}
 
 
-def build_layer7b(fp8, dev, layout="copies"):
-    """Inputs and the ordered list of calls of one 7B-layer step."""
+WORKLOADS = {
+    "c3": "7B-class layer (d=4096, ffn=11008, QKV 4096->12288, M=4096 tokens): the four linears fwd+bwd, "
+          "MLP forward chained through the fused SwiGLU requant",
+    "c4": "14B-class layer (d=5120, ffn=13824, QKV 5120->7168, M=8192 tokens): the four linears fwd+bwd, "
+          "Student-t(3) activations with 0.1% outlier channels x50, MLP forward chained through the SwiGLU requant",
+    "c5": "32B-class layer (d=5120, ffn=27648, QKV 5120->7168, M=16384 tokens): the four linears fwd+bwd, "
+          "MLP forward chained; backward recomputes the MLP block from the retained absmax statistics",
+}
+
+
+def build_step(fp8, dev, cfg_name="c3", layout="copies"):
+    """Inputs and the ordered list of calls of one layer step of a configuration.
+
+    Forward: absmax + quantise of X and W, FP8 GEMM, for QKV, O and gate/up;
+    the fused SwiGLU requant of the gate/up output feeds the down linear.
+    Backward: absmax + e5m2 quantise of dY, then dgrad and wgrad in one launch.
+    With recomputation (c5) the backward first re-quantises the retained bf16
+    gate/up input with its retained absmax, reruns the gate/up GEMM and
+    requantises the SwiGLU output with the retained absmax_h (no reduction), and
+    the forward keeps no transposed copies for the MLP block.
+    """
     mn = layout == "mn"
-    cfg = workloads.CONFIGS["c3"]
+    cfg = workloads.CONFIGS[cfg_name]
+    recompute = cfg.recompute
     M = cfg.M
     E4M3, E5M2 = fp8.E4M3, fp8.E5M2
     ops = []
@@ -84,16 +109,34 @@ def build_layer7b(fp8, dev, layout="copies"):
     u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
     bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)
     lin = {l.name: (i, l) for i, l in enumerate(cfg.linears)}
+    gemm_fwd_kernel = GEMM_KERNEL[(0, 0, 0)]
 
-    def quant_ops(tag, x, rows, cols, fmt):
-        am, sc, inv = f32(), f32(), f32()
-        q, qt = u8(rows, cols), (None if mn else u8(cols, rows))
+    def quantize_op(tag, x, rows, cols, fmt, am, want_qt):
+        sc, inv = f32(), f32()
+        q, qt = u8(rows, cols), (u8(cols, rows) if want_qt else None)
         n = rows * cols
-        ops.append(Op(f"absmax {tag}", lambda: fp8.absmax(x, am), "absmax", 2 * n,
-                      meta={"rows": rows, "cols": cols, "fmt": fmt}))
         ops.append(Op(f"quantize {tag}", lambda: fp8.quantize(x, fmt, am, q=q, qt=qt, scale=sc, inv_scale=inv),
-                      "quantize", (3 if mn else 4) * n, meta={"rows": rows, "cols": cols, "fmt": fmt, "qt": not mn}))
+                      "quantize", (4 if want_qt else 3) * n, meta={"rows": rows, "cols": cols, "fmt": fmt,
+                                                                   "qt": want_qt}))
         return q, qt, inv
+
+    def quant_ops(tag, x, rows, cols, fmt, want_qt):
+        am = f32()
+        ops.append(Op(f"absmax {tag}", lambda: fp8.absmax(x, am), "absmax", 2 * rows * cols,
+                      meta={"rows": rows, "cols": cols, "fmt": fmt}))
+        return quantize_op(tag, x, rows, cols, fmt, am, want_qt) + (am,)
+
+    def gemm_fwd_op(tag, xq, wq, ix, iw, y, L):
+        ops.append(Op(f"gemm_fwd {tag}", lambda: fp8.gemm_fwd(xq, wq, ix, iw, y), "gemm", 2 * M * L.N * L.K,
+                      gemm_fwd_kernel, {"probs": [(M, L.N, L.K, E4M3)]}))
+
+    def swiglu_op(tag, gu, am_h, compute, want_hqt, F):
+        hq, hqt, inv_h = u8(M, F), (u8(F, M) if want_hqt else None), f32()
+        work = (4 * M * F if compute else 0) + (6 if want_hqt else 5) * M * F
+        ops.append(Op(f"swiglu_requant {tag}", lambda: fp8.swiglu_requant(gu, am_h, compute, hq=hq, hqt=hqt,
+                                                                         inv_scale_h=inv_h),
+                      "swiglu", work, meta={"M": M, "F": F, "qt": want_hqt, "compute": compute}))
+        return hq, hqt, inv_h
 
     # ---- forward
     fwd = {}
@@ -102,43 +145,50 @@ def build_layer7b(fp8, dev, layout="copies"):
         x = workloads.draw_x(cfg, li).to(dev)
         w = workloads.draw_w(cfg, li).to(dev)
         bufs[name] = (x, w)
-        xq, xqt, inv_x = quant_ops(f"X_{name}", x, M, L.K, E4M3)
-        wq, wqt, inv_w = quant_ops(f"W_{name}", w, L.N, L.K, E4M3)
+        keep_xt = not mn and not (recompute and name == "gate_up")
+        xq, xqt, inv_x, am_x = quant_ops(f"X_{name}", x, M, L.K, E4M3, keep_xt)
+        wq, wqt, inv_w, _ = quant_ops(f"W_{name}", w, L.N, L.K, E4M3, not mn)
         y = bf(M, L.N)
-        ops.append(Op(f"gemm_fwd {name}", lambda xq=xq, wq=wq, ix=inv_x, iw=inv_w, y=y: fp8.gemm_fwd(xq, wq, ix, iw, y),
-                      "gemm", 2 * M * L.N * L.K, GEMM_KERNEL[(0, 0, 0)], {"probs": [(M, L.N, L.K, E4M3)]}))
-        fwd[name] = (xq, wq, xqt, wqt, inv_x, inv_w, y)
+        gemm_fwd_op(name, xq, wq, inv_x, inv_w, y, L)
+        fwd[name] = {"x": x, "am_x": am_x, "xq": xq, "wq": wq, "xqt": xqt, "wqt": wqt, "inv_x": inv_x,
+                     "inv_w": inv_w, "y": y}
     # SwiGLU requantisation of the gate/up output feeds the down linear
     li, L = lin["down"]
     F = L.K
-    gu = fwd["gate_up"][6]
-    am_h, inv_h = f32(), f32()
-    hq, hqt = u8(M, F), (None if mn else u8(F, M))
-    ops.append(Op("swiglu_requant fwd", lambda: fp8.swiglu_requant(gu, am_h, True, hq=hq, hqt=hqt, inv_scale_h=inv_h),
-                  "swiglu", 4 * M * F + (5 if mn else 6) * M * F, meta={"M": M, "F": F, "qt": not mn}))
+    am_h = f32()
+    hq, hqt, inv_h = swiglu_op("fwd", fwd["gate_up"]["y"], am_h, True, not mn and not recompute, F)
     w = workloads.draw_w(cfg, li).to(dev)
     bufs["down"] = (None, w)
-    wq, wqt, inv_w = quant_ops("W_down", w, L.N, L.K, E4M3)
+    wq, wqt, inv_w, _ = quant_ops("W_down", w, L.N, L.K, E4M3, not mn)
     y = bf(M, L.N)
-    ops.append(Op("gemm_fwd down", lambda: fp8.gemm_fwd(hq, wq, inv_h, inv_w, y), "gemm", 2 * M * L.N * L.K,
-                  GEMM_KERNEL[(0, 0, 0)], {"probs": [(M, L.N, L.K, E4M3)]}))
-    fwd["down"] = (hq, wq, hqt, wqt, inv_h, inv_w, y)
+    gemm_fwd_op("down", hq, wq, inv_h, inv_w, y, L)
+    fwd["down"] = {"xq": hq, "wq": wq, "xqt": hqt, "wqt": wqt, "inv_x": inv_h, "inv_w": inv_w, "y": y}
 
     # ---- backward
+    if recompute:
+        # MLP block recomputation from the retained bf16 input and absmax statistics: no reduction runs
+        _, Lg = lin["gate_up"]
+        g = fwd["gate_up"]
+        xq, xqt, inv_x = quantize_op("X_gate_up (recompute)", g["x"], M, Lg.K, E4M3, g["am_x"], not mn)
+        gu2 = bf(M, Lg.N)
+        gemm_fwd_op("gate_up (recompute)", xq, g["wq"], inv_x, g["inv_w"], gu2, Lg)
+        g.update({"xq": xq, "xqt": xqt, "inv_x": inv_x})
+        hq2, hqt2, inv_h2 = swiglu_op("recompute", gu2, am_h, False, not mn, F)
+        fwd["down"].update({"xq": hq2, "xqt": hqt2, "inv_x": inv_h2})
     for name in ("qkv", "o", "gate_up", "down"):
         li, L = lin[name]
         dy = workloads.draw_dy(cfg, li).to(dev)
-        xq, wq, xqt, wqt, inv_x, inv_w, _ = fwd[name]
-        dyq, dyqt, inv_dy = quant_ops(f"dY_{name}", dy, M, L.N, E5M2)
+        f = fwd[name]
+        dyq, dyqt, inv_dy, _ = quant_ops(f"dY_{name}", dy, M, L.N, E5M2, not mn)
         dx = bf(M, L.K)
         dw = bf(L.N, L.K)
         # dgrad dX = dY . W and wgrad dW = dY^T . X in one launch
         if mn:
-            fn = (lambda dyq=dyq, wq=wq, xq=xq, a=inv_dy, b=inv_w, c=inv_x, dx=dx, dw=dw:
+            fn = (lambda dyq=dyq, wq=f["wq"], xq=f["xq"], a=inv_dy, b=f["inv_w"], c=f["inv_x"], dx=dx, dw=dw:
                   fp8.gemm_backward_mn(dyq, E5M2, wq, xq, a, b, c, dx, dw))
         else:
-            fn = (lambda dyq=dyq, dyqt=dyqt, wqt=wqt, xqt=xqt, a=inv_dy, b=inv_w, c=inv_x, dx=dx, dw=dw:
-                  fp8.gemm_backward(dyq, dyqt, E5M2, wqt, xqt, a, b, c, dx, dw))
+            fn = (lambda dyq=dyq, dyqt=dyqt, wqt=f["wqt"], xqt=f["xqt"], a=inv_dy, b=f["inv_w"], c=f["inv_x"],
+                  dx=dx, dw=dw: fp8.gemm_backward(dyq, dyqt, E5M2, wqt, xqt, a, b, c, dx, dw))
         ops.append(Op(f"gemm_backward {name}", fn, "gemm", 4 * M * L.N * L.K, GEMM_KERNEL[(1, 0, 1 if mn else 0)],
                       {"probs": [(M, L.K, L.N, E5M2), (L.N, L.K, M, E5M2)]}))
         bufs["dy_" + name] = dy
@@ -178,11 +228,15 @@ def time_steps(ops, steps, stream, instrument_kinds=("gemm",)):
     return wall, start.elapsed_time(end) * 1e-3, per_op
 
 
+STREAM_SAMPLE_ELEMS = 1 << 25      # oracle sample of a streaming call: at most 32 M elements
+
+
 def cpu_baseline(ops, gemm_rows):
     """The oracle, as it stands, on a bounded sample of the same step, scaled to a full step.
 
-    Sample: every absmax / quantise / SwiGLU call over its full tensor (random
-    bf16 of the same shape); every GEMM on `gemm_rows` and 2 * `gemm_rows`
+    Sample: every absmax / quantise / SwiGLU call on its tensor's shape (random
+    bf16), cut to its first rows when larger than STREAM_SAMPLE_ELEMS elements
+    and scaled by the row count; every GEMM on `gemm_rows` and 2 * `gemm_rows`
     output rows, extrapolated linearly to all its rows.
     """
     import oracle
@@ -192,6 +246,11 @@ def cpu_baseline(ops, gemm_rows):
     est = 0.0
     gemm_flop = 0.0
     t_start = time.perf_counter()
+
+    def sample_rows(rows, cols):
+        r = max(16, min(rows, STREAM_SAMPLE_ELEMS // cols // 16 * 16))
+        return r, rows / r
+
     for op in ops:
         m = op.meta
         if op.kind == "gemm":
@@ -209,25 +268,30 @@ def cpu_baseline(ops, gemm_rows):
                 est += fixed + per_row * P
                 gemm_flop += 2.0 * P * Q * R
         elif op.kind == "absmax":
-            x = rng.integers(0, 0x3F80, (m["rows"], m["cols"]), dtype=np.uint16)
+            r, f = sample_rows(m["rows"], m["cols"])
+            x = rng.integers(0, 0x3F80, (r, m["cols"]), dtype=np.uint16)
             t = time.perf_counter()
             oracle.absmax_bf16(x)
-            est += time.perf_counter() - t
+            est += (time.perf_counter() - t) * f
         elif op.kind == "quantize":
-            x = rng.integers(0, 0x3F80, (m["rows"], m["cols"]), dtype=np.uint16)
+            r, f = sample_rows(m["rows"], m["cols"])
+            x = rng.integers(0, 0x3F80, (r, m["cols"]), dtype=np.uint16)
+            s_, _ = oracle.scale(np.float32(1.0), m["fmt"])
             t = time.perf_counter()
-            s_, _ = oracle.scale(oracle.absmax_bf16(x), m["fmt"])
             oracle.quantize(x, m["fmt"], s_, want_q=True, want_qt=m["qt"])
-            est += time.perf_counter() - t
+            est += (time.perf_counter() - t) * f
         elif op.kind == "swiglu":
-            gu = rng.integers(0, 0x4080, (m["M"], 2 * m["F"]), dtype=np.uint16)
+            r, f = sample_rows(m["M"], 2 * m["F"])
+            gu = rng.integers(0, 0x4080, (r, 2 * m["F"]), dtype=np.uint16)
             t = time.perf_counter()
-            oracle.swiglu_requant(gu, want_hq=True, want_hqt=m["qt"])
-            est += time.perf_counter() - t
+            oracle.swiglu_requant(gu, absmax_h=None if m["compute"] else np.float32(8.0), want_hq=True,
+                                  want_hqt=m["qt"])
+            est += (time.perf_counter() - t) * f
     spent = time.perf_counter() - t_start
     return {"value": round(gemm_flop / est / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": (f"every absmax/quantise/SwiGLU call of the step over its full tensor, every GEMM on "
-                       f"{gemm_rows} and {2 * gemm_rows} output rows extrapolated to all rows; {spent:.1f} s of CPU work, "
+            "sample": (f"every absmax/quantise/SwiGLU call of the step on its tensor shape (first rows, up to "
+                       f"{STREAM_SAMPLE_ELEMS} elements, scaled by the row count), every GEMM on {gemm_rows} and "
+                       f"{2 * gemm_rows} output rows extrapolated to all rows; {spent:.1f} s of CPU work, "
                        f"estimated full step {est:.1f} s on {threads} threads")}
 
 
@@ -237,9 +301,13 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline", action="store_true",
+                    help="also time the oracle for the c4 / c5 workloads (always done for c3 unless disabled)")
     ap.add_argument("--layout", choices=("copies", "mn"), default="copies",
                     help="backward GEMM operands: transposed FP8 copies, or the untransposed tensors")
-    ap.add_argument("--cpu-gemm-rows", type=int, default=16)
+    ap.add_argument("--cpu-gemm-rows", type=int, default=96)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="c3",
+                    help="c3: 7B-class layer (the headline); c4: 14B-class; c5: 32B-class with MLP recomputation")
     ap.add_argument("--breakdown", action="store_true", help="also time every call (separate pass)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -254,7 +322,8 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
-    ops, bufs = build_layer7b(fp8, dev, args.layout)
+    cfg = workloads.CONFIGS[args.workload]
+    ops, bufs = build_step(fp8, dev, args.workload, args.layout)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         run_step(ops)
@@ -295,7 +364,8 @@ def main():
     else:
         quant_gbs = None
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(ops, args.cpu_gemm_rows)
+    want_cpu = not args.no_cpu_baseline and (args.workload == "c3" or args.cpu_baseline)
+    cpu = cpu_baseline(ops, args.cpu_gemm_rows) if want_cpu else None
 
     line = {
         "metric": "FP8 GEMM TFLOP/s + % of MI355X FP8 peak at 7B shapes; quant/absmax HBM GB/s",
@@ -310,8 +380,9 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8",
         "data": "synthetic",
-        "config": {"workload": "7B-class layer linears fwd+bwd with SwiGLU requant chain (c3 shapes + c2 MLP chain)",
-                   "M": 4096, "d": 4096, "ffn": 11008, "qkv_out": 12288, "gemms": 12, "gemm_launches": 8,
+        "config": {"workload": WORKLOADS[args.workload], "name": args.workload, "M": cfg.M,
+                   "linears": {l.name: [l.K, l.N] for l in cfg.linears},
+                   "gemm_launches": sum(1 for op in ops if op.kind == "gemm"),
                    "backward_operands": "untransposed (MN-major)" if args.layout == "mn" else "transposed copies",
                    "gemm_gflop_per_step": round(gemm_flop / 1e9, 1)},
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
