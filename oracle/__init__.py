@@ -12,5 +12,5 @@ of the FastML report that it follows, is written in the C file next to it.
 from .oracle import (  # noqa: F401
     E4M3, E5M2, FP8_MAX, build, lib_path, num_threads,
     bf16_to_f32, f32_to_bf16, encode, decode, absmax_bf16, absmax_f32, scale,
-    quantize, exp_neg, swiglu_h, swiglu_requant, gemm,
+    quantize, exp_neg, swiglu_h, swiglu_requant, gemm, swiglu_grad, swiglu_grad_one, swiglu_backward,
 )

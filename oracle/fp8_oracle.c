@@ -35,6 +35,12 @@
  *       concatenated as [gate | up] along the feature axis, every step one
  *       fp32 operation in the order E = RN32(e^-g), t = 1 + E, s_g = g / t,
  *       h = s_g * u, and e^-g correctly rounded to fp32;
+ *     - SwiGLU backward (the gradients of gate and up, quantised for the
+ *       gate/up backward GEMMs): with sigma = 1 / (1 + e^-g) and
+ *       silu'(g) = sigma * (1 + g * (1 - sigma)) (the textbook derivative of
+ *       g * sigma), du = dh * silu(g) and dg = (dh * u) * silu'(g), every step
+ *       one fp32 operation in the order written below, then the per-tensor
+ *       absmax / scale / encode of [dg | du] like any other tensor;
  *     - GEMM: fp32 sum over ascending k of the decoded products (every
  *       FP8 x FP8 product is exact in fp32), then one multiply by
  *       RN32(da * db), then round-to-nearest-even to bf16.
@@ -238,6 +244,71 @@ void oracle_swiglu_requant(const uint16_t* gu, int64_t M, int64_t F, int compute
             uint8_t c = oracle_encode(h_buf[i * F + j] * s, FMT_E4M3);
             if (hq) hq[i * F + j] = c;
             if (hqt) hqt[j * M + i] = c;
+        }
+}
+
+/*
+ * SwiGLU backward, one element pair.  g, u: the gate and up values; d: the
+ * gradient of h = silu(g) * u.  Every step is one fp32 operation:
+ *   E = RN32(e^-g), t = 1 + E, sig = 1 / t, s = g / t            (s = silu(g))
+ *   c = 1 - sig, p = g * c, q = 1 + p, ds = sig * q               (ds = silu'(g))
+ *   du = d * s
+ *   dg = (d * u) * ds
+ */
+void oracle_swiglu_grad_one(float g, float u, float d, float* dg, float* du)
+{
+    float E = oracle_exp_neg(g);
+    float t = 1.0f + E;
+    float sig = 1.0f / t;
+    float s = g / t;
+    float c = 1.0f - sig;
+    float p = g * c;
+    float q = 1.0f + p;
+    float ds = sig * q;
+    *du = d * s;
+    float du_ = d * u;
+    *dg = du_ * ds;
+}
+
+/*
+ * The gradient of gu = [gate | up] (fp32, [M, 2F]) from gu (bf16 [M, 2F]) and
+ * dh (bf16 [M, F]): dgu[i, j] = dg, dgu[i, F + j] = du.
+ */
+void oracle_swiglu_grad(const uint16_t* gu, const uint16_t* dh, int64_t M, int64_t F, float* dgu)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < F; ++j) {
+            float g = oracle_bf16_to_f32(gu[i * 2 * F + j]);
+            float u = oracle_bf16_to_f32(gu[i * 2 * F + F + j]);
+            float d = oracle_bf16_to_f32(dh[i * F + j]);
+            oracle_swiglu_grad_one(g, u, d, &dgu[i * 2 * F + j], &dgu[i * 2 * F + F + j]);
+        }
+}
+
+/*
+ * SwiGLU backward fused with the quantisation of its output: dgu as above
+ * (caller scratch of M*2F floats), absmax = max |dgu| (fresh: gradients have no
+ * retained statistic), scale for fmt, q = encode(RN32(dgu * s)) [M, 2F] and its
+ * transpose qt [2F, M] (either may be NULL).
+ */
+void oracle_swiglu_backward(const uint16_t* gu, const uint16_t* dh, int64_t M, int64_t F, int fmt,
+                            float* absmax, float* scale, float* inv_scale, float* dgu,
+                            uint8_t* q, uint8_t* qt)
+{
+    float s, inv;
+    oracle_swiglu_grad(gu, dh, M, F, dgu);
+    *absmax = oracle_absmax_f32(dgu, M * 2 * F);
+    oracle_scale(*absmax, fmt, &s, &inv);
+    if (scale) *scale = s;
+    if (inv_scale) *inv_scale = inv;
+    const int64_t C = 2 * F;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < C; ++j) {
+            uint8_t c = oracle_encode(dgu[i * C + j] * s, fmt);
+            if (q) q[i * C + j] = c;
+            if (qt) qt[j * M + i] = c;
         }
 }
 

@@ -63,6 +63,9 @@ def _load():
             "oracle_swiglu_h": (None, [vp, i64, i64, vp]),
             "oracle_swiglu_requant": (None, [vp, i64, i64, i32, vp, vp, vp, vp, vp]),
             "oracle_gemm": (None, [vp, i32, vp, i32, i64, i64, i64, f32, f32, vp, i64, vp, vp, vp]),
+            "oracle_swiglu_grad_one": (None, [f32, f32, f32, vp, vp]),
+            "oracle_swiglu_grad": (None, [vp, vp, i64, i64, vp]),
+            "oracle_swiglu_backward": (None, [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, vp]),
             "oracle_encode_vec": (None, [vp, i64, i32, vp]),
             "oracle_decode_vec": (None, [vp, i64, i32, vp]),
             "oracle_exp_neg_vec": (None, [vp, i64, vp]),
@@ -205,6 +208,45 @@ def swiglu_requant(gu: np.ndarray, absmax_h=None, want_hq: bool = True, want_hqt
     _load().oracle_swiglu_requant(_ptr(gu), M, F, 1 if absmax_h is None else 0, _ptr(am),
                                   _ptr(inv), _ptr(hbuf), _ptr(hq), _ptr(hqt))
     return hq, hqt, am[0], inv[0]
+
+
+
+def swiglu_grad(gu: np.ndarray, dh: np.ndarray) -> np.ndarray:
+    """The fp32 gradient [dg | du] ([M, 2F]) of gu = [gate | up] given dh = dL/dh (bf16 bits)."""
+    _need(gu, np.uint16, "gu")
+    _need(dh, np.uint16, "dh")
+    M, F = gu.shape[0], gu.shape[1] // 2
+    if gu.ndim != 2 or gu.shape[1] % 2 or dh.shape != (M, F):
+        raise ValueError("gu must be [M, 2F] and dh [M, F]")
+    out = np.empty((M, 2 * F), np.float32)
+    _load().oracle_swiglu_grad(_ptr(gu), _ptr(dh), M, F, _ptr(out))
+    return out
+
+
+def swiglu_backward(gu: np.ndarray, dh: np.ndarray, fmt: int = E5M2, want_q: bool = True, want_qt: bool = False):
+    """SwiGLU backward fused with the quantisation of [dg | du].
+
+    Returns (q [M, 2F] or None, qt [2F, M] or None, absmax, scale, inv_scale).
+    """
+    _need(gu, np.uint16, "gu")
+    _need(dh, np.uint16, "dh")
+    M, F = gu.shape[0], gu.shape[1] // 2
+    if gu.ndim != 2 or gu.shape[1] % 2 or dh.shape != (M, F):
+        raise ValueError("gu must be [M, 2F] and dh [M, F]")
+    am, sc, inv = (np.zeros(1, np.float32) for _ in range(3))
+    buf = np.empty((M, 2 * F), np.float32)
+    q = np.empty((M, 2 * F), np.uint8) if want_q else None
+    qt = np.empty((2 * F, M), np.uint8) if want_qt else None
+    _load().oracle_swiglu_backward(_ptr(gu), _ptr(dh), M, F, _fmt(fmt), _ptr(am), _ptr(sc), _ptr(inv), _ptr(buf),
+                                   _ptr(q), _ptr(qt))
+    return q, qt, am[0], sc[0], inv[0]
+
+
+def swiglu_grad_one(g, u, d):
+    """(dg, du) of one element pair, fp32."""
+    dg, du = np.zeros(1, np.float32), np.zeros(1, np.float32)
+    _load().oracle_swiglu_grad_one(np.float32(g), np.float32(u), np.float32(d), _ptr(dg), _ptr(du))
+    return dg[0], du[0]
 
 
 def gemm(a: np.ndarray, fmt_a: int, b: np.ndarray, fmt_b: int, da, db, rows=None) -> np.ndarray:
