@@ -87,7 +87,7 @@ WORKLOADS = {
 }
 
 
-def build_step(fp8, dev, cfg_name="c3", layout="copies"):
+def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False):
     """Inputs and the ordered list of calls of one layer step of a configuration.
 
     Forward: absmax + quantise of X and W, FP8 GEMM, for QKV, O and gate/up;
@@ -97,6 +97,9 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies"):
     gate/up input with its retained absmax, reruns the gate/up GEMM and
     requantises the SwiGLU output with the retained absmax_h (no reduction), and
     the forward keeps no transposed copies for the MLP block.
+    With swiglu_bwd the gate/up output gradient is not drawn: the down linear's
+    dgrad output dH goes through the fused SwiGLU backward, whose e5m2
+    d[gate | up] feeds the gate/up backward GEMMs.
     """
     mn = layout == "mn"
     cfg = workloads.CONFIGS[cfg_name]
@@ -165,6 +168,7 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies"):
     fwd["down"] = {"xq": hq, "wq": wq, "xqt": hqt, "wqt": wqt, "inv_x": inv_h, "inv_w": inv_w, "y": y}
 
     # ---- backward
+    gu2 = None
     if recompute:
         # MLP block recomputation from the retained bf16 input and absmax statistics: no reduction runs
         _, Lg = lin["gate_up"]
@@ -175,13 +179,29 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies"):
         g.update({"xq": xq, "xqt": xqt, "inv_x": inv_x})
         hq2, hqt2, inv_h2 = swiglu_op("recompute", gu2, am_h, False, not mn, F)
         fwd["down"].update({"xq": hq2, "xqt": hqt2, "inv_x": inv_h2})
-    for name in ("qkv", "o", "gate_up", "down"):
+    gu_bwd = fwd["gate_up"]["y"] if not recompute else gu2
+    order = ("down", "gate_up", "o", "qkv") if swiglu_bwd else ("qkv", "o", "gate_up", "down")
+    dh = None
+    for name in order:
         li, L = lin[name]
-        dy = workloads.draw_dy(cfg, li).to(dev)
         f = fwd[name]
-        dyq, dyqt, inv_dy, _ = quant_ops(f"dY_{name}", dy, M, L.N, E5M2, not mn)
+        if swiglu_bwd and name == "gate_up":
+            # the MLP chain: dH (the down dgrad output) -> fused SwiGLU backward -> e5m2 d[gate | up]
+            am, sc, inv_dy = f32(), f32(), f32()
+            dyq, dyqt = u8(M, L.N), (None if mn else u8(L.N, M))
+            Fh = L.N // 2
+            ops.append(Op("swiglu_backward", lambda dyq=dyq, dyqt=dyqt, am=am, sc=sc, inv=inv_dy:
+                          fp8.swiglu_backward(gu_bwd, dh, E5M2, q=dyq, qt=dyqt, absmax=am, scale=sc, inv_scale=inv),
+                          "swiglu_bwd", (12 + (4 if not mn else 2)) * M * Fh,
+                          meta={"M": M, "F": Fh, "qt": not mn}))
+        else:
+            dy = workloads.draw_dy(cfg, li).to(dev)
+            bufs["dy_" + name] = dy
+            dyq, dyqt, inv_dy, _ = quant_ops(f"dY_{name}", dy, M, L.N, E5M2, not mn)
         dx = bf(M, L.K)
         dw = bf(L.N, L.K)
+        if name == "down":
+            dh = dx
         # dgrad dX = dY . W and wgrad dW = dY^T . X in one launch
         if mn:
             fn = (lambda dyq=dyq, wq=f["wq"], xq=f["xq"], a=inv_dy, b=f["inv_w"], c=f["inv_x"], dx=dx, dw=dw:
@@ -191,7 +211,6 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies"):
                   dx=dx, dw=dw: fp8.gemm_backward(dyq, dyqt, E5M2, wqt, xqt, a, b, c, dx, dw))
         ops.append(Op(f"gemm_backward {name}", fn, "gemm", 4 * M * L.N * L.K, GEMM_KERNEL[(1, 0, 1 if mn else 0)],
                       {"probs": [(M, L.K, L.N, E5M2), (L.N, L.K, M, E5M2)]}))
-        bufs["dy_" + name] = dy
     return ops, bufs
 
 
@@ -280,6 +299,13 @@ def cpu_baseline(ops, gemm_rows):
             t = time.perf_counter()
             oracle.quantize(x, m["fmt"], s_, want_q=True, want_qt=m["qt"])
             est += (time.perf_counter() - t) * f
+        elif op.kind == "swiglu_bwd":
+            r, f = sample_rows(m["M"], 3 * m["F"])
+            gu = rng.integers(0, 0x4080, (r, 2 * m["F"]), dtype=np.uint16)
+            dh = rng.integers(0, 0x3A80, (r, m["F"]), dtype=np.uint16)
+            t = time.perf_counter()
+            oracle.swiglu_backward(gu, dh, 1, want_q=True, want_qt=m["qt"])
+            est += (time.perf_counter() - t) * f
         elif op.kind == "swiglu":
             r, f = sample_rows(m["M"], 2 * m["F"])
             gu = rng.integers(0, 0x4080, (r, 2 * m["F"]), dtype=np.uint16)
@@ -308,6 +334,9 @@ def main():
     ap.add_argument("--cpu-gemm-rows", type=int, default=96)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="c3",
                     help="c3: 7B-class layer (the headline); c4: 14B-class; c5: 32B-class with MLP recomputation")
+    ap.add_argument("--swiglu-backward", action="store_true",
+                    help="chain the MLP backward: down dgrad -> fused SwiGLU backward -> gate/up backward "
+                         "(instead of a drawn gate/up output gradient)")
     ap.add_argument("--breakdown", action="store_true", help="also time every call (separate pass)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -323,7 +352,7 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     cfg = workloads.CONFIGS[args.workload]
-    ops, bufs = build_step(fp8, dev, args.workload, args.layout)
+    ops, bufs = build_step(fp8, dev, args.workload, args.layout, args.swiglu_backward)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         run_step(ops)
@@ -351,7 +380,7 @@ def main():
     breakdown = None
     if args.breakdown:
         _, _, per_all = time_steps(ops, max(3, args.steps // 2), stream,
-                                   instrument_kinds=("gemm", "absmax", "quantize", "swiglu"))
+                                   instrument_kinds=("gemm", "absmax", "quantize", "swiglu", "swiglu_bwd"))
         breakdown = []
         for op in ops:
             t = float(np.mean(per_all[op.name]))
@@ -384,6 +413,8 @@ def main():
                    "linears": {l.name: [l.K, l.N] for l in cfg.linears},
                    "gemm_launches": sum(1 for op in ops if op.kind == "gemm"),
                    "backward_operands": "untransposed (MN-major)" if args.layout == "mn" else "transposed copies",
+                   "mlp_backward": "chained through the fused SwiGLU backward" if args.swiglu_backward
+                   else "drawn output gradients",
                    "gemm_gflop_per_step": round(gemm_flop / 1e9, 1)},
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "gemm_only_tflops": round(gemm_flop / gemm_time / 1e12, 1),

@@ -30,6 +30,7 @@ _SIGS = {
     "fp8_absmax": (_i32, [_vp, _i64, _vp, _vp]),
     "fp8_quantize": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp8_swiglu_requant": (_i32, [_vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp]),
+    "fp8_swiglu_backward": (_i32, [_vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp8_gemm_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_gemm_dgrad": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_gemm_wgrad": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
@@ -151,6 +152,37 @@ def swiglu_requant(gu: torch.Tensor, absmax_h: torch.Tensor | None = None, compu
     _check("fp8_swiglu_requant", _lib.fp8_swiglu_requant(_ptr(gu), M, F, _ptr(absmax_h), 1 if compute_absmax else 0,
                                                          _ptr(hq), _ptr(hqt), _ptr(inv_scale_h), _stream(gu)))
     return hq, hqt, absmax_h, inv_scale_h
+
+
+def swiglu_backward(gu: torch.Tensor, dh: torch.Tensor, fmt: int = E5M2, want_q: bool = True, want_qt: bool = False,
+                    absmax: torch.Tensor | None = None, q: torch.Tensor | None = None, qt: torch.Tensor | None = None,
+                    scale: torch.Tensor | None = None, inv_scale: torch.Tensor | None = None):
+    """Gradient of gu = [gate | up] (bf16 [M, 2F]) from dh (bf16 [M, F]), quantised with its own absmax.
+
+    Returns (q uint8 [M, 2F] or None, qt uint8 [2F, M] or None, absmax, scale, inv_scale).
+    """
+    _dev_tensor(gu, "gu", torch.bfloat16)
+    _dev_tensor(dh, "dh", torch.bfloat16)
+    if gu.dim() != 2 or gu.shape[1] % 2:
+        raise ValueError("gu must be [M, 2F]")
+    M, F = gu.shape[0], gu.shape[1] // 2
+    if tuple(dh.shape) != (M, F):
+        raise ValueError("dh must be [M, F]")
+    if want_q and q is None:
+        q = torch.empty((M, 2 * F), dtype=torch.uint8, device=gu.device)
+    if want_qt and qt is None:
+        qt = torch.empty((2 * F, M), dtype=torch.uint8, device=gu.device)
+    for t, n in ((q, "q"), (qt, "qt")):
+        if t is not None:
+            _dev_tensor(t, n, torch.uint8)
+            if t.numel() != 2 * M * F:
+                raise ValueError(f"{n} has the wrong size")
+    absmax = _scalar(absmax, "absmax", gu.device)
+    scale = _scalar(scale, "scale", gu.device)
+    inv_scale = _scalar(inv_scale, "inv_scale", gu.device)
+    _check("fp8_swiglu_backward", _lib.fp8_swiglu_backward(_ptr(gu), _ptr(dh), M, F, int(fmt), _ptr(absmax), _ptr(q),
+                                                           _ptr(qt), _ptr(scale), _ptr(inv_scale), _stream(gu)))
+    return q, qt, absmax, scale, inv_scale
 
 
 def _out_bf16(out, shape, device):

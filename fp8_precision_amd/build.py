@@ -21,9 +21,11 @@ LIB = os.path.join(HERE, "libfp8_precision.so")
 SOURCES = ["quant.hip", "swiglu.hip", "gemm.hip", "api.cpp"]
 ARCH = "gfx950"
 
-# Packed fp32 VALU instructions are kept out of the code object on purpose.
+# Packed fp32 VALU instructions are kept out of the code object on purpose, and
+# no multiply-add is contracted into an FMA: every fp32 step of the
+# definitions (the SwiGLU tables, scales, encoders) is one IEEE operation.
 HIP_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

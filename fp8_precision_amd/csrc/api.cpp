@@ -156,6 +156,32 @@ fp8_status fp8_swiglu_requant(const void* gu, int64_t M, int64_t F, float* absma
     return FP8_OK;
 }
 
+fp8_status fp8_swiglu_backward(const void* gu, const void* dh, int64_t M, int64_t F, fp8_fmt fmt, float* absmax,
+                               uint8_t* q, uint8_t* qt, float* scale, float* inv_scale, hipStream_t stream)
+{
+    t_last_error.clear();
+    if (!gu || !dh || !absmax) return fail(FP8_ERR_INVALID, "fp8_swiglu_backward: null gu, dh or absmax");
+    if (!q && !qt) return fail(FP8_ERR_INVALID, "fp8_swiglu_backward: at least one of q, qt is required");
+    if (fmt != FP8_E4M3 && fmt != FP8_E5M2) return fail(FP8_ERR_INVALID, "fp8_swiglu_backward: bad format");
+    if (!mul_ok(M, 2 * F, kMaxElems) || F <= 0) return fail(FP8_ERR_INVALID, "fp8_swiglu_backward: bad shape");
+    const int64_t n = M * F;
+    const Range r[] = {{gu, 4 * n}, {dh, 2 * n}, {absmax, 4}, {q, q ? 2 * n : 0}, {qt, qt ? 2 * n : 0},
+                       {scale, scale ? 4 : 0}, {inv_scale, inv_scale ? 4 : 0}};
+    // the two inputs may alias each other; no output may alias anything
+    for (int i = 2; i < 7; ++i)
+        for (int j = 0; j < 7; ++j)
+            if (i != j && overlap(r[i].p, r[i].n, r[j].p, r[j].n))
+                return fail(FP8_ERR_INVALID, "fp8_swiglu_backward: overlapping buffers");
+    if (F % 16) return fail(FP8_ERR_UNSUPPORTED, "fp8_swiglu_backward: F must be a multiple of 16");
+    if (qt && M % 16) return fail(FP8_ERR_UNSUPPORTED, "fp8_swiglu_backward: M must be a multiple of 16 with qt");
+    if (!aligned(gu, 16) || !aligned(dh, 16) || (q && !aligned(q, 16)) || (qt && !aligned(qt, 16)) ||
+        !aligned(absmax, 4) || (scale && !aligned(scale, 4)) || (inv_scale && !aligned(inv_scale, 4)))
+        return fail(FP8_ERR_UNSUPPORTED, "fp8_swiglu_backward: misaligned pointer");
+    hipError_t e = fp8k::launch_swiglu_backward(gu, dh, M, F, (int)fmt, absmax, q, qt, scale, inv_scale, stream);
+    if (e != hipSuccess) return fail_hip("fp8_swiglu_backward", e);
+    return FP8_OK;
+}
+
 // Shared checks of the three GEMM calls, in the TN form out[P, Q] = A[P, R] . B[Q, R]^T.
 static fp8_status gemm_common(const char* name, const uint8_t* A, int fmt_a, const uint8_t* B, const float* inv_a,
                               const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream)

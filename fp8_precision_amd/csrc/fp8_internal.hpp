@@ -20,6 +20,10 @@ hipError_t launch_swiglu_requant(const void* gu, int64_t M, int64_t F, float* ab
                                  int compute_absmax, uint8_t* hq, uint8_t* hqt,
                                  float* inv_scale_h, hipStream_t stream);
 
+// SwiGLU backward: absmax of [dg | du], then its quantisation q [M, 2F] and / or qt [2F, M].
+hipError_t launch_swiglu_backward(const void* gu, const void* dh, int64_t M, int64_t F, int fmt, float* absmax,
+                                  uint8_t* q, uint8_t* qt, float* scale, float* inv_scale, hipStream_t stream);
+
 // out[P, Q] = bf16(RN32(sum_r A[p, r] B[q, r] * RN32(*inv_a * *inv_b))).  Operand
 // layouts: 0 = K-major (A[p, r] at A + p R + r), 1 = MN-major (A[p, r] at
 // A + r P + p; B likewise with Q).  Compiled pairs (A, B): (0, 0), (0, 1), (1, 1).

@@ -17,6 +17,16 @@
 // The table (2 signs x 34 exponents x 128 mantissas, 34 KB) is built once per
 // device by a kernel that evaluates each entry in binary64 and rounds every
 // step to binary32 in the order above; kernels copy it into LDS.
+//
+// The backward (the gradients of gate and up, for the gate/up backward GEMMs)
+// uses the textbook derivative of g * sigma(g): with sig = RN32(1 / t),
+//   ds = RN32(sig * RN32(1 + RN32(g * RN32(1 - sig))))          (silu'(g))
+//   du = RN32(dh * s_g),  dg = RN32(RN32(dh * u) * ds)
+// ds is a function of the 16 bits of g too: a second table over the same
+// exponent range, built with the same single roundings; outside it
+//   |g| < 2^-27: sig = 1/2, 1 + g/2 rounds to 1, ds = 1/2;
+//   |g| >= 128 finite: g > 0 gives sig = 1, ds = 1; g < 0 gives sig = 0, ds = -0;
+//   infinities and NaN: ds = NaN.
 #include <mutex>
 #include "fp8_device.hpp"
 #include "fp8_internal.hpp"
@@ -30,9 +40,11 @@ constexpr int kHalf = kNE * 128;              // entries per sign
 constexpr int kTable = 2 * kHalf;             // 8704 entries
 
 __device__ float g_silu_table[kTable];
+__device__ float g_dsilu_table[kTable];
 
 __global__ void __launch_bounds__(256) silu_table_init_kernel()
 {
+#pragma clang fp contract(off)
     const int idx = blockIdx.x * 256 + threadIdx.x;
     if (idx >= kTable) return;
     const uint32_t sign = idx >= kHalf ? 1u : 0u;
@@ -40,8 +52,13 @@ __global__ void __launch_bounds__(256) silu_table_init_kernel()
     const uint32_t bits = (sign << 15) | ((uint32_t)(kELo + rem / 128) << 7) | (rem % 128);
     const float g = __uint_as_float(bits << 16);
     const float E = (float)exp(-(double)g);
-    const float t = 1.0f + E;
+    const float t = __fadd_rn(1.0f, E);
     g_silu_table[idx] = (float)((double)g / (double)t);
+    const float sig = (float)(1.0 / (double)t);
+    const float c = __fsub_rn(1.0f, sig);
+    const float pr = __fmul_rn(g, c);
+    const float q = __fadd_rn(1.0f, pr);
+    g_dsilu_table[idx] = __fmul_rn(sig, q);
 }
 
 static std::mutex g_init_mu;
@@ -74,6 +91,19 @@ __device__ __forceinline__ void load_table_to_lds(float* lds)
     __syncthreads();
 }
 
+// Both tables (s_g, then ds) into 2 * 34 KB of LDS.
+__device__ __forceinline__ void load_tables_to_lds(float* lds)
+{
+    const float4* s0 = reinterpret_cast<const float4*>(g_silu_table);
+    const float4* s1 = reinterpret_cast<const float4*>(g_dsilu_table);
+    float4* dst = reinterpret_cast<float4*>(lds);
+    for (int i = threadIdx.x; i < kTable / 4; i += blockDim.x) {
+        dst[i] = s0[i];
+        dst[kTable / 4 + i] = s1[i];
+    }
+    __syncthreads();
+}
+
 // s_g for one bf16 gate value (16-bit pattern b, fp32 value g).
 __device__ __forceinline__ float silu_of(const float* tbl, uint32_t b, float g)
 {
@@ -85,6 +115,19 @@ __device__ __forceinline__ float silu_of(const float* tbl, uint32_t b, float g)
     if ((int32_t)t < 0) return g * 0.5f;                     // tiny |g|
     if (!neg) return g;                                      // large g, +inf, +NaN
     return ((b & 0x7F80u) == 0x7F80u) ? __builtin_nanf("") : -0.0f;
+}
+
+// silu'(g) for one bf16 gate value (16-bit pattern b).
+__device__ __forceinline__ float dsilu_of(const float* tbl, uint32_t b)
+{
+    const uint32_t t = (b & 0x7FFFu) - (uint32_t)(kELo * 128);
+    const uint32_t neg = b >> 15;
+    const bool in_table = t < (uint32_t)kHalf;
+    const float tv = tbl[in_table ? t + neg * kHalf : 0u];
+    if (in_table) return tv;
+    if ((int32_t)t < 0) return 0.5f;                                 // tiny |g|
+    if ((b & 0x7F80u) == 0x7F80u) return __builtin_nanf("");         // infinities, NaN
+    return neg ? -0.0f : 1.0f;                                       // large finite |g|
 }
 
 // h for the 8 (gate, up) pairs of two 16-byte words.
@@ -288,6 +331,221 @@ hipError_t launch_swiglu_requant(const void* gu, int64_t M, int64_t F, float* ab
     } else {
         swiglu_quant_kernel<<<(unsigned)blocks, 256, 0, stream>>>(g, M, F, absmax_h, hq, inv_scale_h);
     }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU backward fused with the quantisation of [dg | du].
+
+// dg, du for the 8 (gate, up, dh) triples of three 16-byte words.  ts / tds: the
+// s_g and ds tables in LDS.
+__device__ __forceinline__ void swiglu_grad8(const float* ts, const float* tds, uint4 gw, uint4 uw, uint4 dw,
+                                             float dg[8], float du[8])
+{
+    const uint32_t g32[4] = {gw.x, gw.y, gw.z, gw.w};
+    const uint32_t u32[4] = {uw.x, uw.y, uw.z, uw.w};
+    const uint32_t d32[4] = {dw.x, dw.y, dw.z, dw.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const uint32_t b = hf ? (g32[k] >> 16) : (g32[k] & 0xFFFFu);
+            const float g = hf ? bf16_hi(g32[k]) : bf16_lo(g32[k]);
+            const float u = hf ? bf16_hi(u32[k]) : bf16_lo(u32[k]);
+            const float d = hf ? bf16_hi(d32[k]) : bf16_lo(d32[k]);
+            du[2 * k + hf] = d * silu_of(ts, b, g);
+            const float p = d * u;
+            dg[2 * k + hf] = p * dsilu_of(tds, b);
+        }
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ uint2 quant8_f(const float v[8], float s)
+{
+    uint2 r;
+    r.x = enc4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+    r.y = enc4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
+    return r;
+}
+
+// Pass 1: absmax of [dg | du] over the whole [M, 2F] gradient (nothing written).
+__global__ void __launch_bounds__(1024) swiglu_bwd_absmax_kernel(const uint16_t* __restrict__ gu,
+                                                                const uint16_t* __restrict__ dh, int64_t M,
+                                                                int64_t F, uint32_t* __restrict__ out)
+{
+    __shared__ float tbl[2 * kTable];
+    load_tables_to_lds(tbl);
+    const RowItems it = row_items(M, F);
+    const int lane = threadIdx.x & 63;
+    uint32_t m = 0;
+    const int wpb = blockDim.x >> 6;
+    for (int64_t w = (int64_t)blockIdx.x * wpb + (threadIdx.x >> 6); w < it.total; w += (int64_t)gridDim.x * wpb) {
+        const int64_t i = w / it.chunks;
+        const int64_t jb = (w - i * it.chunks) * 1024 + lane * 8;
+        const uint16_t* grow = gu + i * 2 * F;
+        const uint16_t* drow = dh + i * F;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int64_t j = jb + half * 512;
+            if (j < F) {
+                const uint4 gw = *reinterpret_cast<const uint4*>(grow + j);
+                const uint4 uw = *reinterpret_cast<const uint4*>(grow + F + j);
+                const uint4 dw = *reinterpret_cast<const uint4*>(drow + j);
+                float dg[8], du[8];
+                swiglu_grad8(tbl, tbl + kTable, gw, uw, dw, dg, du);
+                m = mag_max8(mag_max8(m, dg), du);
+            }
+        }
+    }
+    block_max_to_global(m, out);
+}
+
+// Pass 2 without the transposed copy: q [M, 2F] = [codes of dg | codes of du].
+template <int FMT>
+__global__ void __launch_bounds__(256) swiglu_bwd_quant_kernel(const uint16_t* __restrict__ gu,
+                                                               const uint16_t* __restrict__ dh, int64_t M, int64_t F,
+                                                               const float* __restrict__ absmax,
+                                                               uint8_t* __restrict__ q, float* __restrict__ scale_out,
+                                                               float* __restrict__ inv_out)
+{
+    __shared__ float tbl[2 * kTable];
+    float s, inv;
+    tensor_scale(*absmax, Fmt<FMT>::max, s, inv);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (scale_out) *scale_out = s;
+        if (inv_out) *inv_out = inv;
+    }
+    load_tables_to_lds(tbl);
+    const RowItems it = row_items(M, F);
+    const int lane = threadIdx.x & 63;
+    for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < it.total; w += (int64_t)gridDim.x * 4) {
+        const int64_t i = w / it.chunks;
+        const int64_t jb = (w - i * it.chunks) * 1024 + lane * 8;
+        const uint16_t* grow = gu + i * 2 * F;
+        const uint16_t* drow = dh + i * F;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int64_t j = jb + half * 512;
+            if (j < F) {
+                const uint4 gw = *reinterpret_cast<const uint4*>(grow + j);
+                const uint4 uw = *reinterpret_cast<const uint4*>(grow + F + j);
+                const uint4 dw = *reinterpret_cast<const uint4*>(drow + j);
+                float dg[8], du[8];
+                swiglu_grad8(tbl, tbl + kTable, gw, uw, dw, dg, du);
+                *reinterpret_cast<uint2*>(q + i * 2 * F + j) = quant8_f<FMT>(dg, s);
+                *reinterpret_cast<uint2*>(q + i * 2 * F + F + j) = quant8_f<FMT>(du, s);
+            }
+        }
+    }
+}
+
+// Pass 2 with the transposed copy qt [2F, M] (and optionally q): a wave owns
+// 64 rows x 64 columns of (g, u, dh), a lane the 8 x 8 block at rows
+// 8 (l / 8) .. +7 and columns 8 (l % 8) .. +7; its dg and du code blocks are
+// transposed in registers and written as 64-byte segments of qt rows j and
+// F + j.  No LDS beyond the two tables, no barrier.
+template <int FMT>
+__global__ void __launch_bounds__(256) swiglu_bwd_quant_t_kernel(const uint16_t* __restrict__ gu,
+                                                                 const uint16_t* __restrict__ dh, int64_t M,
+                                                                 int64_t F, const float* __restrict__ absmax,
+                                                                 uint8_t* __restrict__ q, uint8_t* __restrict__ qt,
+                                                                 float* __restrict__ scale_out,
+                                                                 float* __restrict__ inv_out)
+{
+    __shared__ float tbl[2 * kTable];
+    float s, inv;
+    tensor_scale(*absmax, Fmt<FMT>::max, s, inv);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (scale_out) *scale_out = s;
+        if (inv_out) *inv_out = inv;
+    }
+    load_tables_to_lds(tbl);
+    const int lane = threadIdx.x & 63;
+    const int ri = (lane >> 3) * 8, ci = (lane & 7) * 8;
+    const int64_t items_c = (F + kHtEdge - 1) / kHtEdge;
+    const int64_t items = items_c * ((M + kHtEdge - 1) / kHtEdge);
+    const int64_t wstride = (int64_t)gridDim.x * 4;
+    for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < items; w += wstride) {
+        const int64_t i0 = (w / items_c) * kHtEdge + ri;
+        const int64_t j0 = (w % items_c) * kHtEdge + ci;
+        if (i0 >= M || j0 >= F) continue;             // M, F are multiples of 8: blocks are whole
+        uint32_t glo[8], ghi[8], ulo[8], uhi[8];      // codes of dg (g...) and du (u...), per row
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const uint16_t* grow = gu + (i0 + r) * 2 * F + j0;
+            const uint4 gw = *reinterpret_cast<const uint4*>(grow);
+            const uint4 uw = *reinterpret_cast<const uint4*>(grow + F);
+            const uint4 dw = *reinterpret_cast<const uint4*>(dh + (i0 + r) * F + j0);
+            float dg[8], du[8];
+            swiglu_grad8(tbl, tbl + kTable, gw, uw, dw, dg, du);
+            const uint2 cg = quant8_f<FMT>(dg, s);
+            const uint2 cu = quant8_f<FMT>(du, s);
+            glo[r] = cg.x;
+            ghi[r] = cg.y;
+            ulo[r] = cu.x;
+            uhi[r] = cu.y;
+        }
+        if (q) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                *reinterpret_cast<uint2*>(q + (i0 + r) * 2 * F + j0) = make_uint2(glo[r], ghi[r]);
+                *reinterpret_cast<uint2*>(q + (i0 + r) * 2 * F + F + j0) = make_uint2(ulo[r], uhi[r]);
+            }
+        }
+        uint32_t c0[8], c1[8];
+        transpose4x4(glo[0], glo[1], glo[2], glo[3], c0[0], c0[1], c0[2], c0[3]);
+        transpose4x4(glo[4], glo[5], glo[6], glo[7], c1[0], c1[1], c1[2], c1[3]);
+        transpose4x4(ghi[0], ghi[1], ghi[2], ghi[3], c0[4], c0[5], c0[6], c0[7]);
+        transpose4x4(ghi[4], ghi[5], ghi[6], ghi[7], c1[4], c1[5], c1[6], c1[7]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            *reinterpret_cast<uint2*>(qt + (j0 + k) * M + i0) = make_uint2(c0[k], c1[k]);
+        transpose4x4(ulo[0], ulo[1], ulo[2], ulo[3], c0[0], c0[1], c0[2], c0[3]);
+        transpose4x4(ulo[4], ulo[5], ulo[6], ulo[7], c1[0], c1[1], c1[2], c1[3]);
+        transpose4x4(uhi[0], uhi[1], uhi[2], uhi[3], c0[4], c0[5], c0[6], c0[7]);
+        transpose4x4(uhi[4], uhi[5], uhi[6], uhi[7], c1[4], c1[5], c1[6], c1[7]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            *reinterpret_cast<uint2*>(qt + (F + j0 + k) * M + i0) = make_uint2(c0[k], c1[k]);
+    }
+}
+
+template <int FMT>
+static void launch_swiglu_bwd_quant(const uint16_t* g, const uint16_t* d, int64_t M, int64_t F, float* absmax,
+                                    uint8_t* q, uint8_t* qt, float* scale, float* inv_scale, hipStream_t stream)
+{
+    // two resident blocks per CU (2 x 34 KB tables each), persistent
+    const int64_t cap = 2 * (int64_t)device_cu_count();
+    if (qt) {
+        const int64_t witems = ((F + kHtEdge - 1) / kHtEdge) * ((M + kHtEdge - 1) / kHtEdge);
+        int64_t blocks = (witems + 3) / 4;
+        if (blocks > cap) blocks = cap;
+        swiglu_bwd_quant_t_kernel<FMT><<<(unsigned)blocks, 256, 0, stream>>>(g, d, M, F, absmax, q, qt, scale,
+                                                                             inv_scale);
+    } else {
+        const int64_t items = M * ((F + 1023) / 1024);
+        int64_t blocks = (items + 3) / 4;
+        if (blocks > cap) blocks = cap;
+        if (blocks < 1) blocks = 1;
+        swiglu_bwd_quant_kernel<FMT><<<(unsigned)blocks, 256, 0, stream>>>(g, d, M, F, absmax, q, scale, inv_scale);
+    }
+}
+
+hipError_t launch_swiglu_backward(const void* gu, const void* dh, int64_t M, int64_t F, int fmt, float* absmax,
+                                  uint8_t* q, uint8_t* qt, float* scale, float* inv_scale, hipStream_t stream)
+{
+    hipError_t e = ensure_silu_table(stream);
+    if (e != hipSuccess) return e;
+    const uint16_t* g = reinterpret_cast<const uint16_t*>(gu);
+    const uint16_t* d = reinterpret_cast<const uint16_t*>(dh);
+    zero_u32_kernel_sw<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax));
+    const int64_t items = M * ((F + 1023) / 1024);
+    int64_t ablocks = (items + 15) / 16;
+    if (ablocks > device_cu_count()) ablocks = device_cu_count();
+    swiglu_bwd_absmax_kernel<<<(unsigned)ablocks, 1024, 0, stream>>>(g, d, M, F, reinterpret_cast<uint32_t*>(absmax));
+    if (fmt == 0) launch_swiglu_bwd_quant<0>(g, d, M, F, absmax, q, qt, scale, inv_scale, stream);
+    else launch_swiglu_bwd_quant<1>(g, d, M, F, absmax, q, qt, scale, inv_scale, stream);
     return hipGetLastError();
 }
 

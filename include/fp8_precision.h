@@ -125,6 +125,34 @@ fp8_status fp8_swiglu_requant(const void* gu, int64_t M, int64_t F, float* absma
                               float* inv_scale_h, hipStream_t stream);
 
 /*
+ * SwiGLU backward fused with the quantisation of its output: the gradient of
+ * gu = [gate | up] given dh, the gradient of h = silu(g) * u, is formed and
+ * quantised for the gate/up backward GEMMs (the step downstream of the
+ * requantised SwiGLU of the LLMQ summary, section 3.1; E5M2 gradients,
+ * section 5 / Fig. 2).  For i < M, j < F, with g = gu[i, j], u = gu[i, F + j],
+ * d = dh[i, j] and every step one fp32 operation:
+ *   E = RN32(e^-g), t = 1 + E, sig = 1 / t, s = g / t            (silu(g))
+ *   ds = sig * (1 + g * (1 - sig))                                 (silu'(g), in that order)
+ *   du = d * s,  dg = (d * u) * ds
+ *   dgu = [dg | du] (fp32 [M, 2F], never stored)
+ *   *absmax = max |dgu| (fresh, as for any gradient), s_q = fp8_max / absmax
+ *   q[i, c] = encode_fmt(RN32(dgu[i, c] * s_q)),  qt[c, i] = q[i, c]
+ *
+ *   gu         bf16 [M, 2F] (the forward's or the recomputed gate/up output)
+ *   dh         bf16 [M, F]
+ *   fmt        FP8_E5M2 (gradients) or FP8_E4M3
+ *   absmax     fp32 scalar out
+ *   q          u8 [M, 2F] or NULL;  qt  u8 [2F, M] or NULL (at least one) -- the
+ *              operands of fp8_gemm_dgrad (q) and fp8_gemm_wgrad (qt) of gate/up
+ *   scale, inv_scale  fp32 scalars out, each may be NULL
+ * Constraints: F % 16 == 0; if qt is given, M % 16 == 0.  gu and dh may alias;
+ * no output may overlap another buffer.
+ */
+fp8_status fp8_swiglu_backward(const void* gu, const void* dh, int64_t M, int64_t F, fp8_fmt fmt,
+                               float* absmax, uint8_t* q, uint8_t* qt, float* scale, float* inv_scale,
+                               hipStream_t stream);
+
+/*
  * FP8 GEMMs with fp32 accumulation and per-tensor descale (LLMQ summary,
  * section 2: low-precision matrix products on the matrix units; section 4:
  * large models are dominated by these products).  Every call computes

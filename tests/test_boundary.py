@@ -43,7 +43,7 @@ def test_header_declares_the_hot_path():
     names = declared_functions()
     for want in ("fp8_absmax", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd", "fp8_gemm_dgrad",
                  "fp8_gemm_wgrad", "fp8_gemm_backward", "fp8_gemm_dgrad_mn", "fp8_gemm_wgrad_mn",
-                 "fp8_gemm_backward_mn", "fp8_status_string", "fp8_last_error"):
+                 "fp8_gemm_backward_mn", "fp8_swiglu_backward", "fp8_status_string", "fp8_last_error"):
         assert want in names
 
 
@@ -180,6 +180,30 @@ def test_backward_mn_validation(lib):
     bad = list(ok); bad[1] = 5
     assert f(*bad) == INVALID
     bad = list(ok); bad[9] = 200                # M not a multiple of 16 / 128
+    assert f(*bad) == UNSUPPORTED
+
+
+def test_swiglu_backward_validation(lib):
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    f = lib.fp8_swiglu_backward
+    f.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+    f.restype = i32
+    ok = (A16, B16, 16, 16, 1, C16, D16, None, None, None, None)
+    bad = list(ok); bad[0] = None
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[5] = None                 # absmax
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[6] = None                 # neither q nor qt
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[4] = 9
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[6] = A16 + 32             # q inside gu
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[3] = 24                   # F % 16
+    assert f(*bad) == UNSUPPORTED
+    bad = list(ok); bad[2] = 8; bad[7] = E16      # M % 16 with qt
+    assert f(*bad) == UNSUPPORTED
+    bad = list(ok); bad[1] = B16 + 8              # misaligned dh
     assert f(*bad) == UNSUPPORTED
 
 
