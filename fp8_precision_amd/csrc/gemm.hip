@@ -45,6 +45,9 @@
 //  - Persistent: one workgroup per CU walks tiles in a grouped raster order,
 //    renumbered XCD-major so that the 32 CUs of an XCD (sharing one L2) work on
 //    consecutive tiles; the next tile's first stages load during the epilogue.
+//    When the last round would keep at most half of the CUs busy, its tiles are
+//    split into 128 x 256 half tiles (same loads and fragment reads, a 64 x 128
+//    wave tile), which halves that round.
 //  - Deterministic: every output is reduced by one wave in a fixed order.
 #include "fp8_device.hpp"
 #include "fp8_internal.hpp"
@@ -74,6 +77,7 @@ constexpr int kGroupM = 8;                    // tile rows per raster group
 // vmcnt[5:4] at [15:14]); expcnt and lgkmcnt are left at their maxima.
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitVm16 = 0x4F70;
+constexpr int kWaitVm12 = 0x0F7C;
 
 // Operand layouts.
 constexpr int kKMajor = 0;
@@ -121,19 +125,21 @@ struct Sources {
     OpSrc a, b;
 };
 
+// K-major: a wave fills `wave_rows` consecutive rows of the stage (64 for the
+// 256-row operand tiles, 32 for the A operand of a 128-row half tile).
 template <int L>
 __device__ __forceinline__ void set_op(OpSrc& s, const uint8_t* base, int origin, int extent, int R, int wave,
-                                       int lane)
+                                       int lane, int wave_rows = 64)
 {
     s.base = base;
     if (L == kKMajor) {
         s.ld = (uint32_t)R;
         s.step = 8u * (uint32_t)R;
-        s.row = origin + wave * 64 + (lane >> 3);
+        s.row = origin + wave * wave_rows + (lane >> 3);
         s.last = extent - 1;
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
-            const int row = (wave * 8 + par) * 8 + (lane >> 3);      // row within the tile
+            const int row = wave * wave_rows + par * 8 + (lane >> 3);  // row within the tile
             const uint32_t c16 = (uint32_t)(((lane & 7) ^ swz(row)) * 16);
             s.off[par] = c16;                                         // EDGE form: chunk only
             s.off[par + 2] = (uint32_t)s.row * (uint32_t)R + c16;     // interior form
@@ -191,6 +197,27 @@ __device__ __forceinline__ void issue_stage(const Sources& src, uint32_t stage, 
 {
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) issue_one<EDGE, LA, LB>(src, stage, kt, wave, idx);
+}
+
+// Half tile (128 rows of A x 256 columns of B, K-major operands): a stage
+// holds 16 KB of A (4 loads per wave) and the usual 32 KB of B (8 per wave).
+// Load idx (0..11): 0..3 fill A, 4..11 fill B.
+__device__ __forceinline__ void issue_half(const Sources& src, uint32_t stage, int kt, int wave, int idx)
+{
+    if (idx < 4) {
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(stage + (uint32_t)(wave * 4 + idx) * 1024u);
+        issue_op<kKMajor, false>(src.a, lds, kt, idx);
+    } else {
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(stage + (uint32_t)kStageA +
+                                                            (uint32_t)(wave * 8 + idx - 4) * 1024u);
+        issue_op<kKMajor, false>(src.b, lds, kt, idx - 4);
+    }
+}
+
+__device__ __forceinline__ void issue_half_stage(const Sources& src, uint32_t stage, int kt, int wave)
+{
+#pragma unroll
+    for (int idx = 0; idx < 12; ++idx) issue_half(src, stage, kt, wave, idx);
 }
 
 // Fragments of the 16x16x128 instruction: block b covers 16 rows of A (or of
@@ -329,6 +356,71 @@ __device__ __forceinline__ void tile_mainloop(v4f (&acc)[8][8], v8i (&bq)[8], v8
     __syncthreads();
 }
 
+// Half tiles balance the last partial round of a launch (tiles that would
+// leave most CUs idle are split into two 128-row halves, each a unit of work).
+// A wave owns 64 x 128 outputs (A blocks 0..3 of its 64 rows, B blocks 0..7 of
+// its 128 columns).  A step is 32 instructions (B block outer); interleaved
+// with them: the next step's B block j is read into the registers of block j
+// right after its last use, the next step's A blocks go to the other A buffer,
+// and the 12 loads of tile k+2 are issued into the stage this step's fragments
+// came from.  One barrier per step (after this wave's loads of tile k+1 are
+// waited for) separates the reads of a stage from the loads that refill it.
+template <int FA, int FB, bool NEXT>
+__device__ __forceinline__ void half_step(v4f (&acc)[8][8], v8i (&bq)[8], const v8i (&ac)[4], v8i (&an)[4],
+                                          const Sources& src, uint32_t cur_addr, const uint8_t* nxt, int kt_issue,
+                                          int wave, int wm, int wn, int lane)
+{
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+        const int j = t >> 2, i = t & 3;
+        mma16<FA, FB>(acc, ac[i], bq[j], i, j);
+        if (NEXT) {
+            if (i == 3) bq[j] = frag_k(nxt + kStageA, wn * 8 + j, lane);
+            if ((t & 7) == 1) an[t >> 3] = frag_k(nxt, wm * 4 + (t >> 3), lane);
+            if ((t & 1) == 0 && t < 24) issue_half(src, cur_addr, kt_issue, wave, t >> 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int FA, int FB>
+__device__ __forceinline__ void tile_mainloop_half(v4f (&acc)[8][8], v8i (&bq)[8], v8i (&a0)[4], v8i (&a1)[4],
+                                                   const Sources& src, uint8_t* lds, uint32_t lds_addr, int KT,
+                                                   int wave, int wm, int wn, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
+    __builtin_amdgcn_s_waitcnt(kWaitVm12);    // stage 0 landed; stage 1's 12 loads may be in flight
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bq[j] = frag_k(lds + kStageA, wn * 8 + j, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a0[i] = frag_k(lds, wm * 4 + i, lane);
+    int kt = 0;
+    for (; kt + 2 < KT; kt += 2) {            // steps kt (even stage) and kt + 1 (odd stage)
+        mid_step_barrier();
+        half_step<FA, FB, true>(acc, bq, a0, a1, src, lds_addr, lds + kStage, kt + 2, wave, wm, wn, lane);
+        mid_step_barrier();
+        half_step<FA, FB, true>(acc, bq, a1, a0, src, lds_addr + kStage, lds, min(kt + 3, KT - 1), wave, wm, wn,
+                                lane);
+    }
+    if (kt + 1 < KT) {                        // two steps left
+        mid_step_barrier();
+        half_step<FA, FB, true>(acc, bq, a0, a1, src, lds_addr, lds + kStage, KT - 1, wave, wm, wn, lane);
+        mid_step_barrier();
+        half_step<FA, FB, false>(acc, bq, a1, a0, src, 0, lds, 0, wave, wm, wn, lane);
+    } else {                                  // one step left
+        mid_step_barrier();
+        half_step<FA, FB, false>(acc, bq, a0, a1, src, 0, lds, 0, wave, wm, wn, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+}
+
 // A launch covers a group of up to kMaxGroup independent problems of the same
 // operand formats (e.g. the dgrad and wgrad products of one linear).  Their
 // tiles form one virtual tile range, problem after problem; the host orders
@@ -352,6 +444,10 @@ struct GemmGroup {
     GemmProblem p[kMaxGroup];
     int count;
     int total_tiles;
+    int full_units;       // units 0 .. full_units - 1 are the tiles of the same index; unit
+                          // full_units + 2 k + h is half h of tile full_units + k
+    int first_unit;       // this launch walks units first_unit .. units - 1
+    int units;
 };
 
 // Everything a workgroup needs about its current tile (all wave-uniform).
@@ -359,8 +455,7 @@ struct Work {
     const uint8_t* A;
     const uint8_t* B;
     uint16_t* out;
-    const float* inv_a;
-    const float* inv_b;
+    int prob;       // index of the tile's problem in the group
     int P, Q, R, KT;
     int la, lb;
     int ms, ns;     // logical origin (first row / column this tile stores)
@@ -370,17 +465,21 @@ struct Work {
 // Output tile of a virtual tile id: the problem it falls in, then a grouped
 // raster order within it (kGroupM tile rows per group, column-major within a
 // group), so consecutive ids share A and B panels.
-template <bool EDGE>
-__device__ __forceinline__ Work work_of(const GemmGroup& g, int v)
+template <bool EDGE, bool HALF>
+__device__ __forceinline__ Work work_of(const GemmGroup& g, int u)
 {
+    int v = u, hh = -1;
+    if (HALF) {
+        v = g.full_units + ((u - g.full_units) >> 1);
+        hh = (u - g.full_units) & 1;
+    }
     const bool second = g.count > 1 && v >= g.p[1].first_tile;
     const GemmProblem& pr = second ? g.p[1] : g.p[0];
     Work w;
     w.A = pr.A;
     w.B = pr.B;
     w.out = pr.out;
-    w.inv_a = pr.inv_a;
-    w.inv_b = pr.inv_b;
+    w.prob = second;
     w.P = pr.P;
     w.Q = pr.Q;
     w.R = pr.R;
@@ -395,9 +494,11 @@ __device__ __forceinline__ Work work_of(const GemmGroup& g, int v)
     const int in_group = lv - group * group_size;
     w.ms = (first_m + in_group % gm) * kBM;
     w.ns = (in_group / gm) * kBN;
+    if (HALF) w.ms += hh * (kBM / 2);
     // A last partial tile is shifted back to end at the matrix edge (P, Q >= 256),
-    // recomputing rows / columns of its neighbour that it then does not store.
-    w.m0 = EDGE ? w.ms : min(w.ms, w.P - kBM);
+    // recomputing rows / columns of its neighbour that it then does not store
+    // (a half tile that starts past the last row stores nothing).
+    w.m0 = EDGE ? w.ms : min(w.ms, w.P - (HALF ? kBM / 2 : kBM));
     w.n0 = EDGE ? w.ns : min(w.ns, w.Q - kBN);
     return w;
 }
@@ -415,10 +516,15 @@ constexpr int kSetKK = 0;       // (K, K)
 constexpr int kSetMN = 1;       // (K, MN) and (MN, MN)
 
 // Set up the sources of tile w and issue its first two stages.
-template <bool EDGE, int SET>
+template <bool EDGE, int SET, bool HALF>
 __device__ __forceinline__ void start_tile(Sources& src, const Work& w, uint32_t lds_addr, int wave, int lane)
 {
-    if (SET == kSetKK) {
+    if (HALF) {
+        set_op<kKMajor>(src.a, w.A, w.m0, w.P, w.R, wave, lane, 32);
+        set_op<kKMajor>(src.b, w.B, w.n0, w.Q, w.R, wave, lane);
+        issue_half_stage(src, lds_addr, 0, wave);
+        issue_half_stage(src, lds_addr + kStage, min(1, w.KT - 1), wave);
+    } else if (SET == kSetKK) {
         set_sources<kKMajor, kKMajor>(src, w, wave, lane);
         issue_stage<EDGE, kKMajor, kKMajor>(src, lds_addr, 0, wave);
         issue_stage<EDGE, kKMajor, kKMajor>(src, lds_addr + kStage, min(1, w.KT - 1), wave);
@@ -433,13 +539,61 @@ __device__ __forceinline__ void start_tile(Sources& src, const Work& w, uint32_t
     }
 }
 
-// Persistent kernel: one workgroup per CU walks the virtual tiles v = slot,
-// slot + G, slot + 2G, ... where slot renumbers the workgroups XCD-major
-// (workgroups are dealt round-robin to the 8 XCDs, each with its own L2), so in
-// every round the 32 CUs of one XCD work on 32 consecutive tiles of the raster
-// order.  While a tile's epilogue stores run, the first two stages of the next
-// tile are already loading.
-template <int FA, int FB, bool EDGE, int SET>
+// Epilogue of a finished tile: descale and round to bf16, stage 32-row chunks of
+// the wave's tile (8 A blocks x 128 columns, 4 for a half tile) in its private
+// LDS region (16-byte chunks of a 256-byte row XOR-swizzled by row), read back
+// 16 bytes per lane and store four full 256-byte row segments per instruction.
+template <bool HALF>
+__device__ __forceinline__ void epilogue(const v4f (&acc)[8][8], const Work& done, float d, uint8_t* epi, int wave,
+                                         int wm, int wn, int lane)
+{
+    uint8_t* ew = epi + wave * kEpiWave;
+    // The LDS addresses below depend only on the lane; computing them here from
+    // an opaque copy of it keeps the compiler from holding ~40 of them live
+    // across the whole persistent loop (where they would spill).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int r16 = ln & 15, q4 = ln >> 4;
+    const int wrow = done.m0 + wm * (HALF ? 64 : 128);
+#pragma unroll
+    for (int c2 = 0; c2 < (HALF ? 2 : 4); ++c2) {        // chunk: A blocks 2*c2, 2*c2+1 (32 rows)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int i = 2 * c2 + h;
+            const int row = h * 16 + r16;             // row within the chunk
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const f32x2 v01 = {acc[i][j][0] * d, acc[i][j][1] * d};
+                const f32x2 v23 = {acc[i][j][2] * d, acc[i][j][3] * d};
+                uint2 o;
+                o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
+                o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
+                // columns j*16 + 4*q4 .. +3 = bytes j*32 + 8*q4: 16-byte chunk 2j + q4/2
+                const int chunk = (2 * j + (q4 >> 1)) ^ (row & 15);
+                *reinterpret_cast<uint2*>(ew + row * 256 + chunk * 16 + (q4 & 1) * 8) = o;
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < kEpiRows / 4; ++it) {
+            const int rr = it * 4 + q4;                           // row within the chunk
+            const int c = r16;                                    // logical 16-byte chunk
+            const uint4 o = *reinterpret_cast<const uint4*>(ew + rr * 256 + ((c ^ (rr & 15)) * 16));
+            const int m = wrow + c2 * 32 + rr;
+            const int n = done.n0 + wn * 128 + c * 8;
+            if (m >= done.ms && m < done.P && n >= done.ns && n < done.Q)
+                *reinterpret_cast<uint4*>(done.out + (size_t)m * done.Q + n) = o;
+        }
+    }
+}
+
+// Persistent kernel: one workgroup per CU walks the units v = slot, slot + G,
+// slot + 2G, ... (a unit is a tile, or a half tile in a balanced last round)
+// where slot renumbers the workgroups XCD-major (workgroups are dealt
+// round-robin to the 8 XCDs, each with its own L2), so in every round the 32
+// CUs of one XCD work on 32 consecutive units of the raster order.  While a
+// tile's epilogue stores run, the first two stages of the next tile are
+// already loading.
+template <int FA, int FB, bool EDGE, int SET, bool HALF>
 __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
@@ -458,12 +612,21 @@ __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
     v8i bq[8], alo[4], ahi[4];
     v4f acc[8][8];
 
-    int v = slot;
-    if (v >= g.total_tiles) return;
-    Work w = work_of<EDGE>(g, v);
-    start_tile<EDGE, SET>(src, w, lds_addr, wave, lane);
+    int v = g.first_unit + slot;
+    if (v >= g.units) return;
+    // The descale factors are loaded once, here, ahead of every direct-to-LDS
+    // load, and first used after a K loop (whose final wait has drained all
+    // loads).  The compiler does not see the inline-assembly loads: a wait of
+    // its own for a plain load issued after them (e.g. in the epilogue) would
+    // be a full vmcnt(0), i.e. a wait for the next tile's whole prefetch.
+    const float d0 = g.p[0].inv_a[0] * g.p[0].inv_b[0];
+    const float d1 = g.count > 1 ? g.p[1].inv_a[0] * g.p[1].inv_b[0] : d0;
+    Work w = work_of<EDGE, HALF>(g, v);
+    start_tile<EDGE, SET, HALF>(src, w, lds_addr, wave, lane);
     for (;;) {
-        if (SET == kSetKK)
+        if (HALF)
+            tile_mainloop_half<FA, FB>(acc, bq, alo, ahi, src, lds, lds_addr, w.KT, wave, wm, wn, lane);
+        else if (SET == kSetKK)
             tile_mainloop<FA, FB, EDGE, kKMajor, kKMajor>(acc, bq, alo, ahi, src, lds, lds_addr, w.KT, wave, wm, wn,
                                                           lane);
         else if (w.la == kMNMajor)
@@ -473,55 +636,22 @@ __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
             tile_mainloop<FA, FB, EDGE, kKMajor, kMNMajor>(acc, bq, alo, ahi, src, lds, lds_addr, w.KT, wave, wm, wn,
                                                            lane);
 
+        float d = w.prob ? d1 : d0;
+        asm volatile("" : "+v"(d));           // materialised here, before the next prefetch
         const Work done = w;
         const int next = v + G;
-        if (next < g.total_tiles) {
+        if (next < g.units) {
             v = next;
-            w = work_of<EDGE>(g, v);
-            start_tile<EDGE, SET>(src, w, lds_addr, wave, lane);
+            w = work_of<EDGE, HALF>(g, v);
+            start_tile<EDGE, SET, HALF>(src, w, lds_addr, wave, lane);
         }
 
-        // ---- epilogue of `done`: descale and round to bf16, stage 32-row chunks of
-        // the wave's 128 x 128 tile in its private LDS region (16-byte chunks of a
-        // 256-byte row XOR-swizzled by row), read back 16 bytes per lane and store
-        // four full 256-byte row segments per instruction.
-        const float d = done.inv_a[0] * done.inv_b[0];
-        uint8_t* ew = epi + wave * kEpiWave;
-        const int r16 = lane & 15, q4 = lane >> 4;
-#pragma unroll
-        for (int c2 = 0; c2 < 4; ++c2) {                 // chunk: A blocks 2*c2, 2*c2+1 (32 rows)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int i = 2 * c2 + h;
-                const int row = h * 16 + r16;             // row within the chunk
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const f32x2 v01 = {acc[i][j][0] * d, acc[i][j][1] * d};
-                    const f32x2 v23 = {acc[i][j][2] * d, acc[i][j][3] * d};
-                    uint2 o;
-                    o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
-                    o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
-                    // columns j*16 + 4*q4 .. +3 = bytes j*32 + 8*q4: 16-byte chunk 2j + q4/2
-                    const int chunk = (2 * j + (q4 >> 1)) ^ (row & 15);
-                    *reinterpret_cast<uint2*>(ew + row * 256 + chunk * 16 + (q4 & 1) * 8) = o;
-                }
-            }
-#pragma unroll
-            for (int it = 0; it < kEpiRows / 4; ++it) {
-                const int rr = it * 4 + (lane >> 4);                   // row within the chunk
-                const int c = lane & 15;                              // logical 16-byte chunk
-                const uint4 o = *reinterpret_cast<const uint4*>(ew + rr * 256 + ((c ^ (rr & 15)) * 16));
-                const int m = done.m0 + wm * 128 + c2 * 32 + rr;
-                const int n = done.n0 + wn * 128 + c * 8;
-                if (m >= done.ms && m < done.P && n >= done.ns && n < done.Q)
-                    *reinterpret_cast<uint4*>(done.out + (size_t)m * done.Q + n) = o;
-            }
-        }
-        // The loop-top wait (vmcnt <= 16) then proves the next tile's first stage
-        // has landed: if one of its loads were pending, the 16 later loads of the
-        // second stage would be too (loads complete in order), whatever the
-        // interleaved stores do.
-        if (next >= g.total_tiles) break;
+        epilogue<HALF>(acc, done, d, epi, wave, wm, wn, lane);
+        // The loop-top wait (vmcnt <= 16, or 12 for a half tile) then proves the
+        // next tile's first stage has landed: if one of its loads were pending,
+        // the 16 (12) later loads of the second stage would be too (loads
+        // complete in order), whatever the interleaved stores do.
+        if (next >= g.units) break;
     }
 }
 
@@ -556,11 +686,31 @@ static hipError_t launch_group(GemmGroup g, hipStream_t stream)
         edge = edge || g.p[i].P < kBM || g.p[i].Q < kBN;
     }
     g.total_tiles = total;
-    const int grid = total < device_cu_count() ? total : device_cu_count();   // one workgroup per CU
-    if (!edge)
-        gemm_tn_kernel<FA, FB, false, SET><<<grid, 256, 0, stream>>>(g);
-    else
-        gemm_tn_kernel<FA, FB, true, SET><<<grid, 256, 0, stream>>>(g);
+    const int cus = device_cu_count();
+    if (edge) {
+        g.full_units = g.units = total;
+        g.first_unit = 0;
+        gemm_tn_kernel<FA, FB, true, SET, false><<<total < cus ? total : cus, 256, 0, stream>>>(g);
+        return hipGetLastError();
+    }
+    // Balance the last round: when the tiles past the last full round of the
+    // persistent grid fill at most half of it, each becomes two half tiles (a
+    // second launch of their own), so that round takes about half as long.
+    // K-major operands only.
+    const int tail = total % cus;
+    const bool split = SET == kSetKK && tail > 0 && 2 * tail <= cus;
+    g.full_units = split ? total - tail : total;
+    g.units = g.full_units;
+    g.first_unit = 0;
+    if (g.full_units > 0)
+        gemm_tn_kernel<FA, FB, false, SET, false><<<g.full_units < cus ? g.full_units : cus, 256, 0, stream>>>(g);
+    if constexpr (SET == kSetKK) {
+        if (split) {
+            g.first_unit = g.full_units;
+            g.units = total + tail;
+            gemm_tn_kernel<FA, FB, false, SET, true><<<2 * tail, 256, 0, stream>>>(g);
+        }
+    }
     return hipGetLastError();
 }
 

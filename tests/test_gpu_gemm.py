@@ -85,7 +85,7 @@ def test_identity_and_ones(fp8, orc):
 
 @pytest.mark.parametrize("entry,fa", ENTRIES)
 @pytest.mark.parametrize("P,Q,R", [(16, 16, 128), (128, 256, 256), (272, 528, 384), (512, 768, 1024),
-                                   (1040, 272, 640), (768, 1280, 2048)])
+                                   (1040, 272, 640), (768, 1280, 2048), (256, 512, 128), (528, 1008, 384)])
 def test_random_shapes(fp8, orc, entry, fa, P, Q, R):
     say("gemm random", entry, fa, P, Q, R)
     rng = np.random.default_rng(P * 3 + Q * 5 + R)
@@ -100,6 +100,31 @@ def test_random_shapes(fp8, orc, entry, fa, P, Q, R):
     # determinism
     y2 = u16(run(fp8, entry, a, fa, b, inv_a, inv_b))
     assert np.array_equal(y, y2)
+
+
+# Launches whose last round is balanced with 128-row half tiles: 17 x 16 tiles
+# (a full round of 256, then the 16 tiles of the last tile row as 32 halves),
+# with an exact and a ragged last tile row, even and odd reductions.
+@pytest.mark.parametrize("entry,fa", [("fwd", E4M3), ("wgrad", E5M2)])
+@pytest.mark.parametrize("P,Q,R", [(4352, 4096, 256), (4304, 4096, 384), (4208, 4000, 128)])
+def test_balanced_last_round(fp8, orc, entry, fa, P, Q, R):
+    say("gemm balanced tail", entry, fa, P, Q, R)
+    rng = np.random.default_rng(P + Q + R + fa)
+    a = random_codes(rng, (P, R), fa, 40.0 if fa == E4M3 else 2000.0)
+    b = random_codes(rng, (Q, R), E4M3, 40.0)
+    inv_a, inv_b = np.float32(1 / 448.0), np.float32(0.0123)
+    y = u16(run(fp8, entry, a, fa, b, inv_a, inv_b))
+    # every row of the last tile row (the half tiles) and of its neighbour, plus a sample
+    rows = np.unique(np.concatenate([np.arange(4096 - 64, P), np.random.default_rng(2).integers(0, 4096, 64)]))
+    ref = orc.gemm(a, fa, b, E4M3, inv_a, inv_b, rows=rows.astype(np.int64))
+    gemm_compare(y[rows], ref, f"{entry} {P}x{Q}x{R}")
+    assert_within_sum_bound(y[rows], ref, a, fa, b, E4M3, inv_a, inv_b, rows.astype(np.int64), f"{entry} {P}x{Q}x{R}")
+    # rows computed by half tiles are bit-identical to the same rows computed by
+    # full tiles: put the last 256 rows first in a 4096-row launch (exactly one
+    # full round of 16 x 16 tiles, nothing split)
+    a2 = np.ascontiguousarray(np.concatenate([a[P - 256:], a[:4096 - 256]]))
+    y2 = u16(run(fp8, entry, a2, fa, b, inv_a, inv_b))
+    assert np.array_equal(y[P - 256:], y2[:256])
 
 
 FULL = [
