@@ -46,9 +46,22 @@ import workloads  # noqa: E402
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA peak
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E peak
 
-# rocprofv3 kernel names of the library's kernels
-GEMM_KERNEL = {(0, 0, 0): "fp8k::gemm_tn_kernel<0, 0, false, 0>", (1, 0, 0): "fp8k::gemm_tn_kernel<1, 0, false, 0>",
-               (1, 0, 1): "fp8k::gemm_tn_kernel<1, 0, false, 1>"}
+# rocprofv3 kernel names of the library's kernels (format of A, format of B,
+# edge tiles, layout set, half tiles); a GEMM call whose last round is balanced
+# runs a second launch of the half-tile instantiation
+GEMM_KERNEL = {(0, 0, 0): "fp8k::gemm_tn_kernel<0, 0, false, 0, false>",
+               (1, 0, 0): "fp8k::gemm_tn_kernel<1, 0, false, 0, false>",
+               (1, 0, 1): "fp8k::gemm_tn_kernel<1, 0, false, 1, false>"}
+
+
+def tail_launch(probs, kmajor, cus):
+    """Whether a GEMM call also launches the half-tile kernel: the same rule as the
+    library's launcher (K-major operands, no edge tiles, and the tiles past the
+    last full round of `cus` workgroups fill at most half of it)."""
+    if not kmajor or any(P < 256 or Q < 256 for P, Q, _, _ in probs):
+        return False
+    tail = sum(-(-P // 256) * -(-Q // 256) for P, Q, _, _ in probs) % cus
+    return 0 < tail and 2 * tail <= cus
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_traffic_layer7b.txt")
 GEMM_SOURCE = os.path.join(ROOT, "fp8_precision_amd", "csrc", "gemm.hip")
 
@@ -90,6 +103,8 @@ WORKLOADS = {
 def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False):
     """Inputs and the ordered list of calls of one layer step of a configuration.
 
+    The step starts by clearing its buffer of per-tensor absmax statistics (one
+    fill); every absmax then accumulates into its own slot.
     Forward: absmax + quantise of X and W, FP8 GEMM, for QKV, O and gate/up;
     the fused SwiGLU requant of the gate/up output feeds the down linear.
     Backward: absmax + e5m2 quantise of dY, then dgrad and wgrad in one launch.
@@ -113,6 +128,11 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False):
     bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)
     lin = {l.name: (i, l) for i, l in enumerate(cfg.linears)}
     gemm_fwd_kernel = GEMM_KERNEL[(0, 0, 0)]
+    # the step's per-tensor absmax statistics live in one buffer, cleared once at
+    # the start of the step; each absmax accumulates into its slot
+    stats = torch.empty(64, dtype=torch.float32, device=dev)
+    ops.append(Op("clear statistics", lambda: stats.zero_(), "zero", 0))
+    slots = iter(range(64))
 
     def quantize_op(tag, x, rows, cols, fmt, am, want_qt):
         sc, inv = f32(), f32()
@@ -124,8 +144,9 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False):
         return q, qt, inv
 
     def quant_ops(tag, x, rows, cols, fmt, want_qt):
-        am = f32()
-        ops.append(Op(f"absmax {tag}", lambda: fp8.absmax(x, am), "absmax", 2 * rows * cols,
+        k = next(slots)
+        am = stats[k:k + 1]
+        ops.append(Op(f"absmax {tag}", lambda: fp8.absmax(x, am, accumulate=True), "absmax", 2 * rows * cols,
                       meta={"rows": rows, "cols": cols, "fmt": fmt}))
         return quantize_op(tag, x, rows, cols, fmt, am, want_qt) + (am,)
 
@@ -321,6 +342,54 @@ def cpu_baseline(ops, gemm_rows):
                        f"estimated full step {est:.1f} s on {threads} threads")}
 
 
+def sustained_clock(ops, seconds=4.0):
+    """Median graphics clock and socket power while the step loops (outside the timed region).
+
+    A background thread queries `amd-smi metric -c -p --json` (current clock of
+    every graphics clock domain, socket power) while the main thread keeps the
+    GPU busy with the step.  Returns None when amd-smi is not available.
+    """
+    import shutil
+    import subprocess
+    import threading
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(exe):
+        return None
+    samples, stop = [], threading.Event()
+
+    def loop():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([exe, "metric", "-c", "-p", "--json", "-g", "0"], capture_output=True, text=True,
+                                   timeout=20)
+                d = json.loads(r.stdout)
+                g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+                clks = [v["clk"]["value"] for k, v in g["clock"].items()
+                        if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+                pw = g["power"]["socket_power"]["value"]
+                if clks:
+                    samples.append((float(np.median(clks)), float(pw)))
+            except Exception:   # a malformed or missing sample is skipped
+                pass
+
+    for _ in range(5):          # the clock ramps up under load
+        run_step(ops)
+    th = threading.Thread(target=loop, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            run_step(ops)
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=30)
+    if not samples:
+        return None
+    c = float(np.median([x[0] for x in samples]))
+    return {"gfx_mhz_median": round(c, 1), "socket_power_w_median": float(np.median([x[1] for x in samples])),
+            "samples": len(samples), "source": "amd-smi metric -c -p while the step loops, after the timed region"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +407,7 @@ def main():
                     help="chain the MLP backward: down dgrad -> fused SwiGLU backward -> gate/up backward "
                          "(instead of a drawn gate/up output gradient)")
     ap.add_argument("--breakdown", action="store_true", help="also time every call (separate pass)")
+    ap.add_argument("--no-clock", action="store_true", help="skip the sustained-clock sampling (amd-smi)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every box here has one GPU "
@@ -363,16 +433,19 @@ def main():
     gemm_flop = sum(op.work for op in ops if op.kind == "gemm")
     value = gemm_flop / step_s / 1e12
 
-    # dominant kernel: the GEMM kernel with the largest summed time in the step
+    # dominant kernel: the GEMM kernel with the largest summed time in the step;
+    # its figures are per library call (a call may add a half-tile tail launch)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     by_kernel = {}
     for op in ops:
         if op.kind != "gemm":
             continue
-        d = by_kernel.setdefault(op.kernel, {"flop": 0.0, "time": 0.0, "launches": 0})
+        d = by_kernel.setdefault(op.kernel, {"flop": 0.0, "time": 0.0, "launches": 0, "tail_launches": 0})
         ts = per_op[op.name]
         d["flop"] += op.work
         d["time"] += float(np.mean(ts))
         d["launches"] += 1
+        d["tail_launches"] += tail_launch(op.meta["probs"], op.kernel.endswith(", 0, false>"), cus)
     dom_name, dom = max(by_kernel.items(), key=lambda kv: kv[1]["time"])
     achieved = dom["flop"] / dom["time"] / 1e12
     gemm_time = sum(d["time"] for d in by_kernel.values())
@@ -380,10 +453,13 @@ def main():
     breakdown = None
     if args.breakdown:
         _, _, per_all = time_steps(ops, max(3, args.steps // 2), stream,
-                                   instrument_kinds=("gemm", "absmax", "quantize", "swiglu", "swiglu_bwd"))
+                                   instrument_kinds=("gemm", "absmax", "quantize", "swiglu", "swiglu_bwd", "zero"))
         breakdown = []
         for op in ops:
             t = float(np.mean(per_all[op.name]))
+            if op.kind == "zero":
+                breakdown.append({"call": op.name, "us": round(t * 1e6, 2)})
+                continue
             unit = "TFLOP/s" if op.kind == "gemm" else "GB/s"
             rate = op.work / t / (1e12 if op.kind == "gemm" else 1e9)
             breakdown.append({"call": op.name, "us": round(t * 1e6, 2), "rate": round(rate, 1), "unit": unit})
@@ -393,6 +469,7 @@ def main():
     else:
         quant_gbs = None
 
+    clock = None if args.no_clock else sustained_clock(ops)
     want_cpu = not args.no_cpu_baseline and (args.workload == "c3" or args.cpu_baseline)
     cpu = cpu_baseline(ops, args.cpu_gemm_rows) if want_cpu else None
 
@@ -422,8 +499,15 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(dom_name),
                      "kernel": dom_name, "launches_per_step": dom["launches"],
-                     "avg_launch_us": round(dom["time"] / dom["launches"] * 1e6, 2)},
+                     "tail_launches_per_step": dom["tail_launches"],
+                     "peak_at_sustained_clock": (round(FP8_PEAK_TFLOPS * clock["gfx_mhz_median"] / 2400.0, 1)
+                                                 if clock else None),
+                     "frac_at_sustained_clock": (round(achieved / (FP8_PEAK_TFLOPS * clock["gfx_mhz_median"] / 2400.0), 4)
+                                                 if clock else None),
+                     "avg_launch_us": round(dom["time"] / dom["launches"] * 1e6, 2),
+                     "timing": "per library call (events around the call), including its tail launch if any"},
         "cpu_baseline": cpu,
+        "sustained_clock": clock,
         "wall_s": round(wall, 3),
     }
     if quant_gbs is not None:

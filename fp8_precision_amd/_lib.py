@@ -28,6 +28,7 @@ _SIGS = {
     "fp8_status_string": (ctypes.c_char_p, [_i32]),
     "fp8_last_error": (ctypes.c_char_p, []),
     "fp8_absmax": (_i32, [_vp, _i64, _vp, _vp]),
+    "fp8_absmax_accumulate": (_i32, [_vp, _i64, _vp, _vp]),
     "fp8_quantize": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp8_swiglu_requant": (_i32, [_vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp]),
     "fp8_swiglu_backward": (_i32, [_vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -86,9 +87,19 @@ def _scalar(t, name, device):
     return t
 
 
-def absmax(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """max |x| of a bf16 tensor, as a one-element fp32 device tensor."""
+def absmax(x: torch.Tensor, out: torch.Tensor | None = None, accumulate: bool = False) -> torch.Tensor:
+    """max |x| of a bf16 tensor, as a one-element fp32 device tensor.
+
+    With ``accumulate`` the result is max(out, max |x|) (``out`` required,
+    holding +0 or an earlier result): fp8_absmax_accumulate.
+    """
     _dev_tensor(x, "x", torch.bfloat16)
+    if accumulate:
+        if out is None:
+            raise ValueError("accumulate needs out")
+        out = _scalar(out, "out", x.device)
+        _check("fp8_absmax_accumulate", _lib.fp8_absmax_accumulate(_ptr(x), x.numel(), _ptr(out), _stream(x)))
+        return out
     out = _scalar(out, "out", x.device)
     _check("fp8_absmax", _lib.fp8_absmax(_ptr(x), x.numel(), _ptr(out), _stream(x)))
     return out

@@ -23,6 +23,12 @@ fp8_status fail(fp8_status st, const char* what)
     return st;
 }
 
+fp8_status fail(fp8_status st, const std::string& what)
+{
+    t_last_error = what;
+    return st;
+}
+
 fp8_status fail_hip(const char* call, hipError_t e)
 {
     char buf[256];
@@ -97,17 +103,29 @@ const char* fp8_status_string(fp8_status s)
 
 const char* fp8_last_error(void) { return t_last_error.c_str(); }
 
-fp8_status fp8_absmax(const void* x, int64_t n, float* absmax, hipStream_t stream)
+static fp8_status absmax_common(const char* name, const void* x, int64_t n, float* absmax, bool accumulate,
+                                hipStream_t stream)
 {
     t_last_error.clear();
-    if (!x || !absmax) return fail(FP8_ERR_INVALID, "fp8_absmax: null pointer");
-    if (n <= 0 || n > kMaxElems) return fail(FP8_ERR_INVALID, "fp8_absmax: n must be in [1, 2^40]");
-    if (overlap(x, 2 * n, absmax, 4)) return fail(FP8_ERR_INVALID, "fp8_absmax: absmax overlaps x");
+    const std::string f(name);
+    if (!x || !absmax) return fail(FP8_ERR_INVALID, f + ": null pointer");
+    if (n <= 0 || n > kMaxElems) return fail(FP8_ERR_INVALID, f + ": n must be in [1, 2^40]");
+    if (overlap(x, 2 * n, absmax, 4)) return fail(FP8_ERR_INVALID, f + ": absmax overlaps x");
     if (!aligned(x, 16) || !aligned(absmax, 4))
-        return fail(FP8_ERR_UNSUPPORTED, "fp8_absmax: x must be 16-byte and absmax 4-byte aligned");
-    hipError_t e = fp8k::launch_absmax_bf16(x, n, absmax, stream);
-    if (e != hipSuccess) return fail_hip("fp8_absmax", e);
+        return fail(FP8_ERR_UNSUPPORTED, f + ": x must be 16-byte and absmax 4-byte aligned");
+    hipError_t e = fp8k::launch_absmax_bf16(x, n, absmax, accumulate, stream);
+    if (e != hipSuccess) return fail_hip(name, e);
     return FP8_OK;
+}
+
+fp8_status fp8_absmax(const void* x, int64_t n, float* absmax, hipStream_t stream)
+{
+    return absmax_common("fp8_absmax", x, n, absmax, false, stream);
+}
+
+fp8_status fp8_absmax_accumulate(const void* x, int64_t n, float* absmax, hipStream_t stream)
+{
+    return absmax_common("fp8_absmax_accumulate", x, n, absmax, true, stream);
 }
 
 fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt, const float* absmax,

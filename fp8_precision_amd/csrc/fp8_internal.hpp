@@ -10,7 +10,7 @@ namespace fp8k {
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
-hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, hipStream_t stream);
+hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, bool accumulate, hipStream_t stream);
 
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, const float* absmax,
                            uint8_t* q, uint8_t* qt, float* scale, float* inv_scale,

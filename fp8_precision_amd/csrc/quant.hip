@@ -84,7 +84,7 @@ __global__ void __launch_bounds__(kAbsThreads) absmax_bf16_kernel(const u32x4* _
     block_max_to_global(r << 16, out);
 }
 
-hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, hipStream_t stream)
+hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, bool accumulate, hipStream_t stream)
 {
     const int64_t nvec = n / 8;
     const int ntail = (int)(n - nvec * 8);
@@ -92,7 +92,7 @@ hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, hipStream
     const int64_t cap = (int64_t)device_cu_count();  // one block per CU (one atomic per block)
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
-    zero_u32_kernel<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax));
+    if (!accumulate) zero_u32_kernel<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax));
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
     const uint16_t* tail = reinterpret_cast<const uint16_t*>(x) + nvec * 8;
     uint32_t* out = reinterpret_cast<uint32_t*>(absmax);

@@ -79,6 +79,22 @@ const char* fp8_last_error(void);
 fp8_status fp8_absmax(const void* x, int64_t n, float* absmax, hipStream_t stream);
 
 /*
+ * Running absmax: *absmax = max(*absmax, max over i < n of |x[i]|), the same
+ * reduction as fp8_absmax without resetting the accumulator first, for a
+ * statistic gathered over several calls (a tensor held in pieces) or a set of
+ * statistics that the caller clears together once per step (one fill instead
+ * of one per tensor).  The maximum is taken on the fp32 bit patterns, so the
+ * NaN / infinity rules of fp8_absmax hold across calls; *absmax must start as
+ * +0 or as an earlier result (its sign bit clear).  Calls that accumulate into
+ * one location may run in any order or concurrently.
+ *
+ *   x       bf16 [n], 16-byte aligned
+ *   n       number of elements, n >= 1
+ *   absmax  one fp32 in device memory (read and updated)
+ */
+fp8_status fp8_absmax_accumulate(const void* x, int64_t n, float* absmax, hipStream_t stream);
+
+/*
  * Quantise a bf16 [rows, cols] tensor with the scale of its absmax:
  *   s      = fp8_max / absmax  (one fp32 division; 1 when absmax == 0; held at
  *            FLT_MAX if the division overflows)

@@ -26,6 +26,7 @@ def lib():
     lib = ctypes.CDLL(LIB)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     lib.fp8_absmax.argtypes = [vp, i64, vp, vp]
+    lib.fp8_absmax_accumulate.argtypes = [vp, i64, vp, vp]
     lib.fp8_quantize.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp]
     lib.fp8_swiglu_requant.argtypes = [vp, i64, i64, vp, i32, vp, vp, vp, vp]
     lib.fp8_gemm_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
@@ -33,15 +34,15 @@ def lib():
     lib.fp8_gemm_wgrad.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.fp8_last_error.restype = ctypes.c_char_p
     lib.fp8_status_string.restype = ctypes.c_char_p
-    for f in ("fp8_absmax", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd", "fp8_gemm_dgrad",
-              "fp8_gemm_wgrad"):
+    for f in ("fp8_absmax", "fp8_absmax_accumulate", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd",
+              "fp8_gemm_dgrad", "fp8_gemm_wgrad"):
         getattr(lib, f).restype = i32
     return lib
 
 
 def test_header_declares_the_hot_path():
     names = declared_functions()
-    for want in ("fp8_absmax", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd", "fp8_gemm_dgrad",
+    for want in ("fp8_absmax", "fp8_absmax_accumulate", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd", "fp8_gemm_dgrad",
                  "fp8_gemm_wgrad", "fp8_gemm_backward", "fp8_gemm_dgrad_mn", "fp8_gemm_wgrad_mn",
                  "fp8_gemm_backward_mn", "fp8_swiglu_backward", "fp8_status_string", "fp8_last_error"):
         assert want in names
@@ -76,6 +77,17 @@ def test_absmax_validation(lib):
     assert b"overlaps" in lib.fp8_last_error()
     assert lib.fp8_absmax(A16 + 2, 16, C16, None) == UNSUPPORTED  # misaligned x
     assert lib.fp8_absmax(A16, 16, C16 + 1, None) == UNSUPPORTED
+
+
+def test_absmax_accumulate_validation(lib):
+    f = lib.fp8_absmax_accumulate
+    assert f(None, 16, C16, None) == INVALID
+    assert f(A16, 16, None, None) == INVALID
+    assert f(A16, 0, C16, None) == INVALID
+    assert f(A16, 16, A16 + 4, None) == INVALID
+    assert b"fp8_absmax_accumulate" in lib.fp8_last_error()
+    assert f(A16 + 8, 16, C16, None) == UNSUPPORTED
+    assert f(A16, 16, C16 + 2, None) == UNSUPPORTED
 
 
 def test_quantize_validation(lib):

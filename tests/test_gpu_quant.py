@@ -1,7 +1,8 @@
 """GPU parity of fp8_absmax and fp8_quantize against the oracle (bit-exact).
 
 * absmax: ragged lengths (including n < 8 and n % 8 != 0), planted maxima,
-  -0, infinities, NaN, subnormals;
+  -0, infinities, NaN, subnormals; the running (accumulating) form over pieces
+  and prior values;
 * the scale and inverse scale for every positive finite bf16 absmax;
 * every bf16 input pattern quantised under a set of retained absmax values
   (fresh, stale, zero, tiny -> clamped scale, huge, inf, NaN), both formats,
@@ -58,6 +59,44 @@ def test_absmax_special_values(fp8, orc):
         xt = torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16)
         got = scalar(fp8.absmax(dev(xt)))
         assert_f32_equal(got, orc.absmax_bf16(b), name)
+
+
+def test_absmax_accumulate(fp8, orc):
+    """fp8_absmax_accumulate: a tensor in pieces gives the whole tensor's absmax;
+    a prior value is kept when larger (NaN and +inf stay); neighbours untouched."""
+    n = 3 * 65536 + 40
+    x = workloads.draw(101, 7, (n,), 1.0)
+    bits = u16(x)
+    bits[70000] = 0xC2F6                                     # -123, the planted maximum
+    whole = orc.absmax_bf16(bits)
+    xd = dev(torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16))
+    stats = torch.full((5,), -7.0, dtype=torch.float32, device="cuda")
+    stats[2] = 0.0
+    cuts = [0, 65536, 65536 + 1000, n]                        # 16-byte aligned piece starts
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        fp8.absmax(xd[a:b], out=stats[2:3], accumulate=True)
+    torch.cuda.synchronize()
+    got = stats.cpu().numpy()
+    assert_f32_equal(got[2], whole, "pieces")
+    assert np.all(got[[0, 1, 3, 4]] == -7.0), "neighbouring statistics changed"
+    say("absmax accumulate priors")
+    for prior, want in [(1e6, np.float32(1e6)), (1.0, whole), (0.0, whole),
+                        (float("inf"), np.float32("inf")), (float("nan"), None)]:
+        o = torch.tensor([prior], dtype=torch.float32, device="cuda")
+        fp8.absmax(xd, out=o, accumulate=True)
+        r = scalar(o)
+        if want is None:
+            assert np.isnan(r)
+        else:
+            assert_f32_equal(r, want, f"prior {prior}")
+    # a NaN in the data wins over any prior, as in fp8_absmax
+    b2 = bits.copy()
+    b2[5] = 0x7FC1
+    o = torch.tensor([1e30], dtype=torch.float32, device="cuda")
+    fp8.absmax(dev(torch.from_numpy(b2.view(np.int16).copy()).view(torch.bfloat16)), out=o, accumulate=True)
+    assert np.isnan(scalar(o))
+    with pytest.raises(ValueError):
+        fp8.absmax(xd, accumulate=True)
 
 
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
