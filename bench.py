@@ -47,11 +47,13 @@ FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA peak
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E peak
 
 # rocprofv3 kernel names of the library's kernels (format of A, format of B,
-# edge tiles, layout set, half tiles); a GEMM call whose last round is balanced
-# runs a second launch of the half-tile instantiation
-GEMM_KERNEL = {(0, 0, 0): "fp8k::gemm_tn_kernel<0, 0, false, 0, false>",
-               (1, 0, 0): "fp8k::gemm_tn_kernel<1, 0, false, 0, false>",
-               (1, 0, 1): "fp8k::gemm_tn_kernel<1, 0, false, 1, false>"}
+# edge tiles, layout set, half tiles, gate/up with the SwiGLU statistic); a
+# GEMM call whose last round is balanced runs a second launch of the half-tile
+# instantiation
+GEMM_KERNEL = {(0, 0, 0): "fp8k::gemm_tn_kernel<0, 0, false, 0, false, false>",
+               (1, 0, 0): "fp8k::gemm_tn_kernel<1, 0, false, 0, false, false>",
+               (1, 0, 1): "fp8k::gemm_tn_kernel<1, 0, false, 1, false, false>",
+               "gate_up": "fp8k::gemm_tn_kernel<0, 0, false, 0, false, true>"}
 
 
 def tail_launch(probs, kmajor, cus):
@@ -100,11 +102,15 @@ WORKLOADS = {
 }
 
 
-def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False):
+def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False, fused_absmax_h=False):
     """Inputs and the ordered list of calls of one layer step of a configuration.
 
     The step starts by clearing its buffer of per-tensor absmax statistics (one
-    fill); every absmax then accumulates into its own slot.
+    fill); every absmax then accumulates into its own slot.  With
+    fused_absmax_h the SwiGLU statistic absmax_h comes out of the gate/up GEMM's
+    epilogue (fp8_gemm_fwd_swiglu_absmax) and fp8_swiglu_requant runs without a
+    reduction pass; by default (measured faster in this step) fp8_swiglu_requant
+    takes it in its own pass.
     Forward: absmax + quantise of X and W, FP8 GEMM, for QKV, O and gate/up;
     the fused SwiGLU requant of the gate/up output feeds the down linear.
     Backward: absmax + e5m2 quantise of dY, then dgrad and wgrad in one launch.
@@ -150,9 +156,14 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False):
                       meta={"rows": rows, "cols": cols, "fmt": fmt}))
         return quantize_op(tag, x, rows, cols, fmt, am, want_qt) + (am,)
 
-    def gemm_fwd_op(tag, xq, wq, ix, iw, y, L):
-        ops.append(Op(f"gemm_fwd {tag}", lambda: fp8.gemm_fwd(xq, wq, ix, iw, y), "gemm", 2 * M * L.N * L.K,
-                      gemm_fwd_kernel, {"probs": [(M, L.N, L.K, E4M3)]}))
+    def gemm_fwd_op(tag, xq, wq, ix, iw, y, L, am_h=None):
+        if am_h is None:
+            fn = lambda: fp8.gemm_fwd(xq, wq, ix, iw, y)
+        else:
+            fn = lambda: fp8.gemm_fwd_swiglu_absmax(xq, wq, ix, iw, am_h, out=y)
+        ops.append(Op(f"gemm_fwd {tag}", fn, "gemm", 2 * M * L.N * L.K,
+                      GEMM_KERNEL["gate_up"] if am_h is not None else gemm_fwd_kernel,
+                      {"probs": [(M, L.N, L.K, E4M3)], "kmajor": True, "swiglu_absmax": am_h is not None}))
 
     def swiglu_op(tag, gu, am_h, compute, want_hqt, F):
         hq, hqt, inv_h = u8(M, F), (u8(F, M) if want_hqt else None), f32()
@@ -164,6 +175,9 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False):
 
     # ---- forward
     fwd = {}
+    # absmax_h of the SwiGLU output: from the gate/up GEMM's epilogue (one slot of
+    # the step's statistics), or from the SwiGLU kernel's own reduction pass
+    am_h = stats[63:64] if fused_absmax_h else f32()
     for name in ("qkv", "o", "gate_up"):
         li, L = lin[name]
         x = workloads.draw_x(cfg, li).to(dev)
@@ -173,14 +187,13 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False):
         xq, xqt, inv_x, am_x = quant_ops(f"X_{name}", x, M, L.K, E4M3, keep_xt)
         wq, wqt, inv_w, _ = quant_ops(f"W_{name}", w, L.N, L.K, E4M3, not mn)
         y = bf(M, L.N)
-        gemm_fwd_op(name, xq, wq, inv_x, inv_w, y, L)
+        gemm_fwd_op(name, xq, wq, inv_x, inv_w, y, L, am_h if (name == "gate_up" and fused_absmax_h) else None)
         fwd[name] = {"x": x, "am_x": am_x, "xq": xq, "wq": wq, "xqt": xqt, "wqt": wqt, "inv_x": inv_x,
                      "inv_w": inv_w, "y": y}
     # SwiGLU requantisation of the gate/up output feeds the down linear
     li, L = lin["down"]
     F = L.K
-    am_h = f32()
-    hq, hqt, inv_h = swiglu_op("fwd", fwd["gate_up"]["y"], am_h, True, not mn and not recompute, F)
+    hq, hqt, inv_h = swiglu_op("fwd", fwd["gate_up"]["y"], am_h, not fused_absmax_h, not mn and not recompute, F)
     w = workloads.draw_w(cfg, li).to(dev)
     bufs["down"] = (None, w)
     wq, wqt, inv_w, _ = quant_ops("W_down", w, L.N, L.K, E4M3, not mn)
@@ -231,7 +244,7 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False):
             fn = (lambda dyq=dyq, dyqt=dyqt, wqt=f["wqt"], xqt=f["xqt"], a=inv_dy, b=f["inv_w"], c=f["inv_x"],
                   dx=dx, dw=dw: fp8.gemm_backward(dyq, dyqt, E5M2, wqt, xqt, a, b, c, dx, dw))
         ops.append(Op(f"gemm_backward {name}", fn, "gemm", 4 * M * L.N * L.K, GEMM_KERNEL[(1, 0, 1 if mn else 0)],
-                      {"probs": [(M, L.K, L.N, E5M2), (L.N, L.K, M, E5M2)]}))
+                      {"probs": [(M, L.K, L.N, E5M2), (L.N, L.K, M, E5M2)], "kmajor": not mn}))
     return ops, bufs
 
 
@@ -307,6 +320,13 @@ def cpu_baseline(ops, gemm_rows):
                 fixed = max(times[0] - per_row * gemm_rows, 0.0)
                 est += fixed + per_row * P
                 gemm_flop += 2.0 * P * Q * R
+                if m.get("swiglu_absmax"):
+                    # the SwiGLU statistic this GEMM also produces: the oracle's reduction pass
+                    r, f = sample_rows(P, Q)
+                    gu = rng.integers(0, 0x4080, (r, Q), dtype=np.uint16)
+                    t = time.perf_counter()
+                    oracle.swiglu_requant(gu, want_hq=False)
+                    est += (time.perf_counter() - t) * f
         elif op.kind == "absmax":
             r, f = sample_rows(m["rows"], m["cols"])
             x = rng.integers(0, 0x3F80, (r, m["cols"]), dtype=np.uint16)
@@ -403,6 +423,9 @@ def main():
     ap.add_argument("--cpu-gemm-rows", type=int, default=96)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="c3",
                     help="c3: 7B-class layer (the headline); c4: 14B-class; c5: 32B-class with MLP recomputation")
+    ap.add_argument("--fused-swiglu-absmax", action="store_true",
+                    help="take the SwiGLU statistic in the gate/up GEMM's epilogue (fp8_gemm_fwd_swiglu_absmax) "
+                         "instead of fp8_swiglu_requant's own reduction pass")
     ap.add_argument("--swiglu-backward", action="store_true",
                     help="chain the MLP backward: down dgrad -> fused SwiGLU backward -> gate/up backward "
                          "(instead of a drawn gate/up output gradient)")
@@ -422,7 +445,8 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     cfg = workloads.CONFIGS[args.workload]
-    ops, bufs = build_step(fp8, dev, args.workload, args.layout, args.swiglu_backward)
+    ops, bufs = build_step(fp8, dev, args.workload, args.layout, args.swiglu_backward,
+                           args.fused_swiglu_absmax)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         run_step(ops)
@@ -445,7 +469,7 @@ def main():
         d["flop"] += op.work
         d["time"] += float(np.mean(ts))
         d["launches"] += 1
-        d["tail_launches"] += tail_launch(op.meta["probs"], op.kernel.endswith(", 0, false>"), cus)
+        d["tail_launches"] += tail_launch(op.meta["probs"], op.meta["kmajor"], cus)
     dom_name, dom = max(by_kernel.items(), key=lambda kv: kv[1]["time"])
     achieved = dom["flop"] / dom["time"] / 1e12
     gemm_time = sum(d["time"] for d in by_kernel.values())
@@ -492,6 +516,8 @@ def main():
                    "backward_operands": "untransposed (MN-major)" if args.layout == "mn" else "transposed copies",
                    "mlp_backward": "chained through the fused SwiGLU backward" if args.swiglu_backward
                    else "drawn output gradients",
+                   "swiglu_absmax": ("gate/up GEMM epilogue" if args.fused_swiglu_absmax
+                                     else "separate reduction pass"),
                    "gemm_gflop_per_step": round(gemm_flop / 1e9, 1)},
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "gemm_only_tflops": round(gemm_flop / gemm_time / 1e12, 1),

@@ -33,6 +33,7 @@ _SIGS = {
     "fp8_swiglu_requant": (_i32, [_vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp]),
     "fp8_swiglu_backward": (_i32, [_vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp8_gemm_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "fp8_gemm_fwd_swiglu_absmax": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_gemm_dgrad": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_gemm_wgrad": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_gemm_backward": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
@@ -216,6 +217,23 @@ def gemm_fwd(xq, wq, inv_sx, inv_sw, out=None) -> torch.Tensor:
     out = _out_bf16(out, (M, N), xq.device)
     _check("fp8_gemm_fwd", _lib.fp8_gemm_fwd(_ptr(xq), _ptr(wq), _ptr(inv_sx), _ptr(inv_sw), _ptr(out),
                                              M, N, K, _stream(xq)))
+    return out
+
+
+def gemm_fwd_swiglu_absmax(xq, wq, inv_sx, inv_sw, absmax_h, out=None) -> torch.Tensor:
+    """gu[M, 2F] = X[M, K] . Wgu[2F, K]^T (e4m3), bf16 out, and absmax_h (fp32 [1],
+    holding +0 or an earlier result) updated to max(absmax_h, max |silu(gate) * up|)."""
+    _dev_tensor(xq, "xq", torch.uint8)
+    _dev_tensor(wq, "wq", torch.uint8)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or N % 2:
+        raise ValueError("xq is [M, K] and wq must be [2F, K]")
+    absmax_h = _scalar(absmax_h, "absmax_h", xq.device)
+    out = _out_bf16(out, (M, N), xq.device)
+    _check("fp8_gemm_fwd_swiglu_absmax",
+           _lib.fp8_gemm_fwd_swiglu_absmax(_ptr(xq), _ptr(wq), _ptr(inv_sx), _ptr(inv_sw), _ptr(out), _ptr(absmax_h),
+                                          M, N // 2, K, _stream(xq)))
     return out
 
 

@@ -253,6 +253,28 @@ fp8_status fp8_gemm_fwd(const uint8_t* xq, const uint8_t* wq, const float* inv_s
     return FP8_OK;
 }
 
+fp8_status fp8_gemm_fwd_swiglu_absmax(const uint8_t* xq, const uint8_t* wq, const float* inv_sx,
+                                      const float* inv_sw, void* gu, float* absmax_h, int64_t M, int64_t F,
+                                      int64_t K, hipStream_t stream)
+{
+    t_last_error.clear();
+    const char* name = "fp8_gemm_fwd_swiglu_absmax";
+    if (!absmax_h) return fail(FP8_ERR_INVALID, "fp8_gemm_fwd_swiglu_absmax: null absmax_h");
+    if (F <= 0 || F > ((int64_t)1 << 29)) return fail(FP8_ERR_INVALID, "fp8_gemm_fwd_swiglu_absmax: bad F");
+    fp8_status st = gemm_common(name, xq, FP8_E4M3, wq, inv_sx, inv_sw, gu, M, 2 * F, K, stream);
+    if (st != FP8_OK) return st;
+    const Range r[] = {{xq, M * K}, {wq, 2 * F * K}, {inv_sx, 4}, {inv_sw, 4}, {gu, 2 * M * 2 * F}};
+    for (const Range& x : r)
+        if (overlap(x.p, x.n, absmax_h, 4))
+            return fail(FP8_ERR_INVALID, "fp8_gemm_fwd_swiglu_absmax: absmax_h overlaps another buffer");
+    if (!aligned(absmax_h, 4)) return fail(FP8_ERR_UNSUPPORTED, "fp8_gemm_fwd_swiglu_absmax: misaligned absmax_h");
+    if (F % 128 || M < 256)
+        return fail(FP8_ERR_UNSUPPORTED, "fp8_gemm_fwd_swiglu_absmax: needs F % 128 == 0 and M >= 256");
+    hipError_t e = fp8k::launch_gemm_gate_up(xq, wq, inv_sx, inv_sw, gu, absmax_h, M, F, K, stream);
+    if (e != hipSuccess) return fail_hip(name, e);
+    return FP8_OK;
+}
+
 fp8_status fp8_gemm_dgrad(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_t* wqt, const float* inv_sdy,
                           const float* inv_sw, void* dx, int64_t M, int64_t N, int64_t K, hipStream_t stream)
 {

@@ -10,6 +10,14 @@ namespace fp8k {
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// The SwiGLU s_g table (swiglu.hip): fp32 [2 signs][kSiluEHi - kSiluELo + 1 bf16
+// exponents][128 mantissas], entry = s_g of the bf16 gate value with that sign,
+// exponent and mantissa.  silu_table() builds it on the current device the
+// first time and returns its device address.
+constexpr int kSiluELo = 100;
+constexpr int kSiluEHi = 133;
+hipError_t silu_table(const float** table, hipStream_t stream);
+
 hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, bool accumulate, hipStream_t stream);
 
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, const float* absmax,
@@ -30,6 +38,12 @@ hipError_t launch_swiglu_backward(const void* gu, const void* dh, int64_t M, int
 hipError_t launch_gemm_tn(const uint8_t* A, int fmt_a, int la, const uint8_t* B, int fmt_b, int lb,
                           const float* inv_a, const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R,
                           hipStream_t stream);
+
+// Gate/up forward product with the SwiGLU statistic: out[M, 2F] = A[M, K] . B[2F, K]^T
+// as launch_gemm_tn (e4m3 x e4m3, K-major), and *absmax_h = max(*absmax_h, max |h|)
+// over h = s_g(gate) * up of the bf16 outputs (bit-pattern max).  M >= 256, F % 128 == 0.
+hipError_t launch_gemm_gate_up(const uint8_t* A, const uint8_t* B, const float* inv_a, const float* inv_b, void* out,
+                               float* absmax_h, int64_t M, int64_t F, int64_t K, hipStream_t stream);
 
 // Two independent products of the same operand formats (and the same B layout) in one launch.
 hipError_t launch_gemm_tn_pair(const uint8_t* A0, int la0, const uint8_t* B0, int lb0, const float* ia0,

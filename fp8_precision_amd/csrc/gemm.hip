@@ -442,6 +442,8 @@ struct GemmProblem {
 
 struct GemmGroup {
     GemmProblem p[kMaxGroup];
+    uint32_t* absmax_h;   // gate/up launches: the SwiGLU absmax accumulator (fp32 bits)
+    const float* table;   // gate/up launches: the s_g table (bf16 exponents kGuELo - 3 .. 133)
     int count;
     int total_tiles;
     int full_units;       // units 0 .. full_units - 1 are the tiles of the same index; unit
@@ -465,7 +467,7 @@ struct Work {
 // Output tile of a virtual tile id: the problem it falls in, then a grouped
 // raster order within it (kGroupM tile rows per group, column-major within a
 // group), so consecutive ids share A and B panels.
-template <bool EDGE, bool HALF>
+template <bool EDGE, bool HALF, bool GU>
 __device__ __forceinline__ Work work_of(const GemmGroup& g, int u)
 {
     int v = u, hh = -1;
@@ -493,13 +495,13 @@ __device__ __forceinline__ Work work_of(const GemmGroup& g, int u)
     const int gm = min(pr.tiles_m - first_m, kGroupM);
     const int in_group = lv - group * group_size;
     w.ms = (first_m + in_group % gm) * kBM;
-    w.ns = (in_group / gm) * kBN;
+    w.ns = (in_group / gm) * (GU ? kBN / 2 : kBN);   // gate/up: 128 gate columns per tile
     if (HALF) w.ms += hh * (kBM / 2);
     // A last partial tile is shifted back to end at the matrix edge (P, Q >= 256),
     // recomputing rows / columns of its neighbour that it then does not store
     // (a half tile that starts past the last row stores nothing).
     w.m0 = EDGE ? w.ms : min(w.ms, w.P - (HALF ? kBM / 2 : kBM));
-    w.n0 = EDGE ? w.ns : min(w.ns, w.Q - kBN);
+    w.n0 = (EDGE || GU) ? w.ns : min(w.ns, w.Q - kBN);
     return w;
 }
 
@@ -516,14 +518,24 @@ constexpr int kSetKK = 0;       // (K, K)
 constexpr int kSetMN = 1;       // (K, MN) and (MN, MN)
 
 // Set up the sources of tile w and issue its first two stages.
-template <bool EDGE, int SET, bool HALF>
+template <bool EDGE, int SET, bool HALF, bool GU>
 __device__ __forceinline__ void start_tile(Sources& src, const Work& w, uint32_t lds_addr, int wave, int lane)
 {
+    // Gate/up launches (B = [gate rows | up rows], F = Q / 2 each): wave w fills
+    // B tile rows 64 w .. 64 w + 63 from the gate panel (w even) or the up panel
+    // (w odd) at gate column n0 + 64 (w / 2), so the B blocks 0..3 of a wave are
+    // gate columns and blocks 4..7 the up columns of the same outputs.
+    const int b_origin = GU ? w.n0 + (wave >> 1) * 64 + (wave & 1) * (w.Q >> 1) - wave * 64 : w.n0;
     if (HALF) {
         set_op<kKMajor>(src.a, w.A, w.m0, w.P, w.R, wave, lane, 32);
-        set_op<kKMajor>(src.b, w.B, w.n0, w.Q, w.R, wave, lane);
+        set_op<kKMajor>(src.b, w.B, b_origin, w.Q, w.R, wave, lane);
         issue_half_stage(src, lds_addr, 0, wave);
         issue_half_stage(src, lds_addr + kStage, min(1, w.KT - 1), wave);
+    } else if (GU) {
+        set_op<kKMajor>(src.a, w.A, w.m0, w.P, w.R, wave, lane);
+        set_op<kKMajor>(src.b, w.B, b_origin, w.Q, w.R, wave, lane);
+        issue_stage<false, kKMajor, kKMajor>(src, lds_addr, 0, wave);
+        issue_stage<false, kKMajor, kKMajor>(src, lds_addr + kStage, min(1, w.KT - 1), wave);
     } else if (SET == kSetKK) {
         set_sources<kKMajor, kKMajor>(src, w, wave, lane);
         issue_stage<EDGE, kKMajor, kKMajor>(src, lds_addr, 0, wave);
@@ -586,6 +598,113 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[8][8], const Work& don
     }
 }
 
+// ---- gate/up launches: the SwiGLU statistic in the epilogue ("LLMQ", section
+// 3.1: the forward computes absmax_h, which recomputation later reuses; here it
+// comes out of the GEMM that produces [gate | up], saving the separate read
+// pass over that output).  h = RN32(s_g * u) on the bf16 values as stored, with
+// s_g = RN32(g / RN32(1 + RN32(e^-g))) read from the SwiGLU kernels' table for
+// the bf16 exponents kGuELo .. kSiluEHi (31 KB, held in the LDS that other
+// launches use to stage output rows) and exact rules elsewhere:
+//   exponent < kGuELo: s_g = g / 2 (1 + e^-g rounds to exactly 2 there; the
+//                      table's entries for exponents kSiluELo .. kGuELo - 1
+//                      are g / 2 as well);
+//   |g| >= 128 (and inf, NaN): s_g = g for g > 0, -0 for finite g < 0, NaN for
+//                      -inf and negative NaN.
+constexpr int kGuELo = 103;
+constexpr int kGuHalf = (kSiluEHi - kGuELo + 1) * 128;           // entries per sign
+constexpr int kSiluHalf = (kSiluEHi - kSiluELo + 1) * 128;       // source table, entries per sign
+static_assert(2 * kGuHalf * 4 + 4 <= 4 * kEpiWave, "table and the maximum slot must fit the epilogue LDS");
+
+__device__ __forceinline__ void load_gu_table(float* dst, const float* src, int tid)
+{
+    constexpr int kV = kGuHalf / 4;                                // float4 per sign
+    for (int k = tid; k < 2 * kV; k += 256) {
+        const int sgn = k >= kV;
+        const int r = k - sgn * kV;
+        reinterpret_cast<float4*>(dst)[k] =
+            reinterpret_cast<const float4*>(src)[(sgn * kSiluHalf + (kGuELo - kSiluELo) * 128) / 4 + r];
+    }
+}
+
+// Early returns, not selects: almost every gate value of real data is in the
+// table's range, so the rule branches are skipped by whole waves (a branch-free
+// form that evaluates every rule for every value measured slower).
+__device__ __forceinline__ float s_g_of(const float* tbl, uint32_t b)
+{
+    const float g = __uint_as_float(b << 16);
+    const uint32_t t = (b & 0x7FFFu) - (uint32_t)(kGuELo * 128);
+    const uint32_t neg = b >> 15;
+    const bool in_table = t < (uint32_t)kGuHalf;
+    const float tv = tbl[in_table ? t + neg * kGuHalf : 0u];
+    if (in_table) return tv;
+    if ((int32_t)t < 0) return g * 0.5f;
+    if (!neg) return g;
+    return ((b & 0x7F80u) == 0x7F80u) ? __builtin_nanf("") : -0.0f;
+}
+
+// Epilogue of a gate/up tile: B blocks 0..3 of the wave are gate columns
+// n0 + 64 wn + 16 j .., blocks 4..7 the up columns F + (the same); each lane
+// holds 4 consecutive columns of one row.  Stores go straight from registers
+// (8 bytes per lane; swapping halves between lanes for 16-byte stores measured
+// no faster); every computed row enters the maximum of |h| bit patterns
+// (rows that a shifted-back tile recomputes but does not store are its
+// neighbour's values).  The wave's maximum goes into the workgroup's LDS slot
+// `wg_max`; global memory sees one atomic per workgroup, after the last tile
+// (an atomic per tile would sit in the vector-memory counter in front of the
+// next tile's loads and stall its first wait, and a register held across the
+// K loop would be spilled).
+template <bool HALF>
+__device__ __forceinline__ void epilogue_gu(const v4f (&acc)[8][8], const Work& done, float d, const float* tbl,
+                                            uint32_t* wg_max, int wm, int wn, int lane)
+{
+    uint32_t mx = 0;
+    const int F = done.Q >> 1;
+    // the lane number recomputed here (volatile, so it is not hoisted), so that
+    // no per-lane term is held live across the persistent loop (where it would
+    // be spilled)
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const int r16 = ln & 15, q4 = ln >> 4;
+#pragma unroll
+    for (int i = 0; i < (HALF ? 4 : 8); ++i) {
+        const int m = done.m0 + wm * (HALF ? 64 : 128) + i * 16 + r16;
+        uint16_t* row = done.out + (size_t)m * done.Q;
+        const bool st = m >= done.ms;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f32x2 g01 = {acc[i][j][0] * d, acc[i][j][1] * d};
+            const f32x2 g23 = {acc[i][j][2] * d, acc[i][j][3] * d};
+            const f32x2 u01 = {acc[i][j + 4][0] * d, acc[i][j + 4][1] * d};
+            const f32x2 u23 = {acc[i][j + 4][2] * d, acc[i][j + 4][3] * d};
+            uint2 go, uo;
+            go.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(g01, bf16x2));
+            go.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(g23, bf16x2));
+            uo.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(u01, bf16x2));
+            uo.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(u23, bf16x2));
+            const int c = done.n0 + wn * 64 + j * 16 + 4 * q4;
+            if (st) {
+                *reinterpret_cast<uint2*>(row + c) = go;
+                *reinterpret_cast<uint2*>(row + F + c) = uo;
+            }
+            const uint32_t gb[4] = {go.x & 0xFFFFu, go.x >> 16, go.y & 0xFFFFu, go.y >> 16};
+            const uint32_t ub[4] = {uo.x << 16, uo.x & 0xFFFF0000u, uo.y << 16, uo.y & 0xFFFF0000u};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float h = s_g_of(tbl, gb[e]) * __uint_as_float(ub[e]);
+                const uint32_t a = __float_as_uint(h) & 0x7FFFFFFFu;
+                mx = mx > a ? mx : a;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);    // one row block at a time: bounded register use
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)mx, off, 64);
+        mx = mx > o ? mx : o;
+    }
+    if (ln == 0) atomicMax(wg_max, mx);
+}
+
 // Persistent kernel: one workgroup per CU walks the units v = slot, slot + G,
 // slot + 2G, ... (a unit is a tile, or a half tile in a balanced last round)
 // where slot renumbers the workgroups XCD-major (workgroups are dealt
@@ -593,7 +712,7 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[8][8], const Work& don
 // CUs of one XCD work on 32 consecutive units of the raster order.  While a
 // tile's epilogue stores run, the first two stages of the next tile are
 // already loading.
-template <int FA, int FB, bool EDGE, int SET, bool HALF>
+template <int FA, int FB, bool EDGE, int SET, bool HALF, bool GU>
 __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
@@ -621,8 +740,15 @@ __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
     // be a full vmcnt(0), i.e. a wait for the next tile's whole prefetch.
     const float d0 = g.p[0].inv_a[0] * g.p[0].inv_b[0];
     const float d1 = g.count > 1 ? g.p[1].inv_a[0] * g.p[1].inv_b[0] : d0;
-    Work w = work_of<EDGE, HALF>(g, v);
-    start_tile<EDGE, SET, HALF>(src, w, lds_addr, wave, lane);
+    Work w = work_of<EDGE, HALF, GU>(g, v);
+    start_tile<EDGE, SET, HALF, GU>(src, w, lds_addr, wave, lane);
+    // gate/up: the s_g table and, after it, the workgroup's running max of |h|
+    // (both read only after the first K loop's barriers)
+    uint32_t* wg_max = reinterpret_cast<uint32_t*>(epi + 2 * kGuHalf * 4);
+    if (GU) {
+        load_gu_table(reinterpret_cast<float*>(epi), g.table, tid);
+        if (tid == 0) *wg_max = 0;
+    }
     for (;;) {
         if (HALF)
             tile_mainloop_half<FA, FB>(acc, bq, alo, ahi, src, lds, lds_addr, w.KT, wave, wm, wn, lane);
@@ -642,16 +768,23 @@ __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
         const int next = v + G;
         if (next < g.units) {
             v = next;
-            w = work_of<EDGE, HALF>(g, v);
-            start_tile<EDGE, SET, HALF>(src, w, lds_addr, wave, lane);
+            w = work_of<EDGE, HALF, GU>(g, v);
+            start_tile<EDGE, SET, HALF, GU>(src, w, lds_addr, wave, lane);
         }
 
-        epilogue<HALF>(acc, done, d, epi, wave, wm, wn, lane);
+        if (GU)
+            epilogue_gu<HALF>(acc, done, d, reinterpret_cast<const float*>(epi), wg_max, wm, wn, lane);
+        else
+            epilogue<HALF>(acc, done, d, epi, wave, wm, wn, lane);
         // The loop-top wait (vmcnt <= 16, or 12 for a half tile) then proves the
         // next tile's first stage has landed: if one of its loads were pending,
         // the 16 (12) later loads of the second stage would be too (loads
         // complete in order), whatever the interleaved stores do.
         if (next >= g.units) break;
+    }
+    if (GU) {
+        __syncthreads();
+        if (tid == 0) atomicMax(g.absmax_h, *wg_max);
     }
 }
 
@@ -675,7 +808,7 @@ static GemmProblem make_problem(const uint8_t* A, int la, const uint8_t* B, int 
     return p;
 }
 
-template <int FA, int FB, int SET>
+template <int FA, int FB, int SET, bool GU = false>
 static hipError_t launch_group(GemmGroup g, hipStream_t stream)
 {
     bool edge = false;
@@ -687,11 +820,13 @@ static hipError_t launch_group(GemmGroup g, hipStream_t stream)
     }
     g.total_tiles = total;
     const int cus = device_cu_count();
-    if (edge) {
-        g.full_units = g.units = total;
-        g.first_unit = 0;
-        gemm_tn_kernel<FA, FB, true, SET, false><<<total < cus ? total : cus, 256, 0, stream>>>(g);
-        return hipGetLastError();
+    if constexpr (!GU) {
+        if (edge) {
+            g.full_units = g.units = total;
+            g.first_unit = 0;
+            gemm_tn_kernel<FA, FB, true, SET, false, false><<<total < cus ? total : cus, 256, 0, stream>>>(g);
+            return hipGetLastError();
+        }
     }
     // Balance the last round: when the tiles past the last full round of the
     // persistent grid fill at most half of it, each becomes two half tiles (a
@@ -703,12 +838,12 @@ static hipError_t launch_group(GemmGroup g, hipStream_t stream)
     g.units = g.full_units;
     g.first_unit = 0;
     if (g.full_units > 0)
-        gemm_tn_kernel<FA, FB, false, SET, false><<<g.full_units < cus ? g.full_units : cus, 256, 0, stream>>>(g);
+        gemm_tn_kernel<FA, FB, false, SET, false, GU><<<g.full_units < cus ? g.full_units : cus, 256, 0, stream>>>(g);
     if constexpr (SET == kSetKK) {
         if (split) {
             g.first_unit = g.full_units;
             g.units = total + tail;
-            gemm_tn_kernel<FA, FB, false, SET, true><<<2 * tail, 256, 0, stream>>>(g);
+            gemm_tn_kernel<FA, FB, false, SET, true, GU><<<2 * tail, 256, 0, stream>>>(g);
         }
     }
     return hipGetLastError();
@@ -733,11 +868,25 @@ static hipError_t dispatch(int fmt_a, int fmt_b, const GemmGroup& g, hipStream_t
     return launch_group<1, 0, kSetMN>(g, stream);
 }
 
+hipError_t launch_gemm_gate_up(const uint8_t* A, const uint8_t* B, const float* inv_a, const float* inv_b, void* out,
+                               float* absmax_h, int64_t M, int64_t F, int64_t K, hipStream_t stream)
+{
+    GemmGroup g{};
+    hipError_t e = silu_table(&g.table, stream);
+    if (e != hipSuccess) return e;
+    g.absmax_h = reinterpret_cast<uint32_t*>(absmax_h);
+    g.p[0] = make_problem(A, kKMajor, B, kKMajor, inv_a, inv_b, out, M, 2 * F, K);
+    g.p[0].tiles_n = (int)(F / (kBN / 2));        // a tile: 128 gate and the matching 128 up columns
+    g.p[1] = g.p[0];
+    g.count = 1;
+    return launch_group<0, 0, kSetKK, true>(g, stream);
+}
+
 hipError_t launch_gemm_tn(const uint8_t* A, int fmt_a, int la, const uint8_t* B, int fmt_b, int lb,
                           const float* inv_a, const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R,
                           hipStream_t stream)
 {
-    GemmGroup g;
+    GemmGroup g{};
     g.p[0] = make_problem(A, la, B, lb, inv_a, inv_b, out, P, Q, R);
     g.p[1] = g.p[0];
     g.count = 1;
@@ -749,7 +898,7 @@ hipError_t launch_gemm_tn_pair(const uint8_t* A0, int la0, const uint8_t* B0, in
                                int la1, const uint8_t* B1, int lb1, const float* ia1, const float* ib1, void* out1,
                                int64_t P1, int64_t Q1, int64_t R1, int fmt_a, int fmt_b, hipStream_t stream)
 {
-    GemmGroup g;
+    GemmGroup g{};
     GemmProblem p0 = make_problem(A0, la0, B0, lb0, ia0, ib0, out0, P0, Q0, R0);
     GemmProblem p1 = make_problem(A1, la1, B1, lb1, ia1, ib1, out1, P1, Q1, R1);
     // longest reduction first: the first round then starts the longest tiles

@@ -33,8 +33,8 @@
 
 namespace fp8k {
 
-constexpr int kELo = 100;                     // bf16 biased exponent range of the table
-constexpr int kEHi = 133;                     // |g| in [2^-27, 128)
+constexpr int kELo = kSiluELo;                // bf16 biased exponent range of the table
+constexpr int kEHi = kSiluEHi;                // |g| in [2^-27, 128)
 constexpr int kNE = kEHi - kELo + 1;          // 34
 constexpr int kHalf = kNE * 128;              // entries per sign
 constexpr int kTable = 2 * kHalf;             // 8704 entries
@@ -80,6 +80,25 @@ static hipError_t ensure_silu_table(hipStream_t stream)
     e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return e;
     g_init_done[dev] = true;
+    return hipSuccess;
+}
+
+hipError_t silu_table(const float** table, hipStream_t stream)
+{
+    static const float* addr[64];
+    hipError_t e = ensure_silu_table(stream);
+    if (e != hipSuccess) return e;
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_init_mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_silu_table));
+        if (e != hipSuccess) return e;
+        addr[dev] = static_cast<const float*>(p);
+    }
+    *table = addr[dev];
     return hipSuccess;
 }
 

@@ -200,6 +200,30 @@ fp8_status fp8_gemm_wgrad(const uint8_t* dyqt, fp8_fmt dy_fmt, const uint8_t* xq
                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
+ * The gate/up forward GEMM with the SwiGLU statistic taken in its epilogue
+ * (LLMQ summary, section 3.1: the forward produces the absmax of the SwiGLU
+ * output that quantisation -- and, later, recomputation -- uses; computing it
+ * where [gate | up] is produced saves the separate read pass over that
+ * tensor):
+ *   gu[M, 2F] = X[M, K] . Wgu[2F, K]^T   exactly as fp8_gemm_fwd (same bytes)
+ *   *absmax_h = max(*absmax_h, max over m, j of |h[m, j]|),
+ *   h[m, j]   = RN32(s_g(gu[m, j]) * gu[m, F + j])  on the bf16 values of gu,
+ * with s_g and the NaN / infinity rules of fp8_swiglu_requant, so the result
+ * equals that call's computed absmax_h on this gu.  Like fp8_absmax_accumulate,
+ * absmax_h is read and updated: it must start as +0 (or an earlier result);
+ * fp8_swiglu_requant then runs with compute_absmax = 0 on it.
+ *
+ *   xq   e4m3 [M, K],  wq  e4m3 [2F, K]: gate rows 0 .. F-1, up rows F .. 2F-1
+ *   inv_sx, inv_sw   fp32 inverse scales of the operands
+ *   gu   bf16 [M, 2F] (written),  absmax_h  one fp32 (read and updated)
+ * Constraints: those of fp8_gemm_fwd with N = 2F, plus F % 128 == 0 and
+ * M >= 256.  No buffer may overlap gu or absmax_h.
+ */
+fp8_status fp8_gemm_fwd_swiglu_absmax(const uint8_t* xq, const uint8_t* wq, const float* inv_sx,
+                                      const float* inv_sw, void* gu, float* absmax_h, int64_t M,
+                                      int64_t F, int64_t K, hipStream_t stream);
+
+/*
  * Both backward products of one linear in a single launch: dgrad
  * dX[M, K] = dY[M, N] . W[N, K] and wgrad dW[N, K] = dY[M, N]^T . X[M, K] are
  * independent, so one persistent launch runs both tile sets, longest

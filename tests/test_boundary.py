@@ -30,12 +30,13 @@ def lib():
     lib.fp8_quantize.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp]
     lib.fp8_swiglu_requant.argtypes = [vp, i64, i64, vp, i32, vp, vp, vp, vp]
     lib.fp8_gemm_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.fp8_gemm_fwd_swiglu_absmax.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.fp8_gemm_dgrad.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.fp8_gemm_wgrad.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.fp8_last_error.restype = ctypes.c_char_p
     lib.fp8_status_string.restype = ctypes.c_char_p
     for f in ("fp8_absmax", "fp8_absmax_accumulate", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd",
-              "fp8_gemm_dgrad", "fp8_gemm_wgrad"):
+              "fp8_gemm_fwd_swiglu_absmax", "fp8_gemm_dgrad", "fp8_gemm_wgrad"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -43,7 +44,7 @@ def lib():
 def test_header_declares_the_hot_path():
     names = declared_functions()
     for want in ("fp8_absmax", "fp8_absmax_accumulate", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd", "fp8_gemm_dgrad",
-                 "fp8_gemm_wgrad", "fp8_gemm_backward", "fp8_gemm_dgrad_mn", "fp8_gemm_wgrad_mn",
+                 "fp8_gemm_wgrad", "fp8_gemm_fwd_swiglu_absmax", "fp8_gemm_backward", "fp8_gemm_dgrad_mn", "fp8_gemm_wgrad_mn",
                  "fp8_gemm_backward_mn", "fp8_swiglu_backward", "fp8_status_string", "fp8_last_error"):
         assert want in names
 
@@ -231,3 +232,17 @@ def test_python_binding_imports_and_fails_loudly_without_gpu():
     x = torch.zeros(16, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         fp8.absmax(x)   # a CPU tensor is refused: there is no CPU path
+
+
+def test_gemm_fwd_swiglu_absmax_validation(lib):
+    f = lib.fp8_gemm_fwd_swiglu_absmax
+    # (xq, wq, inv_sx, inv_sw, gu, absmax_h, M, F, K)
+    assert f(A16, B16, C16, C16 + 16, D16, None, 256, 128, 128, None) == INVALID       # null absmax_h
+    assert f(None, B16, C16, C16 + 16, D16, E16, 256, 128, 128, None) == INVALID
+    assert f(A16, B16, C16, C16 + 16, D16, E16, 256, 0, 128, None) == INVALID          # F = 0
+    assert f(A16, B16, C16, C16 + 16, D16, D16 + 64, 256, 128, 128, None) == INVALID   # absmax_h inside gu
+    assert b"overlaps" in lib.fp8_last_error()
+    assert f(A16, B16, C16, C16 + 16, D16, E16, 256, 64, 128, None) == UNSUPPORTED     # F % 128
+    assert f(A16, B16, C16, C16 + 16, D16, E16, 128, 128, 128, None) == UNSUPPORTED    # M < 256
+    assert f(A16, B16, C16, C16 + 16, D16, E16, 256, 128, 100, None) == UNSUPPORTED    # K % 128
+    assert f(A16, B16, C16, C16 + 16, D16, E16 + 2, 256, 128, 128, None) == UNSUPPORTED  # misaligned absmax_h

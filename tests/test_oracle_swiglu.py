@@ -123,3 +123,24 @@ def test_requant_with_stale_statistic_saturates(orc):
     big = np.abs(h) * orc.scale(stale, E4M3)[0] > 448
     assert big.any()
     assert np.all((hq[big] & 0x7F) == 0x7E)
+
+
+def test_tiny_gate_rule_holds_through_exponent_102(orc):
+    """For every bf16 gate value whose biased exponent is at most 102 (both
+    signs, every mantissa, zeros and subnormals), 1 + e^-g rounds to exactly 2
+    and s_g = g / 2; at exponent 103 it does not for every value.  The GEMM
+    epilogue that takes the SwiGLU statistic relies on the first fact to hold
+    its s_g table in 31 KB (exponents 103..133).  Why: for |g| < 2^-24,
+    RN32(e^-g) is 1 (g < 0, or 0 <= g <= 2^-25) or 1 - 2^-24 (2^-25 < g <
+    2^-24); 1 + 1 = 2, and 2 - 2^-24 is the midpoint of 2 - 2^-23 and 2,
+    which rounds to the even 2.  The check below is exhaustive."""
+    bits = np.array([(s << 15) | (e << 7) | m for s in (0, 1) for e in range(0, 103) for m in range(128)],
+                    np.uint16)
+    one = np.full_like(bits, 0x3F80)                                  # u = 1: h = s_g
+    h = orc.swiglu_h(np.concatenate([bits, one])[None, :]).ravel()
+    g = (bits.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(h.view(np.uint32), (g * np.float32(0.5)).astype(np.float32).view(np.uint32))
+    b103 = np.array([(s << 15) | (103 << 7) | m for s in (0, 1) for m in range(128)], np.uint16)
+    h103 = orc.swiglu_h(np.concatenate([b103, np.full_like(b103, 0x3F80)])[None, :]).ravel()
+    g103 = (b103.astype(np.uint32) << 16).view(np.float32)
+    assert not np.array_equal(h103.view(np.uint32), (g103 * np.float32(0.5)).view(np.uint32))
