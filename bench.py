@@ -68,10 +68,12 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_traffic_layer7b.txt")
 GEMM_SOURCE = os.path.join(ROOT, "fp8_precision_amd", "csrc", "gemm.hip")
 
 
-def measured_traffic(kernel):
-    """HBM bytes per dispatch of `kernel` from the committed rocprofv3 PMC summary
-    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy of known size), or
-    None when the summary is missing or the GEMM source changed since it was taken."""
+def measured_traffic(kernel, tail_fraction=0.0):
+    """HBM bytes per call of `kernel` from the committed rocprofv3 PMC summary
+    (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by a plain copy of known
+    size; a call adds its half-tile launch's bytes, `tail_fraction` of the calls
+    have one), or None when the summary is missing or the GEMM source changed
+    since it was taken."""
     import hashlib
     try:
         line = next(l for l in open(TRAFFIC_SUMMARY) if l.startswith("TRAFFIC_JSON "))
@@ -81,7 +83,14 @@ def measured_traffic(kernel):
     if hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()[:16] != data["gemm_source_sha256_16"]:
         return None
     b = data["per_dispatch_bytes"].get(kernel)
-    return None if b is None else int(b)
+    if b is None:
+        return None
+    if tail_fraction > 0:
+        t = data["per_dispatch_bytes"].get(kernel.replace(", false, false>", ", true, false>"))
+        if t is None:
+            return None
+        b += tail_fraction * t
+    return int(b)
 
 
 class Op:
@@ -523,7 +532,7 @@ def main():
         "gemm_only_tflops": round(gemm_flop / gemm_time / 1e12, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(dom_name),
+                     "traffic": measured_traffic(dom_name, dom["tail_launches"] / dom["launches"]),
                      "kernel": dom_name, "launches_per_step": dom["launches"],
                      "tail_launches_per_step": dom["tail_launches"],
                      "peak_at_sustained_clock": (round(FP8_PEAK_TFLOPS * clock["gfx_mhz_median"] / 2400.0, 1)
