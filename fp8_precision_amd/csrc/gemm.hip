@@ -567,6 +567,9 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[8][8], const Work& don
     asm volatile("" : "+v"(ln));
     const int r16 = ln & 15, q4 = ln >> 4;
     const int wrow = done.m0 + wm * (HALF ? 64 : 128);
+    // a tile that is not shifted back and lies inside the matrix stores every output it computes
+    const bool full = done.ms == done.m0 && done.ns == done.n0 && done.m0 + (HALF ? kBM / 2 : kBM) <= done.P &&
+                      done.n0 + kBN <= done.Q;
 #pragma unroll
     for (int c2 = 0; c2 < (HALF ? 2 : 4); ++c2) {        // chunk: A blocks 2*c2, 2*c2+1 (32 rows)
 #pragma unroll
@@ -585,15 +588,40 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[8][8], const Work& don
                 *reinterpret_cast<uint2*>(ew + row * 256 + chunk * 16 + (q4 & 1) * 8) = o;
             }
         }
+        if (full) {
+            // every row and column is the tile's own: the chunk's 8 LDS reads go
+            // out together, then 8 stores through a uniform base plus a per-lane
+            // offset (no per-store bounds test, branch or 64-bit address math)
+            static_assert(kEpiRows == 32, "8 row groups of 4 per chunk");
+            auto rd = [&](int it) {
+                const int rr = it * 4 + q4;
+                return *reinterpret_cast<const uint4*>(ew + rr * 256 + ((r16 ^ (rr & 15)) * 16));
+            };
+            const uint4 o0 = rd(0), o1 = rd(1), o2 = rd(2), o3 = rd(3), o4 = rd(4), o5 = rd(5), o6 = rd(6),
+                        o7 = rd(7);
+            uint8_t* base = reinterpret_cast<uint8_t*>(done.out) +
+                            ((size_t)(wrow + c2 * 32) * done.Q + done.n0 + wn * 128) * 2;
+            const uint32_t loff = (uint32_t)(q4 * done.Q + r16 * 8) * 2u;
+            const size_t rs = (size_t)8 * done.Q;                 // 4 rows, in bytes
+            *reinterpret_cast<uint4*>(base + loff) = o0;
+            *reinterpret_cast<uint4*>(base + rs + loff) = o1;
+            *reinterpret_cast<uint4*>(base + 2 * rs + loff) = o2;
+            *reinterpret_cast<uint4*>(base + 3 * rs + loff) = o3;
+            *reinterpret_cast<uint4*>(base + 4 * rs + loff) = o4;
+            *reinterpret_cast<uint4*>(base + 5 * rs + loff) = o5;
+            *reinterpret_cast<uint4*>(base + 6 * rs + loff) = o6;
+            *reinterpret_cast<uint4*>(base + 7 * rs + loff) = o7;
+        } else {
 #pragma unroll
-        for (int it = 0; it < kEpiRows / 4; ++it) {
-            const int rr = it * 4 + q4;                           // row within the chunk
-            const int c = r16;                                    // logical 16-byte chunk
-            const uint4 o = *reinterpret_cast<const uint4*>(ew + rr * 256 + ((c ^ (rr & 15)) * 16));
-            const int m = wrow + c2 * 32 + rr;
-            const int n = done.n0 + wn * 128 + c * 8;
-            if (m >= done.ms && m < done.P && n >= done.ns && n < done.Q)
-                *reinterpret_cast<uint4*>(done.out + (size_t)m * done.Q + n) = o;
+            for (int it = 0; it < kEpiRows / 4; ++it) {
+                const int rr = it * 4 + q4;                       // row within the chunk
+                const int c = r16;                                // logical 16-byte chunk
+                const uint4 o = *reinterpret_cast<const uint4*>(ew + rr * 256 + ((c ^ (rr & 15)) * 16));
+                const int m = wrow + c2 * 32 + rr;
+                const int n = done.n0 + wn * 128 + c * 8;
+                if (m >= done.ms && m < done.P && n >= done.ns && n < done.Q)
+                    *reinterpret_cast<uint4*>(done.out + (size_t)m * done.Q + n) = o;
+            }
         }
     }
 }
