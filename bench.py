@@ -177,8 +177,9 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False, fused
     def swiglu_op(tag, gu, am_h, compute, want_hqt, F):
         hq, hqt, inv_h = u8(M, F), (u8(F, M) if want_hqt else None), f32()
         work = (4 * M * F if compute else 0) + (6 if want_hqt else 5) * M * F
+        # a computed statistic accumulates into its (step-cleared) slot: no reset launch
         ops.append(Op(f"swiglu_requant {tag}", lambda: fp8.swiglu_requant(gu, am_h, compute, hq=hq, hqt=hqt,
-                                                                         inv_scale_h=inv_h),
+                                                                         inv_scale_h=inv_h, accumulate=compute),
                       "swiglu", work, meta={"M": M, "F": F, "qt": want_hqt, "compute": compute}))
         return hq, hqt, inv_h
 
@@ -186,7 +187,7 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False, fused
     fwd = {}
     # absmax_h of the SwiGLU output: from the gate/up GEMM's epilogue (one slot of
     # the step's statistics), or from the SwiGLU kernel's own reduction pass
-    am_h = stats[63:64] if fused_absmax_h else f32()
+    am_h = stats[63:64]
     for name in ("qkv", "o", "gate_up"):
         li, L = lin[name]
         x = workloads.draw_x(cfg, li).to(dev)

@@ -137,12 +137,14 @@ def quantize(x: torch.Tensor, fmt: int, amax: torch.Tensor, want_q: bool = True,
 
 def swiglu_requant(gu: torch.Tensor, absmax_h: torch.Tensor | None = None, compute_absmax: bool = True,
                    want_hq: bool = True, want_hqt: bool = False, hq: torch.Tensor | None = None,
-                   hqt: torch.Tensor | None = None, inv_scale_h: torch.Tensor | None = None):
+                   hqt: torch.Tensor | None = None, inv_scale_h: torch.Tensor | None = None,
+                   accumulate: bool = False):
     """SwiGLU of gu = [gate | up] (bf16 [M, 2F]) requantised to e4m3.
 
-    compute_absmax True: absmax_h is computed (forward).  False: the given
-    retained absmax_h is used and no reduction runs (recomputation).
-    Returns (hq or None, hqt or None, absmax_h, inv_scale_h).
+    compute_absmax True: absmax_h is computed (forward); with ``accumulate``
+    it is max(absmax_h, max |h|) (absmax_h given, holding +0 or an earlier
+    result).  False: the given retained absmax_h is used and no reduction runs
+    (recomputation).  Returns (hq or None, hqt or None, absmax_h, inv_scale_h).
     """
     _dev_tensor(gu, "gu", torch.bfloat16)
     if gu.dim() != 2 or gu.shape[1] % 2:
@@ -150,6 +152,8 @@ def swiglu_requant(gu: torch.Tensor, absmax_h: torch.Tensor | None = None, compu
     M, F = gu.shape[0], gu.shape[1] // 2
     if not compute_absmax and absmax_h is None:
         raise ValueError("recomputation needs the retained absmax_h")
+    if accumulate and (absmax_h is None or not compute_absmax):
+        raise ValueError("accumulate needs compute_absmax and the absmax_h to update")
     absmax_h = _scalar(absmax_h, "absmax_h", gu.device)
     if want_hq and hq is None:
         hq = torch.empty((M, F), dtype=torch.uint8, device=gu.device)
@@ -161,7 +165,8 @@ def swiglu_requant(gu: torch.Tensor, absmax_h: torch.Tensor | None = None, compu
             if t.numel() != M * F:
                 raise ValueError(f"{n} has the wrong size")
     inv_scale_h = _scalar(inv_scale_h, "inv_scale_h", gu.device)
-    _check("fp8_swiglu_requant", _lib.fp8_swiglu_requant(_ptr(gu), M, F, _ptr(absmax_h), 1 if compute_absmax else 0,
+    _check("fp8_swiglu_requant", _lib.fp8_swiglu_requant(_ptr(gu), M, F, _ptr(absmax_h),
+                                                         (2 if accumulate else 1) if compute_absmax else 0,
                                                          _ptr(hq), _ptr(hqt), _ptr(inv_scale_h), _stream(gu)))
     return hq, hqt, absmax_h, inv_scale_h
 

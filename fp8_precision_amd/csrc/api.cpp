@@ -157,8 +157,8 @@ fp8_status fp8_swiglu_requant(const void* gu, int64_t M, int64_t F, float* absma
     t_last_error.clear();
     if (!gu || !absmax_h) return fail(FP8_ERR_INVALID, "fp8_swiglu_requant: null gu or absmax_h");
     if (!hq && !hqt) return fail(FP8_ERR_INVALID, "fp8_swiglu_requant: at least one of hq, hqt is required");
-    if (compute_absmax != 0 && compute_absmax != 1)
-        return fail(FP8_ERR_INVALID, "fp8_swiglu_requant: compute_absmax must be 0 or 1");
+    if (compute_absmax < 0 || compute_absmax > 2)
+        return fail(FP8_ERR_INVALID, "fp8_swiglu_requant: compute_absmax must be 0, 1 or 2");
     if (!mul_ok(M, 2 * F, kMaxElems) || F <= 0) return fail(FP8_ERR_INVALID, "fp8_swiglu_requant: bad shape");
     const int64_t n = M * F;
     const Range r[] = {{gu, 4 * n}, {absmax_h, 4}, {hq, hq ? n : 0}, {hqt, hqt ? n : 0},

@@ -335,7 +335,8 @@ hipError_t launch_swiglu_requant(const void* gu, int64_t M, int64_t F, float* ab
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     if (compute_absmax) {
-        zero_u32_kernel_sw<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax_h));
+        // 1: reset first; 2: accumulate into the caller's (cleared) statistic
+        if (compute_absmax == 1) zero_u32_kernel_sw<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax_h));
         // one 1024-thread block per CU: one atomic per CU, the table copied once per CU
         int64_t ablocks = (items + 15) / 16;
         if (ablocks > device_cu_count()) ablocks = device_cu_count();

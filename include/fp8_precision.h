@@ -123,6 +123,10 @@ fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt,
  *   h = RN32(RN32(g / RN32(1 + RN32(e^-g))) * u)       (silu(g) * u, fp32)
  *   hq[i, j] = encode_e4m3(RN32(h * s_h)),  s_h = 448 / absmax_h
  * compute_absmax = 1 (forward): absmax_h = max |h| is computed and written.
+ * compute_absmax = 2 (forward, running statistic): as 1 without resetting
+ *   *absmax_h first: it becomes max(*absmax_h, max |h|) (bit-pattern max; the
+ *   caller clears it, e.g. with the other statistics of a step -- see
+ *   fp8_absmax_accumulate), and quantisation uses that value.
  * compute_absmax = 0 (recomputation): *absmax_h is the retained statistic and
  * is only read; no global reduction runs, and the bytes equal the forward's
  * for the same gu (LLMQ summary, section 3.1: keeping absmax statistics
@@ -130,7 +134,7 @@ fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt,
  * nonlinearity during recomputation).
  *
  *   gu           bf16 [M, 2F]
- *   absmax_h     fp32 scalar (written when compute_absmax = 1, read otherwise)
+ *   absmax_h     fp32 scalar (written when compute_absmax = 1, updated when 2, read when 0)
  *   hq           u8 [M, F] or NULL
  *   hqt          u8 [F, M] (transpose of hq) or NULL (at least one of hq, hqt)
  *   inv_scale_h  fp32 scalar out (RN32(1 / s_h)) or NULL

@@ -112,7 +112,8 @@ def test_swiglu_validation(lib):
     assert s(None, 16, 16, C16, 1, B16, None, None, None) == INVALID
     assert s(A16, 16, 16, None, 1, B16, None, None, None) == INVALID
     assert s(A16, 16, 16, C16, 1, None, None, None, None) == INVALID
-    assert s(A16, 16, 16, C16, 2, B16, None, None, None) == INVALID
+    assert s(A16, 16, 16, C16, 3, B16, None, None, None) == INVALID          # compute_absmax in {0, 1, 2}
+    assert s(A16, 16, 16, C16, -1, B16, None, None, None) == INVALID
     assert s(A16, 0, 16, C16, 1, B16, None, None, None) == INVALID
     assert s(A16, 16, 0, C16, 1, B16, None, None, None) == INVALID
     assert s(A16, 16, 16, A16 + 4, 1, B16, None, None, None) == INVALID       # absmax inside gu

@@ -115,3 +115,30 @@ def test_nonfinite_gates(fp8, orc):
         hq_r, _, am_r, _ = orc.swiglu_requant(rows)
         assert_f32_equal(scalar(am), am_r, name)
         assert_codes_equal(u8(hq), hq_r, E4M3, name)
+
+
+@pytest.mark.parametrize("M,F", [(16, 48), (512, 11008)])
+def test_forward_accumulating_statistic(fp8, orc, M, F):
+    """compute_absmax = 2: the statistic accumulates into a caller-cleared slot
+    (no reset launch); from +0 the bytes equal the resetting forward's, a larger
+    prior value stays and sets the scale (saturating like a stale statistic)."""
+    say("swiglu accumulate", M, F)
+    gu = dev(workloads.draw(13, M + F, (M, 2 * F), 2.0))
+    hq, hqt, am, inv = fp8.swiglu_requant(gu, compute_absmax=True, want_hq=True, want_hqt=True)
+    slots = torch.zeros(4, dtype=torch.float32, device="cuda")
+    hq2, hqt2, am2, inv2 = fp8.swiglu_requant(gu, absmax_h=slots[1:2], compute_absmax=True, accumulate=True,
+                                             want_hq=True, want_hqt=True)
+    torch.cuda.synchronize()
+    assert torch.equal(am2.view(torch.int32), am.view(torch.int32))
+    assert torch.equal(hq2, hq) and torch.equal(hqt2, hqt)
+    assert torch.equal(inv2.view(torch.int32), inv.view(torch.int32))
+    assert float(slots[0]) == 0.0 and float(slots[2]) == 0.0
+    big = am * 8
+    prior = big.clone()
+    hq3, _, am3, _ = fp8.swiglu_requant(gu, absmax_h=prior, compute_absmax=True, accumulate=True, want_hq=True)
+    torch.cuda.synchronize()
+    assert torch.equal(am3.view(torch.int32), big.view(torch.int32))
+    hq3_r, _, _, _ = orc.swiglu_requant(u16(gu.cpu()), absmax_h=scalar(big))
+    assert_codes_equal(u8(hq3), hq3_r, E4M3, "larger prior")
+    with pytest.raises(ValueError):
+        fp8.swiglu_requant(gu, compute_absmax=True, accumulate=True)
