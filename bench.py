@@ -120,7 +120,8 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False, fused
     epilogue (fp8_gemm_fwd_swiglu_absmax) and fp8_swiglu_requant runs without a
     reduction pass; by default (measured faster in this step) fp8_swiglu_requant
     takes it in its own pass.
-    Forward: absmax + quantise of X and W, FP8 GEMM, for QKV, O and gate/up;
+    Forward: the absmax of X and W (one launch), quantise of X and W, FP8 GEMM,
+    for QKV, O and gate/up;
     the fused SwiGLU requant of the gate/up output feeds the down linear.
     Backward: absmax + e5m2 quantise of dY, then dgrad and wgrad in one launch.
     With recomputation (c5) the backward first re-quantises the retained bf16
@@ -158,6 +159,17 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False, fused
                                                                    "qt": want_qt}))
         return q, qt, inv
 
+    def quant_pair_ops(name, x, w, L, want_xt, want_wt):
+        """A linear's input and weight: both statistics in one launch, then their quantisations."""
+        kx, kw = next(slots), next(slots)
+        am_x, am_w = stats[kx:kx + 1], stats[kw:kw + 1]
+        ops.append(Op(f"absmax X_{name}+W_{name}", lambda: fp8.absmax_accumulate_many([x, w], [am_x, am_w]),
+                      "absmax", 2 * (M + L.N) * L.K,
+                      meta={"shapes": [(M, L.K), (L.N, L.K)]}))
+        xq, xqt, inv_x = quantize_op(f"X_{name}", x, M, L.K, E4M3, am_x, want_xt)
+        wq, wqt, inv_w = quantize_op(f"W_{name}", w, L.N, L.K, E4M3, am_w, want_wt)
+        return xq, xqt, inv_x, am_x, wq, wqt, inv_w
+
     def quant_ops(tag, x, rows, cols, fmt, want_qt):
         k = next(slots)
         am = stats[k:k + 1]
@@ -194,8 +206,14 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False, fused
         w = workloads.draw_w(cfg, li).to(dev)
         bufs[name] = (x, w)
         keep_xt = not mn and not (recompute and name == "gate_up")
-        xq, xqt, inv_x, am_x = quant_ops(f"X_{name}", x, M, L.K, E4M3, keep_xt)
-        wq, wqt, inv_w, _ = quant_ops(f"W_{name}", w, L.N, L.K, E4M3, not mn)
+        if name != "gate_up":
+            xq, xqt, inv_x, am_x, wq, wqt, inv_w = quant_pair_ops(name, x, w, L, keep_xt, not mn)
+        else:
+            # the gate/up weight is streamed non-temporally: a shared launch would
+            # stream X too and cost its quantisation the Infinity Cache, for no
+            # shorter statistics pass (measured)
+            xq, xqt, inv_x, am_x = quant_ops(f"X_{name}", x, M, L.K, E4M3, keep_xt)
+            wq, wqt, inv_w, _ = quant_ops(f"W_{name}", w, L.N, L.K, E4M3, not mn)
         y = bf(M, L.N)
         gemm_fwd_op(name, xq, wq, inv_x, inv_w, y, L, am_h if (name == "gate_up" and fused_absmax_h) else None)
         fwd[name] = {"x": x, "am_x": am_x, "xq": xq, "wq": wq, "xqt": xqt, "wqt": wqt, "inv_x": inv_x,
@@ -338,11 +356,12 @@ def cpu_baseline(ops, gemm_rows):
                     oracle.swiglu_requant(gu, want_hq=False)
                     est += (time.perf_counter() - t) * f
         elif op.kind == "absmax":
-            r, f = sample_rows(m["rows"], m["cols"])
-            x = rng.integers(0, 0x3F80, (r, m["cols"]), dtype=np.uint16)
-            t = time.perf_counter()
-            oracle.absmax_bf16(x)
-            est += (time.perf_counter() - t) * f
+            for rows, cols in m.get("shapes", [(m.get("rows"), m.get("cols"))]):
+                r, f = sample_rows(rows, cols)
+                x = rng.integers(0, 0x3F80, (r, cols), dtype=np.uint16)
+                t = time.perf_counter()
+                oracle.absmax_bf16(x)
+                est += (time.perf_counter() - t) * f
         elif op.kind == "quantize":
             r, f = sample_rows(m["rows"], m["cols"])
             x = rng.integers(0, 0x3F80, (r, m["cols"]), dtype=np.uint16)

@@ -29,6 +29,7 @@ _SIGS = {
     "fp8_last_error": (ctypes.c_char_p, []),
     "fp8_absmax": (_i32, [_vp, _i64, _vp, _vp]),
     "fp8_absmax_accumulate": (_i32, [_vp, _i64, _vp, _vp]),
+    "fp8_absmax_accumulate_many": (_i32, [ctypes.c_int, _vp, _vp, _vp, _vp]),
     "fp8_quantize": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp8_swiglu_requant": (_i32, [_vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp]),
     "fp8_swiglu_backward": (_i32, [_vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -104,6 +105,23 @@ def absmax(x: torch.Tensor, out: torch.Tensor | None = None, accumulate: bool = 
     out = _scalar(out, "out", x.device)
     _check("fp8_absmax", _lib.fp8_absmax(_ptr(x), x.numel(), _ptr(out), _stream(x)))
     return out
+
+
+def absmax_accumulate_many(xs, outs) -> None:
+    """Running absmax of up to 4 bf16 tensors in one launch: outs[i] (fp32 [1]
+    device tensors, +0 or an earlier result) become max(outs[i], max |xs[i]|)."""
+    if len(xs) != len(outs) or not 1 <= len(xs) <= 4:
+        raise ValueError("1 to 4 tensors, one output each")
+    for x in xs:
+        _dev_tensor(x, "x", torch.bfloat16)
+    outs = [_scalar(o, "out", xs[0].device) for o in outs]
+    k = len(xs)
+    xp = (ctypes.c_void_p * k)(*[_ptr(x) for x in xs])
+    ns = (ctypes.c_int64 * k)(*[x.numel() for x in xs])
+    op = (ctypes.c_void_p * k)(*[_ptr(o) for o in outs])
+    _check("fp8_absmax_accumulate_many",
+           _lib.fp8_absmax_accumulate_many(k, ctypes.cast(xp, _vp), ctypes.cast(ns, _vp), ctypes.cast(op, _vp),
+                                           _stream(xs[0])))
 
 
 def quantize(x: torch.Tensor, fmt: int, amax: torch.Tensor, want_q: bool = True, want_qt: bool = False,

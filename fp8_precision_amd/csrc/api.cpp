@@ -128,6 +128,31 @@ fp8_status fp8_absmax_accumulate(const void* x, int64_t n, float* absmax, hipStr
     return absmax_common("fp8_absmax_accumulate", x, n, absmax, true, stream);
 }
 
+fp8_status fp8_absmax_accumulate_many(int count, const void* const* x, const int64_t* n, float* const* absmax,
+                                      hipStream_t stream)
+{
+    t_last_error.clear();
+    const char* name = "fp8_absmax_accumulate_many";
+    if (!x || !n || !absmax) return fail(FP8_ERR_INVALID, "fp8_absmax_accumulate_many: null array");
+    if (count < 1 || count > fp8k::kMaxAbsTensors)
+        return fail(FP8_ERR_INVALID, "fp8_absmax_accumulate_many: count must be in [1, 4]");
+    for (int i = 0; i < count; ++i) {
+        if (!x[i] || !absmax[i]) return fail(FP8_ERR_INVALID, "fp8_absmax_accumulate_many: null pointer");
+        if (n[i] <= 0 || n[i] > kMaxElems)
+            return fail(FP8_ERR_INVALID, "fp8_absmax_accumulate_many: every n must be in [1, 2^40]");
+        if (!aligned(x[i], 16) || !aligned(absmax[i], 4))
+            return fail(FP8_ERR_UNSUPPORTED, "fp8_absmax_accumulate_many: x 16-byte and absmax 4-byte aligned");
+    }
+    // an accumulator may be shared (the max is order-free), but none may lie inside an input
+    for (int i = 0; i < count; ++i)
+        for (int j = 0; j < count; ++j)
+            if (overlap(x[j], 2 * n[j], absmax[i], 4))
+                return fail(FP8_ERR_INVALID, "fp8_absmax_accumulate_many: an absmax overlaps an input");
+    hipError_t e = fp8k::launch_absmax_many(count, x, n, absmax, stream);
+    if (e != hipSuccess) return fail_hip(name, e);
+    return FP8_OK;
+}
+
 fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt, const float* absmax,
                         uint8_t* q, uint8_t* qt, float* scale, float* inv_scale, hipStream_t stream)
 {

@@ -20,6 +20,11 @@ hipError_t silu_table(const float** table, hipStream_t stream);
 
 hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, bool accumulate, hipStream_t stream);
 
+// Running absmax of up to kMaxAbsTensors tensors in one launch (no reset).
+constexpr int kMaxAbsTensors = 4;
+hipError_t launch_absmax_many(int count, const void* const* x, const int64_t* n, float* const* absmax,
+                              hipStream_t stream);
+
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, const float* absmax,
                            uint8_t* q, uint8_t* qt, float* scale, float* inv_scale,
                            hipStream_t stream);

@@ -60,14 +60,16 @@ __device__ __forceinline__ u32x4 ld16(const u32x4* p)
     return *p;
 }
 
+// The pass of block `blk` of `nblk` over one tensor (nvec 16-byte vectors and
+// ntail trailing elements, which block 0 takes).
 template <bool NT>
-__global__ void __launch_bounds__(kAbsThreads) absmax_bf16_kernel(const u32x4* __restrict__ x, int64_t nvec,
-                                                                  const uint16_t* __restrict__ tail, int ntail,
-                                                                  uint32_t* __restrict__ out)
+__device__ __forceinline__ void absmax_body(const u32x4* __restrict__ x, int64_t nvec,
+                                            const uint16_t* __restrict__ tail, int ntail, uint32_t* __restrict__ out,
+                                            int blk, int nblk)
 {
     us2 m = {0, 0};
-    const int64_t stride = (int64_t)gridDim.x * kAbsThreads;
-    int64_t i = (int64_t)blockIdx.x * kAbsThreads + threadIdx.x;
+    const int64_t stride = (int64_t)nblk * kAbsThreads;
+    int64_t i = (int64_t)blk * kAbsThreads + threadIdx.x;
     for (; i + 7 * stride < nvec; i += 8 * stride) {
         u32x4 v[8];
 #pragma unroll
@@ -77,11 +79,78 @@ __global__ void __launch_bounds__(kAbsThreads) absmax_bf16_kernel(const u32x4* _
     }
     for (; i < nvec; i += stride) m = absmax_acc4(m, ld16<NT>(x + i));
     uint32_t r = m.x > m.y ? m.x : m.y;
-    if (blockIdx.x == 0 && (int)threadIdx.x < ntail) {
+    if (blk == 0 && (int)threadIdx.x < ntail) {
         uint32_t t = tail[threadIdx.x] & 0x7FFFu;
         r = r > t ? r : t;
     }
     block_max_to_global(r << 16, out);
+}
+
+template <bool NT>
+__global__ void __launch_bounds__(kAbsThreads) absmax_bf16_kernel(const u32x4* __restrict__ x, int64_t nvec,
+                                                                  const uint16_t* __restrict__ tail, int ntail,
+                                                                  uint32_t* __restrict__ out)
+{
+    absmax_body<NT>(x, nvec, tail, ntail, out, blockIdx.x, gridDim.x);
+}
+
+// Several tensors in one launch: blocks first[i] .. first[i + 1] - 1 take tensor i.
+struct AbsmaxGroup {
+    const u32x4* x[kMaxAbsTensors];
+    const uint16_t* tail[kMaxAbsTensors];
+    uint32_t* out[kMaxAbsTensors];
+    int64_t nvec[kMaxAbsTensors];
+    int ntail[kMaxAbsTensors];
+    int nt[kMaxAbsTensors];                   // non-temporal loads for this tensor
+    int first[kMaxAbsTensors + 1];
+    int count;
+};
+
+__global__ void __launch_bounds__(kAbsThreads) absmax_many_kernel(const AbsmaxGroup g)
+{
+    int i = 0;
+    while (i + 1 < g.count && (int)blockIdx.x >= g.first[i + 1]) ++i;
+    const int blk = blockIdx.x - g.first[i], nblk = g.first[i + 1] - g.first[i];
+    if (g.nt[i])
+        absmax_body<true>(g.x[i], g.nvec[i], g.tail[i], g.ntail[i], g.out[i], blk, nblk);
+    else
+        absmax_body<false>(g.x[i], g.nvec[i], g.tail[i], g.ntail[i], g.out[i], blk, nblk);
+}
+
+hipError_t launch_absmax_many(int count, const void* const* x, const int64_t* n, float* const* absmax,
+                              hipStream_t stream)
+{
+    AbsmaxGroup g;
+    g.count = count;
+    // one load form for the whole launch, chosen by its largest tensor (non-temporal
+    // when that one is 64 MiB or more): blocks of mixed forms ran slower together
+    // than the two tensors did in launches of their own (measured)
+    int64_t total = 0, largest = 0;
+    for (int i = 0; i < count; ++i) {
+        total += n[i];
+        largest = n[i] > largest ? n[i] : largest;
+    }
+    const bool nt = 2 * largest >= kAbsStreamBytes;
+    // blocks in proportion to the sizes (at least one per tensor), about one per CU
+    // in all, each at most what its tensor fills (8 vectors per lane)
+    const int64_t cus = device_cu_count();
+    g.first[0] = 0;
+    for (int i = 0; i < count; ++i) {
+        const int64_t nvec = n[i] / 8;
+        g.x[i] = reinterpret_cast<const u32x4*>(x[i]);
+        g.nvec[i] = nvec;
+        g.ntail[i] = (int)(n[i] - nvec * 8);
+        g.tail[i] = reinterpret_cast<const uint16_t*>(x[i]) + nvec * 8;
+        g.out[i] = reinterpret_cast<uint32_t*>(absmax[i]);
+        g.nt[i] = nt;
+        int64_t b = (cus * n[i] + total - 1) / total;
+        const int64_t need = (nvec + 8 * kAbsThreads - 1) / (8 * kAbsThreads);
+        if (b > need) b = need;
+        if (b < 1) b = 1;
+        g.first[i + 1] = g.first[i] + (int)b;
+    }
+    absmax_many_kernel<<<(unsigned)g.first[count], kAbsThreads, 0, stream>>>(g);
+    return hipGetLastError();
 }
 
 hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, bool accumulate, hipStream_t stream)

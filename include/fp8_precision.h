@@ -95,6 +95,24 @@ fp8_status fp8_absmax(const void* x, int64_t n, float* absmax, hipStream_t strea
 fp8_status fp8_absmax_accumulate(const void* x, int64_t n, float* absmax, hipStream_t stream);
 
 /*
+ * The running absmax of several tensors in one launch: for i < count,
+ *   *absmax[i] = max(*absmax[i], max over j < n[i] of |x[i][j]|)
+ * exactly as count calls of fp8_absmax_accumulate (the same statistic as
+ * fp8_absmax, per tensor), but sharing the fixed cost of a launch -- for the
+ * tensors that are ready together, such as a linear's input and weight
+ * (LLMQ summary, section 1: every operand of an FP8 product gets its own
+ * just-in-time statistic).
+ *
+ *   count      1 .. 4
+ *   x, n       host arrays of count bf16 device pointers (16-byte aligned) and
+ *              element counts (>= 1); read during the call
+ *   absmax     host array of count device fp32 pointers (read and updated; each
+ *              starts as +0 or an earlier result; two may be the same slot)
+ */
+fp8_status fp8_absmax_accumulate_many(int count, const void* const* x, const int64_t* n,
+                                      float* const* absmax, hipStream_t stream);
+
+/*
  * Quantise a bf16 [rows, cols] tensor with the scale of its absmax:
  *   s      = fp8_max / absmax  (one fp32 division; 1 when absmax == 0; held at
  *            FLT_MAX if the division overflows)

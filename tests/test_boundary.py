@@ -27,6 +27,7 @@ def lib():
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     lib.fp8_absmax.argtypes = [vp, i64, vp, vp]
     lib.fp8_absmax_accumulate.argtypes = [vp, i64, vp, vp]
+    lib.fp8_absmax_accumulate_many.argtypes = [i32, vp, vp, vp, vp]
     lib.fp8_quantize.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp]
     lib.fp8_swiglu_requant.argtypes = [vp, i64, i64, vp, i32, vp, vp, vp, vp]
     lib.fp8_gemm_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
@@ -35,7 +36,7 @@ def lib():
     lib.fp8_gemm_wgrad.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.fp8_last_error.restype = ctypes.c_char_p
     lib.fp8_status_string.restype = ctypes.c_char_p
-    for f in ("fp8_absmax", "fp8_absmax_accumulate", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd",
+    for f in ("fp8_absmax", "fp8_absmax_accumulate", "fp8_absmax_accumulate_many", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd",
               "fp8_gemm_fwd_swiglu_absmax", "fp8_gemm_dgrad", "fp8_gemm_wgrad"):
         getattr(lib, f).restype = i32
     return lib
@@ -43,7 +44,7 @@ def lib():
 
 def test_header_declares_the_hot_path():
     names = declared_functions()
-    for want in ("fp8_absmax", "fp8_absmax_accumulate", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd", "fp8_gemm_dgrad",
+    for want in ("fp8_absmax", "fp8_absmax_accumulate", "fp8_absmax_accumulate_many", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd", "fp8_gemm_dgrad",
                  "fp8_gemm_wgrad", "fp8_gemm_fwd_swiglu_absmax", "fp8_gemm_backward", "fp8_gemm_dgrad_mn", "fp8_gemm_wgrad_mn",
                  "fp8_gemm_backward_mn", "fp8_swiglu_backward", "fp8_status_string", "fp8_last_error"):
         assert want in names
@@ -247,3 +248,26 @@ def test_gemm_fwd_swiglu_absmax_validation(lib):
     assert f(A16, B16, C16, C16 + 16, D16, E16, 128, 128, 128, None) == UNSUPPORTED    # M < 256
     assert f(A16, B16, C16, C16 + 16, D16, E16, 256, 128, 100, None) == UNSUPPORTED    # K % 128
     assert f(A16, B16, C16, C16 + 16, D16, E16 + 2, 256, 128, 128, None) == UNSUPPORTED  # misaligned absmax_h
+
+
+def test_absmax_accumulate_many_validation(lib):
+    f = lib.fp8_absmax_accumulate_many
+
+    def call(xs, ns, outs, count=None):
+        k = len(xs)
+        xa = (ctypes.c_void_p * k)(*xs)
+        na = (ctypes.c_int64 * k)(*ns)
+        oa = (ctypes.c_void_p * k)(*outs)
+        return f(k if count is None else count, ctypes.cast(xa, ctypes.c_void_p), ctypes.cast(na, ctypes.c_void_p),
+                 ctypes.cast(oa, ctypes.c_void_p), None)
+
+    assert f(1, None, None, None, None) == INVALID
+    assert call([A16, B16], [16, 16], [C16, C16 + 4], count=0) == INVALID
+    assert call([A16, B16], [16, 16], [C16, C16 + 4], count=5) == INVALID
+    assert call([A16, None], [16, 16], [C16, C16 + 4]) == INVALID
+    assert call([A16, B16], [16, 16], [C16, None]) == INVALID
+    assert call([A16, B16], [16, 0], [C16, C16 + 4]) == INVALID
+    assert call([A16, B16], [16, 16], [C16, B16 + 8]) == INVALID        # an accumulator inside an input
+    assert b"overlaps" in lib.fp8_last_error()
+    assert call([A16, B16 + 2], [16, 16], [C16, C16 + 4]) == UNSUPPORTED
+    assert call([A16, B16], [16, 16], [C16, C16 + 2]) == UNSUPPORTED

@@ -99,6 +99,37 @@ def test_absmax_accumulate(fp8, orc):
         fp8.absmax(xd, accumulate=True)
 
 
+def test_absmax_accumulate_many(fp8, orc):
+    """Up to 4 tensors in one launch: each slot gets its tensor's absmax (sizes
+    from a ragged 37 elements to 48 M, below and above the non-temporal
+    threshold), a shared slot gets the maximum of its tensors, priors stay."""
+    say("absmax many")
+    sizes = [37, 1 << 20, 3 * (1 << 24) + 5, 4096 * 4096]
+    xs, bits = [], []
+    for k, n in enumerate(sizes):
+        b = u16(workloads.draw(102, k, (n,), 1.0 + k))
+        b[(n * 2) // 3] = 0xC300 + 16 * k                     # a planted negative maximum per tensor
+        bits.append(b)
+        xs.append(dev(torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16)))
+    want = [orc.absmax_bf16(b) for b in bits]
+    slots = torch.zeros(6, dtype=torch.float32, device="cuda")
+    fp8.absmax_accumulate_many(xs, [slots[i:i + 1] for i in range(4)])
+    torch.cuda.synchronize()
+    got = slots.cpu().numpy()
+    for i in range(4):
+        assert_f32_equal(got[i], want[i], f"tensor {i} (n={sizes[i]})")
+    assert got[4] == 0 and got[5] == 0
+    # two tensors into one slot, a larger prior in another
+    s2 = torch.tensor([0.0, 1e30], dtype=torch.float32, device="cuda")
+    fp8.absmax_accumulate_many([xs[0], xs[3], xs[1]], [s2[0:1], s2[0:1], s2[1:2]])
+    torch.cuda.synchronize()
+    r = s2.cpu().numpy()
+    assert_f32_equal(r[0], max(np.float32(want[0]), np.float32(want[3])), "shared slot")
+    assert_f32_equal(r[1], np.float32(1e30), "larger prior")
+    with pytest.raises(ValueError):
+        fp8.absmax_accumulate_many(xs + xs[:1], [slots[i:i + 1] for i in range(5)])
+
+
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
 def test_scale_every_bf16_absmax(fp8, orc, fmt):
     say("scale sweep", fmt)
