@@ -110,6 +110,24 @@ __device__ __forceinline__ void load_table_to_lds(float* lds)
     __syncthreads();
 }
 
+// The forward statistic's LDS table: |s_g| (only magnitudes are needed), the
+// positive half at entry 0 and the negative half at entry kAbsNeg, in a 64 KB
+// array: every 16-bit byte offset lies inside it.
+constexpr int kAbsNeg = 8192;
+constexpr int kAbsLds = 16384;
+
+__device__ __forceinline__ void load_abs_table_to_lds(float* lds)
+{
+    const float4* src = reinterpret_cast<const float4*>(g_silu_table);
+    float4* dst = reinterpret_cast<float4*>(lds);
+    for (int i = threadIdx.x; i < kTable / 4; i += blockDim.x) {
+        const float4 v = src[i];
+        const int d = i < kHalf / 4 ? i : i - kHalf / 4 + kAbsNeg / 4;
+        dst[d] = make_float4(fabsf(v.x), fabsf(v.y), fabsf(v.z), fabsf(v.w));
+    }
+    __syncthreads();
+}
+
 // Both tables (s_g, then ds) into 2 * 34 KB of LDS.
 __device__ __forceinline__ void load_tables_to_lds(float* lds)
 {
@@ -123,13 +141,15 @@ __device__ __forceinline__ void load_tables_to_lds(float* lds)
     __syncthreads();
 }
 
-// s_g for one bf16 gate value (16-bit pattern b, fp32 value g).
+// s_g for one bf16 gate value (16-bit pattern b, fp32 value g).  NEG: the index
+// of the first entry of the negative half in tbl.
+template <int NEG = kHalf>
 __device__ __forceinline__ float silu_of(const float* tbl, uint32_t b, float g)
 {
     const uint32_t t = (b & 0x7FFFu) - (uint32_t)(kELo * 128);
     const uint32_t neg = b >> 15;
     const bool in_table = t < (uint32_t)kHalf;
-    const float tv = tbl[in_table ? t + neg * kHalf : 0u];
+    const float tv = tbl[in_table ? t + neg * NEG : 0u];
     if (in_table) return tv;
     if ((int32_t)t < 0) return g * 0.5f;                     // tiny |g|
     if (!neg) return g;                                      // large g, +inf, +NaN
@@ -150,6 +170,7 @@ __device__ __forceinline__ float dsilu_of(const float* tbl, uint32_t b)
 }
 
 // h for the 8 (gate, up) pairs of two 16-byte words.
+template <int NEG = kHalf>
 __device__ __forceinline__ void swiglu8(const float* tbl, uint4 gw, uint4 uw, float h[8])
 {
     const uint32_t g32[4] = {gw.x, gw.y, gw.z, gw.w};
@@ -157,8 +178,8 @@ __device__ __forceinline__ void swiglu8(const float* tbl, uint4 gw, uint4 uw, fl
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const float g0 = bf16_lo(g32[k]), g1 = bf16_hi(g32[k]);
-        h[2 * k] = silu_of(tbl, g32[k] & 0xFFFFu, g0) * bf16_lo(u32[k]);
-        h[2 * k + 1] = silu_of(tbl, g32[k] >> 16, g1) * bf16_hi(u32[k]);
+        h[2 * k] = silu_of<NEG>(tbl, g32[k] & 0xFFFFu, g0) * bf16_lo(u32[k]);
+        h[2 * k + 1] = silu_of<NEG>(tbl, g32[k] >> 16, g1) * bf16_hi(u32[k]);
     }
 }
 
@@ -197,30 +218,126 @@ __device__ __forceinline__ RowItems row_items(int64_t M, int64_t F)
 }
 
 // Forward pass 1: absmax of h over the whole [M, F] output (no output written).
+//
+// Only magnitudes matter here: |h| = RN(|s_g| |u|) (rounding is symmetric in
+// sign), read from the magnitude table above.  The fast form handles eight gate
+// values without branches: for each 32-bit word (two gate values) the table
+// byte offsets are ((|b| - base) << 2) | sign << 15 in packed 16-bit integer
+// arithmetic, so they always fall inside the 64 KB table; a value outside the
+// table's exponent range (tiny or large |g|, infinities, NaN) reads an entry
+// that is discarded: it sets chk to kHalf or more, and its lane recomputes the
+// whole item with the exact rules of silu_of.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+__device__ __forceinline__ uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+__device__ __forceinline__ void swiglu_abs8_fast(const float* tbl, uint4 gw, uint4 uw, uint32_t& m, u16x2& chk)
+{
+    const uint32_t g32[4] = {gw.x, gw.y, gw.z, gw.w};
+    const uint32_t u32[4] = {uw.x, uw.y, uw.z, uw.w};
+    const char* base = reinterpret_cast<const char*>(tbl);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const u16x2 t = as_u16x2(g32[k] & 0x7FFF7FFFu) - (u16x2)(unsigned short)(kELo * 128);
+        chk = __builtin_elementwise_max(chk, t);
+        const uint32_t o = as_u32(t << (unsigned short)2) | (g32[k] & 0x80008000u);
+        const float s0 = *reinterpret_cast<const float*>(base + (o & 0xFFFFu));
+        const float s1 = *reinterpret_cast<const float*>(base + (o >> 16));
+        // s0, s1 >= +0: the products are >= +0 or NaN (a NaN's sign is cleared
+        // by the caller once per item)
+        const uint32_t b0 = __float_as_uint(s0 * fabsf(bf16_lo(u32[k])));
+        const uint32_t b1 = __float_as_uint(s1 * fabsf(bf16_hi(u32[k])));
+        m = m > b0 ? m : b0;
+        m = m > b1 ? m : b1;
+    }
+}
+
+// A lane's share of one wave item: the gate and up words of its two half rows.
+// A half row past F re-reads the row's last eight columns (F >= 16): repeated
+// elements leave a maximum unchanged.
+struct GuWords {
+    uint4 g[2], u[2];
+};
+
+// Item (row i, chunk c) of a wave's walk through the items.  Successive items of
+// a wave are `stride` apart: (i, c) advances by (q, r) = divmod(stride, chunks)
+// with a carry, so the walk needs no division per item.
+struct ItemPos {
+    int64_t i;
+    int64_t c;
+};
+
+__device__ __forceinline__ ItemPos advance(ItemPos p, int64_t q, int64_t r, int64_t chunks)
+{
+    p.i += q;
+    p.c += r;
+    if (p.c >= chunks) {
+        p.c -= chunks;
+        p.i += 1;
+    }
+    return p;
+}
+
+__device__ __forceinline__ GuWords load_item(const uint16_t* __restrict__ gu, int64_t F, ItemPos p, int lane)
+{
+    GuWords r;
+    const int64_t jb = p.c * 1024 + lane * 8;
+    const uint16_t* grow = gu + p.i * 2 * F;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int64_t j0 = jb + half * 512;
+        const int64_t j = j0 < F ? j0 : F - 8;
+        r.g[half] = *reinterpret_cast<const uint4*>(grow + j);
+        r.u[half] = *reinterpret_cast<const uint4*>(grow + F + j);
+    }
+    return r;
+}
+
+__device__ __forceinline__ uint32_t item_absmax(const float* tbl, const GuWords& x)
+{
+    uint32_t mi = 0;
+    u16x2 chk = (u16x2)(unsigned short)0;
+    swiglu_abs8_fast(tbl, x.g[0], x.u[0], mi, chk);
+    swiglu_abs8_fast(tbl, x.g[1], x.u[1], mi, chk);
+    if (chk.x >= (unsigned short)kHalf || chk.y >= (unsigned short)kHalf) {
+        mi = 0;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            float h[8];
+            swiglu8<kAbsNeg>(tbl, x.g[half], x.u[half], h);
+            mi = mag_max8(mi, h);
+        }
+    }
+    return mi & 0x7FFFFFFFu;
+}
+
+// Each wave takes two items per iteration (w and w + stride), all eight 16-byte
+// loads of a lane issued before any of them is used.  The wave's item index is
+// uniform (kept in scalar registers).
 __global__ void __launch_bounds__(1024) swiglu_absmax_kernel(const uint16_t* __restrict__ gu, int64_t M,
                                                             int64_t F, uint32_t* __restrict__ out)
 {
-    __shared__ float tbl[kTable];
-    load_table_to_lds(tbl);
+    __shared__ float tbl[kAbsLds];
+    load_abs_table_to_lds(tbl);
     const RowItems it = row_items(M, F);
     const int lane = threadIdx.x & 63;
+    const int64_t wpb = blockDim.x >> 6;
+    const int64_t stride = (int64_t)gridDim.x * wpb;
+    const int64_t w0 = (int64_t)blockIdx.x * wpb + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t q = stride / it.chunks, r = stride - q * it.chunks;
+    ItemPos pa = {w0 / it.chunks, w0 - (w0 / it.chunks) * it.chunks};
     uint32_t m = 0;
-    const int wpb = blockDim.x >> 6;
-    for (int64_t w = (int64_t)blockIdx.x * wpb + (threadIdx.x >> 6); w < it.total; w += (int64_t)gridDim.x * wpb) {
-        const int64_t i = w / it.chunks;
-        const int64_t jb = (w - i * it.chunks) * 1024 + lane * 8;
-        const uint16_t* grow = gu + i * 2 * F;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int64_t j = jb + half * 512;
-            if (j < F) {
-                const uint4 gw = *reinterpret_cast<const uint4*>(grow + j);
-                const uint4 uw = *reinterpret_cast<const uint4*>(grow + F + j);
-                float h[8];
-                swiglu8(tbl, gw, uw, h);
-                m = mag_max8(m, h);
-            }
-        }
+    for (int64_t w = w0; w < it.total; w += 2 * stride) {
+        // past the end, the second item repeats the first (harmless for a maximum)
+        const ItemPos pn = advance(pa, q, r, it.chunks);
+        const ItemPos pb = w + stride < it.total ? pn : pa;
+        const GuWords a = load_item(gu, F, pa, lane);
+        const GuWords b = load_item(gu, F, pb, lane);
+        const uint32_t ma = item_absmax(tbl, a), mb = item_absmax(tbl, b);
+        m = m > ma ? m : ma;
+        m = m > mb ? m : mb;
+        pa = advance(pn, q, r, it.chunks);
     }
     block_max_to_global(m, out);
 }
