@@ -334,6 +334,7 @@ __global__ void __launch_bounds__(1024) swiglu_absmax_kernel(const uint16_t* __r
         const ItemPos pb = w + stride < it.total ? pn : pa;
         const GuWords a = load_item(gu, F, pa, lane);
         const GuWords b = load_item(gu, F, pb, lane);
+        __builtin_amdgcn_sched_barrier(0);    // every load in flight before the first use
         const uint32_t ma = item_absmax(tbl, a), mb = item_absmax(tbl, b);
         m = m > ma ? m : ma;
         m = m > mb ? m : mb;

@@ -30,11 +30,17 @@ def bits_tensor(b: np.ndarray) -> torch.Tensor:
 
 
 @pytest.mark.parametrize("up_bits", [0x3F80, 0xC0A0])   # u = 1.0 and u = -5.0
-def test_silu_every_gate_value(fp8, orc, up_bits):
-    say("silu sweep", hex(up_bits))
+# the other 15 gates of a row: 0 (outside the table's exponent range: the whole
+# row takes the exact rules) or 1.0 (inside: a swept value inside the range is
+# the only one that decides between the table and the rules); their up values
+# are 0, so h = 0 there
+@pytest.mark.parametrize("filler", [0x0000, 0x3F80])
+def test_silu_every_gate_value(fp8, orc, up_bits, filler):
+    say("silu sweep", hex(up_bits), hex(filler))
     n = 65536
     F = 16
     gu = np.zeros((n, 2 * F), np.uint16)
+    gu[:, 1:F] = filler
     gu[:, 0] = np.arange(n, dtype=np.uint32).astype(np.uint16)
     gu[:, F] = up_bits
     gud = dev(bits_tensor(gu))
