@@ -24,8 +24,14 @@ GEMMs read W, X, dY and h untransposed (fp8_gemm_backward_mn).
 wall time of the whole step, quantisation included: effective FP8 TFLOP/s.
 Inputs are resident in HBM before the timed region starts.
 
+Besides the timed steps the line reports every call of the step (`breakdown`:
+GEMM TFLOP/s, absmax / quantise / SwiGLU GB/s with their algorithmic bytes)
+and `streaming`: the bytes-weighted GB/s of those streaming calls in the step,
+the same calls timed one at a time with a cold Infinity Cache, each as % of the
+8 TB/s HBM peak and against a plain copy kernel measured the same way.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c4|c5]
-                       [--layout copies|mn] [--breakdown] [--no-cpu-baseline]
+                       [--layout copies|mn] [--no-cold] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -309,6 +315,58 @@ def time_steps(ops, steps, stream, instrument_kinds=("gemm",)):
     return wall, start.elapsed_time(end) * 1e-3, per_op
 
 
+STREAM_KINDS = ("absmax", "quantize", "swiglu", "swiglu_bwd")
+FLUSH_BYTES = 1 << 30               # a cold call follows a read of this many bytes
+
+
+def streaming_cold(fp8, ops, stream, dev, reps=20, warm=3):
+    """Every absmax / quantise / SwiGLU call of the step timed on its own with a
+    cold Infinity Cache (median of `reps`, each after a 1 GiB read: a read
+    evicts the 256 MB cache without leaving dirty lines for the timed call to
+    write back), and a plain copy kernel measured the same way as the
+    achievable read+write reference.  Calls that accumulate a statistic are
+    idempotent, so repeating them is harmless."""
+    flush = torch.ones(FLUSH_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    fam = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        for _ in range(warm):
+            fp8.absmax(flush, fam, accumulate=True)
+            fn()
+        pairs = []
+        for _ in range(reps):
+            fp8.absmax(flush, fam, accumulate=True)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            pairs.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) * 1e-3 for a, b in pairs]))
+
+    src = torch.ones(1 << 27, dtype=torch.bfloat16, device=dev)          # 256 MiB
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    copy_gbs = 2 * src.numel() * 2 / t_copy / 1e9
+    del src, dst
+    calls, tb, tt = [], 0, 0.0
+    for op in ops:
+        if op.kind not in STREAM_KINDS:
+            continue
+        t = timed(op.fn)
+        gbs = op.work / t / 1e9
+        calls.append({"call": op.name, "bytes": int(op.work), "us": round(t * 1e6, 2), "gbs": round(gbs, 1),
+                      "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1), "vs_copy": round(gbs / copy_gbs, 3)})
+        tb += op.work
+        tt += t
+    del flush
+    torch.cuda.empty_cache()
+    agg = tb / tt / 1e9
+    return copy_gbs, {"gbs": round(agg, 1), "pct_hbm": round(100 * agg / HBM_PEAK_GBS, 1),
+                      "vs_copy": round(agg / copy_gbs, 3), "calls": calls}
+
+
 STREAM_SAMPLE_ELEMS = 1 << 25      # oracle sample of a streaming call: at most 32 M elements
 
 
@@ -458,7 +516,10 @@ def main():
     ap.add_argument("--swiglu-backward", action="store_true",
                     help="chain the MLP backward: down dgrad -> fused SwiGLU backward -> gate/up backward "
                          "(instead of a drawn gate/up output gradient)")
-    ap.add_argument("--breakdown", action="store_true", help="also time every call (separate pass)")
+    ap.add_argument("--breakdown", action="store_true",
+                    help="accepted for compatibility: the per-call breakdown is always reported")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache per-call streaming measurement")
     ap.add_argument("--no-clock", action="store_true", help="skip the sustained-clock sampling (amd-smi)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -503,24 +564,26 @@ def main():
     achieved = dom["flop"] / dom["time"] / 1e12
     gemm_time = sum(d["time"] for d in by_kernel.values())
 
-    breakdown = None
-    if args.breakdown:
-        _, _, per_all = time_steps(ops, max(3, args.steps // 2), stream,
-                                   instrument_kinds=("gemm", "absmax", "quantize", "swiglu", "swiglu_bwd", "zero"))
-        breakdown = []
-        for op in ops:
-            t = float(np.mean(per_all[op.name]))
-            if op.kind == "zero":
-                breakdown.append({"call": op.name, "us": round(t * 1e6, 2)})
-                continue
-            unit = "TFLOP/s" if op.kind == "gemm" else "GB/s"
-            rate = op.work / t / (1e12 if op.kind == "gemm" else 1e9)
-            breakdown.append({"call": op.name, "us": round(t * 1e6, 2), "rate": round(rate, 1), "unit": unit})
-        qt = sum(float(np.mean(per_all[op.name])) for op in ops if op.kind != "gemm")
-        qb = sum(op.work for op in ops if op.kind != "gemm")
-        quant_gbs = qb / qt / 1e9
-    else:
-        quant_gbs = None
+    # every call of the step, in the step (a separate instrumented pass: events
+    # around each call; the pipeline's legitimate cache reuse included)
+    _, _, per_all = time_steps(ops, max(3, args.steps // 2), stream,
+                               instrument_kinds=("gemm", "zero") + STREAM_KINDS)
+    breakdown = []
+    for op in ops:
+        t = float(np.mean(per_all[op.name]))
+        if op.kind == "zero":
+            breakdown.append({"call": op.name, "us": round(t * 1e6, 2)})
+            continue
+        if op.kind == "gemm":
+            breakdown.append({"call": op.name, "us": round(t * 1e6, 2), "rate": round(op.work / t / 1e12, 1),
+                              "unit": "TFLOP/s"})
+        else:
+            breakdown.append({"call": op.name, "bytes": int(op.work), "us": round(t * 1e6, 2),
+                              "rate": round(op.work / t / 1e9, 1), "unit": "GB/s"})
+    qt = sum(float(np.mean(per_all[op.name])) for op in ops if op.kind in STREAM_KINDS)
+    qb = sum(op.work for op in ops if op.kind in STREAM_KINDS)
+    quant_gbs = qb / qt / 1e9
+    copy_gbs, cold = (None, None) if args.no_cold else streaming_cold(fp8, ops, stream, dev)
 
     clock = None if args.no_clock else sustained_clock(ops)
     want_cpu = not args.no_cpu_baseline and (args.workload == "c3" or args.cpu_baseline)
@@ -565,9 +628,15 @@ def main():
         "sustained_clock": clock,
         "wall_s": round(wall, 3),
     }
-    if quant_gbs is not None:
-        line["quant_absmax_swiglu_gbs"] = round(quant_gbs, 1)
-        line["breakdown"] = breakdown
+    line["quant_absmax_swiglu_gbs"] = round(quant_gbs, 1)
+    line["streaming"] = {
+        "unit": "GB/s", "hbm_peak": HBM_PEAK_GBS, "copy_cold_gbs": round(copy_gbs, 1) if copy_gbs else None,
+        "in_step": {"gbs": round(quant_gbs, 1), "pct_hbm": round(100 * quant_gbs / HBM_PEAK_GBS, 1),
+                    "vs_copy": round(quant_gbs / copy_gbs, 3) if copy_gbs else None,
+                    "bytes": int(qb), "note": "bytes-weighted over the step's absmax/quantise/SwiGLU calls"},
+        "cold": cold,
+    }
+    line["breakdown"] = breakdown
     print(json.dumps(line))
 
 
