@@ -68,6 +68,40 @@ def test_every_gate_value(fp8):
     check(fp8, gu, dh, E5M2, True, True, "every gate value")
 
 
+@pytest.mark.parametrize("up,d", [(-5.0, 0.75), (1.0, -3.0)])
+def test_statistic_of_every_gate_value(fp8, up, d):
+    """Each of the 65536 gate patterns alone decides a call's statistic: its row
+    holds the pattern (with the given u and dh) and 15 in-range neighbours with
+    g = 1, u = 0, dh = 0 (dg = du = 0), so the table lookup or the exact rules
+    for that one value alone give absmax; compared with the oracle's gradient
+    row by row."""
+    say("swiglu_backward statistic sweep", up, d)
+    n, F = 65536, 16
+    gu = np.zeros((n, 2 * F), np.uint16)
+    gu[:, :F] = 0x3F80
+    gu[:, 0] = np.arange(n, dtype=np.uint32).astype(np.uint16)
+    gu[:, F] = bf16(np.float32(up))
+    dh = np.zeros((n, F), np.uint16)
+    dh[:, 0] = bf16(np.float32(d))
+    gud, dhd = to_dev(gu), to_dev(dh)
+    am = torch.empty(n, dtype=torch.float32, device="cuda")
+    q = torch.empty((n, 2 * F), dtype=torch.uint8, device="cuda")
+    for i in range(n):
+        fp8.swiglu_backward(gud[i:i + 1], dhd[i:i + 1], E5M2, absmax=am[i:i + 1], q=q[i:i + 1])
+    am_g = am.cpu().numpy()
+    grad = oracle.swiglu_grad(gu, dh)
+    bad = []
+    for i in range(n):
+        want = oracle.absmax_f32(np.ascontiguousarray(grad[i]))
+        ok = (np.isnan(want) and np.isnan(am_g[i])) or \
+            np.float32(am_g[i]).view(np.uint32) == np.float32(want).view(np.uint32)
+        if not ok:
+            bad.append((hex(gu[i, 0]), float(am_g[i]), float(want)))
+            if len(bad) > 10:
+                break
+    assert not bad, bad
+
+
 def test_special_values(fp8):
     rng = np.random.default_rng(4)
     M, F = 64, 256
