@@ -209,7 +209,9 @@ fp8_status fp8_swiglu_backward(const void* gu, const void* dh, int64_t M, int64_
  *           fp8_swiglu_requant for the two operands
  *   dy_fmt  FP8_E5M2 (default reading of the pages) or FP8_E4M3
  * Constraints: every dimension >= 16 and a multiple of 16; the reduction
- * length (K, N and M respectively) a multiple of 128.
+ * length (K, N and M respectively) a multiple of 128; each FP8 operand smaller
+ * than 2^31 bytes and each output dimension below 2^30 (operand offsets are
+ * 32-bit); anything else returns FP8_ERR_UNSUPPORTED.
  */
 fp8_status fp8_gemm_fwd(const uint8_t* xq, const uint8_t* wq, const float* inv_sx,
                         const float* inv_sw, void* y, int64_t M, int64_t N, int64_t K,

@@ -141,6 +141,10 @@ def test_gemm_validation(lib, entry):
     assert call(A16, B16, C16, C16 + 4, D16, *red) == UNSUPPORTED
     assert call(A16, B16, C16, C16 + 4, D16 + 4, 128, 128, 128) == UNSUPPORTED  # misaligned out
     assert call(A16 + 1, B16, C16, C16 + 4, D16, 128, 128, 128) == UNSUPPORTED
+    # an operand of 2^31 bytes (A = 131072 rows of a 16384-byte reduction): 32-bit offsets
+    big = {"fwd": (131072, 128, 16384), "dgrad": (131072, 16384, 128), "wgrad": (16384, 131072, 128)}[entry]
+    far_a, far_b, far_out = 1 << 40, 2 << 40, 3 << 40
+    assert call(far_a, far_b, C16, C16 + 4, far_out, *big) == UNSUPPORTED
 
 
 def test_backward_validation(lib):
