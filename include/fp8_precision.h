@@ -19,8 +19,13 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Every pointer argument is a DEVICE pointer owned by the caller.  The
- *    library allocates no device memory for any call, keeps no reference
- *    after the call returns, and never synchronises the host.
+ *    library allocates no device memory for any call and keeps no reference
+ *    after the call returns.  It never synchronises the host, with one
+ *    exception: the first call on a device that needs the SwiGLU tables
+ *    (fp8_swiglu_requant, fp8_swiglu_backward, fp8_gemm_fwd_swiglu_absmax)
+ *    builds them in the library's static device memory on its stream and
+ *    waits for that stream once, so that later calls on any stream see the
+ *    complete tables.  Make that first call outside stream capture.
  *  - All work is enqueued on `stream` (0 = the null stream).  Inputs must stay
  *    valid until the stream reaches the work.
  *  - absmax, scale and inverse-scale values stay in device memory as fp32
