@@ -93,6 +93,7 @@ def linear_backward(fp8, orc, cfg, li, xqt, inv_x, wqt, inv_w):
     dx2, dw2 = fp8.gemm_backward(dyq, dyqt, E5M2, wqt, xqt, inv_dy, inv_w, inv_x)
     assert torch.equal(dx2.view(torch.int16), dx.view(torch.int16)), "paired dgrad differs from fp8_gemm_dgrad"
     assert torch.equal(dw2.view(torch.int16), dw.view(torch.int16)), "paired wgrad differs from fp8_gemm_wgrad"
+    return dx
 
 
 # every linear of each configuration, except the down linear of an MLP chain,
@@ -127,8 +128,11 @@ def swiglu_step(fp8, orc, gu, want_hqt, what):
 
 @pytest.mark.parametrize("cname", ["c2", "c5"])
 def test_mlp_chain(fp8, orc, cname):
-    """X -> e4m3 -> gate/up GEMM -> fused SwiGLU requant -> down GEMM (and, for the
-    32B configuration, the down linear's backward and the MLP recomputation)."""
+    """X -> e4m3 -> gate/up GEMM -> fused SwiGLU requant -> down GEMM; for the 32B
+    configuration also the down linear's backward, the MLP recomputation, and the
+    MLP backward on the recomputed gate/up output: dH (the down dgrad output) ->
+    fused SwiGLU backward (e5m2 [dg | du] and its transposed copy, bit-exact in
+    full) -> gate/up dgrad and wgrad (sampled rows)."""
     cfg = workloads.CONFIGS[cname]
     gi = [l.name for l in cfg.linears].index("gate_up")
     di = [l.name for l in cfg.linears].index("down")
@@ -142,7 +146,7 @@ def test_mlp_chain(fp8, orc, cname):
     if not cfg.recompute:
         return
     # down linear backward: dgrad with W_down^T, wgrad with the SwiGLU output's transposed copy
-    linear_backward(fp8, orc, cfg, di, hqt, inv_h, wdqt, inv_wd)
+    dh = linear_backward(fp8, orc, cfg, di, hqt, inv_h, wdqt, inv_wd)
     del y
     # recomputation with retained statistics: no reduction, identical bytes
     say("recompute", cname)
@@ -159,4 +163,29 @@ def test_mlp_chain(fp8, orc, cname):
     assert torch.equal(am_x.view(torch.int32), am_x_before.view(torch.int32))
     assert torch.equal(hq2, hq) and torch.equal(hqt2, hqt)
     assert torch.equal(inv_h2.view(torch.int32), inv_h.view(torch.int32))
+    del hq, hqt, hq2, hqt2, hq_h
+    torch.cuda.empty_cache()
+    # MLP backward through the fused SwiGLU backward
+    say("swiglu_backward", cname)
+    dgq, dgqt, am_dg, _, inv_dg = fp8.swiglu_backward(gu2, dh, E5M2, want_q=True, want_qt=True)
+    q_r, qt_r, am_r, _, inv_r = orc.swiglu_backward(u16(gu2), u16(dh), E5M2, want_q=True, want_qt=True)
+    assert_f32_equal(scalar(am_dg), am_r, f"{cname} d[gate | up] absmax")
+    assert_f32_equal(scalar(inv_dg), inv_r, f"{cname} d[gate | up] inv_scale")
+    dgq_h = u8(dgq)
+    assert_codes_equal(dgq_h, q_r, E5M2, f"{cname} d[gate | up] q")
+    del q_r
+    assert_codes_equal(u8(dgqt), qt_r, E5M2, f"{cname} d[gate | up] qt")
+    del qt_r, gu, gu2, dh
+    torch.cuda.empty_cache()
+    # the gate/up backward operands: W_gu^T (the forward's statistic, recomputed) and X^T
+    _, _, _, wqt_gu, inv_wgu2, _ = quant_step(fp8, orc, workloads.draw_w(cfg, gi), E4M3, True, f"{cname} W_gate_up")
+    assert torch.equal(inv_wgu2.view(torch.int32), inv_wgu.view(torch.int32))
+    _, xqt2, _, _ = fp8.quantize(x.cuda(), E4M3, am_x, want_q=False, want_qt=True)
+    say("gemm_dgrad gate_up", cname)
+    dx_gu = fp8.gemm_dgrad(dgq, E5M2, wqt_gu, inv_dg, inv_wgu)
+    gemm_step(orc, dx_gu, dgq_h, E5M2, wqt_gu, inv_dg, inv_wgu, f"{cname} dgrad gate_up", 500)
+    del dx_gu, dgq_h
+    say("gemm_wgrad gate_up", cname)
+    dw_gu = fp8.gemm_wgrad(dgqt, E5M2, xqt2, inv_dg, inv_x)
+    gemm_step(orc, dw_gu, u8(dgqt), E5M2, xqt2, inv_dg, inv_x, f"{cname} wgrad gate_up", 501)
     torch.cuda.empty_cache()
