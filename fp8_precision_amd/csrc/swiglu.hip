@@ -374,65 +374,90 @@ __global__ void __launch_bounds__(256) swiglu_quant_kernel(const uint16_t* __res
     }
 }
 
-// Requantisation with the transposed copy hqt [F, M] (and optionally hq).
-// A wave owns 64 rows x 64 columns of h; lane l handles the 8 x 8 block at
-// rows 8 (l / 8) .. +7 and columns 8 (l % 8) .. +7.  Every load instruction
-// reads eight full 128-byte row segments of gate (or up); the lane transposes
-// its 8 x 8 code block in registers (v_perm_b32), so each hq store writes 64
-// contiguous bytes of eight rows and each hqt store 64 contiguous bytes of
-// eight hqt rows.  No LDS tile and no barrier: the only LDS is the s_g table,
-// and waves of one block never wait for each other.  Persistent blocks, three
-// per CU (three 34 KB tables; about 150 VGPRs per lane).
-constexpr int kHtEdge = 64;
+// Requantisation with the transposed copy hqt [F, M] (and optionally hq).  A
+// block of 4 waves owns a 128 x 128 tile of h and walks the tiles persistently
+// (the s_g table is copied into LDS once per block).  Lane l of wave w takes the
+// 8 x 8 block at rows 32 w + 8 (l / 16) .. and columns 8 (l % 16) ..: its 16
+// loads (gate and up) are all issued first, each instruction reading four
+// 256-byte row segments; hq is written as 128-byte row segments; the lane's
+// 8 x 8 code block is transposed in registers (v_perm_b32) into eight 8-byte
+// pieces of hqt rows, parked in a 16 KB LDS tile laid out as hqt ([128
+// columns][128 rows], 16-byte pieces XOR-swizzled by column), and written back
+// after a barrier as full 128-byte hqt row segments.  (Writing hqt straight from
+// registers, 64 bytes per row and instruction, ran at 3.1-3.5 TB/s with a cold
+// cache.)  M and F are multiples of 16, so a lane's block is whole.
+constexpr int kHtEdge = 64;                   // wave item edge of the backward kernels
+constexpr int kSqEdge = 128;
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 swiglu_quant_t_kernel(const uint16_t* __restrict__ gu, int64_t M, int64_t F, const float* __restrict__ absmax_h,
                       uint8_t* __restrict__ hq, uint8_t* __restrict__ hqt, float* __restrict__ inv_out)
 {
-    __shared__ float tbl[kTable];
+    __shared__ float tbl[kTable];                                               // 34 KB
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kSqEdge * kSqEdge];    // 16 KB
     float s, inv;
     tensor_scale(*absmax_h, kMaxE4M3, s, inv);
     if (blockIdx.x == 0 && threadIdx.x == 0 && inv_out) *inv_out = inv;
     load_table_to_lds(tbl);
-    const int lane = threadIdx.x & 63;
-    const int ri = (lane >> 3) * 8, ci = (lane & 7) * 8;   // the lane's block within the wave item
-    const int64_t items_c = (F + kHtEdge - 1) / kHtEdge;
-    const int64_t items = items_c * ((M + kHtEdge - 1) / kHtEdge);
-    const int64_t wstride = (int64_t)gridDim.x * 4;
-    for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < items; w += wstride) {
-        const int64_t i0 = (w / items_c) * kHtEdge + ri;
-        const int64_t j0 = (w % items_c) * kHtEdge + ci;
-        if (i0 >= M || j0 >= F) continue;             // M, F are multiples of 8: blocks are whole
-        uint4 gw[8], uw[8];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rt = wave * 32 + (lane >> 4) * 8;           // first row of the lane within the tile
+    const int ct = (lane & 15) * 8;                       // first column of the lane within the tile
+    const int64_t ntc = (F + kSqEdge - 1) / kSqEdge;
+    const int64_t ntiles = ntc * ((M + kSqEdge - 1) / kSqEdge);
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t tr = (t / ntc) * kSqEdge, tc = (t % ntc) * kSqEdge;
+        if (tr + rt < M && tc + ct < F) {
+            const int64_t i0 = tr + rt, j = tc + ct;
+            uint4 gw[8], uw[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const uint16_t* grow = gu + (i0 + r) * 2 * F + j0;
-            gw[r] = *reinterpret_cast<const uint4*>(grow);
-            uw[r] = *reinterpret_cast<const uint4*>(grow + F);
+            for (int r = 0; r < 8; ++r) {
+                const uint16_t* grow = gu + (i0 + r) * 2 * F + j;
+                gw[r] = *reinterpret_cast<const uint4*>(grow);
+                uw[r] = *reinterpret_cast<const uint4*>(grow + F);
+            }
+            uint32_t lo[8], hi[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                float h[8];
+                swiglu8(tbl, gw[r], uw[r], h);
+                const uint2 c = quant8_h(h, s);
+                lo[r] = c.x;
+                hi[r] = c.y;
+            }
+            if (hq) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    *reinterpret_cast<uint2*>(hq + (i0 + r) * F + j) = make_uint2(lo[r], hi[r]);
+            }
+            // column k of the block: rows 0..3 (word 0) and rows 4..7 (word 1)
+            uint32_t c0[8], c1[8];
+            transpose4x4(lo[0], lo[1], lo[2], lo[3], c0[0], c0[1], c0[2], c0[3]);
+            transpose4x4(lo[4], lo[5], lo[6], lo[7], c1[0], c1[1], c1[2], c1[3]);
+            transpose4x4(hi[0], hi[1], hi[2], hi[3], c0[4], c0[5], c0[6], c0[7]);
+            transpose4x4(hi[4], hi[5], hi[6], hi[7], c1[4], c1[5], c1[6], c1[7]);
+            const int piece = rt >> 4, half = (rt >> 3) & 1;   // 8-byte half of a 16-byte piece
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int col = ct + k;
+                const int phys = piece ^ ((col >> 3) & 7);
+                *reinterpret_cast<uint2*>(tile + col * kSqEdge + phys * 16 + half * 8) = make_uint2(c0[k], c1[k]);
+            }
         }
-        uint32_t lo[8], hi[8];
+        __syncthreads();
+        // write-back: 1024 pieces of 16 bytes, 4 per thread; a wave instruction
+        // covers 8 hqt rows x 128 bytes
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            float h[8];
-            swiglu8(tbl, gw[r], uw[r], h);
-            const uint2 c = quant8_h(h, s);
-            lo[r] = c.x;
-            hi[r] = c.y;
+        for (int u = 0; u < 4; ++u) {
+            const int id = u * 256 + threadIdx.x;
+            const int col = id >> 3, p = id & 7;
+            const int64_t qrow = tc + col, qcol = tr + p * 16;
+            if (qrow < F && qcol < M) {
+                const int phys = p ^ ((col >> 3) & 7);
+                *reinterpret_cast<uint4*>(hqt + qrow * M + qcol) =
+                    *reinterpret_cast<const uint4*>(tile + col * kSqEdge + phys * 16);
+            }
         }
-        if (hq) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                *reinterpret_cast<uint2*>(hq + (i0 + r) * F + j0) = make_uint2(lo[r], hi[r]);
-        }
-        // column k of the block = rows 0..3 (word 0) and rows 4..7 (word 1)
-        uint32_t c0[8], c1[8];
-        transpose4x4(lo[0], lo[1], lo[2], lo[3], c0[0], c0[1], c0[2], c0[3]);
-        transpose4x4(lo[4], lo[5], lo[6], lo[7], c1[0], c1[1], c1[2], c1[3]);
-        transpose4x4(hi[0], hi[1], hi[2], hi[3], c0[4], c0[5], c0[6], c0[7]);
-        transpose4x4(hi[4], hi[5], hi[6], hi[7], c1[4], c1[5], c1[6], c1[7]);
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            *reinterpret_cast<uint2*>(hqt + (j0 + k) * M + i0) = make_uint2(c0[k], c1[k]);
+        __syncthreads();                                  // the tile is read back before it is reused
     }
 }
 
@@ -461,9 +486,9 @@ hipError_t launch_swiglu_requant(const void* gu, int64_t M, int64_t F, float* ab
         swiglu_absmax_kernel<<<(unsigned)ablocks, 1024, 0, stream>>>(g, M, F, reinterpret_cast<uint32_t*>(absmax_h));
     }
     if (hqt) {
-        // three resident blocks per CU (register-limited), persistent over the wave items
-        const int64_t witems = ((F + kHtEdge - 1) / kHtEdge) * ((M + kHtEdge - 1) / kHtEdge);
-        int64_t tblocks = (witems + 3) / 4;
+        // three resident blocks per CU (50 KB of LDS each), persistent over the tiles
+        const int64_t tiles = ((F + kSqEdge - 1) / kSqEdge) * ((M + kSqEdge - 1) / kSqEdge);
+        int64_t tblocks = tiles;
         if (tblocks > 3 * (int64_t)device_cu_count()) tblocks = 3 * (int64_t)device_cu_count();
         swiglu_quant_t_kernel<<<(unsigned)tblocks, 256, 0, stream>>>(g, M, F, absmax_h, hq, hqt, inv_scale_h);
     } else {
