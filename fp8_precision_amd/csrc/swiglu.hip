@@ -386,7 +386,6 @@ __global__ void __launch_bounds__(256) swiglu_quant_kernel(const uint16_t* __res
 // after a barrier as full 128-byte hqt row segments.  (Writing hqt straight from
 // registers, 64 bytes per row and instruction, ran at 3.1-3.5 TB/s with a cold
 // cache.)  M and F are multiples of 16, so a lane's block is whole.
-constexpr int kHtEdge = 64;                   // wave item edge of the backward kernels
 constexpr int kSqEdge = 128;
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
@@ -603,20 +602,24 @@ __global__ void __launch_bounds__(256) swiglu_bwd_quant_kernel(const uint16_t* _
     }
 }
 
-// Pass 2 with the transposed copy qt [2F, M] (and optionally q): a wave owns
-// 64 rows x 64 columns of (g, u, dh), a lane the 8 x 8 block at rows
-// 8 (l / 8) .. +7 and columns 8 (l % 8) .. +7; its dg and du code blocks are
-// transposed in registers and written as 64-byte segments of qt rows j and
-// F + j.  No LDS beyond the two tables, no barrier.
+// Pass 2 with the transposed copy qt [2F, M] (and optionally q).  The layout
+// of the forward's transposed requant: a 4-wave group owns a 128 x 128 tile of
+// (g, u, dh) and a lane its 8 x 8 block (24 loads, all issued first); the dg
+// and du code blocks are transposed in registers and parked in two 16 KB LDS
+// tiles laid out as qt rows j and F + j, then written back as full 128-byte
+// rows.  A block is two such groups (512 threads, one copy of the two tables:
+// 132 KB of LDS, one block per CU) taking two tiles per iteration, so both
+// groups meet every barrier.  M and F are multiples of 16: blocks are whole.
 template <int FMT>
-__global__ void __launch_bounds__(256) swiglu_bwd_quant_t_kernel(const uint16_t* __restrict__ gu,
+__global__ void __launch_bounds__(512) swiglu_bwd_quant_t_kernel(const uint16_t* __restrict__ gu,
                                                                  const uint16_t* __restrict__ dh, int64_t M,
                                                                  int64_t F, const float* __restrict__ absmax,
                                                                  uint8_t* __restrict__ q, uint8_t* __restrict__ qt,
                                                                  float* __restrict__ scale_out,
                                                                  float* __restrict__ inv_out)
 {
-    __shared__ float tbl[2 * kTable];
+    __shared__ float tbl[2 * kTable];                                                   // 68 KB
+    __shared__ __attribute__((aligned(16))) uint8_t tiles[2][2][kSqEdge * kSqEdge];     // [group][dg | du], 64 KB
     float s, inv;
     tensor_scale(*absmax, Fmt<FMT>::max, s, inv);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -624,53 +627,89 @@ __global__ void __launch_bounds__(256) swiglu_bwd_quant_t_kernel(const uint16_t*
         if (inv_out) *inv_out = inv;
     }
     load_tables_to_lds(tbl);
-    const int lane = threadIdx.x & 63;
-    const int ri = (lane >> 3) * 8, ci = (lane & 7) * 8;
-    const int64_t items_c = (F + kHtEdge - 1) / kHtEdge;
-    const int64_t items = items_c * ((M + kHtEdge - 1) / kHtEdge);
-    const int64_t wstride = (int64_t)gridDim.x * 4;
-    for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < items; w += wstride) {
-        const int64_t i0 = (w / items_c) * kHtEdge + ri;
-        const int64_t j0 = (w % items_c) * kHtEdge + ci;
-        if (i0 >= M || j0 >= F) continue;             // M, F are multiples of 8: blocks are whole
-        uint32_t glo[8], ghi[8], ulo[8], uhi[8];      // codes of dg (g...) and du (u...), per row
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const uint16_t* grow = gu + (i0 + r) * 2 * F + j0;
-            const uint4 gw = *reinterpret_cast<const uint4*>(grow);
-            const uint4 uw = *reinterpret_cast<const uint4*>(grow + F);
-            const uint4 dw = *reinterpret_cast<const uint4*>(dh + (i0 + r) * F + j0);
-            float dg[8], du[8];
-            swiglu_grad8(tbl, tbl + kTable, gw, uw, dw, dg, du);
-            const uint2 cg = quant8_f<FMT>(dg, s);
-            const uint2 cu = quant8_f<FMT>(du, s);
-            glo[r] = cg.x;
-            ghi[r] = cg.y;
-            ulo[r] = cu.x;
-            uhi[r] = cu.y;
-        }
-        if (q) {
+    const int grp = threadIdx.x >> 8, gt = threadIdx.x & 255;
+    const int lane = gt & 63, wave = gt >> 6;
+    const int rt = wave * 32 + (lane >> 4) * 8;           // first row of the lane within the tile
+    const int ct = (lane & 15) * 8;                       // first column of the lane within the tile
+    uint8_t* tg = tiles[grp][0];
+    uint8_t* tu = tiles[grp][1];
+    const int64_t ntc = (F + kSqEdge - 1) / kSqEdge;
+    const int64_t ntiles = ntc * ((M + kSqEdge - 1) / kSqEdge);
+    for (int64_t t0 = 2 * (int64_t)blockIdx.x; t0 < ntiles; t0 += 2 * (int64_t)gridDim.x) {
+        const int64_t t = t0 + grp;
+        const bool has = t < ntiles;
+        const int64_t tr = has ? (t / ntc) * kSqEdge : 0, tc = has ? (t % ntc) * kSqEdge : 0;
+        if (has && tr + rt < M && tc + ct < F) {
+            const int64_t i0 = tr + rt, j = tc + ct;
+            uint4 gw[8], uw[8], dw[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                *reinterpret_cast<uint2*>(q + (i0 + r) * 2 * F + j0) = make_uint2(glo[r], ghi[r]);
-                *reinterpret_cast<uint2*>(q + (i0 + r) * 2 * F + F + j0) = make_uint2(ulo[r], uhi[r]);
+                const uint16_t* grow = gu + (i0 + r) * 2 * F + j;
+                gw[r] = *reinterpret_cast<const uint4*>(grow);
+                uw[r] = *reinterpret_cast<const uint4*>(grow + F);
+                dw[r] = *reinterpret_cast<const uint4*>(dh + (i0 + r) * F + j);
+            }
+            uint32_t glo[8], ghi[8], ulo[8], uhi[8];      // codes of dg (g...) and du (u...), per row
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                float dg[8], du[8];
+                swiglu_grad8(tbl, tbl + kTable, gw[r], uw[r], dw[r], dg, du);
+                const uint2 cg = quant8_f<FMT>(dg, s);
+                const uint2 cu = quant8_f<FMT>(du, s);
+                glo[r] = cg.x;
+                ghi[r] = cg.y;
+                ulo[r] = cu.x;
+                uhi[r] = cu.y;
+            }
+            if (q) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    *reinterpret_cast<uint2*>(q + (i0 + r) * 2 * F + j) = make_uint2(glo[r], ghi[r]);
+                    *reinterpret_cast<uint2*>(q + (i0 + r) * 2 * F + F + j) = make_uint2(ulo[r], uhi[r]);
+                }
+            }
+            const int piece = rt >> 4, half = (rt >> 3) & 1;
+            uint32_t c0[8], c1[8];
+            transpose4x4(glo[0], glo[1], glo[2], glo[3], c0[0], c0[1], c0[2], c0[3]);
+            transpose4x4(glo[4], glo[5], glo[6], glo[7], c1[0], c1[1], c1[2], c1[3]);
+            transpose4x4(ghi[0], ghi[1], ghi[2], ghi[3], c0[4], c0[5], c0[6], c0[7]);
+            transpose4x4(ghi[4], ghi[5], ghi[6], ghi[7], c1[4], c1[5], c1[6], c1[7]);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int col = ct + k;
+                const int phys = piece ^ ((col >> 3) & 7);
+                *reinterpret_cast<uint2*>(tg + col * kSqEdge + phys * 16 + half * 8) = make_uint2(c0[k], c1[k]);
+            }
+            transpose4x4(ulo[0], ulo[1], ulo[2], ulo[3], c0[0], c0[1], c0[2], c0[3]);
+            transpose4x4(ulo[4], ulo[5], ulo[6], ulo[7], c1[0], c1[1], c1[2], c1[3]);
+            transpose4x4(uhi[0], uhi[1], uhi[2], uhi[3], c0[4], c0[5], c0[6], c0[7]);
+            transpose4x4(uhi[4], uhi[5], uhi[6], uhi[7], c1[4], c1[5], c1[6], c1[7]);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int col = ct + k;
+                const int phys = piece ^ ((col >> 3) & 7);
+                *reinterpret_cast<uint2*>(tu + col * kSqEdge + phys * 16 + half * 8) = make_uint2(c0[k], c1[k]);
             }
         }
-        uint32_t c0[8], c1[8];
-        transpose4x4(glo[0], glo[1], glo[2], glo[3], c0[0], c0[1], c0[2], c0[3]);
-        transpose4x4(glo[4], glo[5], glo[6], glo[7], c1[0], c1[1], c1[2], c1[3]);
-        transpose4x4(ghi[0], ghi[1], ghi[2], ghi[3], c0[4], c0[5], c0[6], c0[7]);
-        transpose4x4(ghi[4], ghi[5], ghi[6], ghi[7], c1[4], c1[5], c1[6], c1[7]);
+        __syncthreads();
+        // write-back of the group's two tiles: 2 x 1024 pieces of 16 bytes, 8 per
+        // thread; a wave instruction covers 8 qt rows x 128 bytes
+        if (has) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            *reinterpret_cast<uint2*>(qt + (j0 + k) * M + i0) = make_uint2(c0[k], c1[k]);
-        transpose4x4(ulo[0], ulo[1], ulo[2], ulo[3], c0[0], c0[1], c0[2], c0[3]);
-        transpose4x4(ulo[4], ulo[5], ulo[6], ulo[7], c1[0], c1[1], c1[2], c1[3]);
-        transpose4x4(uhi[0], uhi[1], uhi[2], uhi[3], c0[4], c0[5], c0[6], c0[7]);
-        transpose4x4(uhi[4], uhi[5], uhi[6], uhi[7], c1[4], c1[5], c1[6], c1[7]);
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            *reinterpret_cast<uint2*>(qt + (F + j0 + k) * M + i0) = make_uint2(c0[k], c1[k]);
+            for (int u = 0; u < 4; ++u) {
+                const int id = u * 256 + gt;
+                const int col = id >> 3, p = id & 7;
+                const int64_t qrow = tc + col, qcol = tr + p * 16;
+                if (qrow < F && qcol < M) {
+                    const int phys = p ^ ((col >> 3) & 7);
+                    *reinterpret_cast<uint4*>(qt + qrow * M + qcol) =
+                        *reinterpret_cast<const uint4*>(tg + col * kSqEdge + phys * 16);
+                    *reinterpret_cast<uint4*>(qt + (F + qrow) * M + qcol) =
+                        *reinterpret_cast<const uint4*>(tu + col * kSqEdge + phys * 16);
+                }
+            }
+        }
+        __syncthreads();                                  // the tiles are read back before they are reused
     }
 }
 
@@ -681,10 +720,11 @@ static void launch_swiglu_bwd_quant(const uint16_t* g, const uint16_t* d, int64_
     // two resident blocks per CU (2 x 34 KB tables each), persistent
     const int64_t cap = 2 * (int64_t)device_cu_count();
     if (qt) {
-        const int64_t witems = ((F + kHtEdge - 1) / kHtEdge) * ((M + kHtEdge - 1) / kHtEdge);
-        int64_t blocks = (witems + 3) / 4;
-        if (blocks > cap) blocks = cap;
-        swiglu_bwd_quant_t_kernel<FMT><<<(unsigned)blocks, 256, 0, stream>>>(g, d, M, F, absmax, q, qt, scale,
+        // one 512-thread block per CU (132 KB of LDS), two tiles per iteration
+        const int64_t tiles = ((F + kSqEdge - 1) / kSqEdge) * ((M + kSqEdge - 1) / kSqEdge);
+        int64_t blocks = (tiles + 1) / 2;
+        if (blocks > (int64_t)device_cu_count()) blocks = device_cu_count();
+        swiglu_bwd_quant_t_kernel<FMT><<<(unsigned)blocks, 512, 0, stream>>>(g, d, M, F, absmax, q, qt, scale,
                                                                              inv_scale);
     } else {
         const int64_t items = M * ((F + 1023) / 1024);
