@@ -225,7 +225,7 @@ __global__ void __launch_bounds__(256) quantize_flat_kernel(const uint4* __restr
 constexpr int kQtRows = 128;
 constexpr int kQtCols = 256;
 
-template <int FMT>
+template <int FMT, bool NT>
 __global__ void __launch_bounds__(256) quantize_t_kernel(const uint8_t* __restrict__ x, int64_t rows,
                                                          int64_t cols, const float* __restrict__ absmax,
                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ qt,
@@ -248,8 +248,11 @@ __global__ void __launch_bounds__(256) quantize_t_kernel(const uint8_t* __restri
         const int64_t i0 = tr + rt, j = tc + ct;
         uint4 v[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            v[r] = *reinterpret_cast<const uint4*>(x + ((i0 + r) * cols + j) * 2);
+        for (int r = 0; r < 16; ++r) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(x + ((i0 + r) * cols + j) * 2);
+            const u32x4 w = NT ? __builtin_nontemporal_load(src) : *src;
+            v[r] = make_uint4(w.x, w.y, w.z, w.w);
+        }
         uint32_t lo[16], hi[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -300,8 +303,14 @@ static void launch_quantize_fmt(const void* x, int64_t rows, int64_t cols, const
 {
     if (qt) {
         dim3 grid((unsigned)((cols + kQtCols - 1) / kQtCols), (unsigned)((rows + kQtRows - 1) / kQtRows));
-        quantize_t_kernel<FMT><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(x), rows, cols,
-                                                         absmax, q, qt, scale, inv_scale);
+        // a large input is read non-temporally: nothing reads it again, and the
+        // Infinity Cache is left to the codes the GEMMs read next
+        if (2 * rows * cols >= kAbsStreamBytes)
+            quantize_t_kernel<FMT, true><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(x), rows, cols,
+                                                                   absmax, q, qt, scale, inv_scale);
+        else
+            quantize_t_kernel<FMT, false><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(x), rows, cols,
+                                                                    absmax, q, qt, scale, inv_scale);
     } else {
         const int64_t nvec = rows * cols / 8;
         const int64_t ntiles = (nvec + 127) / 128;
