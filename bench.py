@@ -507,7 +507,7 @@ def main():
                     help="also time the oracle for the c4 / c5 workloads (always done for c3 unless disabled)")
     ap.add_argument("--layout", choices=("copies", "mn"), default="copies",
                     help="backward GEMM operands: transposed FP8 copies, or the untransposed tensors")
-    ap.add_argument("--cpu-gemm-rows", type=int, default=96)
+    ap.add_argument("--cpu-gemm-rows", type=int, default=128)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="c3",
                     help="c3: 7B-class layer (the headline); c4: 14B-class; c5: 32B-class with MLP recomputation")
     ap.add_argument("--fused-swiglu-absmax", action="store_true",
