@@ -37,7 +37,7 @@ __global__ void __launch_bounds__(64) zero_u32_kernel(uint32_t* p)
 // One pass over x; each block folds its maximum into *out with one atomicMax on
 // the fp32 bit pattern (for non-negative values the unsigned order of the bits
 // is the numeric order, and NaN patterns sort above infinity).  One block of 16
-// waves per CU; every lane keeps eight 16-byte loads in flight.  Tensors of at
+// waves per CU; every lane keeps kAbsUnroll 16-byte loads in flight.  Tensors of at
 // least kAbsStreamBytes are read with non-temporal loads: measured on MI355X
 // (7B-layer shapes), that makes the pass ~30% faster on 90-180 MB tensors at a
 // small cost to the quantise pass that follows; below that size the plain
@@ -51,6 +51,12 @@ __device__ __forceinline__ us2 absmax_acc4(us2 m, u32x4 v)
 }
 
 constexpr int kAbsThreads = 1024;
+// Loads in flight per lane: 2 x 16 B x 1024 lanes x 256 CUs = 8 MiB for the
+// whole chip.  Measured with a cold Infinity Cache, plain streaming reads on
+// MI355X peak at about 8 MiB in flight (7.0 TB/s over 1 GiB) and fall to
+// 5.5-6.5 TB/s at 16-32 MiB; with 8 loads per lane the 90-180 MB statistics ran
+// 6-10% slower.
+constexpr int kAbsUnroll = 2;
 constexpr int64_t kAbsStreamBytes = 64ll << 20;
 
 template <bool NT>
@@ -70,12 +76,12 @@ __device__ __forceinline__ void absmax_body(const u32x4* __restrict__ x, int64_t
     us2 m = {0, 0};
     const int64_t stride = (int64_t)nblk * kAbsThreads;
     int64_t i = (int64_t)blk * kAbsThreads + threadIdx.x;
-    for (; i + 7 * stride < nvec; i += 8 * stride) {
-        u32x4 v[8];
+    for (; i + (kAbsUnroll - 1) * stride < nvec; i += kAbsUnroll * stride) {
+        u32x4 v[kAbsUnroll];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = ld16<NT>(x + i + u * stride);
+        for (int u = 0; u < kAbsUnroll; ++u) v[u] = ld16<NT>(x + i + u * stride);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) m = absmax_acc4(m, v[u]);
+        for (int u = 0; u < kAbsUnroll; ++u) m = absmax_acc4(m, v[u]);
     }
     for (; i < nvec; i += stride) m = absmax_acc4(m, ld16<NT>(x + i));
     uint32_t r = m.x > m.y ? m.x : m.y;
