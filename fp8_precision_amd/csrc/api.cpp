@@ -184,7 +184,8 @@ fp8_status fp8_swiglu_requant(const void* gu, int64_t M, int64_t F, float* absma
     if (!hq && !hqt) return fail(FP8_ERR_INVALID, "fp8_swiglu_requant: at least one of hq, hqt is required");
     if (compute_absmax < 0 || compute_absmax > 2)
         return fail(FP8_ERR_INVALID, "fp8_swiglu_requant: compute_absmax must be 0, 1 or 2");
-    if (!mul_ok(M, 2 * F, kMaxElems) || F <= 0) return fail(FP8_ERR_INVALID, "fp8_swiglu_requant: bad shape");
+    if (F <= 0 || F > kMaxElems || !mul_ok(M, 2 * F, kMaxElems))
+        return fail(FP8_ERR_INVALID, "fp8_swiglu_requant: bad shape");
     const int64_t n = M * F;
     const Range r[] = {{gu, 4 * n}, {absmax_h, 4}, {hq, hq ? n : 0}, {hqt, hqt ? n : 0},
                        {inv_scale_h, inv_scale_h ? 4 : 0}};
@@ -206,7 +207,8 @@ fp8_status fp8_swiglu_backward(const void* gu, const void* dh, int64_t M, int64_
     if (!gu || !dh || !absmax) return fail(FP8_ERR_INVALID, "fp8_swiglu_backward: null gu, dh or absmax");
     if (!q && !qt) return fail(FP8_ERR_INVALID, "fp8_swiglu_backward: at least one of q, qt is required");
     if (fmt != FP8_E4M3 && fmt != FP8_E5M2) return fail(FP8_ERR_INVALID, "fp8_swiglu_backward: bad format");
-    if (!mul_ok(M, 2 * F, kMaxElems) || F <= 0) return fail(FP8_ERR_INVALID, "fp8_swiglu_backward: bad shape");
+    if (F <= 0 || F > kMaxElems || !mul_ok(M, 2 * F, kMaxElems))
+        return fail(FP8_ERR_INVALID, "fp8_swiglu_backward: bad shape");
     const int64_t n = M * F;
     const Range r[] = {{gu, 4 * n}, {dh, 2 * n}, {absmax, 4}, {q, q ? 2 * n : 0}, {qt, qt ? 2 * n : 0},
                        {scale, scale ? 4 : 0}, {inv_scale, inv_scale ? 4 : 0}};
@@ -241,6 +243,11 @@ static fp8_status gemm_common(const char* name, const uint8_t* A, int fmt_a, con
     if (P <= 0 || Q <= 0 || R <= 0) {
         std::snprintf(msg, sizeof(msg), "%s: dimensions must be positive", name);
         return fail(FP8_ERR_INVALID, msg);
+    }
+    // bound each dimension before forming any product (P * R, 2 * P * Q stay far below 2^63)
+    if (P >= ((int64_t)1 << 30) || Q >= ((int64_t)1 << 30) || R >= ((int64_t)1 << 31)) {
+        std::snprintf(msg, sizeof(msg), "%s: operand larger than 2 GiB", name);
+        return fail(FP8_ERR_UNSUPPORTED, msg);
     }
     const Range r[] = {{A, P * R}, {B, Q * R}, {inv_a, 4}, {inv_b, 4}, {out, 2 * P * Q}};
     // the two inputs may alias each other (e.g. A == B); the output may alias nothing

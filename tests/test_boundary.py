@@ -120,6 +120,8 @@ def test_swiglu_validation(lib):
     assert s(A16, 16, 16, A16 + 4, 1, B16, None, None, None) == INVALID       # absmax inside gu
     assert s(A16, 16, 24, C16, 1, B16, None, None, None) == UNSUPPORTED       # F % 16
     assert s(A16, 8, 16, C16, 0, None, D16, None, None) == UNSUPPORTED        # M % 16 with hqt
+    assert s(A16, 16, 1 << 62, C16, 1, B16, None, None, None) == INVALID     # 2 F would overflow
+    assert s(A16, 1 << 40, 1 << 40, C16, 1, B16, None, None, None) == INVALID
 
 
 @pytest.mark.parametrize("entry", ["fwd", "dgrad", "wgrad"])
@@ -145,6 +147,10 @@ def test_gemm_validation(lib, entry):
     big = {"fwd": (131072, 128, 16384), "dgrad": (131072, 16384, 128), "wgrad": (16384, 131072, 128)}[entry]
     far_a, far_b, far_out = 1 << 40, 2 << 40, 3 << 40
     assert call(far_a, far_b, C16, C16 + 4, far_out, *big) == UNSUPPORTED
+    # dimensions whose products would overflow 64 bits are refused before any product is formed
+    huge = 1 << 40
+    for dims in ((huge, huge, huge), (16, huge, huge), (huge, 16, 128), (1 << 62, 1 << 62, 1 << 62)):
+        assert call(far_a, far_b, C16, C16 + 4, far_out, *dims) == UNSUPPORTED
 
 
 def test_backward_validation(lib):
@@ -224,6 +230,8 @@ def test_swiglu_backward_validation(lib):
     assert f(*bad) == UNSUPPORTED
     bad = list(ok); bad[1] = B16 + 8              # misaligned dh
     assert f(*bad) == UNSUPPORTED
+    bad = list(ok); bad[3] = 1 << 62              # 2 F would overflow
+    assert f(*bad) == INVALID
 
 
 def test_bad_dy_format(lib):
