@@ -66,8 +66,20 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else t.data_ptr()
 
 
-def _stream(t: torch.Tensor):
-    return torch.cuda.current_stream(t.device).cuda_stream
+def _run(call: str, fn, tensors, *args) -> None:
+    """Call entry point ``fn`` with ``args`` and the stream.  Every tensor of the
+    call must be on one device; that device is made current for the call (the
+    library acts on the current HIP device) and its current stream is passed."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{call}: all tensors must be on one device (got {dev} and {t.device})")
+    with torch.cuda.device(dev):
+        _check(call, fn(*args, torch.cuda.current_stream(dev).cuda_stream))
 
 
 def _dev_tensor(t, name, dtype=None):
@@ -77,6 +89,14 @@ def _dev_tensor(t, name, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _scalar_in(t, name):
+    """An fp32 scalar input (absmax, inverse scale): a device tensor holding at least one value."""
+    _dev_tensor(t, name, torch.float32)
+    if t.numel() < 1:
+        raise ValueError(f"{name} must hold at least one fp32")
     return t
 
 
@@ -100,10 +120,10 @@ def absmax(x: torch.Tensor, out: torch.Tensor | None = None, accumulate: bool = 
         if out is None:
             raise ValueError("accumulate needs out")
         out = _scalar(out, "out", x.device)
-        _check("fp8_absmax_accumulate", _lib.fp8_absmax_accumulate(_ptr(x), x.numel(), _ptr(out), _stream(x)))
+        _run("fp8_absmax_accumulate", _lib.fp8_absmax_accumulate, (x, out), _ptr(x), x.numel(), _ptr(out))
         return out
     out = _scalar(out, "out", x.device)
-    _check("fp8_absmax", _lib.fp8_absmax(_ptr(x), x.numel(), _ptr(out), _stream(x)))
+    _run("fp8_absmax", _lib.fp8_absmax, (x, out), _ptr(x), x.numel(), _ptr(out))
     return out
 
 
@@ -119,9 +139,8 @@ def absmax_accumulate_many(xs, outs) -> None:
     xp = (ctypes.c_void_p * k)(*[_ptr(x) for x in xs])
     ns = (ctypes.c_int64 * k)(*[x.numel() for x in xs])
     op = (ctypes.c_void_p * k)(*[_ptr(o) for o in outs])
-    _check("fp8_absmax_accumulate_many",
-           _lib.fp8_absmax_accumulate_many(k, ctypes.cast(xp, _vp), ctypes.cast(ns, _vp), ctypes.cast(op, _vp),
-                                           _stream(xs[0])))
+    _run("fp8_absmax_accumulate_many", _lib.fp8_absmax_accumulate_many, list(xs) + outs,
+         k, ctypes.cast(xp, _vp), ctypes.cast(ns, _vp), ctypes.cast(op, _vp))
 
 
 def quantize(x: torch.Tensor, fmt: int, amax: torch.Tensor, want_q: bool = True, want_qt: bool = False,
@@ -136,7 +155,7 @@ def quantize(x: torch.Tensor, fmt: int, amax: torch.Tensor, want_q: bool = True,
     if x.dim() != 2:
         raise ValueError("x must be 2-D")
     rows, cols = x.shape
-    _dev_tensor(amax, "amax", torch.float32)
+    _scalar_in(amax, "amax")
     if want_q and q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if want_qt and qt is None:
@@ -148,8 +167,8 @@ def quantize(x: torch.Tensor, fmt: int, amax: torch.Tensor, want_q: bool = True,
                 raise ValueError(f"{n} has the wrong size")
     scale = _scalar(scale, "scale", x.device)
     inv_scale = _scalar(inv_scale, "inv_scale", x.device)
-    _check("fp8_quantize", _lib.fp8_quantize(_ptr(x), rows, cols, int(fmt), _ptr(amax), _ptr(q), _ptr(qt),
-                                             _ptr(scale), _ptr(inv_scale), _stream(x)))
+    _run("fp8_quantize", _lib.fp8_quantize, (x, amax, q, qt, scale, inv_scale),
+         _ptr(x), rows, cols, int(fmt), _ptr(amax), _ptr(q), _ptr(qt), _ptr(scale), _ptr(inv_scale))
     return q, qt, scale, inv_scale
 
 
@@ -183,9 +202,9 @@ def swiglu_requant(gu: torch.Tensor, absmax_h: torch.Tensor | None = None, compu
             if t.numel() != M * F:
                 raise ValueError(f"{n} has the wrong size")
     inv_scale_h = _scalar(inv_scale_h, "inv_scale_h", gu.device)
-    _check("fp8_swiglu_requant", _lib.fp8_swiglu_requant(_ptr(gu), M, F, _ptr(absmax_h),
-                                                         (2 if accumulate else 1) if compute_absmax else 0,
-                                                         _ptr(hq), _ptr(hqt), _ptr(inv_scale_h), _stream(gu)))
+    _run("fp8_swiglu_requant", _lib.fp8_swiglu_requant, (gu, absmax_h, hq, hqt, inv_scale_h),
+         _ptr(gu), M, F, _ptr(absmax_h), (2 if accumulate else 1) if compute_absmax else 0,
+         _ptr(hq), _ptr(hqt), _ptr(inv_scale_h))
     return hq, hqt, absmax_h, inv_scale_h
 
 
@@ -215,8 +234,8 @@ def swiglu_backward(gu: torch.Tensor, dh: torch.Tensor, fmt: int = E5M2, want_q:
     absmax = _scalar(absmax, "absmax", gu.device)
     scale = _scalar(scale, "scale", gu.device)
     inv_scale = _scalar(inv_scale, "inv_scale", gu.device)
-    _check("fp8_swiglu_backward", _lib.fp8_swiglu_backward(_ptr(gu), _ptr(dh), M, F, int(fmt), _ptr(absmax), _ptr(q),
-                                                           _ptr(qt), _ptr(scale), _ptr(inv_scale), _stream(gu)))
+    _run("fp8_swiglu_backward", _lib.fp8_swiglu_backward, (gu, dh, absmax, q, qt, scale, inv_scale),
+         _ptr(gu), _ptr(dh), M, F, int(fmt), _ptr(absmax), _ptr(q), _ptr(qt), _ptr(scale), _ptr(inv_scale))
     return q, qt, absmax, scale, inv_scale
 
 
@@ -237,9 +256,11 @@ def gemm_fwd(xq, wq, inv_sx, inv_sw, out=None) -> torch.Tensor:
     N = wq.shape[0]
     if wq.shape[1] != K:
         raise ValueError("xq is [M, K] and wq must be [N, K]")
+    _scalar_in(inv_sx, "inv_sx")
+    _scalar_in(inv_sw, "inv_sw")
     out = _out_bf16(out, (M, N), xq.device)
-    _check("fp8_gemm_fwd", _lib.fp8_gemm_fwd(_ptr(xq), _ptr(wq), _ptr(inv_sx), _ptr(inv_sw), _ptr(out),
-                                             M, N, K, _stream(xq)))
+    _run("fp8_gemm_fwd", _lib.fp8_gemm_fwd, (xq, wq, inv_sx, inv_sw, out),
+         _ptr(xq), _ptr(wq), _ptr(inv_sx), _ptr(inv_sw), _ptr(out), M, N, K)
     return out
 
 
@@ -252,11 +273,12 @@ def gemm_fwd_swiglu_absmax(xq, wq, inv_sx, inv_sw, absmax_h, out=None) -> torch.
     N = wq.shape[0]
     if wq.shape[1] != K or N % 2:
         raise ValueError("xq is [M, K] and wq must be [2F, K]")
+    _scalar_in(inv_sx, "inv_sx")
+    _scalar_in(inv_sw, "inv_sw")
     absmax_h = _scalar(absmax_h, "absmax_h", xq.device)
     out = _out_bf16(out, (M, N), xq.device)
-    _check("fp8_gemm_fwd_swiglu_absmax",
-           _lib.fp8_gemm_fwd_swiglu_absmax(_ptr(xq), _ptr(wq), _ptr(inv_sx), _ptr(inv_sw), _ptr(out), _ptr(absmax_h),
-                                          M, N // 2, K, _stream(xq)))
+    _run("fp8_gemm_fwd_swiglu_absmax", _lib.fp8_gemm_fwd_swiglu_absmax, (xq, wq, inv_sx, inv_sw, out, absmax_h),
+         _ptr(xq), _ptr(wq), _ptr(inv_sx), _ptr(inv_sw), _ptr(out), _ptr(absmax_h), M, N // 2, K)
     return out
 
 
@@ -268,9 +290,11 @@ def gemm_dgrad(dyq, dy_fmt, wqt, inv_sdy, inv_sw, out=None) -> torch.Tensor:
     K = wqt.shape[0]
     if wqt.shape[1] != N:
         raise ValueError("dyq is [M, N] and wqt must be [K, N]")
+    _scalar_in(inv_sdy, "inv_sdy")
+    _scalar_in(inv_sw, "inv_sw")
     out = _out_bf16(out, (M, K), dyq.device)
-    _check("fp8_gemm_dgrad", _lib.fp8_gemm_dgrad(_ptr(dyq), int(dy_fmt), _ptr(wqt), _ptr(inv_sdy), _ptr(inv_sw),
-                                                 _ptr(out), M, N, K, _stream(dyq)))
+    _run("fp8_gemm_dgrad", _lib.fp8_gemm_dgrad, (dyq, wqt, inv_sdy, inv_sw, out),
+         _ptr(dyq), int(dy_fmt), _ptr(wqt), _ptr(inv_sdy), _ptr(inv_sw), _ptr(out), M, N, K)
     return out
 
 
@@ -282,9 +306,11 @@ def gemm_wgrad(dyqt, dy_fmt, xqt, inv_sdy, inv_sx, out=None) -> torch.Tensor:
     K = xqt.shape[0]
     if xqt.shape[1] != M:
         raise ValueError("dyqt is [N, M] and xqt must be [K, M]")
+    _scalar_in(inv_sdy, "inv_sdy")
+    _scalar_in(inv_sx, "inv_sx")
     out = _out_bf16(out, (N, K), dyqt.device)
-    _check("fp8_gemm_wgrad", _lib.fp8_gemm_wgrad(_ptr(dyqt), int(dy_fmt), _ptr(xqt), _ptr(inv_sdy), _ptr(inv_sx),
-                                                 _ptr(out), M, N, K, _stream(dyqt)))
+    _run("fp8_gemm_wgrad", _lib.fp8_gemm_wgrad, (dyqt, xqt, inv_sdy, inv_sx, out),
+         _ptr(dyqt), int(dy_fmt), _ptr(xqt), _ptr(inv_sdy), _ptr(inv_sx), _ptr(out), M, N, K)
     return out
 
 
@@ -296,11 +322,13 @@ def gemm_backward(dyq, dyqt, dy_fmt, wqt, xqt, inv_sdy, inv_sw, inv_sx, dx=None,
     K = wqt.shape[0]
     if tuple(dyqt.shape) != (N, M) or wqt.shape[1] != N or tuple(xqt.shape) != (K, M):
         raise ValueError("expected dyq [M, N], dyqt [N, M], wqt [K, N], xqt [K, M]")
+    for t, n in ((inv_sdy, "inv_sdy"), (inv_sw, "inv_sw"), (inv_sx, "inv_sx")):
+        _scalar_in(t, n)
     dx = _out_bf16(dx, (M, K), dyq.device)
     dw = _out_bf16(dw, (N, K), dyq.device)
-    _check("fp8_gemm_backward", _lib.fp8_gemm_backward(_ptr(dyq), _ptr(dyqt), int(dy_fmt), _ptr(wqt), _ptr(xqt),
-                                                       _ptr(inv_sdy), _ptr(inv_sw), _ptr(inv_sx), _ptr(dx), _ptr(dw),
-                                                       M, N, K, _stream(dyq)))
+    _run("fp8_gemm_backward", _lib.fp8_gemm_backward, (dyq, dyqt, wqt, xqt, inv_sdy, inv_sw, inv_sx, dx, dw),
+         _ptr(dyq), _ptr(dyqt), int(dy_fmt), _ptr(wqt), _ptr(xqt), _ptr(inv_sdy), _ptr(inv_sw), _ptr(inv_sx),
+         _ptr(dx), _ptr(dw), M, N, K)
     return dx, dw
 
 
@@ -312,9 +340,11 @@ def gemm_dgrad_mn(dyq, dy_fmt, wq, inv_sdy, inv_sw, out=None) -> torch.Tensor:
     K = wq.shape[1]
     if wq.shape[0] != N:
         raise ValueError("dyq is [M, N] and wq must be [N, K]")
+    _scalar_in(inv_sdy, "inv_sdy")
+    _scalar_in(inv_sw, "inv_sw")
     out = _out_bf16(out, (M, K), dyq.device)
-    _check("fp8_gemm_dgrad_mn", _lib.fp8_gemm_dgrad_mn(_ptr(dyq), int(dy_fmt), _ptr(wq), _ptr(inv_sdy), _ptr(inv_sw),
-                                                       _ptr(out), M, N, K, _stream(dyq)))
+    _run("fp8_gemm_dgrad_mn", _lib.fp8_gemm_dgrad_mn, (dyq, wq, inv_sdy, inv_sw, out),
+         _ptr(dyq), int(dy_fmt), _ptr(wq), _ptr(inv_sdy), _ptr(inv_sw), _ptr(out), M, N, K)
     return out
 
 
@@ -326,9 +356,11 @@ def gemm_wgrad_mn(dyq, dy_fmt, xq, inv_sdy, inv_sx, out=None) -> torch.Tensor:
     K = xq.shape[1]
     if xq.shape[0] != M:
         raise ValueError("dyq is [M, N] and xq must be [M, K]")
+    _scalar_in(inv_sdy, "inv_sdy")
+    _scalar_in(inv_sx, "inv_sx")
     out = _out_bf16(out, (N, K), dyq.device)
-    _check("fp8_gemm_wgrad_mn", _lib.fp8_gemm_wgrad_mn(_ptr(dyq), int(dy_fmt), _ptr(xq), _ptr(inv_sdy), _ptr(inv_sx),
-                                                       _ptr(out), M, N, K, _stream(dyq)))
+    _run("fp8_gemm_wgrad_mn", _lib.fp8_gemm_wgrad_mn, (dyq, xq, inv_sdy, inv_sx, out),
+         _ptr(dyq), int(dy_fmt), _ptr(xq), _ptr(inv_sdy), _ptr(inv_sx), _ptr(out), M, N, K)
     return out
 
 
@@ -340,9 +372,11 @@ def gemm_backward_mn(dyq, dy_fmt, wq, xq, inv_sdy, inv_sw, inv_sx, dx=None, dw=N
     K = wq.shape[1]
     if wq.shape[0] != N or tuple(xq.shape) != (M, K):
         raise ValueError("expected dyq [M, N], wq [N, K], xq [M, K]")
+    for t, n in ((inv_sdy, "inv_sdy"), (inv_sw, "inv_sw"), (inv_sx, "inv_sx")):
+        _scalar_in(t, n)
     dx = _out_bf16(dx, (M, K), dyq.device)
     dw = _out_bf16(dw, (N, K), dyq.device)
-    _check("fp8_gemm_backward_mn", _lib.fp8_gemm_backward_mn(_ptr(dyq), int(dy_fmt), _ptr(wq), _ptr(xq),
-                                                             _ptr(inv_sdy), _ptr(inv_sw), _ptr(inv_sx), _ptr(dx),
-                                                             _ptr(dw), M, N, K, _stream(dyq)))
+    _run("fp8_gemm_backward_mn", _lib.fp8_gemm_backward_mn, (dyq, wq, xq, inv_sdy, inv_sw, inv_sx, dx, dw),
+         _ptr(dyq), int(dy_fmt), _ptr(wq), _ptr(xq), _ptr(inv_sdy), _ptr(inv_sw), _ptr(inv_sx), _ptr(dx), _ptr(dw),
+         M, N, K)
     return dx, dw

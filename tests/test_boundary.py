@@ -248,6 +248,19 @@ def test_python_binding_imports_and_fails_loudly_without_gpu():
         fp8.absmax(x)   # a CPU tensor is refused: there is no CPU path
 
 
+def test_binding_refuses_tensors_on_two_devices():
+    """Every call's tensors must share one device (the library acts on the
+    current device, which the binding sets from them): a mix is refused before
+    the entry point is called."""
+    import torch
+    from fp8_precision_amd import _lib as b
+    called = []
+    with pytest.raises(ValueError, match="one device"):
+        b._run("fp8_absmax", lambda *a: called.append(a) or 0,
+               (torch.empty(1), None, torch.empty(1, device="meta")), 0, 1, 0)
+    assert not called
+
+
 def test_gemm_fwd_swiglu_absmax_validation(lib):
     f = lib.fp8_gemm_fwd_swiglu_absmax
     # (xq, wq, inv_sx, inv_sw, gu, absmax_h, M, F, K)

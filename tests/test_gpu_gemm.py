@@ -173,3 +173,33 @@ def test_backward_pair_matches_separate_calls(fp8, orc, M, N, K):
     rows = np.array([0, M // 2, M - 1], np.int64)
     ref = orc.gemm(dyq.numpy(), E5M2, wqt.numpy(), E4M3, np.float32(1 / 57344.0), np.float32(1 / 448.0), rows=rows)
     gemm_compare(u16(dx)[rows], ref, "backward dgrad rows")
+
+
+def test_binding_refuses_host_or_empty_scalars(fp8):
+    """The inverse scales and statistics are device fp32 scalars: a host tensor
+    (whose address a kernel could not read) or an empty one is refused by the
+    binding before anything is launched."""
+    say("binding scalar checks")
+    xq = torch.zeros((256, 256), dtype=torch.uint8, device="cuda")
+    wq = torch.zeros_like(xq)
+    one = scal(1.0)
+    host = torch.ones(1, dtype=torch.float32)
+    empty = torch.empty(0, dtype=torch.float32, device="cuda")
+    with pytest.raises(TypeError):
+        fp8.gemm_fwd(xq, wq, host, one)
+    with pytest.raises(ValueError):
+        fp8.gemm_fwd(xq, wq, one, empty)
+    with pytest.raises(TypeError):
+        fp8.gemm_dgrad(xq, E5M2, wq, one, host)
+    with pytest.raises(TypeError):
+        fp8.gemm_wgrad(xq, E5M2, wq, host, one)
+    with pytest.raises(TypeError):
+        fp8.gemm_backward(xq, xq, E5M2, wq, wq, one, one, host)
+    with pytest.raises(TypeError):
+        fp8.gemm_backward_mn(xq, E5M2, wq, wq, one, host, one)
+    x = torch.zeros((16, 16), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        fp8.quantize(x, E4M3, empty)
+    with pytest.raises(TypeError):
+        fp8.quantize(x, E4M3, torch.zeros(1, dtype=torch.float64, device="cuda"))
+    torch.cuda.synchronize()
