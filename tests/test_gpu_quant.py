@@ -211,3 +211,31 @@ def test_quantize_rejects_bad_arguments(fp8):
     x = torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(fp8.Fp8Error):
         fp8.quantize(x, E4M3, amax, want_qt=True)   # rows % 16 != 0 with qt
+
+
+def test_absmax_every_loop_region(fp8, orc):
+    """One planted maximum at a time in each region of the single pass: the
+    first vector, the last vector of the unrolled part, the remainder vectors
+    past it, the last full vector and the ragged tail -- at lengths whose
+    vector count is not a multiple of the unrolled step, for a full-chip grid
+    (1024 lanes per CU) and for small grids."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stride = cus * 1024                                    # 16-byte vectors per full-grid step
+    lengths = [8 * (2 * stride + stride // 2) + 5,         # one unrolled step, half a step of remainder
+               8 * (4 * stride + 1) + 7,                   # two steps and one remainder vector
+               8 * (3 * stride - 3),                       # one step, then most of another by remainders
+               8 * 3000 + 3, 8 * 8193 + 1]                 # one- and two-block grids
+    for n in lengths:
+        nvec = n // 8
+        base = u16(workloads.draw(103, n % 991, (n,), 1.0))
+        xd = dev(torch.from_numpy(base.view(np.int16).copy()).view(torch.bfloat16))
+        spots = sorted({0, min(nvec - 1, 2 * stride - 1) * 8 + 3, min(nvec - 1, 2 * stride) * 8 + 6,
+                        (nvec - 1) * 8 + 1, n - 1})
+        for p in spots:
+            say("absmax region", n, p)
+            b = base.copy()
+            b[p] = 0xC580                                   # -4096: larger than every drawn value
+            xd[p] = torch.tensor(-4096.0, dtype=torch.bfloat16)
+            got = scalar(fp8.absmax(xd))
+            assert_f32_equal(got, orc.absmax_bf16(b), f"absmax n={n} max at {p}")
+            xd[p] = torch.from_numpy(base[p:p + 1].view(np.int16).copy()).view(torch.bfloat16).cuda()[0]
