@@ -27,7 +27,7 @@ ARCH = "gfx950"
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    f"-I{INCLUDE}", f"-I{CSRC}",
+    f"-I{INCLUDE}", f"-I{CSRC}", f"-I{OBJDIR}",
 ]
 
 
@@ -51,6 +51,11 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
+    # the SwiGLU tables swiglu.hip compiles in (silu_tables.inc)
+    res = subprocess.run([sys.executable, os.path.join(CSRC, "gen_silu_tables.py"), OBJDIR],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gen_silu_tables.py failed:\n{res.stdout}\n{res.stderr}")
     jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))

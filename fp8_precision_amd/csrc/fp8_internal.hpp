@@ -12,8 +12,8 @@ int device_cu_count();
 
 // The SwiGLU s_g table (swiglu.hip): fp32 [2 signs][kSiluEHi - kSiluELo + 1 bf16
 // exponents][128 mantissas], entry = s_g of the bf16 gate value with that sign,
-// exponent and mantissa.  silu_table() builds it on the current device the
-// first time and returns its device address.
+// exponent and mantissa.  It is constant data of the code object (generated at
+// build time); silu_table() returns its address on the current device.
 constexpr int kSiluELo = 100;
 constexpr int kSiluEHi = 133;
 hipError_t silu_table(const float** table, hipStream_t stream);

@@ -14,16 +14,17 @@
 //   |g| >= 2^(E_HI-126), g > 0 (and +inf, NaN): e^-g < 2^-24, 1 + E = 1, s_g = g;
 //   same range, g < 0: e^-g overflows to +inf, s_g = g / inf = -0; -inf and
 //                       NaN give NaN.
-// The table (2 signs x 34 exponents x 128 mantissas, 34 KB) is built once per
-// device by a kernel that evaluates each entry in binary64 and rounds every
-// step to binary32 in the order above; kernels copy it into LDS.
+// The table (2 signs x 34 exponents x 128 mantissas, 34 KB) is constant device
+// data compiled into the library: gen_silu_tables.py evaluates each entry
+// exactly (e^-g to 60 digits) and rounds every step once to binary32 in the
+// order above, at build time; kernels copy it into LDS.
 //
 // The backward (the gradients of gate and up, for the gate/up backward GEMMs)
 // uses the textbook derivative of g * sigma(g): with sig = RN32(1 / t),
 //   ds = RN32(sig * RN32(1 + RN32(g * RN32(1 - sig))))          (silu'(g))
 //   du = RN32(dh * s_g),  dg = RN32(RN32(dh * u) * ds)
 // ds is a function of the 16 bits of g too: a second table over the same
-// exponent range, built with the same single roundings; outside it
+// exponent range, generated with the same single roundings; outside it
 //   |g| < 2^-27: sig = 1/2, 1 + g/2 rounds to 1, ds = 1/2;
 //   |g| >= 128 finite: g > 0 gives sig = 1, ds = 1; g < 0 gives sig = 0, ds = -0;
 //   infinities and NaN: ds = NaN.
@@ -39,59 +40,27 @@ constexpr int kNE = kEHi - kELo + 1;          // 34
 constexpr int kHalf = kNE * 128;              // entries per sign
 constexpr int kTable = 2 * kHalf;             // 8704 entries
 
-__device__ float g_silu_table[kTable];
-__device__ float g_dsilu_table[kTable];
+// Bit patterns of s_g and ds, written by gen_silu_tables.py into the build directory.
+#include "silu_tables.inc"
+static_assert(FP8_SILU_ELO == kELo && FP8_SILU_EHI == kEHi && FP8_SILU_ENTRIES == kTable,
+              "generated SwiGLU tables do not match the kernel's exponent range");
 
-__global__ void __launch_bounds__(256) silu_table_init_kernel()
+__device__ __attribute__((aligned(16))) uint32_t g_silu_table[kTable] = {FP8_SILU_SG_BITS};
+__device__ __attribute__((aligned(16))) uint32_t g_dsilu_table[kTable] = {FP8_SILU_DS_BITS};
+
+// Device address of the s_g table on the current device (for kernels in other
+// translation units), looked up once per device.  No kernel runs and the host
+// does not wait: the table is part of the loaded code object.
+hipError_t silu_table(const float** table, hipStream_t stream)
 {
-#pragma clang fp contract(off)
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= kTable) return;
-    const uint32_t sign = idx >= kHalf ? 1u : 0u;
-    const uint32_t rem = idx - sign * kHalf;
-    const uint32_t bits = (sign << 15) | ((uint32_t)(kELo + rem / 128) << 7) | (rem % 128);
-    const float g = __uint_as_float(bits << 16);
-    const float E = (float)exp(-(double)g);
-    const float t = __fadd_rn(1.0f, E);
-    g_silu_table[idx] = (float)((double)g / (double)t);
-    const float sig = (float)(1.0 / (double)t);
-    const float c = __fsub_rn(1.0f, sig);
-    const float pr = __fmul_rn(g, c);
-    const float q = __fadd_rn(1.0f, pr);
-    g_dsilu_table[idx] = __fmul_rn(sig, q);
-}
-
-static std::mutex g_init_mu;
-static bool g_init_done[64];
-
-// Builds the table on the current device the first time it is needed.  The host
-// waits for it once, so later calls on any stream see a complete table.
-static hipError_t ensure_silu_table(hipStream_t stream)
-{
+    (void)stream;
+    static std::mutex mu;
+    static const float* addr[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lk(g_init_mu);
-    if (g_init_done[dev]) return hipSuccess;
-    silu_table_init_kernel<<<(kTable + 255) / 256, 256, 0, stream>>>();
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return e;
-    g_init_done[dev] = true;
-    return hipSuccess;
-}
-
-hipError_t silu_table(const float** table, hipStream_t stream)
-{
-    static const float* addr[64];
-    hipError_t e = ensure_silu_table(stream);
-    if (e != hipSuccess) return e;
-    int dev = 0;
-    e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lk(g_init_mu);
+    std::lock_guard<std::mutex> lk(mu);
     if (!addr[dev]) {
         void* p = nullptr;
         e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_silu_table));
@@ -468,8 +437,6 @@ __global__ void __launch_bounds__(64) zero_u32_kernel_sw(uint32_t* p)
 hipError_t launch_swiglu_requant(const void* gu, int64_t M, int64_t F, float* absmax_h, int compute_absmax,
                                  uint8_t* hq, uint8_t* hqt, float* inv_scale_h, hipStream_t stream)
 {
-    hipError_t e = ensure_silu_table(stream);
-    if (e != hipSuccess) return e;
     const uint16_t* g = reinterpret_cast<const uint16_t*>(gu);
     const int64_t items = M * ((F + 1023) / 1024);
     int64_t blocks = (items + 3) / 4;
@@ -738,8 +705,6 @@ static void launch_swiglu_bwd_quant(const uint16_t* g, const uint16_t* d, int64_
 hipError_t launch_swiglu_backward(const void* gu, const void* dh, int64_t M, int64_t F, int fmt, float* absmax,
                                   uint8_t* q, uint8_t* qt, float* scale, float* inv_scale, hipStream_t stream)
 {
-    hipError_t e = ensure_silu_table(stream);
-    if (e != hipSuccess) return e;
     const uint16_t* g = reinterpret_cast<const uint16_t*>(gu);
     const uint16_t* d = reinterpret_cast<const uint16_t*>(dh);
     zero_u32_kernel_sw<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax));

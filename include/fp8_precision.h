@@ -20,12 +20,10 @@
  * --------------------------------
  *  - Every pointer argument is a DEVICE pointer owned by the caller.  The
  *    library allocates no device memory for any call and keeps no reference
- *    after the call returns.  It never synchronises the host, with one
- *    exception: the first call on a device that needs the SwiGLU tables
- *    (fp8_swiglu_requant, fp8_swiglu_backward, fp8_gemm_fwd_swiglu_absmax)
- *    builds them in the library's static device memory on its stream and
- *    waits for that stream once, so that later calls on any stream see the
- *    complete tables.  Make that first call outside stream capture.
+ *    after the call returns.  It never synchronises the host.  The SwiGLU
+ *    tables (s_g and its derivative per bf16 gate value) are constant data
+ *    of the library's code object, so every call, the first included, can be
+ *    recorded under stream capture.
  *  - All work is enqueued on `stream` (0 = the null stream).  Inputs must stay
  *    valid until the stream reaches the work.
  *  - absmax, scale and inverse-scale values stay in device memory as fp32

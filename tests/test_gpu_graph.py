@@ -6,9 +6,16 @@ The step: clear a statistics buffer (a fill kernel), X and W statistics in one
 launch, e4m3 quantisation with transposed copies, the forward GEMM, the
 gate/up GEMM with the SwiGLU statistic in its epilogue and the requant that
 uses it, e5m2 quantisation of dY, the paired backward GEMMs, and the SwiGLU
-backward.  The first SwiGLU call on the device (which builds its tables and
-waits for them once) runs before the capture.
+backward.
+
+A second test records a fresh process's very first SwiGLU calls (the SwiGLU
+tables are constant data of the library, so nothing has to run before a
+capture) and checks its replays against eager calls made afterwards.
 """
+import os
+import subprocess
+import sys
+
 import pytest
 import torch
 
@@ -84,3 +91,58 @@ def test_step_replays_in_a_graph(fp8):
         torch.cuda.synchronize()
         for k, v in out.items():
             assert torch.equal(v.view(torch.uint8), ref[k].view(torch.uint8)), f"replay {rep}: {k} differs"
+
+
+FIRST_CALLS_CAPTURED = r"""
+import sys, torch
+import fp8_precision_amd as fp8
+M, K, F = 256, 512, 512
+g = torch.Generator().manual_seed(5)
+gu = (torch.randn(M, 2 * F, generator=g) * 3).to(torch.bfloat16).cuda()
+xq = (torch.randn(M, K, generator=g)).to(torch.float8_e4m3fn).view(torch.uint8).cuda()
+wq = (torch.randn(2 * F, K, generator=g) * 0.5).to(torch.float8_e4m3fn).view(torch.uint8).cuda()
+one = torch.ones(1, dtype=torch.float32, device="cuda")
+outs = lambda: dict(am=torch.zeros(1, dtype=torch.float32, device="cuda"),
+                    hq=torch.empty(M, F, dtype=torch.uint8, device="cuda"),
+                    hqt=torch.empty(F, M, dtype=torch.uint8, device="cuda"),
+                    inv=torch.empty(1, dtype=torch.float32, device="cuda"),
+                    am2=torch.zeros(1, dtype=torch.float32, device="cuda"),
+                    y=torch.empty(M, 2 * F, dtype=torch.bfloat16, device="cuda"))
+def step(o):
+    o["am"].zero_()
+    o["am2"].zero_()
+    fp8.swiglu_requant(gu, absmax_h=o["am"], want_hqt=True, hq=o["hq"], hqt=o["hqt"], inv_scale_h=o["inv"],
+                       accumulate=True)
+    fp8.gemm_fwd_swiglu_absmax(xq, wq, one, one, o["am2"], out=o["y"])
+torch.cuda.synchronize()
+cap = outs()
+graph = torch.cuda.CUDAGraph()
+side = torch.cuda.Stream()
+side.wait_stream(torch.cuda.current_stream())
+with torch.cuda.stream(side):
+    with torch.cuda.graph(graph, stream=side):
+        step(cap)          # the process's first SwiGLU and gate/up-statistic calls
+torch.cuda.current_stream().wait_stream(side)
+torch.cuda.synchronize()
+ref = outs()
+step(ref)
+torch.cuda.synchronize()
+for r in range(3):
+    for t in cap.values():
+        t.fill_(0)
+    graph.replay()
+    torch.cuda.synchronize()
+    for k in cap:
+        if not torch.equal(cap[k].view(torch.uint8), ref[k].view(torch.uint8)):
+            print(f"replay {r}: {k} differs from the eager call"); sys.exit(1)
+print("first calls captured: 3 replays bit-exact")
+"""
+
+
+def test_first_swiglu_calls_of_a_process_capture():
+    say("fresh process: first SwiGLU calls under capture")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", FIRST_CALLS_CAPTURED], cwd=root, capture_output=True, text=True,
+                       timeout=240)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "bit-exact" in r.stdout
