@@ -2,7 +2,7 @@
 """Benchmark of the FP8 training hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input at the
-shapes of one workload configuration (default c3: the 7B-class layer, M = 4096
+shapes of one workload configuration (default layer7b: the 7B-class layer, M = 4096
 tokens, d = 4096, ffn = 11008): for the QKV, O, gate/up and down linears,
 forward and backward --
 
@@ -13,8 +13,8 @@ forward and backward --
   backward: absmax -> quantise dY to e5m2 (+ transposed copy) -> dgrad
             (dY . W) and wgrad (dY^T . X) FP8 GEMMs -> bf16.
 
---workload c4 runs the 14B-class shapes (M = 8192, Student-t activations with
-outlier channels); c5 the 32B-class shapes (M = 16384) with the MLP block
+--workload layer14b runs the 14B-class shapes (M = 8192, Student-t activations with
+outlier channels); layer32b the 32B-class shapes (M = 16384) with the MLP block
 recomputed in the backward from the retained absmax statistics.
 --layout mn runs the same step without the transposed FP8 copies: the
 quantise and SwiGLU calls write only the row-major codes and the backward
@@ -30,7 +30,7 @@ and `streaming`: the bytes-weighted GB/s of those streaming calls in the step,
 the same calls timed one at a time with a cold Infinity Cache, each as % of the
 8 TB/s HBM peak and against a plain copy kernel measured the same way.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c4|c5]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload layer7b|layer14b|layer32b]
                        [--layout copies|mn] [--no-cold] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -108,16 +108,16 @@ class Op:
 
 
 WORKLOADS = {
-    "c3": "7B-class layer (d=4096, ffn=11008, QKV 4096->12288, M=4096 tokens): the four linears fwd+bwd, "
+    "layer7b": "7B-class layer (d=4096, ffn=11008, QKV 4096->12288, M=4096 tokens): the four linears fwd+bwd, "
           "MLP forward chained through the fused SwiGLU requant",
-    "c4": "14B-class layer (d=5120, ffn=13824, QKV 5120->7168, M=8192 tokens): the four linears fwd+bwd, "
+    "layer14b": "14B-class layer (d=5120, ffn=13824, QKV 5120->7168, M=8192 tokens): the four linears fwd+bwd, "
           "Student-t(3) activations with 0.1% outlier channels x50, MLP forward chained through the SwiGLU requant",
-    "c5": "32B-class layer (d=5120, ffn=27648, QKV 5120->7168, M=16384 tokens): the four linears fwd+bwd, "
+    "layer32b": "32B-class layer (d=5120, ffn=27648, QKV 5120->7168, M=16384 tokens): the four linears fwd+bwd, "
           "MLP forward chained; backward recomputes the MLP block from the retained absmax statistics",
 }
 
 
-def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False, fused_absmax_h=False):
+def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, fused_absmax_h=False):
     """Inputs and the ordered list of calls of one layer step of a configuration.
 
     The step starts by clearing its buffer of per-tensor absmax statistics (one
@@ -130,7 +130,7 @@ def build_step(fp8, dev, cfg_name="c3", layout="copies", swiglu_bwd=False, fused
     for QKV, O and gate/up;
     the fused SwiGLU requant of the gate/up output feeds the down linear.
     Backward: absmax + e5m2 quantise of dY, then dgrad and wgrad in one launch.
-    With recomputation (c5) the backward first re-quantises the retained bf16
+    With recomputation (layer32b) the backward first re-quantises the retained bf16
     gate/up input with its retained absmax, reruns the gate/up GEMM and
     requantises the SwiGLU output with the retained absmax_h (no reduction), and
     the forward keeps no transposed copies for the MLP block.
@@ -504,12 +504,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline", action="store_true",
-                    help="also time the oracle for the c4 / c5 workloads (always done for c3 unless disabled)")
+                    help="also time the oracle for the layer14b / layer32b workloads (always done for layer7b unless disabled)")
     ap.add_argument("--layout", choices=("copies", "mn"), default="copies",
                     help="backward GEMM operands: transposed FP8 copies, or the untransposed tensors")
     ap.add_argument("--cpu-gemm-rows", type=int, default=128)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="c3",
-                    help="c3: 7B-class layer (the headline); c4: 14B-class; c5: 32B-class with MLP recomputation")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="layer7b",
+                    help="layer7b: 7B-class layer (the headline); layer14b: 14B-class; layer32b: 32B-class with MLP recomputation")
     ap.add_argument("--fused-swiglu-absmax", action="store_true",
                     help="take the SwiGLU statistic in the gate/up GEMM's epilogue (fp8_gemm_fwd_swiglu_absmax) "
                          "instead of fp8_swiglu_requant's own reduction pass")
@@ -586,7 +586,7 @@ def main():
     copy_gbs, cold = (None, None) if args.no_cold else streaming_cold(fp8, ops, stream, dev)
 
     clock = None if args.no_clock else sustained_clock(ops)
-    want_cpu = not args.no_cpu_baseline and (args.workload == "c3" or args.cpu_baseline)
+    want_cpu = not args.no_cpu_baseline and (args.workload == "layer7b" or args.cpu_baseline)
     cpu = cpu_baseline(ops, args.cpu_gemm_rows) if want_cpu else None
 
     line = {

@@ -98,7 +98,7 @@ def linear_backward(fp8, orc, cfg, li, xqt, inv_x, wqt, inv_w):
 
 # every linear of each configuration, except the down linear of an MLP chain,
 # which consumes the SwiGLU output (covered by test_mlp_chain)
-LINEAR_CASES = [(c, i) for c in ("c1", "c3", "c4", "c5") for i, L in enumerate(workloads.CONFIGS[c].linears)
+LINEAR_CASES = [(c, i) for c in ("fc256", "layer7b", "layer14b", "layer32b") for i, L in enumerate(workloads.CONFIGS[c].linears)
                 if not (workloads.CONFIGS[c].mlp_chain and L.name == "down")]
 
 
@@ -126,7 +126,7 @@ def swiglu_step(fp8, orc, gu, want_hqt, what):
     return hq, hqt, am, inv, hq_h
 
 
-@pytest.mark.parametrize("cname", ["c2", "c5"])
+@pytest.mark.parametrize("cname", ["mlp7b", "layer32b"])
 def test_mlp_chain(fp8, orc, cname):
     """X -> e4m3 -> gate/up GEMM -> fused SwiGLU requant -> down GEMM; for the 32B
     configuration also the down linear's backward, the MLP recomputation, and the

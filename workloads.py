@@ -101,17 +101,17 @@ def _layer(d, ffn, qkv_out):
 
 
 CONFIGS = {
-    "c1": Config("c1", 0, 128, [Linear("fc", 256, 256)], backward=False,
+    "fc256": Config("fc256", 0, 128, [Linear("fc", 256, 256)], backward=False,
                  description="single FP8 linear forward, X [128,256] N(0,1), W [256,256] N(0,0.02)"),
-    "c2": Config("c2", 1, 4096, [Linear("gate_up", 4096, 22016), Linear("down", 11008, 4096)],
+    "mlp7b": Config("mlp7b", 1, 4096, [Linear("gate_up", 4096, 22016), Linear("down", 11008, 4096)],
                  backward=False, mlp_chain=True,
                  description="7B-class SwiGLU MLP forward, M=4096, d=4096, ffn=11008"),
-    "c3": Config("c3", 2, 4096, _layer(4096, 11008, 12288),
+    "layer7b": Config("layer7b", 2, 4096, _layer(4096, 11008, 12288),
                  description="7B-class layer linears forward+backward, M=4096"),
-    "c4": Config("c4", 3, 8192, _layer(5120, 13824, 7168), x_dist="student_t", x_outlier_frac=0.001,
+    "layer14b": Config("layer14b", 3, 8192, _layer(5120, 13824, 7168), x_dist="student_t", x_outlier_frac=0.001,
                  description="14B-class layer linears forward+backward, M=8192, Student-t(3) X with "
                              "0.1% of channels x50"),
-    "c5": Config("c5", 4, 16384, _layer(5120, 27648, 7168), mlp_chain=True, recompute=True,
+    "layer32b": Config("layer32b", 4, 16384, _layer(5120, 27648, 7168), mlp_chain=True, recompute=True,
                  description="32B-class layer linears forward+backward, M=16384, MLP recomputation "
                              "with retained statistics"),
 }
