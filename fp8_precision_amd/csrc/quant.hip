@@ -220,16 +220,18 @@ __global__ void __launch_bounds__(256) quantize_flat_kernel(const uint4* __restr
 
 // ---------------------------------------------------------------------------
 // Quantisation with the transposed copy (and optionally the plain one).  A block
-// of 4 waves owns a 128-row x 256-column tile.  Lane l of wave w converts the
-// 16-byte vectors at columns 8 (l % 32) .. +7 of 16 consecutive rows (row group
-// l / 32 of the wave's 32 rows): every load instruction reads two 512-byte row
-// segments, every q store writes two 256-byte segments.  The lane transposes
-// its 16 x 8 code block in registers (v_perm_b32) into 8 column pieces of 16
-// bytes and parks them in an LDS tile laid out as qt ([256 columns][128 rows],
-// 16-byte pieces XOR-swizzled by column); after a barrier the block writes qt
-// back as full 128-byte row segments.
-constexpr int kQtRows = 128;
-constexpr int kQtCols = 256;
+// of 4 waves owns a 128 x 128 tile.  Lane l of wave w converts the 16-byte
+// vectors of 8 consecutive rows (w * 32 + (l / 16) * 8 ..) at columns
+// 8 (l % 16) .. +7: every load instruction reads four 256-byte row segments,
+// every q store writes four 128-byte segments.  The lane transposes its 8 x 8
+// code block in registers (v_perm_b32) into 8 column pieces of 8 bytes and parks
+// them in an LDS tile laid out as qt ([128 columns][128 rows], 16-byte pieces
+// XOR-swizzled by column); after a barrier the block writes qt back as full
+// 128-byte row segments.  Measured on MI355X against a 128 x 256 tile (16 rows
+// per lane): 4096 x 4096 15.0 -> 14.0 us, 4096 x 11008 36.9 -> 35.1 us, the
+// 7B-layer step's quantisations 318 -> 314 us -- twice the blocks, so a small
+// tensor fills more of each CU and the blocks' load and store phases overlap.
+constexpr int kQtEdge = 128;
 
 template <int FMT, bool NT>
 __global__ void __launch_bounds__(256) quantize_t_kernel(const uint8_t* __restrict__ x, int64_t rows,
@@ -238,7 +240,7 @@ __global__ void __launch_bounds__(256) quantize_t_kernel(const uint8_t* __restri
                                                          float* __restrict__ scale_out,
                                                          float* __restrict__ inv_out)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[kQtCols * kQtRows];    // 32 KB
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kQtEdge * kQtEdge];    // 16 KB
     float s, inv;
     tensor_scale(*absmax, Fmt<FMT>::max, s, inv);
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
@@ -246,57 +248,57 @@ __global__ void __launch_bounds__(256) quantize_t_kernel(const uint8_t* __restri
         if (inv_out) *inv_out = inv;
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t tr = (int64_t)blockIdx.y * kQtRows, tc = (int64_t)blockIdx.x * kQtCols;
-    const int rt = wave * 32 + (lane >> 5) * 16;          // first row of the lane within the tile
-    const int ct = (lane & 31) * 8;                       // first column of the lane within the tile
-    const bool active = tr + rt < rows && tc + ct < cols;
-    if (active) {
+    const int64_t tr = (int64_t)blockIdx.y * kQtEdge, tc = (int64_t)blockIdx.x * kQtEdge;
+    const int rt = wave * 32 + (lane >> 4) * 8;           // first row of the lane within the tile
+    const int ct = (lane & 15) * 8;                       // first column of the lane within the tile
+    // rows and cols are multiples of 16, rt and ct of 8: an active lane's 8 x 8 block is inside
+    if (tr + rt < rows && tc + ct < cols) {
         const int64_t i0 = tr + rt, j = tc + ct;
-        uint4 v[16];
+        uint4 v[8];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 8; ++r) {
             const u32x4* src = reinterpret_cast<const u32x4*>(x + ((i0 + r) * cols + j) * 2);
             const u32x4 w = NT ? __builtin_nontemporal_load(src) : *src;
             v[r] = make_uint4(w.x, w.y, w.z, w.w);
         }
-        uint32_t lo[16], hi[16];
+        uint32_t lo[8], hi[8];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 8; ++r) {
             const uint2 c = quant8<FMT>(v[r], s);
             lo[r] = c.x;
             hi[r] = c.y;
         }
         if (q) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int r = 0; r < 8; ++r)
                 *reinterpret_cast<uint2*>(q + (i0 + r) * cols + j) = make_uint2(lo[r], hi[r]);
         }
-        uint32_t w[8][4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            transpose4x4(lo[4 * g], lo[4 * g + 1], lo[4 * g + 2], lo[4 * g + 3], w[0][g], w[1][g], w[2][g], w[3][g]);
-            transpose4x4(hi[4 * g], hi[4 * g + 1], hi[4 * g + 2], hi[4 * g + 3], w[4][g], w[5][g], w[6][g], w[7][g]);
-        }
-        const int piece = rt >> 4;                        // 16-byte piece of the 128-byte qt row
+        // column k of the block: rows 0..3 (word 0) and rows 4..7 (word 1)
+        uint32_t c0[8], c1[8];
+        transpose4x4(lo[0], lo[1], lo[2], lo[3], c0[0], c0[1], c0[2], c0[3]);
+        transpose4x4(lo[4], lo[5], lo[6], lo[7], c1[0], c1[1], c1[2], c1[3]);
+        transpose4x4(hi[0], hi[1], hi[2], hi[3], c0[4], c0[5], c0[6], c0[7]);
+        transpose4x4(hi[4], hi[5], hi[6], hi[7], c1[4], c1[5], c1[6], c1[7]);
+        const int piece = rt >> 4, half = (rt >> 3) & 1;   // 8-byte half of a 16-byte piece of the qt row
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int col = ct + k;
             const int phys = piece ^ ((col >> 3) & 7);
-            *reinterpret_cast<uint4*>(tile + col * kQtRows + phys * 16) = make_uint4(w[k][0], w[k][1], w[k][2], w[k][3]);
+            *reinterpret_cast<uint2*>(tile + col * kQtEdge + phys * 16 + half * 8) = make_uint2(c0[k], c1[k]);
         }
     }
     __syncthreads();
-    // write-back: 2048 pieces of 16 bytes, 8 per thread; a wave instruction
+    // write-back: 1024 pieces of 16 bytes, 4 per thread; a wave instruction
     // covers 8 qt rows x 128 bytes
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 4; ++u) {
         const int id = u * 256 + threadIdx.x;
         const int col = id >> 3, p = id & 7;
         const int64_t qrow = tc + col, qcol = tr + p * 16;
         if (qrow < cols && qcol < rows) {
             const int phys = p ^ ((col >> 3) & 7);
             *reinterpret_cast<uint4*>(qt + qrow * rows + qcol) =
-                *reinterpret_cast<const uint4*>(tile + col * kQtRows + phys * 16);
+                *reinterpret_cast<const uint4*>(tile + col * kQtEdge + phys * 16);
         }
     }
 }
@@ -308,7 +310,7 @@ static void launch_quantize_fmt(const void* x, int64_t rows, int64_t cols, const
                                 hipStream_t stream)
 {
     if (qt) {
-        dim3 grid((unsigned)((cols + kQtCols - 1) / kQtCols), (unsigned)((rows + kQtRows - 1) / kQtRows));
+        dim3 grid((unsigned)((cols + kQtEdge - 1) / kQtEdge), (unsigned)((rows + kQtEdge - 1) / kQtEdge));
         // a large input is read non-temporally: nothing reads it again, and the
         // Infinity Cache is left to the codes the GEMMs read next
         if (2 * rows * cols >= kAbsStreamBytes)
