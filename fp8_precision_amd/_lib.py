@@ -134,7 +134,9 @@ def absmax_accumulate_many(xs, outs) -> None:
         raise ValueError("1 to 4 tensors, one output each")
     for x in xs:
         _dev_tensor(x, "x", torch.bfloat16)
-    outs = [_scalar(o, "out", xs[0].device) for o in outs]
+    if any(o is None for o in outs):
+        raise ValueError("every output is read and updated: pass a tensor holding +0 or an earlier result")
+    outs = [_scalar_in(o, "out") for o in outs]
     k = len(xs)
     xp = (ctypes.c_void_p * k)(*[_ptr(x) for x in xs])
     ns = (ctypes.c_int64 * k)(*[x.numel() for x in xs])
@@ -275,7 +277,9 @@ def gemm_fwd_swiglu_absmax(xq, wq, inv_sx, inv_sw, absmax_h, out=None) -> torch.
         raise ValueError("xq is [M, K] and wq must be [2F, K]")
     _scalar_in(inv_sx, "inv_sx")
     _scalar_in(inv_sw, "inv_sw")
-    absmax_h = _scalar(absmax_h, "absmax_h", xq.device)
+    if absmax_h is None:
+        raise ValueError("absmax_h is read and updated: pass a tensor holding +0 or an earlier result")
+    _scalar_in(absmax_h, "absmax_h")
     out = _out_bf16(out, (M, N), xq.device)
     _run("fp8_gemm_fwd_swiglu_absmax", _lib.fp8_gemm_fwd_swiglu_absmax, (xq, wq, inv_sx, inv_sw, out, absmax_h),
          _ptr(xq), _ptr(wq), _ptr(inv_sx), _ptr(inv_sw), _ptr(out), _ptr(absmax_h), M, N // 2, K)

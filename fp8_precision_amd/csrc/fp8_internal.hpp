@@ -5,7 +5,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
 namespace fp8k {
+
+// Enqueue kernel<<<grid, block, 0, stream>>>(args...) and return the status of
+// this launch itself, so that an error left behind by unrelated earlier work
+// (which hipGetLastError would report) is never taken for this call's.
+template <typename... P, typename... A>
+inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, A&&... args)
+{
+    static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+    std::tuple<std::decay_t<P>...> vals(std::forward<A>(args)...);
+    void* ptrs[sizeof...(P)];
+    std::apply([&ptrs](auto&... v) {
+        int i = 0;
+        ((ptrs[i++] = static_cast<void*>(&v)), ...);
+    }, vals);
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, stream);
+}
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -852,8 +852,8 @@ static hipError_t launch_group(GemmGroup g, hipStream_t stream)
         if (edge) {
             g.full_units = g.units = total;
             g.first_unit = 0;
-            gemm_tn_kernel<FA, FB, true, SET, false, false><<<total < cus ? total : cus, 256, 0, stream>>>(g);
-            return hipGetLastError();
+            return launch(gemm_tn_kernel<FA, FB, true, SET, false, false>, dim3(total < cus ? total : cus), dim3(256),
+                          stream, g);
         }
     }
     // Balance the last round: when the tiles past the last full round of the
@@ -865,16 +865,19 @@ static hipError_t launch_group(GemmGroup g, hipStream_t stream)
     g.full_units = split ? total - tail : total;
     g.units = g.full_units;
     g.first_unit = 0;
-    if (g.full_units > 0)
-        gemm_tn_kernel<FA, FB, false, SET, false, GU><<<g.full_units < cus ? g.full_units : cus, 256, 0, stream>>>(g);
+    if (g.full_units > 0) {
+        const hipError_t e = launch(gemm_tn_kernel<FA, FB, false, SET, false, GU>,
+                                    dim3(g.full_units < cus ? g.full_units : cus), dim3(256), stream, g);
+        if (e != hipSuccess) return e;
+    }
     if constexpr (SET == kSetKK) {
         if (split) {
             g.first_unit = g.full_units;
             g.units = total + tail;
-            gemm_tn_kernel<FA, FB, false, SET, true, GU><<<2 * tail, 256, 0, stream>>>(g);
+            return launch(gemm_tn_kernel<FA, FB, false, SET, true, GU>, dim3(2 * tail), dim3(256), stream, g);
         }
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 // B is always E4M3 (weights or activations); A is E4M3 or E5M2.  Layout sets:

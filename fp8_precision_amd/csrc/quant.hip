@@ -155,8 +155,7 @@ hipError_t launch_absmax_many(int count, const void* const* x, const int64_t* n,
         if (b < 1) b = 1;
         g.first[i + 1] = g.first[i] + (int)b;
     }
-    absmax_many_kernel<<<(unsigned)g.first[count], kAbsThreads, 0, stream>>>(g);
-    return hipGetLastError();
+    return launch(absmax_many_kernel, dim3((unsigned)g.first[count]), dim3(kAbsThreads), stream, g);
 }
 
 hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, bool accumulate, hipStream_t stream)
@@ -167,15 +166,18 @@ hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, bool accu
     const int64_t cap = (int64_t)device_cu_count();  // one block per CU (one atomic per block)
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
-    if (!accumulate) zero_u32_kernel<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax));
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
     const uint16_t* tail = reinterpret_cast<const uint16_t*>(x) + nvec * 8;
     uint32_t* out = reinterpret_cast<uint32_t*>(absmax);
+    if (!accumulate) {
+        const hipError_t e = launch(zero_u32_kernel, dim3(1), dim3(64), stream, out);
+        if (e != hipSuccess) return e;
+    }
     if (2 * n >= kAbsStreamBytes)
-        absmax_bf16_kernel<true><<<(unsigned)blocks, kAbsThreads, 0, stream>>>(xv, nvec, tail, ntail, out);
-    else
-        absmax_bf16_kernel<false><<<(unsigned)blocks, kAbsThreads, 0, stream>>>(xv, nvec, tail, ntail, out);
-    return hipGetLastError();
+        return launch(absmax_bf16_kernel<true>, dim3((unsigned)blocks), dim3(kAbsThreads), stream, xv, nvec, tail,
+                      ntail, out);
+    return launch(absmax_bf16_kernel<false>, dim3((unsigned)blocks), dim3(kAbsThreads), stream, xv, nvec, tail,
+                  ntail, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -305,7 +307,7 @@ __global__ void __launch_bounds__(256) quantize_t_kernel(const uint8_t* __restri
 
 // Plain quantisation only: the flat kernel above; with qt: the tile kernel.
 template <int FMT>
-static void launch_quantize_fmt(const void* x, int64_t rows, int64_t cols, const float* absmax,
+static hipError_t launch_quantize_fmt(const void* x, int64_t rows, int64_t cols, const float* absmax,
                                 uint8_t* q, uint8_t* qt, float* scale, float* inv_scale,
                                 hipStream_t stream)
 {
@@ -314,11 +316,10 @@ static void launch_quantize_fmt(const void* x, int64_t rows, int64_t cols, const
         // a large input is read non-temporally: nothing reads it again, and the
         // Infinity Cache is left to the codes the GEMMs read next
         if (2 * rows * cols >= kAbsStreamBytes)
-            quantize_t_kernel<FMT, true><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(x), rows, cols,
-                                                                   absmax, q, qt, scale, inv_scale);
-        else
-            quantize_t_kernel<FMT, false><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint8_t*>(x), rows, cols,
-                                                                    absmax, q, qt, scale, inv_scale);
+            return launch(quantize_t_kernel<FMT, true>, grid, dim3(256), stream, reinterpret_cast<const uint8_t*>(x),
+                          rows, cols, absmax, q, qt, scale, inv_scale);
+        return launch(quantize_t_kernel<FMT, false>, grid, dim3(256), stream, reinterpret_cast<const uint8_t*>(x),
+                      rows, cols, absmax, q, qt, scale, inv_scale);
     } else {
         const int64_t nvec = rows * cols / 8;
         const int64_t ntiles = (nvec + 127) / 128;
@@ -326,17 +327,16 @@ static void launch_quantize_fmt(const void* x, int64_t rows, int64_t cols, const
         const int64_t cap = (int64_t)device_cu_count() * 8;
         if (blocks > cap) blocks = cap;
         if (blocks < 1) blocks = 1;
-        quantize_flat_kernel<FMT><<<(unsigned)blocks, 256, 0, stream>>>(
-            reinterpret_cast<const uint4*>(x), nvec, absmax, reinterpret_cast<uint2*>(q), scale, inv_scale);
+        return launch(quantize_flat_kernel<FMT>, dim3((unsigned)blocks), dim3(256), stream,
+                      reinterpret_cast<const uint4*>(x), nvec, absmax, reinterpret_cast<uint2*>(q), scale, inv_scale);
     }
 }
 
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, const float* absmax,
                            uint8_t* q, uint8_t* qt, float* scale, float* inv_scale, hipStream_t stream)
 {
-    if (fmt == 0) launch_quantize_fmt<0>(x, rows, cols, absmax, q, qt, scale, inv_scale, stream);
-    else launch_quantize_fmt<1>(x, rows, cols, absmax, q, qt, scale, inv_scale, stream);
-    return hipGetLastError();
+    if (fmt == 0) return launch_quantize_fmt<0>(x, rows, cols, absmax, q, qt, scale, inv_scale, stream);
+    return launch_quantize_fmt<1>(x, rows, cols, absmax, q, qt, scale, inv_scale, stream);
 }
 
 }  // namespace fp8k

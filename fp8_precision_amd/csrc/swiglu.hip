@@ -1,9 +1,9 @@
 // swiglu.hip -- SwiGLU fused with its E4M3 requantisation, for gfx950.
 //
 // "LLMQ: Efficient Lower-Precision Pretraining for Consumer GPUs", section 3.1:
-// the block input and the absmax statistics are retained, so during
-// recomputation the quantisation fuses with the nonlinearity and no second
-// global reduction is needed.
+// the block input and the forward's absmax statistic are kept, so the
+// recomputed SwiGLU output is requantised in the kernel that evaluates it,
+// with no second pass to find its maximum.
 //
 // h = RN32(s_g * u), s_g = RN32(g / RN32(1 + RN32(e^-g))) with e^-g correctly
 // rounded.  g is a bf16 value, so s_g is a function of 16 bits.  It is read
@@ -445,22 +445,27 @@ hipError_t launch_swiglu_requant(const void* gu, int64_t M, int64_t F, float* ab
     if (blocks < 1) blocks = 1;
     if (compute_absmax) {
         // 1: reset first; 2: accumulate into the caller's (cleared) statistic
-        if (compute_absmax == 1) zero_u32_kernel_sw<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax_h));
+        hipError_t e = hipSuccess;
+        if (compute_absmax == 1)
+            e = launch(zero_u32_kernel_sw, dim3(1), dim3(64), stream, reinterpret_cast<uint32_t*>(absmax_h));
+        if (e != hipSuccess) return e;
         // one 1024-thread block per CU: one atomic per CU, the table copied once per CU
         int64_t ablocks = (items + 15) / 16;
         if (ablocks > device_cu_count()) ablocks = device_cu_count();
-        swiglu_absmax_kernel<<<(unsigned)ablocks, 1024, 0, stream>>>(g, M, F, reinterpret_cast<uint32_t*>(absmax_h));
+        e = launch(swiglu_absmax_kernel, dim3((unsigned)ablocks), dim3(1024), stream, g, M, F,
+                   reinterpret_cast<uint32_t*>(absmax_h));
+        if (e != hipSuccess) return e;
     }
     if (hqt) {
         // three resident blocks per CU (50 KB of LDS each), persistent over the tiles
         const int64_t tiles = ((F + kSqEdge - 1) / kSqEdge) * ((M + kSqEdge - 1) / kSqEdge);
         int64_t tblocks = tiles;
         if (tblocks > 3 * (int64_t)device_cu_count()) tblocks = 3 * (int64_t)device_cu_count();
-        swiglu_quant_t_kernel<<<(unsigned)tblocks, 256, 0, stream>>>(g, M, F, absmax_h, hq, hqt, inv_scale_h);
-    } else {
-        swiglu_quant_kernel<<<(unsigned)blocks, 256, 0, stream>>>(g, M, F, absmax_h, hq, inv_scale_h);
+        return launch(swiglu_quant_t_kernel, dim3((unsigned)tblocks), dim3(256), stream, g, M, F, absmax_h, hq, hqt,
+                      inv_scale_h);
     }
-    return hipGetLastError();
+    return launch(swiglu_quant_kernel, dim3((unsigned)blocks), dim3(256), stream, g, M, F, absmax_h, hq,
+                  inv_scale_h);
 }
 
 // ---------------------------------------------------------------------------
@@ -681,7 +686,7 @@ __global__ void __launch_bounds__(512) swiglu_bwd_quant_t_kernel(const uint16_t*
 }
 
 template <int FMT>
-static void launch_swiglu_bwd_quant(const uint16_t* g, const uint16_t* d, int64_t M, int64_t F, float* absmax,
+static hipError_t launch_swiglu_bwd_quant(const uint16_t* g, const uint16_t* d, int64_t M, int64_t F, float* absmax,
                                     uint8_t* q, uint8_t* qt, float* scale, float* inv_scale, hipStream_t stream)
 {
     // two resident blocks per CU (2 x 34 KB tables each), persistent
@@ -691,14 +696,15 @@ static void launch_swiglu_bwd_quant(const uint16_t* g, const uint16_t* d, int64_
         const int64_t tiles = ((F + kSqEdge - 1) / kSqEdge) * ((M + kSqEdge - 1) / kSqEdge);
         int64_t blocks = (tiles + 1) / 2;
         if (blocks > (int64_t)device_cu_count()) blocks = device_cu_count();
-        swiglu_bwd_quant_t_kernel<FMT><<<(unsigned)blocks, 512, 0, stream>>>(g, d, M, F, absmax, q, qt, scale,
-                                                                             inv_scale);
+        return launch(swiglu_bwd_quant_t_kernel<FMT>, dim3((unsigned)blocks), dim3(512), stream, g, d, M, F, absmax,
+                      q, qt, scale, inv_scale);
     } else {
         const int64_t items = M * ((F + 1023) / 1024);
         int64_t blocks = (items + 3) / 4;
         if (blocks > cap) blocks = cap;
         if (blocks < 1) blocks = 1;
-        swiglu_bwd_quant_kernel<FMT><<<(unsigned)blocks, 256, 0, stream>>>(g, d, M, F, absmax, q, scale, inv_scale);
+        return launch(swiglu_bwd_quant_kernel<FMT>, dim3((unsigned)blocks), dim3(256), stream, g, d, M, F, absmax,
+                      q, scale, inv_scale);
     }
 }
 
@@ -707,14 +713,16 @@ hipError_t launch_swiglu_backward(const void* gu, const void* dh, int64_t M, int
 {
     const uint16_t* g = reinterpret_cast<const uint16_t*>(gu);
     const uint16_t* d = reinterpret_cast<const uint16_t*>(dh);
-    zero_u32_kernel_sw<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t*>(absmax));
+    hipError_t e = launch(zero_u32_kernel_sw, dim3(1), dim3(64), stream, reinterpret_cast<uint32_t*>(absmax));
+    if (e != hipSuccess) return e;
     const int64_t items = M * ((F + 1023) / 1024);
     int64_t ablocks = (items + 15) / 16;
     if (ablocks > device_cu_count()) ablocks = device_cu_count();
-    swiglu_bwd_absmax_kernel<<<(unsigned)ablocks, 1024, 0, stream>>>(g, d, M, F, reinterpret_cast<uint32_t*>(absmax));
-    if (fmt == 0) launch_swiglu_bwd_quant<0>(g, d, M, F, absmax, q, qt, scale, inv_scale, stream);
-    else launch_swiglu_bwd_quant<1>(g, d, M, F, absmax, q, qt, scale, inv_scale, stream);
-    return hipGetLastError();
+    e = launch(swiglu_bwd_absmax_kernel, dim3((unsigned)ablocks), dim3(1024), stream, g, d, M, F,
+               reinterpret_cast<uint32_t*>(absmax));
+    if (e != hipSuccess) return e;
+    if (fmt == 0) return launch_swiglu_bwd_quant<0>(g, d, M, F, absmax, q, qt, scale, inv_scale, stream);
+    return launch_swiglu_bwd_quant<1>(g, d, M, F, absmax, q, qt, scale, inv_scale, stream);
 }
 
 }  // namespace fp8k

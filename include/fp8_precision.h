@@ -150,9 +150,9 @@ fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt,
  *   fp8_absmax_accumulate), and quantisation uses that value.
  * compute_absmax = 0 (recomputation): *absmax_h is the retained statistic and
  * is only read; no global reduction runs, and the bytes equal the forward's
- * for the same gu (LLMQ summary, section 3.1: keeping absmax statistics
- * avoids another global reduction and lets quantisation fuse with the
- * nonlinearity during recomputation).
+ * for the same gu (LLMQ summary, section 3.1: the forward's statistic is
+ * reused, so the recomputed SwiGLU output is requantised in the pass that
+ * evaluates it and the tensor is never reduced a second time).
  *
  *   gu           bf16 [M, 2F]
  *   absmax_h     fp32 scalar (written when compute_absmax = 1, updated when 2, read when 0)

@@ -10,9 +10,9 @@
  *
  *   Sources.  "LLMQ: Efficient Lower-Precision Pretraining for Consumer GPUs"
  *   (paperlayer.ai summary of arXiv 2512.15306): section 1 (FP8 training with
- *   dynamic tensor-level scaling), section 3.1 (retained absmax statistics let
- *   the requantisation fuse with the nonlinearity during recomputation, with no
- *   second global reduction), section 4 (dynamic quantisation and
+ *   dynamic tensor-level scaling), section 3.1 (the forward's absmax statistic
+ *   is kept, so the recomputed SwiGLU output is requantised in the same pass
+ *   that evaluates it and is not reduced again), section 4 (dynamic quantisation and
  *   backward-pass transposes are overhead; extra transpose and quantisation
  *   buffers), section 5 / Figure 2 (E4M3 forward and backward versus E5M2
  *   activation gradients).  "FastML periodic report" (EU CORDIS), the item on
