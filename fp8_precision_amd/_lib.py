@@ -31,6 +31,7 @@ _SIGS = {
     "fp8_absmax_accumulate": (_i32, [_vp, _i64, _vp, _vp]),
     "fp8_absmax_accumulate_many": (_i32, [ctypes.c_int, _vp, _vp, _vp, _vp]),
     "fp8_quantize": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "fp8_quantize_many": (_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp8_swiglu_requant": (_i32, [_vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp]),
     "fp8_swiglu_backward": (_i32, [_vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp8_gemm_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
@@ -128,10 +129,10 @@ def absmax(x: torch.Tensor, out: torch.Tensor | None = None, accumulate: bool = 
 
 
 def absmax_accumulate_many(xs, outs) -> None:
-    """Running absmax of up to 4 bf16 tensors in one launch: outs[i] (fp32 [1]
+    """Running absmax of up to 8 bf16 tensors in one launch: outs[i] (fp32 [1]
     device tensors, +0 or an earlier result) become max(outs[i], max |xs[i]|)."""
-    if len(xs) != len(outs) or not 1 <= len(xs) <= 4:
-        raise ValueError("1 to 4 tensors, one output each")
+    if len(xs) != len(outs) or not 1 <= len(xs) <= 8:
+        raise ValueError("1 to 8 tensors, one output each")
     for x in xs:
         _dev_tensor(x, "x", torch.bfloat16)
     if any(o is None for o in outs):
@@ -172,6 +173,55 @@ def quantize(x: torch.Tensor, fmt: int, amax: torch.Tensor, want_q: bool = True,
     _run("fp8_quantize", _lib.fp8_quantize, (x, amax, q, qt, scale, inv_scale),
          _ptr(x), rows, cols, int(fmt), _ptr(amax), _ptr(q), _ptr(qt), _ptr(scale), _ptr(inv_scale))
     return q, qt, scale, inv_scale
+
+
+def quantize_many(xs, fmts, amaxs, want_q=True, want_qt=False, qs=None, qts=None, scales=None, inv_scales=None):
+    """Quantise up to 8 2-D bf16 tensors in one launch, each exactly as ``quantize``.
+
+    ``fmts``, ``amaxs``, ``want_q``, ``want_qt`` and the optional output lists
+    are per tensor (a single bool applies to all).  Returns lists
+    (qs, qts, scales, inv_scales), None where an output was not asked for.
+    """
+    k = len(xs)
+    if not 1 <= k <= 8:
+        raise ValueError("1 to 8 tensors")
+    per = lambda v: list(v) if isinstance(v, (list, tuple)) else [v] * k
+    fmts, amaxs, want_q, want_qt = per(fmts), per(amaxs), per(want_q), per(want_qt)
+    qs, qts = per(qs) if qs is not None else [None] * k, per(qts) if qts is not None else [None] * k
+    scales = per(scales) if scales is not None else [None] * k
+    inv_scales = per(inv_scales) if inv_scales is not None else [None] * k
+    if any(len(v) != k for v in (fmts, amaxs, want_q, want_qt, qs, qts, scales, inv_scales)):
+        raise ValueError("one entry per tensor")
+    rows, cols = [], []
+    for i, x in enumerate(xs):
+        _dev_tensor(x, "x", torch.bfloat16)
+        if x.dim() != 2:
+            raise ValueError("every x must be 2-D")
+        r, c = x.shape
+        rows.append(r)
+        cols.append(c)
+        _scalar_in(amaxs[i], "amax")
+        if want_q[i] and qs[i] is None:
+            qs[i] = torch.empty((r, c), dtype=torch.uint8, device=x.device)
+        if want_qt[i] and qts[i] is None:
+            qts[i] = torch.empty((c, r), dtype=torch.uint8, device=x.device)
+        for t, n in ((qs[i], "q"), (qts[i], "qt")):
+            if t is not None:
+                _dev_tensor(t, n, torch.uint8)
+                if t.numel() != r * c:
+                    raise ValueError(f"{n} has the wrong size")
+        scales[i] = _scalar(scales[i], "scale", x.device)
+        inv_scales[i] = _scalar(inv_scales[i], "inv_scale", x.device)
+    arr = lambda ts: (ctypes.c_void_p * k)(*[_ptr(t) for t in ts])
+    xa, aa, qa, qta, sa, ia = arr(xs), arr(amaxs), arr(qs), arr(qts), arr(scales), arr(inv_scales)
+    ra, ca = (ctypes.c_int64 * k)(*rows), (ctypes.c_int64 * k)(*cols)
+    fa = (ctypes.c_int * k)(*[int(f) for f in fmts])
+    _run("fp8_quantize_many", _lib.fp8_quantize_many,
+         list(xs) + list(amaxs) + qs + qts + scales + inv_scales,
+         k, ctypes.cast(xa, _vp), ctypes.cast(ra, _vp), ctypes.cast(ca, _vp), ctypes.cast(fa, _vp),
+         ctypes.cast(aa, _vp), ctypes.cast(qa, _vp), ctypes.cast(qta, _vp), ctypes.cast(sa, _vp),
+         ctypes.cast(ia, _vp))
+    return qs, qts, scales, inv_scales
 
 
 def swiglu_requant(gu: torch.Tensor, absmax_h: torch.Tensor | None = None, compute_absmax: bool = True,

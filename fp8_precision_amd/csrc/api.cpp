@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "fp8_internal.hpp"
 
@@ -135,7 +136,7 @@ fp8_status fp8_absmax_accumulate_many(int count, const void* const* x, const int
     const char* name = "fp8_absmax_accumulate_many";
     if (!x || !n || !absmax) return fail(FP8_ERR_INVALID, "fp8_absmax_accumulate_many: null array");
     if (count < 1 || count > fp8k::kMaxAbsTensors)
-        return fail(FP8_ERR_INVALID, "fp8_absmax_accumulate_many: count must be in [1, 4]");
+        return fail(FP8_ERR_INVALID, "fp8_absmax_accumulate_many: count must be in [1, 8]");
     for (int i = 0; i < count; ++i) {
         if (!x[i] || !absmax[i]) return fail(FP8_ERR_INVALID, "fp8_absmax_accumulate_many: null pointer");
         if (n[i] <= 0 || n[i] > kMaxElems)
@@ -173,6 +174,52 @@ fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt, 
         return fail(FP8_ERR_UNSUPPORTED, "fp8_quantize: misaligned pointer");
     hipError_t e = fp8k::launch_quantize(x, rows, cols, (int)fmt, absmax, q, qt, scale, inv_scale, stream);
     if (e != hipSuccess) return fail_hip("fp8_quantize", e);
+    return FP8_OK;
+}
+
+fp8_status fp8_quantize_many(int count, const void* const* x, const int64_t* rows, const int64_t* cols,
+                             const fp8_fmt* fmt, const float* const* absmax, uint8_t* const* q, uint8_t* const* qt,
+                             float* const* scale, float* const* inv_scale, hipStream_t stream)
+{
+    t_last_error.clear();
+    const std::string f("fp8_quantize_many");
+    if (!x || !rows || !cols || !fmt || !absmax || !q || !qt || !scale || !inv_scale)
+        return fail(FP8_ERR_INVALID, f + ": null array");
+    if (count < 1 || count > fp8k::kMaxQuantTensors) return fail(FP8_ERR_INVALID, f + ": count must be in [1, 8]");
+    std::vector<Range> in, out;
+    int64_t tiles = 0;
+    int fm[fp8k::kMaxQuantTensors];
+    for (int i = 0; i < count; ++i) {
+        const std::string t = f + ": tensor " + std::to_string(i);
+        if (!x[i] || !absmax[i]) return fail(FP8_ERR_INVALID, t + ": null x or absmax");
+        if (!q[i] && !qt[i]) return fail(FP8_ERR_INVALID, t + ": at least one of q, qt is required");
+        if (fmt[i] != FP8_E4M3 && fmt[i] != FP8_E5M2) return fail(FP8_ERR_INVALID, t + ": bad format");
+        if (!mul_ok(rows[i], cols[i], kMaxElems)) return fail(FP8_ERR_INVALID, t + ": bad shape");
+        if (rows[i] % 16 || cols[i] % 16)
+            return fail(FP8_ERR_UNSUPPORTED, t + ": rows and cols must be multiples of 16");
+        if (!aligned(x[i], 16) || (q[i] && !aligned(q[i], 16)) || (qt[i] && !aligned(qt[i], 16)) ||
+            !aligned(absmax[i], 4) || (scale[i] && !aligned(scale[i], 4)) || (inv_scale[i] && !aligned(inv_scale[i], 4)))
+            return fail(FP8_ERR_UNSUPPORTED, t + ": misaligned pointer");
+        const int64_t n = rows[i] * cols[i];
+        tiles += ((rows[i] + 127) / 128) * ((cols[i] + 127) / 128);
+        in.push_back({x[i], 2 * n});
+        in.push_back({absmax[i], 4});
+        out.push_back({q[i], q[i] ? n : 0});
+        out.push_back({qt[i], qt[i] ? n : 0});
+        out.push_back({scale[i], scale[i] ? 4 : 0});
+        out.push_back({inv_scale[i], inv_scale[i] ? 4 : 0});
+        fm[i] = (int)fmt[i];
+    }
+    if (tiles > 0x7FFFFFFF) return fail(FP8_ERR_UNSUPPORTED, f + ": too many tiles for one launch");
+    // inputs may be shared (they are only read); no output may overlap an input or another output
+    for (size_t a = 0; a < out.size(); ++a) {
+        for (size_t b = a + 1; b < out.size(); ++b)
+            if (overlap(out[a].p, out[a].n, out[b].p, out[b].n)) return fail(FP8_ERR_INVALID, f + ": overlapping outputs");
+        for (const Range& r : in)
+            if (overlap(out[a].p, out[a].n, r.p, r.n)) return fail(FP8_ERR_INVALID, f + ": an output overlaps an input");
+    }
+    hipError_t e = fp8k::launch_quantize_many(count, x, rows, cols, fm, absmax, q, qt, scale, inv_scale, stream);
+    if (e != hipSuccess) return fail_hip("fp8_quantize_many", e);
     return FP8_OK;
 }
 

@@ -41,13 +41,20 @@ hipError_t silu_table(const float** table, hipStream_t stream);
 hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, bool accumulate, hipStream_t stream);
 
 // Running absmax of up to kMaxAbsTensors tensors in one launch (no reset).
-constexpr int kMaxAbsTensors = 4;
+constexpr int kMaxAbsTensors = 8;
 hipError_t launch_absmax_many(int count, const void* const* x, const int64_t* n, float* const* absmax,
                               hipStream_t stream);
 
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, const float* absmax,
                            uint8_t* q, uint8_t* qt, float* scale, float* inv_scale,
                            hipStream_t stream);
+
+// Quantisation of up to kMaxQuantTensors tensors in one launch (the tile form,
+// q and / or qt per tensor); the arrays are host arrays of count entries.
+constexpr int kMaxQuantTensors = 8;
+hipError_t launch_quantize_many(int count, const void* const* x, const int64_t* rows, const int64_t* cols,
+                                const int* fmt, const float* const* absmax, uint8_t* const* q, uint8_t* const* qt,
+                                float* const* scale, float* const* inv_scale, hipStream_t stream);
 
 hipError_t launch_swiglu_requant(const void* gu, int64_t M, int64_t F, float* absmax_h,
                                  int compute_absmax, uint8_t* hq, uint8_t* hqt,

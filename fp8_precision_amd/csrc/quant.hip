@@ -235,22 +235,15 @@ __global__ void __launch_bounds__(256) quantize_flat_kernel(const uint4* __restr
 // tensor fills more of each CU and the blocks' load and store phases overlap.
 constexpr int kQtEdge = 128;
 
+// The 128 x 128 tile with origin (tr, tc) of one tensor: q (if given) and qt
+// (if given; with qt == nullptr the LDS tile and its barrier are skipped, a
+// uniform choice per tensor).
 template <int FMT, bool NT>
-__global__ void __launch_bounds__(256) quantize_t_kernel(const uint8_t* __restrict__ x, int64_t rows,
-                                                         int64_t cols, const float* __restrict__ absmax,
-                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ qt,
-                                                         float* __restrict__ scale_out,
-                                                         float* __restrict__ inv_out)
+__device__ __forceinline__ void quantize_tile(const uint8_t* __restrict__ x, int64_t rows, int64_t cols, float s,
+                                              uint8_t* __restrict__ q, uint8_t* __restrict__ qt, int64_t tr,
+                                              int64_t tc, uint8_t* tile)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[kQtEdge * kQtEdge];    // 16 KB
-    float s, inv;
-    tensor_scale(*absmax, Fmt<FMT>::max, s, inv);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-        if (scale_out) *scale_out = s;
-        if (inv_out) *inv_out = inv;
-    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t tr = (int64_t)blockIdx.y * kQtEdge, tc = (int64_t)blockIdx.x * kQtEdge;
     const int rt = wave * 32 + (lane >> 4) * 8;           // first row of the lane within the tile
     const int ct = (lane & 15) * 8;                       // first column of the lane within the tile
     // rows and cols are multiples of 16, rt and ct of 8: an active lane's 8 x 8 block is inside
@@ -275,20 +268,23 @@ __global__ void __launch_bounds__(256) quantize_t_kernel(const uint8_t* __restri
             for (int r = 0; r < 8; ++r)
                 *reinterpret_cast<uint2*>(q + (i0 + r) * cols + j) = make_uint2(lo[r], hi[r]);
         }
-        // column k of the block: rows 0..3 (word 0) and rows 4..7 (word 1)
-        uint32_t c0[8], c1[8];
-        transpose4x4(lo[0], lo[1], lo[2], lo[3], c0[0], c0[1], c0[2], c0[3]);
-        transpose4x4(lo[4], lo[5], lo[6], lo[7], c1[0], c1[1], c1[2], c1[3]);
-        transpose4x4(hi[0], hi[1], hi[2], hi[3], c0[4], c0[5], c0[6], c0[7]);
-        transpose4x4(hi[4], hi[5], hi[6], hi[7], c1[4], c1[5], c1[6], c1[7]);
-        const int piece = rt >> 4, half = (rt >> 3) & 1;   // 8-byte half of a 16-byte piece of the qt row
+        if (qt) {
+            // column k of the block: rows 0..3 (word 0) and rows 4..7 (word 1)
+            uint32_t c0[8], c1[8];
+            transpose4x4(lo[0], lo[1], lo[2], lo[3], c0[0], c0[1], c0[2], c0[3]);
+            transpose4x4(lo[4], lo[5], lo[6], lo[7], c1[0], c1[1], c1[2], c1[3]);
+            transpose4x4(hi[0], hi[1], hi[2], hi[3], c0[4], c0[5], c0[6], c0[7]);
+            transpose4x4(hi[4], hi[5], hi[6], hi[7], c1[4], c1[5], c1[6], c1[7]);
+            const int piece = rt >> 4, half = (rt >> 3) & 1;   // 8-byte half of a 16-byte piece of the qt row
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int col = ct + k;
-            const int phys = piece ^ ((col >> 3) & 7);
-            *reinterpret_cast<uint2*>(tile + col * kQtEdge + phys * 16 + half * 8) = make_uint2(c0[k], c1[k]);
+            for (int k = 0; k < 8; ++k) {
+                const int col = ct + k;
+                const int phys = piece ^ ((col >> 3) & 7);
+                *reinterpret_cast<uint2*>(tile + col * kQtEdge + phys * 16 + half * 8) = make_uint2(c0[k], c1[k]);
+            }
         }
     }
+    if (!qt) return;
     __syncthreads();
     // write-back: 1024 pieces of 16 bytes, 4 per thread; a wave instruction
     // covers 8 qt rows x 128 bytes
@@ -303,6 +299,99 @@ __global__ void __launch_bounds__(256) quantize_t_kernel(const uint8_t* __restri
                 *reinterpret_cast<const uint4*>(tile + col * kQtEdge + phys * 16);
         }
     }
+}
+
+template <int FMT, bool NT>
+__global__ void __launch_bounds__(256) quantize_t_kernel(const uint8_t* __restrict__ x, int64_t rows,
+                                                         int64_t cols, const float* __restrict__ absmax,
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ qt,
+                                                         float* __restrict__ scale_out,
+                                                         float* __restrict__ inv_out)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kQtEdge * kQtEdge];    // 16 KB
+    float s, inv;
+    tensor_scale(*absmax, Fmt<FMT>::max, s, inv);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        if (scale_out) *scale_out = s;
+        if (inv_out) *inv_out = inv;
+    }
+    quantize_tile<FMT, NT>(x, rows, cols, s, q, qt, (int64_t)blockIdx.y * kQtEdge, (int64_t)blockIdx.x * kQtEdge,
+                           tile);
+}
+
+// Several tensors in one launch (each exactly as its own fp8_quantize call with
+// the tile kernel): the blocks first[i] .. first[i + 1] - 1 are the 128 x 128
+// tiles of tensor i, column tile fastest, as the grid of the single-tensor
+// launch orders them.  The format and the load form are per tensor (uniform
+// within a block).
+struct QuantGroup {
+    const uint8_t* x[kMaxQuantTensors];
+    const float* absmax[kMaxQuantTensors];
+    uint8_t* q[kMaxQuantTensors];
+    uint8_t* qt[kMaxQuantTensors];
+    float* scale[kMaxQuantTensors];
+    float* inv[kMaxQuantTensors];
+    int64_t rows[kMaxQuantTensors];
+    int64_t cols[kMaxQuantTensors];
+    int tiles_c[kMaxQuantTensors];
+    int fmt[kMaxQuantTensors];
+    int nt[kMaxQuantTensors];
+    int first[kMaxQuantTensors + 1];
+    int count;
+};
+
+template <int FMT>
+__device__ __forceinline__ void quantize_group_tile(const QuantGroup& g, int i, int64_t tr, int64_t tc, uint8_t* tile)
+{
+    float s, inv;
+    tensor_scale(*g.absmax[i], Fmt<FMT>::max, s, inv);
+    if (tr == 0 && tc == 0 && threadIdx.x == 0) {
+        if (g.scale[i]) *g.scale[i] = s;
+        if (g.inv[i]) *g.inv[i] = inv;
+    }
+    if (g.nt[i])
+        quantize_tile<FMT, true>(g.x[i], g.rows[i], g.cols[i], s, g.q[i], g.qt[i], tr, tc, tile);
+    else
+        quantize_tile<FMT, false>(g.x[i], g.rows[i], g.cols[i], s, g.q[i], g.qt[i], tr, tc, tile);
+}
+
+__global__ void __launch_bounds__(256) quantize_many_kernel(const QuantGroup g)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kQtEdge * kQtEdge];    // 16 KB
+    int i = 0;
+    while (i + 1 < g.count && (int)blockIdx.x >= g.first[i + 1]) ++i;
+    const int t = blockIdx.x - g.first[i];
+    const int64_t tr = (int64_t)(t / g.tiles_c[i]) * kQtEdge, tc = (int64_t)(t % g.tiles_c[i]) * kQtEdge;
+    if (g.fmt[i] == 0)
+        quantize_group_tile<0>(g, i, tr, tc, tile);
+    else
+        quantize_group_tile<1>(g, i, tr, tc, tile);
+}
+
+hipError_t launch_quantize_many(int count, const void* const* x, const int64_t* rows, const int64_t* cols,
+                                const int* fmt, const float* const* absmax, uint8_t* const* q, uint8_t* const* qt,
+                                float* const* scale, float* const* inv_scale, hipStream_t stream)
+{
+    QuantGroup g;
+    g.count = count;
+    g.first[0] = 0;
+    for (int i = 0; i < count; ++i) {
+        g.x[i] = reinterpret_cast<const uint8_t*>(x[i]);
+        g.absmax[i] = absmax[i];
+        g.q[i] = q[i];
+        g.qt[i] = qt[i];
+        g.scale[i] = scale[i];
+        g.inv[i] = inv_scale[i];
+        g.rows[i] = rows[i];
+        g.cols[i] = cols[i];
+        g.fmt[i] = fmt[i];
+        // as the single-tensor launch: inputs of 64 MiB or more are read non-temporally
+        g.nt[i] = 2 * rows[i] * cols[i] >= kAbsStreamBytes;
+        g.tiles_c[i] = (int)((cols[i] + kQtEdge - 1) / kQtEdge);
+        const int64_t tiles = (int64_t)g.tiles_c[i] * ((rows[i] + kQtEdge - 1) / kQtEdge);
+        g.first[i + 1] = g.first[i] + (int)tiles;
+    }
+    return launch(quantize_many_kernel, dim3((unsigned)g.first[count]), dim3(256), stream, g);
 }
 
 // Plain quantisation only: the flat kernel above; with qt: the tile kernel.

@@ -106,7 +106,7 @@ fp8_status fp8_absmax_accumulate(const void* x, int64_t n, float* absmax, hipStr
  * (LLMQ summary, section 1: every operand of an FP8 product gets its own
  * just-in-time statistic).
  *
- *   count      1 .. 4
+ *   count      1 .. 8
  *   x, n       host arrays of count bf16 device pointers (16-byte aligned) and
  *              element counts (>= 1); read during the call
  *   absmax     host array of count device fp32 pointers (read and updated; each
@@ -136,6 +136,31 @@ fp8_status fp8_absmax_accumulate_many(int count, const void* const* x, const int
 fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt,
                         const float* absmax, uint8_t* q, uint8_t* qt,
                         float* scale, float* inv_scale, hipStream_t stream);
+
+/*
+ * Several quantisations in one launch: for i < count, exactly the bytes of
+ *   fp8_quantize(x[i], rows[i], cols[i], fmt[i], absmax[i], q[i], qt[i],
+ *                scale[i], inv_scale[i], stream)
+ * (same scale, codes and transposed copy), with the fixed cost of a launch
+ * paid once -- for tensors that are ready together, such as the weights of a
+ * layer and its input at the start of a step (LLMQ summary, section 1: every
+ * operand gets its own just-in-time scale; section 4: the quantisation passes
+ * and transposes are overhead of FP8 training).
+ *
+ *   count              1 .. 8
+ *   x, rows, cols, fmt, absmax, q, qt, scale, inv_scale
+ *                      host arrays of count entries, read during the call: the
+ *                      device pointers and sizes of each tensor, as for
+ *                      fp8_quantize (q[i] or qt[i] may be NULL, not both;
+ *                      scale[i] and inv_scale[i] may be NULL)
+ * Constraints: every rows[i] and cols[i] a multiple of 16.  Inputs (x, absmax)
+ * may be shared between entries; no output may overlap an input or another
+ * output.
+ */
+fp8_status fp8_quantize_many(int count, const void* const* x, const int64_t* rows, const int64_t* cols,
+                             const fp8_fmt* fmt, const float* const* absmax, uint8_t* const* q,
+                             uint8_t* const* qt, float* const* scale, float* const* inv_scale,
+                             hipStream_t stream);
 
 /*
  * SwiGLU fused with its E4M3 requantisation.  gu = [gate | up] is the bf16

@@ -46,7 +46,7 @@ def test_header_declares_the_hot_path():
     names = declared_functions()
     for want in ("fp8_absmax", "fp8_absmax_accumulate", "fp8_absmax_accumulate_many", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd", "fp8_gemm_dgrad",
                  "fp8_gemm_wgrad", "fp8_gemm_fwd_swiglu_absmax", "fp8_gemm_backward", "fp8_gemm_dgrad_mn", "fp8_gemm_wgrad_mn",
-                 "fp8_gemm_backward_mn", "fp8_swiglu_backward", "fp8_status_string", "fp8_last_error"):
+                 "fp8_gemm_backward_mn", "fp8_swiglu_backward", "fp8_quantize_many", "fp8_status_string", "fp8_last_error"):
         assert want in names
 
 
@@ -288,7 +288,7 @@ def test_absmax_accumulate_many_validation(lib):
 
     assert f(1, None, None, None, None) == INVALID
     assert call([A16, B16], [16, 16], [C16, C16 + 4], count=0) == INVALID
-    assert call([A16, B16], [16, 16], [C16, C16 + 4], count=5) == INVALID
+    assert call([A16, B16], [16, 16], [C16, C16 + 4], count=9) == INVALID
     assert call([A16, None], [16, 16], [C16, C16 + 4]) == INVALID
     assert call([A16, B16], [16, 16], [C16, None]) == INVALID
     assert call([A16, B16], [16, 0], [C16, C16 + 4]) == INVALID
@@ -296,3 +296,34 @@ def test_absmax_accumulate_many_validation(lib):
     assert b"overlaps" in lib.fp8_last_error()
     assert call([A16, B16 + 2], [16, 16], [C16, C16 + 4]) == UNSUPPORTED
     assert call([A16, B16], [16, 16], [C16, C16 + 2]) == UNSUPPORTED
+
+
+def test_quantize_many_validation(lib):
+    f = lib.fp8_quantize_many
+    f.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+
+    def call(xs, rows, cols, fmts, ams, qs, qts, count=None):
+        k = len(xs)
+        P = lambda v: ctypes.cast((ctypes.c_void_p * k)(*v), vp)
+        I = lambda v: ctypes.cast((ctypes.c_int64 * k)(*v), vp)
+        F = lambda v: ctypes.cast((ctypes.c_int * k)(*v), vp)
+        return f(k if count is None else count, P(xs), I(rows), I(cols), F(fmts), P(ams), P(qs), P(qts),
+                 P([None] * k), P([None] * k), None)
+
+    ok = dict(xs=[A16, B16], rows=[16, 16], cols=[16, 32], fmts=[0, 1], ams=[C16, C16 + 4], qs=[D16, D16 + 256],
+              qts=[E16, None])
+    assert f(1, None, None, None, None, None, None, None, None, None, None) == INVALID
+    assert call(**ok, count=0) == INVALID
+    assert call(**ok, count=9) == INVALID
+    assert call(**{**ok, "xs": [A16, None]}) == INVALID
+    assert call(**{**ok, "qs": [D16, None], "qts": [E16, None]}) == INVALID          # tensor 1 has no output
+    assert call(**{**ok, "fmts": [0, 2]}) == INVALID
+    assert call(**{**ok, "rows": [16, 0]}) == INVALID
+    assert call(**{**ok, "qs": [D16, D16 + 128]}) == INVALID                         # outputs overlap
+    assert b"overlapping outputs" in lib.fp8_last_error()
+    assert call(**{**ok, "qs": [D16, A16 + 64]}) == INVALID                          # an output inside an input
+    assert b"overlaps an input" in lib.fp8_last_error()
+    assert call(**{**ok, "rows": [16, 24]}) == UNSUPPORTED                           # rows % 16
+    assert call(**{**ok, "cols": [16, 40]}) == UNSUPPORTED                           # cols % 16
+    assert call(**{**ok, "xs": [A16, B16 + 2]}) == UNSUPPORTED                       # misaligned input

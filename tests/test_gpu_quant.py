@@ -100,7 +100,7 @@ def test_absmax_accumulate(fp8, orc):
 
 
 def test_absmax_accumulate_many(fp8, orc):
-    """Up to 4 tensors in one launch: each slot gets its tensor's absmax (sizes
+    """Up to 8 tensors in one launch: each slot gets its tensor's absmax (sizes
     from a ragged 37 elements to 48 M, below and above the non-temporal
     threshold), a shared slot gets the maximum of its tensors, priors stay."""
     say("absmax many")
@@ -126,8 +126,56 @@ def test_absmax_accumulate_many(fp8, orc):
     r = s2.cpu().numpy()
     assert_f32_equal(r[0], max(np.float32(want[0]), np.float32(want[3])), "shared slot")
     assert_f32_equal(r[1], np.float32(1e30), "larger prior")
+    # eight tensors in one launch (the largest count), each into its own slot
+    s8 = torch.zeros(8, dtype=torch.float32, device="cuda")
+    xs8 = xs + xs[:3] + [xs[2]]
+    fp8.absmax_accumulate_many(xs8, [s8[i:i + 1] for i in range(8)])
+    torch.cuda.synchronize()
+    r8 = s8.cpu().numpy()
+    for i, k in enumerate([0, 1, 2, 3, 0, 1, 2, 2]):
+        assert_f32_equal(r8[i], want[k], f"eight tensors, slot {i}")
     with pytest.raises(ValueError):
-        fp8.absmax_accumulate_many(xs + xs[:1], [slots[i:i + 1] for i in range(5)])
+        fp8.absmax_accumulate_many(xs8 + xs[:1], [s8[i:i + 1] for i in range(8)] + [slots[0:1]])
+
+
+def test_quantize_many(fp8, orc):
+    """Up to 8 tensors in one launch, each bit-identical to its own fp8_quantize
+    call and to the oracle: mixed formats, q only / qt only / both, ragged
+    multiples of 16 spanning several 128 x 128 tiles, one input of 64 MiB
+    (read non-temporally) next to small ones, a retained (stale) statistic."""
+    shapes = [(144, 272), (4096, 8192), (16, 16), (400, 1040), (272, 144), (1024, 2048), (128, 128), (48, 4112)]
+    fmts = [E4M3, E5M2, E4M3, E5M2, E4M3, E4M3, E5M2, E4M3]
+    want_q = [True, True, False, True, True, False, True, True]
+    want_qt = [True, True, True, False, True, True, True, False]
+    say("quantize many", len(shapes))
+    xs, bits, amaxs = [], [], []
+    for k, (r, c) in enumerate(shapes):
+        x = workloads.draw(103, k, (r, c), 1.0 if fmts[k] == E4M3 else 1e-3)
+        bits.append(u16(x))
+        xs.append(dev(x))
+        amaxs.append(fp8.absmax(xs[-1]))
+    amaxs[3] = amaxs[3] * 0.25              # a stale statistic: some codes saturate
+    qs, qts, scs, invs = fp8.quantize_many(xs, fmts, amaxs, want_q=want_q, want_qt=want_qt)
+    torch.cuda.synchronize()
+    for k, (r, c) in enumerate(shapes):
+        what = f"tensor {k} {r}x{c} fmt {fmts[k]}"
+        am = scalar(amaxs[k])
+        s_ref, inv_ref = orc.scale(am, fmts[k])
+        assert_f32_equal(scalar(scs[k]), s_ref, what + " scale")
+        assert_f32_equal(scalar(invs[k]), inv_ref, what + " inv")
+        q_ref, _ = orc.quantize(bits[k], fmts[k], s_ref)
+        assert (qs[k] is not None) == want_q[k] and (qts[k] is not None) == want_qt[k]
+        if want_q[k]:
+            assert_codes_equal(u8(qs[k]), q_ref, fmts[k], what + " q")
+        if want_qt[k]:
+            assert_codes_equal(u8(qts[k]), q_ref.T.copy(), fmts[k], what + " qt")
+        q1, qt1, _, _ = fp8.quantize(xs[k], fmts[k], amaxs[k], want_q=want_q[k], want_qt=want_qt[k])
+        if want_q[k]:
+            assert torch.equal(q1, qs[k]), what + " vs fp8_quantize"
+        if want_qt[k]:
+            assert torch.equal(qt1, qts[k]), what + " vs fp8_quantize (qt)"
+    with pytest.raises(fp8.Fp8Error):     # rows % 16 != 0 in one entry: refused before any launch
+        fp8.quantize_many([xs[0], torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda")], E4M3, amaxs[0])
 
 
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
