@@ -9,7 +9,10 @@ forward and backward --
   forward:  absmax -> quantise to e4m3 (with the transposed copies the
             backward reads) for X and W -> FP8 GEMM -> bf16 Y; the gate/up
             output goes through the fused SwiGLU absmax + requantisation and
-            the down linear consumes its e4m3 output;
+            the down linear consumes its e4m3 output.  The tensors ready at
+            the start of the step (the four weights and the first linear's
+            input) take their statistics in one launch and their
+            quantisations in one launch;
   backward: absmax -> quantise dY to e5m2 (+ transposed copy) -> dgrad
             (dY . W) and wgrad (dY^T . X) FP8 GEMMs -> bf16.
 
@@ -117,7 +120,8 @@ WORKLOADS = {
 }
 
 
-def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, fused_absmax_h=False):
+def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, fused_absmax_h=False,
+               quant_mode="pair"):
     """Inputs and the ordered list of calls of one layer step of a configuration.
 
     The step starts by clearing its buffer of per-tensor absmax statistics (one
@@ -126,9 +130,12 @@ def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, 
     epilogue (fp8_gemm_fwd_swiglu_absmax) and fp8_swiglu_requant runs without a
     reduction pass; by default (measured faster in this step) fp8_swiglu_requant
     takes it in its own pass.
-    Forward: the absmax of X and W (one launch), quantise of X and W, FP8 GEMM,
-    for QKV, O and gate/up;
-    the fused SwiGLU requant of the gate/up output feeds the down linear.
+    Forward (group_weights): the statistics of the four weights and of the QKV
+    input in one launch, their quantisations in one launch; then for QKV, O and
+    gate/up the FP8 GEMM, preceded (O, gate/up) by the absmax and quantisation
+    of that linear's input.  Without group_weights each linear takes the
+    statistics of its X and W in one launch and quantises them separately.
+    The fused SwiGLU requant of the gate/up output feeds the down linear.
     Backward: absmax + e5m2 quantise of dY, then dgrad and wgrad in one launch.
     With recomputation (layer32b) the backward first re-quantises the retained bf16
     gate/up input with its retained absmax, reruns the gate/up GEMM and
@@ -165,16 +172,34 @@ def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, 
                                                                    "qt": want_qt}))
         return q, qt, inv
 
-    def quant_pair_ops(name, x, w, L, want_xt, want_wt):
-        """A linear's input and weight: both statistics in one launch, then their quantisations."""
+    def quant_pair_ops(name, x, w, L, want_xt, want_wt, pair_absmax=True, pair_quant=False):
+        """A linear's input and weight: their statistics (in one launch, or two), then
+        their quantisations (in one launch, or two)."""
         kx, kw = next(slots), next(slots)
         am_x, am_w = stats[kx:kx + 1], stats[kw:kw + 1]
-        ops.append(Op(f"absmax X_{name}+W_{name}", lambda: fp8.absmax_accumulate_many([x, w], [am_x, am_w]),
-                      "absmax", 2 * (M + L.N) * L.K,
-                      meta={"shapes": [(M, L.K), (L.N, L.K)]}))
-        xq, xqt, inv_x = quantize_op(f"X_{name}", x, M, L.K, E4M3, am_x, want_xt)
-        wq, wqt, inv_w = quantize_op(f"W_{name}", w, L.N, L.K, E4M3, am_w, want_wt)
-        return xq, xqt, inv_x, am_x, wq, wqt, inv_w
+        if pair_absmax:
+            ops.append(Op(f"absmax X_{name}+W_{name}", lambda: fp8.absmax_accumulate_many([x, w], [am_x, am_w]),
+                          "absmax", 2 * (M + L.N) * L.K, meta={"shapes": [(M, L.K), (L.N, L.K)]}))
+        else:
+            # the gate/up weight is streamed non-temporally: a shared launch would
+            # stream X too and cost its quantisation the Infinity Cache (measured)
+            for tag, t, am, r in (("X", x, am_x, M), ("W", w, am_w, L.N)):
+                ops.append(Op(f"absmax {tag}_{name}", lambda t=t, am=am: fp8.absmax(t, am, accumulate=True),
+                              "absmax", 2 * r * L.K, meta={"rows": r, "cols": L.K}))
+        if not pair_quant:
+            xq, xqt, inv_x = quantize_op(f"X_{name}", x, M, L.K, E4M3, am_x, want_xt)
+            wq, wqt, inv_w = quantize_op(f"W_{name}", w, L.N, L.K, E4M3, am_w, want_wt)
+            return xq, xqt, inv_x, am_x, wq, wqt, inv_w
+        shp, want_t = [(M, L.K), (L.N, L.K)], [want_xt, want_wt]
+        qs = [u8(r, c) for r, c in shp]
+        qts = [u8(c, r) if t else None for (r, c), t in zip(shp, want_t)]
+        scs, invs = [f32(), f32()], [f32(), f32()]
+        ops.append(Op(f"quantize X_{name}+W_{name}",
+                      lambda: fp8.quantize_many([x, w], E4M3, [am_x, am_w], want_q=True, want_qt=want_t, qs=qs,
+                                                qts=qts, scales=scs, inv_scales=invs),
+                      "quantize", sum((4 if t else 3) * r * c for (r, c), t in zip(shp, want_t)),
+                      meta={"group": [{"rows": r, "cols": c, "fmt": E4M3, "qt": t} for (r, c), t in zip(shp, want_t)]}))
+        return qs[0], qts[0], invs[0], am_x, qs[1], qts[1], invs[1]
 
     def quant_ops(tag, x, rows, cols, fmt, want_qt):
         k = next(slots)
@@ -206,19 +231,55 @@ def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, 
     # absmax_h of the SwiGLU output: from the gate/up GEMM's epilogue (one slot of
     # the step's statistics), or from the SwiGLU kernel's own reduction pass
     am_h = stats[63:64]
+    names = ("qkv", "o", "gate_up", "down")
+    xs = {n: workloads.draw_x(cfg, lin[n][0]).to(dev) for n in names[:3]}
+    ws = {n: workloads.draw_w(cfg, lin[n][0]).to(dev) for n in names}
+    for n in names:
+        bufs[n] = (xs.get(n), ws[n])
+    keep_xt = {n: not mn and not (recompute and n == "gate_up") for n in names[:3]}
+    qd = {}      # (tensor tag) -> (q, qt, inv, absmax slot)
+    group_weights = quant_mode == "step"
+    if group_weights:
+        # the tensors ready when the layer's step starts -- its four weights and the
+        # first linear's input -- take their statistics in one launch and their
+        # quantisations (with the transposed copies) in one launch
+        tags = ["X_qkv"] + [f"W_{n}" for n in names]
+        tens = [xs["qkv"]] + [ws[n] for n in names]
+        shp = [(M, lin["qkv"][1].K)] + [(lin[n][1].N, lin[n][1].K) for n in names]
+        want_t = [keep_xt["qkv"]] + [not mn] * 4
+        ams = [stats[k:k + 1] for k in (next(slots) for _ in tags)]
+        ops.append(Op("absmax [" + ", ".join(tags) + "]",
+                      lambda: fp8.absmax_accumulate_many(tens, ams), "absmax", sum(2 * r * c for r, c in shp),
+                      meta={"shapes": shp}))
+        qs = [u8(r, c) for r, c in shp]
+        qts = [u8(c, r) if t else None for (r, c), t in zip(shp, want_t)]
+        scs, invs = [f32() for _ in tags], [f32() for _ in tags]
+        ops.append(Op("quantize [" + ", ".join(tags) + "]",
+                      lambda: fp8.quantize_many(tens, E4M3, ams, want_q=True, want_qt=want_t, qs=qs, qts=qts,
+                                                scales=scs, inv_scales=invs),
+                      "quantize", sum((4 if t else 3) * r * c for (r, c), t in zip(shp, want_t)),
+                      meta={"group": [{"rows": r, "cols": c, "fmt": E4M3, "qt": t} for (r, c), t in zip(shp, want_t)]}))
+        for k, t in enumerate(tags):
+            qd[t] = (qs[k], qts[k], invs[k], ams[k])
     for name in ("qkv", "o", "gate_up"):
         li, L = lin[name]
-        x = workloads.draw_x(cfg, li).to(dev)
-        w = workloads.draw_w(cfg, li).to(dev)
-        bufs[name] = (x, w)
-        keep_xt = not mn and not (recompute and name == "gate_up")
-        if name != "gate_up":
-            xq, xqt, inv_x, am_x, wq, wqt, inv_w = quant_pair_ops(name, x, w, L, keep_xt, not mn)
+        x, w = xs[name], ws[name]
+        if group_weights:
+            if name != "qkv":
+                xq, xqt, inv_x, am_x = quant_ops(f"X_{name}", x, M, L.K, E4M3, keep_xt[name])
+            else:
+                xq, xqt, inv_x, am_x = qd["X_qkv"]
+            wq, wqt, inv_w, _ = qd[f"W_{name}"]
+        elif quant_mode == "pair":
+            xq, xqt, inv_x, am_x, wq, wqt, inv_w = quant_pair_ops(name, x, w, L, keep_xt[name], not mn,
+                                                                  pair_absmax=name != "gate_up", pair_quant=True)
+        elif name != "gate_up":
+            xq, xqt, inv_x, am_x, wq, wqt, inv_w = quant_pair_ops(name, x, w, L, keep_xt[name], not mn)
         else:
             # the gate/up weight is streamed non-temporally: a shared launch would
             # stream X too and cost its quantisation the Infinity Cache, for no
             # shorter statistics pass (measured)
-            xq, xqt, inv_x, am_x = quant_ops(f"X_{name}", x, M, L.K, E4M3, keep_xt)
+            xq, xqt, inv_x, am_x = quant_ops(f"X_{name}", x, M, L.K, E4M3, keep_xt[name])
             wq, wqt, inv_w, _ = quant_ops(f"W_{name}", w, L.N, L.K, E4M3, not mn)
         y = bf(M, L.N)
         gemm_fwd_op(name, xq, wq, inv_x, inv_w, y, L, am_h if (name == "gate_up" and fused_absmax_h) else None)
@@ -228,9 +289,10 @@ def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, 
     li, L = lin["down"]
     F = L.K
     hq, hqt, inv_h = swiglu_op("fwd", fwd["gate_up"]["y"], am_h, not fused_absmax_h, not mn and not recompute, F)
-    w = workloads.draw_w(cfg, li).to(dev)
-    bufs["down"] = (None, w)
-    wq, wqt, inv_w, _ = quant_ops("W_down", w, L.N, L.K, E4M3, not mn)
+    if group_weights:
+        wq, wqt, inv_w, _ = qd["W_down"]
+    else:
+        wq, wqt, inv_w, _ = quant_ops("W_down", ws["down"], L.N, L.K, E4M3, not mn)
     y = bf(M, L.N)
     gemm_fwd_op("down", hq, wq, inv_h, inv_w, y, L)
     fwd["down"] = {"xq": hq, "wq": wq, "xqt": hqt, "wqt": wqt, "inv_x": inv_h, "inv_w": inv_w, "y": y}
@@ -367,86 +429,243 @@ def streaming_cold(fp8, ops, stream, dev, reps=20, warm=3):
                       "vs_copy": round(agg / copy_gbs, 3), "calls": calls}
 
 
-STREAM_SAMPLE_ELEMS = 1 << 25      # oracle sample of a streaming call: at most 32 M elements
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(ops, gemm_rows):
-    """The oracle, as it stands, on a bounded sample of the same step, scaled to a full step.
-
-    Sample: every absmax / quantise / SwiGLU call on its tensor's shape (random
-    bf16), cut to its first rows when larger than STREAM_SAMPLE_ELEMS elements
-    and scaled by the row count; every GEMM on `gemm_rows` and 2 * `gemm_rows`
-    output rows, extrapolated linearly to all its rows.
+    """The oracle, as it stands, on the same step: every absmax / quantise / SwiGLU
+    call over its full tensor (random bf16 of the call's shape), every GEMM on
+    `gemm_rows` and 2 * `gemm_rows` output rows, extrapolated linearly to all its
+    rows (the two sizes separate the per-call cost of decoding B from the per-row
+    cost).  Reported as the step's GEMM FLOP over the estimated step time.
     """
     import oracle
     oracle.build(force=False)
     threads = oracle.num_threads()
     rng = np.random.default_rng(0)
-    est = 0.0
+    gemm_est = gemm_spent = stream_s = 0.0
+    stream_bytes = 0
     gemm_flop = 0.0
     t_start = time.perf_counter()
 
-    def sample_rows(rows, cols):
-        r = max(16, min(rows, STREAM_SAMPLE_ELEMS // cols // 16 * 16))
-        return r, rows / r
+    def timed(fn):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
 
     for op in ops:
         m = op.meta
         if op.kind == "gemm":
             for P, Q, R, fa in m["probs"]:
-                # two sample sizes separate the per-call cost (decoding B) from the per-row cost
                 b = rng.integers(0, 0x7E, (Q, R), dtype=np.uint8)
                 times = []
                 for r in (gemm_rows, 2 * gemm_rows):
                     a = rng.integers(0, 0x7E, (r, R), dtype=np.uint8)
-                    t = time.perf_counter()
-                    oracle.gemm(a, fa, b, 0, 1.0, 1.0)
-                    times.append(time.perf_counter() - t)
+                    times.append(timed(lambda: oracle.gemm(a, fa, b, 0, 1.0, 1.0)))
+                gemm_spent += sum(times)
                 per_row = max(times[1] - times[0], 0.0) / gemm_rows
                 fixed = max(times[0] - per_row * gemm_rows, 0.0)
-                est += fixed + per_row * P
+                gemm_est += fixed + per_row * P
                 gemm_flop += 2.0 * P * Q * R
-                if m.get("swiglu_absmax"):
-                    # the SwiGLU statistic this GEMM also produces: the oracle's reduction pass
-                    r, f = sample_rows(P, Q)
-                    gu = rng.integers(0, 0x4080, (r, Q), dtype=np.uint16)
-                    t = time.perf_counter()
-                    oracle.swiglu_requant(gu, want_hq=False)
-                    est += (time.perf_counter() - t) * f
+            if m.get("swiglu_absmax"):
+                # the SwiGLU statistic this GEMM also produces: the oracle's reduction pass
+                P, Q = m["probs"][0][:2]
+                gu = rng.integers(0, 0x4080, (P, Q), dtype=np.uint16)
+                stream_s += timed(lambda: oracle.swiglu_requant(gu, want_hq=False))
+                stream_bytes += 2 * P * Q
+                del gu
         elif op.kind == "absmax":
             for rows, cols in m.get("shapes", [(m.get("rows"), m.get("cols"))]):
-                r, f = sample_rows(rows, cols)
-                x = rng.integers(0, 0x3F80, (r, cols), dtype=np.uint16)
-                t = time.perf_counter()
-                oracle.absmax_bf16(x)
-                est += (time.perf_counter() - t) * f
+                x = rng.integers(0, 0x3F80, (rows, cols), dtype=np.uint16)
+                stream_s += timed(lambda: oracle.absmax_bf16(x))
+                del x
+            stream_bytes += op.work
         elif op.kind == "quantize":
-            r, f = sample_rows(m["rows"], m["cols"])
-            x = rng.integers(0, 0x3F80, (r, m["cols"]), dtype=np.uint16)
-            s_, _ = oracle.scale(np.float32(1.0), m["fmt"])
-            t = time.perf_counter()
-            oracle.quantize(x, m["fmt"], s_, want_q=True, want_qt=m["qt"])
-            est += (time.perf_counter() - t) * f
+            for g in m.get("group", [m]):
+                x = rng.integers(0, 0x3F80, (g["rows"], g["cols"]), dtype=np.uint16)
+                s_, _ = oracle.scale(np.float32(1.0), g["fmt"])
+                stream_s += timed(lambda: oracle.quantize(x, g["fmt"], s_, want_q=True, want_qt=g["qt"]))
+                del x
+            stream_bytes += op.work
         elif op.kind == "swiglu_bwd":
-            r, f = sample_rows(m["M"], 3 * m["F"])
-            gu = rng.integers(0, 0x4080, (r, 2 * m["F"]), dtype=np.uint16)
-            dh = rng.integers(0, 0x3A80, (r, m["F"]), dtype=np.uint16)
-            t = time.perf_counter()
-            oracle.swiglu_backward(gu, dh, 1, want_q=True, want_qt=m["qt"])
-            est += (time.perf_counter() - t) * f
+            gu = rng.integers(0, 0x4080, (m["M"], 2 * m["F"]), dtype=np.uint16)
+            dh = rng.integers(0, 0x3A80, (m["M"], m["F"]), dtype=np.uint16)
+            stream_s += timed(lambda: oracle.swiglu_backward(gu, dh, 1, want_q=True, want_qt=m["qt"]))
+            stream_bytes += op.work
+            del gu, dh
         elif op.kind == "swiglu":
-            r, f = sample_rows(m["M"], 2 * m["F"])
-            gu = rng.integers(0, 0x4080, (r, 2 * m["F"]), dtype=np.uint16)
-            t = time.perf_counter()
-            oracle.swiglu_requant(gu, absmax_h=None if m["compute"] else np.float32(8.0), want_hq=True,
-                                  want_hqt=m["qt"])
-            est += (time.perf_counter() - t) * f
+            gu = rng.integers(0, 0x4080, (m["M"], 2 * m["F"]), dtype=np.uint16)
+            stream_s += timed(lambda: oracle.swiglu_requant(gu, absmax_h=None if m["compute"] else np.float32(8.0),
+                                                            want_hq=True, want_hqt=m["qt"]))
+            stream_bytes += op.work
+            del gu
     spent = time.perf_counter() - t_start
-    return {"value": round(gemm_flop / est / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": (f"every absmax/quantise/SwiGLU call of the step on its tensor shape (first rows, up to "
-                       f"{STREAM_SAMPLE_ELEMS} elements, scaled by the row count), every GEMM on {gemm_rows} and "
-                       f"{2 * gemm_rows} output rows extrapolated to all rows; {spent:.1f} s of CPU work, "
-                       f"estimated full step {est:.1f} s on {threads} threads")}
+    est = gemm_est + stream_s
+    return {"value": round(gemm_flop / est / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "cpu_model": cpu_model(),
+            "kind": "oracle",
+            "streaming_full_s": round(stream_s, 3),
+            "streaming_gbs": round(stream_bytes / stream_s / 1e9, 2) if stream_s > 0 else None,
+            "gemm_sampled_s": round(gemm_spent, 3), "gemm_estimated_s": round(gemm_est, 2),
+            "sample": (f"every absmax/quantise/SwiGLU call of the step over its full tensor ({stream_bytes / 1e9:.2f} GB "
+                       f"in {stream_s:.2f} s); every GEMM on {gemm_rows} and {2 * gemm_rows} output rows "
+                       f"({gemm_spent:.1f} s), extrapolated to all rows; {spent:.1f} s of CPU work in all (input "
+                       f"generation included), estimated full step {est:.1f} s on {threads} threads")}
+
+
+def gemm_shapes(fp8, dev, cfg_name, reps=5, warm=2):
+    """The FP8 GEMM calls of a configuration's layer (each linear's forward and its
+    dgrad + wgrad launch) on device-drawn operands of the step's kind (normal
+    draws -- Student-t(3) activations with outlier channels where the
+    configuration has them -- quantised with their own absmax, dY to e5m2), run
+    as a sequence of
+    GEMMs only -- all forwards, then all backwards -- `reps` times after `warm`
+    untimed rounds, every call timed with HIP events.  Back to back, without
+    the step's memory-bound calls in between, the chip runs nearer its power
+    limit than in the step, so these rates are a lower bound for the step's."""
+    cfg = workloads.CONFIGS[cfg_name]
+    M = cfg.M
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+
+    def codes(r, c, fmt, want_qt, activation=False):
+        if activation and cfg.x_dist == "student_t":
+            # the configuration's activations: Student-t(3), 0.1% of the channels x50
+            torch.manual_seed(cfg.seed)
+            x = torch.distributions.StudentT(torch.tensor(3.0, device=dev)).sample((r, c))
+            pick = torch.randperm(c, generator=gen, device=dev)[:int(round(cfg.x_outlier_frac * c))]
+            x[:, pick] *= 50.0
+            x = x.to(torch.bfloat16)
+        else:
+            x = torch.randn((r, c), generator=gen, device=dev, dtype=torch.bfloat16)
+        q, qt, _, inv = fp8.quantize(x, fmt, fp8.absmax(x), want_q=True, want_qt=want_qt)
+        del x
+        return q, qt, inv
+
+    calls = []
+    for L in cfg.linears:
+        xq, xqt, ix = codes(M, L.K, fp8.E4M3, True, activation=True)
+        wq, wqt, iw = codes(L.N, L.K, fp8.E4M3, True)
+        dyq, dyqt, idy = codes(M, L.N, fp8.E5M2, True)
+        y = torch.empty((M, L.N), dtype=torch.bfloat16, device=dev)
+        dx = torch.empty((M, L.K), dtype=torch.bfloat16, device=dev)
+        dw = torch.empty((L.N, L.K), dtype=torch.bfloat16, device=dev)
+        calls.append((f"gemm_fwd {L.name}", 2 * M * L.N * L.K,
+                      lambda xq=xq, wq=wq, ix=ix, iw=iw, y=y: fp8.gemm_fwd(xq, wq, ix, iw, out=y)))
+        calls.append((f"gemm_backward {L.name}", 4 * M * L.N * L.K,
+                      lambda a=(dyq, dyqt, wqt, xqt, idy, iw, ix, dx, dw):
+                      fp8.gemm_backward(a[0], a[1], fp8.E5M2, a[2], a[3], a[4], a[5], a[6], dx=a[7], dw=a[8])))
+    order = [c for c in calls if c[0].startswith("gemm_fwd")] + [c for c in calls if c[0].startswith("gemm_back")]
+    for _ in range(warm):
+        for _, _, fn in order:
+            fn()
+    times = {name: [] for name, _, _ in order}
+    for _ in range(reps):
+        evs = []
+        for name, _, fn in order:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((name, a, b))
+        torch.cuda.synchronize()
+        for name, a, b in evs:
+            times[name].append(a.elapsed_time(b) * 1e-3)
+    rows, tf, tt = [], 0.0, 0.0
+    for name, flop, _ in order:
+        t = float(np.median(times[name]))
+        rows.append({"call": name, "tflops": round(flop / t / 1e12, 1),
+                     "frac": round(flop / t / 1e12 / FP8_PEAK_TFLOPS, 4), "us": round(t * 1e6, 1)})
+        tf += flop
+        tt += t
+    del calls, order
+    torch.cuda.empty_cache()
+    return {"workload": WORKLOADS[cfg_name], "gemm_tflops": round(tf / tt / 1e12, 1),
+            "frac": round(tf / tt / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "timing": f"GEMMs only, back to back, median of {reps} after {warm} untimed rounds", "calls": rows}
+
+
+def vs_hipblaslt(fp8, ops, dev, reps=10, rounds=3):
+    """Every GEMM call of the step next to hipBLASLt (torch._scaled_mm, per-tensor
+    scales, bf16 out) on the same FP8 operand bytes, timed interleaved (ours,
+    hipBLASLt, ours, ...) so that neither runs at a different clock.  A
+    backward call (dgrad + wgrad in one launch here) is compared with the two
+    hipBLASLt products run back to back.  For context only."""
+    dt = {fp8.E4M3: torch.float8_e4m3fn, fp8.E5M2: torch.float8_e5m2}
+
+    def events(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        return a, b
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    one = torch.ones((), dtype=torch.float32, device=dev)
+    rows = []
+    for op in ops:
+        if op.kind != "gemm":
+            continue
+        calls = []
+        for P, Q, R, fa in op.meta["probs"]:
+            # operand codes of the step's kind: normal draws quantised with their own absmax
+            a = torch.randn((P, R), generator=gen, device=dev, dtype=torch.bfloat16)
+            b = torch.randn((Q, R), generator=gen, device=dev, dtype=torch.bfloat16)
+            aq = fp8.quantize(a, fa, fp8.absmax(a))[0]
+            bq = fp8.quantize(b, fp8.E4M3, fp8.absmax(b))[0]
+            del a, b
+            calls.append((aq, bq, fa, torch.empty((P, Q), dtype=torch.bfloat16, device=dev)))
+        inv = torch.ones(1, dtype=torch.float32, device=dev)
+
+        def ours():
+            if len(calls) == 1:
+                aq, bq, fa, y = calls[0]
+                if fa == fp8.E4M3:
+                    fp8.gemm_fwd(aq, bq, inv, inv, out=y)
+                else:
+                    fp8.gemm_dgrad(aq, fa, bq, inv, inv, out=y)
+            else:
+                # a backward call: dgrad (dY [M, N], W^T [K, N]) and wgrad (dY^T [N, M],
+                # X^T [K, M]) in one launch
+                (dyq, wqt, fa, dx), (dyqt, xqt, _, dw) = calls
+                fp8.gemm_backward(dyq, dyqt, fa, wqt, xqt, inv, inv, inv, dx=dx, dw=dw)
+
+        def theirs():
+            for aq, bq, fa, y in calls:
+                torch._scaled_mm(aq.view(dt[fa]), bq.view(torch.float8_e4m3fn).t(), scale_a=one, scale_b=one,
+                                 out_dtype=torch.bfloat16, out=y)
+        row = {"call": op.name, "gflop": round(op.work / 1e9, 1)}
+        try:
+            theirs()
+        except Exception as ex:      # a format pair the vendor library does not take
+            row["hipblaslt"] = f"n/a ({type(ex).__name__})"
+            theirs = None
+        ours()
+        torch.cuda.synchronize()
+        t_ours, t_theirs = [], []
+        for _ in range(rounds):
+            e1 = events(ours)
+            e2 = events(theirs) if theirs else None
+            torch.cuda.synchronize()
+            t_ours.append(e1[0].elapsed_time(e1[1]) * 1e-3 / reps)
+            if e2:
+                t_theirs.append(e2[0].elapsed_time(e2[1]) * 1e-3 / reps)
+        row["ours_tflops"] = round(op.work / float(np.median(t_ours)) / 1e12, 1)
+        if t_theirs:
+            row["hipblaslt_tflops"] = round(op.work / float(np.median(t_theirs)) / 1e12, 1)
+        rows.append(row)
+        del calls
+        torch.cuda.empty_cache()
+    return rows
 
 
 def sustained_clock(ops, seconds=4.0):
@@ -521,6 +740,15 @@ def main():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache per-call streaming measurement")
     ap.add_argument("--no-clock", action="store_true", help="skip the sustained-clock sampling (amd-smi)")
+    ap.add_argument("--no-shapes", action="store_true",
+                    help="skip the 14B- and 32B-class GEMM figures reported with the layer7b workload")
+    ap.add_argument("--quant-mode", choices=("pair", "linear", "step"), default="pair",
+                    help="pair: each linear's X and W quantised in one launch (their statistics in one launch for "
+                         "QKV and O); linear: X and W quantised in separate launches; step: the four weights and the "
+                         "first input quantised together at the start of the step")
+    ap.add_argument("--vs-hipblaslt", action="store_true",
+                    help="only compare every GEMM call of the step with hipBLASLt (torch._scaled_mm) on the same "
+                         "operand bytes, interleaved, and print that as the JSON line (context, not the metric)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every box here has one GPU "
@@ -535,8 +763,17 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     cfg = workloads.CONFIGS[args.workload]
+    if args.vs_hipblaslt:
+        ops, _ = build_step(fp8, dev, args.workload, "copies", False, False)
+        for _ in range(3):
+            run_step(ops)
+        rows = vs_hipblaslt(fp8, ops, dev)
+        print(json.dumps({"comparison": "hipBLASLt (torch._scaled_mm, per-tensor scales, bf16 out) vs this library, "
+                                        "same FP8 operand bytes, interleaved, median of 3 rounds of 10 calls",
+                          "workload": args.workload, "calls": rows}))
+        return
     ops, bufs = build_step(fp8, dev, args.workload, args.layout, args.swiglu_backward,
-                           args.fused_swiglu_absmax)
+                           args.fused_swiglu_absmax, args.quant_mode)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         run_step(ops)
@@ -585,6 +822,10 @@ def main():
     quant_gbs = qb / qt / 1e9
     copy_gbs, cold = (None, None) if args.no_cold else streaming_cold(fp8, ops, stream, dev)
 
+    shapes = {}
+    if args.workload == "layer7b" and not args.no_shapes:
+        for other in ("layer14b", "layer32b"):
+            shapes[other] = gemm_shapes(fp8, dev, other)
     clock = None if args.no_clock else sustained_clock(ops)
     want_cpu = not args.no_cpu_baseline and (args.workload == "layer7b" or args.cpu_baseline)
     cpu = cpu_baseline(ops, args.cpu_gemm_rows) if want_cpu else None
@@ -610,6 +851,10 @@ def main():
                    else "drawn output gradients",
                    "swiglu_absmax": ("gate/up GEMM epilogue" if args.fused_swiglu_absmax
                                      else "separate reduction pass"),
+                   "quantisation_launches": {"pair": "X and W of a linear in one launch",
+                                             "linear": "X and W of a linear in separate launches",
+                                             "step": "the weights and the layer input in one launch at step start"
+                                             }[args.quant_mode],
                    "gemm_gflop_per_step": round(gemm_flop / 1e9, 1)},
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "gemm_only_tflops": round(gemm_flop / gemm_time / 1e12, 1),
@@ -636,6 +881,8 @@ def main():
                     "bytes": int(qb), "note": "bytes-weighted over the step's absmax/quantise/SwiGLU calls"},
         "cold": cold,
     }
+    if shapes:
+        line["shapes"] = shapes
     line["breakdown"] = breakdown
     print(json.dumps(line))
 
