@@ -668,23 +668,20 @@ def vs_hipblaslt(fp8, ops, dev, reps=10, rounds=3):
     return rows
 
 
-def sustained_clock(ops, seconds=4.0):
-    """Median graphics clock and socket power while the step loops (outside the timed region).
-
-    A background thread queries `amd-smi metric -c -p --json` (current clock of
-    every graphics clock domain, socket power) while the main thread keeps the
-    GPU busy with the step.  Returns None when amd-smi is not available.
-    """
+def amd_smi_sampler():
+    """A background sampler of the median graphics clock and the socket power
+    (`amd-smi metric -c -p`); returns (start, stop) where stop() gives the
+    (clock MHz, power W) samples taken meanwhile, or None without amd-smi."""
     import shutil
     import subprocess
     import threading
     exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
     if not os.path.exists(exe):
         return None
-    samples, stop = [], threading.Event()
+    samples, stop_ev = [], threading.Event()
 
     def loop():
-        while not stop.is_set():
+        while not stop_ev.is_set():
             try:
                 r = subprocess.run([exe, "metric", "-c", "-p", "--json", "-g", "0"], capture_output=True, text=True,
                                    timeout=20)
@@ -698,17 +695,85 @@ def sustained_clock(ops, seconds=4.0):
             except Exception:   # a malformed or missing sample is skipped
                 pass
 
+    th = threading.Thread(target=loop, daemon=True)
+
+    def stop():
+        stop_ev.set()
+        th.join(timeout=30)
+        return samples
+    return th.start, stop
+
+
+def sustained_vs_hipblaslt(fp8, dev, shapes, seconds=2.0, rounds=2):
+    """One forward GEMM shape at a time, this library and hipBLASLt alternately,
+    each run back to back for `seconds` while amd-smi samples the clock and the
+    socket power: TFLOP/s, and per GHz and per joule, under the power limit."""
+    one = torch.ones((), dtype=torch.float32, device=dev)
+    inv = torch.ones(1, dtype=torch.float32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    rows = []
+    for P, Q, R in shapes:
+        a = torch.randn((P, R), generator=gen, device=dev, dtype=torch.bfloat16)
+        b = torch.randn((Q, R), generator=gen, device=dev, dtype=torch.bfloat16)
+        aq = fp8.quantize(a, fp8.E4M3, fp8.absmax(a))[0]
+        bq = fp8.quantize(b, fp8.E4M3, fp8.absmax(b))[0]
+        del a, b
+        y = torch.empty((P, Q), dtype=torch.bfloat16, device=dev)
+        fns = {"ours": lambda: fp8.gemm_fwd(aq, bq, inv, inv, out=y),
+               "hipblaslt": lambda: torch._scaled_mm(aq.view(torch.float8_e4m3fn), bq.view(torch.float8_e4m3fn).t(),
+                                                     scale_a=one, scale_b=one, out_dtype=torch.bfloat16, out=y)}
+        flop = 2.0 * P * Q * R
+        for _ in range(rounds):
+            for name, fn in fns.items():
+                for _ in range(20):
+                    fn()
+                torch.cuda.synchronize()
+                sampler = amd_smi_sampler()
+                if sampler:
+                    sampler[0]()
+                n, t0 = 0, time.perf_counter()
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                while time.perf_counter() - t0 < seconds:
+                    for _ in range(10):
+                        fn()
+                    n += 10
+                    torch.cuda.synchronize()
+                e.record()
+                torch.cuda.synchronize()
+                smp = sampler[1]() if sampler else []
+                tf = flop / (s.elapsed_time(e) * 1e-3 / n) / 1e12
+                row = {"shape": f"{P}x{Q}x{R}", "kernel": name, "tflops": round(tf, 1)}
+                if smp:
+                    mhz, w = float(np.median([x[0] for x in smp])), float(np.median([x[1] for x in smp]))
+                    row.update({"gfx_mhz": round(mhz), "power_w": round(w), "tflops_per_ghz": round(tf / (mhz / 1e3), 1),
+                                "gflop_per_joule": round(tf * 1e3 / w, 1), "samples": len(smp)})
+                rows.append(row)
+        del aq, bq, y
+        torch.cuda.empty_cache()
+    return rows
+
+
+def sustained_clock(ops, seconds=4.0):
+    """Median graphics clock and socket power while the step loops (outside the timed region).
+
+    A background thread queries `amd-smi metric -c -p --json` (current clock of
+    every graphics clock domain, socket power) while the main thread keeps the
+    GPU busy with the step.  Returns None when amd-smi is not available.
+    """
+    sampler = amd_smi_sampler()
+    if sampler is None:
+        return None
     for _ in range(5):          # the clock ramps up under load
         run_step(ops)
-    th = threading.Thread(target=loop, daemon=True)
-    th.start()
+    sampler[0]()
     t_end = time.perf_counter() + seconds
     while time.perf_counter() < t_end:
         for _ in range(20):
             run_step(ops)
         torch.cuda.synchronize()
-    stop.set()
-    th.join(timeout=30)
+    samples = sampler[1]()
     if not samples:
         return None
     c = float(np.median([x[0] for x in samples]))
@@ -768,9 +833,13 @@ def main():
         for _ in range(3):
             run_step(ops)
         rows = vs_hipblaslt(fp8, ops, dev)
+        sus = sustained_vs_hipblaslt(fp8, dev, [(4096, 12288, 4096), (4096, 4096, 11008), (4096, 4096, 4096)])
         print(json.dumps({"comparison": "hipBLASLt (torch._scaled_mm, per-tensor scales, bf16 out) vs this library, "
                                         "same FP8 operand bytes, interleaved, median of 3 rounds of 10 calls",
-                          "workload": args.workload, "calls": rows}))
+                          "workload": args.workload, "calls": rows,
+                          "sustained": {"note": "forward shapes, each kernel back to back for 2 s, alternating, with "
+                                                "amd-smi sampling the graphics clock and socket power",
+                                        "runs": sus}}))
         return
     ops, bufs = build_step(fp8, dev, args.workload, args.layout, args.swiglu_backward,
                            args.fused_swiglu_absmax, args.quant_mode)
