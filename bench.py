@@ -56,13 +56,21 @@ FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA peak
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E peak
 
 # rocprofv3 kernel names of the library's kernels (format of A, format of B,
-# edge tiles, layout set, half tiles, gate/up with the SwiGLU statistic); a
-# GEMM call whose last round is balanced runs a second launch of the half-tile
-# instantiation
-GEMM_KERNEL = {(0, 0, 0): "fp8k::gemm_tn_kernel<0, 0, false, 0, false, false>",
-               (1, 0, 0): "fp8k::gemm_tn_kernel<1, 0, false, 0, false, false>",
-               (1, 0, 1): "fp8k::gemm_tn_kernel<1, 0, false, 1, false, false>",
-               "gate_up": "fp8k::gemm_tn_kernel<0, 0, false, 0, false, true>"}
+# edge tiles, layout set, half tiles, gate/up with the SwiGLU statistic,
+# non-temporal output stores -- the backward products); a GEMM call whose last
+# round is balanced runs a second launch of the half-tile instantiation
+GEMM_KERNEL = {(0, 0, 0): "fp8k::gemm_tn_kernel<0, 0, false, 0, false, false, false>",
+               (1, 0, 0): "fp8k::gemm_tn_kernel<1, 0, false, 0, false, false, true>",
+               (1, 0, 1): "fp8k::gemm_tn_kernel<1, 0, false, 1, false, false, true>",
+               "gate_up": "fp8k::gemm_tn_kernel<0, 0, false, 0, false, true, false>"}
+
+
+def half_tile_kernel(kernel):
+    """The half-tile instantiation that balances the last round of `kernel`'s calls."""
+    head, args = kernel[:-1].split("<", 1)
+    a = [x.strip() for x in args.split(",")]
+    a[4] = "true"
+    return head + "<" + ", ".join(a) + ">"
 
 
 def tail_launch(probs, kmajor, cus):
@@ -95,7 +103,7 @@ def measured_traffic(kernel, tail_fraction=0.0):
     if b is None:
         return None
     if tail_fraction > 0:
-        t = data["per_dispatch_bytes"].get(kernel.replace(", false, false>", ", true, false>"))
+        t = data["per_dispatch_bytes"].get(half_tile_kernel(kernel))
         if t is None:
             return None
         b += tail_fraction * t

@@ -327,7 +327,7 @@ fp8_status fp8_gemm_fwd(const uint8_t* xq, const uint8_t* wq, const float* inv_s
     t_last_error.clear();
     fp8_status st = gemm_common("fp8_gemm_fwd", xq, FP8_E4M3, wq, inv_sx, inv_sw, y, M, N, K, stream);
     if (st != FP8_OK) return st;
-    hipError_t e = fp8k::launch_gemm_tn(xq, 0, 0, wq, 0, 0, inv_sx, inv_sw, y, M, N, K, stream);
+    hipError_t e = fp8k::launch_gemm_tn(xq, 0, 0, wq, 0, 0, inv_sx, inv_sw, y, M, N, K, false, stream);
     if (e != hipSuccess) return fail_hip("fp8_gemm_fwd", e);
     return FP8_OK;
 }
@@ -360,7 +360,7 @@ fp8_status fp8_gemm_dgrad(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_t* wqt
     t_last_error.clear();
     fp8_status st = gemm_common("fp8_gemm_dgrad", dyq, (int)dy_fmt, wqt, inv_sdy, inv_sw, dx, M, K, N, stream);
     if (st != FP8_OK) return st;
-    hipError_t e = fp8k::launch_gemm_tn(dyq, (int)dy_fmt, 0, wqt, 0, 0, inv_sdy, inv_sw, dx, M, K, N, stream);
+    hipError_t e = fp8k::launch_gemm_tn(dyq, (int)dy_fmt, 0, wqt, 0, 0, inv_sdy, inv_sw, dx, M, K, N, true, stream);
     if (e != hipSuccess) return fail_hip("fp8_gemm_dgrad", e);
     return FP8_OK;
 }
@@ -371,7 +371,7 @@ fp8_status fp8_gemm_wgrad(const uint8_t* dyqt, fp8_fmt dy_fmt, const uint8_t* xq
     t_last_error.clear();
     fp8_status st = gemm_common("fp8_gemm_wgrad", dyqt, (int)dy_fmt, xqt, inv_sdy, inv_sx, dw, N, K, M, stream);
     if (st != FP8_OK) return st;
-    hipError_t e = fp8k::launch_gemm_tn(dyqt, (int)dy_fmt, 0, xqt, 0, 0, inv_sdy, inv_sx, dw, N, K, M, stream);
+    hipError_t e = fp8k::launch_gemm_tn(dyqt, (int)dy_fmt, 0, xqt, 0, 0, inv_sdy, inv_sx, dw, N, K, M, true, stream);
     if (e != hipSuccess) return fail_hip("fp8_gemm_wgrad", e);
     return FP8_OK;
 }
@@ -407,7 +407,7 @@ fp8_status fp8_gemm_dgrad_mn(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_t* 
     t_last_error.clear();
     fp8_status st = gemm_common("fp8_gemm_dgrad_mn", dyq, (int)dy_fmt, wq, inv_sdy, inv_sw, dx, M, K, N, stream);
     if (st != FP8_OK) return st;
-    hipError_t e = fp8k::launch_gemm_tn(dyq, (int)dy_fmt, 0, wq, 0, 1, inv_sdy, inv_sw, dx, M, K, N, stream);
+    hipError_t e = fp8k::launch_gemm_tn(dyq, (int)dy_fmt, 0, wq, 0, 1, inv_sdy, inv_sw, dx, M, K, N, true, stream);
     if (e != hipSuccess) return fail_hip("fp8_gemm_dgrad_mn", e);
     return FP8_OK;
 }
@@ -418,7 +418,7 @@ fp8_status fp8_gemm_wgrad_mn(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_t* 
     t_last_error.clear();
     fp8_status st = gemm_common("fp8_gemm_wgrad_mn", dyq, (int)dy_fmt, xq, inv_sdy, inv_sx, dw, N, K, M, stream);
     if (st != FP8_OK) return st;
-    hipError_t e = fp8k::launch_gemm_tn(dyq, (int)dy_fmt, 1, xq, 0, 1, inv_sdy, inv_sx, dw, N, K, M, stream);
+    hipError_t e = fp8k::launch_gemm_tn(dyq, (int)dy_fmt, 1, xq, 0, 1, inv_sdy, inv_sx, dw, N, K, M, true, stream);
     if (e != hipSuccess) return fail_hip("fp8_gemm_wgrad_mn", e);
     return FP8_OK;
 }

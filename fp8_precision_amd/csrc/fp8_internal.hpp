@@ -67,9 +67,11 @@ hipError_t launch_swiglu_backward(const void* gu, const void* dh, int64_t M, int
 // out[P, Q] = bf16(RN32(sum_r A[p, r] B[q, r] * RN32(*inv_a * *inv_b))).  Operand
 // layouts: 0 = K-major (A[p, r] at A + p R + r), 1 = MN-major (A[p, r] at
 // A + r P + p; B likewise with Q).  Compiled pairs (A, B): (0, 0), (0, 1), (1, 1).
+// nt_out: the output is written with non-temporal stores (the backward products:
+// their dX and dW then do not displace the operand panels the launch re-reads).
 hipError_t launch_gemm_tn(const uint8_t* A, int fmt_a, int la, const uint8_t* B, int fmt_b, int lb,
                           const float* inv_a, const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R,
-                          hipStream_t stream);
+                          bool nt_out, hipStream_t stream);
 
 // Gate/up forward product with the SwiGLU statistic: out[M, 2F] = A[M, K] . B[2F, K]^T
 // as launch_gemm_tn (e4m3 x e4m3, K-major), and *absmax_h = max(*absmax_h, max |h|)
@@ -77,7 +79,8 @@ hipError_t launch_gemm_tn(const uint8_t* A, int fmt_a, int la, const uint8_t* B,
 hipError_t launch_gemm_gate_up(const uint8_t* A, const uint8_t* B, const float* inv_a, const float* inv_b, void* out,
                                float* absmax_h, int64_t M, int64_t F, int64_t K, hipStream_t stream);
 
-// Two independent products of the same operand formats (and the same B layout) in one launch.
+// Two independent products of the same operand formats (and the same B layout) in one
+// launch: the dgrad and wgrad products of a linear, both stored non-temporally.
 hipError_t launch_gemm_tn_pair(const uint8_t* A0, int la0, const uint8_t* B0, int lb0, const float* ia0,
                                const float* ib0, void* out0, int64_t P0, int64_t Q0, int64_t R0, const uint8_t* A1,
                                int la1, const uint8_t* B1, int lb1, const float* ia1, const float* ib1, void* out1,

@@ -3,7 +3,7 @@ replayed: every replay, with eager work and synchronisations between replays,
 reproduces the eager step's bytes exactly.
 
 The step: clear a statistics buffer (a fill kernel), X and W statistics in one
-launch, e4m3 quantisation with transposed copies, the forward GEMM, the
+launch, their e4m3 quantisation with transposed copies in one launch, the forward GEMM, the
 gate/up GEMM with the SwiGLU statistic in its epilogue and the requant that
 uses it, e5m2 quantisation of dY, the paired backward GEMMs, and the SwiGLU
 backward.
@@ -56,8 +56,8 @@ def test_step_replays_in_a_graph(fp8):
     def step():
         stats.zero_()
         fp8.absmax_accumulate_many([x, w, w_gu], [stats[0:1], stats[1:2], stats[2:3]])
-        fp8.quantize(x, E4M3, stats[0:1], q=o["xq"], qt=o["xqt"], inv_scale=o["ix"])
-        fp8.quantize(w, E4M3, stats[1:2], q=o["wq"], qt=o["wqt"], inv_scale=o["iw"])
+        fp8.quantize_many([x, w], E4M3, [stats[0:1], stats[1:2]], want_qt=True, qs=[o["xq"], o["wq"]],
+                          qts=[o["xqt"], o["wqt"]], inv_scales=[o["ix"], o["iw"]])
         fp8.quantize(w_gu, E4M3, stats[2:3], q=o["guq"], inv_scale=o["igu"])
         fp8.gemm_fwd(o["xq"], o["wq"], o["ix"], o["iw"], out=o["y"])
         fp8.gemm_fwd_swiglu_absmax(o["xq"], o["guq"], o["ix"], o["igu"], stats[3:4], out=o["gu"])
