@@ -42,6 +42,7 @@ _SIGS = {
     "fp8_gemm_dgrad_mn": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_gemm_wgrad_mn": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_gemm_backward_mn": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "fp8_stream_copy": (_i32, [_vp, _vp, _i64, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -434,3 +435,16 @@ def gemm_backward_mn(dyq, dy_fmt, wq, xq, inv_sdy, inv_sw, inv_sx, dx=None, dw=N
          _ptr(dyq), int(dy_fmt), _ptr(wq), _ptr(xq), _ptr(inv_sdy), _ptr(inv_sw), _ptr(inv_sx), _ptr(dx), _ptr(dw),
          M, N, K)
     return dx, dw
+
+
+def stream_copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    """dst <- src byte for byte (fp8_stream_copy): the streaming-copy reference
+    that the statistic and quantisation calls are measured against.  Both
+    contiguous device tensors of the same byte size, a multiple of 16."""
+    _dev_tensor(src, "src")
+    _dev_tensor(dst, "dst")
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("src and dst must hold the same number of bytes")
+    _run("fp8_stream_copy", _lib.fp8_stream_copy, (src, dst), _ptr(src), _ptr(dst), nb)
+    return dst

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp8_precision.so")
-SOURCES = ["quant.hip", "swiglu.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["quant.hip", "swiglu.hip", "gemm.hip", "copy.hip", "api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of the code object on purpose, and

@@ -447,4 +447,17 @@ fp8_status fp8_gemm_backward_mn(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_
     return FP8_OK;
 }
 
+fp8_status fp8_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream)
+{
+    t_last_error.clear();
+    if (!src || !dst) return fail(FP8_ERR_INVALID, "fp8_stream_copy: null pointer");
+    if (bytes <= 0 || bytes > 2 * kMaxElems) return fail(FP8_ERR_INVALID, "fp8_stream_copy: bytes must be in [1, 2^41]");
+    if (bytes % 16 != 0 || !aligned(src, 16) || !aligned(dst, 16))
+        return fail(FP8_ERR_UNSUPPORTED, "fp8_stream_copy: bytes a multiple of 16, both buffers 16-byte aligned");
+    if (overlap(src, bytes, dst, bytes)) return fail(FP8_ERR_INVALID, "fp8_stream_copy: src and dst overlap");
+    hipError_t e = fp8k::launch_stream_copy(src, dst, bytes, stream);
+    if (e != hipSuccess) return fail_hip("fp8_stream_copy", e);
+    return FP8_OK;
+}
+
 }  // extern "C"

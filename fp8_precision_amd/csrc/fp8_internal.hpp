@@ -86,4 +86,7 @@ hipError_t launch_gemm_tn_pair(const uint8_t* A0, int la0, const uint8_t* B0, in
                                int la1, const uint8_t* B1, int lb1, const float* ia1, const float* ib1, void* out1,
                                int64_t P1, int64_t Q1, int64_t R1, int fmt_a, int fmt_b, hipStream_t stream);
 
+// dst[0, bytes) = src[0, bytes): the streaming-copy reference (bytes % 16 == 0, both 16-byte aligned).
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 }  // namespace fp8k

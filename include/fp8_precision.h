@@ -331,6 +331,19 @@ fp8_status fp8_gemm_backward_mn(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_
                                 const float* inv_sdy, const float* inv_sw, const float* inv_sx,
                                 void* dx, void* dw, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/*
+ * Measurement reference, not a step of the FP8 method: a plain device copy
+ * dst[0, bytes) = src[0, bytes), built like the streaming kernels above
+ * (16-byte vectors, non-temporal loads, the launch shape at which a copy
+ * reaches its highest measured rate on this chip).  The bandwidth of the
+ * statistic and quantisation calls is reported as a fraction of what this
+ * copy reaches on the same machine.
+ *
+ *   src, dst  device buffers of `bytes` bytes, 16-byte aligned, not overlapping
+ *   bytes     > 0 and a multiple of 16 (else FP8_ERR_INVALID / FP8_ERR_UNSUPPORTED)
+ */
+fp8_status fp8_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -327,3 +327,19 @@ def test_quantize_many_validation(lib):
     assert call(**{**ok, "rows": [16, 24]}) == UNSUPPORTED                           # rows % 16
     assert call(**{**ok, "cols": [16, 40]}) == UNSUPPORTED                           # cols % 16
     assert call(**{**ok, "xs": [A16, B16 + 2]}) == UNSUPPORTED                       # misaligned input
+
+
+def test_stream_copy_validation(lib):
+    f = lib.fp8_stream_copy
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    assert f(None, B16, 64, None) == INVALID
+    assert f(A16, None, 64, None) == INVALID
+    assert f(A16, B16, 0, None) == INVALID
+    assert f(A16, B16, -16, None) == INVALID
+    assert f(A16, A16 + 32, 64, None) == INVALID                    # overlapping
+    assert b"overlap" in lib.fp8_last_error()
+    assert f(A16, B16, 40, None) == UNSUPPORTED                     # not a multiple of 16
+    assert f(A16 + 8, B16, 64, None) == UNSUPPORTED                 # misaligned source
+    assert f(A16, B16 + 4, 64, None) == UNSUPPORTED                 # misaligned destination
+
