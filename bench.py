@@ -59,9 +59,12 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E peak
 # edge tiles, layout set, half tiles, gate/up with the SwiGLU statistic,
 # non-temporal output stores -- the backward products); a GEMM call whose last
 # round is balanced runs a second launch of the half-tile instantiation
-GEMM_KERNEL = {(0, 0, 0): "fp8k::gemm_tn_kernel<0, 0, false, 0, false, false, false>",
-               (1, 0, 0): "fp8k::gemm_tn_kernel<1, 0, false, 0, false, false, true>",
-               (1, 0, 1): "fp8k::gemm_tn_kernel<1, 0, false, 1, false, false, true>",
+# ("bwd", format of dY, layout set): the dgrad + wgrad launches
+GEMM_KERNEL = {"fwd": "fp8k::gemm_tn_kernel<0, 0, false, 0, false, false, false>",
+               ("bwd", 1, 0): "fp8k::gemm_tn_kernel<1, 0, false, 0, false, false, true>",
+               ("bwd", 1, 1): "fp8k::gemm_tn_kernel<1, 0, false, 1, false, false, true>",
+               ("bwd", 0, 0): "fp8k::gemm_tn_kernel<0, 0, false, 0, false, false, true>",
+               ("bwd", 0, 1): "fp8k::gemm_tn_kernel<0, 0, false, 1, false, false, true>",
                "gate_up": "fp8k::gemm_tn_kernel<0, 0, false, 0, false, true, false>"}
 
 
@@ -129,7 +132,7 @@ WORKLOADS = {
 
 
 def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, fused_absmax_h=False,
-               quant_mode="pair"):
+               quant_mode="pair", dy_fmt=None):
     """Inputs and the ordered list of calls of one layer step of a configuration.
 
     The step starts by clearing its buffer of per-tensor absmax statistics (one
@@ -158,13 +161,14 @@ def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, 
     recompute = cfg.recompute
     M = cfg.M
     E4M3, E5M2 = fp8.E4M3, fp8.E5M2
+    DY = E5M2 if dy_fmt is None else dy_fmt       # format of the output gradients
     ops = []
     bufs = {}
     f32 = lambda: torch.empty(1, dtype=torch.float32, device=dev)
     u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
     bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)
     lin = {l.name: (i, l) for i, l in enumerate(cfg.linears)}
-    gemm_fwd_kernel = GEMM_KERNEL[(0, 0, 0)]
+    gemm_fwd_kernel = GEMM_KERNEL["fwd"]
     # the step's per-tensor absmax statistics live in one buffer, cleared once at
     # the start of the step; each absmax accumulates into its slot
     stats = torch.empty(64, dtype=torch.float32, device=dev)
@@ -329,13 +333,13 @@ def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, 
             dyq, dyqt = u8(M, L.N), (None if mn else u8(L.N, M))
             Fh = L.N // 2
             ops.append(Op("swiglu_backward", lambda dyq=dyq, dyqt=dyqt, am=am, sc=sc, inv=inv_dy:
-                          fp8.swiglu_backward(gu_bwd, dh, E5M2, q=dyq, qt=dyqt, absmax=am, scale=sc, inv_scale=inv),
+                          fp8.swiglu_backward(gu_bwd, dh, DY, q=dyq, qt=dyqt, absmax=am, scale=sc, inv_scale=inv),
                           "swiglu_bwd", (12 + (4 if not mn else 2)) * M * Fh,
                           meta={"M": M, "F": Fh, "qt": not mn}))
         else:
             dy = workloads.draw_dy(cfg, li).to(dev)
             bufs["dy_" + name] = dy
-            dyq, dyqt, inv_dy, _ = quant_ops(f"dY_{name}", dy, M, L.N, E5M2, not mn)
+            dyq, dyqt, inv_dy, _ = quant_ops(f"dY_{name}", dy, M, L.N, DY, not mn)
         dx = bf(M, L.K)
         dw = bf(L.N, L.K)
         if name == "down":
@@ -343,12 +347,12 @@ def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, 
         # dgrad dX = dY . W and wgrad dW = dY^T . X in one launch
         if mn:
             fn = (lambda dyq=dyq, wq=f["wq"], xq=f["xq"], a=inv_dy, b=f["inv_w"], c=f["inv_x"], dx=dx, dw=dw:
-                  fp8.gemm_backward_mn(dyq, E5M2, wq, xq, a, b, c, dx, dw))
+                  fp8.gemm_backward_mn(dyq, DY, wq, xq, a, b, c, dx, dw))
         else:
             fn = (lambda dyq=dyq, dyqt=dyqt, wqt=f["wqt"], xqt=f["xqt"], a=inv_dy, b=f["inv_w"], c=f["inv_x"],
-                  dx=dx, dw=dw: fp8.gemm_backward(dyq, dyqt, E5M2, wqt, xqt, a, b, c, dx, dw))
-        ops.append(Op(f"gemm_backward {name}", fn, "gemm", 4 * M * L.N * L.K, GEMM_KERNEL[(1, 0, 1 if mn else 0)],
-                      {"probs": [(M, L.K, L.N, E5M2), (L.N, L.K, M, E5M2)], "kmajor": not mn}))
+                  dx=dx, dw=dw: fp8.gemm_backward(dyq, dyqt, DY, wqt, xqt, a, b, c, dx, dw))
+        ops.append(Op(f"gemm_backward {name}", fn, "gemm", 4 * M * L.N * L.K, GEMM_KERNEL[("bwd", DY, 1 if mn else 0)],
+                      {"probs": [(M, L.K, L.N, DY), (L.N, L.K, M, DY)], "kmajor": not mn}))
     return ops, bufs
 
 
@@ -824,6 +828,8 @@ def main():
                     help="pair: each linear's X and W quantised in one launch (their statistics in one launch for "
                          "QKV and O); linear: X and W quantised in separate launches; step: the four weights and the "
                          "first input quantised together at the start of the step")
+    ap.add_argument("--dy-format", choices=("e5m2", "e4m3"), default="e5m2",
+                    help="format of the output gradients dY (e5m2: the default reading; e4m3: the all-E4M3 variant)")
     ap.add_argument("--vs-hipblaslt", action="store_true",
                     help="only compare every GEMM call of the step with hipBLASLt (torch._scaled_mm) on the same "
                          "operand bytes, interleaved, and print that as the JSON line (context, not the metric)")
@@ -855,7 +861,8 @@ def main():
                                         "runs": sus}}))
         return
     ops, bufs = build_step(fp8, dev, args.workload, args.layout, args.swiglu_backward,
-                           args.fused_swiglu_absmax, args.quant_mode)
+                           args.fused_swiglu_absmax, args.quant_mode,
+                           fp8.E4M3 if args.dy_format == "e4m3" else fp8.E5M2)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         run_step(ops)
@@ -933,6 +940,7 @@ def main():
                    else "drawn output gradients",
                    "swiglu_absmax": ("gate/up GEMM epilogue" if args.fused_swiglu_absmax
                                      else "separate reduction pass"),
+                   "dy_format": args.dy_format,
                    "quantisation_launches": {"pair": "X and W of a linear in one launch",
                                              "linear": "X and W of a linear in separate launches",
                                              "step": "the weights and the layer input in one launch at step start"
