@@ -393,6 +393,40 @@ STREAM_KINDS = ("absmax", "quantize", "swiglu", "swiglu_bwd")
 FLUSH_BYTES = 1 << 30               # a cold call follows a read of this many bytes
 
 
+def time_stream_phases(ops, steps, stream):
+    """The step's streaming phases -- each maximal run of consecutive absmax /
+    quantise / SwiGLU calls between two GEMMs -- timed with one event pair per
+    phase over `steps` steps: (seconds per step in streaming phases, bytes per
+    step).  Fewer events than one pair per call, so less of their dispatch and
+    completion overhead enters the figure."""
+    phases, cur = [], []
+    for op in ops:
+        if op.kind in STREAM_KINDS:
+            cur.append(op)
+        elif cur:
+            phases.append(cur)
+            cur = []
+    if cur:
+        phases.append(cur)
+    evs = []
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        k = 0
+        for op in ops:
+            if k < len(phases) and op is phases[k][0]:
+                a = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+            op.fn()
+            if k < len(phases) and op is phases[k][-1]:
+                b = torch.cuda.Event(enable_timing=True)
+                b.record(stream)
+                evs.append((a, b))
+                k += 1
+    torch.cuda.synchronize()
+    total = sum(a.elapsed_time(b) * 1e-3 for a, b in evs) / steps
+    return total, sum(op.work for ph in phases for op in ph), len(phases)
+
+
 def streaming_cold(fp8, ops, stream, dev, reps=20, warm=3):
     """Every absmax / quantise / SwiGLU call of the step timed on its own with a
     cold Infinity Cache (median of `reps`, each after a 1 GiB read: a read
@@ -913,6 +947,8 @@ def main():
     qt = sum(float(np.mean(per_all[op.name])) for op in ops if op.kind in STREAM_KINDS)
     qb = sum(op.work for op in ops if op.kind in STREAM_KINDS)
     quant_gbs = qb / qt / 1e9
+    ph_s, ph_b, n_ph = time_stream_phases(ops, max(3, args.steps // 2), stream)
+    phase_gbs = ph_b / ph_s / 1e9
     copy_gbs, cold = (None, None) if args.no_cold else streaming_cold(fp8, ops, stream, dev)
 
     shapes = {}
@@ -972,6 +1008,10 @@ def main():
     line["streaming"] = {
         "unit": "GB/s", "hbm_peak": HBM_PEAK_GBS, "copy_cold_gbs": round(copy_gbs, 1) if copy_gbs else None,
         "copy": "fp8_stream_copy, 256 MiB each way after a 1 GiB read (both directions counted)",
+        "in_step_phases": {"gbs": round(phase_gbs, 1), "pct_hbm": round(100 * phase_gbs / HBM_PEAK_GBS, 1),
+                           "vs_copy": round(phase_gbs / copy_gbs, 3) if copy_gbs else None, "bytes": int(ph_b),
+                           "phases": n_ph, "note": "one event pair per run of consecutive streaming calls between "
+                                                   "two GEMMs"},
         "in_step": {"gbs": round(quant_gbs, 1), "pct_hbm": round(100 * quant_gbs / HBM_PEAK_GBS, 1),
                     "vs_copy": round(quant_gbs / copy_gbs, 3) if copy_gbs else None,
                     "bytes": int(qb), "note": "bytes-weighted over the step's absmax/quantise/SwiGLU calls"},
