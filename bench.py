@@ -88,19 +88,30 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_traffic_layer7b.txt")
 GEMM_SOURCE = os.path.join(ROOT, "fp8_precision_amd", "csrc", "gemm.hip")
 
 
+def gemm_code_hash():
+    """SHA-256 (first 16 hex digits) of the GEMM source with its comments and
+    whitespace removed: the key that ties the committed traffic counters to the
+    kernel code they were taken on (a comment edit does not change it)."""
+    import hashlib
+    import re
+    src = open(GEMM_SOURCE).read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return hashlib.sha256("".join(src.split()).encode()).hexdigest()[:16]
+
+
 def measured_traffic(kernel, tail_fraction=0.0):
     """HBM bytes per call of `kernel` from the committed rocprofv3 PMC summary
     (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by a plain copy of known
     size; a call adds its half-tile launch's bytes, `tail_fraction` of the calls
-    have one), or None when the summary is missing or the GEMM source changed
+    have one), or None when the summary is missing or the GEMM code changed
     since it was taken."""
-    import hashlib
     try:
         line = next(l for l in open(TRAFFIC_SUMMARY) if l.startswith("TRAFFIC_JSON "))
     except (OSError, StopIteration):
         return None
     data = json.loads(line[len("TRAFFIC_JSON "):])
-    if hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()[:16] != data["gemm_source_sha256_16"]:
+    if gemm_code_hash() != data.get("gemm_code_sha256_16"):
         return None
     b = data["per_dispatch_bytes"].get(kernel)
     if b is None:

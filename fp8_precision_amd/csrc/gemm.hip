@@ -42,9 +42,15 @@
 //  - The instruction's operands are swapped (B fragment first), so each lane
 //    ends with 4 consecutive output columns of one row; the epilogue stages
 //    them through LDS and writes full 256-byte row segments.
-//  - Persistent: one workgroup per CU walks tiles in a grouped raster order,
-//    renumbered XCD-major so that the 32 CUs of an XCD (sharing one L2) work on
-//    consecutive tiles; the next tile's first stages load during the epilogue.
+//  - Persistent: one workgroup per CU walks tiles in a grouped raster order
+//    (8 tile rows per group; 4 for a backward problem wider than 32 column
+//    tiles), renumbered XCD-major so that the 32 CUs of an XCD (sharing one L2)
+//    work on consecutive tiles; the next tile's first stages load during the
+//    epilogue.
+//  - Output stores: ordinary for the forward products (the statistic or
+//    SwiGLU pass that follows reads them from the Infinity Cache); non-temporal
+//    for the backward products (a template argument: with a run-time choice the
+//    compiler merged the two store forms and dropped the hint).
 //    When the last round would keep at most half of the CUs busy, its tiles are
 //    split into 128 x 256 half tiles (same loads and fragment reads, a 64 x 128
 //    wave tile), which halves that round.
@@ -72,7 +78,7 @@ constexpr int kStage = kStageA + kStageB;     // 64 KB
 constexpr int kLds = 2 * kStage;              // 128 KB
 constexpr int kEpiRows = 32;                  // epilogue chunk: 32 rows x 128 columns of bf16 per wave
 constexpr int kEpiWave = kEpiRows * 256;      // 8 KB per wave, 32 KB per workgroup (LDS total 160 KB)
-constexpr int kGroupM = 8;                    // tile rows per raster group
+constexpr int kGroupM = 8;                    // tile rows per raster group (the default)
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
 // vmcnt[5:4] at [15:14]); expcnt and lgkmcnt are left at their maxima.
