@@ -46,14 +46,13 @@
 //    (8 tile rows per group; 4 for a backward problem wider than 32 column
 //    tiles), renumbered XCD-major so that the 32 CUs of an XCD (sharing one L2)
 //    work on consecutive tiles; the next tile's first stages load during the
-//    epilogue.
+//    epilogue.  When the last round would keep at most half of the CUs busy,
+//    its tiles are split into 128 x 256 half tiles (same loads and fragment
+//    reads, a 64 x 128 wave tile), which halves that round.
 //  - Output stores: ordinary for the forward products (the statistic or
 //    SwiGLU pass that follows reads them from the Infinity Cache); non-temporal
 //    for the backward products (a template argument: with a run-time choice the
 //    compiler merged the two store forms and dropped the hint).
-//    When the last round would keep at most half of the CUs busy, its tiles are
-//    split into 128 x 256 half tiles (same loads and fragment reads, a 64 x 128
-//    wave tile), which halves that round.
 //  - Deterministic: every output is reduced by one wave in a fixed order.
 #include "fp8_device.hpp"
 #include "fp8_internal.hpp"
@@ -559,10 +558,10 @@ __device__ __forceinline__ void start_tile(Sources& src, const Work& w, uint32_t
     }
 }
 
-// A 16-byte output store; NT: non-temporal, for outputs that nothing on the path
-// reads next (the backward products' dX and dW): kept out of the caches, they do
-// not displace the operand panels that the XCDs keep re-fetching (measured on the
-// 7B-layer step: 1.1% shorter, the backward calls 2-3% faster).
+// A 16-byte output store; NT: non-temporal, for the backward products' dX and dW:
+// kept out of the caches, they do not displace the operand panels that the XCDs
+// keep re-fetching (measured on the 7B-layer step: 1.1% shorter, the backward
+// calls 2-3% faster).
 template <bool NT>
 __device__ __forceinline__ void store16(uint8_t* p, const uint4& v)
 {
