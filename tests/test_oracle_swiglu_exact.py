@@ -10,12 +10,12 @@ formula, so the textbook silu(g) = g / (1 + e^-g) is used):
     s_g = RN32(g / t)
     h   = RN32(s_g * u)
 
-Here every step is recomputed in this file from its definition: e^-g from
-Python's ``decimal`` (60 digits, and the rounding decision is made only when
-the value is provably away from a rounding boundary), the sum, quotient and
-product exactly on ``fractions.Fraction``, and each result rounded once to
-binary32 (nearest, ties to even, subnormals and overflow included) by an
-integer procedure written here.  Nothing is imported from the GPU library or
+Here every step is recomputed from its definition (``exact_f32``, the tests'
+exact binary32 helpers): e^-g from Python's ``decimal`` (60 digits, and the
+rounding decision is made only when the value is provably away from a rounding
+boundary), the sum, quotient and product exactly on ``fractions.Fraction``, and
+each result rounded once to binary32 (nearest, ties to even, subnormals and
+overflow included) by an integer procedure.  Nothing is imported from the GPU library or
 its table generator.  The oracle's h must equal it bit for bit for every
 finite bf16 gate value (u = 1, so h = s_g), and for a seeded sample of gate
 values times several up values (the last rounding).  A plausible slip -- g
@@ -23,53 +23,11 @@ multiplied by RN32(1 / t) instead of divided by t, an FMA contraction of any
 two steps, a float exponential that is not correctly rounded, or the halves
 of [gate | up] swapped -- changes some of these bits.
 """
-import decimal
 from fractions import Fraction
 
 import numpy as np
 
-decimal.getcontext().prec = 60
-TWO = Fraction(2)
-F32_OVERFLOW = TWO ** 128 - TWO ** 103      # at or above: rounds to infinity
-
-
-def rn32(x: Fraction) -> float:
-    """x rounded once to the nearest binary32 (ties to even), as a Python float."""
-    if x == 0:
-        return 0.0
-    neg = x < 0
-    a = -x if neg else x
-    if a >= F32_OVERFLOW:
-        return -np.inf if neg else np.inf
-    e = a.numerator.bit_length() - a.denominator.bit_length()
-    if a < TWO ** e:
-        e -= 1                                   # now 2^e <= a < 2^(e+1)
-    q = max(e, -126) - 23                        # the binary32 quantum at a (subnormals: 2^-149)
-    m = a / TWO ** q
-    n = m.numerator // m.denominator
-    r = m - n
-    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
-        n += 1
-    v = float(n * TWO ** q)                      # exact in binary64
-    return -v if neg else v
-
-
-def exp_neg_rn32(g: float) -> float:
-    """RN32(e^-g), the decision checked to lie clear of the rounding boundary."""
-    if g < -100.0:            # e^100 > FLT_MAX (ln FLT_MAX = 88.72): rounds to infinity
-        return np.inf
-    if g > 110.0:             # e^-110 < 2^-151, below half the smallest subnormal
-        return 0.0
-    d = (-decimal.Decimal(g)).exp()
-    if d >= decimal.Decimal(2 ** 128 - 2 ** 103):
-        return np.inf
-    f = np.float32(float(d))
-    cands = {float(c) for c in (np.nextafter(f, np.float32(0)), f, np.nextafter(f, np.float32(np.inf)))
-             if np.isfinite(c)}
-    dist = sorted((abs(decimal.Decimal(c) - d), c) for c in cands)
-    # the nearest candidate must win by far more than the 60-digit evaluation error
-    assert dist[1][0] - dist[0][0] > d * decimal.Decimal(10) ** -50, g
-    return dist[0][1]
+from exact_f32 import F32_OVERFLOW, TWO, exp_neg_rn32, f32_bits, finite_bf16_patterns, rn32
 
 
 def swiglu_exact(gbits: int, ubits: int) -> float:
@@ -88,15 +46,6 @@ def swiglu_exact(gbits: int, ubits: int) -> float:
     if u == 0.0:
         return float(np.float32(s) * np.float32(u))
     return rn32(Fraction(s) * Fraction(u))
-
-
-def f32_bits(v) -> np.ndarray:
-    return np.asarray(v, np.float32).view(np.uint32)
-
-
-def finite_bf16_patterns():
-    b = np.arange(65536, dtype=np.uint32)
-    return b[(b & 0x7F80) != 0x7F80].astype(np.uint16)
 
 
 def test_exact_rounding_helper():
