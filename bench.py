@@ -880,8 +880,8 @@ def main():
                          "operand bytes, interleaved, and print that as the JSON line (context, not the metric)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every box here has one GPU "
-              "and this path has no multi-GPU code.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the path has no multi-GPU code; "
+              "its value is one GPU's throughput.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (MI355X)", file=sys.stderr)
