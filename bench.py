@@ -582,76 +582,38 @@ def cpu_baseline(ops, gemm_rows):
                        f"generation included), estimated full step {est:.1f} s on {threads} threads")}
 
 
-def gemm_shapes(fp8, dev, cfg_name, reps=5, warm=2):
-    """The FP8 GEMM calls of a configuration's layer (each linear's forward and its
-    dgrad + wgrad launch) on device-drawn operands of the step's kind (normal
-    draws -- Student-t(3) activations with outlier channels where the
-    configuration has them -- quantised with their own absmax, dY to e5m2), run
-    as a sequence of
-    GEMMs only -- all forwards, then all backwards -- `reps` times after `warm`
-    untimed rounds, every call timed with HIP events.  Back to back, without
-    the step's memory-bound calls in between, the chip runs nearer its power
-    limit than in the step, so these rates are a lower bound for the step's."""
-    cfg = workloads.CONFIGS[cfg_name]
-    M = cfg.M
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(cfg.seed)
-
-    def codes(r, c, fmt, want_qt, activation=False):
-        if activation and cfg.x_dist == "student_t":
-            # the configuration's activations: Student-t(3), 0.1% of the channels x50
-            torch.manual_seed(cfg.seed)
-            x = torch.distributions.StudentT(torch.tensor(3.0, device=dev)).sample((r, c))
-            pick = torch.randperm(c, generator=gen, device=dev)[:int(round(cfg.x_outlier_frac * c))]
-            x[:, pick] *= 50.0
-            x = x.to(torch.bfloat16)
-        else:
-            x = torch.randn((r, c), generator=gen, device=dev, dtype=torch.bfloat16)
-        q, qt, _, inv = fp8.quantize(x, fmt, fp8.absmax(x), want_q=True, want_qt=want_qt)
-        del x
-        return q, qt, inv
-
-    calls = []
-    for L in cfg.linears:
-        xq, xqt, ix = codes(M, L.K, fp8.E4M3, True, activation=True)
-        wq, wqt, iw = codes(L.N, L.K, fp8.E4M3, True)
-        dyq, dyqt, idy = codes(M, L.N, fp8.E5M2, True)
-        y = torch.empty((M, L.N), dtype=torch.bfloat16, device=dev)
-        dx = torch.empty((M, L.K), dtype=torch.bfloat16, device=dev)
-        dw = torch.empty((L.N, L.K), dtype=torch.bfloat16, device=dev)
-        calls.append((f"gemm_fwd {L.name}", 2 * M * L.N * L.K,
-                      lambda xq=xq, wq=wq, ix=ix, iw=iw, y=y: fp8.gemm_fwd(xq, wq, ix, iw, out=y)))
-        calls.append((f"gemm_backward {L.name}", 4 * M * L.N * L.K,
-                      lambda a=(dyq, dyqt, wqt, xqt, idy, iw, ix, dx, dw):
-                      fp8.gemm_backward(a[0], a[1], fp8.E5M2, a[2], a[3], a[4], a[5], a[6], dx=a[7], dw=a[8])))
-    order = [c for c in calls if c[0].startswith("gemm_fwd")] + [c for c in calls if c[0].startswith("gemm_back")]
-    for _ in range(warm):
-        for _, _, fn in order:
-            fn()
-    times = {name: [] for name, _, _ in order}
-    for _ in range(reps):
-        evs = []
-        for name, _, fn in order:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            evs.append((name, a, b))
-        torch.cuda.synchronize()
-        for name, a, b in evs:
-            times[name].append(a.elapsed_time(b) * 1e-3)
+def step_shapes(fp8, dev, stream, cfg_name, steps=5, warmup=5):
+    """The GEMM figures of another configuration's layer, measured inside that
+    configuration's own step (the same construction as the headline's: its
+    inputs drawn by workloads.py, every quantisation and SwiGLU call in place,
+    so each GEMM reads operands the step has just written, as in training):
+    `warmup` untimed steps, `steps` timed ones with no event inside, then as many
+    with an event pair around every GEMM call for the per-call rates."""
+    ops, _ = build_step(fp8, dev, cfg_name)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        run_step(ops)
+    _, gpu_s, _ = time_steps(ops, steps, stream, instrument_kinds=())
+    _, _, per = time_steps(ops, steps, stream)
     rows, tf, tt = [], 0.0, 0.0
-    for name, flop, _ in order:
-        t = float(np.median(times[name]))
-        rows.append({"call": name, "tflops": round(flop / t / 1e12, 1),
-                     "frac": round(flop / t / 1e12 / FP8_PEAK_TFLOPS, 4), "us": round(t * 1e6, 1)})
-        tf += flop
+    for op in ops:
+        if op.kind != "gemm":
+            continue
+        t = float(np.mean(per[op.name]))
+        rows.append({"call": op.name, "tflops": round(op.work / t / 1e12, 1),
+                     "frac": round(op.work / t / 1e12 / FP8_PEAK_TFLOPS, 4), "us": round(t * 1e6, 1)})
+        tf += op.work
         tt += t
-    del calls, order
+    step_s = gpu_s / steps
+    del ops
+    torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return {"workload": WORKLOADS[cfg_name], "gemm_tflops": round(tf / tt / 1e12, 1),
-            "frac": round(tf / tt / 1e12 / FP8_PEAK_TFLOPS, 4),
-            "timing": f"GEMMs only, back to back, median of {reps} after {warm} untimed rounds", "calls": rows}
+            "frac": round(tf / tt / 1e12 / FP8_PEAK_TFLOPS, 4), "ms_per_step": round(step_s * 1e3, 4),
+            "step_tflops": round(tf / step_s / 1e12, 1),
+            "timing": f"inside the configuration's own step: {warmup} untimed steps, {steps} timed without events, "
+                      f"then {steps} with an event pair around every GEMM call",
+            "calls": rows}
 
 
 def vs_hipblaslt(fp8, ops, dev, reps=10, rounds=3):
@@ -868,7 +830,8 @@ def main():
                     help="skip the cold-cache per-call streaming measurement")
     ap.add_argument("--no-clock", action="store_true", help="skip the sustained-clock sampling (amd-smi)")
     ap.add_argument("--no-shapes", action="store_true",
-                    help="skip the 14B- and 32B-class GEMM figures reported with the layer7b workload")
+                    help="skip the 14B- and 32B-class layer steps (their GEMM figures) reported with the layer7b "
+                         "workload")
     ap.add_argument("--quant-mode", choices=("pair", "linear", "step"), default="pair",
                     help="pair: each linear's X and W quantised in one launch (their statistics in one launch for "
                          "QKV and O); linear: X and W quantised in separate launches; step: the four weights and the "
@@ -965,7 +928,7 @@ def main():
     shapes = {}
     if args.workload == "layer7b" and not args.no_shapes:
         for other in ("layer14b", "layer32b"):
-            shapes[other] = gemm_shapes(fp8, dev, other)
+            shapes[other] = step_shapes(fp8, dev, stream, other)
     clock = None if args.no_clock else sustained_clock(ops)
     want_cpu = not args.no_cpu_baseline and (args.workload == "layer7b" or args.cpu_baseline)
     cpu = cpu_baseline(ops, args.cpu_gemm_rows) if want_cpu else None
