@@ -327,7 +327,17 @@ fp8_status fp8_gemm_fwd(const uint8_t* xq, const uint8_t* wq, const float* inv_s
     t_last_error.clear();
     fp8_status st = gemm_common("fp8_gemm_fwd", xq, FP8_E4M3, wq, inv_sx, inv_sw, y, M, N, K, stream);
     if (st != FP8_OK) return st;
-    hipError_t e = fp8k::launch_gemm_tn(xq, 0, 0, wq, 0, 0, inv_sx, inv_sw, y, M, N, K, false, stream);
+    // Y is stored non-temporally when it is too large to stay in the 256 MiB Infinity
+    // Cache for the pass that reads it next while the operands are small enough to
+    // stay there: then ordinary stores would only push out the operand panels the
+    // launch keeps re-reading.  Measured on MI355X: the 14B-class gate/up forward
+    // (453 MB out, 183 MB in) 9.6% faster, the step 1.6% shorter; with operands that
+    // do not fit either (the 32B-class gate/up forward, 367 MB in) non-temporal
+    // stores were 1% slower, and below 256 MiB of output (every 7B-class forward)
+    // the next pass reads Y from the cache.
+    const int64_t cache_bytes = (int64_t)256 << 20;
+    const bool nt = 2 * M * N >= cache_bytes && (M + N) * K <= cache_bytes;
+    hipError_t e = fp8k::launch_gemm_tn(xq, 0, 0, wq, 0, 0, inv_sx, inv_sw, y, M, N, K, nt, stream);
     if (e != hipSuccess) return fail_hip("fp8_gemm_fwd", e);
     return FP8_OK;
 }

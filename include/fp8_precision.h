@@ -242,10 +242,12 @@ fp8_status fp8_swiglu_backward(const void* gu, const void* dh, int64_t M, int64_
  * 32-bit); anything else returns FP8_ERR_UNSUPPORTED.
  * Cache policy of the output (bytes and results are the same either way):
  * fp8_gemm_fwd writes Y with ordinary stores, so the statistic or SwiGLU pass
- * that reads it next finds it in the Infinity Cache; every backward product
- * (dgrad, wgrad, and the pair and MN-major forms below) stores dX / dW
- * non-temporally, so the outputs do not displace the operand panels that the
- * rest of the launch re-reads.
+ * that reads it next finds it in the 256 MiB Infinity Cache -- unless Y is
+ * 256 MiB or more while X and W together are at most 256 MiB, when Y is stored
+ * non-temporally (it could not stay cached, and would push out the operands);
+ * every backward product (dgrad, wgrad, and the pair and MN-major forms below)
+ * stores dX / dW non-temporally, so the outputs do not displace the operand
+ * panels that the rest of the launch re-reads.
  */
 fp8_status fp8_gemm_fwd(const uint8_t* xq, const uint8_t* wq, const float* inv_sx,
                         const float* inv_sw, void* y, int64_t M, int64_t N, int64_t K,
