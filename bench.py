@@ -217,19 +217,28 @@ def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, 
         qs = [u8(r, c) for r, c in shp]
         qts = [u8(c, r) if t else None for (r, c), t in zip(shp, want_t)]
         scs, invs = [f32(), f32()], [f32(), f32()]
+        # the transposed copies are for the backward pass: written non-temporally
         ops.append(Op(f"quantize X_{name}+W_{name}",
                       lambda: fp8.quantize_many([x, w], E4M3, [am_x, am_w], want_q=True, want_qt=want_t, qs=qs,
-                                                qts=qts, scales=scs, inv_scales=invs),
+                                                qts=qts, scales=scs, inv_scales=invs, qt_later=True),
                       "quantize", sum((4 if t else 3) * r * c for (r, c), t in zip(shp, want_t)),
                       meta={"group": [{"rows": r, "cols": c, "fmt": E4M3, "qt": t} for (r, c), t in zip(shp, want_t)]}))
         return qs[0], qts[0], invs[0], am_x, qs[1], qts[1], invs[1]
 
-    def quant_ops(tag, x, rows, cols, fmt, want_qt):
+    def quant_ops(tag, x, rows, cols, fmt, want_qt, qt_later=False):
         k = next(slots)
         am = stats[k:k + 1]
         ops.append(Op(f"absmax {tag}", lambda: fp8.absmax(x, am, accumulate=True), "absmax", 2 * rows * cols,
                       meta={"rows": rows, "cols": cols, "fmt": fmt}))
-        return quantize_op(tag, x, rows, cols, fmt, am, want_qt) + (am,)
+        if not (qt_later and want_qt):
+            return quantize_op(tag, x, rows, cols, fmt, am, want_qt) + (am,)
+        # a forward weight's transposed copy is for the backward pass: written non-temporally
+        q, qt, sc, inv = u8(rows, cols), u8(cols, rows), f32(), f32()
+        ops.append(Op(f"quantize {tag}", lambda: fp8.quantize_many([x], fmt, [am], want_q=True, want_qt=True, qs=[q],
+                                                                   qts=[qt], scales=[sc], inv_scales=[inv],
+                                                                   qt_later=True),
+                      "quantize", 4 * rows * cols, meta={"rows": rows, "cols": cols, "fmt": fmt, "qt": True}))
+        return q, qt, inv, am
 
     def gemm_fwd_op(tag, xq, wq, ix, iw, y, L, am_h=None):
         if am_h is None:
@@ -279,7 +288,7 @@ def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, 
         scs, invs = [f32() for _ in tags], [f32() for _ in tags]
         ops.append(Op("quantize [" + ", ".join(tags) + "]",
                       lambda: fp8.quantize_many(tens, E4M3, ams, want_q=True, want_qt=want_t, qs=qs, qts=qts,
-                                                scales=scs, inv_scales=invs),
+                                                scales=scs, inv_scales=invs, qt_later=True),
                       "quantize", sum((4 if t else 3) * r * c for (r, c), t in zip(shp, want_t)),
                       meta={"group": [{"rows": r, "cols": c, "fmt": E4M3, "qt": t} for (r, c), t in zip(shp, want_t)]}))
         for k, t in enumerate(tags):
@@ -289,7 +298,7 @@ def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, 
         x, w = xs[name], ws[name]
         if group_weights:
             if name != "qkv":
-                xq, xqt, inv_x, am_x = quant_ops(f"X_{name}", x, M, L.K, E4M3, keep_xt[name])
+                xq, xqt, inv_x, am_x = quant_ops(f"X_{name}", x, M, L.K, E4M3, keep_xt[name], qt_later=True)
             else:
                 xq, xqt, inv_x, am_x = qd["X_qkv"]
             wq, wqt, inv_w, _ = qd[f"W_{name}"]
@@ -302,8 +311,8 @@ def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, 
             # the gate/up weight is streamed non-temporally: a shared launch would
             # stream X too and cost its quantisation the Infinity Cache, for no
             # shorter statistics pass (measured)
-            xq, xqt, inv_x, am_x = quant_ops(f"X_{name}", x, M, L.K, E4M3, keep_xt[name])
-            wq, wqt, inv_w, _ = quant_ops(f"W_{name}", w, L.N, L.K, E4M3, not mn)
+            xq, xqt, inv_x, am_x = quant_ops(f"X_{name}", x, M, L.K, E4M3, keep_xt[name], qt_later=True)
+            wq, wqt, inv_w, _ = quant_ops(f"W_{name}", w, L.N, L.K, E4M3, not mn, qt_later=True)
         y = bf(M, L.N)
         gemm_fwd_op(name, xq, wq, inv_x, inv_w, y, L, am_h if (name == "gate_up" and fused_absmax_h) else None)
         fwd[name] = {"x": x, "am_x": am_x, "xq": xq, "wq": wq, "xqt": xqt, "wqt": wqt, "inv_x": inv_x,
@@ -315,7 +324,7 @@ def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, 
     if group_weights:
         wq, wqt, inv_w, _ = qd["W_down"]
     else:
-        wq, wqt, inv_w, _ = quant_ops("W_down", ws["down"], L.N, L.K, E4M3, not mn)
+        wq, wqt, inv_w, _ = quant_ops("W_down", ws["down"], L.N, L.K, E4M3, not mn, qt_later=True)
     y = bf(M, L.N)
     gemm_fwd_op("down", hq, wq, inv_h, inv_w, y, L)
     fwd["down"] = {"xq": hq, "wq": wq, "xqt": hqt, "wqt": wqt, "inv_x": inv_h, "inv_w": inv_w, "y": y}

@@ -31,7 +31,7 @@ _SIGS = {
     "fp8_absmax_accumulate": (_i32, [_vp, _i64, _vp, _vp]),
     "fp8_absmax_accumulate_many": (_i32, [ctypes.c_int, _vp, _vp, _vp, _vp]),
     "fp8_quantize": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "fp8_quantize_many": (_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "fp8_quantize_many": (_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp8_swiglu_requant": (_i32, [_vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp]),
     "fp8_swiglu_backward": (_i32, [_vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp8_gemm_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
@@ -176,22 +176,25 @@ def quantize(x: torch.Tensor, fmt: int, amax: torch.Tensor, want_q: bool = True,
     return q, qt, scale, inv_scale
 
 
-def quantize_many(xs, fmts, amaxs, want_q=True, want_qt=False, qs=None, qts=None, scales=None, inv_scales=None):
+def quantize_many(xs, fmts, amaxs, want_q=True, want_qt=False, qs=None, qts=None, scales=None, inv_scales=None,
+                  qt_later=False):
     """Quantise up to 8 2-D bf16 tensors in one launch, each exactly as ``quantize``.
 
-    ``fmts``, ``amaxs``, ``want_q``, ``want_qt`` and the optional output lists
-    are per tensor (a single bool applies to all).  Returns lists
+    ``fmts``, ``amaxs``, ``want_q``, ``want_qt``, ``qt_later`` and the optional
+    output lists are per tensor (a single value applies to all).  ``qt_later``:
+    the transposed copy is read later (the backward pass), not by the next
+    call, and is stored non-temporally (same bytes).  Returns lists
     (qs, qts, scales, inv_scales), None where an output was not asked for.
     """
     k = len(xs)
     if not 1 <= k <= 8:
         raise ValueError("1 to 8 tensors")
     per = lambda v: list(v) if isinstance(v, (list, tuple)) else [v] * k
-    fmts, amaxs, want_q, want_qt = per(fmts), per(amaxs), per(want_q), per(want_qt)
+    fmts, amaxs, want_q, want_qt, qt_later = per(fmts), per(amaxs), per(want_q), per(want_qt), per(qt_later)
     qs, qts = per(qs) if qs is not None else [None] * k, per(qts) if qts is not None else [None] * k
     scales = per(scales) if scales is not None else [None] * k
     inv_scales = per(inv_scales) if inv_scales is not None else [None] * k
-    if any(len(v) != k for v in (fmts, amaxs, want_q, want_qt, qs, qts, scales, inv_scales)):
+    if any(len(v) != k for v in (fmts, amaxs, want_q, want_qt, qt_later, qs, qts, scales, inv_scales)):
         raise ValueError("one entry per tensor")
     rows, cols = [], []
     for i, x in enumerate(xs):
@@ -217,11 +220,12 @@ def quantize_many(xs, fmts, amaxs, want_q=True, want_qt=False, qs=None, qts=None
     xa, aa, qa, qta, sa, ia = arr(xs), arr(amaxs), arr(qs), arr(qts), arr(scales), arr(inv_scales)
     ra, ca = (ctypes.c_int64 * k)(*rows), (ctypes.c_int64 * k)(*cols)
     fa = (ctypes.c_int * k)(*[int(f) for f in fmts])
+    la = (ctypes.c_int * k)(*[1 if v else 0 for v in qt_later])
     _run("fp8_quantize_many", _lib.fp8_quantize_many,
          list(xs) + list(amaxs) + qs + qts + scales + inv_scales,
          k, ctypes.cast(xa, _vp), ctypes.cast(ra, _vp), ctypes.cast(ca, _vp), ctypes.cast(fa, _vp),
          ctypes.cast(aa, _vp), ctypes.cast(qa, _vp), ctypes.cast(qta, _vp), ctypes.cast(sa, _vp),
-         ctypes.cast(ia, _vp))
+         ctypes.cast(ia, _vp), ctypes.cast(la, _vp))
     return qs, qts, scales, inv_scales
 
 

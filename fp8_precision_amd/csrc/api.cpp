@@ -179,7 +179,7 @@ fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt, 
 
 fp8_status fp8_quantize_many(int count, const void* const* x, const int64_t* rows, const int64_t* cols,
                              const fp8_fmt* fmt, const float* const* absmax, uint8_t* const* q, uint8_t* const* qt,
-                             float* const* scale, float* const* inv_scale, hipStream_t stream)
+                             float* const* scale, float* const* inv_scale, const int* qt_later, hipStream_t stream)
 {
     t_last_error.clear();
     const std::string f("fp8_quantize_many");
@@ -218,7 +218,8 @@ fp8_status fp8_quantize_many(int count, const void* const* x, const int64_t* row
         for (const Range& r : in)
             if (overlap(out[a].p, out[a].n, r.p, r.n)) return fail(FP8_ERR_INVALID, f + ": an output overlaps an input");
     }
-    hipError_t e = fp8k::launch_quantize_many(count, x, rows, cols, fm, absmax, q, qt, scale, inv_scale, stream);
+    hipError_t e = fp8k::launch_quantize_many(count, x, rows, cols, fm, absmax, q, qt, scale, inv_scale, qt_later,
+                                              stream);
     if (e != hipSuccess) return fail_hip("fp8_quantize_many", e);
     return FP8_OK;
 }

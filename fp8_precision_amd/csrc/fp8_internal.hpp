@@ -51,10 +51,13 @@ hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, c
 
 // Quantisation of up to kMaxQuantTensors tensors in one launch (the tile form,
 // q and / or qt per tensor); the arrays are host arrays of count entries.
+// qt_later (may be null): per tensor, nonzero when its qt is read later rather
+// than by the next call, so it is stored non-temporally.
 constexpr int kMaxQuantTensors = 8;
 hipError_t launch_quantize_many(int count, const void* const* x, const int64_t* rows, const int64_t* cols,
                                 const int* fmt, const float* const* absmax, uint8_t* const* q, uint8_t* const* qt,
-                                float* const* scale, float* const* inv_scale, hipStream_t stream);
+                                float* const* scale, float* const* inv_scale, const int* qt_later,
+                                hipStream_t stream);
 
 hipError_t launch_swiglu_requant(const void* gu, int64_t M, int64_t F, float* absmax_h,
                                  int compute_absmax, uint8_t* hq, uint8_t* hqt,

@@ -237,8 +237,10 @@ constexpr int kQtEdge = 128;
 
 // The 128 x 128 tile with origin (tr, tc) of one tensor: q (if given) and qt
 // (if given; with qt == nullptr the LDS tile and its barrier are skipped, a
-// uniform choice per tensor).
-template <int FMT, bool NT>
+// uniform choice per tensor).  NT: non-temporal loads of x.  NTQ: qt written
+// with non-temporal stores (a copy that is read later -- by the backward pass --
+// and not by the next call; a compile-time choice, so the hint cannot be lost).
+template <int FMT, bool NT, bool NTQ = false>
 __device__ __forceinline__ void quantize_tile(const uint8_t* __restrict__ x, int64_t rows, int64_t cols, float s,
                                               uint8_t* __restrict__ q, uint8_t* __restrict__ qt, int64_t tr,
                                               int64_t tc, uint8_t* tile)
@@ -295,8 +297,12 @@ __device__ __forceinline__ void quantize_tile(const uint8_t* __restrict__ x, int
         const int64_t qrow = tc + col, qcol = tr + p * 16;
         if (qrow < cols && qcol < rows) {
             const int phys = p ^ ((col >> 3) & 7);
-            *reinterpret_cast<uint4*>(qt + qrow * rows + qcol) =
-                *reinterpret_cast<const uint4*>(tile + col * kQtEdge + phys * 16);
+            const u32x4 piece16 = *reinterpret_cast<const u32x4*>(tile + col * kQtEdge + phys * 16);
+            u32x4* dst = reinterpret_cast<u32x4*>(qt + qrow * rows + qcol);
+            if (NTQ)
+                __builtin_nontemporal_store(piece16, dst);
+            else
+                *dst = piece16;
         }
     }
 }
@@ -340,7 +346,7 @@ struct QuantGroup {
     int count;
 };
 
-template <int FMT>
+template <int FMT, bool NTQ>
 __device__ __forceinline__ void quantize_group_tile(const QuantGroup& g, int i, int64_t tr, int64_t tc, uint8_t* tile)
 {
     float s, inv;
@@ -350,11 +356,14 @@ __device__ __forceinline__ void quantize_group_tile(const QuantGroup& g, int i, 
         if (g.inv[i]) *g.inv[i] = inv;
     }
     if (g.nt[i])
-        quantize_tile<FMT, true>(g.x[i], g.rows[i], g.cols[i], s, g.q[i], g.qt[i], tr, tc, tile);
+        quantize_tile<FMT, true, NTQ>(g.x[i], g.rows[i], g.cols[i], s, g.q[i], g.qt[i], tr, tc, tile);
     else
-        quantize_tile<FMT, false>(g.x[i], g.rows[i], g.cols[i], s, g.q[i], g.qt[i], tr, tc, tile);
+        quantize_tile<FMT, false, NTQ>(g.x[i], g.rows[i], g.cols[i], s, g.q[i], g.qt[i], tr, tc, tile);
 }
 
+// NTQ: every qt of the launch is read later (non-temporal stores); a launch
+// quantises tensors of one kind only, so the hint is fixed at compile time.
+template <bool NTQ>
 __global__ void __launch_bounds__(256) quantize_many_kernel(const QuantGroup g)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[kQtEdge * kQtEdge];    // 16 KB
@@ -363,35 +372,60 @@ __global__ void __launch_bounds__(256) quantize_many_kernel(const QuantGroup g)
     const int t = blockIdx.x - g.first[i];
     const int64_t tr = (int64_t)(t / g.tiles_c[i]) * kQtEdge, tc = (int64_t)(t % g.tiles_c[i]) * kQtEdge;
     if (g.fmt[i] == 0)
-        quantize_group_tile<0>(g, i, tr, tc, tile);
+        quantize_group_tile<0, NTQ>(g, i, tr, tc, tile);
     else
-        quantize_group_tile<1>(g, i, tr, tc, tile);
+        quantize_group_tile<1, NTQ>(g, i, tr, tc, tile);
 }
 
-hipError_t launch_quantize_many(int count, const void* const* x, const int64_t* rows, const int64_t* cols,
-                                const int* fmt, const float* const* absmax, uint8_t* const* q, uint8_t* const* qt,
-                                float* const* scale, float* const* inv_scale, hipStream_t stream)
+static hipError_t launch_quantize_group(int count, const int* idx, const void* const* x, const int64_t* rows,
+                                        const int64_t* cols, const int* fmt, const float* const* absmax,
+                                        uint8_t* const* q, uint8_t* const* qt, float* const* scale,
+                                        float* const* inv_scale, bool ntq, hipStream_t stream)
 {
     QuantGroup g;
     g.count = count;
     g.first[0] = 0;
-    for (int i = 0; i < count; ++i) {
-        g.x[i] = reinterpret_cast<const uint8_t*>(x[i]);
-        g.absmax[i] = absmax[i];
-        g.q[i] = q[i];
-        g.qt[i] = qt[i];
-        g.scale[i] = scale[i];
-        g.inv[i] = inv_scale[i];
-        g.rows[i] = rows[i];
-        g.cols[i] = cols[i];
-        g.fmt[i] = fmt[i];
+    for (int k = 0; k < count; ++k) {
+        const int i = idx[k];
+        g.x[k] = reinterpret_cast<const uint8_t*>(x[i]);
+        g.absmax[k] = absmax[i];
+        g.q[k] = q[i];
+        g.qt[k] = qt[i];
+        g.scale[k] = scale[i];
+        g.inv[k] = inv_scale[i];
+        g.rows[k] = rows[i];
+        g.cols[k] = cols[i];
+        g.fmt[k] = fmt[i];
         // as the single-tensor launch: inputs of 64 MiB or more are read non-temporally
-        g.nt[i] = 2 * rows[i] * cols[i] >= kAbsStreamBytes;
-        g.tiles_c[i] = (int)((cols[i] + kQtEdge - 1) / kQtEdge);
-        const int64_t tiles = (int64_t)g.tiles_c[i] * ((rows[i] + kQtEdge - 1) / kQtEdge);
-        g.first[i + 1] = g.first[i] + (int)tiles;
+        g.nt[k] = 2 * rows[i] * cols[i] >= kAbsStreamBytes;
+        g.tiles_c[k] = (int)((cols[i] + kQtEdge - 1) / kQtEdge);
+        const int64_t tiles = (int64_t)g.tiles_c[k] * ((rows[i] + kQtEdge - 1) / kQtEdge);
+        g.first[k + 1] = g.first[k] + (int)tiles;
     }
-    return launch(quantize_many_kernel, dim3((unsigned)g.first[count]), dim3(256), stream, g);
+    if (ntq) return launch(quantize_many_kernel<true>, dim3((unsigned)g.first[count]), dim3(256), stream, g);
+    return launch(quantize_many_kernel<false>, dim3((unsigned)g.first[count]), dim3(256), stream, g);
+}
+
+// Tensors whose qt is read later and those whose qt (or none) is read next go to
+// separate launches (one launch when all are of one kind).
+hipError_t launch_quantize_many(int count, const void* const* x, const int64_t* rows, const int64_t* cols,
+                                const int* fmt, const float* const* absmax, uint8_t* const* q, uint8_t* const* qt,
+                                float* const* scale, float* const* inv_scale, const int* qt_later,
+                                hipStream_t stream)
+{
+    int later[kMaxQuantTensors], next[kMaxQuantTensors], nl = 0, nn = 0;
+    for (int i = 0; i < count; ++i) {
+        if (qt_later && qt_later[i] && qt[i])
+            later[nl++] = i;
+        else
+            next[nn++] = i;
+    }
+    if (nl > 0) {
+        const hipError_t e = launch_quantize_group(nl, later, x, rows, cols, fmt, absmax, q, qt, scale, inv_scale,
+                                                   true, stream);
+        if (e != hipSuccess || nn == 0) return e;
+    }
+    return launch_quantize_group(nn, next, x, rows, cols, fmt, absmax, q, qt, scale, inv_scale, false, stream);
 }
 
 // Plain quantisation only: the flat kernel above; with qt: the tile kernel.

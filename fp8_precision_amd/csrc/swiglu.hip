@@ -356,7 +356,11 @@ __global__ void __launch_bounds__(256) swiglu_quant_kernel(const uint16_t* __res
 // registers, 64 bytes per row and instruction, ran at 3.1-3.5 TB/s with a cold
 // cache.)  M and F are multiples of 16, so a lane's block is whole.
 constexpr int kSqEdge = 128;
+typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
 
+// NTQ: hqt written with non-temporal stores (the forward form: hqt is read by the
+// backward pass, not by the next call; a compile-time choice, so the hint stays).
+template <bool NTQ>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 swiglu_quant_t_kernel(const uint16_t* __restrict__ gu, int64_t M, int64_t F, const float* __restrict__ absmax_h,
                       uint8_t* __restrict__ hq, uint8_t* __restrict__ hqt, float* __restrict__ inv_out)
@@ -421,8 +425,12 @@ swiglu_quant_t_kernel(const uint16_t* __restrict__ gu, int64_t M, int64_t F, con
             const int64_t qrow = tc + col, qcol = tr + p * 16;
             if (qrow < F && qcol < M) {
                 const int phys = p ^ ((col >> 3) & 7);
-                *reinterpret_cast<uint4*>(hqt + qrow * M + qcol) =
-                    *reinterpret_cast<const uint4*>(tile + col * kSqEdge + phys * 16);
+                const u32x4s piece16 = *reinterpret_cast<const u32x4s*>(tile + col * kSqEdge + phys * 16);
+                u32x4s* dst = reinterpret_cast<u32x4s*>(hqt + qrow * M + qcol);
+                if (NTQ)
+                    __builtin_nontemporal_store(piece16, dst);
+                else
+                    *dst = piece16;
             }
         }
         __syncthreads();                                  // the tile is read back before it is reused
@@ -457,12 +465,17 @@ hipError_t launch_swiglu_requant(const void* gu, int64_t M, int64_t F, float* ab
         if (e != hipSuccess) return e;
     }
     if (hqt) {
-        // three resident blocks per CU (50 KB of LDS each), persistent over the tiles
+        // three resident blocks per CU (50 KB of LDS each), persistent over the tiles;
+        // the forward form (the statistic computed here) writes hqt for the backward
+        // pass, the recomputation form for the backward product that follows it
         const int64_t tiles = ((F + kSqEdge - 1) / kSqEdge) * ((M + kSqEdge - 1) / kSqEdge);
         int64_t tblocks = tiles;
         if (tblocks > 3 * (int64_t)device_cu_count()) tblocks = 3 * (int64_t)device_cu_count();
-        return launch(swiglu_quant_t_kernel, dim3((unsigned)tblocks), dim3(256), stream, g, M, F, absmax_h, hq, hqt,
-                      inv_scale_h);
+        if (compute_absmax)
+            return launch(swiglu_quant_t_kernel<true>, dim3((unsigned)tblocks), dim3(256), stream, g, M, F, absmax_h,
+                          hq, hqt, inv_scale_h);
+        return launch(swiglu_quant_t_kernel<false>, dim3((unsigned)tblocks), dim3(256), stream, g, M, F, absmax_h, hq,
+                      hqt, inv_scale_h);
     }
     return launch(swiglu_quant_kernel, dim3((unsigned)blocks), dim3(256), stream, g, M, F, absmax_h, hq,
                   inv_scale_h);

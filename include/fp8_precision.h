@@ -153,6 +153,13 @@ fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt,
  *                      device pointers and sizes of each tensor, as for
  *                      fp8_quantize (q[i] or qt[i] may be NULL, not both;
  *                      scale[i] and inv_scale[i] may be NULL)
+ *   qt_later           host array of count entries, or NULL (all 0): nonzero
+ *                      when tensor i's qt is read later -- in the forward pass,
+ *                      the copies the backward products use -- rather than by
+ *                      the next call; such a qt is written with non-temporal
+ *                      stores, leaving the Infinity Cache to q, which the next
+ *                      GEMM reads (the bytes are the same either way; tensors
+ *                      of the two kinds go to separate launches)
  * Constraints: every rows[i] and cols[i] a multiple of 16.  Inputs (x, absmax)
  * may be shared between entries; no output may overlap an input or another
  * output.
@@ -160,7 +167,7 @@ fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt,
 fp8_status fp8_quantize_many(int count, const void* const* x, const int64_t* rows, const int64_t* cols,
                              const fp8_fmt* fmt, const float* const* absmax, uint8_t* const* q,
                              uint8_t* const* qt, float* const* scale, float* const* inv_scale,
-                             hipStream_t stream);
+                             const int* qt_later, hipStream_t stream);
 
 /*
  * SwiGLU fused with its E4M3 requantisation.  gu = [gate | up] is the bf16
@@ -185,6 +192,11 @@ fp8_status fp8_quantize_many(int count, const void* const* x, const int64_t* row
  *   hqt          u8 [F, M] (transpose of hq) or NULL (at least one of hq, hqt)
  *   inv_scale_h  fp32 scalar out (RN32(1 / s_h)) or NULL
  * Constraints: F % 16 == 0; if hqt is given, M % 16 == 0.
+ * Cache policy (same bytes either way): in the forward forms (compute_absmax
+ * 1 or 2) hqt is written with non-temporal stores -- the backward pass reads
+ * it, not the down projection's forward GEMM that reads hq next; in the
+ * recomputation form (0) the backward product that follows reads hqt, and it
+ * is written with ordinary stores.
  */
 fp8_status fp8_swiglu_requant(const void* gu, int64_t M, int64_t F, float* absmax_h,
                               int compute_absmax, uint8_t* hq, uint8_t* hqt,

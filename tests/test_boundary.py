@@ -309,11 +309,11 @@ def test_quantize_many_validation(lib):
         I = lambda v: ctypes.cast((ctypes.c_int64 * k)(*v), vp)
         F = lambda v: ctypes.cast((ctypes.c_int * k)(*v), vp)
         return f(k if count is None else count, P(xs), I(rows), I(cols), F(fmts), P(ams), P(qs), P(qts),
-                 P([None] * k), P([None] * k), None)
+                 P([None] * k), P([None] * k), F([1] * k), None)
 
     ok = dict(xs=[A16, B16], rows=[16, 16], cols=[16, 32], fmts=[0, 1], ams=[C16, C16 + 4], qs=[D16, D16 + 256],
               qts=[E16, None])
-    assert f(1, None, None, None, None, None, None, None, None, None, None) == INVALID
+    assert f(1, None, None, None, None, None, None, None, None, None, None, None) == INVALID
     assert call(**ok, count=0) == INVALID
     assert call(**ok, count=9) == INVALID
     assert call(**{**ok, "xs": [A16, None]}) == INVALID

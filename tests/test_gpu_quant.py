@@ -142,7 +142,8 @@ def test_quantize_many(fp8, orc):
     """Up to 8 tensors in one launch, each bit-identical to its own fp8_quantize
     call and to the oracle: mixed formats, q only / qt only / both, ragged
     multiples of 16 spanning several 128 x 128 tiles, one input of 64 MiB
-    (read non-temporally) next to small ones, a retained (stale) statistic."""
+    (read non-temporally) next to small ones, a retained (stale) statistic;
+    and the same bytes with the transposed copies marked as read later."""
     shapes = [(144, 272), (4096, 8192), (16, 16), (400, 1040), (272, 144), (1024, 2048), (128, 128), (48, 4112)]
     fmts = [E4M3, E5M2, E4M3, E5M2, E4M3, E4M3, E5M2, E4M3]
     want_q = [True, True, False, True, True, False, True, True]
@@ -174,6 +175,18 @@ def test_quantize_many(fp8, orc):
             assert torch.equal(q1, qs[k]), what + " vs fp8_quantize"
         if want_qt[k]:
             assert torch.equal(qt1, qts[k]), what + " vs fp8_quantize (qt)"
+    # the transposed copies marked as read later (non-temporal stores): every other
+    # tensor (two launches, one per kind), then all of them (one launch) -- same bytes
+    for later in ([k % 2 == 0 for k in range(len(shapes))], True):
+        qs2, qts2, scs2, invs2 = fp8.quantize_many(xs, fmts, amaxs, want_q=want_q, want_qt=want_qt, qt_later=later)
+        torch.cuda.synchronize()
+        for k in range(len(shapes)):
+            what = f"tensor {k} qt_later {later}"
+            if want_q[k]:
+                assert torch.equal(qs2[k], qs[k]), what + " q"
+            if want_qt[k]:
+                assert torch.equal(qts2[k], qts[k]), what + " qt"
+            assert torch.equal(scs2[k], scs[k]) and torch.equal(invs2[k], invs[k]), what + " scales"
     with pytest.raises(fp8.Fp8Error):     # rows % 16 != 0 in one entry: refused before any launch
         fp8.quantize_many([xs[0], torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda")], E4M3, amaxs[0])
 
