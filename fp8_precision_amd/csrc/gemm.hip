@@ -78,6 +78,9 @@ constexpr int kLds = 2 * kStage;              // 128 KB
 constexpr int kEpiRows = 32;                  // epilogue chunk: 32 rows x 128 columns of bf16 per wave
 constexpr int kEpiWave = kEpiRows * 256;      // 8 KB per wave, 32 KB per workgroup (LDS total 160 KB)
 constexpr int kGroupM = 8;                    // tile rows per raster group (the default)
+constexpr int kBlockM = 8;                    // tile rows of a raster block (8 x 4 tiles: one XCD's round)
+constexpr int kGroupMBigB = 24;               // tile rows per group when B exceeds the Infinity Cache
+constexpr int64_t kInfinityCache = (int64_t)256 << 20;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
 // vmcnt[5:4] at [15:14]); expcnt and lgkmcnt are left at their maxima.
@@ -472,8 +475,13 @@ struct Work {
 };
 
 // Output tile of a virtual tile id: the problem it falls in, then a grouped
-// raster order within it (group_m tile rows per group, column-major within a
-// group), so consecutive ids share A and B panels.
+// raster order within it: groups of group_m tile rows, top to bottom; within a
+// group, blocks of (up to) kBlockM rows x 4 columns, column blocks left to right
+// and the blocks of a column block top to bottom; within a block, column-major.
+// So the 32 consecutive ids an XCD takes in a round are one 8 x 4 block (12
+// panels through its L2), and a group taller than a block spreads a round over
+// several block rows (more rows, fewer columns: fewer passes over B).  For
+// group_m <= kBlockM this is plain column-major order within the group.
 template <bool EDGE, bool HALF, bool GU>
 __device__ __forceinline__ Work work_of(const GemmGroup& g, int u)
 {
@@ -501,8 +509,15 @@ __device__ __forceinline__ Work work_of(const GemmGroup& g, int u)
     const int first_m = group * pr.group_m;
     const int gm = min(pr.tiles_m - first_m, pr.group_m);
     const int in_group = lv - group * group_size;
-    w.ms = (first_m + in_group % gm) * kBM;
-    w.ns = (in_group / gm) * (GU ? kBN / 2 : kBN);   // gate/up: 128 gate columns per tile
+    const int cb = in_group / (4 * gm);                   // column block
+    const int r1 = in_group - cb * 4 * gm;
+    const int wcb = min(4, pr.tiles_n - 4 * cb);           // its width (the last may be narrower)
+    const int bh = min(kBlockM, gm);
+    const int rb = r1 / (bh * wcb);                        // block within the column block
+    const int r2 = r1 - rb * bh * wcb;
+    const int hrb = min(bh, gm - rb * bh);                 // its height
+    w.ms = (first_m + rb * bh + r2 % hrb) * kBM;
+    w.ns = (4 * cb + r2 / hrb) * (GU ? kBN / 2 : kBN);   // gate/up: 128 gate columns per tile
     if (HALF) w.ms += hh * (kBM / 2);
     // A last partial tile is shifted back to end at the matrix edge (P, Q >= 256),
     // recomputing rows / columns of its neighbour that it then does not store
@@ -852,7 +867,12 @@ static GemmProblem make_problem(const uint8_t* A, int la, const uint8_t* B, int 
     p.lb = lb;
     p.tiles_m = (int)((P + kBM - 1) / kBM);
     p.tiles_n = (int)((Q + kBN - 1) / kBN);
-    p.group_m = kGroupM;
+    // A B operand larger than the Infinity Cache is re-read from HBM by every
+    // group: taller groups read it fewer times.  Measured on MI355X, the 32B-class
+    // gate/up forward (16384 x 55296 x 5120, B 283 MB) took 3582 / 3493 / 3385 /
+    // 3334 / 3432 us with groups of 8 / 16 / 20 / 24 / 32 tile rows; no other
+    // product of the 7B-, 14B- and 32B-class layers has such a B.
+    p.group_m = Q * R > kInfinityCache ? kGroupMBigB : kGroupM;
     p.first_tile = 0;
     return p;
 }
@@ -968,7 +988,7 @@ hipError_t launch_gemm_tn_pair(const uint8_t* A0, int la0, const uint8_t* B0, in
     // other pair of those layers (16-28 column tiles) changed; forward launches
     // keep 8 (the 86-column gate/up forward ran 3% slower with 4)
     for (int i = 0; i < 2; ++i)
-        if (g.p[i].tiles_n > 32) g.p[i].group_m = 4;
+        if (g.p[i].group_m == kGroupM && g.p[i].tiles_n > 32) g.p[i].group_m = 4;
     g.count = 2;
     return dispatch(fmt_a, fmt_b, g, true, stream);      // dX and dW: stored non-temporally
 }

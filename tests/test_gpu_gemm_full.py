@@ -11,6 +11,10 @@ summation bound), for each compiled form:
 * forward (e4m3 x e4m3, K-major), three full rounds (the 7B qkv shape) and a
   launch with a balanced half-tile round, and the edge form (a matrix with
   fewer than 256 rows) over two rounds;
+* a forward whose B operand is larger than the Infinity Cache (groups of 24
+  tile rows instead of 8): every output bit for bit against the same product
+  in column slices (each with the default groups), sampled rows against the
+  oracle;
 * the backward pair (e5m2 x e4m3, one launch for dgrad and wgrad): the 7B qkv
   pair (four rounds, long dgrad tiles first), and a pair whose tiles end in a
   balanced half-tile round;
@@ -25,7 +29,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import E4M3, E5M2, assert_f32_equal, assert_within_sum_bound, bf16_to_f64, dev, gemm_compare, say, u16
+from gpu_util import (E4M3, E5M2, assert_f32_equal, assert_within_sum_bound, bf16_to_f64, dev, gemm_compare, say, u16,
+                      u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,6 +86,35 @@ def test_forward_every_output(fp8, orc, name, P, Q, R):
     a, b = rand_codes(g, (P, R), E4M3), rand_codes(g, (Q, R), E4M3)
     y = fp8.gemm_fwd(dev(torch.from_numpy(a)), dev(torch.from_numpy(b)), scal(INV_A[E4M3]), scal(INV_B))
     check_full(orc, y, a, E4M3, b, INV_A[E4M3], INV_B, name)
+
+
+def test_forward_large_b_groups(fp8, orc):
+    """6800 x 16592 x 16384: B is 272 MB, so the launch walks groups of 24 tile
+    rows (27 row tiles: a full group and a group of 3; the last row and column
+    tiles ragged).  Each output is reduced in the same order whatever tile or
+    raster position computes it, so the launch must equal, bit for bit, the
+    same product computed in column slices of 4096 (64 MiB of B each: the
+    default groups of 8; the 208-column remainder in the edge form)."""
+    P, Q, R = 6800, 16592, 16384
+    say("gemm full output, large B", P, Q, R)
+    g = torch.Generator(device="cuda").manual_seed(24)
+    a = torch.randn((P, R), generator=g, device="cuda").mul_(SIGMA[E4M3]).to(TDT[E4M3]).view(torch.uint8)
+    b = torch.randn((Q, R), generator=g, device="cuda").mul_(SIGMA[E4M3]).to(TDT[E4M3]).view(torch.uint8)
+    ia, ib = scal(INV_A[E4M3]), scal(INV_B)
+    y = torch.full((P, Q), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)   # 0xFFFF: NaN
+    fp8.gemm_fwd(a, b, ia, ib, out=y)
+    yh = u16(y)
+    for c0 in range(0, Q, 4096):
+        c1 = min(c0 + 4096, Q)
+        ys = u16(fp8.gemm_fwd(a, b[c0:c1], ia, ib))
+        bad = np.argwhere(ys != yh[:, c0:c1])
+        assert bad.size == 0, ("large-B launch differs from its column slice", c0, c1, bad[:4].tolist())
+    rows = np.unique(np.concatenate([[0, 255, 256, 6143, 6144, P - 1],
+                                     np.random.default_rng(24).integers(0, P, 26)])).astype(np.int64)
+    a_h, b_h = u8(a), u8(b)
+    ref = orc.gemm(a_h, E4M3, b_h, E4M3, INV_A[E4M3], INV_B, rows=rows)
+    gemm_compare(yh[rows], ref, "large-B forward, sampled rows")
+    assert_within_sum_bound(yh[rows], ref, a_h, E4M3, b_h, E4M3, INV_A[E4M3], INV_B, rows, "large-B forward")
 
 
 # (name, M, N, K): the qkv pair has 256 dgrad tiles (reduction 12288) and 768
