@@ -44,6 +44,20 @@
  *     - GEMM: fp32 sum over ascending k of the decoded products (every
  *       FP8 x FP8 product is exact in fp32), then one multiply by
  *       RN32(da * db), then round-to-nearest-even to bf16.
+ *     - Block (MX) scaling, the alternative to per-tensor scaling that the
+ *       LLMQ summary (section 2) says needs native hardware support: the pages
+ *       define no format, so this file follows the OCP Microscaling (MX)
+ *       formats specification v1.0 (section 6.3, the scale and conversion of a
+ *       block): blocks of 32 consecutive elements of a row; one shared scale
+ *       2^e per block stored as an E8M0 byte e + 127 (255 = NaN), with
+ *       e = floor(log2(max |x|)) - emax, emax = 8 for E4M3 and 15 for E5M2
+ *       (the exponent of the format's largest normal), clamped to
+ *       [-127, 127] (e = -127 for an all-zero block); the elements are
+ *       x / 2^e (exact) encoded like every other value (nearest-even,
+ *       saturating).  A block holding a NaN or an infinity gets the NaN
+ *       scale and the unscaled encodings.  The MX GEMM is the GEMM above with
+ *       each product dec(a) dec(b) multiplied by 2^(ea + eb) (its two blocks'
+ *       scales) before the fp32 sum, and no per-tensor factor.
  *
  * Built with gcc -O2 -ffp-contract=off (no fast-math), so every float
  * operation below is exactly one IEEE binary32 operation (x86-64 SSE).
@@ -343,6 +357,79 @@ void oracle_gemm(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
             float acc = 0.0f;
             for (int64_t k = 0; k < K; ++k) acc += a[k] * b[k];
             Y[r * N + n] = oracle_f32_to_bf16(acc * descale);
+        }
+    }
+}
+
+/* ---- block (MX) scaling: see the header for the reading of the OCP MX specification. */
+#define MX_BLOCK 32
+
+/*
+ * MX quantisation of a row-major bf16 [rows, cols] tensor (cols a multiple of
+ * 32): q[i, j] = encode(x[i, j] / 2^e), scales[i, j / 32] = e + 127 for the
+ * block's e (255 for a block with a NaN or an infinity, whose codes are the
+ * unscaled encodings).
+ */
+void oracle_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* q, uint8_t* scales)
+{
+    const int emax = fmt == FMT_E4M3 ? 8 : 15;
+    const int64_t nb = cols / MX_BLOCK;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t* xb = x + i * cols + b * MX_BLOCK;
+            uint8_t* qb = q + i * cols + b * MX_BLOCK;
+            float m = 0.0f;
+            int nonfinite = 0;
+            for (int k = 0; k < MX_BLOCK; ++k) {
+                float v = oracle_bf16_to_f32(xb[k]);
+                if (!isfinite(v)) nonfinite = 1;
+                else if (fabsf(v) > m) m = fabsf(v);
+            }
+            if (nonfinite) {
+                scales[i * nb + b] = 255;
+                for (int k = 0; k < MX_BLOCK; ++k) qb[k] = oracle_encode(oracle_bf16_to_f32(xb[k]), fmt);
+                continue;
+            }
+            int e = -127;
+            if (m > 0.0f) {
+                int k2;
+                frexpf(m, &k2);                     /* m = r * 2^k2, r in [0.5, 1): floor(log2 m) = k2 - 1 */
+                e = (k2 - 1) - emax;
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+            }
+            scales[i * nb + b] = (uint8_t)(e + 127);
+            for (int k = 0; k < MX_BLOCK; ++k)
+                qb[k] = oracle_encode(ldexpf(oracle_bf16_to_f32(xb[k]), -e), fmt);
+        }
+    }
+}
+
+/*
+ * MX GEMM: Y[m, n] = bf16(RN32(sum over ascending k of
+ * ldexp(dec(A[m, k]) dec(B[n, k]), ea + eb))) with ea, eb the scales of the
+ * blocks holding A[m, k] and B[n, k] (a NaN scale makes the product NaN).
+ * A [M, K], B [N, K], scales [M, K / 32] and [N, K / 32]; rows as in oracle_gemm.
+ */
+void oracle_mx_gemm(const uint8_t* A, const uint8_t* SA, int fmt_a, const uint8_t* B, const uint8_t* SB,
+                    int fmt_b, int64_t M, int64_t N, int64_t K, const int64_t* rows, int64_t nrows, uint16_t* Y)
+{
+    const int64_t nb = K / MX_BLOCK;
+    if (!rows) nrows = M;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t m = rows ? rows[r] : r;
+        for (int64_t n = 0; n < N; ++n) {
+            float acc = 0.0f;
+            for (int64_t k = 0; k < K; ++k) {
+                uint8_t sa = SA[m * nb + k / MX_BLOCK], sb = SB[n * nb + k / MX_BLOCK];
+                float p = oracle_decode(A[m * K + k], fmt_a) * oracle_decode(B[n * K + k], fmt_b);
+                if (sa == 255 || sb == 255) p = NAN;
+                else p = ldexpf(p, (int)sa + (int)sb - 254);
+                acc += p;
+            }
+            Y[r * N + n] = oracle_f32_to_bf16(acc);
         }
     }
 }

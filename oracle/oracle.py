@@ -66,6 +66,8 @@ def _load():
             "oracle_swiglu_grad_one": (None, [f32, f32, f32, vp, vp]),
             "oracle_swiglu_grad": (None, [vp, vp, i64, i64, vp]),
             "oracle_swiglu_backward": (None, [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, vp]),
+            "oracle_mx_quantize": (None, [vp, i64, i64, i32, vp, vp]),
+            "oracle_mx_gemm": (None, [vp, vp, i32, vp, vp, i32, i64, i64, i64, vp, i64, vp]),
             "oracle_encode_vec": (None, [vp, i64, i32, vp]),
             "oracle_decode_vec": (None, [vp, i64, i32, vp]),
             "oracle_exp_neg_vec": (None, [vp, i64, vp]),
@@ -274,4 +276,48 @@ def gemm(a: np.ndarray, fmt_a: int, b: np.ndarray, fmt_b: int, da, db, rows=None
     _load().oracle_gemm(_ptr(a), _fmt(fmt_a), _ptr(b), _fmt(fmt_b), M, N, K,
                         float(np.float32(da)), float(np.float32(db)), _ptr(r_arr), nrows,
                         _ptr(a_dec), _ptr(b_dec), _ptr(y))
+    return y
+
+
+MX_BLOCK = 32
+
+
+def mx_quantize(x: np.ndarray, fmt: int):
+    """Block (MX) quantisation of a bf16 [rows, cols] tensor (uint16 bits, cols a
+    multiple of 32): returns (codes uint8 [rows, cols], E8M0 scales uint8 [rows, cols / 32])."""
+    _need(x, np.uint16, "x")
+    if x.ndim != 2 or x.shape[1] % MX_BLOCK:
+        raise ValueError("x must be 2-D with a multiple of 32 columns")
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    sc = np.empty((rows, cols // MX_BLOCK), np.uint8)
+    _load().oracle_mx_quantize(_ptr(x), rows, cols, _fmt(fmt), _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def mx_gemm(a: np.ndarray, sa: np.ndarray, fmt_a: int, b: np.ndarray, sb: np.ndarray, fmt_b: int,
+            rows=None) -> np.ndarray:
+    """Y = bf16(RN32(sum_k ldexp(dec(A[m,k]) dec(B[n,k]), ea + eb))) with per-block scales, bf16 bits.
+
+    a: uint8 [M, K] and sa: uint8 [M, K / 32]; b: uint8 [N, K] and sb: uint8 [N, K / 32].
+    rows: optional int64 row indices, as in gemm().
+    """
+    for t, n in ((a, "a"), (sa, "sa"), (b, "b"), (sb, "sb")):
+        _need(t, np.uint8, n)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[1] or a.shape[1] % MX_BLOCK:
+        raise ValueError("a must be [M, K] and b [N, K], K a multiple of 32")
+    M, K = a.shape
+    N = b.shape[0]
+    if sa.shape != (M, K // MX_BLOCK) or sb.shape != (N, K // MX_BLOCK):
+        raise ValueError("scales must be [M, K / 32] and [N, K / 32]")
+    if rows is None:
+        r_arr, nrows = None, M
+    else:
+        r_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        if r_arr.ndim != 1 or (r_arr.size and (r_arr.min() < 0 or r_arr.max() >= M)):
+            raise ValueError("rows out of range")
+        nrows = r_arr.size
+    y = np.empty((nrows, N), np.uint16)
+    _load().oracle_mx_gemm(_ptr(a), _ptr(sa), _fmt(fmt_a), _ptr(b), _ptr(sb), _fmt(fmt_b), M, N, K,
+                           _ptr(r_arr), nrows, _ptr(y))
     return y
