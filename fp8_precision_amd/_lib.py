@@ -43,6 +43,8 @@ _SIGS = {
     "fp8_gemm_wgrad_mn": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_gemm_backward_mn": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_stream_copy": (_i32, [_vp, _vp, _i64, _vp]),
+    "fp8_mx_quantize": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "fp8_mx_gemm_fwd": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -439,6 +441,47 @@ def gemm_backward_mn(dyq, dy_fmt, wq, xq, inv_sdy, inv_sw, inv_sx, dx=None, dw=N
          _ptr(dyq), int(dy_fmt), _ptr(wq), _ptr(xq), _ptr(inv_sdy), _ptr(inv_sw), _ptr(inv_sx), _ptr(dx), _ptr(dw),
          M, N, K)
     return dx, dw
+
+
+def mx_quantize(x: torch.Tensor, fmt: int, q: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """Block (MX) quantisation of a 2-D bf16 tensor (cols a multiple of 32):
+    returns (q uint8 [rows, cols], scales uint8 [rows, cols / 32], E8M0)."""
+    _dev_tensor(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    for t, n, size in ((q, "q", rows * cols), (scales, "scales", rows * (cols // 32))):
+        _dev_tensor(t, n, torch.uint8)
+        if t.numel() != size:
+            raise ValueError(f"{n} has the wrong size")
+    _run("fp8_mx_quantize", _lib.fp8_mx_quantize, (x, q, scales), _ptr(x), rows, cols, int(fmt), _ptr(q), _ptr(scales))
+    return q, scales
+
+
+def mx_gemm_fwd(xq, sx, wq, sw, x_fmt: int = E4M3, out=None) -> torch.Tensor:
+    """Y[M, N] = bf16(sum_k dec(X) 2^ex dec(W) 2^ew) of block-scaled operands (from
+    mx_quantize): xq uint8 [M, K] with sx uint8 [M, K / 32], wq uint8 [N, K] (e4m3)
+    with sw uint8 [N, K / 32]."""
+    for t, n in ((xq, "xq"), (sx, "sx"), (wq, "wq"), (sw, "sw")):
+        _dev_tensor(t, n, torch.uint8)
+    if xq.dim() != 2 or wq.dim() != 2 or xq.shape[1] != wq.shape[1]:
+        raise ValueError("xq must be [M, K] and wq [N, K]")
+    M, K = xq.shape
+    N = wq.shape[0]
+    if sx.numel() != M * (K // 32) or sw.numel() != N * (K // 32):
+        raise ValueError("sx must be [M, K / 32] and sw [N, K / 32]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _dev_tensor(out, "out", torch.bfloat16)
+    if out.numel() != M * N:
+        raise ValueError("out must be [M, N]")
+    _run("fp8_mx_gemm_fwd", _lib.fp8_mx_gemm_fwd, (xq, sx, wq, sw, out), _ptr(xq), _ptr(sx), int(x_fmt), _ptr(wq),
+         _ptr(sw), _ptr(out), M, N, K)
+    return out
 
 
 def stream_copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:

@@ -276,11 +276,13 @@ fp8_status fp8_swiglu_backward(const void* gu, const void* dh, int64_t M, int64_
 }
 
 // Shared checks of the three GEMM calls, in the TN form out[P, Q] = A[P, R] . B[Q, R]^T.
+// The block-scaled call passes need_inv = false (it has no per-tensor factors).
 static fp8_status gemm_common(const char* name, const uint8_t* A, int fmt_a, const uint8_t* B, const float* inv_a,
-                              const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream)
+                              const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream,
+                              bool need_inv = true)
 {
     char msg[160];
-    if (!A || !B || !inv_a || !inv_b || !out) {
+    if (!A || !B || (need_inv && (!inv_a || !inv_b)) || !out) {
         std::snprintf(msg, sizeof(msg), "%s: null pointer", name);
         return fail(FP8_ERR_INVALID, msg);
     }
@@ -297,7 +299,8 @@ static fp8_status gemm_common(const char* name, const uint8_t* A, int fmt_a, con
         std::snprintf(msg, sizeof(msg), "%s: operand larger than 2 GiB", name);
         return fail(FP8_ERR_UNSUPPORTED, msg);
     }
-    const Range r[] = {{A, P * R}, {B, Q * R}, {inv_a, 4}, {inv_b, 4}, {out, 2 * P * Q}};
+    const Range r[] = {{A, P * R}, {B, Q * R}, {inv_a, need_inv ? 4 : 0}, {inv_b, need_inv ? 4 : 0},
+                       {out, 2 * P * Q}};
     // the two inputs may alias each other (e.g. A == B); the output may alias nothing
     for (int i = 0; i < 4; ++i)
         if (overlap(r[i].p, r[i].n, r[4].p, r[4].n)) {
@@ -314,7 +317,7 @@ static fp8_status gemm_common(const char* name, const uint8_t* A, int fmt_a, con
         std::snprintf(msg, sizeof(msg), "%s: operand larger than 2 GiB", name);
         return fail(FP8_ERR_UNSUPPORTED, msg);
     }
-    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(out, 16) || !aligned(inv_a, 4) || !aligned(inv_b, 4)) {
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(out, 16) || (need_inv && (!aligned(inv_a, 4) || !aligned(inv_b, 4)))) {
         std::snprintf(msg, sizeof(msg), "%s: misaligned pointer", name);
         return fail(FP8_ERR_UNSUPPORTED, msg);
     }
@@ -455,6 +458,40 @@ fp8_status fp8_gemm_backward_mn(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_
     hipError_t e = fp8k::launch_gemm_tn_pair(dyq, 0, wq, 1, inv_sdy, inv_sw, dx, M, K, N, dyq, 1, xq, 1, inv_sdy,
                                              inv_sx, dw, N, K, M, (int)dy_fmt, 0, stream);
     if (e != hipSuccess) return fail_hip("fp8_gemm_backward_mn", e);
+    return FP8_OK;
+}
+
+fp8_status fp8_mx_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt, uint8_t* q, uint8_t* scales,
+                           hipStream_t stream)
+{
+    t_last_error.clear();
+    if (!x || !q || !scales) return fail(FP8_ERR_INVALID, "fp8_mx_quantize: null pointer");
+    if (fmt != FP8_E4M3 && fmt != FP8_E5M2) return fail(FP8_ERR_INVALID, "fp8_mx_quantize: bad format");
+    if (!mul_ok(rows, cols, kMaxElems)) return fail(FP8_ERR_INVALID, "fp8_mx_quantize: bad shape");
+    const int64_t n = rows * cols;
+    const Range r[] = {{x, 2 * n}, {q, n}, {scales, n / 32}};
+    if (any_overlap(r)) return fail(FP8_ERR_INVALID, "fp8_mx_quantize: overlapping buffers");
+    if (cols % 32) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_quantize: cols must be a multiple of 32");
+    if (!aligned(x, 16) || !aligned(q, 16)) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_quantize: misaligned pointer");
+    hipError_t e = fp8k::launch_mx_quantize(x, n, (int)fmt, q, scales, stream);
+    if (e != hipSuccess) return fail_hip("fp8_mx_quantize", e);
+    return FP8_OK;
+}
+
+fp8_status fp8_mx_gemm_fwd(const uint8_t* xq, const uint8_t* sx, fp8_fmt x_fmt, const uint8_t* wq, const uint8_t* sw,
+                           void* y, int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    t_last_error.clear();
+    const char* name = "fp8_mx_gemm_fwd";
+    if (!sx || !sw) return fail(FP8_ERR_INVALID, "fp8_mx_gemm_fwd: null scales");
+    fp8_status st = gemm_common(name, xq, (int)x_fmt, wq, nullptr, nullptr, y, M, N, K, stream, false);
+    if (st != FP8_OK) return st;
+    if (overlap(sx, M * (K / 32), y, 2 * M * N) || overlap(sw, N * (K / 32), y, 2 * M * N))
+        return fail(FP8_ERR_INVALID, "fp8_mx_gemm_fwd: output overlaps the scales");
+    if (M < 256 || N < 256) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_gemm_fwd: M and N must be at least 256");
+    if (!aligned(sx, 4) || !aligned(sw, 4)) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_gemm_fwd: misaligned scales");
+    hipError_t e = fp8k::launch_gemm_mx(xq, sx, (int)x_fmt, wq, sw, 0, y, M, N, K, stream);
+    if (e != hipSuccess) return fail_hip(name, e);
     return FP8_OK;
 }
 

@@ -77,6 +77,12 @@ constexpr int kStage = kStageA + kStageB;     // 64 KB
 constexpr int kLds = 2 * kStage;              // 128 KB
 constexpr int kEpiRows = 32;                  // epilogue chunk: 32 rows x 128 columns of bf16 per wave
 constexpr int kEpiWave = kEpiRows * 256;      // 8 KB per wave, 32 KB per workgroup (LDS total 160 KB)
+// Block-scaled (MX) launches: per stage, the E8M0 scales of the step's four
+// 32-byte reduction blocks for the 256 A rows and the 256 B rows (4 bytes per
+// row, 2 KB); two stages take 4 KB, so the epilogue stages 16-row chunks
+// (16 KB) and the LDS total is 148 KB.
+constexpr int kScStage = 2 * 256 * 4;
+constexpr int kEpiRowsMx = 16;
 constexpr int kGroupM = 8;                    // tile rows per raster group (the default)
 constexpr int kBlockM = 8;                    // tile rows of a raster block (8 x 4 tiles: one XCD's round)
 constexpr int kGroupMBigB = 24;               // tile rows per group when B exceeds the Infinity Cache
@@ -86,6 +92,7 @@ constexpr int64_t kInfinityCache = (int64_t)256 << 20;
 // vmcnt[5:4] at [15:14]); expcnt and lgkmcnt are left at their maxima.
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitVm16 = 0x4F70;
+constexpr int kWaitVm18 = 0x4F72;
 constexpr int kWaitVm12 = 0x0F7C;
 
 // Operand layouts.
@@ -104,6 +111,16 @@ __device__ __forceinline__ int swz_mn(int r) { return (r & 7) | (((r >> 4) & 1) 
 __device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+
+// 4-byte direct-to-LDS load (lane L writes LDS bytes [lds + 4 L, lds + 4 L + 4)):
+// one row's four block scales of a reduction step.
+__device__ __forceinline__ void dma4(uint32_t voff, const uint8_t* sbase, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                  :
                  : "v"(voff), "s"(sbase), "s"(lds)
                  : "memory", "m0");
@@ -132,6 +149,11 @@ struct OpSrc {
 
 struct Sources {
     OpSrc a, b;
+    // block-scaled launches: scale tensors [rows][R / 32] and the lane's row offsets
+    // (wave w loads the scales of tile rows 64 w + lane of A and of B)
+    const uint8_t* sa;
+    const uint8_t* sb;
+    uint32_t sa_off, sb_off;
 };
 
 // K-major: a wave fills `wave_rows` consecutive rows of the stage (64 for the
@@ -206,6 +228,25 @@ __device__ __forceinline__ void issue_stage(const Sources& src, uint32_t stage, 
 {
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) issue_one<EDGE, LA, LB>(src, stage, kt, wave, idx);
+}
+
+// Block-scaled launches: the scale loads of a stage for one wave -- `which` 0: the
+// scales of A rows 64 w .. 64 w + 63, 1: those of B rows (LDS: A rows at 4 r,
+// B rows at 1024 + 4 r of the scale stage).
+__device__ __forceinline__ void issue_scale(const Sources& src, uint32_t sc_stage, int kt, int wave, int which)
+{
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(sc_stage + (uint32_t)(which * 1024 + wave * 256));
+    if (which == 0)
+        dma4(src.sa_off, src.sa + (size_t)kt * 4, lds);
+    else
+        dma4(src.sb_off, src.sb + (size_t)kt * 4, lds);
+}
+
+__device__ __forceinline__ void issue_stage_mx(const Sources& src, uint32_t stage, uint32_t sc_stage, int kt, int wave)
+{
+    issue_stage<false, kKMajor, kKMajor>(src, stage, kt, wave);
+    issue_scale(src, sc_stage, kt, wave, 0);
+    issue_scale(src, sc_stage, kt, wave, 1);
 }
 
 // Half tile (128 rows of A x 256 columns of B, K-major operands): a stage
@@ -365,6 +406,139 @@ __device__ __forceinline__ void tile_mainloop(v4f (&acc)[8][8], v8i (&bq)[8], v8
     __syncthreads();
 }
 
+// ---- block-scaled (MX) launches.  The matrix instruction takes, per lane, one
+// E8M0 scale of its operand row (lane % 16 of the block) and reduction block
+// (lane / 16: bytes 32 g .. 32 g + 31 of the step) for each operand, picked from
+// a 32-bit register by a byte selector (op_sel) that is part of the instruction.
+// A wave's scales of a step are packed four blocks per register: A blocks
+// 4 h .. 4 h + 3 in sa[h] (byte i % 4), B blocks 4 h .. in sb[h].  (Measured on
+// gfx950 with an in-bounds probe: byte 127 is 1.0, 255 gives NaN, and the scale
+// of lane group g applies to the step's bytes 32 g .. 32 g + 31, which the
+// fragment layout above -- chunks g and g + 4, i.e. bytes 16 g .. and
+// 64 + 16 g .. -- feeds to the instruction in its own order.)
+__device__ __forceinline__ uint32_t pack_scales(const uint8_t* rows16, int lane)
+{
+    // rows 16 i + lane % 16 (i = 0..3, 64 bytes apart), byte lane / 16 of each
+    const uint8_t* p = rows16 + (lane & 15) * 4 + (lane >> 4);
+    return (uint32_t)p[0] | ((uint32_t)p[64] << 8) | ((uint32_t)p[128] << 16) | ((uint32_t)p[192] << 24);
+}
+
+__device__ __forceinline__ void read_scales(const uint8_t* sc_stage, int wm, int wn, int lane, uint32_t (&sa)[2],
+                                            uint32_t (&sb)[2])
+{
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        sa[h] = pack_scales(sc_stage + wm * 512 + h * 256, lane);
+        sb[h] = pack_scales(sc_stage + 1024 + wn * 512 + h * 256, lane);
+    }
+}
+
+template <int FA, int FB, int OA, int OB>
+__device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, const v4f& c, uint32_t sa, uint32_t sb)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, FB, FA, OB, (int)sb, OA, (int)sa);
+}
+
+// acc[i][j] += A block i x B block j with their scales (i, j are constants once
+// the callers' loops are unrolled, so the switch folds to one instruction).
+template <int FA, int FB>
+__device__ __forceinline__ void mma16_mx(v4f (&acc)[8][8], const v8i& a, const v8i& b, int i, int j,
+                                         const uint32_t (&sa)[2], const uint32_t (&sb)[2])
+{
+    const uint32_t xa = sa[i >> 2], xb = sb[j >> 2];
+    v4f& c = acc[i][j];
+    switch ((i & 3) * 4 + (j & 3)) {
+#define FP8_MX_CASE(OA, OB) \
+    case OA * 4 + OB: c = mfma_mx<FA, FB, OA, OB>(a, b, c, xa, xb); break;
+        FP8_MX_CASE(0, 0) FP8_MX_CASE(0, 1) FP8_MX_CASE(0, 2) FP8_MX_CASE(0, 3)
+        FP8_MX_CASE(1, 0) FP8_MX_CASE(1, 1) FP8_MX_CASE(1, 2) FP8_MX_CASE(1, 3)
+        FP8_MX_CASE(2, 0) FP8_MX_CASE(2, 1) FP8_MX_CASE(2, 2) FP8_MX_CASE(2, 3)
+        FP8_MX_CASE(3, 0) FP8_MX_CASE(3, 1) FP8_MX_CASE(3, 2) FP8_MX_CASE(3, 3)
+#undef FP8_MX_CASE
+    }
+}
+
+// The two halves of a step as half0 / half1 above, with the scales: sc holds
+// the step's, and half1 also reads the next step's into sn (from the next
+// stage's scales, landed at the barrier before it) and issues the two scale
+// loads of tile k + 2 beside its 16 operand loads.
+template <int FA, int FB>
+__device__ __forceinline__ void half0_mx(v4f (&acc)[8][8], const v8i (&bq)[8], const v8i (&alo)[4], v8i (&ahi)[4],
+                                         const uint8_t* stage, int wm, int lane, const uint32_t (&sa)[2],
+                                         const uint32_t (&sb)[2])
+{
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+        const int j = t >> 2, i = t & 3;
+        mma16_mx<FA, FB>(acc, alo[i], bq[j], i, j, sa, sb);
+        if ((t & 7) == 1) ahi[t >> 3] = frag_k(stage, wm * 8 + 4 + (t >> 3), lane);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int FA, int FB, bool NEXT>
+__device__ __forceinline__ void half1_mx(v4f (&acc)[8][8], v8i (&bq)[8], v8i (&alo)[4], const v8i (&ahi)[4],
+                                         const Sources& src, uint32_t cur_addr, uint32_t cur_sc, const uint8_t* nxt,
+                                         const uint8_t* nxt_sc, int kt_issue, int wave, int wm, int wn, int lane,
+                                         const uint32_t (&sa)[2], const uint32_t (&sb)[2], uint32_t (&na)[2],
+                                         uint32_t (&nb)[2])
+{
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+        const int j = t >> 2, i = t & 3;
+        mma16_mx<FA, FB>(acc, ahi[i], bq[j], 4 + i, j, sa, sb);
+        if (NEXT) {
+            if (i == 3) bq[j] = frag_k(nxt + kStageA, wn * 8 + j, lane);
+            if ((t & 7) == 1) alo[t >> 3] = frag_k(nxt, wm * 8 + (t >> 3), lane);
+            if ((t & 1) == 0) issue_one<false, kKMajor, kKMajor>(src, cur_addr, kt_issue, wave, t >> 1);
+            if (t == 1 || t == 3) issue_scale(src, cur_sc, kt_issue, wave, t >> 1);
+            if (t == 5) read_scales(nxt_sc, wm, wn, lane, na, nb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The reduction of one block-scaled tile whose first two stages (operands and
+// scales) have been issued; as tile_mainloop, with 18 loads per stage.
+template <int FA, int FB>
+__device__ __forceinline__ void tile_mainloop_mx(v4f (&acc)[8][8], v8i (&bq)[8], v8i (&alo)[4], v8i (&ahi)[4],
+                                                 const Sources& src, uint8_t* lds, uint32_t lds_addr, uint8_t* sc,
+                                                 uint32_t sc_addr, int KT, int wave, int wm, int wn, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
+    __builtin_amdgcn_s_waitcnt(kWaitVm18);    // stage 0 landed; stage 1's 18 loads may be in flight
+    __syncthreads();
+    uint32_t sa[2], sb[2], na[2], nb[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bq[j] = frag_k(lds + kStageA, wn * 8 + j, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) alo[i] = frag_k(lds, wm * 8 + i, lane);
+    read_scales(sc, wm, wn, lane, sa, sb);
+    half0_mx<FA, FB>(acc, bq, alo, ahi, lds, wm, lane, sa, sb);
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+        const int cur = kt & 1;
+        mid_step_barrier();
+        half1_mx<FA, FB, true>(acc, bq, alo, ahi, src, lds_addr + cur * kStage, sc_addr + cur * kScStage,
+                               lds + (cur ^ 1) * kStage, sc + (cur ^ 1) * kScStage, min(kt + 2, KT - 1), wave, wm,
+                               wn, lane, sa, sb, na, nb);
+        half0_mx<FA, FB>(acc, bq, alo, ahi, lds + (cur ^ 1) * kStage, wm, lane, na, nb);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            sa[h] = na[h];
+            sb[h] = nb[h];
+        }
+    }
+    mid_step_barrier();
+    half1_mx<FA, FB, false>(acc, bq, alo, ahi, src, 0, 0, lds, sc, 0, wave, wm, wn, lane, sa, sb, na, nb);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+}
+
 // Half tiles balance the last partial round of a launch (tiles that would
 // leave most CUs idle are split into two 128-row halves, each a unit of work).
 // A wave owns 64 x 128 outputs (A blocks 0..3 of its 64 rows, B blocks 0..7 of
@@ -460,6 +634,8 @@ struct GemmGroup {
                           // full_units + 2 k + h is half h of tile full_units + k
     int first_unit;       // this launch walks units first_unit .. units - 1
     int units;
+    const uint8_t* sa;    // block-scaled launches (one problem): E8M0 scales [P][R / 32]
+    const uint8_t* sb;    // and [Q][R / 32]
 };
 
 // Everything a workgroup needs about its current tile (all wave-uniform).
@@ -573,6 +749,21 @@ __device__ __forceinline__ void start_tile(Sources& src, const Work& w, uint32_t
     }
 }
 
+// Block-scaled launches (K-major operands, tiles inside the matrices): set up
+// the sources of tile w and issue its first two stages with their scales.
+__device__ __forceinline__ void start_tile_mx(Sources& src, const GemmGroup& g, const Work& w, uint32_t lds_addr,
+                                              uint32_t sc_addr, int wave, int lane)
+{
+    set_sources<kKMajor, kKMajor>(src, w, wave, lane);
+    const uint32_t nb = (uint32_t)(w.R / 32);                 // scale bytes per row
+    src.sa = g.sa;
+    src.sb = g.sb;
+    src.sa_off = (uint32_t)(w.m0 + wave * 64 + lane) * nb;
+    src.sb_off = (uint32_t)(w.n0 + wave * 64 + lane) * nb;
+    issue_stage_mx(src, lds_addr, sc_addr, 0, wave);
+    issue_stage_mx(src, lds_addr + kStage, sc_addr + kScStage, min(1, w.KT - 1), wave);
+}
+
 // A 16-byte output store; NT: non-temporal, for the backward products' dX and dW:
 // kept out of the caches, they do not displace the operand panels that the XCDs
 // keep re-fetching (measured on the 7B-layer step: 1.1% shorter, the backward
@@ -654,6 +845,59 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[8][8], const Work& don
                 const uint4 o = *reinterpret_cast<const uint4*>(ew + rr * 256 + ((c ^ (rr & 15)) * 16));
                 const int m = wrow + c2 * 32 + rr;
                 const int n = done.n0 + wn * 128 + c * 8;
+                if (m >= done.ms && m < done.P && n >= done.ns && n < done.Q)
+                    store16<NT>(reinterpret_cast<uint8_t*>(done.out + (size_t)m * done.Q + n), o);
+            }
+        }
+    }
+}
+
+// Epilogue of a block-scaled tile: as epilogue() above (no descale: the block
+// scales are inside the sums), staging 16-row chunks (one A block) in a 4 KB
+// LDS region per wave.
+template <bool NT>
+__device__ __forceinline__ void epilogue_mx(const v4f (&acc)[8][8], const Work& done, uint8_t* epi, int wave,
+                                            int wm, int wn, int lane)
+{
+    uint8_t* ew = epi + wave * (kEpiRowsMx * 256);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int r16 = ln & 15, q4 = ln >> 4;
+    const int wrow = done.m0 + wm * 128;
+    const bool full = done.ms == done.m0 && done.ns == done.n0 && done.m0 + kBM <= done.P && done.n0 + kBN <= done.Q;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {                          // chunk: A block i (16 rows)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const f32x2 v01 = {acc[i][j][0], acc[i][j][1]};
+            const f32x2 v23 = {acc[i][j][2], acc[i][j][3]};
+            uint2 o;
+            o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
+            o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
+            const int chunk = (2 * j + (q4 >> 1)) ^ r16;
+            *reinterpret_cast<uint2*>(ew + r16 * 256 + chunk * 16 + (q4 & 1) * 8) = o;
+        }
+        if (full) {
+            auto rd = [&](int it) {
+                const int rr = it * 4 + q4;
+                return *reinterpret_cast<const uint4*>(ew + rr * 256 + ((r16 ^ rr) * 16));
+            };
+            const uint4 o0 = rd(0), o1 = rd(1), o2 = rd(2), o3 = rd(3);
+            uint8_t* base = reinterpret_cast<uint8_t*>(done.out) +
+                            ((size_t)(wrow + i * 16) * done.Q + done.n0 + wn * 128) * 2;
+            const uint32_t loff = (uint32_t)(q4 * done.Q + r16 * 8) * 2u;
+            const size_t rs = (size_t)8 * done.Q;                 // 4 rows, in bytes
+            store16<NT>(base + loff, o0);
+            store16<NT>(base + rs + loff, o1);
+            store16<NT>(base + 2 * rs + loff, o2);
+            store16<NT>(base + 3 * rs + loff, o3);
+        } else {
+#pragma unroll
+            for (int it = 0; it < kEpiRowsMx / 4; ++it) {
+                const int rr = it * 4 + q4;
+                const uint4 o = *reinterpret_cast<const uint4*>(ew + rr * 256 + ((r16 ^ rr) * 16));
+                const int m = wrow + i * 16 + rr;
+                const int n = done.n0 + wn * 128 + r16 * 8;
                 if (m >= done.ms && m < done.P && n >= done.ns && n < done.Q)
                     store16<NT>(reinterpret_cast<uint8_t*>(done.out + (size_t)m * done.Q + n), o);
             }
@@ -851,6 +1095,53 @@ __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
     }
 }
 
+// Block-scaled (MX) products: the persistent walk of gemm_tn_kernel (XCD-major
+// slots, grouped raster, next tile's first stages issued before the epilogue)
+// over full-size tiles of K-major operands, with each operand row's E8M0 block
+// scales loaded beside its codes and applied by the matrix instruction; the
+// output is the bf16 of the fp32 sums (no per-tensor factor).  No half-tile
+// round: a launch's last partial round runs as full tiles.
+template <int FA, int FB, bool NT>
+__global__ void __launch_bounds__(256, 1) gemm_mx_kernel(const GemmGroup g)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+    __shared__ __attribute__((aligned(1024))) uint8_t epi[4 * kEpiRowsMx * 256];
+    __shared__ __attribute__((aligned(1024))) uint8_t sc[2 * kScStage];
+
+    const int G = gridDim.x;
+    int slot = blockIdx.x;
+    if (G % 8 == 0) slot = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+    const uint32_t sc_addr = (uint32_t)(uintptr_t)sc;
+
+    Sources src;
+    v8i bq[8], alo[4], ahi[4];
+    v4f acc[8][8];
+
+    int v = g.first_unit + slot;
+    if (v >= g.units) return;
+    Work w = work_of<false, false, false>(g, v);
+    start_tile_mx(src, g, w, lds_addr, sc_addr, wave, lane);
+    for (;;) {
+        tile_mainloop_mx<FA, FB>(acc, bq, alo, ahi, src, lds, lds_addr, sc, sc_addr, w.KT, wave, wm, wn, lane);
+        const Work done = w;
+        const int next = v + G;
+        if (next < g.units) {
+            v = next;
+            w = work_of<false, false, false>(g, v);
+            start_tile_mx(src, g, w, lds_addr, sc_addr, wave, lane);
+        }
+        epilogue_mx<NT>(acc, done, epi, wave, wm, wn, lane);
+        // the loop-top wait (vmcnt <= 18) then proves the next tile's first stage
+        // has landed, as in gemm_tn_kernel
+        if (next >= g.units) break;
+    }
+}
+
 static GemmProblem make_problem(const uint8_t* A, int la, const uint8_t* B, int lb, const float* inv_a,
                                 const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R)
 {
@@ -958,6 +1249,24 @@ hipError_t launch_gemm_gate_up(const uint8_t* A, const uint8_t* B, const float* 
     g.p[1] = g.p[0];
     g.count = 1;
     return launch_group<0, 0, kSetKK, true, false>(g, stream);
+}
+
+hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* sa, int fmt_a, const uint8_t* B, const uint8_t* sb,
+                          int fmt_b, void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream)
+{
+    if (fmt_b != 0 || P < kBM || Q < kBN) return hipErrorInvalidValue;
+    GemmGroup g{};
+    g.p[0] = make_problem(A, kKMajor, B, kKMajor, nullptr, nullptr, out, P, Q, R);
+    g.sa = sa;
+    g.sb = sb;
+    g.p[1] = g.p[0];
+    g.count = 1;
+    g.total_tiles = g.full_units = g.units = g.p[0].tiles_m * g.p[0].tiles_n;
+    g.first_unit = 0;
+    const int cus = device_cu_count();
+    const dim3 grid(g.units < cus ? g.units : cus);
+    if (fmt_a == 0) return launch(gemm_mx_kernel<0, 0, false>, grid, dim3(256), stream, g);
+    return launch(gemm_mx_kernel<1, 0, false>, grid, dim3(256), stream, g);
 }
 
 hipError_t launch_gemm_tn(const uint8_t* A, int fmt_a, int la, const uint8_t* B, int fmt_b, int lb,

@@ -462,4 +462,90 @@ hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, c
     return launch_quantize_fmt<1>(x, rows, cols, absmax, q, qt, scale, inv_scale, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Block (MX) quantisation: the alternative to the per-tensor scale that the LLMQ
+// summary (section 2) says needs native hardware support, as gfx950's
+// block-scaled matrix instructions provide.  Following the OCP Microscaling
+// (MX) formats specification v1.0 (section 6.3): every 32 consecutive elements
+// of a row share the scale 2^e, e = floor(log2 max |x|) - emax (emax = 8 for
+// E4M3, 15 for E5M2: the exponent of the format's largest normal), clamped to
+// [-127, 127] (-127 for an all-zero block), stored as the E8M0 byte e + 127;
+// the elements are x * 2^-e (exact) encoded like every other value (nearest
+// even, saturating).  A block holding a NaN or an infinity gets the NaN scale
+// (255) and the unscaled encodings.  One pass, no statistic launch before it:
+// reads 2 B and writes 1 + 1/32 B per element.
+//
+// Lane l converts the 16-byte vector v (8 elements); the 4 lanes of a block are
+// 4 consecutive lanes (v % 4 == l % 4: the grid stride is a multiple of 4), so
+// the block's maximum takes two shuffles.  Each lane keeps one 16-byte load in
+// flight: four 256-lane blocks per CU are 4 MiB over the chip, the best figure of
+// the streaming-copy probe.  NT: non-temporal loads (large inputs).
+template <int FMT, bool NT>
+__global__ void __launch_bounds__(256) mx_quantize_kernel(const u32x4* __restrict__ x, int64_t nvec,
+                                                          uint2* __restrict__ q, uint8_t* __restrict__ scales)
+{
+    constexpr int emax = FMT == 0 ? 8 : 15;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += stride) {
+        const u32x4 w = NT ? __builtin_nontemporal_load(x + v) : x[v];
+        // the largest finite magnitude (bf16 bits) and whether a NaN or an infinity occurs
+        uint32_t m = 0, bad = 0;
+        const uint32_t hw[8] = {w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16,
+                                w.z & 0xFFFFu, w.z >> 16, w.w & 0xFFFFu, w.w >> 16};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t a = hw[i] & 0x7FFFu;
+            bad |= a >= 0x7F80u;
+            m = (a < 0x7F80u && a > m) ? a : m;
+        }
+#pragma unroll
+        for (int off = 1; off <= 2; off <<= 1) {
+            const uint32_t om = (uint32_t)__shfl_xor((int)m, off, 64);
+            bad |= (uint32_t)__shfl_xor((int)bad, off, 64);
+            m = om > m ? om : m;
+        }
+        float s = 1.0f;                   // a block with a NaN or an infinity: unscaled
+        uint32_t sbyte = 255;
+        if (!bad) {
+            // floor(log2 m): the exponent field of a normal bf16; m * 2^-133 for a subnormal one
+            const int fl = m >= 0x80u ? (int)(m >> 7) - 127 : 31 - __builtin_clz(m | 1u) - 133;
+            int e = m ? fl - emax : -127;
+            e = e < -127 ? -127 : e;      // at most 127 - emax: no upper clamp is reached
+            s = __uint_as_float((uint32_t)(127 - e) << 23);       // 2^-e, a normal fp32
+            sbyte = (uint32_t)(e + 127);
+        }
+        uint2 c = quant8<FMT>(make_uint4(w.x, w.y, w.z, w.w), s);
+        if (bad) {
+            // a NaN element takes the NaN code with its sign (S.1111111), whatever
+            // the converter makes of an unscaled NaN payload
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if ((hw[i] & 0x7FFFu) > 0x7F80u) {
+                    const uint32_t code = ((hw[i] >> 8) & 0x80u) | 0x7Fu, sh = (uint32_t)(i & 3) * 8;
+                    if (i < 4) c.x = (c.x & ~(0xFFu << sh)) | (code << sh);
+                    else c.y = (c.y & ~(0xFFu << sh)) | (code << sh);
+                }
+            }
+        }
+        q[v] = c;
+        if ((threadIdx.x & 3) == 0) scales[v >> 2] = (uint8_t)sbyte;
+    }
+}
+
+hipError_t launch_mx_quantize(const void* x, int64_t n, int fmt, uint8_t* q, uint8_t* scales, hipStream_t stream)
+{
+    const int64_t nvec = n / 8;
+    int64_t blocks = (nvec + 255) / 256;
+    const int64_t cap = (int64_t)device_cu_count() * 4;
+    if (blocks > cap) blocks = cap;
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+    uint2* qv = reinterpret_cast<uint2*>(q);
+    const bool nt = 2 * n >= kAbsStreamBytes;
+    if (fmt == 0)
+        return nt ? launch(mx_quantize_kernel<0, true>, dim3((unsigned)blocks), dim3(256), stream, xv, nvec, qv, scales)
+                  : launch(mx_quantize_kernel<0, false>, dim3((unsigned)blocks), dim3(256), stream, xv, nvec, qv, scales);
+    return nt ? launch(mx_quantize_kernel<1, true>, dim3((unsigned)blocks), dim3(256), stream, xv, nvec, qv, scales)
+              : launch(mx_quantize_kernel<1, false>, dim3((unsigned)blocks), dim3(256), stream, xv, nvec, qv, scales);
+}
+
 }  // namespace fp8k

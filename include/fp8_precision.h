@@ -346,6 +346,47 @@ fp8_status fp8_gemm_backward_mn(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_
                                 void* dx, void* dw, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
+ * Block (MX) scaling -- the alternative to one scale per tensor that the LLMQ
+ * summary (section 2) says needs native hardware support (gfx950 has
+ * block-scaled matrix instructions).  The pages define no format; these calls
+ * follow the OCP Microscaling (MX) formats specification v1.0 (section 6.3).
+ *
+ * fp8_mx_quantize: every 32 consecutive elements of a row of the bf16
+ * [rows, cols] tensor x share one scale 2^e,
+ *   e = floor(log2(max |x| over the block)) - emax   (emax = 8 for E4M3, 15 for E5M2)
+ * clamped to [-127, 127] (-127 for an all-zero block), and
+ *   q[i, j]           = encode_fmt(x[i, j] * 2^-e)   (exact product; nearest even, saturating)
+ *   scales[i, j / 32] = e + 127                      (an E8M0 byte)
+ * A block holding a NaN or an infinity gets scales = 255 (NaN) and the unscaled
+ * encodings.  One pass: no statistic call comes first.
+ *
+ *   x       bf16 [rows, cols], 16-byte aligned
+ *   fmt     FP8_E4M3 or FP8_E5M2
+ *   q       u8 [rows, cols], 16-byte aligned
+ *   scales  u8 [rows, cols / 32] (row-major: block b of row i at i * cols / 32 + b)
+ * Constraints: cols % 32 == 0 (else FP8_ERR_UNSUPPORTED); buffers must not overlap.
+ */
+fp8_status fp8_mx_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt, uint8_t* q,
+                           uint8_t* scales, hipStream_t stream);
+
+/*
+ * fp8_mx_gemm_fwd: the forward product of block-scaled operands,
+ *   Y[m, n] = bf16_RNE( RN32( sum_k dec(X[m, k]) 2^ex(m, k / 32) dec(W[n, k]) 2^ew(n, k / 32) ) )
+ * with fp32 accumulation and no per-tensor factor (each 2^e is the E8M0 scale
+ * of the 32-element block holding the code; a NaN scale gives NaN).  The
+ * block scales are applied by the matrix instruction itself.
+ *
+ *   xq, sx   codes [M, K] (x_fmt: FP8_E4M3 or FP8_E5M2) and scales [M, K / 32]
+ *            from fp8_mx_quantize of X
+ *   wq, sw   codes [N, K] (E4M3) and scales [N, K / 32] from fp8_mx_quantize of W
+ *   y        bf16 [M, N]
+ * Constraints: those of fp8_gemm_fwd, and M >= 256, N >= 256; scales 4-byte
+ * aligned; y may not overlap any input.
+ */
+fp8_status fp8_mx_gemm_fwd(const uint8_t* xq, const uint8_t* sx, fp8_fmt x_fmt, const uint8_t* wq,
+                           const uint8_t* sw, void* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
  * Measurement reference, not a step of the FP8 method: a plain device copy
  * dst[0, bytes) = src[0, bytes), built like the streaming kernels above
  * (16-byte vectors, non-temporal loads, the launch shape at which a copy

@@ -343,3 +343,39 @@ def test_stream_copy_validation(lib):
     assert f(A16 + 8, B16, 64, None) == UNSUPPORTED                 # misaligned source
     assert f(A16, B16 + 4, 64, None) == UNSUPPORTED                 # misaligned destination
 
+
+
+def test_mx_quantize_validation(lib):
+    f = lib.fp8_mx_quantize
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    q, sc = B16, B16 + (1 << 20)
+    assert f(None, 4, 64, 0, q, sc, None) == INVALID
+    assert f(A16, 4, 64, 0, None, sc, None) == INVALID
+    assert f(A16, 4, 64, 0, q, None, None) == INVALID
+    assert f(A16, 4, 64, 2, q, sc, None) == INVALID                  # bad format
+    assert f(A16, 0, 64, 0, q, sc, None) == INVALID                  # empty
+    assert f(A16, 4, 64, 0, A16 + 64, sc, None) == INVALID           # q overlaps x
+    assert b"overlap" in lib.fp8_last_error()
+    assert f(A16, 4, 48, 0, q, sc, None) == UNSUPPORTED              # cols not a multiple of 32
+    assert f(A16 + 2, 4, 64, 0, q, sc, None) == UNSUPPORTED          # misaligned input
+    assert f(A16, 4, 64, 0, q + 8, sc, None) == UNSUPPORTED          # misaligned codes
+
+
+def test_mx_gemm_validation(lib):
+    f = lib.fp8_mx_gemm_fwd
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    X, SX, W, SW, Y = A16, A16 + (1 << 24), B16, B16 + (1 << 24), C16
+    ok = (X, SX, 0, W, SW, Y, 512, 512, 256, None)
+    bad = lambda **kw: f(*[kw.get(k, v) for k, v in zip(("x", "sx", "fmt", "w", "sw", "y", "M", "N", "K", "s"), ok)])
+    assert bad(sx=None) == INVALID and bad(sw=None) == INVALID and bad(x=None) == INVALID
+    assert bad(fmt=3) == INVALID
+    assert bad(y=SX) == INVALID                                       # output over the scales
+    assert b"overlaps" in lib.fp8_last_error()
+    assert bad(M=128) == UNSUPPORTED and bad(N=240) == UNSUPPORTED    # below one tile
+    assert bad(K=192) == UNSUPPORTED                                  # reduction not a multiple of 128
+    assert bad(sx=SX + 2) == UNSUPPORTED                              # misaligned scales
+    assert bad(x=X + 8) == UNSUPPORTED                                # misaligned codes

@@ -1,0 +1,186 @@
+"""GPU parity of the block (MX) calls against the oracle.
+
+fp8_mx_quantize (bit-exact codes and E8M0 scales):
+* every bf16 pattern, in blocks whose maximum is planted at 1, 2 and 32 times
+  the largest magnitude of the others (so each pattern is seen under several
+  block scales), both formats; NaN and infinity patterns make their block's
+  scale NaN;
+* all-zero, tiny (clamped scale), saturating and mixed blocks;
+* random tensors over several grid-stride rounds, a ragged column count
+  (cols % 128 != 0), and the 7B-layer input and weight at full size.
+
+fp8_mx_gemm_fwd (the oracle's MX GEMM on the GPU's own codes and scales;
+relative Frobenius error <= 5e-3 and the any-order fp32 summation bound):
+* with every scale 1.0 it equals the per-tensor GEMM with unit factors, bit
+  for bit (same tiles, same reduction order, the block-scaled instruction);
+* every output of a launch over two rounds with ragged rows and columns
+  (tiles shifted back at both edges), for E4M3 and E5M2 inputs, on data whose
+  blocks span 2^30 of scale;
+* the 7B-layer QKV forward and the 14B-layer (outlier channels) QKV forward at
+  full size on sampled rows;
+* a NaN scale makes exactly its row's (column's) outputs NaN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import E4M3, E5M2, bf16_to_f64, decode_abs64, gemm_compare, say, u16, u8
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fp8():
+    import fp8_precision_amd
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return fp8_precision_amd
+
+
+def to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def check_mx(fp8, orc, bits, fmt, what):
+    say("mx_quantize", what, bits.shape, fmt)
+    q, sc = fp8.mx_quantize(to_dev(bits), fmt)
+    torch.cuda.synchronize()
+    q_r, sc_r = orc.mx_quantize(np.ascontiguousarray(bits), fmt)
+    gq, gs = u8(q), u8(sc)
+    bad = np.argwhere(gs != sc_r)
+    assert bad.size == 0, (what, "scales", bad[:4].tolist(), gs[tuple(bad[0])], sc_r[tuple(bad[0])])
+    bad = np.argwhere(gq != q_r)
+    assert bad.size == 0, (what, "codes", bad[:4].tolist(), hex(gq[tuple(bad[0])]), hex(q_r[tuple(bad[0])]))
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("lift", [0, 1, 5])
+def test_every_bf16_pattern(fp8, orc, fmt, lift):
+    """31 patterns per block and a planted maximum 2^lift times their largest magnitude."""
+    pats = np.arange(65536, dtype=np.uint32)
+    pats = np.concatenate([pats, pats[:(-len(pats)) % 31]])     # whole blocks of 31
+    blocks = pats.reshape(-1, 31)
+    mag = blocks & 0x7FFF
+    finite = np.where(mag < 0x7F80, mag, 0)
+    top = finite.max(axis=1)
+    # the planted maximum: the largest finite magnitude times 2^lift (bf16 bits: add to the
+    # exponent field; kept finite and made at least the smallest normal)
+    planted = np.minimum(np.maximum(top, 0x80) + (lift << 7), 0x7F7F)
+    x = np.concatenate([planted[:, None], blocks], axis=1).astype(np.uint16)
+    check_mx(fp8, orc, x, fmt, f"every pattern, lift {lift}")
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_special_blocks(fp8, orc, fmt):
+    rows = []
+    rows.append(np.zeros(32, np.uint16))                                    # all zero
+    z = np.zeros(32, np.uint16); z[3] = 0x8000; rows.append(z)              # -0
+    rows.append(np.full(32, 0x0001, np.uint16))                             # smallest subnormal: clamped scale
+    t = np.full(32, 0x0C00, np.uint16); t[7] = 0x8C40; rows.append(t)       # tiny normals
+    s = np.full(32, 0x3F00, np.uint16); s[0] = 0x41F8; s[1] = 0xC1F8; rows.append(s)   # 31, -31: saturate
+    for bad in (0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x7F81):
+        r = np.full(32, 0x3FC0, np.uint16); r[17] = bad; rows.append(r)
+    big = np.full(32, 0x7F7F, np.uint16); big[4] = 0xFF7F; rows.append(big)  # largest finite
+    check_mx(fp8, orc, np.stack(rows).reshape(len(rows), 32), fmt, "special blocks")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (3, 96), (17, 4128), (1024, 1024), (777, 2080)])
+def test_random_shapes(fp8, orc, rows, cols):
+    x = workloads.draw(31, rows + cols, (rows, cols), 2.0)
+    bits = workloads.bf16_bits(x)
+    for fmt in (E4M3, E5M2):
+        check_mx(fp8, orc, bits, fmt, f"random {rows}x{cols}")
+
+
+def test_layer7b_full_size(fp8, orc):
+    cfg = workloads.CONFIGS["layer7b"]
+    for li, draw in ((0, workloads.draw_x), (0, workloads.draw_w), (2, workloads.draw_w)):
+        x = draw(cfg, li)
+        check_mx(fp8, orc, workloads.bf16_bits(x), E4M3, f"7B {draw.__name__} linear {li}")
+
+
+def mx_bound_check(y_bits, ref_bits, a, sa, fa, b, sb, rows, what):
+    """|gpu - oracle| within the bf16 rounding of both plus 4 K 2^-24 sum_k |a_k b_k| (scaled)."""
+    K = a.shape[1]
+    ea = np.exp2(np.repeat(sa[rows].astype(np.float64) - 127, 32, axis=1))
+    eb = np.exp2(np.repeat(sb.astype(np.float64) - 127, 32, axis=1))
+    absprod = (decode_abs64(a[rows], fa) * ea) @ (decode_abs64(b, E4M3) * eb).T
+    g, r = bf16_to_f64(y_bits), bf16_to_f64(ref_bits)
+    bound = (np.abs(r) + np.abs(g)) * 2.0 ** -8 + 4.0 * K * 2.0 ** -24 * absprod + 1e-37
+    bad = np.abs(g - r) > bound
+    assert not bad.any(), (what, int(bad.sum()), np.argwhere(bad)[:4].tolist())
+
+
+def mx_operands(fp8, x, w, fx=E4M3):
+    xq, sx = fp8.mx_quantize(x.cuda(), fx)
+    wq, sw = fp8.mx_quantize(w.cuda(), E4M3)
+    return xq, sx, wq, sw
+
+
+def test_unit_scales_equal_per_tensor_gemm(fp8):
+    say("mx_gemm unit scales", 4096, 4352, 1024)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    a = torch.randn((4096, 1024), generator=g, device="cuda").mul_(60).to(torch.float8_e4m3fn).view(torch.uint8)
+    b = torch.randn((4352, 1024), generator=g, device="cuda").mul_(60).to(torch.float8_e4m3fn).view(torch.uint8)
+    sa = torch.full((4096, 32), 127, dtype=torch.uint8, device="cuda")
+    sb = torch.full((4352, 32), 127, dtype=torch.uint8, device="cuda")
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    y = u16(fp8.mx_gemm_fwd(a, sa, b, sb))
+    ref = u16(fp8.gemm_fwd(a, b, one, one))
+    bad = np.argwhere(y != ref)
+    assert bad.size == 0, ("unit-scale MX product differs from the per-tensor one", bad[:4].tolist())
+
+
+@pytest.mark.parametrize("fx", [E4M3, E5M2])
+def test_every_output_two_rounds(fp8, orc, fx):
+    """4000 x 4368 x 512: 16 x 18 = 288 tiles (a round and 32 more), last row and
+    column tiles shifted back; blocks scaled over 2^30."""
+    M, N, K = 4000, 4368, 512
+    say("mx_gemm every output", M, N, K, fx)
+    rng = np.random.default_rng(17 + fx)
+    xs = rng.standard_normal((M, K)) * np.exp2(rng.integers(-15, 15, (M, K // 32))).repeat(32, axis=1)
+    ws = rng.standard_normal((N, K)) * np.exp2(rng.integers(-6, 6, (1, K // 32))).repeat(32, axis=1)
+    x = torch.from_numpy(xs.astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy(ws.astype(np.float32)).to(torch.bfloat16)
+    xq, sx, wq, sw = mx_operands(fp8, x, w, fx)
+    y = u16(fp8.mx_gemm_fwd(xq, sx, wq, sw, fx))
+    a, sa, b, sb = u8(xq), u8(sx), u8(wq), u8(sw)
+    ref = orc.mx_gemm(a, sa, fx, b, sb, E4M3)
+    gemm_compare(y, ref, "mx every output")
+    rows = np.arange(M, dtype=np.int64)
+    for r0 in range(0, M, 1000):
+        rr = rows[r0:r0 + 1000]
+        mx_bound_check(y[rr], ref[rr], a, sa, fx, b, sb, rr, "mx every output")
+
+
+@pytest.mark.parametrize("cfg_name", ["layer7b", "layer14b"])
+def test_qkv_forward_full_size(fp8, orc, cfg_name):
+    cfg = workloads.CONFIGS[cfg_name]
+    x, w = workloads.draw_x(cfg, 0), workloads.draw_w(cfg, 0)
+    say("mx_gemm qkv full size", cfg_name, tuple(x.shape), tuple(w.shape))
+    xq, sx, wq, sw = mx_operands(fp8, x, w)
+    y = u16(fp8.mx_gemm_fwd(xq, sx, wq, sw))
+    a, sa, b, sb = u8(xq), u8(sx), u8(wq), u8(sw)
+    rng = np.random.default_rng(3)
+    M = a.shape[0]
+    rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], rng.integers(0, M, 252)])).astype(np.int64)
+    ref = orc.mx_gemm(a, sa, E4M3, b, sb, E4M3, rows=rows)
+    gemm_compare(y[rows], ref, f"{cfg_name} mx qkv")
+    mx_bound_check(y[rows], ref, a, sa, E4M3, b, sb, rows, f"{cfg_name} mx qkv")
+
+
+def test_nan_scale(fp8):
+    M, N, K = 512, 768, 256
+    say("mx_gemm nan scale", M, N, K)
+    g = torch.Generator(device="cuda").manual_seed(8)
+    a = torch.randn((M, K), generator=g, device="cuda").mul_(30).to(torch.float8_e4m3fn).view(torch.uint8)
+    b = torch.randn((N, K), generator=g, device="cuda").mul_(30).to(torch.float8_e4m3fn).view(torch.uint8)
+    sa = torch.full((M, K // 32), 120, dtype=torch.uint8, device="cuda")
+    sb = torch.full((N, K // 32), 125, dtype=torch.uint8, device="cuda")
+    sa[300, 5] = 255
+    sb[700, 0] = 255
+    y = bf16_to_f64(u16(fp8.mx_gemm_fwd(a, sa, b, sb)))
+    want = np.zeros((M, N), bool)
+    want[300, :] = True
+    want[:, 700] = True
+    assert np.array_equal(np.isnan(y), want)
