@@ -625,6 +625,91 @@ def step_shapes(fp8, dev, stream, cfg_name, steps=5, warmup=5):
             "calls": rows}
 
 
+def mx_forward(fp8, dev, cfg_name="layer7b", reps=10):
+    """Block (MX) scaling next to the per-tensor path, for each linear's forward
+    (the measured alternative, not the headline): per-tensor = the statistics of
+    X and W in one launch, their quantisation (codes only) in one launch, the
+    FP8 GEMM; MX = fp8_mx_quantize of X, of W (one pass each, no statistic
+    launch), the block-scaled GEMM.  Inputs drawn by workloads.py (X of the down
+    linear drawn like the others); the two paths interleaved, `reps` rounds, an
+    event pair around every call, medians."""
+    cfg = workloads.CONFIGS[cfg_name]
+    E4M3 = fp8.E4M3
+    ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    rows = []
+    tot = {"pt_q": 0.0, "pt_g": 0.0, "mx_q": 0.0, "mx_g": 0.0, "flop": 0.0, "mx_bytes": 0.0, "pt_bytes": 0.0}
+    for li, L in enumerate(cfg.linears):
+        x = workloads.draw_x(cfg, li).to(dev)
+        w = workloads.draw_w(cfg, li).to(dev)
+        M, K, N = cfg.M, L.K, L.N
+        stats = torch.zeros(2, dtype=torch.float32, device=dev)
+        am = [stats[0:1], stats[1:2]]
+        xq, wq = torch.empty((M, K), dtype=torch.uint8, device=dev), torch.empty((N, K), dtype=torch.uint8, device=dev)
+        sc = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(4)]
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        mxq, mwq = torch.empty_like(xq), torch.empty_like(wq)
+        sx = torch.empty((K // 128, M, 4), dtype=torch.uint8, device=dev)
+        sw = torch.empty((K // 128, N, 4), dtype=torch.uint8, device=dev)
+        calls = {
+            "pt_abs": lambda: fp8.absmax_accumulate_many([x, w], am),
+            "pt_quant": lambda: fp8.quantize_many([x, w], E4M3, am, want_q=True, want_qt=False, qs=[xq, wq],
+                                                  scales=[sc[0], sc[1]], inv_scales=[sc[2], sc[3]]),
+            "pt_gemm": lambda: fp8.gemm_fwd(xq, wq, sc[2], sc[3], y),
+            "mx_x": lambda: fp8.mx_quantize(x, E4M3, q=mxq, scales=sx),
+            "mx_w": lambda: fp8.mx_quantize(w, E4M3, q=mwq, scales=sw),
+            "mx_gemm": lambda: fp8.mx_gemm_fwd(mxq, sx, mwq, sw, E4M3, out=y),
+        }
+        order = [["pt_abs", "pt_quant", "pt_gemm"], ["mx_x", "mx_w", "mx_gemm"]]
+        t = {k: [] for k in calls}
+        for r in range(reps + 2):
+            for seq in order:
+                stats.zero_()
+                pairs = []
+                for k in seq:
+                    a, b = ev()
+                    a.record()
+                    calls[k]()
+                    b.record()
+                    pairs.append((k, a, b))
+                torch.cuda.synchronize()
+                if r >= 2:
+                    for k, a, b in pairs:
+                        t[k].append(a.elapsed_time(b) * 1e-3)
+        med = {k: float(np.median(v)) for k, v in t.items()}
+        flop = 2.0 * M * N * K
+        pt_q, mx_q = med["pt_abs"] + med["pt_quant"], med["mx_x"] + med["mx_w"]
+        pt_bytes = 2 * (M + N) * K + 3 * (M + N) * K           # statistic pass + quantise pass
+        mx_bytes = 3 * (M + N) * K + (M + N) * K / 32           # one pass: read 2 B, write 1 + 1/32 B
+        rows.append({"linear": L.name, "M": M, "N": N, "K": K,
+                     "per_tensor": {"quantise_us": round(pt_q * 1e6, 1), "gemm_us": round(med["pt_gemm"] * 1e6, 1),
+                                    "gemm_tflops": round(flop / med["pt_gemm"] / 1e12, 1),
+                                    "quantise_gbs": round(pt_bytes / pt_q / 1e9, 1)},
+                     "mx": {"quantise_us": round(mx_q * 1e6, 1), "gemm_us": round(med["mx_gemm"] * 1e6, 1),
+                            "gemm_tflops": round(flop / med["mx_gemm"] / 1e12, 1),
+                            "quantise_gbs": round(mx_bytes / mx_q / 1e9, 1)}})
+        tot["pt_q"] += pt_q
+        tot["pt_g"] += med["pt_gemm"]
+        tot["mx_q"] += mx_q
+        tot["mx_g"] += med["mx_gemm"]
+        tot["flop"] += flop
+        tot["mx_bytes"] += mx_bytes
+        tot["pt_bytes"] += pt_bytes
+        del x, w, xq, wq, mxq, mwq, sx, sw, y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"workload": WORKLOADS[cfg_name] + ", forward of each linear",
+            "per_tensor": {"quantise_us": round(tot["pt_q"] * 1e6, 1), "gemm_us": round(tot["pt_g"] * 1e6, 1),
+                           "gemm_tflops": round(tot["flop"] / tot["pt_g"] / 1e12, 1),
+                           "quantise_gbs": round(tot["pt_bytes"] / tot["pt_q"] / 1e9, 1)},
+            "mx": {"quantise_us": round(tot["mx_q"] * 1e6, 1), "gemm_us": round(tot["mx_g"] * 1e6, 1),
+                   "gemm_tflops": round(tot["flop"] / tot["mx_g"] / 1e12, 1),
+                   "gemm_frac": round(tot["flop"] / tot["mx_g"] / 1e12 / FP8_PEAK_TFLOPS, 4),
+                   "quantise_gbs": round(tot["mx_bytes"] / tot["mx_q"] / 1e9, 1)},
+            "timing": f"{reps} interleaved rounds, an event pair around every call, medians; quantisation "
+                      "without transposed copies on both paths",
+            "linears": rows}
+
+
 def vs_hipblaslt(fp8, ops, dev, reps=10, rounds=3):
     """Every GEMM call of the step next to hipBLASLt (torch._scaled_mm, per-tensor
     scales, bf16 out) on the same FP8 operand bytes, timed interleaved (ours,
@@ -841,6 +926,8 @@ def main():
     ap.add_argument("--no-shapes", action="store_true",
                     help="skip the 14B- and 32B-class layer steps (their GEMM figures) reported with the layer7b "
                          "workload")
+    ap.add_argument("--no-mx", action="store_true",
+                    help="skip the block-scaled (MX) forward measurement reported with the layer7b workload")
     ap.add_argument("--quant-mode", choices=("pair", "linear", "step"), default="pair",
                     help="pair: each linear's X and W quantised in one launch (their statistics in one launch for "
                          "QKV and O); linear: X and W quantised in separate launches; step: the four weights and the "
@@ -938,6 +1025,7 @@ def main():
     if args.workload == "layer7b" and not args.no_shapes:
         for other in ("layer14b", "layer32b"):
             shapes[other] = step_shapes(fp8, dev, stream, other)
+    mx = mx_forward(fp8, dev) if args.workload == "layer7b" and not args.no_mx else None
     clock = None if args.no_clock else sustained_clock(ops)
     want_cpu = not args.no_cpu_baseline and (args.workload == "layer7b" or args.cpu_baseline)
     cpu = cpu_baseline(ops, args.cpu_gemm_rows) if want_cpu else None
@@ -1002,6 +1090,8 @@ def main():
     }
     if shapes:
         line["shapes"] = shapes
+    if mx:
+        line["mx_forward"] = mx
     line["breakdown"] = breakdown
     print(json.dumps(line))
 

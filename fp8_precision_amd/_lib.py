@@ -444,8 +444,9 @@ def gemm_backward_mn(dyq, dy_fmt, wq, xq, inv_sdy, inv_sw, inv_sx, dx=None, dw=N
 
 
 def mx_quantize(x: torch.Tensor, fmt: int, q: torch.Tensor | None = None, scales: torch.Tensor | None = None):
-    """Block (MX) quantisation of a 2-D bf16 tensor (cols a multiple of 32):
-    returns (q uint8 [rows, cols], scales uint8 [rows, cols / 32], E8M0)."""
+    """Block (MX) quantisation of a 2-D bf16 tensor (cols a multiple of 128):
+    returns (q uint8 [rows, cols], scales uint8 [cols / 128, rows, 4], E8M0: the
+    scale of block b of row i at [b // 4, i, b % 4])."""
     _dev_tensor(x, "x", torch.bfloat16)
     if x.dim() != 2:
         raise ValueError("x must be 2-D")
@@ -453,7 +454,7 @@ def mx_quantize(x: torch.Tensor, fmt: int, q: torch.Tensor | None = None, scales
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((cols // 128, rows, 4), dtype=torch.uint8, device=x.device)
     for t, n, size in ((q, "q", rows * cols), (scales, "scales", rows * (cols // 32))):
         _dev_tensor(t, n, torch.uint8)
         if t.numel() != size:
@@ -464,8 +465,8 @@ def mx_quantize(x: torch.Tensor, fmt: int, q: torch.Tensor | None = None, scales
 
 def mx_gemm_fwd(xq, sx, wq, sw, x_fmt: int = E4M3, out=None) -> torch.Tensor:
     """Y[M, N] = bf16(sum_k dec(X) 2^ex dec(W) 2^ew) of block-scaled operands (from
-    mx_quantize): xq uint8 [M, K] with sx uint8 [M, K / 32], wq uint8 [N, K] (e4m3)
-    with sw uint8 [N, K / 32]."""
+    mx_quantize): xq uint8 [M, K] with sx uint8 [K / 128, M, 4], wq uint8 [N, K]
+    (e4m3) with sw uint8 [K / 128, N, 4]."""
     for t, n in ((xq, "xq"), (sx, "sx"), (wq, "wq"), (sw, "sw")):
         _dev_tensor(t, n, torch.uint8)
     if xq.dim() != 2 or wq.dim() != 2 or xq.shape[1] != wq.shape[1]:
@@ -473,7 +474,7 @@ def mx_gemm_fwd(xq, sx, wq, sw, x_fmt: int = E4M3, out=None) -> torch.Tensor:
     M, K = xq.shape
     N = wq.shape[0]
     if sx.numel() != M * (K // 32) or sw.numel() != N * (K // 32):
-        raise ValueError("sx must be [M, K / 32] and sw [N, K / 32]")
+        raise ValueError("sx must hold M * K / 32 and sw N * K / 32 scales")
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     _dev_tensor(out, "out", torch.bfloat16)

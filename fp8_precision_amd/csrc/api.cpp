@@ -471,9 +471,10 @@ fp8_status fp8_mx_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fm
     const int64_t n = rows * cols;
     const Range r[] = {{x, 2 * n}, {q, n}, {scales, n / 32}};
     if (any_overlap(r)) return fail(FP8_ERR_INVALID, "fp8_mx_quantize: overlapping buffers");
-    if (cols % 32) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_quantize: cols must be a multiple of 32");
+    if (cols % 128) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_quantize: cols must be a multiple of 128");
+    if (n / 32 >= ((int64_t)1 << 32)) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_quantize: more than 2^32 blocks");
     if (!aligned(x, 16) || !aligned(q, 16)) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_quantize: misaligned pointer");
-    hipError_t e = fp8k::launch_mx_quantize(x, n, (int)fmt, q, scales, stream);
+    hipError_t e = fp8k::launch_mx_quantize(x, rows, cols, (int)fmt, q, scales, stream);
     if (e != hipSuccess) return fail_hip("fp8_mx_quantize", e);
     return FP8_OK;
 }

@@ -46,14 +46,16 @@ hipError_t launch_absmax_many(int count, const void* const* x, const int64_t* n,
                               hipStream_t stream);
 
 // Block-scaled GEMM out[P, Q] = bf16(sum_r dec(A) 2^ea dec(B) 2^eb) of K-major
-// operands A [P, R], B [Q, R] (B in E4M3) with E8M0 scales [P][R / 32], [Q][R / 32];
-// P, Q >= 256.
+// operands A [P, R], B [Q, R] (B in E4M3) with E8M0 scales stored step-major,
+// [R / 128][P][4] and [R / 128][Q][4]; P, Q >= 256.
 hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* sa, int fmt_a, const uint8_t* B, const uint8_t* sb,
                           int fmt_b, void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream);
 
-// Block (MX) quantisation of n bf16 elements (n a multiple of 32): codes q[n] and
-// one E8M0 scale per 32 consecutive elements, scales[n / 32].
-hipError_t launch_mx_quantize(const void* x, int64_t n, int fmt, uint8_t* q, uint8_t* scales, hipStream_t stream);
+// Block (MX) quantisation of a bf16 [rows, cols] tensor (cols a multiple of 128):
+// codes q[rows, cols] and one E8M0 scale per 32 consecutive elements of a row,
+// stored step-major: the scale of block b of row i at ((b / 4) rows + i) 4 + b % 4.
+hipError_t launch_mx_quantize(const void* x, int64_t rows, int64_t cols, int fmt, uint8_t* q, uint8_t* scales,
+                              hipStream_t stream);
 
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, const float* absmax,
                            uint8_t* q, uint8_t* qt, float* scale, float* inv_scale,

@@ -473,79 +473,123 @@ hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, c
 // the elements are x * 2^-e (exact) encoded like every other value (nearest
 // even, saturating).  A block holding a NaN or an infinity gets the NaN scale
 // (255) and the unscaled encodings.  One pass, no statistic launch before it:
-// reads 2 B and writes 1 + 1/32 B per element.
+// reads 2 B and writes 1 + 1/32 B per element.  The scales are stored
+// step-major, [cols / 128][rows][4] (the four blocks of a 128-element
+// reduction step of every row together), the layout the block-scaled GEMM
+// loads contiguously.
 //
-// Lane l converts the 16-byte vector v (8 elements); the 4 lanes of a block are
-// 4 consecutive lanes (v % 4 == l % 4: the grid stride is a multiple of 4), so
-// the block's maximum takes two shuffles.  Each lane keeps one 16-byte load in
-// flight: four 256-lane blocks per CU are 4 MiB over the chip, the best figure of
-// the streaming-copy probe.  NT: non-temporal loads (large inputs).
-template <int FMT, bool NT>
-__global__ void __launch_bounds__(256) mx_quantize_kernel(const u32x4* __restrict__ x, int64_t nvec,
-                                                          uint2* __restrict__ q, uint8_t* __restrict__ scales)
+// Lane l converts the 16-byte vectors v (8 elements each); the 4 lanes of a
+// block are 4 consecutive lanes (v % 4 == l % 4: the grid stride is a multiple
+// of 4, and the element count one of 32), so the block's maximum takes two
+// shuffles, and the 4 lanes leave every loop together.  NT: non-temporal loads
+// (large inputs).
+// Saturate and encode four fp32 values (finite or infinite; a NaN reaches the
+// converter as a bound and its code is replaced by the caller).
+template <int FMT>
+__device__ __forceinline__ uint32_t mx_enc4(float a, float b, float c, float d)
+{
+    constexpr float mx = Fmt<FMT>::max;
+    a = __builtin_amdgcn_fmed3f(a, -mx, mx);
+    b = __builtin_amdgcn_fmed3f(b, -mx, mx);
+    c = __builtin_amdgcn_fmed3f(c, -mx, mx);
+    d = __builtin_amdgcn_fmed3f(d, -mx, mx);
+    if (FMT == 0) {
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+    }
+    const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, d, lo, true);
+}
+
+// Max over the 4 lanes of a block (lanes 4 j .. 4 j + 3) through DPP quad permutes.
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v)
+{
+    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // lanes 1 0 3 2
+    v = v > o ? v : o;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);            // lanes 2 3 0 1
+    return v > o ? v : o;
+}
+
+// One 16-byte vector of 8 elements: its share of the block maximum is combined
+// over the block's 4 lanes, then the codes are written.  The maximum is taken
+// over all magnitude bit patterns: it reaches 0x7F80 exactly when the block
+// holds an infinity or a NaN, and is the largest finite magnitude otherwise.
+template <int FMT>
+__device__ __forceinline__ void mx_vector(const u32x4 w, int64_t v, uint2* __restrict__ q, uint8_t* __restrict__ scales,
+                                          uint32_t rows, uint32_t nb)
 {
     constexpr int emax = FMT == 0 ? 8 : 15;
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += stride) {
-        const u32x4 w = NT ? __builtin_nontemporal_load(x + v) : x[v];
-        // the largest finite magnitude (bf16 bits) and whether a NaN or an infinity occurs
-        uint32_t m = 0, bad = 0;
+    us2 m2 = {0, 0};
+    m2 = absmax_acc(m2, make_uint4(w.x, w.y, w.z, w.w));
+    const uint32_t m = quad_max_u32(m2.x > m2.y ? m2.x : m2.y);
+    const bool bad = m >= 0x7F80u;
+    float s = 1.0f;                       // a block with a NaN or an infinity: unscaled
+    uint32_t sbyte = 255;
+    if (!bad) {
+        // floor(log2 m): the exponent field of a normal bf16; m * 2^-133 for a subnormal one
+        const int fl = m >= 0x80u ? (int)(m >> 7) - 127 : 31 - __builtin_clz(m | 1u) - 133;
+        int e = m ? fl - emax : -127;
+        e = e < -127 ? -127 : e;          // at most 127 - emax: no upper clamp is reached
+        s = __uint_as_float((uint32_t)(127 - e) << 23);           // 2^-e, a normal fp32
+        sbyte = (uint32_t)(e + 127);
+    }
+    uint2 c;
+    c.x = mx_enc4<FMT>(bf16_lo(w.x) * s, bf16_hi(w.x) * s, bf16_lo(w.y) * s, bf16_hi(w.y) * s);
+    c.y = mx_enc4<FMT>(bf16_lo(w.z) * s, bf16_hi(w.z) * s, bf16_lo(w.w) * s, bf16_hi(w.w) * s);
+    if (bad) {
+        // a NaN element takes the NaN code with its sign (S.1111111)
         const uint32_t hw[8] = {w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16,
                                 w.z & 0xFFFFu, w.z >> 16, w.w & 0xFFFFu, w.w >> 16};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint32_t a = hw[i] & 0x7FFFu;
-            bad |= a >= 0x7F80u;
-            m = (a < 0x7F80u && a > m) ? a : m;
-        }
-#pragma unroll
-        for (int off = 1; off <= 2; off <<= 1) {
-            const uint32_t om = (uint32_t)__shfl_xor((int)m, off, 64);
-            bad |= (uint32_t)__shfl_xor((int)bad, off, 64);
-            m = om > m ? om : m;
-        }
-        float s = 1.0f;                   // a block with a NaN or an infinity: unscaled
-        uint32_t sbyte = 255;
-        if (!bad) {
-            // floor(log2 m): the exponent field of a normal bf16; m * 2^-133 for a subnormal one
-            const int fl = m >= 0x80u ? (int)(m >> 7) - 127 : 31 - __builtin_clz(m | 1u) - 133;
-            int e = m ? fl - emax : -127;
-            e = e < -127 ? -127 : e;      // at most 127 - emax: no upper clamp is reached
-            s = __uint_as_float((uint32_t)(127 - e) << 23);       // 2^-e, a normal fp32
-            sbyte = (uint32_t)(e + 127);
-        }
-        uint2 c = quant8<FMT>(make_uint4(w.x, w.y, w.z, w.w), s);
-        if (bad) {
-            // a NaN element takes the NaN code with its sign (S.1111111), whatever
-            // the converter makes of an unscaled NaN payload
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if ((hw[i] & 0x7FFFu) > 0x7F80u) {
-                    const uint32_t code = ((hw[i] >> 8) & 0x80u) | 0x7Fu, sh = (uint32_t)(i & 3) * 8;
-                    if (i < 4) c.x = (c.x & ~(0xFFu << sh)) | (code << sh);
-                    else c.y = (c.y & ~(0xFFu << sh)) | (code << sh);
-                }
+            if ((hw[i] & 0x7FFFu) > 0x7F80u) {
+                const uint32_t code = ((hw[i] >> 8) & 0x80u) | 0x7Fu, sh = (uint32_t)(i & 3) * 8;
+                if (i < 4)
+                    c.x = (c.x & ~(0xFFu << sh)) | (code << sh);
+                else
+                    c.y = (c.y & ~(0xFFu << sh)) | (code << sh);
             }
         }
-        q[v] = c;
-        if ((threadIdx.x & 3) == 0) scales[v >> 2] = (uint8_t)sbyte;
+    }
+    q[v] = c;
+    if ((threadIdx.x & 3) == 0) {
+        // block f = i nb + b of row i: stored step-major at ((b / 4) rows + i) 4 + b % 4
+        const uint32_t f = (uint32_t)(v >> 2), i = f / nb, b = f - i * nb;
+        scales[((size_t)(b >> 2) * rows + i) * 4 + (b & 3)] = (uint8_t)sbyte;
     }
 }
 
-hipError_t launch_mx_quantize(const void* x, int64_t n, int fmt, uint8_t* q, uint8_t* scales, hipStream_t stream)
+// A plain grid-stride loop, one 16-byte load per lane and pass, eight 256-lane
+// blocks per CU (32 waves): measured on MI355X (cold, 7B-layer tensors of
+// 90-180 MB) 4.8-5.2 TB/s against 4.4-4.7 with 4 blocks per CU, 3.3-3.5 with 2,
+// and no better with two or four loads per lane issued ahead.
+template <int FMT, bool NT>
+__global__ void __launch_bounds__(256) mx_quantize_kernel(const u32x4* __restrict__ x, int64_t nvec,
+                                                          uint2* __restrict__ q, uint8_t* __restrict__ scales,
+                                                          uint32_t rows, uint32_t nb)
 {
-    const int64_t nvec = n / 8;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += stride)
+        mx_vector<FMT>(NT ? __builtin_nontemporal_load(x + v) : x[v], v, q, scales, rows, nb);
+}
+
+hipError_t launch_mx_quantize(const void* x, int64_t rows, int64_t cols, int fmt, uint8_t* q, uint8_t* scales,
+                              hipStream_t stream)
+{
+    const int64_t n = rows * cols, nvec = n / 8;
     int64_t blocks = (nvec + 255) / 256;
-    const int64_t cap = (int64_t)device_cu_count() * 4;
+    const int64_t cap = (int64_t)device_cu_count() * 8;
     if (blocks > cap) blocks = cap;
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
     uint2* qv = reinterpret_cast<uint2*>(q);
+    const uint32_t r = (uint32_t)rows, nb = (uint32_t)(cols / 32);
     const bool nt = 2 * n >= kAbsStreamBytes;
+    const dim3 grid((unsigned)blocks), block(256);
     if (fmt == 0)
-        return nt ? launch(mx_quantize_kernel<0, true>, dim3((unsigned)blocks), dim3(256), stream, xv, nvec, qv, scales)
-                  : launch(mx_quantize_kernel<0, false>, dim3((unsigned)blocks), dim3(256), stream, xv, nvec, qv, scales);
-    return nt ? launch(mx_quantize_kernel<1, true>, dim3((unsigned)blocks), dim3(256), stream, xv, nvec, qv, scales)
-              : launch(mx_quantize_kernel<1, false>, dim3((unsigned)blocks), dim3(256), stream, xv, nvec, qv, scales);
+        return nt ? launch(mx_quantize_kernel<0, true>, grid, block, stream, xv, nvec, qv, scales, r, nb)
+                  : launch(mx_quantize_kernel<0, false>, grid, block, stream, xv, nvec, qv, scales, r, nb);
+    return nt ? launch(mx_quantize_kernel<1, true>, grid, block, stream, xv, nvec, qv, scales, r, nb)
+              : launch(mx_quantize_kernel<1, false>, grid, block, stream, xv, nvec, qv, scales, r, nb);
 }
 
 }  // namespace fp8k

@@ -363,8 +363,13 @@ fp8_status fp8_gemm_backward_mn(const uint8_t* dyq, fp8_fmt dy_fmt, const uint8_
  *   x       bf16 [rows, cols], 16-byte aligned
  *   fmt     FP8_E4M3 or FP8_E5M2
  *   q       u8 [rows, cols], 16-byte aligned
- *   scales  u8 [rows, cols / 32] (row-major: block b of row i at i * cols / 32 + b)
- * Constraints: cols % 32 == 0 (else FP8_ERR_UNSUPPORTED); buffers must not overlap.
+ *   scales  u8, rows * cols / 32 bytes, stored step-major as [cols / 128][rows][4]:
+ *           the scale of block b (elements 32 b .. 32 b + 31) of row i is at
+ *           ((b / 4) * rows + i) * 4 + b % 4, so the four scales of one
+ *           128-element reduction step of every row lie together, in the order
+ *           fp8_mx_gemm_fwd reads them
+ * Constraints: cols % 128 == 0 and rows * cols / 32 < 2^32 (else
+ * FP8_ERR_UNSUPPORTED); buffers must not overlap.
  */
 fp8_status fp8_mx_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt, uint8_t* q,
                            uint8_t* scales, hipStream_t stream);
@@ -376,9 +381,9 @@ fp8_status fp8_mx_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fm
  * of the 32-element block holding the code; a NaN scale gives NaN).  The
  * block scales are applied by the matrix instruction itself.
  *
- *   xq, sx   codes [M, K] (x_fmt: FP8_E4M3 or FP8_E5M2) and scales [M, K / 32]
+ *   xq, sx   codes [M, K] (x_fmt: FP8_E4M3 or FP8_E5M2) and scales [K / 128][M][4]
  *            from fp8_mx_quantize of X
- *   wq, sw   codes [N, K] (E4M3) and scales [N, K / 32] from fp8_mx_quantize of W
+ *   wq, sw   codes [N, K] (E4M3) and scales [K / 128][N][4] from fp8_mx_quantize of W
  *   y        bf16 [M, N]
  * Constraints: those of fp8_gemm_fwd, and M >= 256, N >= 256; scales 4-byte
  * aligned; y may not overlap any input.

@@ -351,16 +351,16 @@ def test_mx_quantize_validation(lib):
     f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_void_p]
     q, sc = B16, B16 + (1 << 20)
-    assert f(None, 4, 64, 0, q, sc, None) == INVALID
-    assert f(A16, 4, 64, 0, None, sc, None) == INVALID
-    assert f(A16, 4, 64, 0, q, None, None) == INVALID
-    assert f(A16, 4, 64, 2, q, sc, None) == INVALID                  # bad format
-    assert f(A16, 0, 64, 0, q, sc, None) == INVALID                  # empty
-    assert f(A16, 4, 64, 0, A16 + 64, sc, None) == INVALID           # q overlaps x
+    assert f(None, 4, 128, 0, q, sc, None) == INVALID
+    assert f(A16, 4, 128, 0, None, sc, None) == INVALID
+    assert f(A16, 4, 128, 0, q, None, None) == INVALID
+    assert f(A16, 4, 128, 2, q, sc, None) == INVALID                 # bad format
+    assert f(A16, 0, 128, 0, q, sc, None) == INVALID                 # empty
+    assert f(A16, 4, 128, 0, A16 + 64, sc, None) == INVALID          # q overlaps x
     assert b"overlap" in lib.fp8_last_error()
-    assert f(A16, 4, 48, 0, q, sc, None) == UNSUPPORTED              # cols not a multiple of 32
-    assert f(A16 + 2, 4, 64, 0, q, sc, None) == UNSUPPORTED          # misaligned input
-    assert f(A16, 4, 64, 0, q + 8, sc, None) == UNSUPPORTED          # misaligned codes
+    assert f(A16, 4, 96, 0, q, sc, None) == UNSUPPORTED              # cols not a multiple of 128
+    assert f(A16 + 2, 4, 128, 0, q, sc, None) == UNSUPPORTED         # misaligned input
+    assert f(A16, 4, 128, 0, q + 8, sc, None) == UNSUPPORTED         # misaligned codes
 
 
 def test_mx_gemm_validation(lib):

@@ -6,8 +6,8 @@ fp8_mx_quantize (bit-exact codes and E8M0 scales):
   block scales), both formats; NaN and infinity patterns make their block's
   scale NaN;
 * all-zero, tiny (clamped scale), saturating and mixed blocks;
-* random tensors over several grid-stride rounds, a ragged column count
-  (cols % 128 != 0), and the 7B-layer input and weight at full size.
+* random tensors over several grid-stride rounds and the 7B-layer input and
+  weight at full size; scales compared in the library's step-major layout.
 
 fp8_mx_gemm_fwd (the oracle's MX GEMM on the GPU's own codes and scales;
 relative Frobenius error <= 5e-3 and the any-order fp32 summation bound):
@@ -41,11 +41,24 @@ def to_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+def step_major(sc):
+    """Row-major scales [rows, cols / 32] -> the library's step-major [cols / 128, rows, 4]."""
+    rows, nb = sc.shape
+    return np.ascontiguousarray(sc.reshape(rows, nb // 4, 4).transpose(1, 0, 2))
+
+
+def row_major(sc):
+    """The library's step-major scales [cols / 128, rows, 4] -> [rows, cols / 32]."""
+    ns, rows, _ = sc.shape
+    return np.ascontiguousarray(sc.transpose(1, 0, 2).reshape(rows, 4 * ns))
+
+
 def check_mx(fp8, orc, bits, fmt, what):
     say("mx_quantize", what, bits.shape, fmt)
     q, sc = fp8.mx_quantize(to_dev(bits), fmt)
     torch.cuda.synchronize()
     q_r, sc_r = orc.mx_quantize(np.ascontiguousarray(bits), fmt)
+    sc_r = step_major(sc_r)
     gq, gs = u8(q), u8(sc)
     bad = np.argwhere(gs != sc_r)
     assert bad.size == 0, (what, "scales", bad[:4].tolist(), gs[tuple(bad[0])], sc_r[tuple(bad[0])])
@@ -67,7 +80,8 @@ def test_every_bf16_pattern(fp8, orc, fmt, lift):
     # exponent field; kept finite and made at least the smallest normal)
     planted = np.minimum(np.maximum(top, 0x80) + (lift << 7), 0x7F7F)
     x = np.concatenate([planted[:, None], blocks], axis=1).astype(np.uint16)
-    check_mx(fp8, orc, x, fmt, f"every pattern, lift {lift}")
+    x = np.concatenate([x, np.zeros(((-len(x)) % 4, 32), np.uint16)])       # whole rows of 4 blocks
+    check_mx(fp8, orc, x.reshape(-1, 128), fmt, f"every pattern, lift {lift}")
 
 
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
@@ -81,10 +95,12 @@ def test_special_blocks(fp8, orc, fmt):
     for bad in (0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x7F81):
         r = np.full(32, 0x3FC0, np.uint16); r[17] = bad; rows.append(r)
     big = np.full(32, 0x7F7F, np.uint16); big[4] = 0xFF7F; rows.append(big)  # largest finite
-    check_mx(fp8, orc, np.stack(rows).reshape(len(rows), 32), fmt, "special blocks")
+    while len(rows) % 4:
+        rows.append(np.full(32, 0x3F80, np.uint16))
+    check_mx(fp8, orc, np.stack(rows).reshape(len(rows) // 4, 128), fmt, "special blocks")
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 32), (3, 96), (17, 4128), (1024, 1024), (777, 2080)])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (3, 384), (17, 4224), (1024, 1024), (777, 2176)])
 def test_random_shapes(fp8, orc, rows, cols):
     x = workloads.draw(31, rows + cols, (rows, cols), 2.0)
     bits = workloads.bf16_bits(x)
@@ -122,8 +138,8 @@ def test_unit_scales_equal_per_tensor_gemm(fp8):
     g = torch.Generator(device="cuda").manual_seed(5)
     a = torch.randn((4096, 1024), generator=g, device="cuda").mul_(60).to(torch.float8_e4m3fn).view(torch.uint8)
     b = torch.randn((4352, 1024), generator=g, device="cuda").mul_(60).to(torch.float8_e4m3fn).view(torch.uint8)
-    sa = torch.full((4096, 32), 127, dtype=torch.uint8, device="cuda")
-    sb = torch.full((4352, 32), 127, dtype=torch.uint8, device="cuda")
+    sa = torch.full((8, 4096, 4), 127, dtype=torch.uint8, device="cuda")
+    sb = torch.full((8, 4352, 4), 127, dtype=torch.uint8, device="cuda")
     one = torch.ones(1, dtype=torch.float32, device="cuda")
     y = u16(fp8.mx_gemm_fwd(a, sa, b, sb))
     ref = u16(fp8.gemm_fwd(a, b, one, one))
@@ -144,7 +160,7 @@ def test_every_output_two_rounds(fp8, orc, fx):
     w = torch.from_numpy(ws.astype(np.float32)).to(torch.bfloat16)
     xq, sx, wq, sw = mx_operands(fp8, x, w, fx)
     y = u16(fp8.mx_gemm_fwd(xq, sx, wq, sw, fx))
-    a, sa, b, sb = u8(xq), u8(sx), u8(wq), u8(sw)
+    a, sa, b, sb = u8(xq), row_major(u8(sx)), u8(wq), row_major(u8(sw))
     ref = orc.mx_gemm(a, sa, fx, b, sb, E4M3)
     gemm_compare(y, ref, "mx every output")
     rows = np.arange(M, dtype=np.int64)
@@ -160,7 +176,7 @@ def test_qkv_forward_full_size(fp8, orc, cfg_name):
     say("mx_gemm qkv full size", cfg_name, tuple(x.shape), tuple(w.shape))
     xq, sx, wq, sw = mx_operands(fp8, x, w)
     y = u16(fp8.mx_gemm_fwd(xq, sx, wq, sw))
-    a, sa, b, sb = u8(xq), u8(sx), u8(wq), u8(sw)
+    a, sa, b, sb = u8(xq), row_major(u8(sx)), u8(wq), row_major(u8(sw))
     rng = np.random.default_rng(3)
     M = a.shape[0]
     rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], rng.integers(0, M, 252)])).astype(np.int64)
@@ -175,10 +191,10 @@ def test_nan_scale(fp8):
     g = torch.Generator(device="cuda").manual_seed(8)
     a = torch.randn((M, K), generator=g, device="cuda").mul_(30).to(torch.float8_e4m3fn).view(torch.uint8)
     b = torch.randn((N, K), generator=g, device="cuda").mul_(30).to(torch.float8_e4m3fn).view(torch.uint8)
-    sa = torch.full((M, K // 32), 120, dtype=torch.uint8, device="cuda")
-    sb = torch.full((N, K // 32), 125, dtype=torch.uint8, device="cuda")
-    sa[300, 5] = 255
-    sb[700, 0] = 255
+    sa = torch.full((K // 128, M, 4), 120, dtype=torch.uint8, device="cuda")
+    sb = torch.full((K // 128, N, 4), 125, dtype=torch.uint8, device="cuda")
+    sa[5 // 4, 300, 5 % 4] = 255           # block 5 of row 300
+    sb[0, 700, 0] = 255                     # block 0 of row 700
     y = bf16_to_f64(u16(fp8.mx_gemm_fwd(a, sa, b, sb)))
     want = np.zeros((M, N), bool)
     want[300, :] = True
