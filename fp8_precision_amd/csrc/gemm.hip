@@ -782,8 +782,13 @@ __device__ __forceinline__ void start_tile_mx(Sources& src, const GemmGroup& g, 
     set_sources<kKMajor, kKMajor>(src, w, wave, lane);
     src.sa = g.sa;
     src.sb = g.sb;
-    src.sa_off = (uint32_t)(w.m0 + wave * 64 + lane) * 4u;   // one row's 4 scales of a step
-    src.sb_off = (uint32_t)(w.n0 + wave * 64 + lane) * 4u;
+    // the lane number recomputed here (volatile, so it is not hoisted): held live
+    // across the persistent loop, the allocator spilled it, and the reload's wait
+    // here was a wait for the whole first stage just issued
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    src.sa_off = (uint32_t)(w.m0 + wave * 64 + ln) * 4u;     // one row's 4 scales of a step
+    src.sb_off = (uint32_t)(w.n0 + wave * 64 + ln) * 4u;
     src.sa_step = (uint32_t)w.P * 4u;
     src.sb_step = (uint32_t)w.Q * 4u;
     issue_stage_mx(src, lds_addr, sc_addr, 0, wave);
