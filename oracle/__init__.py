@@ -13,5 +13,5 @@ from .oracle import (  # noqa: F401
     E4M3, E5M2, FP8_MAX, build, lib_path, num_threads,
     bf16_to_f32, f32_to_bf16, encode, decode, absmax_bf16, absmax_f32, scale,
     quantize, exp_neg, swiglu_h, swiglu_requant, gemm, swiglu_grad, swiglu_grad_one, swiglu_backward,
-    MX_BLOCK, mx_quantize, mx_gemm,
+    MX_BLOCK, mx_quantize, mx_gemm, mx_quantize_f32, mx_swiglu,
 )

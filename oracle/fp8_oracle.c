@@ -365,6 +365,37 @@ void oracle_gemm(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
 #define MX_BLOCK 32
 
 /*
+ * One block of MX_BLOCK fp32 values: its scale byte and codes (the reading in
+ * the header).  The maximum is taken over the finite magnitudes; a NaN or an
+ * infinity makes the block's scale NaN (255) and its codes the unscaled encodings.
+ */
+static void mx_block(const float* v, int fmt, uint8_t* q, uint8_t* scale)
+{
+    const int emax = fmt == FMT_E4M3 ? 8 : 15;
+    float m = 0.0f;
+    int nonfinite = 0;
+    for (int k = 0; k < MX_BLOCK; ++k) {
+        if (!isfinite(v[k])) nonfinite = 1;
+        else if (fabsf(v[k]) > m) m = fabsf(v[k]);
+    }
+    if (nonfinite) {
+        *scale = 255;
+        for (int k = 0; k < MX_BLOCK; ++k) q[k] = oracle_encode(v[k], fmt);
+        return;
+    }
+    int e = -127;
+    if (m > 0.0f) {
+        int k2;
+        frexpf(m, &k2);                         /* m = r * 2^k2, r in [0.5, 1): floor(log2 m) = k2 - 1 */
+        e = (k2 - 1) - emax;
+        if (e < -127) e = -127;
+        if (e > 127) e = 127;
+    }
+    *scale = (uint8_t)(e + 127);
+    for (int k = 0; k < MX_BLOCK; ++k) q[k] = oracle_encode(ldexpf(v[k], -e), fmt);
+}
+
+/*
  * MX quantisation of a row-major bf16 [rows, cols] tensor (cols a multiple of
  * 32): q[i, j] = encode(x[i, j] / 2^e), scales[i, j / 32] = e + 127 for the
  * block's e (255 for a block with a NaN or an infinity, whose codes are the
@@ -372,36 +403,46 @@ void oracle_gemm(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
  */
 void oracle_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* q, uint8_t* scales)
 {
-    const int emax = fmt == FMT_E4M3 ? 8 : 15;
     const int64_t nb = cols / MX_BLOCK;
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < rows; ++i) {
+        float v[MX_BLOCK];
         for (int64_t b = 0; b < nb; ++b) {
-            const uint16_t* xb = x + i * cols + b * MX_BLOCK;
-            uint8_t* qb = q + i * cols + b * MX_BLOCK;
-            float m = 0.0f;
-            int nonfinite = 0;
+            for (int k = 0; k < MX_BLOCK; ++k) v[k] = oracle_bf16_to_f32(x[i * cols + b * MX_BLOCK + k]);
+            mx_block(v, fmt, q + i * cols + b * MX_BLOCK, scales + i * nb + b);
+        }
+    }
+}
+
+/*
+ * MX quantisation of an fp32 [rows, cols] tensor (the same blocks and rule).
+ */
+void oracle_mx_quantize_f32(const float* x, int64_t rows, int64_t cols, int fmt, uint8_t* q, uint8_t* scales)
+{
+    const int64_t nb = cols / MX_BLOCK;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t b = 0; b < nb; ++b)
+            mx_block(x + i * cols + b * MX_BLOCK, fmt, q + i * cols + b * MX_BLOCK, scales + i * nb + b);
+}
+
+/*
+ * The SwiGLU output h [M, F] of gu = [gate | up] (oracle_swiglu_one, one fp32
+ * value per element, never rounded to bf16), quantised in MX blocks along F
+ * (E4M3: h is an activation).  F a multiple of 32.
+ */
+void oracle_mx_swiglu(const uint16_t* gu, int64_t M, int64_t F, uint8_t* hq, uint8_t* scales)
+{
+    const int64_t nb = F / MX_BLOCK;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        float v[MX_BLOCK];
+        for (int64_t b = 0; b < nb; ++b) {
             for (int k = 0; k < MX_BLOCK; ++k) {
-                float v = oracle_bf16_to_f32(xb[k]);
-                if (!isfinite(v)) nonfinite = 1;
-                else if (fabsf(v) > m) m = fabsf(v);
+                const int64_t j = b * MX_BLOCK + k;
+                v[k] = oracle_swiglu_one(oracle_bf16_to_f32(gu[i * 2 * F + j]), oracle_bf16_to_f32(gu[i * 2 * F + F + j]));
             }
-            if (nonfinite) {
-                scales[i * nb + b] = 255;
-                for (int k = 0; k < MX_BLOCK; ++k) qb[k] = oracle_encode(oracle_bf16_to_f32(xb[k]), fmt);
-                continue;
-            }
-            int e = -127;
-            if (m > 0.0f) {
-                int k2;
-                frexpf(m, &k2);                     /* m = r * 2^k2, r in [0.5, 1): floor(log2 m) = k2 - 1 */
-                e = (k2 - 1) - emax;
-                if (e < -127) e = -127;
-                if (e > 127) e = 127;
-            }
-            scales[i * nb + b] = (uint8_t)(e + 127);
-            for (int k = 0; k < MX_BLOCK; ++k)
-                qb[k] = oracle_encode(ldexpf(oracle_bf16_to_f32(xb[k]), -e), fmt);
+            mx_block(v, FMT_E4M3, hq + i * F + b * MX_BLOCK, scales + i * nb + b);
         }
     }
 }

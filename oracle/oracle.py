@@ -68,6 +68,8 @@ def _load():
             "oracle_swiglu_backward": (None, [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, vp]),
             "oracle_mx_quantize": (None, [vp, i64, i64, i32, vp, vp]),
             "oracle_mx_gemm": (None, [vp, vp, i32, vp, vp, i32, i64, i64, i64, vp, i64, vp]),
+            "oracle_mx_quantize_f32": (None, [vp, i64, i64, i32, vp, vp]),
+            "oracle_mx_swiglu": (None, [vp, i64, i64, vp, vp]),
             "oracle_encode_vec": (None, [vp, i64, i32, vp]),
             "oracle_decode_vec": (None, [vp, i64, i32, vp]),
             "oracle_exp_neg_vec": (None, [vp, i64, vp]),
@@ -321,3 +323,29 @@ def mx_gemm(a: np.ndarray, sa: np.ndarray, fmt_a: int, b: np.ndarray, sb: np.nda
     _load().oracle_mx_gemm(_ptr(a), _ptr(sa), _fmt(fmt_a), _ptr(b), _ptr(sb), _fmt(fmt_b), M, N, K,
                            _ptr(r_arr), nrows, _ptr(y))
     return y
+
+
+def mx_quantize_f32(x: np.ndarray, fmt: int):
+    """Block (MX) quantisation of an fp32 [rows, cols] tensor (cols a multiple of 32),
+    the rule of mx_quantize: returns (codes [rows, cols], scales [rows, cols / 32])."""
+    _need(x, np.float32, "x")
+    if x.ndim != 2 or x.shape[1] % MX_BLOCK:
+        raise ValueError("x must be 2-D with a multiple of 32 columns")
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    sc = np.empty((rows, cols // MX_BLOCK), np.uint8)
+    _load().oracle_mx_quantize_f32(_ptr(x), rows, cols, _fmt(fmt), _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def mx_swiglu(gu: np.ndarray):
+    """The SwiGLU output of gu = [gate | up] (bf16 bits [M, 2F], F a multiple of 32),
+    MX-quantised (E4M3) along F: returns (hq [M, F], scales [M, F / 32])."""
+    _need(gu, np.uint16, "gu")
+    if gu.ndim != 2 or gu.shape[1] % (2 * MX_BLOCK):
+        raise ValueError("gu must be [M, 2F] with F a multiple of 32")
+    M, F = gu.shape[0], gu.shape[1] // 2
+    hq = np.empty((M, F), np.uint8)
+    sc = np.empty((M, F // MX_BLOCK), np.uint8)
+    _load().oracle_mx_swiglu(_ptr(gu), M, F, _ptr(hq), _ptr(sc))
+    return hq, sc

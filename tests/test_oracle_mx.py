@@ -208,3 +208,53 @@ def test_gemm_nan_scale(orc):
     want[2, :] = True
     want[:, 5] = True
     assert np.array_equal(nan, want)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_f32_blocks_equal_bf16_blocks_on_bf16_values(orc, fmt):
+    """The fp32 form of the rule gives the bf16 form's codes and scales on bf16 values."""
+    rng = np.random.default_rng(21 + fmt)
+    x = (rng.standard_normal((16, 256)) * np.exp2(rng.integers(-30, 30, (16, 1)))).astype(np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    q1, s1 = orc.mx_quantize(xb, fmt)
+    q2, s2 = orc.mx_quantize_f32(bits_f32(xb).astype(np.float32), fmt)
+    assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_f32_blocks_brute_force(orc, fmt):
+    """fp32 values with full 24-bit significands, maxima just below powers of two
+    (2^k (1 - 2^-24): e = k - 1 - emax) and fp32 subnormal maxima (clamped scale)."""
+    rng = np.random.default_rng(33 + fmt)
+    vals = tdecode(np.arange(256, dtype=np.uint8), fmt).astype(np.float64)
+    x = (rng.standard_normal((6, 64)) * np.exp2(rng.integers(-20, 20, (6, 1)))).astype(np.float32)
+    x[0, 3] = np.float32(2.0 ** 5 * (1 - 2.0 ** -24))
+    x[1, :32] = np.float32(2.0 ** -140) * np.arange(1, 33, dtype=np.float32)
+    q, s = orc.mx_quantize_f32(x, fmt)
+    for i in range(6):
+        for b in range(2):
+            blk = x[i, b * 32:(b + 1) * 32].astype(np.float64)
+            m = np.max(np.abs(blk))
+            e = -127 if m == 0 else max(-127, min(127, math.frexp(m)[1] - 1 - EMAX[fmt]))
+            assert int(s[i, b]) == e + 127, (i, b)
+            for k in range(32):
+                scaled = float(np.float32(blk[k] * 2.0 ** -e))       # RN32 of the exact quotient
+                assert q[i, b * 32 + k] == brute_force_code(scaled, fmt, vals), (i, b, k)
+    assert int(s[0, 0]) == 4 - EMAX[fmt] + 127
+
+
+def test_mx_swiglu_is_mx_of_swiglu_h(orc):
+    """The MX SwiGLU requant is the (pinned) SwiGLU output h put through the (pinned)
+    fp32 block rule, for drawn and for hand-picked gate/up values."""
+    rng = np.random.default_rng(41)
+    M, F = 8, 128
+    g = (rng.standard_normal((M, F)) * 3).astype(np.float32)
+    u = (rng.standard_normal((M, F)) * np.exp2(rng.integers(-8, 8, (M, 1)))).astype(np.float32)
+    g[0, :4] = [0.0, -np.inf, 200.0, -200.0]
+    u[1, 5] = np.inf
+    gu = np.concatenate([(g.view(np.uint32) >> 16), (u.view(np.uint32) >> 16)], axis=1).astype(np.uint16)
+    hq, sc = orc.mx_swiglu(gu)
+    h = orc.swiglu_h(gu)
+    q2, s2 = orc.mx_quantize_f32(np.ascontiguousarray(h, dtype=np.float32), E4M3)
+    assert np.array_equal(hq, q2) and np.array_equal(sc, s2)
+    assert sc[0, 0] == 255 and sc[1, 0] == 255            # the -inf gate (NaN h) and the infinite up
