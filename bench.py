@@ -695,6 +695,30 @@ def mx_forward(fp8, dev, cfg_name="layer7b", reps=10):
         tot["mx_bytes"] += mx_bytes
         tot["pt_bytes"] += pt_bytes
         del x, w, xq, wq, mxq, mwq, sx, sw, y
+    # the SwiGLU requantisation between the gate/up and down products: the per-tensor
+    # form (statistic pass + quantisation pass, hq only) against the MX form (one pass)
+    F = cfg.linears[3].K
+    gu = workloads.draw(cfg.seed, 99, (cfg.M, 2 * F), 1.0).to(dev)
+    am_h = torch.zeros(1, dtype=torch.float32, device=dev)
+    hq = torch.empty((cfg.M, F), dtype=torch.uint8, device=dev)
+    inv_h = torch.empty(1, dtype=torch.float32, device=dev)
+    mhq = torch.empty_like(hq)
+    msc = torch.empty((F // 128, cfg.M, 4), dtype=torch.uint8, device=dev)
+    sw_calls = {"pt": lambda: fp8.swiglu_requant(gu, am_h, 1, hq=hq, inv_scale_h=inv_h),
+                "mx": lambda: fp8.mx_swiglu_requant(gu, hq=mhq, scales=msc)}
+    sw_t = {k: [] for k in sw_calls}
+    for r in range(reps + 2):
+        for k, fn in sw_calls.items():
+            a, b = ev()
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                sw_t[k].append(a.elapsed_time(b) * 1e-3)
+    sw_pt, sw_mx = float(np.median(sw_t["pt"])), float(np.median(sw_t["mx"]))
+    n_h = cfg.M * F
+    del gu, hq, mhq, msc
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return {"workload": WORKLOADS[cfg_name] + ", forward of each linear",
@@ -705,6 +729,13 @@ def mx_forward(fp8, dev, cfg_name="layer7b", reps=10):
                    "gemm_tflops": round(tot["flop"] / tot["mx_g"] / 1e12, 1),
                    "gemm_frac": round(tot["flop"] / tot["mx_g"] / 1e12 / FP8_PEAK_TFLOPS, 4),
                    "quantise_gbs": round(tot["mx_bytes"] / tot["mx_q"] / 1e9, 1)},
+            "swiglu": {"M": cfg.M, "F": F,
+                       "per_tensor_us": round(sw_pt * 1e6, 1),
+                       "per_tensor_gbs": round((4 + 5) * n_h / sw_pt / 1e9, 1),
+                       "mx_us": round(sw_mx * 1e6, 1),
+                       "mx_gbs": round((4 + 1 + 1 / 32) * n_h / sw_mx / 1e9, 1),
+                       "note": "per tensor: the SwiGLU statistic pass, then the requantisation (hq only); MX: one "
+                               "pass, block maxima local"},
             "timing": f"{reps} interleaved rounds, an event pair around every call, medians; quantisation "
                       "without transposed copies on both paths",
             "linears": rows}

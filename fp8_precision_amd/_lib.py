@@ -45,6 +45,7 @@ _SIGS = {
     "fp8_stream_copy": (_i32, [_vp, _vp, _i64, _vp]),
     "fp8_mx_quantize": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "fp8_mx_gemm_fwd": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "fp8_mx_swiglu_requant": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -461,6 +462,27 @@ def mx_quantize(x: torch.Tensor, fmt: int, q: torch.Tensor | None = None, scales
             raise ValueError(f"{n} has the wrong size")
     _run("fp8_mx_quantize", _lib.fp8_mx_quantize, (x, q, scales), _ptr(x), rows, cols, int(fmt), _ptr(q), _ptr(scales))
     return q, scales
+
+
+def mx_swiglu_requant(gu: torch.Tensor, hq: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """The SwiGLU output of gu = [gate | up] (bf16 [M, 2F], F a multiple of 128),
+    block (MX) quantised to E4M3 along F: returns (hq uint8 [M, F], scales uint8
+    [F / 128, M, 4])."""
+    _dev_tensor(gu, "gu", torch.bfloat16)
+    if gu.dim() != 2 or gu.shape[1] % 2:
+        raise ValueError("gu must be [M, 2F]")
+    M, F = gu.shape[0], gu.shape[1] // 2
+    if hq is None:
+        hq = torch.empty((M, F), dtype=torch.uint8, device=gu.device)
+    if scales is None:
+        scales = torch.empty((F // 128, M, 4), dtype=torch.uint8, device=gu.device)
+    for t, n, size in ((hq, "hq", M * F), (scales, "scales", M * F // 32)):
+        _dev_tensor(t, n, torch.uint8)
+        if t.numel() != size:
+            raise ValueError(f"{n} has the wrong size")
+    _run("fp8_mx_swiglu_requant", _lib.fp8_mx_swiglu_requant, (gu, hq, scales), _ptr(gu), M, F, _ptr(hq),
+         _ptr(scales))
+    return hq, scales
 
 
 def mx_gemm_fwd(xq, sx, wq, sw, x_fmt: int = E4M3, out=None) -> torch.Tensor:

@@ -479,6 +479,21 @@ fp8_status fp8_mx_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fm
     return FP8_OK;
 }
 
+fp8_status fp8_mx_swiglu_requant(const void* gu, int64_t M, int64_t F, uint8_t* hq, uint8_t* scales,
+                                 hipStream_t stream)
+{
+    t_last_error.clear();
+    if (!gu || !hq || !scales) return fail(FP8_ERR_INVALID, "fp8_mx_swiglu_requant: null pointer");
+    if (M <= 0 || F <= 0 || !mul_ok(M, 2 * F, kMaxElems)) return fail(FP8_ERR_INVALID, "fp8_mx_swiglu_requant: bad shape");
+    const Range r[] = {{gu, 4 * M * F}, {hq, M * F}, {scales, M * F / 32}};
+    if (any_overlap(r)) return fail(FP8_ERR_INVALID, "fp8_mx_swiglu_requant: overlapping buffers");
+    if (F % 128) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_swiglu_requant: F must be a multiple of 128");
+    if (!aligned(gu, 16) || !aligned(hq, 16)) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_swiglu_requant: misaligned pointer");
+    hipError_t e = fp8k::launch_mx_swiglu(gu, M, F, hq, scales, stream);
+    if (e != hipSuccess) return fail_hip("fp8_mx_swiglu_requant", e);
+    return FP8_OK;
+}
+
 fp8_status fp8_mx_gemm_fwd(const uint8_t* xq, const uint8_t* sx, fp8_fmt x_fmt, const uint8_t* wq, const uint8_t* sw,
                            void* y, int64_t M, int64_t N, int64_t K, hipStream_t stream)
 {

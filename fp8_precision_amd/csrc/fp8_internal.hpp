@@ -51,6 +51,11 @@ hipError_t launch_absmax_many(int count, const void* const* x, const int64_t* n,
 hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* sa, int fmt_a, const uint8_t* B, const uint8_t* sb,
                           int fmt_b, void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream);
 
+// The SwiGLU output of gu = [gate | up] ([M, 2F] bf16, F a multiple of 128),
+// block (MX) quantised along F: E4M3 codes hq[M, F], scales step-major
+// [F / 128][M][4].
+hipError_t launch_mx_swiglu(const void* gu, int64_t M, int64_t F, uint8_t* hq, uint8_t* scales, hipStream_t stream);
+
 // Block (MX) quantisation of a bf16 [rows, cols] tensor (cols a multiple of 128):
 // codes q[rows, cols] and one E8M0 scale per 32 consecutive elements of a row,
 // stored step-major: the scale of block b of row i at ((b / 4) rows + i) 4 + b % 4.

@@ -482,6 +482,95 @@ hipError_t launch_swiglu_requant(const void* gu, int64_t M, int64_t F, float* ab
 }
 
 // ---------------------------------------------------------------------------
+// Block (MX) requantisation of the SwiGLU output: h in blocks of 32 consecutive
+// features of a row, each with its own scale 2^e (e = floor(log2 max |h|) - 8,
+// clamped at -127; E4M3 codes of h * 2^-e; a block with a NaN or an infinite h
+// gets the NaN scale 255 and the unscaled encodings), following the OCP MX
+// specification v1.0 (section 6.3) -- the block-scaled alternative of the LLMQ
+// summary's section 2.  The block maximum is local to the block, so one pass
+// does it all: no statistic pass over [gate | up] comes first.  The walk of
+// swiglu_quant_kernel: lane l takes columns 8 l .. and 512 + 8 l .. of a
+// 1024-column item, so a block is 4 adjacent lanes (DPP quad maximum); scales
+// stored step-major ([F / 128][M][4]) like fp8_mx_quantize's.
+__device__ __forceinline__ uint32_t quad_max_sw(uint32_t v)
+{
+    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // lanes 1 0 3 2
+    v = v > o ? v : o;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);            // lanes 2 3 0 1
+    return v > o ? v : o;
+}
+
+__global__ void __launch_bounds__(256) mx_swiglu_kernel(const uint16_t* __restrict__ gu, int64_t M, int64_t F,
+                                                        uint8_t* __restrict__ hq, uint8_t* __restrict__ scales)
+{
+    __shared__ float tbl[kTable];
+    load_table_to_lds(tbl);
+    const RowItems it = row_items(M, F);
+    const int lane = threadIdx.x & 63;
+    for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < it.total; w += (int64_t)gridDim.x * 4) {
+        const int64_t i = w / it.chunks;
+        const int64_t jb = (w - i * it.chunks) * 1024 + lane * 8;
+        const uint16_t* grow = gu + i * 2 * F;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int64_t j = jb + half * 512;
+            if (j < F) {                  // F % 32 == 0: the 4 lanes of a block agree
+                const uint4 gw = *reinterpret_cast<const uint4*>(grow + j);
+                const uint4 uw = *reinterpret_cast<const uint4*>(grow + F + j);
+                float h[8];
+                swiglu8(tbl, gw, uw, h);
+                // the largest magnitude pattern reaches 0x7F800000 exactly when a NaN or
+                // an infinity occurs, and is the largest finite |h| otherwise
+                const uint32_t m = quad_max_sw(mag_max8(0u, h));
+                const bool bad = m >= 0x7F800000u;
+                float sc = 1.0f;
+                uint32_t sbyte = 255;
+                if (!bad) {
+                    // floor(log2 m): the exponent field of a normal fp32, the leading bit's
+                    // position - 149 for a subnormal one
+                    const int fl = m >= 0x00800000u ? (int)(m >> 23) - 127 : 31 - __builtin_clz(m | 1u) - 149;
+                    int e = m ? fl - 8 : -127;
+                    e = e < -127 ? -127 : e;                       // at most 119: no upper clamp
+                    sc = __uint_as_float((uint32_t)(127 - e) << 23); // 2^-e
+                    sbyte = (uint32_t)(e + 127);
+                }
+                uint2 c = quant8_h(h, sc);
+                if (bad) {
+                    // a NaN h takes the NaN code (S.1111111)
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        if (__builtin_isnan(h[k])) {
+                            const uint32_t code = ((__float_as_uint(h[k]) >> 24) & 0x80u) | 0x7Fu;
+                            const uint32_t sh = (uint32_t)(k & 3) * 8;
+                            if (k < 4)
+                                c.x = (c.x & ~(0xFFu << sh)) | (code << sh);
+                            else
+                                c.y = (c.y & ~(0xFFu << sh)) | (code << sh);
+                        }
+                    }
+                }
+                *reinterpret_cast<uint2*>(hq + i * F + j) = c;
+                if ((lane & 3) == 0) {
+                    const int64_t b = j / 32;                   // block b of row i, stored step-major
+                    scales[((b >> 2) * M + i) * 4 + (b & 3)] = (uint8_t)sbyte;
+                }
+            }
+        }
+    }
+}
+
+hipError_t launch_mx_swiglu(const void* gu, int64_t M, int64_t F, uint8_t* hq, uint8_t* scales, hipStream_t stream)
+{
+    const int64_t items = M * ((F + 1023) / 1024);
+    int64_t blocks = (items + 3) / 4;
+    const int64_t cap = (int64_t)device_cu_count() * 4;   // 34 KB LDS per block: 4 blocks per CU
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    return launch(mx_swiglu_kernel, dim3((unsigned)blocks), dim3(256), stream, reinterpret_cast<const uint16_t*>(gu),
+                  M, F, hq, scales);
+}
+
+// ---------------------------------------------------------------------------
 // SwiGLU backward fused with the quantisation of [dg | du].
 
 // dg, du for the 8 (gate, up, dh) triples of three 16-byte words.  ts / tds: the

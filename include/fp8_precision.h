@@ -375,6 +375,22 @@ fp8_status fp8_mx_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fm
                            uint8_t* scales, hipStream_t stream);
 
 /*
+ * fp8_mx_swiglu_requant: the SwiGLU output h = silu(g) * u of gu = [gate | up]
+ * (each element exactly as fp8_swiglu_requant evaluates it, never rounded to
+ * bf16), block-quantised to E4M3 along the feature axis by the rule of
+ * fp8_mx_quantize (the block maximum over the 32 fp32 values of h).  One pass:
+ * a block's maximum is local, so no statistic pass over [gate | up] comes first
+ * (LLMQ summary, section 3.1: the per-tensor form needs the retained statistic).
+ *
+ *   gu      bf16 [M, 2F], 16-byte aligned
+ *   hq      u8 [M, F] E4M3 codes, 16-byte aligned
+ *   scales  u8, M * F / 32 bytes, step-major [F / 128][M][4] as for fp8_mx_quantize
+ * Constraints: F % 128 == 0 (else FP8_ERR_UNSUPPORTED); buffers must not overlap.
+ */
+fp8_status fp8_mx_swiglu_requant(const void* gu, int64_t M, int64_t F, uint8_t* hq, uint8_t* scales,
+                                 hipStream_t stream);
+
+/*
  * fp8_mx_gemm_fwd: the forward product of block-scaled operands,
  *   Y[m, n] = bf16_RNE( RN32( sum_k dec(X[m, k]) 2^ex(m, k / 32) dec(W[n, k]) 2^ew(n, k / 32) ) )
  * with fp32 accumulation and no per-tensor factor (each 2^e is the E8M0 scale

@@ -379,3 +379,16 @@ def test_mx_gemm_validation(lib):
     assert bad(K=192) == UNSUPPORTED                                  # reduction not a multiple of 128
     assert bad(sx=SX + 2) == UNSUPPORTED                              # misaligned scales
     assert bad(x=X + 8) == UNSUPPORTED                                # misaligned codes
+
+
+def test_mx_swiglu_validation(lib):
+    f = lib.fp8_mx_swiglu_requant
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    hq, sc = B16, B16 + (1 << 20)
+    assert f(None, 4, 128, hq, sc, None) == INVALID
+    assert f(A16, 4, 128, None, sc, None) == INVALID
+    assert f(A16, 0, 128, hq, sc, None) == INVALID
+    assert f(A16, 4, 128, A16 + 256, sc, None) == INVALID            # hq over gu
+    assert f(A16, 4, 96, hq, sc, None) == UNSUPPORTED                # F not a multiple of 128
+    assert f(A16 + 2, 4, 128, hq, sc, None) == UNSUPPORTED           # misaligned gu

@@ -25,7 +25,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import E4M3, E5M2, bf16_to_f64, decode_abs64, gemm_compare, say, u16, u8
+from gpu_util import E4M3, E5M2, assert_codes_equal, bf16_to_f64, decode_abs64, gemm_compare, say, u16, u8
 
 pytestmark = pytest.mark.gpu
 
@@ -200,3 +200,30 @@ def test_nan_scale(fp8):
     want[300, :] = True
     want[:, 700] = True
     assert np.array_equal(np.isnan(y), want)
+
+
+def check_mx_swiglu(fp8, orc, gu_bits, what):
+    say("mx_swiglu_requant", what, gu_bits.shape)
+    hq, sc = fp8.mx_swiglu_requant(to_dev(gu_bits))
+    torch.cuda.synchronize()
+    hq_r, sc_r = orc.mx_swiglu(np.ascontiguousarray(gu_bits))
+    gs = u8(sc)
+    bad = np.argwhere(gs != step_major(sc_r))
+    assert bad.size == 0, (what, "scales", bad[:4].tolist())
+    # a NaN h's code is a NaN code whose sign is not fixed (IEEE leaves the sign of a NaN open)
+    assert_codes_equal(u8(hq), hq_r, E4M3, what)
+
+
+def test_mx_swiglu_every_gate_value(fp8, orc):
+    """All 65536 bf16 gate values (infinities and NaN included) against two up values,
+    128 features per row: blocks mixing tiny, large, NaN and infinite h."""
+    g = np.arange(65536, dtype=np.uint16).reshape(-1, 128)
+    for ubits in (0x3F80, 0xC2C8):                     # u = 1, u = -100
+        u = np.full(g.shape, ubits, np.uint16)
+        check_mx_swiglu(fp8, orc, np.concatenate([g, u], axis=1), f"every gate value, u {ubits:#x}")
+
+
+@pytest.mark.parametrize("M,F", [(1, 128), (7, 384), (33, 11008), (4096, 11008)])
+def test_mx_swiglu_shapes(fp8, orc, M, F):
+    x = workloads.draw(57, M + F, (M, 2 * F), 2.0)
+    check_mx_swiglu(fp8, orc, workloads.bf16_bits(x), f"{M}x{F}")
