@@ -46,6 +46,7 @@ _SIGS = {
     "fp8_mx_quantize": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "fp8_mx_gemm_fwd": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_mx_swiglu_requant": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "fp8_mx_quantize_t": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -462,6 +463,27 @@ def mx_quantize(x: torch.Tensor, fmt: int, q: torch.Tensor | None = None, scales
             raise ValueError(f"{n} has the wrong size")
     _run("fp8_mx_quantize", _lib.fp8_mx_quantize, (x, q, scales), _ptr(x), rows, cols, int(fmt), _ptr(q), _ptr(scales))
     return q, scales
+
+
+def mx_quantize_t(x: torch.Tensor, fmt: int, qt: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """Block (MX) quantisation of x^T for a 2-D bf16 x [rows, cols] (both multiples of
+    128): returns (qt uint8 [cols, rows], scales uint8 [rows / 128, cols, 4]) -- blocks
+    of 32 consecutive rows of x per column."""
+    _dev_tensor(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    if qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows // 128, cols, 4), dtype=torch.uint8, device=x.device)
+    for t, n, size in ((qt, "qt", rows * cols), (scales, "scales", rows * cols // 32)):
+        _dev_tensor(t, n, torch.uint8)
+        if t.numel() != size:
+            raise ValueError(f"{n} has the wrong size")
+    _run("fp8_mx_quantize_t", _lib.fp8_mx_quantize_t, (x, qt, scales), _ptr(x), rows, cols, int(fmt), _ptr(qt),
+         _ptr(scales))
+    return qt, scales
 
 
 def mx_swiglu_requant(gu: torch.Tensor, hq: torch.Tensor | None = None, scales: torch.Tensor | None = None):

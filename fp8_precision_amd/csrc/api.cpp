@@ -479,6 +479,24 @@ fp8_status fp8_mx_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fm
     return FP8_OK;
 }
 
+fp8_status fp8_mx_quantize_t(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt, uint8_t* qt, uint8_t* scales,
+                             hipStream_t stream)
+{
+    t_last_error.clear();
+    if (!x || !qt || !scales) return fail(FP8_ERR_INVALID, "fp8_mx_quantize_t: null pointer");
+    if (fmt != FP8_E4M3 && fmt != FP8_E5M2) return fail(FP8_ERR_INVALID, "fp8_mx_quantize_t: bad format");
+    if (!mul_ok(rows, cols, kMaxElems)) return fail(FP8_ERR_INVALID, "fp8_mx_quantize_t: bad shape");
+    const int64_t n = rows * cols;
+    const Range r[] = {{x, 2 * n}, {qt, n}, {scales, n / 32}};
+    if (any_overlap(r)) return fail(FP8_ERR_INVALID, "fp8_mx_quantize_t: overlapping buffers");
+    if (rows % 128 || cols % 128) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_quantize_t: rows and cols must be multiples of 128");
+    if (!aligned(x, 16) || !aligned(qt, 16) || !aligned(scales, 4))
+        return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_quantize_t: misaligned pointer");
+    hipError_t e = fp8k::launch_mx_quantize_t(x, rows, cols, (int)fmt, qt, scales, stream);
+    if (e != hipSuccess) return fail_hip("fp8_mx_quantize_t", e);
+    return FP8_OK;
+}
+
 fp8_status fp8_mx_swiglu_requant(const void* gu, int64_t M, int64_t F, uint8_t* hq, uint8_t* scales,
                                  hipStream_t stream)
 {

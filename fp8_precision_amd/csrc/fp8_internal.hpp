@@ -51,6 +51,12 @@ hipError_t launch_absmax_many(int count, const void* const* x, const int64_t* n,
 hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* sa, int fmt_a, const uint8_t* B, const uint8_t* sb,
                           int fmt_b, void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream);
 
+// Transposed block (MX) quantisation: qt [cols, rows] = the codes of x^T with
+// blocks of 32 along qt's rows (32 consecutive rows of a column of x), scales
+// step-major [rows / 128][cols][4]; rows and cols multiples of 128.
+hipError_t launch_mx_quantize_t(const void* x, int64_t rows, int64_t cols, int fmt, uint8_t* qt, uint8_t* scales,
+                                hipStream_t stream);
+
 // The SwiGLU output of gu = [gate | up] ([M, 2F] bf16, F a multiple of 128),
 // block (MX) quantised along F: E4M3 codes hq[M, F], scales step-major
 // [F / 128][M][4].

@@ -573,6 +573,104 @@ __global__ void __launch_bounds__(256) mx_quantize_kernel(const u32x4* __restric
         mx_vector<FMT>(NT ? __builtin_nontemporal_load(x + v) : x[v], v, q, scales, rows, nb);
 }
 
+// Transposed block (MX) quantisation: qt = the codes of x^T [cols, rows] with
+// blocks of 32 consecutive elements along qt's rows, i.e. 32 consecutive rows
+// of one column of x -- the operand layout of a backward product whose
+// reduction runs over x's rows (the blocks must lie along the reduction, so
+// this is a second quantisation of x, not a transpose of the first).  A wave
+// takes 64 rows x 128 columns: lane l reads columns 2 l, 2 l + 1 of each of the
+// 64 rows (every load instruction reads a 256-byte row segment), so each of its
+// two columns' two blocks lies in its own registers; it writes 64 contiguous
+// codes per column (qt row c, columns r0 .. r0 + 63) and the column's two scale
+// bytes.  Scales step-major for qt: block b of qt row c at ((b / 4) cols + c) 4
+// + b % 4.  rows % 128 == 0 and cols % 128 == 0.
+template <int FMT, bool NT>
+__global__ void __launch_bounds__(256) mx_quantize_t_kernel(const uint32_t* __restrict__ x, int64_t rows,
+                                                            int64_t cols, uint8_t* __restrict__ qt,
+                                                            uint8_t* __restrict__ scales)
+{
+    constexpr int emax = FMT == 0 ? 8 : 15;
+    const int lane = threadIdx.x & 63;
+    const int64_t ct = cols / 128, tiles = (rows / 64) * ct;
+    for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < tiles; t += (int64_t)gridDim.x * 4) {
+        const int64_t r0 = (t / ct) * 64, c = (t % ct) * 128 + 2 * lane;    // the lane's columns c, c + 1
+        uint32_t w[64];
+#pragma unroll
+        for (int r = 0; r < 64; ++r) {
+            const uint32_t* src = x + ((r0 + r) * cols + c) / 2;
+            w[r] = NT ? __builtin_nontemporal_load(src) : *src;
+        }
+#pragma unroll
+        for (int col = 0; col < 2; ++col) {
+            uint32_t codes[16];
+            uint32_t sbytes = 0;
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int r = 0; r < 32; ++r) {
+                    const uint32_t a = (col ? (w[blk * 32 + r] >> 16) : w[blk * 32 + r]) & 0x7FFFu;
+                    m = m > a ? m : a;
+                }
+                const bool bad = m >= 0x7F80u;     // an infinity or a NaN in the block
+                float s = 1.0f;
+                uint32_t sbyte = 255;
+                if (!bad) {
+                    const int fl = m >= 0x80u ? (int)(m >> 7) - 127 : 31 - __builtin_clz(m | 1u) - 133;
+                    int e = m ? fl - emax : -127;
+                    e = e < -127 ? -127 : e;
+                    s = __uint_as_float((uint32_t)(127 - e) << 23);
+                    sbyte = (uint32_t)(e + 127);
+                }
+                sbytes |= sbyte << (8 * blk);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    float v[4];
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) {
+                        const uint32_t wv = w[blk * 32 + 4 * k + e4];
+                        v[e4] = (col ? bf16_hi(wv) : bf16_lo(wv)) * s;
+                    }
+                    uint32_t cw = mx_enc4<FMT>(v[0], v[1], v[2], v[3]);
+                    if (bad) {
+#pragma unroll
+                        for (int e4 = 0; e4 < 4; ++e4) {
+                            const uint32_t hb = (col ? (w[blk * 32 + 4 * k + e4] >> 16) : w[blk * 32 + 4 * k + e4]) & 0xFFFFu;
+                            if ((hb & 0x7FFFu) > 0x7F80u)
+                                cw = (cw & ~(0xFFu << (8 * e4))) | ((((hb >> 8) & 0x80u) | 0x7Fu) << (8 * e4));
+                        }
+                    }
+                    codes[blk * 8 + k] = cw;
+                }
+            }
+            uint4* dst = reinterpret_cast<uint4*>(qt + (c + col) * rows + r0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                dst[k] = make_uint4(codes[4 * k], codes[4 * k + 1], codes[4 * k + 2], codes[4 * k + 3]);
+            // blocks r0 / 32 and r0 / 32 + 1 of qt row c + col (both in the same group of 4)
+            const int64_t b0 = r0 / 32;
+            *reinterpret_cast<uint16_t*>(scales + ((b0 >> 2) * cols + c + col) * 4 + (b0 & 3)) = (uint16_t)sbytes;
+        }
+    }
+}
+
+hipError_t launch_mx_quantize_t(const void* x, int64_t rows, int64_t cols, int fmt, uint8_t* qt, uint8_t* scales,
+                                hipStream_t stream)
+{
+    const int64_t tiles = (rows / 64) * (cols / 128);
+    int64_t blocks = (tiles + 3) / 4;
+    const int64_t cap = (int64_t)device_cu_count() * 4;
+    if (blocks > cap) blocks = cap;
+    const uint32_t* xv = reinterpret_cast<const uint32_t*>(x);
+    const bool nt = 2 * rows * cols >= kAbsStreamBytes;
+    const dim3 grid((unsigned)blocks), block(256);
+    if (fmt == 0)
+        return nt ? launch(mx_quantize_t_kernel<0, true>, grid, block, stream, xv, rows, cols, qt, scales)
+                  : launch(mx_quantize_t_kernel<0, false>, grid, block, stream, xv, rows, cols, qt, scales);
+    return nt ? launch(mx_quantize_t_kernel<1, true>, grid, block, stream, xv, rows, cols, qt, scales)
+              : launch(mx_quantize_t_kernel<1, false>, grid, block, stream, xv, rows, cols, qt, scales);
+}
+
 hipError_t launch_mx_quantize(const void* x, int64_t rows, int64_t cols, int fmt, uint8_t* q, uint8_t* scales,
                               hipStream_t stream)
 {

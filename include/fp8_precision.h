@@ -375,6 +375,26 @@ fp8_status fp8_mx_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fm
                            uint8_t* scales, hipStream_t stream);
 
 /*
+ * fp8_mx_quantize_t: the block (MX) quantisation of x^T, for a backward
+ * product whose reduction runs over x's rows (dgrad reads W^T with blocks
+ * along N, wgrad reads dY^T and X^T with blocks along M).  The blocks must lie
+ * along the reduction, so this is a second quantisation of x (its own scales),
+ * not a transpose of fp8_mx_quantize's codes:
+ *   qt[j, i] = encode_fmt(x[i, j] * 2^-e), blocks of 32 consecutive i for one j
+ *   scales: block b of qt row j at ((b / 4) * cols + j) * 4 + b % 4  ([rows / 128][cols][4])
+ * with the rule of fp8_mx_quantize for e, saturation and non-finite blocks.
+ *
+ *   x       bf16 [rows, cols], 16-byte aligned
+ *   fmt     FP8_E4M3 or FP8_E5M2
+ *   qt      u8 [cols, rows], 16-byte aligned
+ *   scales  u8, rows * cols / 32 bytes, 4-byte aligned
+ * Constraints: rows % 128 == 0 and cols % 128 == 0 (else FP8_ERR_UNSUPPORTED);
+ * buffers must not overlap.
+ */
+fp8_status fp8_mx_quantize_t(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt, uint8_t* qt,
+                             uint8_t* scales, hipStream_t stream);
+
+/*
  * fp8_mx_swiglu_requant: the SwiGLU output h = silu(g) * u of gu = [gate | up]
  * (each element exactly as fp8_swiglu_requant evaluates it, never rounded to
  * bf16), block-quantised to E4M3 along the feature axis by the rule of

@@ -392,3 +392,17 @@ def test_mx_swiglu_validation(lib):
     assert f(A16, 4, 128, A16 + 256, sc, None) == INVALID            # hq over gu
     assert f(A16, 4, 96, hq, sc, None) == UNSUPPORTED                # F not a multiple of 128
     assert f(A16 + 2, 4, 128, hq, sc, None) == UNSUPPORTED           # misaligned gu
+
+
+def test_mx_quantize_t_validation(lib):
+    f = lib.fp8_mx_quantize_t
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    qt, sc = B16, B16 + (1 << 20)
+    assert f(None, 128, 128, 0, qt, sc, None) == INVALID
+    assert f(A16, 128, 128, 5, qt, sc, None) == INVALID
+    assert f(A16, 128, 128, 0, A16 + 512, sc, None) == INVALID       # qt over x
+    assert f(A16, 64, 128, 0, qt, sc, None) == UNSUPPORTED           # rows not a multiple of 128
+    assert f(A16, 128, 144, 0, qt, sc, None) == UNSUPPORTED          # cols not a multiple of 128
+    assert f(A16, 128, 128, 0, qt, sc + 2, None) == UNSUPPORTED      # misaligned scales

@@ -227,3 +227,57 @@ def test_mx_swiglu_every_gate_value(fp8, orc):
 def test_mx_swiglu_shapes(fp8, orc, M, F):
     x = workloads.draw(57, M + F, (M, 2 * F), 2.0)
     check_mx_swiglu(fp8, orc, workloads.bf16_bits(x), f"{M}x{F}")
+
+
+def check_mx_t(fp8, orc, bits, fmt, what):
+    """The transposed MX quantisation against the oracle's MX quantisation of x^T."""
+    say("mx_quantize_t", what, bits.shape, fmt)
+    qt, sc = fp8.mx_quantize_t(to_dev(bits), fmt)
+    torch.cuda.synchronize()
+    q_r, sc_r = orc.mx_quantize(np.ascontiguousarray(bits.T), fmt)
+    bad = np.argwhere(u8(sc) != step_major(sc_r))
+    assert bad.size == 0, (what, "scales", bad[:4].tolist())
+    assert_codes_equal(u8(qt), q_r, fmt, what)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_mx_quantize_t_every_pattern(fp8, orc, fmt):
+    """Every bf16 pattern down the columns of a 512 x 128 tensor (blocks of 32 rows
+    mix all magnitudes, infinities and NaN), and planted column maxima."""
+    x = np.arange(65536, dtype=np.uint16).reshape(128, 512).T.copy()
+    check_mx_t(fp8, orc, x, fmt, "every pattern")
+    rng = np.random.default_rng(fmt)
+    y = workloads.bf16_bits(workloads.draw(61, fmt, (512, 256), 1.0)).copy()
+    y[rng.integers(0, 512, 64), rng.integers(0, 256, 64)] = 0x4F80     # 2^32: saturating maxima elsewhere
+    check_mx_t(fp8, orc, y, fmt, "planted maxima")
+
+
+@pytest.mark.parametrize("rows,cols", [(128, 128), (384, 1280), (4096, 4096)])
+def test_mx_quantize_t_shapes(fp8, orc, rows, cols):
+    x = workloads.bf16_bits(workloads.draw(67, rows, (rows, cols), 3.0))
+    check_mx_t(fp8, orc, x, E5M2, f"{rows}x{cols}")
+
+
+def test_mx_backward_products(fp8, orc):
+    """dgrad = dY . W and wgrad = dY^T . X on block-scaled operands (dY e5m2 blocked
+    along N for dgrad and along M for wgrad, W^T and X^T from fp8_mx_quantize_t),
+    against the oracle's MX GEMM on the same codes, every output."""
+    M, N, K = 512, 768, 640
+    dy = workloads.draw(71, 1, (M, N), 1e-3)
+    w = workloads.draw(71, 2, (N, K), 0.02)
+    x = workloads.draw(71, 3, (M, K), 1.0)
+    E5 = E5M2
+    dyq, sdy = fp8.mx_quantize(dy.cuda(), E5)
+    wt, swt = fp8.mx_quantize_t(w.cuda(), E4M3)
+    dx = u16(fp8.mx_gemm_fwd(dyq, sdy, wt, swt, E5))
+    a, sa, b, sb = u8(dyq), row_major(u8(sdy)), u8(wt), row_major(u8(swt))
+    ref = orc.mx_gemm(a, sa, E5, b, sb, E4M3)
+    gemm_compare(dx, ref, "mx dgrad")
+    mx_bound_check(dx, ref, a, sa, E5, b, sb, np.arange(M, dtype=np.int64), "mx dgrad")
+    dyt, sdyt = fp8.mx_quantize_t(dy.cuda(), E5)
+    xt, sxt = fp8.mx_quantize_t(x.cuda(), E4M3)
+    dw = u16(fp8.mx_gemm_fwd(dyt, sdyt, xt, sxt, E5))
+    a, sa, b, sb = u8(dyt), row_major(u8(sdyt)), u8(xt), row_major(u8(sxt))
+    ref = orc.mx_gemm(a, sa, E5, b, sb, E4M3)
+    gemm_compare(dw, ref, "mx wgrad")
+    mx_bound_check(dw, ref, a, sa, E5, b, sb, np.arange(N, dtype=np.int64), "mx wgrad")
