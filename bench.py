@@ -625,41 +625,61 @@ def step_shapes(fp8, dev, stream, cfg_name, steps=5, warmup=5):
             "calls": rows}
 
 
-def mx_forward(fp8, dev, cfg_name="layer7b", reps=10):
-    """Block (MX) scaling next to the per-tensor path, for each linear's forward
-    (the measured alternative, not the headline): per-tensor = the statistics of
-    X and W in one launch, their quantisation (codes only) in one launch, the
-    FP8 GEMM; MX = fp8_mx_quantize of X, of W (one pass each, no statistic
-    launch), the block-scaled GEMM.  Inputs drawn by workloads.py (X of the down
-    linear drawn like the others); the two paths interleaved, `reps` rounds, an
-    event pair around every call, medians."""
+def mx_layer(fp8, dev, cfg_name="layer7b", reps=10):
+    """Block (MX) scaling next to the per-tensor path for each linear's forward and
+    backward (the measured alternative, not the headline).  Per tensor: the
+    statistics of X and W in one launch, their quantisation with the transposed
+    copies in one launch, the forward GEMM; the statistic and e5m2 quantisation
+    (with the transposed copy) of dY, the dgrad + wgrad launch.  MX: fp8_mx_quantize
+    of X and W, the block-scaled forward; fp8_mx_quantize_t of X and W (their blocks
+    along the backward reductions), fp8_mx_quantize and fp8_mx_quantize_t of dY
+    (e5m2), the block-scaled dgrad and wgrad.  Inputs drawn by workloads.py; the two
+    paths interleaved, `reps` rounds, an event pair around every call, medians."""
     cfg = workloads.CONFIGS[cfg_name]
-    E4M3 = fp8.E4M3
+    E4, E5 = fp8.E4M3, fp8.E5M2
     ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    u8 = lambda *sh: torch.empty(sh, dtype=torch.uint8, device=dev)
+    f32 = lambda: torch.empty(1, dtype=torch.float32, device=dev)
     rows = []
-    tot = {"pt_q": 0.0, "pt_g": 0.0, "mx_q": 0.0, "mx_g": 0.0, "flop": 0.0, "mx_bytes": 0.0, "pt_bytes": 0.0}
+    tot = {k: 0.0 for k in ("pt_qf", "pt_gf", "pt_qb", "pt_gb", "mx_qf", "mx_gf", "mx_qb", "mx_gb", "ff", "fb")}
     for li, L in enumerate(cfg.linears):
         x = workloads.draw_x(cfg, li).to(dev)
         w = workloads.draw_w(cfg, li).to(dev)
+        dy = workloads.draw_dy(cfg, li).to(dev)
         M, K, N = cfg.M, L.K, L.N
-        stats = torch.zeros(2, dtype=torch.float32, device=dev)
+        stats = torch.zeros(3, dtype=torch.float32, device=dev)
         am = [stats[0:1], stats[1:2]]
-        xq, wq = torch.empty((M, K), dtype=torch.uint8, device=dev), torch.empty((N, K), dtype=torch.uint8, device=dev)
-        sc = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(4)]
+        xq, wq, xqt, wqt = u8(M, K), u8(N, K), u8(K, M), u8(K, N)
+        dyq, dyqt = u8(M, N), u8(N, M)
+        sc = [f32() for _ in range(6)]
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        mxq, mwq = torch.empty_like(xq), torch.empty_like(wq)
-        sx = torch.empty((K // 128, M, 4), dtype=torch.uint8, device=dev)
-        sw = torch.empty((K // 128, N, 4), dtype=torch.uint8, device=dev)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        mxq, mwq, mxt, mwt, mdq, mdt = u8(M, K), u8(N, K), u8(K, M), u8(K, N), u8(M, N), u8(N, M)
+        sx, sw = u8(K // 128, M, 4), u8(K // 128, N, 4)
+        sxt, swt = u8(M // 128, K, 4), u8(N // 128, K, 4)
+        sdq, sdt = u8(N // 128, M, 4), u8(M // 128, N, 4)
         calls = {
             "pt_abs": lambda: fp8.absmax_accumulate_many([x, w], am),
-            "pt_quant": lambda: fp8.quantize_many([x, w], E4M3, am, want_q=True, want_qt=False, qs=[xq, wq],
-                                                  scales=[sc[0], sc[1]], inv_scales=[sc[2], sc[3]]),
-            "pt_gemm": lambda: fp8.gemm_fwd(xq, wq, sc[2], sc[3], y),
-            "mx_x": lambda: fp8.mx_quantize(x, E4M3, q=mxq, scales=sx),
-            "mx_w": lambda: fp8.mx_quantize(w, E4M3, q=mwq, scales=sw),
-            "mx_gemm": lambda: fp8.mx_gemm_fwd(mxq, sx, mwq, sw, E4M3, out=y),
+            "pt_quant": lambda: fp8.quantize_many([x, w], E4, am, want_q=True, want_qt=True, qs=[xq, wq],
+                                                  qts=[xqt, wqt], scales=[sc[0], sc[1]], inv_scales=[sc[2], sc[3]]),
+            "pt_fwd": lambda: fp8.gemm_fwd(xq, wq, sc[2], sc[3], y),
+            "pt_dyabs": lambda: fp8.absmax(dy, stats[2:3], accumulate=True),
+            "pt_dyquant": lambda: fp8.quantize(dy, E5, stats[2:3], want_q=True, want_qt=True, q=dyq, qt=dyqt,
+                                               scale=sc[4], inv_scale=sc[5]),
+            "pt_bwd": lambda: fp8.gemm_backward(dyq, dyqt, E5, wqt, xqt, sc[5], sc[3], sc[2], dx, dw),
+            "mx_x": lambda: fp8.mx_quantize(x, E4, q=mxq, scales=sx),
+            "mx_w": lambda: fp8.mx_quantize(w, E4, q=mwq, scales=sw),
+            "mx_fwd": lambda: fp8.mx_gemm_fwd(mxq, sx, mwq, sw, E4, out=y),
+            "mx_xt": lambda: fp8.mx_quantize_t(x, E4, qt=mxt, scales=sxt),
+            "mx_wt": lambda: fp8.mx_quantize_t(w, E4, qt=mwt, scales=swt),
+            "mx_dy": lambda: fp8.mx_quantize(dy, E5, q=mdq, scales=sdq),
+            "mx_dyt": lambda: fp8.mx_quantize_t(dy, E5, qt=mdt, scales=sdt),
+            "mx_dgrad": lambda: fp8.mx_gemm_fwd(mdq, sdq, mwt, swt, E5, out=dx),
+            "mx_wgrad": lambda: fp8.mx_gemm_fwd(mdt, sdt, mxt, sxt, E5, out=dw),
         }
-        order = [["pt_abs", "pt_quant", "pt_gemm"], ["mx_x", "mx_w", "mx_gemm"]]
+        order = [["pt_abs", "pt_quant", "pt_fwd", "pt_dyabs", "pt_dyquant", "pt_bwd"],
+                 ["mx_x", "mx_w", "mx_fwd", "mx_xt", "mx_wt", "mx_dy", "mx_dyt", "mx_dgrad", "mx_wgrad"]]
         t = {k: [] for k in calls}
         for r in range(reps + 2):
             for seq in order:
@@ -675,26 +695,22 @@ def mx_forward(fp8, dev, cfg_name="layer7b", reps=10):
                 if r >= 2:
                     for k, a, b in pairs:
                         t[k].append(a.elapsed_time(b) * 1e-3)
-        med = {k: float(np.median(v)) for k, v in t.items()}
-        flop = 2.0 * M * N * K
-        pt_q, mx_q = med["pt_abs"] + med["pt_quant"], med["mx_x"] + med["mx_w"]
-        pt_bytes = 2 * (M + N) * K + 3 * (M + N) * K           # statistic pass + quantise pass
-        mx_bytes = 3 * (M + N) * K + (M + N) * K / 32           # one pass: read 2 B, write 1 + 1/32 B
+        md = {k: float(np.median(v)) for k, v in t.items()}
+        ff, fb = 2.0 * M * N * K, 4.0 * M * N * K
+        v = {"pt_qf": md["pt_abs"] + md["pt_quant"], "pt_gf": md["pt_fwd"],
+             "pt_qb": md["pt_dyabs"] + md["pt_dyquant"], "pt_gb": md["pt_bwd"],
+             "mx_qf": md["mx_x"] + md["mx_w"], "mx_gf": md["mx_fwd"],
+             "mx_qb": md["mx_xt"] + md["mx_wt"] + md["mx_dy"] + md["mx_dyt"],
+             "mx_gb": md["mx_dgrad"] + md["mx_wgrad"], "ff": ff, "fb": fb}
+        for k in tot:
+            tot[k] += v[k]
+        us = lambda k: round(v[k] * 1e6, 1)
         rows.append({"linear": L.name, "M": M, "N": N, "K": K,
-                     "per_tensor": {"quantise_us": round(pt_q * 1e6, 1), "gemm_us": round(med["pt_gemm"] * 1e6, 1),
-                                    "gemm_tflops": round(flop / med["pt_gemm"] / 1e12, 1),
-                                    "quantise_gbs": round(pt_bytes / pt_q / 1e9, 1)},
-                     "mx": {"quantise_us": round(mx_q * 1e6, 1), "gemm_us": round(med["mx_gemm"] * 1e6, 1),
-                            "gemm_tflops": round(flop / med["mx_gemm"] / 1e12, 1),
-                            "quantise_gbs": round(mx_bytes / mx_q / 1e9, 1)}})
-        tot["pt_q"] += pt_q
-        tot["pt_g"] += med["pt_gemm"]
-        tot["mx_q"] += mx_q
-        tot["mx_g"] += med["mx_gemm"]
-        tot["flop"] += flop
-        tot["mx_bytes"] += mx_bytes
-        tot["pt_bytes"] += pt_bytes
-        del x, w, xq, wq, mxq, mwq, sx, sw, y
+                     "per_tensor": {"fwd_quantise_us": us("pt_qf"), "fwd_gemm_us": us("pt_gf"),
+                                    "bwd_quantise_us": us("pt_qb"), "bwd_gemm_us": us("pt_gb")},
+                     "mx": {"fwd_quantise_us": us("mx_qf"), "fwd_gemm_us": us("mx_gf"),
+                            "bwd_quantise_us": us("mx_qb"), "bwd_gemm_us": us("mx_gb")}})
+        del x, w, dy, xq, wq, xqt, wqt, dyq, dyqt, y, dx, dw, mxq, mwq, mxt, mwt, mdq, mdt
     # the SwiGLU requantisation between the gate/up and down products: the per-tensor
     # form (statistic pass + quantisation pass, hq only) against the MX form (one pass)
     F = cfg.linears[3].K
@@ -721,14 +737,15 @@ def mx_forward(fp8, dev, cfg_name="layer7b", reps=10):
     del gu, hq, mhq, msc
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
-    return {"workload": WORKLOADS[cfg_name] + ", forward of each linear",
-            "per_tensor": {"quantise_us": round(tot["pt_q"] * 1e6, 1), "gemm_us": round(tot["pt_g"] * 1e6, 1),
-                           "gemm_tflops": round(tot["flop"] / tot["pt_g"] / 1e12, 1),
-                           "quantise_gbs": round(tot["pt_bytes"] / tot["pt_q"] / 1e9, 1)},
-            "mx": {"quantise_us": round(tot["mx_q"] * 1e6, 1), "gemm_us": round(tot["mx_g"] * 1e6, 1),
-                   "gemm_tflops": round(tot["flop"] / tot["mx_g"] / 1e12, 1),
-                   "gemm_frac": round(tot["flop"] / tot["mx_g"] / 1e12 / FP8_PEAK_TFLOPS, 4),
-                   "quantise_gbs": round(tot["mx_bytes"] / tot["mx_q"] / 1e9, 1)},
+    path = lambda p: {"fwd_quantise_us": round(tot[p + "_qf"] * 1e6, 1), "fwd_gemm_us": round(tot[p + "_gf"] * 1e6, 1),
+                      "fwd_gemm_tflops": round(tot["ff"] / tot[p + "_gf"] / 1e12, 1),
+                      "bwd_quantise_us": round(tot[p + "_qb"] * 1e6, 1), "bwd_gemm_us": round(tot[p + "_gb"] * 1e6, 1),
+                      "bwd_gemm_tflops": round(tot["fb"] / tot[p + "_gb"] / 1e12, 1),
+                      "total_us": round(sum(tot[p + k] for k in ("_qf", "_gf", "_qb", "_gb")) * 1e6
+                                        + (sw_pt if p == "pt" else sw_mx) * 1e6, 1)}
+    return {"workload": WORKLOADS[cfg_name] + ", forward and backward of each linear",
+            "per_tensor": path("pt"),
+            "mx": path("mx"),
             "swiglu": {"M": cfg.M, "F": F,
                        "per_tensor_us": round(sw_pt * 1e6, 1),
                        "per_tensor_gbs": round((4 + 5) * n_h / sw_pt / 1e9, 1),
@@ -736,8 +753,8 @@ def mx_forward(fp8, dev, cfg_name="layer7b", reps=10):
                        "mx_gbs": round((4 + 1 + 1 / 32) * n_h / sw_mx / 1e9, 1),
                        "note": "per tensor: the SwiGLU statistic pass, then the requantisation (hq only); MX: one "
                                "pass, block maxima local"},
-            "timing": f"{reps} interleaved rounds, an event pair around every call, medians; quantisation "
-                      "without transposed copies on both paths",
+            "timing": f"{reps} interleaved rounds, an event pair around every call, medians; total_us adds "
+                      "the SwiGLU requantisation",
             "linears": rows}
 
 
@@ -958,7 +975,7 @@ def main():
                     help="skip the 14B- and 32B-class layer steps (their GEMM figures) reported with the layer7b "
                          "workload")
     ap.add_argument("--no-mx", action="store_true",
-                    help="skip the block-scaled (MX) forward measurement reported with the layer7b workload")
+                    help="skip the block-scaled (MX) layer measurement reported with the layer7b workload")
     ap.add_argument("--quant-mode", choices=("pair", "linear", "step"), default="pair",
                     help="pair: each linear's X and W quantised in one launch (their statistics in one launch for "
                          "QKV and O); linear: X and W quantised in separate launches; step: the four weights and the "
@@ -1056,7 +1073,7 @@ def main():
     if args.workload == "layer7b" and not args.no_shapes:
         for other in ("layer14b", "layer32b"):
             shapes[other] = step_shapes(fp8, dev, stream, other)
-    mx = mx_forward(fp8, dev) if args.workload == "layer7b" and not args.no_mx else None
+    mx = mx_layer(fp8, dev) if args.workload == "layer7b" and not args.no_mx else None
     clock = None if args.no_clock else sustained_clock(ops)
     want_cpu = not args.no_cpu_baseline and (args.workload == "layer7b" or args.cpu_baseline)
     cpu = cpu_baseline(ops, args.cpu_gemm_rows) if want_cpu else None
@@ -1122,7 +1139,7 @@ def main():
     if shapes:
         line["shapes"] = shapes
     if mx:
-        line["mx_forward"] = mx
+        line["mx_layer"] = mx
     line["breakdown"] = breakdown
     print(json.dumps(line))
 
