@@ -54,6 +54,9 @@
 //    for the backward products (a template argument: with a run-time choice the
 //    compiler merged the two store forms and dropped the hint).
 //  - Deterministic: every output is reduced by one wave in a fixed order.
+//  - Block-scaled (MX) products: gemm_mx_kernel, the same walk and tiles with
+//    each row's E8M0 block scales loaded beside its codes and applied by
+//    v_mfma_scale_f32_16x16x128_f8f6f4 (see the block-scaled section below).
 #include "fp8_device.hpp"
 #include "fp8_internal.hpp"
 

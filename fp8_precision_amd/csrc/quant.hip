@@ -1,14 +1,19 @@
-// quant.hip -- absmax reduction and per-tensor FP8 quantisation for gfx950.
+// quant.hip -- absmax reduction and per-tensor FP8 quantisation for gfx950, and
+// the block-scaled (MX) quantisations.
 //
 // Dynamic tensor-level scaling ("LLMQ: Efficient Lower-Precision Pretraining
 // for Consumer GPUs", section 1; FastML report, FP8 training without delayed
 // scaling): the scale of every tensor is derived from its own current absmax.
+// Block scaling (the same summary's section 2; the OCP MX format): one scale
+// per 32 consecutive elements along the reduction, no statistic pass.
 //
 // All kernels here are HBM-bound streaming kernels:
 //   absmax      reads 2 B per element
 //   quantize    reads 2 B, writes 1 B per element (+1 B with the transposed copy)
+//   MX          reads 2 B, writes 1 + 1/32 B per element (codes and scales)
 // They move data in 16-byte vectors, each wave instruction covering a
-// contiguous 1 KB (loads) or 512 B (stores).
+// contiguous 1 KB (loads) or 512 B (stores); the transposed MX form reads
+// 256-byte row segments.
 #include "fp8_device.hpp"
 #include "fp8_internal.hpp"
 
