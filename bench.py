@@ -630,11 +630,11 @@ def mx_layer(fp8, dev, cfg_name="layer7b", reps=10):
     backward (the measured alternative, not the headline).  Per tensor: the
     statistics of X and W in one launch, their quantisation with the transposed
     copies in one launch, the forward GEMM; the statistic and e5m2 quantisation
-    (with the transposed copy) of dY, the dgrad + wgrad launch.  MX: fp8_mx_quantize
-    of X and W, the block-scaled forward; fp8_mx_quantize_t of X and W (their blocks
-    along the backward reductions), fp8_mx_quantize and fp8_mx_quantize_t of dY
-    (e5m2), the block-scaled dgrad and wgrad.  Inputs drawn by workloads.py; the two
-    paths interleaved, `reps` rounds, an event pair around every call, medians."""
+    (with the transposed copy) of dY, the dgrad + wgrad launch.  MX: fp8_mx_quantize_both
+    of X and of W (the forward blocking and, from the same read, the blocking along the
+    backward reductions), the block-scaled forward; fp8_mx_quantize_both of dY (e5m2),
+    the block-scaled dgrad and wgrad.  Inputs drawn by workloads.py; the two paths
+    interleaved, `reps` rounds, an event pair around every call, medians."""
     cfg = workloads.CONFIGS[cfg_name]
     E4, E5 = fp8.E4M3, fp8.E5M2
     ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -668,18 +668,17 @@ def mx_layer(fp8, dev, cfg_name="layer7b", reps=10):
             "pt_dyquant": lambda: fp8.quantize(dy, E5, stats[2:3], want_q=True, want_qt=True, q=dyq, qt=dyqt,
                                                scale=sc[4], inv_scale=sc[5]),
             "pt_bwd": lambda: fp8.gemm_backward(dyq, dyqt, E5, wqt, xqt, sc[5], sc[3], sc[2], dx, dw),
-            "mx_x": lambda: fp8.mx_quantize(x, E4, q=mxq, scales=sx),
-            "mx_w": lambda: fp8.mx_quantize(w, E4, q=mwq, scales=sw),
+            # each tensor's two blockings from one read (the forward writes the backward's
+            # operands, as the per-tensor forward writes its transposed copies)
+            "mx_x": lambda: fp8.mx_quantize_both(x, E4, mxq, sx, mxt, sxt),
+            "mx_w": lambda: fp8.mx_quantize_both(w, E4, mwq, sw, mwt, swt),
             "mx_fwd": lambda: fp8.mx_gemm_fwd(mxq, sx, mwq, sw, E4, out=y),
-            "mx_xt": lambda: fp8.mx_quantize_t(x, E4, qt=mxt, scales=sxt),
-            "mx_wt": lambda: fp8.mx_quantize_t(w, E4, qt=mwt, scales=swt),
-            "mx_dy": lambda: fp8.mx_quantize(dy, E5, q=mdq, scales=sdq),
-            "mx_dyt": lambda: fp8.mx_quantize_t(dy, E5, qt=mdt, scales=sdt),
+            "mx_dy": lambda: fp8.mx_quantize_both(dy, E5, mdq, sdq, mdt, sdt),
             "mx_dgrad": lambda: fp8.mx_gemm_fwd(mdq, sdq, mwt, swt, E5, out=dx),
             "mx_wgrad": lambda: fp8.mx_gemm_fwd(mdt, sdt, mxt, sxt, E5, out=dw),
         }
         order = [["pt_abs", "pt_quant", "pt_fwd", "pt_dyabs", "pt_dyquant", "pt_bwd"],
-                 ["mx_x", "mx_w", "mx_fwd", "mx_xt", "mx_wt", "mx_dy", "mx_dyt", "mx_dgrad", "mx_wgrad"]]
+                 ["mx_x", "mx_w", "mx_fwd", "mx_dy", "mx_dgrad", "mx_wgrad"]]
         t = {k: [] for k in calls}
         for r in range(reps + 2):
             for seq in order:
@@ -700,7 +699,7 @@ def mx_layer(fp8, dev, cfg_name="layer7b", reps=10):
         v = {"pt_qf": md["pt_abs"] + md["pt_quant"], "pt_gf": md["pt_fwd"],
              "pt_qb": md["pt_dyabs"] + md["pt_dyquant"], "pt_gb": md["pt_bwd"],
              "mx_qf": md["mx_x"] + md["mx_w"], "mx_gf": md["mx_fwd"],
-             "mx_qb": md["mx_xt"] + md["mx_wt"] + md["mx_dy"] + md["mx_dyt"],
+             "mx_qb": md["mx_dy"],
              "mx_gb": md["mx_dgrad"] + md["mx_wgrad"], "ff": ff, "fb": fb}
         for k in tot:
             tot[k] += v[k]

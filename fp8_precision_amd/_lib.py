@@ -47,6 +47,7 @@ _SIGS = {
     "fp8_mx_gemm_fwd": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_mx_swiglu_requant": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "fp8_mx_quantize_t": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "fp8_mx_quantize_both": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -484,6 +485,28 @@ def mx_quantize_t(x: torch.Tensor, fmt: int, qt: torch.Tensor | None = None, sca
     _run("fp8_mx_quantize_t", _lib.fp8_mx_quantize_t, (x, qt, scales), _ptr(x), rows, cols, int(fmt), _ptr(qt),
          _ptr(scales))
     return qt, scales
+
+
+def mx_quantize_both(x: torch.Tensor, fmt: int, q=None, sq=None, qt=None, sqt=None):
+    """Both block quantisations of x [rows, cols] (multiples of 128) in one read: the
+    results of mx_quantize (q, sq) and of mx_quantize_t (qt, sqt)."""
+    _dev_tensor(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    u8 = lambda *sh: torch.empty(sh, dtype=torch.uint8, device=x.device)
+    q = u8(rows, cols) if q is None else q
+    sq = u8(cols // 128, rows, 4) if sq is None else sq
+    qt = u8(cols, rows) if qt is None else qt
+    sqt = u8(rows // 128, cols, 4) if sqt is None else sqt
+    for t, n, size in ((q, "q", rows * cols), (sq, "sq", rows * cols // 32), (qt, "qt", rows * cols),
+                       (sqt, "sqt", rows * cols // 32)):
+        _dev_tensor(t, n, torch.uint8)
+        if t.numel() != size:
+            raise ValueError(f"{n} has the wrong size")
+    _run("fp8_mx_quantize_both", _lib.fp8_mx_quantize_both, (x, q, sq, qt, sqt), _ptr(x), rows, cols, int(fmt),
+         _ptr(q), _ptr(sq), _ptr(qt), _ptr(sqt))
+    return q, sq, qt, sqt
 
 
 def mx_swiglu_requant(gu: torch.Tensor, hq: torch.Tensor | None = None, scales: torch.Tensor | None = None):

@@ -497,6 +497,25 @@ fp8_status fp8_mx_quantize_t(const void* x, int64_t rows, int64_t cols, fp8_fmt 
     return FP8_OK;
 }
 
+fp8_status fp8_mx_quantize_both(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt, uint8_t* q, uint8_t* sq,
+                                uint8_t* qt, uint8_t* sqt, hipStream_t stream)
+{
+    t_last_error.clear();
+    if (!x || !q || !sq || !qt || !sqt) return fail(FP8_ERR_INVALID, "fp8_mx_quantize_both: null pointer");
+    if (fmt != FP8_E4M3 && fmt != FP8_E5M2) return fail(FP8_ERR_INVALID, "fp8_mx_quantize_both: bad format");
+    if (!mul_ok(rows, cols, kMaxElems)) return fail(FP8_ERR_INVALID, "fp8_mx_quantize_both: bad shape");
+    const int64_t n = rows * cols;
+    const Range r[] = {{x, 2 * n}, {q, n}, {sq, n / 32}, {qt, n}, {sqt, n / 32}};
+    if (any_overlap(r)) return fail(FP8_ERR_INVALID, "fp8_mx_quantize_both: overlapping buffers");
+    if (rows % 128 || cols % 128) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_quantize_both: rows and cols must be multiples of 128");
+    if (n / 32 >= ((int64_t)1 << 31)) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_quantize_both: tensor too large");
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(qt, 16))
+        return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_quantize_both: misaligned pointer");
+    hipError_t e = fp8k::launch_mx_quantize_both(x, rows, cols, (int)fmt, q, sq, qt, sqt, stream);
+    if (e != hipSuccess) return fail_hip("fp8_mx_quantize_both", e);
+    return FP8_OK;
+}
+
 fp8_status fp8_mx_swiglu_requant(const void* gu, int64_t M, int64_t F, uint8_t* hq, uint8_t* scales,
                                  hipStream_t stream)
 {

@@ -57,6 +57,12 @@ hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* sa, int fmt_a, const 
 hipError_t launch_mx_quantize_t(const void* x, int64_t rows, int64_t cols, int fmt, uint8_t* qt, uint8_t* scales,
                                 hipStream_t stream);
 
+// Both block quantisations of x in one read: q [rows, cols] (blocks along rows,
+// scales sq [cols / 128][rows][4]) and qt [cols, rows] (blocks along columns,
+// scales sqt [rows / 128][cols][4]); rows, cols multiples of 128.
+hipError_t launch_mx_quantize_both(const void* x, int64_t rows, int64_t cols, int fmt, uint8_t* q, uint8_t* sq,
+                                   uint8_t* qt, uint8_t* sqt, hipStream_t stream);
+
 // The SwiGLU output of gu = [gate | up] ([M, 2F] bf16, F a multiple of 128),
 // block (MX) quantised along F: E4M3 codes hq[M, F], scales step-major
 // [F / 128][M][4].

@@ -578,6 +578,141 @@ __global__ void __launch_bounds__(256) mx_quantize_kernel(const u32x4* __restric
         mx_vector<FMT>(NT ? __builtin_nontemporal_load(x + v) : x[v], v, q, scales, rows, nb);
 }
 
+// Max over the 16 lanes of a DPP row (lanes 16 j .. 16 j + 15).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v)
+{
+    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad: 1 0 3 2
+    v = v > o ? v : o;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);            // quad: 2 3 0 1
+    v = v > o ? v : o;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false);           // row rotate by 4
+    v = v > o ? v : o;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);           // row rotate by 8
+    return v > o ? v : o;
+}
+
+// The block scale 2^-e and its E8M0 byte for a block's largest magnitude bit
+// pattern m (bf16 bits; >= 0x7F80: an infinity or a NaN -- unscaled, byte 255).
+template <int FMT>
+__device__ __forceinline__ float mx_scale_of(uint32_t m, uint32_t& sbyte)
+{
+    constexpr int emax = FMT == 0 ? 8 : 15;
+    if (m >= 0x7F80u) {
+        sbyte = 255;
+        return 1.0f;
+    }
+    const int fl = m >= 0x80u ? (int)(m >> 7) - 127 : 31 - __builtin_clz(m | 1u) - 133;
+    int e = m ? fl - emax : -127;
+    e = e < -127 ? -127 : e;
+    sbyte = (uint32_t)(e + 127);
+    return __uint_as_float((uint32_t)(127 - e) << 23);
+}
+
+// Two codes (bytes 0, 1) of two bf16 values under one block scale; a NaN takes
+// the NaN code with its sign.
+template <int FMT>
+__device__ __forceinline__ uint32_t mx_code2(uint32_t h0, uint32_t h1, float s)
+{
+    constexpr float mx = Fmt<FMT>::max;
+    const float a = __builtin_amdgcn_fmed3f(__uint_as_float(h0 << 16) * s, -mx, mx);
+    const float b = __builtin_amdgcn_fmed3f(__uint_as_float(h1 << 16) * s, -mx, mx);
+    uint32_t c = FMT == 0 ? (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)
+                          : (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    if ((h0 & 0x7FFFu) > 0x7F80u) c = (c & 0xFF00u) | ((h0 >> 8) & 0x80u) | 0x7Fu;
+    if ((h1 & 0x7FFFu) > 0x7F80u) c = (c & 0x00FFu) | ((((h1 >> 8) & 0x80u) | 0x7Fu) << 8);
+    return c & 0xFFFFu;
+}
+
+// Both block quantisations of x in one read: q [rows, cols] with blocks along
+// the rows (the forward operand) and qt [cols, rows] with blocks along the
+// columns (the backward operand), each with its own step-major scales -- the
+// bytes of fp8_mx_quantize and of fp8_mx_quantize_t.  A wave takes 32 rows x
+// 128 columns, a lane columns 2 l, 2 l + 1 of the 32 rows (one 256-byte row
+// segment per load instruction): the column blocks' maxima come from the lane's
+// registers, a row block's (32 columns = 16 lanes) from four DPP steps.
+template <int FMT, bool NT>
+__global__ void __launch_bounds__(256) mx_quantize_both_kernel(const uint32_t* __restrict__ x, int64_t rows,
+                                                               int64_t cols, uint8_t* __restrict__ q,
+                                                               uint8_t* __restrict__ sq, uint8_t* __restrict__ qt,
+                                                               uint8_t* __restrict__ sqt)
+{
+    const int lane = threadIdx.x & 63;
+    const int ct = (int)(cols / 128), tiles = (int)(rows / 32) * ct;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int t = blockIdx.x * 4 + wave; t < tiles; t += gridDim.x * 4) {
+        // wave-uniform tile origin (scalar registers): every address is a uniform
+        // row base plus the lane's column offset
+        const int tr = t / ct, tc = t - tr * ct;
+        const int64_t r0 = (int64_t)tr * 32, c0 = (int64_t)tc * 128;
+        const int c = 2 * lane;                               // the lane's columns c0 + c, c0 + c + 1
+        uint32_t w[32];
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            const uint32_t* src = x + ((r0 + r) * cols + c0) / 2 + lane;
+            w[r] = NT ? __builtin_nontemporal_load(src) : *src;
+        }
+        // column blocks: rows r0 .. r0 + 31 of columns c0 + c and c0 + c + 1
+        const int64_t bt = r0 / 32;
+#pragma unroll
+        for (int col = 0; col < 2; ++col) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+                const uint32_t a = (col ? (w[r] >> 16) : w[r]) & 0x7FFFu;
+                m = m > a ? m : a;
+            }
+            uint32_t sbyte;
+            const float s = mx_scale_of<FMT>(m, sbyte);
+            uint32_t codes[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t h0 = col ? w[4 * k] >> 16 : w[4 * k] & 0xFFFFu;
+                const uint32_t h1 = col ? w[4 * k + 1] >> 16 : w[4 * k + 1] & 0xFFFFu;
+                const uint32_t h2 = col ? w[4 * k + 2] >> 16 : w[4 * k + 2] & 0xFFFFu;
+                const uint32_t h3 = col ? w[4 * k + 3] >> 16 : w[4 * k + 3] & 0xFFFFu;
+                codes[k] = mx_code2<FMT>(h0, h1, s) | (mx_code2<FMT>(h2, h3, s) << 16);
+            }
+            uint4* dst = reinterpret_cast<uint4*>(qt + (c0 + c + col) * rows + r0);
+            dst[0] = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+            dst[1] = make_uint4(codes[4], codes[5], codes[6], codes[7]);
+            sqt[((bt >> 2) * cols + c0 + c + col) * 4 + (bt & 3)] = (uint8_t)sbyte;
+        }
+        // row blocks: block (c0 + c) / 32 of each row (16 lanes); the tile's four
+        // blocks form one group of four, stored at row-dependent offsets
+        const int64_t g4 = c0 / 128;
+        const int bi = lane >> 4;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            const uint32_t lo = w[r] & 0xFFFFu, hi = w[r] >> 16;
+            const uint32_t a0 = lo & 0x7FFFu, a1 = hi & 0x7FFFu;
+            const uint32_t m = row16_max_u32(a0 > a1 ? a0 : a1);
+            uint32_t sbyte;
+            const float s = mx_scale_of<FMT>(m, sbyte);
+            reinterpret_cast<uint16_t*>(q + (r0 + r) * cols + c0)[lane] = (uint16_t)mx_code2<FMT>(lo, hi, s);
+            if ((lane & 15) == 0) sq[(g4 * rows + r0 + r) * 4 + bi] = (uint8_t)sbyte;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+hipError_t launch_mx_quantize_both(const void* x, int64_t rows, int64_t cols, int fmt, uint8_t* q, uint8_t* sq,
+                                   uint8_t* qt, uint8_t* sqt, hipStream_t stream)
+{
+    const int64_t tiles = (rows / 32) * (cols / 128);
+    int64_t blocks = (tiles + 3) / 4;
+    const int64_t cap = (int64_t)device_cu_count() * 8;
+    if (blocks > cap) blocks = cap;
+    const uint32_t* xv = reinterpret_cast<const uint32_t*>(x);
+    const bool nt = 2 * rows * cols >= kAbsStreamBytes;
+    const dim3 grid((unsigned)blocks), block(256);
+    if (fmt == 0)
+        return nt ? launch(mx_quantize_both_kernel<0, true>, grid, block, stream, xv, rows, cols, q, sq, qt, sqt)
+                  : launch(mx_quantize_both_kernel<0, false>, grid, block, stream, xv, rows, cols, q, sq, qt, sqt);
+    return nt ? launch(mx_quantize_both_kernel<1, true>, grid, block, stream, xv, rows, cols, q, sq, qt, sqt)
+              : launch(mx_quantize_both_kernel<1, false>, grid, block, stream, xv, rows, cols, q, sq, qt, sqt);
+}
+
+
 // Transposed block (MX) quantisation: qt = the codes of x^T [cols, rows] with
 // blocks of 32 consecutive elements along qt's rows, i.e. 32 consecutive rows
 // of one column of x -- the operand layout of a backward product whose

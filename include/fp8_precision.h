@@ -395,6 +395,21 @@ fp8_status fp8_mx_quantize_t(const void* x, int64_t rows, int64_t cols, fp8_fmt 
                              uint8_t* scales, hipStream_t stream);
 
 /*
+ * fp8_mx_quantize_both: fp8_mx_quantize and fp8_mx_quantize_t of the same x
+ * from one read of it -- the forward operand (blocks along rows) and the
+ * backward operand (blocks along columns, of x^T), each with its own scales;
+ * the bytes of the two calls.
+ *
+ *   x        bf16 [rows, cols], 16-byte aligned
+ *   q, sq    u8 [rows, cols] (16-byte aligned) and [cols / 128][rows][4]
+ *   qt, sqt  u8 [cols, rows] (16-byte aligned) and [rows / 128][cols][4]
+ * Constraints: rows % 128 == 0 and cols % 128 == 0 (else FP8_ERR_UNSUPPORTED);
+ * buffers must not overlap.
+ */
+fp8_status fp8_mx_quantize_both(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt, uint8_t* q,
+                                uint8_t* sq, uint8_t* qt, uint8_t* sqt, hipStream_t stream);
+
+/*
  * fp8_mx_swiglu_requant: the SwiGLU output h = silu(g) * u of gu = [gate | up]
  * (each element exactly as fp8_swiglu_requant evaluates it, never rounded to
  * bf16), block-quantised to E4M3 along the feature axis by the rule of

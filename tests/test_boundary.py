@@ -406,3 +406,15 @@ def test_mx_quantize_t_validation(lib):
     assert f(A16, 64, 128, 0, qt, sc, None) == UNSUPPORTED           # rows not a multiple of 128
     assert f(A16, 128, 144, 0, qt, sc, None) == UNSUPPORTED          # cols not a multiple of 128
     assert f(A16, 128, 128, 0, qt, sc + 2, None) == UNSUPPORTED      # misaligned scales
+
+
+def test_mx_quantize_both_validation(lib):
+    f = lib.fp8_mx_quantize_both
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int] + [ctypes.c_void_p] * 5
+    q, sq, qt, sqt = B16, B16 + (1 << 20), C16, C16 + (1 << 20)
+    assert f(None, 128, 128, 0, q, sq, qt, sqt, None) == INVALID
+    assert f(A16, 128, 128, 0, q, sq, None, sqt, None) == INVALID
+    assert f(A16, 128, 128, 0, q, sq, q + 64, sqt, None) == INVALID    # qt over q
+    assert f(A16, 128, 96, 0, q, sq, qt, sqt, None) == UNSUPPORTED
+    assert f(A16, 128, 128, 0, q + 8, sq, qt, sqt, None) == UNSUPPORTED

@@ -281,3 +281,22 @@ def test_mx_backward_products(fp8, orc):
     ref = orc.mx_gemm(a, sa, E5, b, sb, E4M3)
     gemm_compare(dw, ref, "mx wgrad")
     mx_bound_check(dw, ref, a, sa, E5, b, sb, np.arange(N, dtype=np.int64), "mx wgrad")
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("rows,cols", [(512, 128), (384, 1280), (4096, 4096)])
+def test_mx_quantize_both_matches_the_two_calls(fp8, orc, fmt, rows, cols):
+    """One read, both blockings: bit for bit the oracle's (and so the two separate calls')."""
+    if rows == 512:
+        bits = np.arange(65536, dtype=np.uint16).reshape(128, 512).T.copy()    # every pattern
+    else:
+        bits = workloads.bf16_bits(workloads.draw(73, rows + fmt, (rows, cols), 2.0))
+    say("mx_quantize_both", rows, cols, fmt)
+    q, sq, qt, sqt = fp8.mx_quantize_both(to_dev(bits), fmt)
+    torch.cuda.synchronize()
+    q_r, sq_r = orc.mx_quantize(np.ascontiguousarray(bits), fmt)
+    qt_r, sqt_r = orc.mx_quantize(np.ascontiguousarray(bits.T), fmt)
+    assert np.array_equal(u8(sq), step_major(sq_r)), "row-block scales"
+    assert np.array_equal(u8(sqt), step_major(sqt_r)), "column-block scales"
+    assert_codes_equal(u8(q), q_r, fmt, "q")
+    assert_codes_equal(u8(qt), qt_r, fmt, "qt")
