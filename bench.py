@@ -641,7 +641,8 @@ def mx_layer(fp8, dev, cfg_name="layer7b", reps=10):
     u8 = lambda *sh: torch.empty(sh, dtype=torch.uint8, device=dev)
     f32 = lambda: torch.empty(1, dtype=torch.float32, device=dev)
     rows = []
-    tot = {k: 0.0 for k in ("pt_qf", "pt_gf", "pt_qb", "pt_gb", "mx_qf", "mx_gf", "mx_qb", "mx_gb", "ff", "fb")}
+    tot = {k: 0.0 for k in ("pt_qf", "pt_gf", "pt_qb", "pt_gb", "mx_qf", "mx_gf", "mx_qb", "mx_gb", "ff", "fb",
+                            "bf", "bb")}
     for li, L in enumerate(cfg.linears):
         x = workloads.draw_x(cfg, li).to(dev)
         w = workloads.draw_w(cfg, li).to(dev)
@@ -700,7 +701,8 @@ def mx_layer(fp8, dev, cfg_name="layer7b", reps=10):
              "pt_qb": md["pt_dyabs"] + md["pt_dyquant"], "pt_gb": md["pt_bwd"],
              "mx_qf": md["mx_x"] + md["mx_w"], "mx_gf": md["mx_fwd"],
              "mx_qb": md["mx_dy"],
-             "mx_gb": md["mx_dgrad"] + md["mx_wgrad"], "ff": ff, "fb": fb}
+             "mx_gb": md["mx_dgrad"] + md["mx_wgrad"], "ff": ff, "fb": fb,
+             "bf": (M + N) * K, "bb": M * N}
         for k in tot:
             tot[k] += v[k]
         us = lambda k: round(v[k] * 1e6, 1)
@@ -736,9 +738,16 @@ def mx_layer(fp8, dev, cfg_name="layer7b", reps=10):
     del gu, hq, mhq, msc
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    # algorithmic bytes per quantised element: per tensor, the statistic's 2-byte read,
+    # then a 2-byte read and the code + transposed-copy writes; MX, one 2-byte read,
+    # both blockings' codes and one scale byte per 32 codes of each
+    epb = {"pt": 6.0, "mx": 4.0 + 2.0 / 32}
+    gbs = lambda p, k, n: round(epb[p] * tot[n] / tot[p + k] / 1e9, 1)
     path = lambda p: {"fwd_quantise_us": round(tot[p + "_qf"] * 1e6, 1), "fwd_gemm_us": round(tot[p + "_gf"] * 1e6, 1),
+                      "fwd_quantise_gbs": gbs(p, "_qf", "bf"),
                       "fwd_gemm_tflops": round(tot["ff"] / tot[p + "_gf"] / 1e12, 1),
                       "bwd_quantise_us": round(tot[p + "_qb"] * 1e6, 1), "bwd_gemm_us": round(tot[p + "_gb"] * 1e6, 1),
+                      "bwd_quantise_gbs": gbs(p, "_qb", "bb"),
                       "bwd_gemm_tflops": round(tot["fb"] / tot[p + "_gb"] / 1e12, 1),
                       "total_us": round(sum(tot[p + k] for k in ("_qf", "_gf", "_qb", "_gb")) * 1e6
                                         + (sw_pt if p == "pt" else sw_mx) * 1e6, 1)}
@@ -981,6 +990,9 @@ def main():
                          "first input quantised together at the start of the step")
     ap.add_argument("--dy-format", choices=("e5m2", "e4m3"), default="e5m2",
                     help="format of the output gradients dY (e5m2: the default reading; e4m3: the all-E4M3 variant)")
+    ap.add_argument("--mx-only", action="store_true",
+                    help="only run the block-scaled (MX) layer comparison and print it as the JSON line (context, "
+                         "not the metric)")
     ap.add_argument("--vs-hipblaslt", action="store_true",
                     help="only compare every GEMM call of the step with hipBLASLt (torch._scaled_mm) on the same "
                          "operand bytes, interleaved, and print that as the JSON line (context, not the metric)")
@@ -998,6 +1010,9 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     cfg = workloads.CONFIGS[args.workload]
+    if args.mx_only:
+        print(json.dumps({"mx_layer": mx_layer(fp8, dev, args.workload)}))
+        return
     if args.vs_hipblaslt:
         ops, _ = build_step(fp8, dev, args.workload, "copies", False, False)
         for _ in range(3):

@@ -509,7 +509,7 @@ fp8_status fp8_mx_quantize_both(const void* x, int64_t rows, int64_t cols, fp8_f
     if (any_overlap(r)) return fail(FP8_ERR_INVALID, "fp8_mx_quantize_both: overlapping buffers");
     if (rows % 128 || cols % 128) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_quantize_both: rows and cols must be multiples of 128");
     if (n / 32 >= ((int64_t)1 << 31)) return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_quantize_both: tensor too large");
-    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(qt, 16))
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(qt, 16) || !aligned(sq, 4) || !aligned(sqt, 4))
         return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_quantize_both: misaligned pointer");
     hipError_t e = fp8k::launch_mx_quantize_both(x, rows, cols, (int)fmt, q, sq, qt, sqt, stream);
     if (e != hipSuccess) return fail_hip("fp8_mx_quantize_both", e);

@@ -578,19 +578,6 @@ __global__ void __launch_bounds__(256) mx_quantize_kernel(const u32x4* __restric
         mx_vector<FMT>(NT ? __builtin_nontemporal_load(x + v) : x[v], v, q, scales, rows, nb);
 }
 
-// Max over the 16 lanes of a DPP row (lanes 16 j .. 16 j + 15).
-__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v)
-{
-    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad: 1 0 3 2
-    v = v > o ? v : o;
-    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);            // quad: 2 3 0 1
-    v = v > o ? v : o;
-    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false);           // row rotate by 4
-    v = v > o ? v : o;
-    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);           // row rotate by 8
-    return v > o ? v : o;
-}
-
 // The block scale 2^-e and its E8M0 byte for a block's largest magnitude bit
 // pattern m (bf16 bits; >= 0x7F80: an infinity or a NaN -- unscaled, byte 255).
 template <int FMT>
@@ -623,93 +610,268 @@ __device__ __forceinline__ uint32_t mx_code2(uint32_t h0, uint32_t h1, float s)
     return c & 0xFFFFu;
 }
 
+// The scaled conversion of gfx950 (v_cvt_scalef32_pk_{fp8,bf8}_bf16): two bf16
+// values divided by the power of two whose fp32 exponent field is that of the
+// scale operand, rounded to nearest-even into the format; an E8M0 byte b is
+// passed as the fp32 bits b << 23 (b = 0 acts as 2^-127).  Checked against the
+// encoder for every bf16 value under every byte 0..254: exact, subnormal results
+// included, except that it does not saturate (a result past the largest finite
+// value becomes NaN for E4M3, infinity for E5M2) -- so magnitudes are clamped
+// first, below.  Four codes: w0's pair in bytes 0, 1 and w1's in bytes 2, 3.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int FMT>
+__device__ __forceinline__ uint32_t mx_cvt4(uint32_t w0, uint32_t w1, float s)
+{
+    const s16x2 z = {0, 0};
+    const bf16x2 a = __builtin_bit_cast(bf16x2, w0), b = __builtin_bit_cast(bf16x2, w1);
+    s16x2 r;
+    if (FMT == 0) {
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(z, a, s, false);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, b, s, true);
+    } else {
+        r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(z, a, s, false);
+        r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, b, s, true);
+    }
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// For a finite block with largest magnitude pattern m (< 0x7F80): the E8M0 byte
+// e + 127 = max(exponent field of m - emax, 0) -- a subnormal or zero maximum
+// gives e = -127 either way -- and the clamp limit: the largest bf16 magnitude
+// that still rounds to the format's largest finite value under 2^-e (464 2^e for
+// E4M3, whose tie at 464 goes to the even 448; just below 61440 2^e for E5M2,
+// whose tie goes up).  Both packed into the two 16-bit halves.
+template <int FMT>
+__device__ __forceinline__ uint32_t mx_fast_scale(uint32_t m, uint32_t& limit2)
+{
+    constexpr int emax = FMT == 0 ? 8 : 15;
+    constexpr uint32_t frac = FMT == 0 ? 0x68u : 0x6Fu;
+    const int b = (int)(m >> 7) - emax;
+    const uint32_t sbyte = (uint32_t)(b > 0 ? b : 0);
+    const uint32_t lim = ((sbyte + emax) << 7) | frac;
+    limit2 = lim | (lim << 16);
+    return sbyte;
+}
+
+// Clamp both bf16 of w to magnitude limit (packed per half), keeping the signs.
+__device__ __forceinline__ uint32_t mx_clamp2(uint32_t w, uint32_t a, uint32_t limit2)
+{
+    const uint32_t c = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(as_us2(a), as_us2(limit2)));
+    return (c & 0x7FFF7FFFu) | (w & 0x80008000u);
+}
+
 // Both block quantisations of x in one read: q [rows, cols] with blocks along
 // the rows (the forward operand) and qt [cols, rows] with blocks along the
 // columns (the backward operand), each with its own step-major scales -- the
-// bytes of fp8_mx_quantize and of fp8_mx_quantize_t.  A wave takes 32 rows x
-// 128 columns, a lane columns 2 l, 2 l + 1 of the 32 rows (one 256-byte row
-// segment per load instruction): the column blocks' maxima come from the lane's
-// registers, a row block's (32 columns = 16 lanes) from four DPP steps.
+// bytes of fp8_mx_quantize and of fp8_mx_quantize_t.  A 256-thread block takes
+// a 128 x 128 tile, each wave 32 rows of it, each lane an 8 x 8 piece: rows
+// 8 (l & 3) .. + 7 of the wave's, columns 8 (l >> 2) .. + 7 (one 16-byte load
+// per row).  A column block (32 rows) is then the 4 lanes of a quad and a row
+// block (32 columns) the lanes l, l ^ 4, ... of one 16-lane DPP row, so both
+// maxima take two DPP steps.  The row codes go straight to q (a wave store
+// covers 4 rows x 128 bytes); the column codes are staged in LDS as qt rows and
+// written out as 128-byte row segments, as are both tiles' 512 scale bytes.
+// Tiles holding an infinity or a NaN take the generic per-element rule
+// (per wave: blocks never cross waves).
 template <int FMT, bool NT>
-__global__ void __launch_bounds__(256) mx_quantize_both_kernel(const uint32_t* __restrict__ x, int64_t rows,
+__global__ void __launch_bounds__(256) mx_quantize_both_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                                int64_t cols, uint8_t* __restrict__ q,
-                                                               uint8_t* __restrict__ sq, uint8_t* __restrict__ qt,
-                                                               uint8_t* __restrict__ sqt)
+                                                               uint32_t* __restrict__ sq, uint8_t* __restrict__ qt,
+                                                               uint32_t* __restrict__ sqt)
 {
-    const int lane = threadIdx.x & 63;
-    const int ct = (int)(cols / 128), tiles = (int)(rows / 32) * ct;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    for (int t = blockIdx.x * 4 + wave; t < tiles; t += gridDim.x * 4) {
-        // wave-uniform tile origin (scalar registers): every address is a uniform
-        // row base plus the lane's column offset
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kQtEdge * kQtEdge];    // qt rows of the tile
+    __shared__ uint32_t srow[kQtEdge], scol[kQtEdge];                           // the tile's scale bytes
+    uint8_t* const sr = reinterpret_cast<uint8_t*>(srow);
+    uint8_t* const sc = reinterpret_cast<uint8_t*>(scol);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rq = lane & 3, g = lane >> 2;          // row group (8 rows), column group (8 columns)
+    const int rt = wave * 32 + 8 * rq;               // the lane's first row within the tile
+    // qt piece of this lane's 8 rows in LDS: qt row col holds 8 pieces of 16 bytes,
+    // piece p at physical slot p ^ ((col >> 3) & 7); the lane's rows are half
+    // (rt >> 3) & 1 of piece rt >> 4, and col >> 3 == g for all its columns
+    uint8_t* const lds_qt = tile + 8 * g * kQtEdge + (((rt >> 4) ^ (g & 7)) * 16) + ((rt >> 3) & 1) * 8;
+    const int ct = (int)(cols / kQtEdge), tiles = (int)(rows / kQtEdge) * ct;
+    for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
         const int tr = t / ct, tc = t - tr * ct;
-        const int64_t r0 = (int64_t)tr * 32, c0 = (int64_t)tc * 128;
-        const int c = 2 * lane;                               // the lane's columns c0 + c, c0 + c + 1
-        uint32_t w[32];
+        const int64_t R0 = (int64_t)tr * kQtEdge, C0 = (int64_t)tc * kQtEdge;
+        const int64_t off = (R0 + rt) * cols + C0 + 8 * g;        // the lane's first element
+        uint32_t v[8][4];
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
-            const uint32_t* src = x + ((r0 + r) * cols + c0) / 2 + lane;
-            w[r] = NT ? __builtin_nontemporal_load(src) : *src;
+        for (int j = 0; j < 8; ++j) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(x + off + j * cols);
+            const u32x4 w = NT ? __builtin_nontemporal_load(src) : *src;
+            v[j][0] = w.x; v[j][1] = w.y; v[j][2] = w.z; v[j][3] = w.w;
         }
-        // column blocks: rows r0 .. r0 + 31 of columns c0 + c and c0 + c + 1
-        const int64_t bt = r0 / 32;
+        __syncthreads();               // the previous tile's write-out has read the LDS
+        uint32_t a[8][4];
 #pragma unroll
-        for (int col = 0; col < 2; ++col) {
-            uint32_t m = 0;
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int r = 0; r < 32; ++r) {
-                const uint32_t a = (col ? (w[r] >> 16) : w[r]) & 0x7FFFu;
-                m = m > a ? m : a;
+            for (int k = 0; k < 4; ++k) a[j][k] = v[j][k] & 0x7FFF7FFFu;
+        // row maxima (the lane's 8 values, then the block's 4 lanes: rotations by 4 and 8)
+        uint32_t rm[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const us2 m2 = __builtin_elementwise_max(__builtin_elementwise_max(as_us2(a[j][0]), as_us2(a[j][1])),
+                                                     __builtin_elementwise_max(as_us2(a[j][2]), as_us2(a[j][3])));
+            uint32_t m = m2.x > m2.y ? m2.x : m2.y;
+            uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x124, 0xF, 0xF, false);
+            m = m > o ? m : o;
+            o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x128, 0xF, 0xF, false);
+            rm[j] = m > o ? m : o;
+        }
+        // column maxima, packed per pair of columns (the lane's 8 rows, then the quad)
+        uint32_t cm[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            us2 m2 = as_us2(a[0][k]);
+#pragma unroll
+            for (int j = 1; j < 8; ++j) m2 = __builtin_elementwise_max(m2, as_us2(a[j][k]));
+            uint32_t m = __builtin_bit_cast(uint32_t, m2);
+            m2 = __builtin_elementwise_max(m2, as_us2((uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false)));
+            m = __builtin_bit_cast(uint32_t, m2);
+            m2 = __builtin_elementwise_max(m2, as_us2((uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false)));
+            cm[k] = __builtin_bit_cast(uint32_t, m2);
+        }
+        uint32_t lane_max = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) lane_max = lane_max > rm[j] ? lane_max : rm[j];
+        uint8_t* const qrow = q + off;
+        if (__builtin_amdgcn_ballot_w64(lane_max >= 0x7F80u) == 0) {
+            // every block of the wave finite: the scaled conversion on clamped values
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                uint32_t lim2;
+                const uint32_t sb = mx_fast_scale<FMT>(rm[j], lim2);
+                const float sf = __uint_as_float(sb << 23);
+                const uint32_t c0 = mx_cvt4<FMT>(mx_clamp2(v[j][0], a[j][0], lim2), mx_clamp2(v[j][1], a[j][1], lim2), sf);
+                const uint32_t c1 = mx_cvt4<FMT>(mx_clamp2(v[j][2], a[j][2], lim2), mx_clamp2(v[j][3], a[j][3], lim2), sf);
+                *reinterpret_cast<uint2*>(qrow + j * cols) = make_uint2(c0, c1);
+                if ((g & 3) == 0) sr[(rt + j) * 4 + (g >> 2)] = (uint8_t)sb;
             }
-            uint32_t sbyte;
-            const float s = mx_scale_of<FMT>(m, sbyte);
-            uint32_t codes[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const uint32_t h0 = col ? w[4 * k] >> 16 : w[4 * k] & 0xFFFFu;
-                const uint32_t h1 = col ? w[4 * k + 1] >> 16 : w[4 * k + 1] & 0xFFFFu;
-                const uint32_t h2 = col ? w[4 * k + 2] >> 16 : w[4 * k + 2] & 0xFFFFu;
-                const uint32_t h3 = col ? w[4 * k + 3] >> 16 : w[4 * k + 3] & 0xFFFFu;
-                codes[k] = mx_code2<FMT>(h0, h1, s) | (mx_code2<FMT>(h2, h3, s) << 16);
+            for (int k = 0; k < 4; ++k) {
+                uint32_t l0, l1;
+                const uint32_t s0 = mx_fast_scale<FMT>(cm[k] & 0xFFFFu, l0), s1 = mx_fast_scale<FMT>(cm[k] >> 16, l1);
+                const uint32_t lim2 = (l0 & 0xFFFFu) | (l1 & 0xFFFF0000u);
+                const float f0 = __uint_as_float(s0 << 23), f1 = __uint_as_float(s1 << 23);
+                uint32_t c[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) c[j] = mx_clamp2(v[j][k], a[j][k], lim2);
+                // column 2k: the low halves of rows (0,1), (2,3), ...; column 2k + 1: the high halves
+                uint2 e, o;
+                e.x = mx_cvt4<FMT>(__builtin_amdgcn_perm(c[1], c[0], 0x05040100u), __builtin_amdgcn_perm(c[3], c[2], 0x05040100u), f0);
+                e.y = mx_cvt4<FMT>(__builtin_amdgcn_perm(c[5], c[4], 0x05040100u), __builtin_amdgcn_perm(c[7], c[6], 0x05040100u), f0);
+                o.x = mx_cvt4<FMT>(__builtin_amdgcn_perm(c[1], c[0], 0x07060302u), __builtin_amdgcn_perm(c[3], c[2], 0x07060302u), f1);
+                o.y = mx_cvt4<FMT>(__builtin_amdgcn_perm(c[5], c[4], 0x07060302u), __builtin_amdgcn_perm(c[7], c[6], 0x07060302u), f1);
+                *reinterpret_cast<uint2*>(lds_qt + (2 * k) * kQtEdge) = e;
+                *reinterpret_cast<uint2*>(lds_qt + (2 * k + 1) * kQtEdge) = o;
+                if (rq == 0) {
+                    sc[(8 * g + 2 * k) * 4 + wave] = (uint8_t)s0;
+                    sc[(8 * g + 2 * k + 1) * 4 + wave] = (uint8_t)s1;
+                }
             }
-            uint4* dst = reinterpret_cast<uint4*>(qt + (c0 + c + col) * rows + r0);
-            dst[0] = make_uint4(codes[0], codes[1], codes[2], codes[3]);
-            dst[1] = make_uint4(codes[4], codes[5], codes[6], codes[7]);
-            sqt[((bt >> 2) * cols + c0 + c + col) * 4 + (bt & 3)] = (uint8_t)sbyte;
-        }
-        // row blocks: block (c0 + c) / 32 of each row (16 lanes); the tile's four
-        // blocks form one group of four, stored at row-dependent offsets
-        const int64_t g4 = c0 / 128;
-        const int bi = lane >> 4;
+        } else {
+            // an infinity or a NaN in the wave's rows: the per-element rule, one row
+            // or pair of columns at a time, re-reading x (rare: kept out of the
+            // registers of the common path)
+#pragma unroll 1
+            for (int j = 0; j < 8; ++j) {
+                const u32x4 w = *reinterpret_cast<const u32x4*>(x + off + j * cols);
+                const uint32_t wr[4] = {w.x, w.y, w.z, w.w};
+                uint32_t m = 0;
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
-            const uint32_t lo = w[r] & 0xFFFFu, hi = w[r] >> 16;
-            const uint32_t a0 = lo & 0x7FFFu, a1 = hi & 0x7FFFu;
-            const uint32_t m = row16_max_u32(a0 > a1 ? a0 : a1);
-            uint32_t sbyte;
-            const float s = mx_scale_of<FMT>(m, sbyte);
-            reinterpret_cast<uint16_t*>(q + (r0 + r) * cols + c0)[lane] = (uint16_t)mx_code2<FMT>(lo, hi, s);
-            if ((lane & 15) == 0) sq[(g4 * rows + r0 + r) * 4 + bi] = (uint8_t)sbyte;
-            __builtin_amdgcn_sched_barrier(0);
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t lo = wr[k] & 0x7FFFu, hi = (wr[k] >> 16) & 0x7FFFu;
+                    m = m > lo ? m : lo;
+                    m = m > hi ? m : hi;
+                }
+                uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x124, 0xF, 0xF, false);
+                m = m > o ? m : o;
+                o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x128, 0xF, 0xF, false);
+                m = m > o ? m : o;
+                uint32_t sb;
+                const float s = mx_scale_of<FMT>(m, sb);
+                uint32_t c[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    c[h] = mx_code2<FMT>(wr[2 * h] & 0xFFFFu, wr[2 * h] >> 16, s) |
+                           (mx_code2<FMT>(wr[2 * h + 1] & 0xFFFFu, wr[2 * h + 1] >> 16, s) << 16);
+                *reinterpret_cast<uint2*>(qrow + j * cols) = make_uint2(c[0], c[1]);
+                if ((g & 3) == 0) sr[(rt + j) * 4 + (g >> 2)] = (uint8_t)sb;
+            }
+#pragma unroll 1
+            for (int k = 0; k < 4; ++k) {
+                uint32_t col[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) col[j] = reinterpret_cast<const uint32_t*>(x + off + j * cols)[k];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int sh = 16 * h;
+                    uint32_t m = 0;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const uint32_t e = (col[j] >> sh) & 0x7FFFu;
+                        m = m > e ? m : e;
+                    }
+                    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false);
+                    m = m > o ? m : o;
+                    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false);
+                    m = m > o ? m : o;
+                    uint32_t sb;
+                    const float s = mx_scale_of<FMT>(m, sb);
+                    uint32_t c[2];
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        const int j = 4 * r;
+                        c[r] = mx_code2<FMT>((col[j] >> sh) & 0xFFFFu, (col[j + 1] >> sh) & 0xFFFFu, s) |
+                               (mx_code2<FMT>((col[j + 2] >> sh) & 0xFFFFu, (col[j + 3] >> sh) & 0xFFFFu, s) << 16);
+                    }
+                    *reinterpret_cast<uint2*>(lds_qt + (2 * k + h) * kQtEdge) = make_uint2(c[0], c[1]);
+                    if (rq == 0) sc[(8 * g + 2 * k + h) * 4 + wave] = (uint8_t)sb;
+                }
+            }
         }
+        __syncthreads();
+        // write-out: 1024 pieces of 16 bytes, 4 per thread (a wave instruction covers
+        // 8 qt rows x 128 bytes), then the two 512-byte scale runs
+        const int p = tid & 7;
+        uint8_t* const qtp = qt + (C0 + (tid >> 3)) * rows + R0 + p * 16;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int col = u * 32 + (tid >> 3);
+            const u32x4 piece16 = *reinterpret_cast<const u32x4*>(tile + col * kQtEdge + ((p ^ ((col >> 3) & 7)) * 16));
+            *reinterpret_cast<u32x4*>(qtp + (int64_t)u * 32 * rows) = piece16;
+        }
+        // sq dword (tc rows + R0 + r): row r's four blocks of this column group;
+        // sqt dword (tr cols + C0 + col): column col's four blocks of this row band
+        if (tid < kQtEdge)
+            sq[(int64_t)tc * rows + R0 + tid] = srow[tid];
+        else
+            sqt[(int64_t)tr * cols + C0 + (tid - kQtEdge)] = scol[tid - kQtEdge];
     }
 }
 
 hipError_t launch_mx_quantize_both(const void* x, int64_t rows, int64_t cols, int fmt, uint8_t* q, uint8_t* sq,
                                    uint8_t* qt, uint8_t* sqt, hipStream_t stream)
 {
-    const int64_t tiles = (rows / 32) * (cols / 128);
-    int64_t blocks = (tiles + 3) / 4;
-    const int64_t cap = (int64_t)device_cu_count() * 8;
+    const int64_t tiles = (rows / kQtEdge) * (cols / kQtEdge);
+    int64_t blocks = tiles;
+    const int64_t cap = (int64_t)device_cu_count() * 4;
     if (blocks > cap) blocks = cap;
-    const uint32_t* xv = reinterpret_cast<const uint32_t*>(x);
+    const uint16_t* xv = reinterpret_cast<const uint16_t*>(x);
+    uint32_t* sqv = reinterpret_cast<uint32_t*>(sq);
+    uint32_t* sqtv = reinterpret_cast<uint32_t*>(sqt);
     const bool nt = 2 * rows * cols >= kAbsStreamBytes;
     const dim3 grid((unsigned)blocks), block(256);
     if (fmt == 0)
-        return nt ? launch(mx_quantize_both_kernel<0, true>, grid, block, stream, xv, rows, cols, q, sq, qt, sqt)
-                  : launch(mx_quantize_both_kernel<0, false>, grid, block, stream, xv, rows, cols, q, sq, qt, sqt);
-    return nt ? launch(mx_quantize_both_kernel<1, true>, grid, block, stream, xv, rows, cols, q, sq, qt, sqt)
-              : launch(mx_quantize_both_kernel<1, false>, grid, block, stream, xv, rows, cols, q, sq, qt, sqt);
+        return nt ? launch(mx_quantize_both_kernel<0, true>, grid, block, stream, xv, rows, cols, q, sqv, qt, sqtv)
+                  : launch(mx_quantize_both_kernel<0, false>, grid, block, stream, xv, rows, cols, q, sqv, qt, sqtv);
+    return nt ? launch(mx_quantize_both_kernel<1, true>, grid, block, stream, xv, rows, cols, q, sqv, qt, sqtv)
+              : launch(mx_quantize_both_kernel<1, false>, grid, block, stream, xv, rows, cols, q, sqv, qt, sqtv);
 }
 
 

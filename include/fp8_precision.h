@@ -401,8 +401,8 @@ fp8_status fp8_mx_quantize_t(const void* x, int64_t rows, int64_t cols, fp8_fmt 
  * the bytes of the two calls.
  *
  *   x        bf16 [rows, cols], 16-byte aligned
- *   q, sq    u8 [rows, cols] (16-byte aligned) and [cols / 128][rows][4]
- *   qt, sqt  u8 [cols, rows] (16-byte aligned) and [rows / 128][cols][4]
+ *   q, sq    u8 [rows, cols] (16-byte aligned) and [cols / 128][rows][4] (4-byte aligned)
+ *   qt, sqt  u8 [cols, rows] (16-byte aligned) and [rows / 128][cols][4] (4-byte aligned)
  * Constraints: rows % 128 == 0 and cols % 128 == 0 (else FP8_ERR_UNSUPPORTED);
  * buffers must not overlap.
  */

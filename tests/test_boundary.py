@@ -418,3 +418,5 @@ def test_mx_quantize_both_validation(lib):
     assert f(A16, 128, 128, 0, q, sq, q + 64, sqt, None) == INVALID    # qt over q
     assert f(A16, 128, 96, 0, q, sq, qt, sqt, None) == UNSUPPORTED
     assert f(A16, 128, 128, 0, q + 8, sq, qt, sqt, None) == UNSUPPORTED
+    assert f(A16, 128, 128, 0, q, sq + 2, qt, sqt, None) == UNSUPPORTED     # misaligned scales
+    assert f(A16, 128, 128, 0, q, sq, qt, sqt + 1, None) == UNSUPPORTED

@@ -283,6 +283,57 @@ def test_mx_backward_products(fp8, orc):
     mx_bound_check(dw, ref, a, sa, E5, b, sb, np.arange(N, dtype=np.int64), "mx wgrad")
 
 
+def planted_finite_blocks(seed):
+    """A finite 256 x 256 bf16 tensor whose row and column blocks hit the edges of
+    the block rule: all-zero and all-subnormal 32 x 32 squares, block maxima at
+    the smallest normal, at and just past the magnitudes where an E4M3 (464 2^e)
+    or E5M2 (61440 2^e) code would round past the largest finite one, at and just
+    below powers of two, the largest finite bf16, with either sign."""
+    rng = np.random.default_rng(seed)
+    bits = workloads.bf16_bits(workloads.draw(seed, 1, (256, 256), 2.0))
+    bits[32:64, 64:96] = 0
+    sub = rng.integers(1, 0x80, size=(32, 32), dtype=np.uint16)
+    bits[64:96, 128:160] = sub | (rng.integers(0, 2, size=(32, 32), dtype=np.uint16) << 15)
+    maxima = [0x0080, 0x43E8, 0x43E9, 0x43E7, 0xC3E9, 0x4770, 0x476F, 0x4771, 0xC770, 0x4380, 0x437F,
+              0x7F7F, 0xFF7F, 0x3F80, 0x3F7F, 0x0100]
+    small = lambda shape, m: (rng.integers(0, max(m & 0x7FFF, 1), size=shape, dtype=np.uint16)
+                              | (rng.integers(0, 2, size=shape, dtype=np.uint16) << 15))
+    for i, m in enumerate(maxima):
+        # a row block (row 128 + i, columns 32 .. 63) and a column block (column 160 + i,
+        # rows 192 .. 223) with small values and one planted maximum at a varying place
+        r = 128 + i
+        bits[r, 32:64] = small(32, m)
+        bits[r, 32 + (5 * i) % 32] = m
+        c = 160 + i
+        bits[192:224, c] = small(32, m)
+        bits[192 + (7 * i) % 32, c] = m
+    return bits
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_mx_quantize_both_planted_blocks(fp8, orc, fmt):
+    """Finite tiles (the scaled-conversion path) at the block rule's edges: bit for bit the oracle's."""
+    bits = planted_finite_blocks(91 + fmt)
+    say("mx_quantize_both planted", fmt)
+    q, sq, qt, sqt = fp8.mx_quantize_both(to_dev(bits), fmt)
+    torch.cuda.synchronize()
+    q_r, sq_r = orc.mx_quantize(np.ascontiguousarray(bits), fmt)
+    qt_r, sqt_r = orc.mx_quantize(np.ascontiguousarray(bits.T), fmt)
+    assert np.array_equal(u8(sq), step_major(sq_r)), "row-block scales"
+    assert np.array_equal(u8(sqt), step_major(sqt_r)), "column-block scales"
+    assert_codes_equal(u8(q), q_r, fmt, "q")
+    assert_codes_equal(u8(qt), qt_r, fmt, "qt")
+    # the same tensor with one NaN: its wave takes the per-element rule, the others not
+    bits[100, 77] = 0x7FC1
+    q, sq, qt, sqt = fp8.mx_quantize_both(to_dev(bits), fmt)
+    torch.cuda.synchronize()
+    q_r, sq_r = orc.mx_quantize(np.ascontiguousarray(bits), fmt)
+    qt_r, sqt_r = orc.mx_quantize(np.ascontiguousarray(bits.T), fmt)
+    assert np.array_equal(u8(sq), step_major(sq_r)) and np.array_equal(u8(sqt), step_major(sqt_r)), "scales"
+    assert_codes_equal(u8(q), q_r, fmt, "q with a NaN")
+    assert_codes_equal(u8(qt), qt_r, fmt, "qt with a NaN")
+
+
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
 @pytest.mark.parametrize("rows,cols", [(512, 128), (384, 1280), (4096, 4096)])
 def test_mx_quantize_both_matches_the_two_calls(fp8, orc, fmt, rows, cols):
