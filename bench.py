@@ -633,7 +633,7 @@ def mx_layer(fp8, dev, cfg_name="layer7b", reps=10):
     (with the transposed copy) of dY, the dgrad + wgrad launch.  MX: fp8_mx_quantize_both
     of X and of W (the forward blocking and, from the same read, the blocking along the
     backward reductions), the block-scaled forward; fp8_mx_quantize_both of dY (e5m2),
-    the block-scaled dgrad and wgrad.  Inputs drawn by workloads.py; the two paths
+    the block-scaled dgrad + wgrad launch.  Inputs drawn by workloads.py; the two paths
     interleaved, `reps` rounds, an event pair around every call, medians."""
     cfg = workloads.CONFIGS[cfg_name]
     E4, E5 = fp8.E4M3, fp8.E5M2
@@ -675,11 +675,10 @@ def mx_layer(fp8, dev, cfg_name="layer7b", reps=10):
             "mx_w": lambda: fp8.mx_quantize_both(w, E4, mwq, sw, mwt, swt),
             "mx_fwd": lambda: fp8.mx_gemm_fwd(mxq, sx, mwq, sw, E4, out=y),
             "mx_dy": lambda: fp8.mx_quantize_both(dy, E5, mdq, sdq, mdt, sdt),
-            "mx_dgrad": lambda: fp8.mx_gemm_fwd(mdq, sdq, mwt, swt, E5, out=dx),
-            "mx_wgrad": lambda: fp8.mx_gemm_fwd(mdt, sdt, mxt, sxt, E5, out=dw),
+            "mx_bwd": lambda: fp8.mx_gemm_backward(mdq, sdq, mdt, sdt, mwt, swt, mxt, sxt, E5, dx=dx, dw=dw),
         }
         order = [["pt_abs", "pt_quant", "pt_fwd", "pt_dyabs", "pt_dyquant", "pt_bwd"],
-                 ["mx_x", "mx_w", "mx_fwd", "mx_dy", "mx_dgrad", "mx_wgrad"]]
+                 ["mx_x", "mx_w", "mx_fwd", "mx_dy", "mx_bwd"]]
         t = {k: [] for k in calls}
         for r in range(reps + 2):
             for seq in order:
@@ -701,7 +700,7 @@ def mx_layer(fp8, dev, cfg_name="layer7b", reps=10):
              "pt_qb": md["pt_dyabs"] + md["pt_dyquant"], "pt_gb": md["pt_bwd"],
              "mx_qf": md["mx_x"] + md["mx_w"], "mx_gf": md["mx_fwd"],
              "mx_qb": md["mx_dy"],
-             "mx_gb": md["mx_dgrad"] + md["mx_wgrad"], "ff": ff, "fb": fb,
+             "mx_gb": md["mx_bwd"], "ff": ff, "fb": fb,
              "bf": (M + N) * K, "bb": M * N}
         for k in tot:
             tot[k] += v[k]

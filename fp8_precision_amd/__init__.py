@@ -8,5 +8,5 @@ from ._lib import (  # noqa: F401
     absmax, absmax_accumulate_many, quantize, quantize_many, swiglu_requant, swiglu_backward, gemm_fwd, gemm_fwd_swiglu_absmax, gemm_dgrad, gemm_wgrad,
     gemm_backward,
     gemm_dgrad_mn, gemm_wgrad_mn, gemm_backward_mn, stream_copy, mx_quantize, mx_gemm_fwd,
-    mx_swiglu_requant, mx_quantize_t, mx_quantize_both,
+    mx_swiglu_requant, mx_quantize_t, mx_quantize_both, mx_gemm_backward,
 )

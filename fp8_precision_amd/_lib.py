@@ -45,6 +45,7 @@ _SIGS = {
     "fp8_stream_copy": (_i32, [_vp, _vp, _i64, _vp]),
     "fp8_mx_quantize": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "fp8_mx_gemm_fwd": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "fp8_mx_gemm_backward": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fp8_mx_swiglu_requant": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "fp8_mx_quantize_t": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "fp8_mx_quantize_both": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp]),
@@ -550,6 +551,39 @@ def mx_gemm_fwd(xq, sx, wq, sw, x_fmt: int = E4M3, out=None) -> torch.Tensor:
     _run("fp8_mx_gemm_fwd", _lib.fp8_mx_gemm_fwd, (xq, sx, wq, sw, out), _ptr(xq), _ptr(sx), int(x_fmt), _ptr(wq),
          _ptr(sw), _ptr(out), M, N, K)
     return out
+
+
+def mx_gemm_backward(dyq, sdy, dyqt, sdyt, wqt, swt, xqt, sxt, dy_fmt: int = E5M2, dx=None, dw=None):
+    """Both backward products of a linear on block-scaled operands in one launch
+    (fp8_mx_gemm_backward): dX [M, K] from dyq [M, N] (scales [N / 128, M, 4], from
+    mx_quantize of dY) and wqt [K, N] (scales [N / 128, K, 4], mx_quantize_t of W);
+    dW [N, K] from dyqt [N, M] (scales [M / 128, N, 4], mx_quantize_t of dY) and
+    xqt [K, M] (scales [M / 128, K, 4], mx_quantize_t of X).  Returns (dx, dw)."""
+    names = ("dyq", "sdy", "dyqt", "sdyt", "wqt", "swt", "xqt", "sxt")
+    ts = (dyq, sdy, dyqt, sdyt, wqt, swt, xqt, sxt)
+    for t, n in zip(ts, names):
+        _dev_tensor(t, n, torch.uint8)
+    if dyq.dim() != 2 or dyqt.dim() != 2 or wqt.dim() != 2 or xqt.dim() != 2:
+        raise ValueError("codes must be 2-D")
+    M, N = dyq.shape
+    K = wqt.shape[0]
+    if tuple(dyqt.shape) != (N, M) or tuple(wqt.shape) != (K, N) or tuple(xqt.shape) != (K, M):
+        raise ValueError("expected dyq [M, N], dyqt [N, M], wqt [K, N], xqt [K, M]")
+    for t, n, size in ((sdy, "sdy", M * N // 32), (sdyt, "sdyt", M * N // 32), (swt, "swt", K * N // 32),
+                       (sxt, "sxt", K * M // 32)):
+        if t.numel() != size:
+            raise ValueError(f"{n} has the wrong size")
+    if dx is None:
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dyq.device)
+    if dw is None:
+        dw = torch.empty((N, K), dtype=torch.bfloat16, device=dyq.device)
+    for t, n, size in ((dx, "dx", M * K), (dw, "dw", N * K)):
+        _dev_tensor(t, n, torch.bfloat16)
+        if t.numel() != size:
+            raise ValueError(f"{n} has the wrong size")
+    _run("fp8_mx_gemm_backward", _lib.fp8_mx_gemm_backward, ts + (dx, dw), _ptr(dyq), _ptr(sdy), _ptr(dyqt),
+         _ptr(sdyt), int(dy_fmt), _ptr(wqt), _ptr(swt), _ptr(xqt), _ptr(sxt), _ptr(dx), _ptr(dw), M, N, K)
+    return dx, dw
 
 
 def stream_copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:

@@ -548,6 +548,38 @@ fp8_status fp8_mx_gemm_fwd(const uint8_t* xq, const uint8_t* sx, fp8_fmt x_fmt, 
     return FP8_OK;
 }
 
+fp8_status fp8_mx_gemm_backward(const uint8_t* dyq, const uint8_t* sdy, const uint8_t* dyqt, const uint8_t* sdyt,
+                                fp8_fmt dy_fmt, const uint8_t* wqt, const uint8_t* swt, const uint8_t* xqt,
+                                const uint8_t* sxt, void* dx, void* dw, int64_t M, int64_t N, int64_t K,
+                                hipStream_t stream)
+{
+    t_last_error.clear();
+    const char* name = "fp8_mx_gemm_backward";
+    if (!sdy || !sdyt || !swt || !sxt) return fail(FP8_ERR_INVALID, "fp8_mx_gemm_backward: null scales");
+    fp8_status st = gemm_common("fp8_mx_gemm_backward (dgrad)", dyq, (int)dy_fmt, wqt, nullptr, nullptr, dx, M, K, N,
+                                stream, false);
+    if (st != FP8_OK) return st;
+    st = gemm_common("fp8_mx_gemm_backward (wgrad)", dyqt, (int)dy_fmt, xqt, nullptr, nullptr, dw, N, K, M, stream,
+                     false);
+    if (st != FP8_OK) return st;
+    if (M < 256 || N < 256 || K < 256)
+        return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_gemm_backward: M, N and K must be at least 256");
+    if (!aligned(sdy, 4) || !aligned(sdyt, 4) || !aligned(swt, 4) || !aligned(sxt, 4))
+        return fail(FP8_ERR_UNSUPPORTED, "fp8_mx_gemm_backward: misaligned scales");
+    if (overlap(dx, 2 * M * K, dw, 2 * N * K)) return fail(FP8_ERR_INVALID, "fp8_mx_gemm_backward: dx and dw overlap");
+    const Range outs[] = {{dx, 2 * M * K}, {dw, 2 * N * K}};
+    const Range ins[] = {{dyq, M * N},       {dyqt, M * N},       {wqt, K * N},       {xqt, K * M},
+                         {sdy, M * N / 32}, {sdyt, M * N / 32}, {swt, K * N / 32}, {sxt, K * M / 32}};
+    for (const Range& o : outs)
+        for (const Range& i : ins)
+            if (overlap(o.p, o.n, i.p, i.n))
+                return fail(FP8_ERR_INVALID, "fp8_mx_gemm_backward: an output overlaps an input");
+    hipError_t e = fp8k::launch_gemm_mx_pair(dyq, sdy, wqt, swt, dx, M, K, N, dyqt, sdyt, xqt, sxt, dw, N, K, M,
+                                             (int)dy_fmt, stream);
+    if (e != hipSuccess) return fail_hip(name, e);
+    return FP8_OK;
+}
+
 fp8_status fp8_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream)
 {
     t_last_error.clear();

@@ -51,6 +51,14 @@ hipError_t launch_absmax_many(int count, const void* const* x, const int64_t* n,
 hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* sa, int fmt_a, const uint8_t* B, const uint8_t* sb,
                           int fmt_b, void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream);
 
+// Two independent block-scaled products in one launch (the dgrad and wgrad
+// products of a linear, A in format fmt_a, B in E4M3), both outputs stored
+// non-temporally; each problem as launch_gemm_mx.
+hipError_t launch_gemm_mx_pair(const uint8_t* A0, const uint8_t* sa0, const uint8_t* B0, const uint8_t* sb0,
+                               void* out0, int64_t P0, int64_t Q0, int64_t R0, const uint8_t* A1,
+                               const uint8_t* sa1, const uint8_t* B1, const uint8_t* sb1, void* out1, int64_t P1,
+                               int64_t Q1, int64_t R1, int fmt_a, hipStream_t stream);
+
 // Transposed block (MX) quantisation: qt [cols, rows] = the codes of x^T with
 // blocks of 32 along qt's rows (32 consecutive rows of a column of x), scales
 // step-major [rows / 128][cols][4]; rows and cols multiples of 128.

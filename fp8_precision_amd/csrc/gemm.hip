@@ -101,6 +101,7 @@ constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitVm16 = 0x4F70;
 constexpr int kWaitVm18 = 0x4F72;
 constexpr int kWaitVm12 = 0x0F7C;
+constexpr int kWaitVm14 = 0x0F7E;
 
 // Operand layouts.
 constexpr int kKMajor = 0;
@@ -240,11 +241,12 @@ __device__ __forceinline__ void issue_stage(const Sources& src, uint32_t stage, 
 }
 
 // Block-scaled launches: the scale loads of a stage for one wave -- `which` 0: the
-// scales of A rows 64 w .. 64 w + 63, 1: those of B rows (LDS: A rows at 4 r,
-// B rows at 1024 + 4 r of the scale stage).
-__device__ __forceinline__ void issue_scale(const Sources& src, uint32_t sc_stage, int kt, int wave, int which)
+// scales of A rows 64 s .. 64 s + 63, 1: those of B rows (LDS: A rows at 4 r,
+// B rows at 1024 + 4 r of the scale stage); s is the wave's slot (the wave
+// itself, or wave % 2 for the 128 A rows of a half tile).
+__device__ __forceinline__ void issue_scale(const Sources& src, uint32_t sc_stage, int kt, int s, int which)
 {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(sc_stage + (uint32_t)(which * 1024 + wave * 256));
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(sc_stage + (uint32_t)(which * 1024 + s * 256));
     if (which == 0)
         dma4(src.sa_off, src.sa + (size_t)kt * src.sa_step, lds);
     else
@@ -277,6 +279,18 @@ __device__ __forceinline__ void issue_half_stage(const Sources& src, uint32_t st
 {
 #pragma unroll
     for (int idx = 0; idx < 12; ++idx) issue_half(src, stage, kt, wave, idx);
+}
+
+// A block-scaled half tile's stage: the 12 operand loads, then the scales of its
+// 128 A rows (waves 0 and 1 load them; waves 2 and 3 load the same rows into the
+// same LDS bytes again, so that every wave issues 14 loads per stage and one
+// vmcnt count serves all of them) and of its 256 B rows.
+__device__ __forceinline__ void issue_half_stage_mx(const Sources& src, uint32_t stage, uint32_t sc_stage, int kt,
+                                                    int wave)
+{
+    issue_half_stage(src, stage, kt, wave);
+    issue_scale(src, sc_stage, kt, wave & 1, 0);
+    issue_scale(src, sc_stage, kt, wave, 1);
 }
 
 // Fragments of the 16x16x128 instruction: block b covers 16 rows of A (or of
@@ -450,6 +464,31 @@ __device__ __forceinline__ void read_scales(const uint8_t* sc_stage, int wm, int
     uint32_t raw[8];
     load_scale_bytes(sc_stage + wm * 512, lane, raw);
     pack_scale_bytes(raw, sa);
+    load_scale_bytes(sc_stage + 1024 + wn * 512, lane, raw);
+    pack_scale_bytes(raw, sb);
+}
+
+// Half tiles: a wave's 4 A blocks are rows 64 wm + 16 i + lane % 16 (i = 0..3),
+// one scale register (sa[1] is a copy, never selected).
+__device__ __forceinline__ void load_scale_bytes4(const uint8_t* rows, int lane, uint32_t (&raw)[4])
+{
+    const uint8_t* p = rows + (lane & 15) * 4 + (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = p[64 * i];
+}
+
+__device__ __forceinline__ void pack_scale_bytes4(const uint32_t (&raw)[4], uint32_t (&s)[2])
+{
+    s[0] = raw[0] | (raw[1] << 8) | (raw[2] << 16) | (raw[3] << 24);
+    s[1] = s[0];
+}
+
+__device__ __forceinline__ void read_scales_half(const uint8_t* sc_stage, int wm, int wn, int lane,
+                                                 uint32_t (&sa)[2], uint32_t (&sb)[2])
+{
+    uint32_t r4[4], raw[8];
+    load_scale_bytes4(sc_stage + wm * 256, lane, r4);
+    pack_scale_bytes4(r4, sa);
     load_scale_bytes(sc_stage + 1024 + wn * 512, lane, raw);
     pack_scale_bytes(raw, sb);
 }
@@ -632,6 +671,91 @@ __device__ __forceinline__ void tile_mainloop_half(v4f (&acc)[8][8], v8i (&bq)[8
     __syncthreads();
 }
 
+// A block-scaled half tile: the steps of tile_mainloop_half with the scales of
+// tile_mainloop_mx.  Each step also reads the next step's scales (from the stage
+// that the step's barrier has seen land: A bytes at t = 2, packed at t = 6; B
+// bytes at t = 10, packed at t = 14) and issues the two scale loads of the tile
+// two steps ahead beside its 12 operand loads (at t = 5 and 21).
+template <int FA, int FB, bool NEXT>
+__device__ __forceinline__ void half_step_mx(v4f (&acc)[8][8], v8i (&bq)[8], const v8i (&ac)[4], v8i (&an)[4],
+                                             const Sources& src, uint32_t cur_addr, uint32_t cur_sc,
+                                             const uint8_t* nxt, const uint8_t* nxt_sc, int kt_issue, int wave,
+                                             int wm, int wn, int lane, const uint32_t (&sa)[2],
+                                             const uint32_t (&sb)[2], uint32_t (&na)[2], uint32_t (&nb)[2])
+{
+    uint32_t r4[4], raw[8];
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+        const int j = t >> 2, i = t & 3;
+        mma16_mx<FA, FB>(acc, ac[i], bq[j], i, j, sa, sb);
+        if (NEXT) {
+            if (i == 3) bq[j] = frag_k(nxt + kStageA, wn * 8 + j, lane);
+            if ((t & 7) == 1) an[t >> 3] = frag_k(nxt, wm * 4 + (t >> 3), lane);
+            if ((t & 1) == 0 && t < 24) issue_half(src, cur_addr, kt_issue, wave, t >> 1);
+            if (t == 5) issue_scale(src, cur_sc, kt_issue, wave & 1, 0);
+            if (t == 21) issue_scale(src, cur_sc, kt_issue, wave, 1);
+            if (t == 2) load_scale_bytes4(nxt_sc + wm * 256, lane, r4);
+            if (t == 6) pack_scale_bytes4(r4, na);
+            if (t == 10) load_scale_bytes(nxt_sc + 1024 + wn * 512, lane, raw);
+            if (t == 14) pack_scale_bytes(raw, nb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int FA, int FB>
+__device__ __forceinline__ void tile_mainloop_half_mx(v4f (&acc)[8][8], v8i (&bq)[8], v8i (&a0)[4], v8i (&a1)[4],
+                                                      const Sources& src, uint8_t* lds, uint32_t lds_addr,
+                                                      uint8_t* sc, uint32_t sc_addr, int KT, int wave, int wm,
+                                                      int wn, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
+    __builtin_amdgcn_s_waitcnt(kWaitVm14);    // stage 0 landed; stage 1's 14 loads may be in flight
+    __syncthreads();
+    uint32_t sa[2], sb[2], na[2], nb[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bq[j] = frag_k(lds + kStageA, wn * 8 + j, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a0[i] = frag_k(lds, wm * 4 + i, lane);
+    read_scales_half(sc, wm, wn, lane, sa, sb);
+    auto take = [&]() {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            sa[h] = na[h];
+            sb[h] = nb[h];
+        }
+    };
+    int kt = 0;
+    for (; kt + 2 < KT; kt += 2) {            // steps kt (even stage) and kt + 1 (odd stage)
+        mid_step_barrier();
+        half_step_mx<FA, FB, true>(acc, bq, a0, a1, src, lds_addr, sc_addr, lds + kStage, sc + kScStage, kt + 2,
+                                   wave, wm, wn, lane, sa, sb, na, nb);
+        take();
+        mid_step_barrier();
+        half_step_mx<FA, FB, true>(acc, bq, a1, a0, src, lds_addr + kStage, sc_addr + kScStage, lds, sc,
+                                   min(kt + 3, KT - 1), wave, wm, wn, lane, sa, sb, na, nb);
+        take();
+    }
+    if (kt + 1 < KT) {                        // two steps left
+        mid_step_barrier();
+        half_step_mx<FA, FB, true>(acc, bq, a0, a1, src, lds_addr, sc_addr, lds + kStage, sc + kScStage, KT - 1,
+                                   wave, wm, wn, lane, sa, sb, na, nb);
+        take();
+        mid_step_barrier();
+        half_step_mx<FA, FB, false>(acc, bq, a1, a0, src, 0, 0, lds, sc, 0, wave, wm, wn, lane, sa, sb, na, nb);
+    } else {                                  // one step left
+        mid_step_barrier();
+        half_step_mx<FA, FB, false>(acc, bq, a0, a1, src, 0, 0, lds, sc, 0, wave, wm, wn, lane, sa, sb, na, nb);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+}
+
 // A launch covers a group of up to kMaxGroup independent problems of the same
 // operand formats (e.g. the dgrad and wgrad products of one linear).  Their
 // tiles form one virtual tile range, problem after problem; the host orders
@@ -650,6 +774,8 @@ struct GemmProblem {
     int tiles_m, tiles_n;
     int group_m;          // tile rows per raster group
     int first_tile;
+    const uint8_t* sa;    // block-scaled launches: E8M0 scales of A, [R / 128][P][4]
+    const uint8_t* sb;    // and of B, [R / 128][Q][4]
 };
 
 struct GemmGroup {
@@ -662,8 +788,6 @@ struct GemmGroup {
                           // full_units + 2 k + h is half h of tile full_units + k
     int first_unit;       // this launch walks units first_unit .. units - 1
     int units;
-    const uint8_t* sa;    // block-scaled launches (one problem): E8M0 scales [P][R / 32]
-    const uint8_t* sb;    // and [Q][R / 32]
 };
 
 // Everything a workgroup needs about its current tile (all wave-uniform).
@@ -778,24 +902,38 @@ __device__ __forceinline__ void start_tile(Sources& src, const Work& w, uint32_t
 }
 
 // Block-scaled launches (K-major operands, tiles inside the matrices): set up
-// the sources of tile w and issue its first two stages with their scales.
+// the sources of unit w (a tile, or a 128-row half tile) and issue its first
+// two stages with their scales.
+template <bool HALF>
 __device__ __forceinline__ void start_tile_mx(Sources& src, const GemmGroup& g, const Work& w, uint32_t lds_addr,
                                               uint32_t sc_addr, int wave, int lane)
 {
-    set_sources<kKMajor, kKMajor>(src, w, wave, lane);
-    src.sa = g.sa;
-    src.sb = g.sb;
+    const GemmProblem& pr = w.prob ? g.p[1] : g.p[0];
+    if (HALF)
+        set_op<kKMajor>(src.a, w.A, w.m0, w.P, w.R, wave, lane, 32);
+    else
+        set_op<kKMajor>(src.a, w.A, w.m0, w.P, w.R, wave, lane);
+    set_op<kKMajor>(src.b, w.B, w.n0, w.Q, w.R, wave, lane);
+    src.sa = pr.sa;
+    src.sb = pr.sb;
     // the lane number recomputed here (volatile, so it is not hoisted): held live
     // across the persistent loop, the allocator spilled it, and the reload's wait
     // here was a wait for the whole first stage just issued
     int ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-    src.sa_off = (uint32_t)(w.m0 + wave * 64 + ln) * 4u;     // one row's 4 scales of a step
+    // one row's 4 scales of a step; a half tile's 128 A rows are loaded by
+    // waves 0 and 1 and again, identically, by waves 2 and 3
+    src.sa_off = (uint32_t)(w.m0 + (HALF ? (wave & 1) : wave) * 64 + ln) * 4u;
     src.sb_off = (uint32_t)(w.n0 + wave * 64 + ln) * 4u;
     src.sa_step = (uint32_t)w.P * 4u;
     src.sb_step = (uint32_t)w.Q * 4u;
-    issue_stage_mx(src, lds_addr, sc_addr, 0, wave);
-    issue_stage_mx(src, lds_addr + kStage, sc_addr + kScStage, min(1, w.KT - 1), wave);
+    if (HALF) {
+        issue_half_stage_mx(src, lds_addr, sc_addr, 0, wave);
+        issue_half_stage_mx(src, lds_addr + kStage, sc_addr + kScStage, min(1, w.KT - 1), wave);
+    } else {
+        issue_stage_mx(src, lds_addr, sc_addr, 0, wave);
+        issue_stage_mx(src, lds_addr + kStage, sc_addr + kScStage, min(1, w.KT - 1), wave);
+    }
 }
 
 // A 16-byte output store; NT: non-temporal, for the backward products' dX and dW:
@@ -889,7 +1027,7 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[8][8], const Work& don
 // Epilogue of a block-scaled tile: as epilogue() above (no descale: the block
 // scales are inside the sums), staging 16-row chunks (one A block) in a 4 KB
 // LDS region per wave.
-template <bool NT>
+template <bool HALF, bool NT>
 __device__ __forceinline__ void epilogue_mx(const v4f (&acc)[8][8], const Work& done, uint8_t* epi, int wave,
                                             int wm, int wn, int lane)
 {
@@ -897,10 +1035,11 @@ __device__ __forceinline__ void epilogue_mx(const v4f (&acc)[8][8], const Work& 
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int r16 = ln & 15, q4 = ln >> 4;
-    const int wrow = done.m0 + wm * 128;
-    const bool full = done.ms == done.m0 && done.ns == done.n0 && done.m0 + kBM <= done.P && done.n0 + kBN <= done.Q;
+    const int wrow = done.m0 + wm * (HALF ? 64 : 128);
+    const bool full = done.ms == done.m0 && done.ns == done.n0 && done.m0 + (HALF ? kBM / 2 : kBM) <= done.P &&
+                      done.n0 + kBN <= done.Q;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {                          // chunk: A block i (16 rows)
+    for (int i = 0; i < (HALF ? 4 : 8); ++i) {             // chunk: A block i (16 rows)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const f32x2 v01 = {acc[i][j][0], acc[i][j][1]};
@@ -1130,12 +1269,12 @@ __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
 }
 
 // Block-scaled (MX) products: the persistent walk of gemm_tn_kernel (XCD-major
-// slots, grouped raster, next tile's first stages issued before the epilogue)
-// over full-size tiles of K-major operands, with each operand row's E8M0 block
+// slots, grouped raster, problem groups, next tile's first stages issued before
+// the epilogue, a balanced last round of half tiles in a launch of its own:
+// HALF) over tiles of K-major operands, with each operand row's E8M0 block
 // scales loaded beside its codes and applied by the matrix instruction; the
-// output is the bf16 of the fp32 sums (no per-tensor factor).  No half-tile
-// round: a launch's last partial round runs as full tiles.
-template <int FA, int FB, bool NT>
+// output is the bf16 of the fp32 sums (no per-tensor factor).
+template <int FA, int FB, bool HALF, bool NT>
 __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(const GemmGroup g)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
@@ -1158,20 +1297,24 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(const GemmGroup g)
 
     int v = g.first_unit + slot;
     if (v >= g.units) return;
-    Work w = work_of<false, false, false>(g, v);
-    start_tile_mx(src, g, w, lds_addr, sc_addr, wave, lane);
+    Work w = work_of<false, HALF, false>(g, v);
+    start_tile_mx<HALF>(src, g, w, lds_addr, sc_addr, wave, lane);
     for (;;) {
-        tile_mainloop_mx<FA, FB>(acc, bq, alo, ahi, src, lds, lds_addr, sc, sc_addr, w.KT, wave, wm, wn, lane);
+        if (HALF)
+            tile_mainloop_half_mx<FA, FB>(acc, bq, alo, ahi, src, lds, lds_addr, sc, sc_addr, w.KT, wave, wm, wn,
+                                          lane);
+        else
+            tile_mainloop_mx<FA, FB>(acc, bq, alo, ahi, src, lds, lds_addr, sc, sc_addr, w.KT, wave, wm, wn, lane);
         const Work done = w;
         const int next = v + G;
         if (next < g.units) {
             v = next;
-            w = work_of<false, false, false>(g, v);
-            start_tile_mx(src, g, w, lds_addr, sc_addr, wave, lane);
+            w = work_of<false, HALF, false>(g, v);
+            start_tile_mx<HALF>(src, g, w, lds_addr, sc_addr, wave, lane);
         }
-        epilogue_mx<NT>(acc, done, epi, wave, wm, wn, lane);
-        // the loop-top wait (vmcnt <= 18) then proves the next tile's first stage
-        // has landed, as in gemm_tn_kernel
+        epilogue_mx<HALF, NT>(acc, done, epi, wave, wm, wn, lane);
+        // the loop-top wait (vmcnt <= 18, or 14 for a half tile) then proves the
+        // next unit's first stage has landed, as in gemm_tn_kernel
         if (next >= g.units) break;
     }
 }
@@ -1179,7 +1322,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(const GemmGroup g)
 static GemmProblem make_problem(const uint8_t* A, int la, const uint8_t* B, int lb, const float* inv_a,
                                 const float* inv_b, void* out, int64_t P, int64_t Q, int64_t R)
 {
-    GemmProblem p;
+    GemmProblem p{};
     p.A = A;
     p.B = B;
     p.inv_a = inv_a;
@@ -1285,22 +1428,76 @@ hipError_t launch_gemm_gate_up(const uint8_t* A, const uint8_t* B, const float* 
     return launch_group<0, 0, kSetKK, true, false>(g, stream);
 }
 
+// Block-scaled launches: full tiles, then (when the tiles past the last full
+// round fill at most half of the grid) those tiles as half tiles in a second
+// launch, as launch_group does.
+template <int FA, bool NT>
+static hipError_t launch_mx_group(GemmGroup g, hipStream_t stream)
+{
+    int total = 0;
+    for (int i = 0; i < g.count; ++i) {
+        if (g.p[i].P < kBM || g.p[i].Q < kBN) return hipErrorInvalidValue;
+        g.p[i].first_tile = total;
+        total += g.p[i].tiles_m * g.p[i].tiles_n;
+    }
+    g.total_tiles = total;
+    const int cus = device_cu_count();
+    const int tail = total % cus;
+    const bool split = tail > 0 && 2 * tail <= cus;
+    g.full_units = split ? total - tail : total;
+    g.units = g.full_units;
+    g.first_unit = 0;
+    if (g.full_units > 0) {
+        const hipError_t e = launch(gemm_mx_kernel<FA, 0, false, NT>, dim3(g.full_units < cus ? g.full_units : cus),
+                                    dim3(256), stream, g);
+        if (e != hipSuccess) return e;
+    }
+    if (split) {
+        g.first_unit = g.full_units;
+        g.units = total + tail;
+        return launch(gemm_mx_kernel<FA, 0, true, NT>, dim3(2 * tail), dim3(256), stream, g);
+    }
+    return hipSuccess;
+}
+
+static GemmProblem make_problem_mx(const uint8_t* A, const uint8_t* sa, const uint8_t* B, const uint8_t* sb,
+                                   void* out, int64_t P, int64_t Q, int64_t R)
+{
+    GemmProblem p = make_problem(A, kKMajor, B, kKMajor, nullptr, nullptr, out, P, Q, R);
+    p.sa = sa;
+    p.sb = sb;
+    return p;
+}
+
 hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* sa, int fmt_a, const uint8_t* B, const uint8_t* sb,
                           int fmt_b, void* out, int64_t P, int64_t Q, int64_t R, hipStream_t stream)
 {
-    if (fmt_b != 0 || P < kBM || Q < kBN) return hipErrorInvalidValue;
+    if (fmt_b != 0) return hipErrorInvalidValue;
     GemmGroup g{};
-    g.p[0] = make_problem(A, kKMajor, B, kKMajor, nullptr, nullptr, out, P, Q, R);
-    g.sa = sa;
-    g.sb = sb;
+    g.p[0] = make_problem_mx(A, sa, B, sb, out, P, Q, R);
     g.p[1] = g.p[0];
     g.count = 1;
-    g.total_tiles = g.full_units = g.units = g.p[0].tiles_m * g.p[0].tiles_n;
-    g.first_unit = 0;
-    const int cus = device_cu_count();
-    const dim3 grid(g.units < cus ? g.units : cus);
-    if (fmt_a == 0) return launch(gemm_mx_kernel<0, 0, false>, grid, dim3(256), stream, g);
-    return launch(gemm_mx_kernel<1, 0, false>, grid, dim3(256), stream, g);
+    if (fmt_a == 0) return launch_mx_group<0, false>(g, stream);
+    return launch_mx_group<1, false>(g, stream);
+}
+
+hipError_t launch_gemm_mx_pair(const uint8_t* A0, const uint8_t* sa0, const uint8_t* B0, const uint8_t* sb0,
+                               void* out0, int64_t P0, int64_t Q0, int64_t R0, const uint8_t* A1,
+                               const uint8_t* sa1, const uint8_t* B1, const uint8_t* sb1, void* out1, int64_t P1,
+                               int64_t Q1, int64_t R1, int fmt_a, hipStream_t stream)
+{
+    GemmGroup g{};
+    GemmProblem p0 = make_problem_mx(A0, sa0, B0, sb0, out0, P0, Q0, R0);
+    GemmProblem p1 = make_problem_mx(A1, sa1, B1, sb1, out1, P1, Q1, R1);
+    // as launch_gemm_tn_pair: longest reduction first, groups of 4 tile rows for
+    // outputs wider than 32 column tiles
+    g.p[0] = R1 > R0 ? p1 : p0;
+    g.p[1] = R1 > R0 ? p0 : p1;
+    for (int i = 0; i < 2; ++i)
+        if (g.p[i].group_m == kGroupM && g.p[i].tiles_n > 32) g.p[i].group_m = 4;
+    g.count = 2;
+    if (fmt_a == 0) return launch_mx_group<0, true>(g, stream);   // dX and dW: stored non-temporally
+    return launch_mx_group<1, true>(g, stream);
 }
 
 hipError_t launch_gemm_tn(const uint8_t* A, int fmt_a, int la, const uint8_t* B, int fmt_b, int lb,

@@ -443,6 +443,32 @@ fp8_status fp8_mx_gemm_fwd(const uint8_t* xq, const uint8_t* sx, fp8_fmt x_fmt, 
                            const uint8_t* sw, void* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
+ * fp8_mx_gemm_backward: both backward products of a linear on block-scaled
+ * operands, in one launch (as fp8_gemm_backward does for per-tensor scales):
+ *   dX[m, k] = bf16_RNE( RN32( sum_n dec(dY[m, n]) 2^e(dY; m, n / 32) dec(W[n, k]) 2^e(W^T; k, n / 32) ) )
+ *   dW[n, k] = bf16_RNE( RN32( sum_m dec(dY[m, n]) 2^e(dY^T; n, m / 32) dec(X[m, k]) 2^e(X^T; k, m / 32) ) )
+ * each block along its product's reduction (LLMQ summary, section 4: the
+ * backward pass needs its operands along the other dimension; the MX block
+ * rule of fp8_mx_quantize).  Each output equals what fp8_mx_gemm_fwd computes
+ * from the same operands, bit for bit; dX and dW are written with
+ * non-temporal stores.
+ *
+ *   dyq, sdy    codes [M, N] (dy_fmt) and scales [N / 128][M][4]: fp8_mx_quantize of dY
+ *   dyqt, sdyt  codes [N, M] (dy_fmt) and scales [M / 128][N][4]: fp8_mx_quantize_t of dY
+ *   wqt, swt    codes [K, N] (E4M3) and scales [N / 128][K][4]: fp8_mx_quantize_t of W [N, K]
+ *   xqt, sxt    codes [K, M] (E4M3) and scales [M / 128][K][4]: fp8_mx_quantize_t of X [M, K]
+ *   dx          bf16 [M, K];  dw  bf16 [N, K]
+ * Constraints: M, N, K >= 256, M and N multiples of 128, K a multiple of 16
+ * (else FP8_ERR_UNSUPPORTED); codes and outputs 16-byte aligned, scales 4-byte
+ * aligned; dx and dw overlap neither each other nor any input (else
+ * FP8_ERR_INVALID).
+ */
+fp8_status fp8_mx_gemm_backward(const uint8_t* dyq, const uint8_t* sdy, const uint8_t* dyqt, const uint8_t* sdyt,
+                                fp8_fmt dy_fmt, const uint8_t* wqt, const uint8_t* swt, const uint8_t* xqt,
+                                const uint8_t* sxt, void* dx, void* dw, int64_t M, int64_t N, int64_t K,
+                                hipStream_t stream);
+
+/*
  * Measurement reference, not a step of the FP8 method: a plain device copy
  * dst[0, bytes) = src[0, bytes), built like the streaming kernels above
  * (16-byte vectors, non-temporal loads, the launch shape at which a copy

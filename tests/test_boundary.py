@@ -381,6 +381,27 @@ def test_mx_gemm_validation(lib):
     assert bad(x=X + 8) == UNSUPPORTED                                # misaligned codes
 
 
+def test_mx_gemm_backward_validation(lib):
+    f = lib.fp8_mx_gemm_backward
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] + [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 3 + [ctypes.c_void_p]
+    G = 1 << 24
+    keys = ("dyq", "sdy", "dyqt", "sdyt", "fmt", "wqt", "swt", "xqt", "sxt", "dx", "dw", "M", "N", "K", "s")
+    ok = (A16, A16 + G, A16 + 2 * G, A16 + 3 * G, 1, B16, B16 + G, B16 + 2 * G, B16 + 3 * G, C16, D16,
+          512, 768, 640, None)
+    bad = lambda **kw: f(*[kw.get(k, v) for k, v in zip(keys, ok)])
+    for k in ("dyq", "sdy", "dyqt", "sdyt", "wqt", "swt", "xqt", "sxt", "dx", "dw"):
+        assert bad(**{k: None}) == INVALID, k
+    assert bad(fmt=2) == INVALID
+    assert bad(dw=C16 + 64) == INVALID                                # dx and dw overlap
+    assert bad(dx=B16 + 3 * G) == INVALID                             # dx over the scales of X^T
+    assert b"overlap" in lib.fp8_last_error()
+    assert bad(M=128) == UNSUPPORTED and bad(K=240) == UNSUPPORTED    # below one tile
+    assert bad(N=704) == UNSUPPORTED and bad(M=576) == UNSUPPORTED    # reductions not multiples of 128
+    assert bad(swt=B16 + G + 2) == UNSUPPORTED                        # misaligned scales
+    assert bad(xqt=B16 + 2 * G + 8) == UNSUPPORTED                    # misaligned codes
+
+
 def test_mx_swiglu_validation(lib):
     f = lib.fp8_mx_swiglu_requant
     f.restype = ctypes.c_int

@@ -19,6 +19,12 @@ relative Frobenius error <= 5e-3 and the any-order fp32 summation bound):
 * the 7B-layer QKV forward and the 14B-layer (outlier channels) QKV forward at
   full size on sampled rows;
 * a NaN scale makes exactly its row's (column's) outputs NaN.
+
+fp8_mx_gemm_backward (dgrad and wgrad of a linear in one launch): every output
+against the oracle and bit for bit the separate fp8_mx_gemm_fwd calls, at a
+shape run entirely as half tiles and one with a full round and a half-tile
+round; the 7B down projection's backward at full size (bit for bit the separate
+calls, sampled rows against the oracle).
 """
 import numpy as np
 import pytest
@@ -281,6 +287,67 @@ def test_mx_backward_products(fp8, orc):
     ref = orc.mx_gemm(a, sa, E5, b, sb, E4M3)
     gemm_compare(dw, ref, "mx wgrad")
     mx_bound_check(dw, ref, a, sa, E5, b, sb, np.arange(N, dtype=np.int64), "mx wgrad")
+
+
+def mx_backward_operands(fp8, M, N, K, seed):
+    """dY (e5m2), W and X of a linear, block-quantised for both backward products."""
+    dy = workloads.draw(seed, 1, (M, N), 1e-3).cuda()
+    w = workloads.draw(seed, 2, (N, K), 0.02).cuda()
+    x = workloads.draw(seed, 3, (M, K), 1.0).cuda()
+    dyq, sdy = fp8.mx_quantize(dy, E5M2)
+    dyqt, sdyt = fp8.mx_quantize_t(dy, E5M2)
+    wqt, swt = fp8.mx_quantize_t(w, E4M3)
+    xqt, sxt = fp8.mx_quantize_t(x, E4M3)
+    return dyq, sdy, dyqt, sdyt, wqt, swt, xqt, sxt
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 768, 640), (4096, 256, 4096)])
+def test_mx_gemm_backward_every_output(fp8, orc, M, N, K):
+    """fp8_mx_gemm_backward: dgrad and wgrad in one launch, every output against the
+    oracle and bit for bit the two products run as separate fp8_mx_gemm_fwd calls.
+    512 x 768 x 640: 6 + 9 tiles, all run as half tiles (ragged last column tiles);
+    4096 x 256 x 4096: 16 + 256 tiles, a full round and 16 tiles of the second
+    problem as 32 half tiles."""
+    say("mx_gemm_backward every output", M, N, K)
+    ops = mx_backward_operands(fp8, M, N, K, 73)
+    dyq, sdy, dyqt, sdyt, wqt, swt, xqt, sxt = ops
+    dx, dw = fp8.mx_gemm_backward(*ops, dy_fmt=E5M2)
+    dx, dw = u16(dx), u16(dw)
+    dx1 = u16(fp8.mx_gemm_fwd(dyq, sdy, wqt, swt, E5M2))
+    dw1 = u16(fp8.mx_gemm_fwd(dyqt, sdyt, xqt, sxt, E5M2))
+    assert np.array_equal(dx, dx1), np.argwhere(dx != dx1)[:4].tolist()
+    assert np.array_equal(dw, dw1), np.argwhere(dw != dw1)[:4].tolist()
+    a, sa, b, sb = u8(dyq), row_major(u8(sdy)), u8(wqt), row_major(u8(swt))
+    ref = orc.mx_gemm(a, sa, E5M2, b, sb, E4M3)
+    gemm_compare(dx, ref, "mx backward dgrad")
+    mx_bound_check(dx, ref, a, sa, E5M2, b, sb, np.arange(M, dtype=np.int64), "mx backward dgrad")
+    a, sa, b, sb = u8(dyqt), row_major(u8(sdyt)), u8(xqt), row_major(u8(sxt))
+    ref = orc.mx_gemm(a, sa, E5M2, b, sb, E4M3)
+    gemm_compare(dw, ref, "mx backward wgrad")
+    mx_bound_check(dw, ref, a, sa, E5M2, b, sb, np.arange(N, dtype=np.int64), "mx backward wgrad")
+
+
+def test_mx_gemm_backward_down_7b(fp8, orc):
+    """The 7B down projection's backward (M = 4096, N = 4096, K = 11008: 688 + 688
+    tiles, five rounds and 96 tiles as half tiles): bit for bit the separate calls
+    over every output, and sampled rows of both products against the oracle."""
+    M, N, K = 4096, 4096, 11008
+    say("mx_gemm_backward 7B down", M, N, K)
+    ops = mx_backward_operands(fp8, M, N, K, 79)
+    dyq, sdy, dyqt, sdyt, wqt, swt, xqt, sxt = ops
+    dx, dw = fp8.mx_gemm_backward(*ops, dy_fmt=E5M2)
+    dx, dw = u16(dx), u16(dw)
+    dx1 = u16(fp8.mx_gemm_fwd(dyq, sdy, wqt, swt, E5M2))
+    dw1 = u16(fp8.mx_gemm_fwd(dyqt, sdyt, xqt, sxt, E5M2))
+    assert np.array_equal(dx, dx1), np.argwhere(dx != dx1)[:4].tolist()
+    assert np.array_equal(dw, dw1), np.argwhere(dw != dw1)[:4].tolist()
+    rng = np.random.default_rng(11)
+    for y, (a, sa, b, sb), P, what in ((dx, (dyq, sdy, wqt, swt), M, "dgrad"), (dw, (dyqt, sdyt, xqt, sxt), N, "wgrad")):
+        a, sa, b, sb = u8(a), row_major(u8(sa)), u8(b), row_major(u8(sb))
+        rows = np.unique(np.concatenate([[0, P - 1], rng.integers(0, P, 62)])).astype(np.int64)
+        ref = orc.mx_gemm(a, sa, E5M2, b, sb, E4M3, rows=rows)
+        gemm_compare(y[rows], ref, f"7B down mx {what}")
+        mx_bound_check(y[rows], ref, a, sa, E5M2, b, sb, rows, f"7B down mx {what}")
 
 
 def planted_finite_blocks(seed):
