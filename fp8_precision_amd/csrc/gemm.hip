@@ -80,6 +80,12 @@ constexpr int kStage = kStageA + kStageB;     // 64 KB
 constexpr int kLds = 2 * kStage;              // 128 KB
 constexpr int kEpiRows = 32;                  // epilogue chunk: 32 rows x 128 columns of bf16 per wave
 constexpr int kEpiWave = kEpiRows * 256;      // 8 KB per wave, 32 KB per workgroup (LDS total 160 KB)
+// Half tiles (128 rows of A) use 48 KB per stage (A at 0, B at 16 KB) and run
+// three stages, with 16-row epilogue chunks (4 KB per wave) after them:
+// 3 x 48 + 16 = 160 KB.
+constexpr int kHalfA = kStageA / 2;           // 16 KB
+constexpr int kHalfStage = kHalfA + kStageB;  // 48 KB
+constexpr int kHalfEpi = 3 * kHalfStage;      // 144 KB: the half tiles' epilogue staging
 // Block-scaled (MX) launches: per stage, the E8M0 scales of the step's four
 // 32-byte reduction blocks for the 256 A rows and the 256 B rows (4 bytes per
 // row, 2 KB); two stages take 4 KB, so the epilogue stages 16-row chunks
@@ -102,6 +108,7 @@ constexpr int kWaitVm16 = 0x4F70;
 constexpr int kWaitVm18 = 0x4F72;
 constexpr int kWaitVm12 = 0x0F7C;
 constexpr int kWaitVm14 = 0x0F7E;
+constexpr int kWaitVm24 = 0x4F78;
 
 // Operand layouts.
 constexpr int kKMajor = 0;
@@ -291,6 +298,26 @@ __device__ __forceinline__ void issue_half_stage_mx(const Sources& src, uint32_t
     issue_half_stage(src, stage, kt, wave);
     issue_scale(src, sc_stage, kt, wave & 1, 0);
     issue_scale(src, sc_stage, kt, wave, 1);
+}
+
+// Three-stage half tiles (48 KB stages, B at 16 KB): load idx (0..11), 0..3
+// fill A, 4..11 fill B.
+__device__ __forceinline__ void issue_half3(const Sources& src, uint32_t stage, int kt, int wave, int idx)
+{
+    if (idx < 4) {
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(stage + (uint32_t)(wave * 4 + idx) * 1024u);
+        issue_op<kKMajor, false>(src.a, lds, kt, idx);
+    } else {
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(stage + (uint32_t)kHalfA +
+                                                            (uint32_t)(wave * 8 + idx - 4) * 1024u);
+        issue_op<kKMajor, false>(src.b, lds, kt, idx - 4);
+    }
+}
+
+__device__ __forceinline__ void issue_half3_stage(const Sources& src, uint32_t stage, int kt, int wave)
+{
+#pragma unroll
+    for (int idx = 0; idx < 12; ++idx) issue_half3(src, stage, kt, wave, idx);
 }
 
 // Fragments of the 16x16x128 instruction: block b covers 16 rows of A (or of
@@ -671,6 +698,87 @@ __device__ __forceinline__ void tile_mainloop_half(v4f (&acc)[8][8], v8i (&bq)[8
     __syncthreads();
 }
 
+// Half tiles with three 48 KB stages.  A step is the 32 instructions of
+// half_step; interleaved with them the wave reads the next step's fragments
+// (tile k+1) and issues the 12 loads of tile k+3 into the stage the current
+// step's fragments came from, so each load has two steps to land (with two
+// stages it had one, and the half tile's steps are half as long as a full
+// tile's: its loads were late at every barrier).
+template <int FA, int FB, bool NEXT>
+__device__ __forceinline__ void half_step3(v4f (&acc)[8][8], v8i (&bq)[8], const v8i (&ac)[4], v8i (&an)[4],
+                                           const Sources& src, uint32_t refill, const uint8_t* nxt, int kt_issue,
+                                           int wave, int wm, int wn, int lane)
+{
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+        const int j = t >> 2, i = t & 3;
+        mma16<FA, FB>(acc, ac[i], bq[j], i, j);
+        if (NEXT) {
+            if (i == 3) bq[j] = frag_k(nxt + kHalfA, wn * 8 + j, lane);
+            if ((t & 7) == 1) an[t >> 3] = frag_k(nxt, wm * 4 + (t >> 3), lane);
+            if ((t & 1) == 0 && t < 24) issue_half3(src, refill, kt_issue, wave, t >> 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Before step k: tile k+1 has landed (this wave's loads: only the 12 of tile
+// k+2 may be pending), and every wave has read the stage that step k refills.
+__device__ __forceinline__ void half3_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(kWaitVm12);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The reduction of one half tile whose first three stages (tiles 0, 1, 2,
+// clamped to the last) have been issued into stages 0, 1, 2.  Tile k lives in
+// stage k % 3; loads past the last tile re-load it into a stage that is not
+// read again, so every step issues 12 loads and one vmcnt count serves all.
+template <int FA, int FB>
+__device__ __forceinline__ void tile_mainloop_half3(v4f (&acc)[8][8], v8i (&bq)[8], v8i (&a0)[4], v8i (&a1)[4],
+                                                    const Sources& src, uint8_t* smem, uint32_t smem_addr, int KT,
+                                                    int wave, int wm, int wn, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
+    __builtin_amdgcn_s_waitcnt(kWaitVm24);    // tile 0 landed; the 24 loads of tiles 1 and 2 may be in flight
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bq[j] = frag_k(smem + kHalfA, wn * 8 + j, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a0[i] = frag_k(smem, wm * 4 + i, lane);
+    int s0 = 0;                               // stage of tile kt
+    int kt = 0;
+    for (; kt + 2 < KT; kt += 2) {            // steps kt (A in a0) and kt + 1 (A in a1)
+        const int s1 = s0 == 2 ? 0 : s0 + 1, s2 = s1 == 2 ? 0 : s1 + 1;
+        half3_barrier();
+        half_step3<FA, FB, true>(acc, bq, a0, a1, src, smem_addr + s0 * kHalfStage, smem + s1 * kHalfStage,
+                                 min(kt + 3, KT - 1), wave, wm, wn, lane);
+        half3_barrier();
+        half_step3<FA, FB, true>(acc, bq, a1, a0, src, smem_addr + s1 * kHalfStage, smem + s2 * kHalfStage,
+                                 min(kt + 4, KT - 1), wave, wm, wn, lane);
+        s0 = s2;
+    }
+    if (kt + 1 < KT) {                        // two steps left
+        const int s1 = s0 == 2 ? 0 : s0 + 1;
+        half3_barrier();
+        half_step3<FA, FB, true>(acc, bq, a0, a1, src, smem_addr + s0 * kHalfStage, smem + s1 * kHalfStage, KT - 1,
+                                 wave, wm, wn, lane);
+        half3_barrier();
+        half_step3<FA, FB, false>(acc, bq, a1, a0, src, 0, smem, 0, wave, wm, wn, lane);
+    } else {                                  // one step left
+        half3_barrier();
+        half_step3<FA, FB, false>(acc, bq, a0, a1, src, 0, smem, 0, wave, wm, wn, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+}
+
 // A block-scaled half tile: the steps of tile_mainloop_half with the scales of
 // tile_mainloop_mx.  Each step also reads the next step's scales (from the stage
 // that the step's barrier has seen land: A bytes at t = 2, packed at t = 6; B
@@ -876,7 +984,13 @@ __device__ __forceinline__ void start_tile(Sources& src, const Work& w, uint32_t
     // (w odd) at gate column n0 + 64 (w / 2), so the B blocks 0..3 of a wave are
     // gate columns and blocks 4..7 the up columns of the same outputs.
     const int b_origin = GU ? w.n0 + (wave >> 1) * 64 + (wave & 1) * (w.Q >> 1) - wave * 64 : w.n0;
-    if (HALF) {
+    if (HALF && !GU) {                        // three 48 KB stages
+        set_op<kKMajor>(src.a, w.A, w.m0, w.P, w.R, wave, lane, 32);
+        set_op<kKMajor>(src.b, w.B, b_origin, w.Q, w.R, wave, lane);
+        issue_half3_stage(src, lds_addr, 0, wave);
+        issue_half3_stage(src, lds_addr + kHalfStage, min(1, w.KT - 1), wave);
+        issue_half3_stage(src, lds_addr + 2 * kHalfStage, min(2, w.KT - 1), wave);
+    } else if (HALF) {
         set_op<kKMajor>(src.a, w.A, w.m0, w.P, w.R, wave, lane, 32);
         set_op<kKMajor>(src.b, w.B, b_origin, w.Q, w.R, wave, lane);
         issue_half_stage(src, lds_addr, 0, wave);
@@ -1024,12 +1138,12 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[8][8], const Work& don
     }
 }
 
-// Epilogue of a block-scaled tile: as epilogue() above (no descale: the block
-// scales are inside the sums), staging 16-row chunks (one A block) in a 4 KB
-// LDS region per wave.
-template <bool HALF, bool NT>
-__device__ __forceinline__ void epilogue_mx(const v4f (&acc)[8][8], const Work& done, uint8_t* epi, int wave,
-                                            int wm, int wn, int lane)
+// Epilogue staging 16-row chunks (one A block) in a 4 KB LDS region per wave:
+// the block-scaled tiles (no descale: the block scales are inside the sums) and
+// the three-stage half tiles (DESCALE: the per-tensor factor d, as epilogue()).
+template <bool HALF, bool NT, bool DESCALE>
+__device__ __forceinline__ void epilogue16(const v4f (&acc)[8][8], const Work& done, float d, uint8_t* epi, int wave,
+                                           int wm, int wn, int lane)
 {
     uint8_t* ew = epi + wave * (kEpiRowsMx * 256);
     int ln = lane;
@@ -1042,8 +1156,8 @@ __device__ __forceinline__ void epilogue_mx(const v4f (&acc)[8][8], const Work& 
     for (int i = 0; i < (HALF ? 4 : 8); ++i) {             // chunk: A block i (16 rows)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const f32x2 v01 = {acc[i][j][0], acc[i][j][1]};
-            const f32x2 v23 = {acc[i][j][2], acc[i][j][3]};
+            const f32x2 v01 = DESCALE ? f32x2{acc[i][j][0] * d, acc[i][j][1] * d} : f32x2{acc[i][j][0], acc[i][j][1]};
+            const f32x2 v23 = DESCALE ? f32x2{acc[i][j][2] * d, acc[i][j][3] * d} : f32x2{acc[i][j][2], acc[i][j][3]};
             uint2 o;
             o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, bf16x2));
             o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, bf16x2));
@@ -1195,8 +1309,12 @@ __device__ __forceinline__ void epilogue_gu(const v4f (&acc)[8][8], const Work& 
 template <int FA, int FB, bool EDGE, int SET, bool HALF, bool GU, bool NT>
 __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
-    __shared__ __attribute__((aligned(1024))) uint8_t epi[4 * kEpiWave];
+    // full tiles: two 64 KB stages, then 32 KB of epilogue staging; half tiles
+    // (not gate/up): three 48 KB stages, then 16 KB of epilogue staging
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds + 4 * kEpiWave];
+    uint8_t* const lds = smem;
+    uint8_t* const epi = smem + kLds;
+    constexpr bool kHalf3 = HALF && !GU;
 
     const int G = gridDim.x;
     int slot = blockIdx.x;
@@ -1230,7 +1348,9 @@ __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
         if (tid == 0) *wg_max = 0;
     }
     for (;;) {
-        if (HALF)
+        if (kHalf3)
+            tile_mainloop_half3<FA, FB>(acc, bq, alo, ahi, src, lds, lds_addr, w.KT, wave, wm, wn, lane);
+        else if (HALF)
             tile_mainloop_half<FA, FB>(acc, bq, alo, ahi, src, lds, lds_addr, w.KT, wave, wm, wn, lane);
         else if (SET == kSetKK)
             tile_mainloop<FA, FB, EDGE, kKMajor, kKMajor>(acc, bq, alo, ahi, src, lds, lds_addr, w.KT, wave, wm, wn,
@@ -1254,12 +1374,14 @@ __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
 
         if (GU)
             epilogue_gu<HALF>(acc, done, d, reinterpret_cast<const float*>(epi), wg_max, wm, wn, lane);
+        else if (kHalf3)
+            epilogue16<true, NT, true>(acc, done, d, smem + kHalfEpi, wave, wm, wn, lane);
         else
             epilogue<HALF, NT>(acc, done, d, epi, wave, wm, wn, lane);
-        // The loop-top wait (vmcnt <= 16, or 12 for a half tile) then proves the
-        // next tile's first stage has landed: if one of its loads were pending,
-        // the 16 (12) later loads of the second stage would be too (loads
-        // complete in order), whatever the interleaved stores do.
+        // The loop-top wait (vmcnt <= 16, or 12 / 24 for a half tile) then proves
+        // the next tile's first stage has landed: if one of its loads were
+        // pending, the 16 (12, 24) later loads of the following stages would be
+        // too (loads complete in order), whatever the interleaved stores do.
         if (next >= g.units) break;
     }
     if (GU) {
@@ -1312,7 +1434,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(const GemmGroup g)
             w = work_of<false, HALF, false>(g, v);
             start_tile_mx<HALF>(src, g, w, lds_addr, sc_addr, wave, lane);
         }
-        epilogue_mx<HALF, NT>(acc, done, epi, wave, wm, wn, lane);
+        epilogue16<HALF, NT, false>(acc, done, 1.0f, epi, wave, wm, wn, lane);
         // the loop-top wait (vmcnt <= 18, or 14 for a half tile) then proves the
         // next unit's first stage has landed, as in gemm_tn_kernel
         if (next >= g.units) break;
