@@ -345,7 +345,16 @@ __device__ __forceinline__ v8i frag_mn(const uint8_t* tile, int blk, int lane)
 {
     const int g = lane >> 4, t = (lane & 15) >> 1, e = lane & 1;
     const int h = t | ((g & 1) << 3);
-    const uint32_t a = (uint32_t)(uintptr_t)tile + (uint32_t)((16 * g + t) * 256 + ((blk ^ h) * 16) + 8 * e);
+    // (blk ^ h) * 16 occupies address bits 4..7, which neither the 256-byte row
+    // term, the 8-byte half nor the (1 KB-aligned) stage base touches: the
+    // lane's address for block 0, XOR blk << 4, is the address for block blk.
+    // The base is made opaque here, so the compiler computes that one XOR at each
+    // read instead of holding the 16 addresses of every stage live across the
+    // persistent loop (where it spilled them, and each reload waited for the
+    // whole prefetch in flight)
+    uint32_t base = (uint32_t)(uintptr_t)tile + (uint32_t)((16 * g + t) * 256 + h * 16 + 8 * e);
+    asm volatile("" : "+v"(base));
+    const uint32_t a = base ^ (uint32_t)(blk << 4);
     const lds_u8* q = (const lds_u8*)(uintptr_t)a;
     const v2i x0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(q));
     const v2i x1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(q + 8 * 256));
@@ -355,6 +364,15 @@ __device__ __forceinline__ v8i frag_mn(const uint8_t* tile, int blk, int lane)
     r[0] = x0[0]; r[1] = x0[1]; r[2] = x1[0]; r[3] = x1[1];
     r[4] = x2[0]; r[5] = x2[1]; r[6] = x3[0]; r[7] = x3[1];
     return r;
+}
+
+// The lane number from v_mbcnt in volatile assembly: a value the compiler cannot
+// hoist out of a loop (see its uses).
+__device__ __forceinline__ int opaque_lane()
+{
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    return ln;
 }
 
 template <int L>
@@ -430,6 +448,11 @@ __device__ __forceinline__ void tile_mainloop(v4f (&acc)[8][8], v8i (&bq)[8], v8
                                               const Sources& src, uint8_t* lds, uint32_t lds_addr, int KT, int wave,
                                               int wm, int wn, int lane)
 {
+    // MN-major forms: the lane number taken afresh for every tile (volatile, so
+    // neither it nor the fragment addresses derived from it are hoisted out of
+    // the persistent loop, where the allocator spilled them and each reload
+    // waited for the whole prefetch in flight)
+    if (LA == kMNMajor || LB == kMNMajor) lane = opaque_lane();
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -984,6 +1007,7 @@ __device__ __forceinline__ void start_tile(Sources& src, const Work& w, uint32_t
     // (w odd) at gate column n0 + 64 (w / 2), so the B blocks 0..3 of a wave are
     // gate columns and blocks 4..7 the up columns of the same outputs.
     const int b_origin = GU ? w.n0 + (wave >> 1) * 64 + (wave & 1) * (w.Q >> 1) - wave * 64 : w.n0;
+    if (SET == kSetMN) lane = opaque_lane();  // as in tile_mainloop: no lane constants held across tiles
     if (HALF && !GU) {                        // three 48 KB stages
         set_op<kKMajor>(src.a, w.A, w.m0, w.P, w.R, wave, lane, 32);
         set_op<kKMajor>(src.b, w.B, b_origin, w.Q, w.R, wave, lane);
@@ -1377,7 +1401,7 @@ __global__ void __launch_bounds__(256, 1) gemm_tn_kernel(const GemmGroup g)
         else if (kHalf3)
             epilogue16<true, NT, true>(acc, done, d, smem + kHalfEpi, wave, wm, wn, lane);
         else
-            epilogue<HALF, NT>(acc, done, d, epi, wave, wm, wn, lane);
+            epilogue<HALF, NT>(acc, done, d, epi, wave, wm, wn, SET == kSetMN ? opaque_lane() : lane);
         // The loop-top wait (vmcnt <= 16, or 12 / 24 for a half tile) then proves
         // the next tile's first stage has landed: if one of its loads were
         // pending, the 16 (12, 24) later loads of the following stages would be
