@@ -9,8 +9,9 @@ with the oracle (relative Frobenius error <= 5e-3 and the any-order fp32
 summation bound), for each compiled form:
 
 * forward (e4m3 x e4m3, K-major), three full rounds (the 7B qkv shape) and a
-  launch with a balanced half-tile round, and the edge form (a matrix with
-  fewer than 256 rows) over two rounds;
+  launch with a balanced half-tile round (at reductions of 1, 2, 3, 4 and 5
+  steps: every branch of the half tile's three-stage step loop), and the edge
+  form (a matrix with fewer than 256 rows) over two rounds;
 * a forward whose B operand is larger than the Infinity Cache (groups of 24
   tile rows instead of 8): every output bit for bit against the same product
   in column slices (each with the default groups), sampled rows against the
@@ -77,6 +78,12 @@ INV_B = np.float32(0.0123)
 FWD = [("7B qkv fwd, 3 rounds", 4096, 12288, 4096),
        ("balanced half-tile round", 4352, 4096, 512),
        ("edge form, 2 rounds", 128, 76800, 256)]
+
+
+# The half-tile round runs a three-stage pipeline whose step loop has separate
+# branches for 1, 2, 3 and more reduction steps: 4352 x 4096 (one round, then 16
+# tiles as 32 half tiles) at reductions of 1, 2, 3 and 5 steps of 128.
+FWD += [(f"half-tile round, {R // 128} reduction steps", 4352, 4096, R) for R in (128, 256, 384, 640)]
 
 
 @pytest.mark.parametrize("name,P,Q,R", FWD)

@@ -18,6 +18,8 @@ relative Frobenius error <= 5e-3 and the any-order fp32 summation bound):
   blocks span 2^30 of scale;
 * the 7B-layer QKV forward and the 14B-layer (outlier channels) QKV forward at
   full size on sampled rows;
+* every output of a launch whose last tiles run as half tiles, at reductions of
+  1, 2, 3 and 5 steps (every branch of the half tile's step loop);
 * a NaN scale makes exactly its row's (column's) outputs NaN.
 
 fp8_mx_gemm_backward (dgrad and wgrad of a linear in one launch): every output
@@ -173,6 +175,24 @@ def test_every_output_two_rounds(fp8, orc, fx):
     for r0 in range(0, M, 1000):
         rr = rows[r0:r0 + 1000]
         mx_bound_check(y[rr], ref[rr], a, sa, fx, b, sb, rr, "mx every output")
+
+
+@pytest.mark.parametrize("K", [128, 256, 384, 640])
+def test_half_tile_round_short_reductions(fp8, orc, K):
+    """4352 x 4096: one round, then 16 tiles as 32 half tiles, at reductions of 1, 2,
+    3 and 5 steps of 128 (every branch of the half tile's step loop), every output."""
+    M, N = 4352, 4096
+    say("mx_gemm half-tile round", M, N, K)
+    x = workloads.draw(83, K, (M, K), 4.0)
+    w = workloads.draw(83, K + 1, (N, K), 0.02)
+    xq, sx, wq, sw = mx_operands(fp8, x, w)
+    y = u16(fp8.mx_gemm_fwd(xq, sx, wq, sw))
+    a, sa, b, sb = u8(xq), row_major(u8(sx)), u8(wq), row_major(u8(sw))
+    ref = orc.mx_gemm(a, sa, E4M3, b, sb, E4M3)
+    gemm_compare(y, ref, f"mx half-tile round K={K}")
+    for r0 in range(0, M, 1088):
+        rr = np.arange(r0, min(r0 + 1088, M), dtype=np.int64)
+        mx_bound_check(y[rr], ref[rr], a, sa, E4M3, b, sb, rr, f"mx half-tile round K={K}")
 
 
 @pytest.mark.parametrize("cfg_name", ["layer7b", "layer14b"])
