@@ -20,6 +20,9 @@ summation bound), for each compiled form:
   pair (four rounds, long dgrad tiles first), and a pair whose tiles end in a
   balanced half-tile round;
 * the same pair on the untransposed operands (MN-major, two rounds);
+* pairs whose products differ in reduction length, with long and short tiles
+  in one round: every output, and bit for bit the separate dgrad / wgrad calls
+  and the MN-major pair;
 * the gate/up forward with the SwiGLU statistic in its epilogue, with a
   half-tile round.
 
@@ -149,6 +152,39 @@ def test_backward_pair_every_output(fp8, orc, name, M, N, K):
                                dev(torch.from_numpy(wqt)), dev(torch.from_numpy(xqt)), scal(ia), scal(iw), scal(ix))
     check_full(orc, dx, dyq, E5M2, wqt, ia, iw, name + " dgrad")
     check_full(orc, dw, dyqt, E5M2, xqt, ia, ix, name + " wgrad")
+
+
+# Pairs whose two products differ in reduction length, with a long-tile count that
+# does not fill the 256-CU grid evenly, so that one round mixes long and short tiles:
+# 512 x 4608 x 3328 (26 dgrad tiles of 36 steps, 234 wgrad tiles of 4 steps; the
+# last 4 as half tiles) and
+# 512 x 4352 x 3584 (28 of 34 steps, 238 of 4; the last 10 as half tiles).
+MIXED_PAIRS = [(512, 4608, 3328), (512, 4352, 3584)]
+
+
+@pytest.mark.parametrize("M,N,K", MIXED_PAIRS)
+def test_backward_pair_mixed_lengths(fp8, orc, M, N, K):
+    """Every output against the oracle; bit for bit the separate dgrad and wgrad
+    calls (each output is reduced in the same order whichever slot computes it),
+    and the untransposed-operand pair bit for bit the same."""
+    say("gemm backward pair, mixed reduction lengths", M, N, K)
+    g = torch.Generator(device="cpu").manual_seed(M + N + K)
+    dyq, wq, xq = pair_operands(g, M, N, K, E5M2)
+    dyqt, wqt, xqt = (np.ascontiguousarray(t.T) for t in (dyq, wq, xq))
+    ia, iw, ix = INV_A[E5M2], np.float32(1 / 448.0), INV_B
+    d = {n: dev(torch.from_numpy(t)) for n, t in (("dyq", dyq), ("dyqt", dyqt), ("wq", wq), ("wqt", wqt),
+                                                    ("xq", xq), ("xqt", xqt))}
+    sa, sw, sx = scal(ia), scal(iw), scal(ix)
+    dx, dw = fp8.gemm_backward(d["dyq"], d["dyqt"], E5M2, d["wqt"], d["xqt"], sa, sw, sx)
+    dx1 = fp8.gemm_dgrad(d["dyq"], E5M2, d["wqt"], sa, sw)
+    dw1 = fp8.gemm_wgrad(d["dyqt"], E5M2, d["xqt"], sa, sx)
+    dxm, dwm = fp8.gemm_backward_mn(d["dyq"], E5M2, d["wq"], d["xq"], sa, sw, sx)
+    for what, x, y in (("dgrad vs separate", dx, dx1), ("wgrad vs separate", dw, dw1),
+                       ("dgrad vs MN-major pair", dx, dxm), ("wgrad vs MN-major pair", dw, dwm)):
+        bad = np.argwhere(u16(x) != u16(y))
+        assert bad.size == 0, (what, bad[:4].tolist())
+    check_full(orc, dx, dyq, E5M2, wqt, ia, iw, "mixed-length pair dgrad")
+    check_full(orc, dw, dyqt, E5M2, xqt, ia, ix, "mixed-length pair wgrad")
 
 
 def test_backward_pair_mn_every_output(fp8, orc):

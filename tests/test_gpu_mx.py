@@ -347,6 +347,25 @@ def test_mx_gemm_backward_every_output(fp8, orc, M, N, K):
     mx_bound_check(dw, ref, a, sa, E5M2, b, sb, np.arange(N, dtype=np.int64), "mx backward wgrad")
 
 
+def test_mx_gemm_backward_mixed_lengths(fp8, orc):
+    """512 x 4608 x 3328: products of different reduction lengths whose long tiles do
+    not fill the grid evenly (one round mixes long and short tiles): every output
+    against the oracle and bit for bit the separate calls."""
+    M, N, K = 512, 4608, 3328
+    say("mx_gemm_backward mixed reduction lengths", M, N, K)
+    ops = mx_backward_operands(fp8, M, N, K, 89)
+    dyq, sdy, dyqt, sdyt, wqt, swt, xqt, sxt = ops
+    dx, dw = fp8.mx_gemm_backward(*ops, dy_fmt=E5M2)
+    dx, dw = u16(dx), u16(dw)
+    assert np.array_equal(dx, u16(fp8.mx_gemm_fwd(dyq, sdy, wqt, swt, E5M2)))
+    assert np.array_equal(dw, u16(fp8.mx_gemm_fwd(dyqt, sdyt, xqt, sxt, E5M2)))
+    for y, (a, sa, b, sb), what in ((dx, (dyq, sdy, wqt, swt), "dgrad"), (dw, (dyqt, sdyt, xqt, sxt), "wgrad")):
+        a, sa, b, sb = u8(a), row_major(u8(sa)), u8(b), row_major(u8(sb))
+        ref = orc.mx_gemm(a, sa, E5M2, b, sb, E4M3)
+        gemm_compare(y, ref, f"mx mixed-length {what}")
+        mx_bound_check(y, ref, a, sa, E5M2, b, sb, np.arange(a.shape[0], dtype=np.int64), f"mx mixed-length {what}")
+
+
 def test_mx_gemm_backward_down_7b(fp8, orc):
     """The 7B down projection's backward (M = 4096, N = 4096, K = 11008: 688 + 688
     tiles, five rounds and 96 tiles as half tiles): bit for bit the separate calls
