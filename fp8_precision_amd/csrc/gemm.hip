@@ -47,8 +47,10 @@
 //    tiles), renumbered XCD-major so that the 32 CUs of an XCD (sharing one L2)
 //    work on consecutive tiles; the next tile's first stages load during the
 //    epilogue.  When the last round would keep at most half of the CUs busy,
-//    its tiles are split into 128 x 256 half tiles (same loads and fragment
-//    reads, a 64 x 128 wave tile), which halves that round.
+//    its tiles are split into 128 x 256 half tiles (the same B loads and
+//    fragment reads, half the A rows, a 64 x 128 wave tile) in a launch of
+//    their own; a half tile's 48 KB stage lets it run three stages, its loads
+//    issued two steps ahead.
 //  - Output stores: ordinary for the forward products (the statistic or
 //    SwiGLU pass that follows reads them from the Infinity Cache); non-temporal
 //    for the backward products (a template argument: with a run-time choice the
