@@ -309,42 +309,43 @@ def test_mx_backward_products(fp8, orc):
     mx_bound_check(dw, ref, a, sa, E5, b, sb, np.arange(N, dtype=np.int64), "mx wgrad")
 
 
-def mx_backward_operands(fp8, M, N, K, seed):
-    """dY (e5m2), W and X of a linear, block-quantised for both backward products."""
+def mx_backward_operands(fp8, M, N, K, seed, dy_fmt=E5M2):
+    """dY (e5m2 unless given), W and X of a linear, block-quantised for both backward products."""
     dy = workloads.draw(seed, 1, (M, N), 1e-3).cuda()
     w = workloads.draw(seed, 2, (N, K), 0.02).cuda()
     x = workloads.draw(seed, 3, (M, K), 1.0).cuda()
-    dyq, sdy = fp8.mx_quantize(dy, E5M2)
-    dyqt, sdyt = fp8.mx_quantize_t(dy, E5M2)
+    dyq, sdy = fp8.mx_quantize(dy, dy_fmt)
+    dyqt, sdyt = fp8.mx_quantize_t(dy, dy_fmt)
     wqt, swt = fp8.mx_quantize_t(w, E4M3)
     xqt, sxt = fp8.mx_quantize_t(x, E4M3)
     return dyq, sdy, dyqt, sdyt, wqt, swt, xqt, sxt
 
 
-@pytest.mark.parametrize("M,N,K", [(512, 768, 640), (4096, 256, 4096)])
-def test_mx_gemm_backward_every_output(fp8, orc, M, N, K):
+@pytest.mark.parametrize("M,N,K,fa", [(512, 768, 640, E5M2), (4096, 256, 4096, E5M2), (512, 768, 640, E4M3),
+                                      (4096, 256, 4096, E4M3)])
+def test_mx_gemm_backward_every_output(fp8, orc, M, N, K, fa):
     """fp8_mx_gemm_backward: dgrad and wgrad in one launch, every output against the
     oracle and bit for bit the two products run as separate fp8_mx_gemm_fwd calls.
     512 x 768 x 640: 6 + 9 tiles, all run as half tiles (ragged last column tiles);
     4096 x 256 x 4096: 16 + 256 tiles, a full round and 16 tiles of the second
     problem as 32 half tiles."""
-    say("mx_gemm_backward every output", M, N, K)
-    ops = mx_backward_operands(fp8, M, N, K, 73)
+    say("mx_gemm_backward every output", M, N, K, fa)
+    ops = mx_backward_operands(fp8, M, N, K, 73, fa)
     dyq, sdy, dyqt, sdyt, wqt, swt, xqt, sxt = ops
-    dx, dw = fp8.mx_gemm_backward(*ops, dy_fmt=E5M2)
+    dx, dw = fp8.mx_gemm_backward(*ops, dy_fmt=fa)
     dx, dw = u16(dx), u16(dw)
-    dx1 = u16(fp8.mx_gemm_fwd(dyq, sdy, wqt, swt, E5M2))
-    dw1 = u16(fp8.mx_gemm_fwd(dyqt, sdyt, xqt, sxt, E5M2))
+    dx1 = u16(fp8.mx_gemm_fwd(dyq, sdy, wqt, swt, fa))
+    dw1 = u16(fp8.mx_gemm_fwd(dyqt, sdyt, xqt, sxt, fa))
     assert np.array_equal(dx, dx1), np.argwhere(dx != dx1)[:4].tolist()
     assert np.array_equal(dw, dw1), np.argwhere(dw != dw1)[:4].tolist()
     a, sa, b, sb = u8(dyq), row_major(u8(sdy)), u8(wqt), row_major(u8(swt))
-    ref = orc.mx_gemm(a, sa, E5M2, b, sb, E4M3)
+    ref = orc.mx_gemm(a, sa, fa, b, sb, E4M3)
     gemm_compare(dx, ref, "mx backward dgrad")
-    mx_bound_check(dx, ref, a, sa, E5M2, b, sb, np.arange(M, dtype=np.int64), "mx backward dgrad")
+    mx_bound_check(dx, ref, a, sa, fa, b, sb, np.arange(M, dtype=np.int64), "mx backward dgrad")
     a, sa, b, sb = u8(dyqt), row_major(u8(sdyt)), u8(xqt), row_major(u8(sxt))
-    ref = orc.mx_gemm(a, sa, E5M2, b, sb, E4M3)
+    ref = orc.mx_gemm(a, sa, fa, b, sb, E4M3)
     gemm_compare(dw, ref, "mx backward wgrad")
-    mx_bound_check(dw, ref, a, sa, E5M2, b, sb, np.arange(N, dtype=np.int64), "mx backward wgrad")
+    mx_bound_check(dw, ref, a, sa, fa, b, sb, np.arange(N, dtype=np.int64), "mx backward wgrad")
 
 
 def test_mx_gemm_backward_mixed_lengths(fp8, orc):
