@@ -183,7 +183,7 @@ def build_step(fp8, dev, cfg_name="layer7b", layout="copies", swiglu_bwd=False, 
     # the step's per-tensor absmax statistics live in one buffer, cleared once at
     # the start of the step; each absmax accumulates into its slot
     stats = torch.empty(64, dtype=torch.float32, device=dev)
-    ops.append(Op("clear statistics", lambda: stats.zero_(), "zero", 0))
+    ops.append(Op("clear statistics", lambda: fp8.absmax_clear(stats), "zero", 0))
     slots = iter(range(64))
 
     def quantize_op(tag, x, rows, cols, fmt, am, want_qt):
@@ -682,7 +682,7 @@ def mx_layer(fp8, dev, cfg_name="layer7b", reps=10):
         t = {k: [] for k in calls}
         for r in range(reps + 2):
             for seq in order:
-                stats.zero_()
+                fp8.absmax_clear(stats)
                 pairs = []
                 for k in seq:
                     a, b = ev()

@@ -30,6 +30,7 @@ _SIGS = {
     "fp8_absmax": (_i32, [_vp, _i64, _vp, _vp]),
     "fp8_absmax_accumulate": (_i32, [_vp, _i64, _vp, _vp]),
     "fp8_absmax_accumulate_many": (_i32, [ctypes.c_int, _vp, _vp, _vp, _vp]),
+    "fp8_absmax_clear": (_i32, [_vp, _i64, _vp]),
     "fp8_quantize": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp8_quantize_many": (_i32, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp8_swiglu_requant": (_i32, [_vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp]),
@@ -151,6 +152,15 @@ def absmax_accumulate_many(xs, outs) -> None:
     op = (ctypes.c_void_p * k)(*[_ptr(o) for o in outs])
     _run("fp8_absmax_accumulate_many", _lib.fp8_absmax_accumulate_many, list(xs) + outs,
          k, ctypes.cast(xp, _vp), ctypes.cast(ns, _vp), ctypes.cast(op, _vp))
+
+
+def absmax_clear(stats: torch.Tensor) -> None:
+    """Set every statistic of a contiguous fp32 device tensor to +0 (the start
+    of the running absmax that the accumulating calls update), in one launch."""
+    _dev_tensor(stats, "stats", torch.float32)
+    if not 1 <= stats.numel() <= 1 << 20:
+        raise ValueError("1 to 2^20 statistics")
+    _run("fp8_absmax_clear", _lib.fp8_absmax_clear, (stats,), _ptr(stats), stats.numel())
 
 
 def quantize(x: torch.Tensor, fmt: int, amax: torch.Tensor, want_q: bool = True, want_qt: bool = False,

@@ -154,6 +154,17 @@ fp8_status fp8_absmax_accumulate_many(int count, const void* const* x, const int
     return FP8_OK;
 }
 
+fp8_status fp8_absmax_clear(float* absmax, int64_t count, hipStream_t stream)
+{
+    t_last_error.clear();
+    if (!absmax) return fail(FP8_ERR_INVALID, "fp8_absmax_clear: null pointer");
+    if (count < 1 || count > ((int64_t)1 << 20)) return fail(FP8_ERR_INVALID, "fp8_absmax_clear: count must be in [1, 2^20]");
+    if (!aligned(absmax, 4)) return fail(FP8_ERR_UNSUPPORTED, "fp8_absmax_clear: absmax must be 4-byte aligned");
+    hipError_t e = fp8k::launch_absmax_clear(absmax, count, stream);
+    if (e != hipSuccess) return fail_hip("fp8_absmax_clear", e);
+    return FP8_OK;
+}
+
 fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_fmt fmt, const float* absmax,
                         uint8_t* q, uint8_t* qt, float* scale, float* inv_scale, hipStream_t stream)
 {

@@ -44,6 +44,8 @@ hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, bool accu
 constexpr int kMaxAbsTensors = 8;
 hipError_t launch_absmax_many(int count, const void* const* x, const int64_t* n, float* const* absmax,
                               hipStream_t stream);
+// count fp32 statistics set to +0 (count <= 2^20).
+hipError_t launch_absmax_clear(float* absmax, int64_t count, hipStream_t stream);
 
 // Block-scaled GEMM out[P, Q] = bf16(sum_r dec(A) 2^ea dec(B) 2^eb) of K-major
 // operands A [P, R], B [Q, R] (B in E4M3) with E8M0 scales stored step-major,

@@ -39,6 +39,13 @@ __global__ void __launch_bounds__(64) zero_u32_kernel(uint32_t* p)
     if (threadIdx.x == 0) *p = 0u;
 }
 
+// n words set to zero (the +0 start of n running statistics), one per lane.
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* __restrict__ p, int n)
+{
+    const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
 // One pass over x; each block folds its maximum into *out with one atomicMax on
 // the fp32 bit pattern (for non-negative values the unsigned order of the bits
 // is the numeric order, and NaN patterns sort above infinity).  One block of 16
@@ -161,6 +168,12 @@ hipError_t launch_absmax_many(int count, const void* const* x, const int64_t* n,
         g.first[i + 1] = g.first[i] + (int)b;
     }
     return launch(absmax_many_kernel, dim3((unsigned)g.first[count]), dim3(kAbsThreads), stream, g);
+}
+
+hipError_t launch_absmax_clear(float* absmax, int64_t count, hipStream_t stream)
+{
+    return launch(zero_words_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), stream,
+                  reinterpret_cast<uint32_t*>(absmax), (int)count);
 }
 
 hipError_t launch_absmax_bf16(const void* x, int64_t n, float* absmax, bool accumulate, hipStream_t stream)

@@ -116,6 +116,19 @@ fp8_status fp8_absmax_accumulate_many(int count, const void* const* x, const int
                                       float* const* absmax, hipStream_t stream);
 
 /*
+ * Sets count running statistics to +0, the start value of the running absmax
+ * that fp8_absmax_accumulate and fp8_absmax_accumulate_many fold tensors into
+ * (FastML report, FP8 training without delayed scaling: each scale comes from
+ * the statistic of the current tensor, so a step's statistics start afresh
+ * rather than carrying an amax history over).  One launch for a step's whole
+ * set of statistics; stream-ordered like every other call.
+ *
+ *   absmax  fp32 [count] in device memory, 4-byte aligned (written)
+ *   count   1 .. 2^20
+ */
+fp8_status fp8_absmax_clear(float* absmax, int64_t count, hipStream_t stream);
+
+/*
  * Quantise a bf16 [rows, cols] tensor with the scale of its absmax:
  *   s      = fp8_max / absmax  (one fp32 division; 1 when absmax == 0; held at
  *            FLT_MAX if the division overflows)

@@ -36,7 +36,7 @@ def lib():
     lib.fp8_gemm_wgrad.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.fp8_last_error.restype = ctypes.c_char_p
     lib.fp8_status_string.restype = ctypes.c_char_p
-    for f in ("fp8_absmax", "fp8_absmax_accumulate", "fp8_absmax_accumulate_many", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd",
+    for f in ("fp8_absmax", "fp8_absmax_accumulate", "fp8_absmax_accumulate_many", "fp8_absmax_clear", "fp8_quantize", "fp8_swiglu_requant", "fp8_gemm_fwd",
               "fp8_gemm_fwd_swiglu_absmax", "fp8_gemm_dgrad", "fp8_gemm_wgrad"):
         getattr(lib, f).restype = i32
     return lib
@@ -441,3 +441,14 @@ def test_mx_quantize_both_validation(lib):
     assert f(A16, 128, 128, 0, q + 8, sq, qt, sqt, None) == UNSUPPORTED
     assert f(A16, 128, 128, 0, q, sq + 2, qt, sqt, None) == UNSUPPORTED     # misaligned scales
     assert f(A16, 128, 128, 0, q, sq, qt, sqt + 1, None) == UNSUPPORTED
+
+
+def test_absmax_clear_validation(lib):
+    f = lib.fp8_absmax_clear
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    assert f(None, 4, None) == INVALID
+    assert f(A16, 0, None) == INVALID and f(A16, -1, None) == INVALID
+    assert f(A16, (1 << 20) + 1, None) == INVALID
+    assert b"count" in lib.fp8_last_error()
+    assert f(A16 + 2, 4, None) == UNSUPPORTED                          # not 4-byte aligned

@@ -138,6 +138,26 @@ def test_absmax_accumulate_many(fp8, orc):
         fp8.absmax_accumulate_many(xs8 + xs[:1], [s8[i:i + 1] for i in range(8)] + [slots[0:1]])
 
 
+def test_absmax_clear(fp8, orc):
+    """fp8_absmax_clear sets exactly its slots to +0 (600 of them: three
+    256-lane blocks, the last one partial) and leaves the neighbours alone; a
+    statistic accumulated after it equals the tensor's fresh absmax."""
+    say("absmax clear")
+    buf = torch.full((700,), -3.5, dtype=torch.float32, device="cuda")   # sign bit set
+    fp8.absmax_clear(buf[5:605])
+    torch.cuda.synchronize()
+    r = buf.cpu().numpy()
+    assert (r[5:605] == 0).all() and not np.signbit(r[5:605]).any()
+    assert (r[:5] == -3.5).all() and (r[605:] == -3.5).all()
+    b = u16(workloads.draw(103, 0, (4097,), 2.0))
+    x = dev(torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16))
+    fp8.absmax(x, buf[7:8], accumulate=True)
+    torch.cuda.synchronize()
+    assert_f32_equal(buf[7:8].cpu().numpy()[0], orc.absmax_bf16(b), "accumulated after the clear")
+    with pytest.raises(ValueError):
+        fp8.absmax_clear(buf[:0])
+
+
 def test_quantize_many(fp8, orc):
     """Up to 8 tensors in one launch, each bit-identical to its own fp8_quantize
     call and to the oracle: mixed formats, q only / qt only / both, ragged
